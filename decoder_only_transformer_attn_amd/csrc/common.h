@@ -1,0 +1,88 @@
+// Shared device helpers for the gfx950 kernels: storage types, bf16 rounding,
+// MFMA traits and wavefront reductions.  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptmi {
+
+typedef uint16_t bf16;  // storage of a bfloat16 value (upper half of an fp32)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite on this path).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return bf16(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return f32_to_bf16(v); }
+
+// 32x32 MFMA traits.  One instruction multiplies a 32 x KPI slice of A (rows
+// m) by a KPI x 32 slice of B (columns n).  Lane l holds KPL consecutive k
+// values of row (l % 32) of A and of column (l % 32) of B, at k offset
+// (l / 32) * KPL; the 32x32 fp32 result is spread over 16 registers per lane:
+// register r of lane l holds row (r/4)*8 + (l/32)*4 + (r%4), column l % 32.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KPL = 8;    // k values per lane per instruction
+  static constexpr int KPI = 16;   // k extent of one instruction
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // KPL consecutive values starting at p (16-byte aligned).
+  static __device__ __forceinline__ frag load(const bf16* p) {
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KPI = 2;
+  typedef float frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+};
+
+// Row index (within a 32x32 tile) of accumulator register r for lane l.
+__device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Reductions over the 32 lanes of one half-wave (lanes sharing l / 32).
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace gptmi

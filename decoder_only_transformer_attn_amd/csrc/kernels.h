@@ -1,0 +1,51 @@
+// Internal launcher interface between the host API (gptmi.cpp) and the HIP
+// kernels.  Every launcher enqueues on the given stream and returns the launch
+// status; none allocates or synchronises.  dtype: 0 = fp32, 1 = bf16.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptmi {
+
+struct QKVArgs {
+  const void* A;      // LN output [M, C]
+  const void* W;      // c_attn weight [3C, C]
+  const void* bias;   // [3C]
+  int M, C, H, D, T_seq;
+  void* q;  long long q_bh;            // Q [B,H,T,D]
+  void* k;  long long k_bh;            // K [B,H,Tk,D]
+  void* vt; long long v_bh; int v_ld;  // U^T [B,H,D,Tk], row stride v_ld
+  const int32_t* pos;                  // nullable: cache position of t = 0
+};
+
+struct AttnArgs {
+  const void* q;  long long q_bh;
+  const void* k;  long long k_bh; int k_ld;
+  const void* vt; long long v_bh; int v_ld;
+  void* o; int o_ld;                   // O [B*T, o_ld], head h at columns [hD, hD+D)
+  int B, H, T_seq, D;
+  float scale_log2;                    // log2(e) / sqrt(D)
+};
+
+hipError_t launch_embed_ln(int dtype, int M, int C, int T_seq, float eps, const int32_t* idx, const void* wte,
+                           const void* wpe, int vocab, float* x, const void* g, const void* b, void* out,
+                           hipStream_t st);
+hipError_t launch_layernorm(int dtype, int M, int C, float eps, const float* x, const void* g, const void* b,
+                            void* out, hipStream_t st);
+hipError_t launch_linear(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N,
+                         int K, void* out, int ldo, int act, int out_f32, hipStream_t st);
+hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M,
+                               int N, int K, float* x, int ldx, hipStream_t st);
+hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st);
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+int head_tile_n(int dtype);
+hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int V, int C, void* logits,
+                          long long ld_logits, float* part_max, float* part_sum, float* tgt, const int32_t* targets,
+                          const int32_t* idx, int T_seq, hipStream_t st);
+// Per-token loss from the head partials, then a deterministic mean.
+int ce_reduce_blocks(int M);
+hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,
+                            const int32_t* targets, const int32_t* idx, int T_seq, int V, float* token_loss,
+                            double* block_sums, float* mean_loss, hipStream_t st);
+
+}  // namespace gptmi

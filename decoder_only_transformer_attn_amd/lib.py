@@ -1,0 +1,205 @@
+"""ctypes binding of libgptmi.so (the C ABI in include/gptmi.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the stream
+(`torch.cuda.current_stream().cuda_stream`).  There is no fallback: if the
+library is missing, `load()` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptmi.so")
+
+GPT_OK = 0
+STATUS = {0: "GPT_OK", -1: "GPT_ERR_NULL", -2: "GPT_ERR_CONFIG", -3: "GPT_ERR_SEQ_TOO_LONG",
+          -4: "GPT_ERR_SHAPE", -5: "GPT_ERR_WORKSPACE", -6: "GPT_ERR_DTYPE", -7: "GPT_ERR_HIP"}
+
+# Every exported function and its ctypes signature.
+_c_int, _c_i64, _vp, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+class gpt_config(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("ctx", ctypes.c_int32), ("n_embd", ctypes.c_int32),
+                ("n_head", ctypes.c_int32), ("n_layer", ctypes.c_int32), ("n_ff", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+_CFG = ctypes.POINTER(gpt_config)
+SIGNATURES = {
+    "gpt_param_count": (_c_i64, [_CFG]),
+    "gpt_param_offsets": (_c_int, [_CFG, ctypes.POINTER(ctypes.c_int64), _c_int]),
+    "gpt_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt_forward": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_forward_timed": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                                   _vp, _vp, _c_int]),
+    "gpt_status_string": (ctypes.c_char_p, [_c_int]),
+    "gpt_debug_layernorm": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _vp, _vp]),
+    "gpt_debug_linear": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "gpt_debug_attention": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+}
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m decoder_only_transformer_attn_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+class GPTError(RuntimeError):
+    pass
+
+
+def check(status: int) -> None:
+    if status != GPT_OK:
+        msg = load().gpt_status_string(status).decode()
+        raise GPTError(f"{STATUS.get(status, status)}: {msg}")
+
+
+def cfg_c(cfg) -> gpt_config:
+    return gpt_config(cfg.vocab, cfg.ctx, cfg.n_embd, cfg.n_head, cfg.n_layer, cfg.n_ff, cfg.ln_eps, cfg.dtype)
+
+
+def param_count(cfg) -> int:
+    return int(load().gpt_param_count(ctypes.byref(cfg_c(cfg))))
+
+
+def param_offsets(cfg):
+    n = 2 + 12 * cfg.n_layer + 3
+    arr = (ctypes.c_int64 * n)()
+    check(load().gpt_param_offsets(ctypes.byref(cfg_c(cfg)), arr, n))
+    return list(arr)
+
+
+def workspace_bytes(cfg, B: int, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().gpt_workspace_bytes(ctypes.byref(cfg_c(cfg)), B, T, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def forward(cfg, params, idx, targets=None, logits=None, token_loss=None, mean_loss=None, ws=None,
+            stream=None) -> None:
+    """Enqueue gpt_forward on the stream.  All tensors are CUDA (HIP) tensors:
+    params [param_count] (float32 or bf16), idx int32 [B,T], optional targets
+    int32 [B,T], logits [B,T,V], token_loss f32 [B,T], mean_loss f32 [1], ws uint8."""
+    B, T = idx.shape
+    check(load().gpt_forward(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets), _ptr(logits),
+                             _ptr(token_loss), _ptr(mean_loss), _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream)))
+
+
+KERNEL = {"head": 0, "qkv": 1, "attn": 2, "proj": 3, "fc": 4, "fcproj": 5, "ln": 6}
+
+
+def forward_timed(cfg, params, idx, targets, logits, token_loss, mean_loss, ws, ev_begin: int, ev_end: int,
+                  which: str, stream=None) -> None:
+    """gpt_forward with hipEvent_t handles recorded around one kernel class."""
+    B, T = idx.shape
+    check(load().gpt_forward_timed(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets),
+                                   _ptr(logits), _ptr(token_loss), _ptr(mean_loss), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream), ev_begin, ev_end,
+                                   KERNEL[which]))
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from libamdhip64 (torch's Event does not expose its handle)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+        self.ev = []
+
+
+def torch_dtype(cfg):
+    import torch
+    return torch.bfloat16 if cfg.dtype == 1 else torch.float32
+
+
+def params_to_device(cfg, blob, device="cuda"):
+    """Upload a packed blob (float32 array, or uint16 bf16 bits) as a device tensor of the config dtype."""
+    import numpy as np
+    import torch
+    if cfg.dtype == 1:
+        t = torch.from_numpy(np.ascontiguousarray(blob).view(np.int16)).to(device)
+        return t.view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(blob, dtype=np.float32)).to(device)
+
+
+class Forward:
+    """Holds the output and workspace tensors for repeated gpt_forward calls on one shape."""
+
+    def __init__(self, cfg, B: int, T: int, want_logits: bool = True, device="cuda"):
+        import torch
+        self.cfg, self.B, self.T = cfg, B, T
+        self.ws = torch.empty(workspace_bytes(cfg, B, T), dtype=torch.uint8, device=device)
+        self.logits = torch.empty((B, T, cfg.vocab), dtype=torch_dtype(cfg), device=device) if want_logits else None
+        self.token_loss = torch.empty((B, T), dtype=torch.float32, device=device)
+        self.mean_loss = torch.empty((1,), dtype=torch.float32, device=device)
+
+    def __call__(self, params, idx, targets=None, stream=None):
+        forward(self.cfg, params, idx, targets, self.logits, self.token_loss, self.mean_loss, self.ws, stream)
+        return self.logits, self.token_loss, self.mean_loss
+
+
+def debug_layernorm(cfg, x, g, b, out, stream=None) -> None:
+    check(load().gpt_debug_layernorm(ctypes.byref(cfg_c(cfg)), _ptr(x), _ptr(g), _ptr(b), x.shape[0], _ptr(out),
+                                     _stream(stream)))
+
+
+def debug_linear(cfg, A, W, bias, out, act=0, out_f32=False, stream=None) -> None:
+    M, K = A.shape
+    N = W.shape[0]
+    check(load().gpt_debug_linear(ctypes.byref(cfg_c(cfg)), _ptr(A), _ptr(W), _ptr(bias), M, N, K, act,
+                                  1 if out_f32 else 0, _ptr(out), _stream(stream)))
+
+
+def debug_attention(cfg, q, k, ut, out, stream=None) -> None:
+    B, H, T, D = q.shape
+    ldt = ut.shape[-1]
+    check(load().gpt_debug_attention(ctypes.byref(cfg_c(cfg)), _ptr(q), _ptr(k), _ptr(ut), ldt, B, T, _ptr(out),
+                                     _stream(stream)))

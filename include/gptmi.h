@@ -1,0 +1,146 @@
+/* gptmi.h -- C ABI of the MI355X (gfx950) GPT-2-style decoder-only forward pass.
+ *
+ * The model (pages cited by title and section):
+ *   x = E[idx] + P[t]                                   "第 25 章 从小 GPT 到 GPT-2" §25.1
+ *   per block (pre-norm):                               §25.1; "预训练一个 Mini GPT" 第4步
+ *     a = LN1(x);  qkv = a W_attn^T + b_attn            §25.2 (fused c_attn, split Q|K|U)
+ *     per head: Y = softmax(Q K^T / sqrt(D) + M) U       §25.2 (M = -inf where s > t)
+ *     x += concat_h(Y) W_proj^T + b_proj                 §25.2 (c_proj)
+ *     x += gelu_tanh(LN2(x) W_fc^T + b_fc) W_fp^T + b_fp §25.3; "GPT-1学习笔记" §3.6
+ *   logits = LN_f(x) E^T   (tied head, same E)          §25.4
+ *   loss   = mean over predicted positions of logsumexp(z) - z[y]
+ *                                                       "预训练一个 Mini GPT" 第6步; §25.7
+ *   LayerNorm: biased variance, eps inside the square root ("GPT-1学习笔记" §3.2).
+ *
+ * Conventions for every entry point:
+ *  - Buffers marked (device) are device pointers owned by the caller; (host)
+ *    are host pointers.  The library never allocates, never frees, keeps no
+ *    state between calls, never synchronises and enqueues work only on
+ *    `stream` (a hipStream_t; NULL = the default stream).
+ *  - Every host-checkable condition is checked before the first HIP call; on
+ *    an error nothing is enqueued and the outputs are untouched.  A HIP
+ *    launch failure returns GPT_ERR_HIP; outputs are then undefined.
+ *  - Matrices are row-major [out, in]; a linear layer is y = x W^T + b.
+ *  - dtype GPT_F32: parameters, activations and outputs fp32, MFMA in fp32.
+ *    dtype GPT_BF16: parameters, activations and logits bf16 (round to
+ *    nearest even), fp32 accumulation, fp32 residual stream, fp32 losses.
+ *  - Token ids outside [0, V) violate the contract: the kernels clamp them
+ *    to stay in bounds, and the results are then unspecified.
+ */
+#ifndef GPTMI_H
+#define GPTMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gpt_dtype { GPT_F32 = 0, GPT_BF16 = 1 };
+
+enum gpt_status {
+  GPT_OK = 0,
+  GPT_ERR_NULL = -1,          /* a required pointer is NULL */
+  GPT_ERR_CONFIG = -2,        /* dims <= 0, C % H != 0, C % 8 != 0, n_ff % 8 != 0, D % 8 != 0 or D > 128 */
+  GPT_ERR_SEQ_TOO_LONG = -3,  /* T > ctx ("Day 16 从零组装 MiniGPT" 三十九: longer inputs are rejected) */
+  GPT_ERR_SHAPE = -4,         /* B <= 0, T <= 0, or a shape argument out of range */
+  GPT_ERR_WORKSPACE = -5,     /* ws_bytes smaller than gpt_workspace_bytes() */
+  GPT_ERR_DTYPE = -6,         /* dtype not GPT_F32 / GPT_BF16 */
+  GPT_ERR_HIP = -7            /* a kernel launch failed */
+};
+
+/* Model configuration (host).  n_ff is the MLP width (4 * n_embd for GPT-2,
+ * "第 25 章 从小 GPT 到 GPT-2" §25.3).  ln_eps is 1e-5 for every model here. */
+typedef struct gpt_config {
+  int32_t vocab;    /* V */
+  int32_t ctx;      /* maximum sequence length (rows of the position table) */
+  int32_t n_embd;   /* C */
+  int32_t n_head;   /* H; head width D = C / H */
+  int32_t n_layer;  /* L */
+  int32_t n_ff;     /* MLP hidden width */
+  float ln_eps;
+  int32_t dtype;    /* enum gpt_dtype */
+} gpt_config;
+
+/* Number of unique parameters, closed form ("第 25 章 从小 GPT 到 GPT-2" §25.4):
+ * L(4C^2+4C + 2C*F+F+C + 4C) + VC + ctx*C + 2C, which is L(12C^2+13C)+VC+ctx*C+2C
+ * at F = 4C.  Also the element count of the parameter blob.  Returns a
+ * negative gpt_status on an invalid config (host only, no HIP call). */
+int64_t gpt_param_count(const gpt_config* cfg);
+
+/* Element offsets of every tensor in the parameter blob, in packing order:
+ *   wte[V,C], wpe[ctx,C],
+ *   per layer l: ln1_g[C], ln1_b[C], attn_w[3C,C], attn_b[3C], proj_w[C,C], proj_b[C],
+ *                ln2_g[C], ln2_b[C], fc_w[F,C], fc_b[F], fcproj_w[C,F], fcproj_b[C],
+ *   lnf_g[C], lnf_b[C], end.
+ * There is no head tensor: the head reads wte (tying as one shared tensor, §25.4).
+ * off (host) receives n = 2 + 12 L + 3 values.  Returns GPT_OK, or
+ * GPT_ERR_SHAPE if n is too small (host only). */
+int gpt_param_offsets(const gpt_config* cfg, int64_t* off, int n);
+
+/* Device workspace bytes needed by gpt_forward for a [B, T] batch (host only). */
+int gpt_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes);
+
+/* Forward pass + next-token cross-entropy.
+ *   params     (device) blob of gpt_param_count() elements in cfg->dtype.
+ *   idx        (device) int32 [B, T] token ids in [0, V).
+ *   targets    (device, nullable) int32 [B, T]; -1 = no target.  NULL means
+ *              derived targets y[b,t] = idx[b,t+1] for t < T-1 and none at the
+ *              last position (§25.7: shift once).
+ *   logits     (device, nullable) [B, T, V] in cfg->dtype; NULL skips writing
+ *              them (the loss is still computed, from fp32 accumulators).
+ *   token_loss (device, nullable) fp32 [B, T]; 0 where there is no target.
+ *   mean_loss  (device, nullable) fp32 [1]; mean over positions with a
+ *              target (NaN if there are none).
+ *   ws         (device) workspace of at least gpt_workspace_bytes(cfg,B,T).
+ * Requires 1 <= T <= ctx. */
+int gpt_forward(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                const int32_t* targets, void* logits, float* token_loss, float* mean_loss,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel classes for gpt_forward_timed. */
+enum gpt_kernel {
+  GPT_KERNEL_HEAD = 0,   /* tied head GEMM + cross-entropy partials (one launch per forward) */
+  GPT_KERNEL_QKV = 1,    /* c_attn GEMM + Q/K/U scatter (last layer's launch) */
+  GPT_KERNEL_ATTN = 2,   /* flash attention (last layer's launch) */
+  GPT_KERNEL_PROJ = 3,   /* c_proj GEMM + residual (last layer's launch) */
+  GPT_KERNEL_FC = 4,     /* c_fc GEMM + GELU (last layer's launch) */
+  GPT_KERNEL_FCPROJ = 5, /* mlp.c_proj GEMM + residual (last layer's launch) */
+  GPT_KERNEL_LN = 6      /* ln_2 LayerNorm (last layer's launch) */
+};
+
+/* gpt_forward with a timing hook: ev_begin and ev_end (hipEvent_t, created by
+ * the caller, nullable) are recorded on `stream` immediately before and after
+ * the launch of kernel class `which`.  Everything else is gpt_forward. */
+int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                      const int32_t* targets, void* logits, float* token_loss, float* mean_loss,
+                      void* ws, size_t ws_bytes, void* stream, void* ev_begin, void* ev_end, int which);
+
+/* Human-readable text for a status code (static storage). */
+const char* gpt_status_string(int status);
+
+/* ---- single-operation entry points (same conventions), used to check each
+ * kernel on its own against the oracle ---- */
+
+/* out[M,C] = LN(x[M,C]; g, b, eps) in cfg->dtype; x fp32 (device). */
+int gpt_debug_layernorm(const gpt_config* cfg, const float* x, const void* g, const void* b, int M,
+                        void* out, void* stream);
+
+/* out[M,N] = act(A[M,K] W[N,K]^T + bias[N]); A, W, bias in cfg->dtype (bias
+ * nullable); act 0 = none, 1 = tanh GELU; out fp32 if out_f32 else cfg->dtype.
+ * Requires K % 8 == 0. */
+int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const void* bias, int M, int N,
+                     int K, int act, int out_f32, void* out, void* stream);
+
+/* Causal attention of every (b, h): q, k [B,H,T,D], ut = U^T [B,H,D,ldt]
+ * (ldt >= T, ldt % 8 == 0), all cfg->dtype; out [B*T, C] in cfg->dtype with
+ * head h in columns [hD, hD+D). */
+int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* ut, int ldt,
+                        int B, int T, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTMI_H */
