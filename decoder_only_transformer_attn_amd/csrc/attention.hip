@@ -11,8 +11,9 @@
 // that each lane owns one query column: the row statistics need a single
 // cross-lane exchange (lanes l and l^32), and the probabilities P^T sit in
 // registers already in the B-operand layout of the second product
-// O^T = U^T P^T.  U is kept transposed (U^T [D, T]) by the QKV projection so
-// the A operand of that product is a contiguous LDS read.  Scores are scaled
+// O^T = U^T P^T.  U is stored [B,H,T,D] like K and written transposed,
+// U^T [D, keys], when its tile is staged into LDS, so the A operand of that
+// product is a contiguous LDS read.  Scores are scaled
 // by log2(e)/sqrt(D) and exponentiated with exp2.  Key tiles entirely above
 // the diagonal are skipped; only diagonal tiles evaluate the mask.
 #include "common.h"
@@ -76,7 +77,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 
   const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * a.q_bh;
   const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * a.k_bh;
-  const T* Vt = reinterpret_cast<const T*>(a.vt) + (long long)bh * a.v_bh;
+  const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.v_bh;
 
   // Q^T fragments (B operand) for this lane's query column.
   typename MF::frag qf[NDI];
@@ -101,25 +102,30 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
       const int row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
       const int key = kb + row;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < T_seq && dc < D) v = *reinterpret_cast<const uint4*>(K + (long long)key * a.k_ld + dc);
+      if (key < T_seq && dc < D) v = *reinterpret_cast<const uint4*>(K + (long long)key * D + dc);
       *reinterpret_cast<uint4*>(sK + row * LDKS + dc) = v;
     }
-    for (int ch = tid; ch < DP * (BKV / VEC); ch += 256) {
-      const int d = ch / (BKV / VEC), kc = (ch % (BKV / VEC)) * VEC;
-      const int key = kb + kc;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (d < D && key < T_seq) {
-        v = *reinterpret_cast<const uint4*>(Vt + (long long)d * a.v_ld + key);
-        if (key + VEC > T_seq) {  // ragged end: zero the keys past the sequence
-          T tmp[VEC];
-          *reinterpret_cast<uint4*>(tmp) = v;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if (key + e >= T_seq) tmp[e] = T(0);
-          v = *reinterpret_cast<uint4*>(tmp);
-        }
+    // U: each item is two consecutive keys x VEC head columns, written
+    // transposed as VEC pairs (key, key + 1) of row d of U^T
+    for (int ch = tid; ch < (BKV / 2) * (DP / VEC); ch += 256) {
+      const int kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
+      const int key = kb + kp;
+      T u0[VEC], u1[VEC];
+      *reinterpret_cast<uint4*>(u0) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(u1) = make_uint4(0, 0, 0, 0);
+      if (dc < D) {
+        if (key < T_seq) *reinterpret_cast<uint4*>(u0) = *reinterpret_cast<const uint4*>(U + (long long)key * D + dc);
+        if (key + 1 < T_seq)
+          *reinterpret_cast<uint4*>(u1) = *reinterpret_cast<const uint4*>(U + (long long)(key + 1) * D + dc);
       }
-      *reinterpret_cast<uint4*>(sV + d * LDVS + kc) = v;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        T* dst = sV + (dc + e) * LDVS + kp;   // kp and LDVS even: pair-aligned
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint32_t*>(dst) = uint32_t(u0[e]) | (uint32_t(u1[e]) << 16);
+        else
+          *reinterpret_cast<float2*>(dst) = make_float2(u0[e], u1[e]);
+      }
     }
     __syncthreads();
 

@@ -12,7 +12,7 @@
 
 namespace gptmi {
 
-constexpr int CE_ROWS = 64;  // rows per block
+constexpr int CE_ROWS = 16;  // rows per block (4 per wave)
 
 __device__ __forceinline__ int target_of(const int32_t* targets, const int32_t* idx, int m, int T_seq) {
   if (targets) return targets[m];

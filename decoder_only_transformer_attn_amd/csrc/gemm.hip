@@ -9,7 +9,7 @@
 // barrier per K step, global loads for step k+1 in flight while step k is
 // multiplied).  Each wave owns a WM x WN sub-tile made of 32x32 MFMA tiles.
 // Epilogues run on the fp32 accumulators:
-//   EpiQKV   : + bias, scatter Q -> [B,H,T,D], K -> [B,H,Tk,D], V -> V^T [B,H,D,Tk]
+//   EpiQKV   : + bias, scatter Q -> [B,H,T,D], K and U -> [B,H,Tk,D]
 //   EpiResid : + bias, x += (fp32 residual stream)
 //   EpiAct   : + bias, optional tanh-GELU, store in the output dtype
 //   head     : optional logits store + per-(row, N-tile) softmax partials
@@ -34,8 +34,19 @@ struct GemmCfg {
   static_assert(BK % Mfma<T>::KPI == 0, "BK must hold whole MFMA k steps");
 };
 
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return zero,
+// which handles the M and N tails of a tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Main loop: acc[i][j] += A[m0 + wm*WM + 32i .., :] . W[n0 + wn*WN + 32j .., :]^T
-template <typename T, int BM, int BN, int BK, int WM, int WN>
+// Rows past M (N) read as zero; KTAIL zeroes the chunks past K when K % BK != 0.
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL>
 __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw,
                                               int M, int N, int K, int m0, int n0, T* smem,
                                               f32x16 (&acc)[WM / 32][WN / 32]) {
@@ -54,19 +65,37 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, int lda, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Resources cover exactly the rows of this tile that exist.
+  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(A + (size_t)m0 * lda, (uint32_t)((size_t)mrows * lda * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(W + (size_t)n0 * ldw, (uint32_t)((size_t)nrows * ldw * sizeof(T)));
+  uint32_t a_off[G::A_PT], b_off[G::B_PT];
+  int a_kc[G::A_PT], b_kc[G::B_PT];
+#pragma unroll
+  for (int c = 0; c < G::A_PT; ++c) {
+    const int ch = tid + c * G::NT, row = ch / G::CPR;
+    a_kc[c] = (ch % G::CPR) * G::VEC;
+    a_off[c] = (uint32_t)((row * lda + a_kc[c]) * sizeof(T));
+  }
+#pragma unroll
+  for (int c = 0; c < G::B_PT; ++c) {
+    const int ch = tid + c * G::NT, row = ch / G::CPR;
+    b_kc[c] = (ch % G::CPR) * G::VEC;
+    b_off[c] = (uint32_t)((row * ldw + b_kc[c]) * sizeof(T));
+  }
+
   uint4 ra[G::A_PT], rb[G::B_PT];
   auto gload = [&](int k0) {
+    const uint32_t so = (uint32_t)(k0 * sizeof(T));
 #pragma unroll
     for (int c = 0; c < G::A_PT; ++c) {
-      const int ch = tid + c * G::NT, row = ch / G::CPR, kc = (ch % G::CPR) * G::VEC;
-      const int gm = m0 + row, gk = k0 + kc;
-      ra[c] = (gm < M && gk < K) ? *reinterpret_cast<const uint4*>(A + (size_t)gm * lda + gk) : make_uint4(0, 0, 0, 0);
+      ra[c] = buf_load16(ra_src, a_off[c], so);
+      if (KTAIL && k0 + a_kc[c] >= K) ra[c] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < G::B_PT; ++c) {
-      const int ch = tid + c * G::NT, row = ch / G::CPR, kc = (ch % G::CPR) * G::VEC;
-      const int gn = n0 + row, gk = k0 + kc;
-      rb[c] = (gn < N && gk < K) ? *reinterpret_cast<const uint4*>(W + (size_t)gn * ldw + gk) : make_uint4(0, 0, 0, 0);
+      rb[c] = buf_load16(rb_src, b_off[c], so);
+      if (KTAIL && k0 + b_kc[c] >= K) rb[c] = make_uint4(0, 0, 0, 0);
     }
   };
   auto sstore = [&](int buf) {
@@ -109,104 +138,330 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, int lda, 
   }
 }
 
-// Block id -> (m tile, n tile), grouped so that GM consecutive blocks share an
-// N tile column band and walk M, keeping W tiles hot in L2.
-__device__ __forceinline__ void tile_of(int pid, int num_m, int num_n, int& mt, int& nt) {
-  constexpr int GM = 8;
+// Block id -> (m tile, n tile).  The hardware hands consecutive workgroups to
+// the 8 XCDs in turn, and each XCD has its own L2; so the block id is first
+// remapped to give every XCD one contiguous range of a grouped tile order, in
+// which GM m-tiles sweep the n-tiles together (operand tiles of blocks that
+// run at the same time on one XCD overlap and stay in that XCD's L2).
+__device__ __forceinline__ void tile_of(int pid, int nblocks, int num_m, int num_n, int& mt, int& nt) {
+  constexpr int NXCD = 8, GM = 8;
+  const int xcd = pid % NXCD, local = pid / NXCD;
+  const int per = nblocks / NXCD, rem = nblocks % NXCD;
+  const int logical = xcd * per + min(xcd, rem) + local;
   const int group = GM * num_n;
-  const int gid = pid / group;
+  const int gid = logical / group;
   const int first_m = gid * GM;
   const int gsz = min(num_m - first_m, GM);
-  const int in = pid - gid * group;
+  const int in = logical - gid * group;
   mt = first_m + in % gsz;
   nt = in / gsz;
 }
 
 // ---------------------------------------------------------------------------
-// Element-wise epilogues
+// Pipelined bf16 main loop with direct-to-LDS loads.
+//
+// Tiles of 256 x 256 with K steps of 32 flow through a ring of four LDS
+// stages: gfx950's buffer_load ... lds writes each 16-byte chunk straight
+// into LDS (no VGPR staging, no ds_write), three K steps are in flight while
+// the fourth is multiplied, and one barrier per K step hands a stage from the
+// loads to the MFMAs.  Each wave waits for its own loads of step t
+// (s_waitcnt vmcnt) before the barrier, so after it every wave's loads of
+// step t are in LDS.  The four stages are distinct LDS objects so the
+// compiler can tell a read of one stage from the loads into another.  Rows
+// are 64 bytes (4 chunks); chunk c of row r is stored at slot c ^ ((r>>1)&3),
+// which makes the MFMA fragment reads (ds_read_b128, 32 rows x one chunk per
+// half-wave) bank-conflict free.  K is a template parameter and the K loop is
+// unrolled completely.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier that keeps the compiler from moving memory accesses across
+// it but, unlike __syncthreads, does not wait for outstanding loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+// One 1 KB direct-to-LDS load: lane l's 16 bytes land at lds + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN>
+struct DmaCfg {
+  static constexpr int BK = 32, NST = 4, ROWB = 64;
+  static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * WAVE;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int STAGE = (BM + BN) * ROWB;        // bytes per stage
+  static constexpr int NI = (BM + BN) / 16;             // 1 KB load instructions per stage
+  static constexpr int DPW = NI / NW;                   // per wave
+  static_assert(NI % NW == 0 && BM % 16 == 0 && BN % 16 == 0, "loads must split evenly over the waves");
+};
+
+template <int BM, int BN, int WM, int WN, int K>
+__device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N,
+                                             int m0, int n0, char* s0, char* s1, char* s2, char* s3,
+                                             f32x16 (&acc)[WM / 32][WN / 32]) {
+  typedef DmaCfg<BM, BN, WM, WN> D;
+  constexpr int NK = K / D::BK;
+  static_assert(K % D::BK == 0, "K must be a multiple of 32");
+  char* const st[4] = {s0, s1, s2, s3};
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / D::NWN, wn = wave % D::NWN;
+#pragma unroll
+  for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < D::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Stage layout: A rows [0, BM) then W rows, 64 bytes each.  Load
+  // instruction i (16 rows) goes to LDS offset 1024 i and is issued by wave
+  // i % NW; the wave index is uniform, so the A/W choice stays scalar.
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)min(BM, M - m0) * K * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)min(BN, N - n0) * K * sizeof(bf16)));
+  uint32_t voff[D::DPW];
+#pragma unroll
+  for (int d = 0; d < D::DPW; ++d) {
+    const int ins = wave + d * D::NW;
+    const int row = (ins < BM / 16 ? ins : ins - BM / 16) * 16 + (lane >> 2), slot = lane & 3;
+    voff[d] = (uint32_t)((row * K + swz4(row, slot) * 8) * sizeof(bf16));
+  }
+  auto issue = [&](int t) {
+    char* s = st[t % D::NST];
+#pragma unroll
+    for (int d = 0; d < D::DPW; ++d) {
+      const int ins = wave + d * D::NW;
+      dma16(ins < BM / 16 ? rsA : rsB, s + ins * 1024, voff[d], t * D::BK * 2);
+    }
+  };
+  const int lrow = lane & 31, g = lane >> 5;
+  auto ldfrag = [&](const char* s, int ks, bf16x8 (&af)[D::TM], bf16x8 (&bfr)[D::TN]) {
+    const int c = ks * 2 + g;
+#pragma unroll
+    for (int i = 0; i < D::TM; ++i) {
+      const int r = wm * WM + i * 32 + lrow;
+      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(s + r * D::ROWB + swz4(r, c) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < D::TN; ++j) {
+      const int r = wn * WN + j * 32 + lrow;
+      bfr[j] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4*>(s + BM * D::ROWB + r * D::ROWB + swz4(r, c) * 16));
+    }
+  };
+  auto mm = [&](const bf16x8 (&af)[D::TM], const bf16x8 (&bfr)[D::TN]) {
+#pragma unroll
+    for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < D::TN; ++j) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
+  };
+  issue(0);
+  if (NK > 1) issue(1);
+  if (NK > 2) issue(2);
+#pragma unroll
+  for (int t = 0; t < NK; ++t) {
+    if (t + 2 < NK) wait_vmcnt<2 * D::DPW>();
+    else if (t + 1 < NK) wait_vmcnt<D::DPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 3 < NK) issue(t + 3);
+    const char* s = st[t % D::NST];
+    bf16x8 a0[D::TM], b0[D::TN], a1[D::TM], b1[D::TN];
+    ldfrag(s, 0, a0, b0);
+    ldfrag(s, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mm(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mm(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // every wave is done with the stages: the epilogue may reuse LDS
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues.  Each is called for two adjacent output columns (n, n+1) of
+// one row; has_b is false only for the last column of an odd N.  Epilogues
+// with kPreload read their extra input (the residual stream) before the main
+// loop, so that its latency hides under the MFMA work.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float gelu_tanh(float v) {
+  // 0.5 z (1 + tanh(u)), u = sqrt(2/pi)(z + 0.044715 z^3), evaluated as z * sigmoid(2u)
+  const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+  return v / (1.0f + __expf(-2.0f * u));
+}
+
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, float a, float b, bool has_b, bool vec_ok) {
+  if (has_b && vec_ok) {
+    if constexpr (sizeof(T) == 4) *reinterpret_cast<float2*>(p) = make_float2(a, b);
+    else *reinterpret_cast<uint32_t*>(p) = uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  } else {
+    p[0] = from_f32<T>(a);
+    if (has_b) p[1] = from_f32<T>(b);
+  }
+}
+
 template <typename T>
 struct EpiAct {  // out[m, n] = act(v + bias[n])
+  static constexpr bool kPreload = false;
   const T* bias;
   void* out;
   int ldo;
   int act;       // 0 none, 1 tanh-GELU
   int out_f32;   // store fp32 instead of T
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
-    if (bias) v += to_f32(bias[n]);
-    if (act == 1) {
-      // GELU tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi)(z + 0.044715 z^3),
-      // evaluated as z * sigmoid(2u) (the same function).
-      const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-      v = v / (1.0f + __expf(-2.0f * u));
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ void pair(int m, int n, float a, float b, bool has_b, float2) const {
+    if (bias) {
+      a += to_f32(bias[n]);
+      if (has_b) b += to_f32(bias[n + 1]);
     }
-    if (out_f32) reinterpret_cast<float*>(out)[(size_t)m * ldo + n] = v;
-    else reinterpret_cast<T*>(out)[(size_t)m * ldo + n] = from_f32<T>(v);
+    if (act == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
+    const size_t o = (size_t)m * ldo + n;
+    if (out_f32) store_pair(reinterpret_cast<float*>(out) + o, a, b, has_b, (ldo & 1) == 0);
+    else store_pair(reinterpret_cast<T*>(out) + o, a, b, has_b, (ldo & 1) == 0);
   }
 };
 
 template <typename T>
 struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
+  static constexpr bool kPreload = true;
   const T* bias;
   float* x;
   int ldx;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
-    float* p = x + (size_t)m * ldx + n;
-    *p = *p + (v + to_f32(bias[n]));
+  __device__ __forceinline__ float2 preload(int m, int n, bool has_b) const {
+    const float* p = x + (size_t)m * ldx + n;
+    if (has_b && (ldx & 1) == 0) return *reinterpret_cast<const float2*>(p);
+    return make_float2(p[0], has_b ? p[1] : 0.f);
+  }
+  __device__ __forceinline__ void pair(int m, int n, float a, float b, bool has_b, float2 xo) const {
+    a = xo.x + (a + to_f32(bias[n]));
+    if (has_b) b = xo.y + (b + to_f32(bias[n + 1]));
+    store_pair(x + (size_t)m * ldx + n, a, b, has_b, (ldx & 1) == 0);
   }
 };
 
 template <typename T>
-struct EpiQKV {  // + bias, split Q|K|V, heads as column blocks of width D
+struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all three [B,H,T,D]
+  static constexpr bool kPreload = false;
   const T* bias;
   int C, H, D, T_seq;
-  T* q;  long long q_bh;            // q[(b*H+h)*q_bh + t*D + d]
-  T* k;  long long k_bh;            // k[(b*H+h)*k_bh + tc*D + d]
-  T* vt; long long v_bh; int v_ld;  // vt[(b*H+h)*v_bh + d*v_ld + tc]
+  T* q; long long q_bh;             // q[(b*H+h)*q_bh + t*D + d]
+  T* k; long long k_bh;             // k[(b*H+h)*k_bh + tc*D + d]
+  T* v; long long v_bh;             // v[(b*H+h)*v_bh + tc*D + d]
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
-    v += to_f32(bias[n]);
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ void pair(int m, int n, float a, float b, bool, float2) const {
+    // D is even, so n and n + 1 fall in the same head of the same projection
+    a += to_f32(bias[n]);
+    b += to_f32(bias[n + 1]);
     const int which = n / C;
     const int c = n - which * C;
     const int h = c / D, d = c - h * D;
-    const int b = m / T_seq, t = m - b * T_seq;
-    const long long bh = (long long)b * H + h;
-    const T val = from_f32<T>(v);
-    if (which == 0) {
-      q[bh * q_bh + (long long)t * D + d] = val;
-    } else {
+    const int bb = m / T_seq, t = m - bb * T_seq;
+    const long long bh = (long long)bb * H + h;
+    T* dst;
+    if (which == 0) dst = q + bh * q_bh + (long long)t * D + d;
+    else {
       const int tc = t + (pos ? *pos : 0);
-      if (which == 1) k[bh * k_bh + (long long)tc * D + d] = val;
-      else vt[bh * v_bh + (long long)d * v_ld + tc] = val;
+      dst = (which == 1 ? k + bh * k_bh : v + bh * v_bh) + (long long)tc * D + d;
     }
+    store_pair(dst, a, b, true, true);
   }
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, typename Epi>
+// Output driver.  Lanes 2k and 2k+1 hold columns n and n+1 of a 32x32 tile,
+// and registers r, r+1 (r even) are rows m, m+1.  One exchange gives the even
+// lane (row m; n, n+1) and the odd lane (row m+1; n, n+1), so every lane
+// stores two adjacent outputs.  `pre` holds the preloaded inputs in the same
+// assignment.
+template <int TM, int TN>
+__device__ __forceinline__ void pair_coords(int i, int j, int rp, int mbase, int nbase, int& m, int& n) {
+  const int lane = threadIdx.x & 63;
+  m = mbase + i * 32 + acc_row(2 * rp, lane) + (lane & 1);
+  n = nbase + j * 32 + ((lane & 31) & ~1);
+}
+
+template <int TM, int TN, typename Epi>
+__device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], int mbase, int nbase, int M, int N,
+                                              const Epi& epi) {
+  if constexpr (Epi::kPreload) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rp = 0; rp < 8; ++rp) {
+          int m, n;
+          pair_coords<TM, TN>(i, j, rp, mbase, nbase, m, n);
+          pre[i][j][rp] = (m < M && n < N) ? epi.preload(m, n, n + 1 < N) : make_float2(0.f, 0.f);
+        }
+  }
+}
+
+template <int TM, int TN, typename Epi>
+__device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], const float2 (&pre)[TM][TN][8], int mbase,
+                                               int nbase, int M, int N, const Epi& epi) {
+  const bool odd = threadIdx.x & 1;
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int rp = 0; rp < 8; ++rp) {
+        const float v0 = acc[i][j][2 * rp], v1 = acc[i][j][2 * rp + 1];
+        const float recv = __shfl_xor(odd ? v0 : v1, 1, 64);
+        int m, n;
+        pair_coords<TM, TN>(i, j, rp, mbase, nbase, m, n);
+        const float a = odd ? recv : v0, b = odd ? v1 : recv;
+        if (m < M && n < N) epi.pair(m, n, a, b, n + 1 < N, pre[i][j][rp]);
+      }
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL, typename Epi>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, int M, int N, int K, Epi epi) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   __shared__ __align__(16) T smem[G::SMEM_ELEMS];
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
   int mt, nt;
-  tile_of(blockIdx.x, num_m, num_n, mt, nt);
+  tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
+  float2 pre[G::TM][G::TN][8];
+  preload_pairs<G::TM, G::TN>(pre, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
-  gemm_mainloop<T, BM, BN, BK, WM, WN>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / G::NWN, wn = wave % G::NWN;
-#pragma unroll
-  for (int j = 0; j < G::TN; ++j) {
-    const int n = n0 + wn * WN + j * 32 + (lane & 31);
-    if (n >= N) continue;
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * WM + i * 32 + acc_row(r, lane);
-        if (m < M) epi(m, n, acc[i][j][r]);
-      }
-  }
+  gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
+  epilogue_pairs<G::TM, G::TN>(acc, pre, mb, nb, M, N, epi);
+}
+
+// bf16 GEMM through the pipelined main loop, element-wise epilogue.
+template <int BM, int BN, int WM, int WN, int K, typename Epi>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64) gemm_dma_kernel(const bf16* __restrict__ A,
+                                                                             const bf16* __restrict__ W, int M, int N,
+                                                                             Epi epi) {
+  typedef DmaCfg<BM, BN, WM, WN> D;
+  __shared__ __align__(1024) char s0[D::STAGE];
+  __shared__ __align__(1024) char s1[D::STAGE];
+  __shared__ __align__(1024) char s2[D::STAGE];
+  __shared__ __align__(1024) char s3[D::STAGE];
+  const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
+  int mt, nt;
+  tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int mb = m0 + (wave / D::NWN) * WM, nb = n0 + (wave % D::NWN) * WN;
+  float2 pre[D::TM][D::TN][8];
+  preload_pairs<D::TM, D::TN>(pre, mb, nb, M, N, epi);
+  f32x16 acc[D::TM][D::TN];
+  dma_mainloop<BM, BN, WM, WN, K>(A, W, M, N, m0, n0, s0, s1, s2, s3, acc);
+  epilogue_pairs<D::TM, D::TN>(acc, pre, mb, nb, M, N, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -230,7 +485,147 @@ struct HeadArgs {
   int T_seq;
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN>
+__device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
+  if (ha.targets) return ha.targets[m];
+  return ((m % ha.T_seq) < ha.T_seq - 1) ? ha.idx[m + 1] : -1;
+}
+
+// bf16 tied head computed transposed, Z^T = E . A^T: the MFMA rows are vocab
+// entries and the columns are tokens, so every lane owns whole tokens.  The
+// softmax partials of a token over this block's 256 vocab entries are then a
+// reduction over the lane's own registers, one exchange with the lane holding
+// the other half of the rows (l ^ 32), and a 4-way combine over the waves
+// along the vocab axis.  Logits are staged through LDS, 32 tokens at a time,
+// shifted so that every 16-byte window of a global logits row is one aligned
+// LDS read and one aligned 16-byte store (V is odd, so rows are only 2-byte
+// aligned); the partial windows at the ends of a row are written per element.
+template <int K>
+__global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act,
+                                                          int V, int Mtok, HeadArgs ha) {
+  constexpr int BM = 256, BN = 256, WM = 64, WN = 128;   // BM: vocab, BN: tokens
+  typedef DmaCfg<BM, BN, WM, WN> D;
+  constexpr int ROWE = BM + 8, ROWBYTES = ROWE * 2;       // staged logits row (elements / bytes)
+  static_assert(32 * ROWBYTES <= D::STAGE, "staging buffer");
+  __shared__ __align__(1024) char s0[D::STAGE];
+  __shared__ __align__(1024) char s1[D::STAGE];
+  __shared__ __align__(1024) char s2[D::STAGE];
+  __shared__ __align__(1024) char s3[D::STAGE];
+  __shared__ float red[D::NWM][BN][2];
+  const int num_v = (V + BM - 1) / BM, num_t = (Mtok + BN - 1) / BN;
+  int tt, vt;
+  tile_of(blockIdx.x, gridDim.x, num_t, num_v, tt, vt);   // groups of token tiles sweep the vocab
+  const int v0 = vt * BM, t0 = tt * BN;
+  f32x16 acc[D::TM][D::TN];
+  dma_mainloop<BM, BN, WM, WN, K>(wte, act, V, Mtok, v0, t0, s0, s1, s2, s3, acc);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / D::NWN, wn = wave % D::NWN;
+  const int vw0 = v0 + wm * WM;   // first vocab row of this wave
+
+  // softmax partials and target logit, per token
+#pragma unroll
+  for (int j = 0; j < D::TN; ++j) {
+    const int tl = wn * WN + j * 32 + (lane & 31);
+    const int m = t0 + tl;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (vw0 + i * 32 + acc_row(r, lane) < V) mx = fmaxf(mx, acc[i][j][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sum = 0.f;
+    if (mx > -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vw0 + i * 32 + acc_row(r, lane) < V) sum += __expf(acc[i][j][r] - mx);
+    }
+    sum += __shfl_xor(sum, 32, 64);
+    if (g == 0) { red[wm][tl][0] = mx; red[wm][tl][1] = sum; }
+    if (m < Mtok) {
+      const int y = head_target(ha, m);
+      if (y >= vw0 && y < vw0 + WM) {
+#pragma unroll
+        for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vw0 + i * 32 + acc_row(r, lane) == y) ha.tgt[m] = acc[i][j][r];
+      }
+    }
+  }
+  __syncthreads();
+  for (int tl = tid; tl < BN; tl += D::NT) {
+    const int m = t0 + tl;
+    if (m >= Mtok) continue;
+    float M_ = red[0][tl][0];
+#pragma unroll
+    for (int w = 1; w < D::NWM; ++w) M_ = fmaxf(M_, red[w][tl][0]);
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < D::NWM; ++w) {
+      const float mw = red[w][tl][0];
+      if (mw > -INFINITY) S += red[w][tl][1] * __expf(mw - M_);
+    }
+    ha.part_max[(long long)m * ha.ntiles + vt] = M_;
+    ha.part_sum[(long long)m * ha.ntiles + vt] = S;
+  }
+  if (!ha.logits) return;
+
+  // logits: 8 rounds of 32 tokens, staging buffers alternate between s0 and s1
+  bf16* const L = reinterpret_cast<bf16*>(ha.logits);
+  const int elem_mis = (int)((reinterpret_cast<uintptr_t>(ha.logits) >> 1) & 7);
+  const int nv = min(BM, V - v0);
+#pragma unroll 1
+  for (int q = 0; q < BN / 32; ++q) {
+    char* buf = (q & 1) ? s1 : s0;
+    // writers: the 4 waves with wn == q / 4 hold these tokens in register block j = q % 4
+    if (wn == q / 4) {
+      const int jq = q % 4;
+      const int tok = lane & 31;                          // token within the round
+      const int m = t0 + q * 32 + tok;
+      const int sh = (int)(((long long)m * ha.ld_logits + v0 + elem_mis) & 7);
+      bf16* row = reinterpret_cast<bf16*>(buf + tok * ROWBYTES);
+#pragma unroll
+      for (int jj = 0; jj < D::TN; ++jj) {
+        if (jj != jq) continue;
+#pragma unroll
+        for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int vl = wm * WM + i * 32 + acc_row(r, lane);
+            row[vl + sh] = f32_to_bf16(acc[i][jj][r]);
+          }
+      }
+    }
+    // LDS writes visible to the block; global stores of earlier rounds stay in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    lds_barrier();
+    const int nwin = (nv + 7 + 8) / 8;   // upper bound of windows per row
+    for (int it = tid; it < 32 * nwin; it += D::NT) {
+      const int tok = it / nwin, k = it - tok * nwin;
+      const int m = t0 + q * 32 + tok;
+      if (m >= Mtok) continue;
+      const long long e0 = (long long)m * ha.ld_logits + v0;
+      const int sh = (int)((e0 + elem_mis) & 7);
+      const int p0 = 8 * k;
+      if (p0 >= sh + nv) continue;
+      const char* row = buf + tok * ROWBYTES;
+      bf16* gp = L + e0 - sh + p0;                        // 16-byte aligned window
+      if (p0 >= sh && p0 + 8 <= sh + nv) {
+        *reinterpret_cast<uint4*>(gp) = *reinterpret_cast<const uint4*>(row + 2 * p0);
+      } else {
+        const bf16* lr = reinterpret_cast<const bf16*>(row);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (p0 + e >= sh && p0 + e < sh + nv) gp[e] = lr[p0 + e];
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, int M, int N, int K, HeadArgs ha) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
@@ -239,10 +634,10 @@ head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ld
   __shared__ float rowmax[BM];
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
   int mt, nt;
-  tile_of(blockIdx.x, num_m, num_n, mt, nt);
+  tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
   f32x16 acc[G::TM][G::TN];
-  gemm_mainloop<T, BM, BN, BK, WM, WN>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
+  gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / G::NWN, wn = wave % G::NWN;
   const int ncol0 = n0 + wn * WN + (lane & 31);
@@ -320,19 +715,43 @@ static hipError_t run_gemm(const T* A, int lda, const T* W, int ldw, int M, int 
                            hipStream_t st) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, Epi>), dim3(blocks), dim3(G::NT), 0, st, A, lda, W, ldw,
-                     M, N, K, epi);
+  if (K % BK == 0)
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, false, Epi>), dim3(blocks), dim3(G::NT), 0, st, A, lda, W,
+                       ldw, M, N, K, epi);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, true, Epi>), dim3(blocks), dim3(G::NT), 0, st, A, lda, W,
+                       ldw, M, N, K, epi);
   return hipGetLastError();
 }
 
-// Tile choice per dtype.  fp32 serves the small correctness configurations.
-template <typename T, typename Epi>
-static hipError_t dispatch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, int K, const Epi& epi,
-                                hipStream_t st);
+// Tile choice.  Large bf16 products use 256x256 tiles (128x128 per wave); the
+// fp32 path serves the small correctness configurations.
+template <int BM, int BN, int WM, int WN, int K, typename Epi>
+static hipError_t run_gemm_dma(const bf16* A, const bf16* W, int M, int N, const Epi& epi, hipStream_t st) {
+  const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, K, Epi>), dim3(blocks), dim3(DmaCfg<BM, BN, WM, WN>::NT), 0, st,
+                     A, W, M, N, epi);
+  return hipGetLastError();
+}
+
+// 128 x 192 tiles (4 waves of 64 x 96) make every block GEMM of the 124M
+// model a whole number of rounds over 256 CUs at M = 8192 (N = 2304: 768
+// tiles, 3072: 1024, 768: 256); 256 x 256 (8 waves of 64 x 128) otherwise.
+template <int K, typename Epi>
+static hipError_t run_gemm_dma_k(const bf16* A, const bf16* W, int M, int N, const Epi& epi, hipStream_t st) {
+  if (N % 192 == 0) return run_gemm_dma<128, 192, 64, 96, K>(A, W, M, N, epi, st);
+  return run_gemm_dma<256, 256, 64, 128, K>(A, W, M, N, epi, st);
+}
 
 template <typename Epi>
 static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
                                 hipStream_t st) {
+  const long long tiles256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles256 >= 64 && lda == K && ldw == K) {
+    if (K == 768) return run_gemm_dma_k<768>(A, W, M, N, epi, st);
+    if (K == 3072) return run_gemm_dma_k<3072>(A, W, M, N, epi, st);
+  }
+  if (tiles256 >= 192) return run_gemm<bf16, 256, 256, 64, 128, 64>(A, lda, W, ldw, M, N, K, epi, st);
   if ((long long)M * N >= (long long)256 * 1024 * 16)
     return run_gemm<bf16, 128, 128, 64, 64, 64>(A, lda, W, ldw, M, N, K, epi, st);
   return run_gemm<bf16, 64, 64, 64, 32, 32>(A, lda, W, ldw, M, N, K, epi, st);
@@ -372,8 +791,7 @@ hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W,
 
 template <typename T>
 static hipError_t qkv_t(const QKVArgs& a, hipStream_t st) {
-  EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh,
-              (T*)a.vt, a.v_bh, a.v_ld, a.pos};
+  EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh, (T*)a.v, a.v_bh, a.pos};
   return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, 3 * a.C, a.C, e, st);
 }
 
@@ -382,7 +800,7 @@ hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st) {
   return qkv_t<bf16>(a, st);
 }
 
-int head_tile_n(int dtype) { return dtype == 0 ? 64 : 128; }
+int head_tile_n(int dtype) { return dtype == 0 ? 64 : 256; }
 
 hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int V, int C, void* logits,
                           long long ld_logits, float* part_max, float* part_sum, float* tgt, const int32_t* targets,
@@ -392,16 +810,31 @@ hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int 
     constexpr int BM = 64, BN = 64;
     ha.ntiles = (V + BN - 1) / BN;
     const int blocks = ((M + BM - 1) / BM) * ha.ntiles;
-    hipLaunchKernelGGL((head_ce_kernel<float, BM, BN, 32, 32, 32>), dim3(blocks),
-                       dim3(GemmCfg<float, BM, BN, 32, 32, 32>::NT), 0, st, (const float*)A, C, (const float*)wte, C,
-                       M, V, C, ha);
+    if (C % 32 == 0)
+      hipLaunchKernelGGL((head_ce_kernel<float, BM, BN, 32, 32, 32, false>), dim3(blocks),
+                         dim3(GemmCfg<float, BM, BN, 32, 32, 32>::NT), 0, st, (const float*)A, C, (const float*)wte, C,
+                         M, V, C, ha);
+    else
+      hipLaunchKernelGGL((head_ce_kernel<float, BM, BN, 32, 32, 32, true>), dim3(blocks),
+                         dim3(GemmCfg<float, BM, BN, 32, 32, 32>::NT), 0, st, (const float*)A, C, (const float*)wte, C,
+                         M, V, C, ha);
   } else {
-    constexpr int BM = 128, BN = 128;
+    constexpr int BM = 256, BN = 256;
     ha.ntiles = (V + BN - 1) / BN;
     const int blocks = ((M + BM - 1) / BM) * ha.ntiles;
-    hipLaunchKernelGGL((head_ce_kernel<bf16, BM, BN, 64, 64, 64>), dim3(blocks),
-                       dim3(GemmCfg<bf16, BM, BN, 64, 64, 64>::NT), 0, st, (const bf16*)A, C, (const bf16*)wte, C, M,
-                       V, C, ha);
+    if (C == 768) {
+      hipLaunchKernelGGL((head_ce_dma_kernel<768>), dim3(blocks), dim3(512), 0, st, (const bf16*)wte, (const bf16*)A, V,
+                         M, ha);
+      return hipGetLastError();
+    }
+    if (C % 64 == 0)
+      hipLaunchKernelGGL((head_ce_kernel<bf16, BM, BN, 64, 128, 64, false>), dim3(blocks),
+                         dim3(GemmCfg<bf16, BM, BN, 64, 128, 64>::NT), 0, st, (const bf16*)A, C, (const bf16*)wte, C,
+                         M, V, C, ha);
+    else
+      hipLaunchKernelGGL((head_ce_kernel<bf16, BM, BN, 64, 128, 64, true>), dim3(blocks),
+                         dim3(GemmCfg<bf16, BM, BN, 64, 128, 64>::NT), 0, st, (const bf16*)A, C, (const bf16*)wte, C,
+                         M, V, C, ha);
   }
   return hipGetLastError();
 }

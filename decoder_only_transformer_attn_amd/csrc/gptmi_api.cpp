@@ -71,14 +71,13 @@ int64_t offsets(const gpt_config* c, int64_t* out, int n) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Plan {
-  size_t x, a, q, k, vt, o, h, pmax, psum, tgt, tok, bsum, total;
-  int Tpad, ntiles, nblocks;
+  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, total;
+  int ntiles, nblocks;
 };
 
 Plan plan(const gpt_config* c, int B, int T) {
   Plan p{};
   const size_t M = (size_t)B * T, C = c->n_embd, F = c->n_ff, es = esize(c);
-  p.Tpad = (int)align_up((size_t)T, 64);
   p.ntiles = (c->vocab + head_tile_n(c->dtype) - 1) / head_tile_n(c->dtype);
   p.nblocks = ce_reduce_blocks((int)M);
   size_t off = 0;
@@ -87,7 +86,7 @@ Plan plan(const gpt_config* c, int B, int T) {
   p.a = take(M * C * es);
   p.q = take(M * C * es);
   p.k = take(M * C * es);
-  p.vt = take((size_t)B * c->n_embd * p.Tpad * es);
+  p.v = take(M * C * es);
   p.o = take(M * C * es);
   p.h = take(M * F * es);
   p.pmax = take(M * p.ntiles * 4);
@@ -202,7 +201,7 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
   void* a = at<char>(ws, p.a);
   void* q = at<char>(ws, p.q);
   void* k = at<char>(ws, p.k);
-  void* vt = at<char>(ws, p.vt);
+  void* v = at<char>(ws, p.v);
   void* o = at<char>(ws, p.o);
   void* h = at<char>(ws, p.h);
   float* pmax = at<float>(ws, p.pmax);
@@ -217,8 +216,8 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
   }
   AttnArgs aa{};
   aa.q = q; aa.q_bh = (long long)T * D;
-  aa.k = k; aa.k_bh = (long long)T * D; aa.k_ld = D;
-  aa.vt = vt; aa.v_bh = (long long)D * p.Tpad; aa.v_ld = p.Tpad;
+  aa.k = k; aa.k_bh = (long long)T * D;
+  aa.v = v; aa.v_bh = (long long)T * D;
   aa.o = o; aa.o_ld = C;
   aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
@@ -229,7 +228,7 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
     qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
     qa.q = q; qa.q_bh = (long long)T * D;
     qa.k = k; qa.k_bh = (long long)T * D;
-    qa.vt = vt; qa.v_bh = (long long)D * p.Tpad; qa.v_ld = p.Tpad;
+    qa.v = v; qa.v_bh = (long long)T * D;
     qa.pos = nullptr;
     const bool last = l == L - 1;
     GPT_TRY(mark(GPT_KERNEL_QKV, last, true));
@@ -280,17 +279,17 @@ int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const 
                                   static_cast<hipStream_t>(stream)));
 }
 
-int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* ut, int ldt, int B, int T,
-                        void* out, void* stream) {
+int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* u, int B, int T, void* out,
+                        void* stream) {
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
-  if (!q || !k || !ut || !out) return GPT_ERR_NULL;
-  if (B <= 0 || T <= 0 || ldt < T || ldt % vec_of(cfg) != 0) return GPT_ERR_SHAPE;
+  if (!q || !k || !u || !out) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
   const int C = cfg->n_embd, H = cfg->n_head, D = C / H;
   AttnArgs aa{};
   aa.q = q; aa.q_bh = (long long)T * D;
-  aa.k = k; aa.k_bh = (long long)T * D; aa.k_ld = D;
-  aa.vt = ut; aa.v_bh = (long long)D * ldt; aa.v_ld = ldt;
+  aa.k = k; aa.k_bh = (long long)T * D;
+  aa.v = u; aa.v_bh = (long long)T * D;
   aa.o = out; aa.o_ld = C;
   aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));

@@ -12,16 +12,16 @@ struct QKVArgs {
   const void* W;      // c_attn weight [3C, C]
   const void* bias;   // [3C]
   int M, C, H, D, T_seq;
-  void* q;  long long q_bh;            // Q [B,H,T,D]
-  void* k;  long long k_bh;            // K [B,H,Tk,D]
-  void* vt; long long v_bh; int v_ld;  // U^T [B,H,D,Tk], row stride v_ld
+  void* q; long long q_bh;             // Q [B,H,T,D]
+  void* k; long long k_bh;             // K [B,H,Tk,D]
+  void* v; long long v_bh;             // U [B,H,Tk,D]
   const int32_t* pos;                  // nullable: cache position of t = 0
 };
 
 struct AttnArgs {
-  const void* q;  long long q_bh;
-  const void* k;  long long k_bh; int k_ld;
-  const void* vt; long long v_bh; int v_ld;
+  const void* q; long long q_bh;       // Q [B,H,T,D]
+  const void* k; long long k_bh;       // K [B,H,*,D]
+  const void* v; long long v_bh;       // U [B,H,*,D]
   void* o; int o_ld;                   // O [B*T, o_ld], head h at columns [hD, hD+D)
   int B, H, T_seq, D;
   float scale_log2;                    // log2(e) / sqrt(D)

@@ -39,7 +39,7 @@ SIGNATURES = {
     "gpt_status_string": (ctypes.c_char_p, [_c_int]),
     "gpt_debug_layernorm": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _vp, _vp]),
     "gpt_debug_linear": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
-    "gpt_debug_attention": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "gpt_debug_attention": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
 }
 
 _lib = None
@@ -198,8 +198,8 @@ def debug_linear(cfg, A, W, bias, out, act=0, out_f32=False, stream=None) -> Non
                                   1 if out_f32 else 0, _ptr(out), _stream(stream)))
 
 
-def debug_attention(cfg, q, k, ut, out, stream=None) -> None:
+def debug_attention(cfg, q, k, u, out, stream=None) -> None:
+    """q, k, u: [B, H, T, D] device tensors; out [B*T, C]."""
     B, H, T, D = q.shape
-    ldt = ut.shape[-1]
-    check(load().gpt_debug_attention(ctypes.byref(cfg_c(cfg)), _ptr(q), _ptr(k), _ptr(ut), ldt, B, T, _ptr(out),
+    check(load().gpt_debug_attention(ctypes.byref(cfg_c(cfg)), _ptr(q), _ptr(k), _ptr(u), B, T, _ptr(out),
                                      _stream(stream)))

@@ -129,14 +129,14 @@ int gpt_debug_layernorm(const gpt_config* cfg, const float* x, const void* g, co
 
 /* out[M,N] = act(A[M,K] W[N,K]^T + bias[N]); A, W, bias in cfg->dtype (bias
  * nullable); act 0 = none, 1 = tanh GELU; out fp32 if out_f32 else cfg->dtype.
- * Requires K % 8 == 0. */
+ * Requires K % 8 == 0 (bf16) or K % 4 == 0 (fp32). */
 int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const void* bias, int M, int N,
                      int K, int act, int out_f32, void* out, void* stream);
 
-/* Causal attention of every (b, h): q, k [B,H,T,D], ut = U^T [B,H,D,ldt]
- * (ldt >= T, ldt % 8 == 0), all cfg->dtype; out [B*T, C] in cfg->dtype with
- * head h in columns [hD, hD+D). */
-int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* ut, int ldt,
+/* Causal attention of every (b, h) ("第 25 章 从小 GPT 到 GPT-2" §25.2):
+ * q, k, u [B,H,T,D] in cfg->dtype; out [B*T, C] in cfg->dtype with head h in
+ * columns [hD, hD+D) (heads merged back). */
+int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* u,
                         int B, int T, void* out, void* stream);
 
 #ifdef __cplusplus

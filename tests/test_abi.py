@@ -91,7 +91,7 @@ def test_debug_entry_validation():
     assert L.gpt_debug_linear(ctypes.byref(c), 1, 1, None, 4, 4, 6, 0, 0, 1, None) == -4  # K % 4
     assert L.gpt_debug_linear(ctypes.byref(c), None, 1, None, 4, 4, 8, 0, 0, 1, None) == -1
     assert L.gpt_debug_layernorm(ctypes.byref(c), 1, 1, 1, 0, 1, None) == -4
-    assert L.gpt_debug_attention(ctypes.byref(c), 1, 1, 1, 10, 2, 12, 1, None) == -4  # ldt < T
+    assert L.gpt_debug_attention(ctypes.byref(c), 1, 1, 1, 0, 12, 1, None) == -4  # B = 0
 
 
 def test_workspace_grows_with_batch():
