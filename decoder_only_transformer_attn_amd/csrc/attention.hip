@@ -36,8 +36,7 @@ template <> struct VtFrag<bf16> {
   static __device__ __forceinline__ bf16x8 pack(const f32x16& p, int hh) {
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = uint32_t(f32_to_bf16(p[8 * hh + 2 * e])) | (uint32_t(f32_to_bf16(p[8 * hh + 2 * e + 1])) << 16);
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
 };
@@ -51,7 +50,10 @@ template <> struct VtFrag<float> {
   static __device__ __forceinline__ float pack(const f32x16& p, int hh) { return p[hh]; }
 };
 
-// Block: 4 waves, 32 queries each (BQ = 128); key/value tiles of BKV keys.
+// Block: 4 waves, 32 queries each (BQ = 128); key/value tiles of BKV keys,
+// double-buffered in LDS: the global loads of tile k+1 are issued into
+// registers before tile k is multiplied and written to the other buffer
+// after it, so their latency hides under the tile's MFMA and softmax work.
 template <typename T, int DP, int BKV>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
@@ -62,13 +64,18 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   constexpr int NDI = DP / MF::KPI; // MFMA k steps over the head dim
   constexpr int NDT = DP / 32;      // 32-row d tiles of O^T
   constexpr int NST = BKV / 32;     // 32-key sub-tiles per KV tile
-  __shared__ __align__(16) T sK[BKV * LDKS];
-  __shared__ __align__(16) T sV[DP * LDVS];
+  constexpr int KTOT = BKV * (DP / VEC), UTOT = (BKV / 2) * (DP / VEC);   // items per tile
+  constexpr int KCH = (KTOT + 255) / 256, UCH = (UTOT + 255) / 256;        // per thread
+  __shared__ __align__(16) T sK[2][BKV * LDKS];
+  __shared__ __align__(16) T sV[2][DP * LDVS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-  const int nqt = gridDim.x;
-  const int qt = nqt - 1 - blockIdx.x;  // longest query tiles first
-  const int bh = blockIdx.y;
+  // 1-D grid, query tile major and longest first: the blocks with the most
+  // key tiles start first, the short ones fill in at the end
+  const int nbh = a.B * a.H;
+  const int nqt = (a.T_seq + BQ - 1) / BQ;
+  const int qt = nqt - 1 - (int)(blockIdx.x / nbh);
+  const int bh = blockIdx.x % nbh;
   const int b = bh / a.H, h = bh - b * a.H;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
@@ -88,46 +95,68 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     else qf[i] = typename MF::frag{};
   }
 
-  f32x16 acc[NDT];
+  // prefetch registers: K chunks and U key pairs; rows/cols outside the sequence are zero
+  uint4 kr[KCH], ur0[UCH], ur1[UCH];
+  auto gload = [&](int kb) {
 #pragma unroll
-  for (int i = 0; i < NDT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int kv_end = min(T_seq, q0 + BQ);  // keys [0, kv_end) can be visible to this block
-  for (int kb = 0; kb < kv_end; kb += BKV) {
-    // stage K [BKV][DP] and U^T [DP][BKV]; rows/cols outside the sequence are zero
-    for (int ch = tid; ch < BKV * (DP / VEC); ch += 256) {
-      const int row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
       const int key = kb + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < T_seq && dc < D) v = *reinterpret_cast<const uint4*>(K + (long long)key * D + dc);
-      *reinterpret_cast<uint4*>(sK + row * LDKS + dc) = v;
+      kr[c] = (ch < KTOT && key < T_seq && dc < D) ? *reinterpret_cast<const uint4*>(K + (long long)key * D + dc)
+                                                   : make_uint4(0, 0, 0, 0);
     }
-    // U: each item is two consecutive keys x VEC head columns, written
-    // transposed as VEC pairs (key, key + 1) of row d of U^T
-    for (int ch = tid; ch < (BKV / 2) * (DP / VEC); ch += 256) {
-      const int kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
+#pragma unroll
+    for (int c = 0; c < UCH; ++c) {
+      const int ch = tid + c * 256, kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
       const int key = kb + kp;
+      const bool in = ch < UTOT && dc < D;
+      ur0[c] = (in && key < T_seq) ? *reinterpret_cast<const uint4*>(U + (long long)key * D + dc)
+                                   : make_uint4(0, 0, 0, 0);
+      ur1[c] = (in && key + 1 < T_seq) ? *reinterpret_cast<const uint4*>(U + (long long)(key + 1) * D + dc)
+                                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // K as is; U transposed to U^T [d][key], written as (key, key+1) pairs
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
+      if (ch < KTOT) *reinterpret_cast<uint4*>(&sK[buf][row * LDKS + dc]) = kr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < UCH; ++c) {
+      const int ch = tid + c * 256, kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
+      if (ch >= UTOT) continue;
       T u0[VEC], u1[VEC];
-      *reinterpret_cast<uint4*>(u0) = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(u1) = make_uint4(0, 0, 0, 0);
-      if (dc < D) {
-        if (key < T_seq) *reinterpret_cast<uint4*>(u0) = *reinterpret_cast<const uint4*>(U + (long long)key * D + dc);
-        if (key + 1 < T_seq)
-          *reinterpret_cast<uint4*>(u1) = *reinterpret_cast<const uint4*>(U + (long long)(key + 1) * D + dc);
-      }
+      *reinterpret_cast<uint4*>(u0) = ur0[c];
+      *reinterpret_cast<uint4*>(u1) = ur1[c];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        T* dst = sV + (dc + e) * LDVS + kp;   // kp and LDVS even: pair-aligned
+        T* dst = &sV[buf][(dc + e) * LDVS + kp];   // kp and LDVS even: pair-aligned
         if constexpr (sizeof(T) == 2)
           *reinterpret_cast<uint32_t*>(dst) = uint32_t(u0[e]) | (uint32_t(u1[e]) << 16);
         else
           *reinterpret_cast<float2*>(dst) = make_float2(u0[e], u1[e]);
       }
     }
-    __syncthreads();
+  };
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 domain) and lane-partial sum
+  const float sc = a.scale_log2;
+
+  const int kv_end = min(T_seq, q0 + BQ);  // keys [0, kv_end) can be visible to this block
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kb = 0, it = 0; kb < kv_end; kb += BKV, ++it) {
+    const int cur = it & 1;
+    const bool more = kb + BKV < kv_end;
+    if (more) gload(kb + BKV);
 
     if (kb <= qw0 + 31) {  // otherwise every key of this tile is in this wave's future
       f32x16 s[NST];
@@ -135,30 +164,31 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
       for (int st = 0; st < NST; ++st) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
-        const T* krow = sK + (st * 32 + (lane & 31)) * LDKS + g * MF::KPL;
+        const T* krow = &sK[cur][(st * 32 + (lane & 31)) * LDKS + g * MF::KPL];
 #pragma unroll
         for (int i = 0; i < NDI; ++i) s[st] = MF::mma(MF::load(krow + i * MF::KPI), qf[i], s[st]);
       }
-      const bool diag = kb + BKV - 1 > qw0;
+      if (kb + BKV - 1 > qw0) {   // diagonal tile: mask keys after the query
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb + st * 32 + acc_row(r, lane) > qcol) s[st][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < NST; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[st][r] * a.scale_log2;
-          if (diag && kb + st * 32 + acc_row(r, lane) > qcol) v = -INFINITY;
-          s[st][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[st][r] - m_new);
+          const float p = fast_exp2(fmaf(s[st][r], sc, -m_new));
           s[st][r] = p;
           psum += p;
         }
@@ -175,11 +205,12 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
           const auto pb = VtFrag<T>::pack(s[st], hh);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const T* vrow = sV + (dt * 32 + (lane & 31)) * LDVS + st * 32;
+            const T* vrow = &sV[cur][(dt * 32 + (lane & 31)) * LDVS + st * 32];
             acc[dt] = MF::mma(VtFrag<T>::load(vrow, hh, g), pb, acc[dt]);
           }
         }
     }
+    if (more) sstore(cur ^ 1);
     __syncthreads();
   }
 
@@ -199,7 +230,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 
 template <typename T>
 static hipError_t attn_t(const AttnArgs& a, hipStream_t st) {
-  dim3 grid((a.T_seq + 127) / 128, a.B * a.H), block(256);
+  dim3 grid(((a.T_seq + 127) / 128) * a.B * a.H), block(256);
   if (a.D <= 32)
     hipLaunchKernelGGL((attn_fwd_kernel<T, 32, 64>), grid, block, 0, st, a);
   else if (a.D <= 64)

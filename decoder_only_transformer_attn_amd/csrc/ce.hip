@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(256) ce_rows_kernel(int M, int ntiles, const f
     for (int t = lane; t < ntiles; t += 64) mx = fmaxf(mx, pm[t]);
     mx = wave_max(mx);
     float s = 0.f;
-    for (int t = lane; t < ntiles; t += 64) s += ps[t] * __expf(pm[t] - mx);
+    for (int t = lane; t < ntiles; t += 64) s += ps[t] * fast_exp2((pm[t] - mx) * 1.4426950408889634f);
     s = wave_sum(s);
     const int y = target_of(targets, idx, m, T_seq);
     const bool valid = y >= 0 && y < V;

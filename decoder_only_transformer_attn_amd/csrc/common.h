@@ -8,6 +8,7 @@ namespace gptmi {
 
 typedef uint16_t bf16;  // storage of a bfloat16 value (upper half of an fp32)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -16,12 +17,18 @@ constexpr int WAVE = 64;
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite on this path).
-__device__ __forceinline__ bf16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return bf16(u >> 16);
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32, two values per instruction).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) { return __builtin_bit_cast(bf16, (__bf16)f); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// 2^x with the hardware v_exp_f32 alone (results below 2^-126 flush to zero,
+// which no softmax or GELU term here can notice).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }

@@ -286,21 +286,24 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 
 // ---------------------------------------------------------------------------
 // Epilogues.  Each is called for two adjacent output columns (n, n+1) of
-// one row; has_b is false only for the last column of an odd N.  Epilogues
-// with kPreload read their extra input (the residual stream) before the main
-// loop, so that its latency hides under the MFMA work.
+// one row; has_b is false only for the last column of an odd N.  All inputs
+// an epilogue reads are fetched before the main loop so that their latency
+// hides under the MFMA work: col(n) returns the per-column values (the bias
+// pair), and epilogues with kPreload also read a per-element input (the
+// residual stream) through preload(m, n).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float gelu_tanh(float v) {
-  // 0.5 z (1 + tanh(u)), u = sqrt(2/pi)(z + 0.044715 z^3), evaluated as z * sigmoid(2u)
-  const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-  return v / (1.0f + __expf(-2.0f * u));
+  // 0.5 z (1 + tanh(u)), u = sqrt(2/pi)(z + 0.044715 z^3), evaluated as
+  // z * sigmoid(2u) = z / (1 + exp(-2u)), with exp(-2u) = exp2(-2 log2(e) u)
+  const float u = v * (0.7978845608028654f + 0.035677408136300125f * v * v);
+  return v * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-2.8853900817779268f * u));
 }
 
 template <typename T>
 __device__ __forceinline__ void store_pair(T* p, float a, float b, bool has_b, bool vec_ok) {
   if (has_b && vec_ok) {
     if constexpr (sizeof(T) == 4) *reinterpret_cast<float2*>(p) = make_float2(a, b);
-    else *reinterpret_cast<uint32_t*>(p) = uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+    else *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
   } else {
     p[0] = from_f32<T>(a);
     if (has_b) p[1] = from_f32<T>(b);
@@ -310,17 +313,20 @@ __device__ __forceinline__ void store_pair(T* p, float a, float b, bool has_b, b
 template <typename T>
 struct EpiAct {  // out[m, n] = act(v + bias[n])
   static constexpr bool kPreload = false;
+  typedef int Row;
+  __device__ __forceinline__ Row row(int) const { return 0; }
   const T* bias;
   void* out;
   int ldo;
   int act;       // 0 none, 1 tanh-GELU
   int out_f32;   // store fp32 instead of T
+  __device__ __forceinline__ float2 col(int n, bool has_b) const {
+    return bias ? make_float2(to_f32(bias[n]), has_b ? to_f32(bias[n + 1]) : 0.f) : make_float2(0.f, 0.f);
+  }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
-  __device__ __forceinline__ void pair(int m, int n, float a, float b, bool has_b, float2) const {
-    if (bias) {
-      a += to_f32(bias[n]);
-      if (has_b) b += to_f32(bias[n + 1]);
-    }
+  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, float2 bs, float2) const {
+    a += bs.x;
+    b += bs.y;
     if (act == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
     const size_t o = (size_t)m * ldo + n;
     if (out_f32) store_pair(reinterpret_cast<float*>(out) + o, a, b, has_b, (ldo & 1) == 0);
@@ -331,46 +337,62 @@ struct EpiAct {  // out[m, n] = act(v + bias[n])
 template <typename T>
 struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
   static constexpr bool kPreload = true;
+  typedef int Row;
+  __device__ __forceinline__ Row row(int) const { return 0; }
   const T* bias;
   float* x;
   int ldx;
+  __device__ __forceinline__ float2 col(int n, bool has_b) const {
+    return make_float2(to_f32(bias[n]), has_b ? to_f32(bias[n + 1]) : 0.f);
+  }
   __device__ __forceinline__ float2 preload(int m, int n, bool has_b) const {
     const float* p = x + (size_t)m * ldx + n;
     if (has_b && (ldx & 1) == 0) return *reinterpret_cast<const float2*>(p);
     return make_float2(p[0], has_b ? p[1] : 0.f);
   }
-  __device__ __forceinline__ void pair(int m, int n, float a, float b, bool has_b, float2 xo) const {
-    a = xo.x + (a + to_f32(bias[n]));
-    if (has_b) b = xo.y + (b + to_f32(bias[n + 1]));
+  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, float2 bs, float2 xo) const {
+    a = xo.x + (a + bs.x);
+    if (has_b) b = xo.y + (b + bs.y);
     store_pair(x + (size_t)m * ldx + n, a, b, has_b, (ldx & 1) == 0);
   }
 };
+
+// q = m / d for 0 <= m < 2^24 with a float reciprocal and one correction step.
+__device__ __forceinline__ int div_small(int m, int d, float inv_d) {
+  int q = (int)((float)m * inv_d);
+  q -= (q * d > m);
+  q += ((q + 1) * d <= m);
+  return q;
+}
 
 template <typename T>
 struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all three [B,H,T,D]
   static constexpr bool kPreload = false;
   const T* bias;
   int C, H, D, T_seq;
+  float inv_T;
   T* q; long long q_bh;             // q[(b*H+h)*q_bh + t*D + d]
   T* k; long long k_bh;             // k[(b*H+h)*k_bh + tc*D + d]
   T* v; long long v_bh;             // v[(b*H+h)*v_bh + tc*D + d]
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
+  struct Row { int b, t, tc; };
+  __device__ __forceinline__ Row row(int m) const {
+    const int bb = div_small(m, T_seq, inv_T), t = m - bb * T_seq;
+    return Row{bb, t, t + (pos ? *pos : 0)};
+  }
+  __device__ __forceinline__ float2 col(int n, bool) const { return make_float2(to_f32(bias[n]), to_f32(bias[n + 1])); }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
-  __device__ __forceinline__ void pair(int m, int n, float a, float b, bool, float2) const {
+  __device__ __forceinline__ void pair(const Row& r, int, int n, float a, float b, bool, float2 bs, float2) const {
     // D is even, so n and n + 1 fall in the same head of the same projection
-    a += to_f32(bias[n]);
-    b += to_f32(bias[n + 1]);
+    a += bs.x;
+    b += bs.y;
     const int which = n / C;
     const int c = n - which * C;
     const int h = c / D, d = c - h * D;
-    const int bb = m / T_seq, t = m - bb * T_seq;
-    const long long bh = (long long)bb * H + h;
+    const long long bh = (long long)r.b * H + h;
     T* dst;
-    if (which == 0) dst = q + bh * q_bh + (long long)t * D + d;
-    else {
-      const int tc = t + (pos ? *pos : 0);
-      dst = (which == 1 ? k + bh * k_bh : v + bh * v_bh) + (long long)tc * D + d;
-    }
+    if (which == 0) dst = q + bh * q_bh + (long long)r.t * D + d;
+    else dst = (which == 1 ? k + bh * k_bh : v + bh * v_bh) + (long long)r.tc * D + d;
     store_pair(dst, a, b, true, true);
   }
 };
@@ -388,8 +410,14 @@ __device__ __forceinline__ void pair_coords(int i, int j, int rp, int mbase, int
 }
 
 template <int TM, int TN, typename Epi>
-__device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], int mbase, int nbase, int M, int N,
-                                              const Epi& epi) {
+__device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], float2 (&colv)[TN], int mbase, int nbase,
+                                              int M, int N, const Epi& epi) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    int m, n;
+    pair_coords<TM, TN>(0, j, 0, mbase, nbase, m, n);
+    colv[j] = n < N ? epi.col(n, n + 1 < N) : make_float2(0.f, 0.f);
+  }
   if constexpr (Epi::kPreload) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -405,22 +433,27 @@ __device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], int mbas
 }
 
 template <int TM, int TN, typename Epi>
-__device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], const float2 (&pre)[TM][TN][8], int mbase,
-                                               int nbase, int M, int N, const Epi& epi) {
+__device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], const float2 (&pre)[TM][TN][8],
+                                               const float2 (&colv)[TN], int mbase, int nbase, int M, int N,
+                                               const Epi& epi) {
   const bool odd = threadIdx.x & 1;
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int rp = 0; rp < 8; ++rp) {
+      int m, n0;
+      pair_coords<TM, TN>(i, 0, rp, mbase, nbase, m, n0);
+      const typename Epi::Row rc = epi.row(m);
 #pragma unroll
-      for (int rp = 0; rp < 8; ++rp) {
+      for (int j = 0; j < TN; ++j) {
+        // every lane takes part in the exchange; only the store is predicated
         const float v0 = acc[i][j][2 * rp], v1 = acc[i][j][2 * rp + 1];
         const float recv = __shfl_xor(odd ? v0 : v1, 1, 64);
-        int m, n;
-        pair_coords<TM, TN>(i, j, rp, mbase, nbase, m, n);
+        const int n = n0 + j * 32;
         const float a = odd ? recv : v0, b = odd ? v1 : recv;
-        if (m < M && n < N) epi.pair(m, n, a, b, n + 1 < N, pre[i][j][rp]);
+        if (m < M && n < N) epi.pair(rc, m, n, a, b, n + 1 < N, colv[j], pre[i][j][rp]);
       }
+    }
 }
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL, typename Epi>
@@ -434,11 +467,11 @@ gemm_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, 
   const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
-  float2 pre[G::TM][G::TN][8];
-  preload_pairs<G::TM, G::TN>(pre, mb, nb, M, N, epi);
+  float2 pre[G::TM][G::TN][8], colv[G::TN];
+  preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
   gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
-  epilogue_pairs<G::TM, G::TN>(acc, pre, mb, nb, M, N, epi);
+  epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
 }
 
 // bf16 GEMM through the pipelined main loop, element-wise epilogue.
@@ -457,11 +490,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64) gemm_dma_kernel(co
   const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / D::NWN) * WM, nb = n0 + (wave % D::NWN) * WN;
-  float2 pre[D::TM][D::TN][8];
-  preload_pairs<D::TM, D::TN>(pre, mb, nb, M, N, epi);
+  float2 pre[D::TM][D::TN][8], colv[D::TN];
+  preload_pairs<D::TM, D::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[D::TM][D::TN];
   dma_mainloop<BM, BN, WM, WN, K>(A, W, M, N, m0, n0, s0, s1, s2, s3, acc);
-  epilogue_pairs<D::TM, D::TN>(acc, pre, mb, nb, M, N, epi);
+  epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -495,17 +528,40 @@ __device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
 // softmax partials of a token over this block's 256 vocab entries are then a
 // reduction over the lane's own registers, one exchange with the lane holding
 // the other half of the rows (l ^ 32), and a 4-way combine over the waves
-// along the vocab axis.  Logits are staged through LDS, 32 tokens at a time,
-// shifted so that every 16-byte window of a global logits row is one aligned
-// LDS read and one aligned 16-byte store (V is odd, so rows are only 2-byte
-// aligned); the partial windows at the ends of a row are written per element.
+// along the vocab axis.  The target ids are read before the main loop.
+// Logits: the whole 256 x 256 bf16 tile is staged in the four (then free)
+// pipeline stages, 64 token rows of 512 bytes each with 16-byte chunks
+// XOR-swizzled by row, behind a single barrier; each 16-byte window of a
+// global logits row (V is odd, so rows are only 2-byte aligned) is then
+// assembled from two LDS chunks and written with one aligned 16-byte store;
+// the partial windows at the two ends of a row are written per element.
+__device__ __forceinline__ uint4 lds_chunk(const char* row, int c, int sw) {
+  if (c < 0 || c >= 32) return make_uint4(0, 0, 0, 0);
+  return *reinterpret_cast<const uint4*>(row + ((c ^ sw) << 4));
+}
+
+// Elements o .. o+7 of the 16-element concatenation lo ++ hi (o in 0..7).
+__device__ __forceinline__ uint4 window8(uint4 lo, uint4 hi, int o) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int o2 = o >> 1;
+  uint32_t y[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const uint32_t a0 = w[j], a1 = w[j + 1], a2 = w[j + 2], a3 = (j + 3 < 8) ? w[j + 3] : 0u;
+    y[j] = o2 == 0 ? a0 : (o2 == 1 ? a1 : (o2 == 2 ? a2 : a3));
+  }
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = (o & 1) ? __builtin_amdgcn_alignbyte(y[j + 1], y[j], 2) : y[j];
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 template <int K>
 __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act,
                                                           int V, int Mtok, HeadArgs ha) {
   constexpr int BM = 256, BN = 256, WM = 64, WN = 128;   // BM: vocab, BN: tokens
   typedef DmaCfg<BM, BN, WM, WN> D;
-  constexpr int ROWE = BM + 8, ROWBYTES = ROWE * 2;       // staged logits row (elements / bytes)
-  static_assert(32 * ROWBYTES <= D::STAGE, "staging buffer");
+  static_assert(64 * BM * 2 == D::STAGE, "a stage holds 64 staged token rows");
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
   __shared__ __align__(1024) char s2[D::STAGE];
@@ -515,44 +571,85 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
   int tt, vt;
   tile_of(blockIdx.x, gridDim.x, num_t, num_v, tt, vt);   // groups of token tiles sweep the vocab
   const int v0 = vt * BM, t0 = tt * BN;
-  f32x16 acc[D::TM][D::TN];
-  dma_mainloop<BM, BN, WM, WN, K>(wte, act, V, Mtok, v0, t0, s0, s1, s2, s3, acc);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / D::NWN, wn = wave % D::NWN;
   const int vw0 = v0 + wm * WM;   // first vocab row of this wave
+  const bool full = vw0 + WM <= V;   // no vocab row of this wave is past V
+
+  int ytok[D::TN];                // target of each of this lane's tokens (-1: none)
+#pragma unroll
+  for (int j = 0; j < D::TN; ++j) {
+    const int m = t0 + wn * WN + j * 32 + (lane & 31);
+    ytok[j] = m < Mtok ? head_target(ha, m) : -1;
+  }
+
+  f32x16 acc[D::TM][D::TN];
+  dma_mainloop<BM, BN, WM, WN, K>(wte, act, V, Mtok, v0, t0, s0, s1, s2, s3, acc);
 
   // softmax partials and target logit, per token
 #pragma unroll
   for (int j = 0; j < D::TN; ++j) {
     const int tl = wn * WN + j * 32 + (lane & 31);
     const int m = t0 + tl;
-    float mx = -INFINITY;
+    float mx = -INFINITY, sum = 0.f;
+    constexpr float LOG2E = 1.4426950408889634f;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < D::TM; ++i)
+      for (int i = 0; i < D::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (vw0 + i * 32 + acc_row(r, lane) < V) mx = fmaxf(mx, acc[i][j][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float sum = 0.f;
-    if (mx > -INFINITY) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mxl = mx * LOG2E;
+#pragma unroll
+      for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[i][j][r], LOG2E, -mxl));
+    } else {
 #pragma unroll
       for (int i = 0; i < D::TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (vw0 + i * 32 + acc_row(r, lane) < V) sum += __expf(acc[i][j][r] - mx);
-    }
-    sum += __shfl_xor(sum, 32, 64);
-    if (g == 0) { red[wm][tl][0] = mx; red[wm][tl][1] = sum; }
-    if (m < Mtok) {
-      const int y = head_target(ha, m);
-      if (y >= vw0 && y < vw0 + WM) {
+          if (vw0 + i * 32 + acc_row(r, lane) < V) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (mx > -INFINITY) {
+        const float mxl = mx * LOG2E;
 #pragma unroll
         for (int i = 0; i < D::TM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (vw0 + i * 32 + acc_row(r, lane) == y) ha.tgt[m] = acc[i][j][r];
+            if (vw0 + i * 32 + acc_row(r, lane) < V) sum += fast_exp2(fmaf(acc[i][j][r], LOG2E, -mxl));
       }
+    }
+    sum += __shfl_xor(sum, 32, 64);
+    if (g == 0) { red[wm][tl][0] = mx; red[wm][tl][1] = sum; }
+    const int y = ytok[j];
+    if (m < Mtok && y >= vw0 && y < vw0 + WM) {
+#pragma unroll
+      for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vw0 + i * 32 + acc_row(r, lane) == y) ha.tgt[m] = acc[i][j][r];
+    }
+  }
+
+  // stage the bf16 logits tile: token row tl -> stage tl / 64, row tl % 64
+  auto stg = [&](int i) -> char* { return i == 0 ? s0 : (i == 1 ? s1 : (i == 2 ? s2 : s3)); };
+  if (ha.logits) {
+#pragma unroll
+    for (int j = 0; j < D::TN; ++j) {
+      const int tl = wn * WN + j * 32 + (lane & 31);
+      char* row = stg((wn * WN + j * 32) >> 6) + (tl & 63) * (BM * 2);
+      const int sw = tl & 31;
+#pragma unroll
+      for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // registers 4q .. 4q+3: 4 consecutive vocab rows
+          const int u = (wm * WM + i * 32 + q * 8 + g * 4) >> 2;   // 8-byte unit within the row
+          const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<uint2*>(row + (((u >> 1) ^ sw) << 4) + ((u & 1) << 3)) = make_uint2(lo, hi);
+        }
     }
   }
   __syncthreads();
@@ -566,61 +663,38 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
 #pragma unroll
     for (int w = 0; w < D::NWM; ++w) {
       const float mw = red[w][tl][0];
-      if (mw > -INFINITY) S += red[w][tl][1] * __expf(mw - M_);
+      if (mw > -INFINITY) S += red[w][tl][1] * fast_exp2((mw - M_) * 1.4426950408889634f);
     }
     ha.part_max[(long long)m * ha.ntiles + vt] = M_;
     ha.part_sum[(long long)m * ha.ntiles + vt] = S;
   }
   if (!ha.logits) return;
 
-  // logits: 8 rounds of 32 tokens, staging buffers alternate between s0 and s1
   bf16* const L = reinterpret_cast<bf16*>(ha.logits);
   const int elem_mis = (int)((reinterpret_cast<uintptr_t>(ha.logits) >> 1) & 7);
   const int nv = min(BM, V - v0);
-#pragma unroll 1
-  for (int q = 0; q < BN / 32; ++q) {
-    char* buf = (q & 1) ? s1 : s0;
-    // writers: the 4 waves with wn == q / 4 hold these tokens in register block j = q % 4
-    if (wn == q / 4) {
-      const int jq = q % 4;
-      const int tok = lane & 31;                          // token within the round
-      const int m = t0 + q * 32 + tok;
-      const int sh = (int)(((long long)m * ha.ld_logits + v0 + elem_mis) & 7);
-      bf16* row = reinterpret_cast<bf16*>(buf + tok * ROWBYTES);
+  constexpr int NWIN = (BM + 7 + 7) / 8;   // windows per row, enough for any shift
+  for (int it = tid; it < BN * NWIN; it += D::NT) {
+    const int tl = it / NWIN, k = it - tl * NWIN;
+    const int m = t0 + tl;
+    if (m >= Mtok) continue;
+    const long long e0 = (long long)m * ha.ld_logits + v0;   // element index of (m, v0)
+    const int sh = (int)((e0 + elem_mis) & 7);                // its offset in a 16-byte window
+    const int p0 = 8 * k;                                       // window start, in shifted positions
+    if (p0 >= sh + nv) continue;
+    const char* row = stg(tl >> 6) + (tl & 63) * (BM * 2);
+    const int q0 = p0 - sh;                                     // first tile column of the window
+    const int clo = q0 >= 0 ? (q0 >> 3) : -1;
+    const int o = q0 - 8 * clo;
+    const uint4 w = window8(lds_chunk(row, clo, tl & 31), lds_chunk(row, clo + 1, tl & 31), o);
+    bf16* gp = L + e0 - sh + p0;                                // 16-byte aligned
+    if (p0 >= sh && p0 + 8 <= sh + nv) {
+      *reinterpret_cast<uint4*>(gp) = w;
+    } else {
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int jj = 0; jj < D::TN; ++jj) {
-        if (jj != jq) continue;
-#pragma unroll
-        for (int i = 0; i < D::TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int vl = wm * WM + i * 32 + acc_row(r, lane);
-            row[vl + sh] = f32_to_bf16(acc[i][jj][r]);
-          }
-      }
-    }
-    // LDS writes visible to the block; global stores of earlier rounds stay in flight
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    lds_barrier();
-    const int nwin = (nv + 7 + 8) / 8;   // upper bound of windows per row
-    for (int it = tid; it < 32 * nwin; it += D::NT) {
-      const int tok = it / nwin, k = it - tok * nwin;
-      const int m = t0 + q * 32 + tok;
-      if (m >= Mtok) continue;
-      const long long e0 = (long long)m * ha.ld_logits + v0;
-      const int sh = (int)((e0 + elem_mis) & 7);
-      const int p0 = 8 * k;
-      if (p0 >= sh + nv) continue;
-      const char* row = buf + tok * ROWBYTES;
-      bf16* gp = L + e0 - sh + p0;                        // 16-byte aligned window
-      if (p0 >= sh && p0 + 8 <= sh + nv) {
-        *reinterpret_cast<uint4*>(gp) = *reinterpret_cast<const uint4*>(row + 2 * p0);
-      } else {
-        const bf16* lr = reinterpret_cast<const bf16*>(row);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (p0 + e >= sh && p0 + e < sh + nv) gp[e] = lr[p0 + e];
-      }
+      for (int e = 0; e < 8; ++e)
+        if (p0 + e >= sh && p0 + e < sh + nv) gp[e] = bf16(ww[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -791,7 +865,8 @@ hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W,
 
 template <typename T>
 static hipError_t qkv_t(const QKVArgs& a, hipStream_t st) {
-  EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh, (T*)a.v, a.v_bh, a.pos};
+  EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, 1.0f / (float)a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh,
+              (T*)a.v, a.v_bh, a.pos};
   return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, 3 * a.C, a.C, e, st);
 }
 

@@ -78,7 +78,9 @@ def test_layernorm_kernel(dtype, C, M):
 
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 @pytest.mark.parametrize("M,N,K,act", [(48, 48, 16, 0), (256, 384, 128, 1), (100, 77, 40, 0),
-                                      (333, 1000, 768, 1), (1024, 2304, 768, 0), (130, 17, 3072, 0)])
+                                      (333, 1000, 768, 1), (1024, 2304, 768, 0), (130, 17, 3072, 0),
+                                      # pipelined bf16 path (K = 768 / 3072), odd and ragged M
+                                      (8191, 2304, 768, 0), (4097, 768, 3072, 1), (2049, 3072, 768, 1)])
 def test_linear_kernel(dtype, M, N, K, act):
     lib = _lib()
     cfg = synth.GPTConfig(vocab=17, ctx=16, n_embd=16, n_head=2, n_layer=1, n_ff=64, dtype=dtype)
@@ -240,6 +242,23 @@ def test_gpt2_bf16_ragged_stress(gpt2_inputs):
     ref_l, ref_t, ref_m = O.forward(P, ids, cfg.n_head)
     _bf16_check(lg, tok, ref_l, ref_t, [0, 1])
     assert abs(mean - ref_m) <= 1e-2
+
+
+def test_gpt2_bf16_odd_length_explicit_targets():
+    # odd token count (ragged last tiles in every GEMM, attention and the head),
+    # explicit targets with ignored positions
+    cfg = synth.GPT2
+    params = synth.make_params(cfg, seed=11, cfg_id=3, init="stress")
+    P = synth.unpack_f64(cfg, params)
+    ids = synth.make_ids(cfg, 1, 999, seed=11, cfg_id=3)
+    rng = np.random.default_rng(5)
+    targets = rng.integers(0, cfg.vocab, (1, 999)).astype(np.int32)
+    targets[0, ::7] = -1
+    lg, tok, mean = run_gpu(cfg, params, ids, targets)
+    ref_l, ref_t, ref_m = O.forward(P, ids, cfg.n_head, targets=targets)
+    _bf16_check(lg, tok, ref_l, ref_t, [0])
+    assert abs(mean - ref_m) <= 1e-2
+    np.testing.assert_array_equal(tok[0, ::7], 0.0)
 
 
 def test_gpt2_bf16_no_logits_b32_matches_logits_path(gpt2_inputs):
