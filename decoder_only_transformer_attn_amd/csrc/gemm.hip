@@ -314,6 +314,7 @@ template <typename T>
 struct EpiAct {  // out[m, n] = act(v + bias[n])
   static constexpr bool kPreload = false;
   typedef int Row;
+  typedef float2 Col;
   __device__ __forceinline__ Row row(int) const { return 0; }
   const T* bias;
   void* out;
@@ -324,7 +325,7 @@ struct EpiAct {  // out[m, n] = act(v + bias[n])
     return bias ? make_float2(to_f32(bias[n]), has_b ? to_f32(bias[n + 1]) : 0.f) : make_float2(0.f, 0.f);
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
-  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, float2 bs, float2) const {
+  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, const Col& bs, float2) const {
     a += bs.x;
     b += bs.y;
     if (act == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
@@ -338,6 +339,7 @@ template <typename T>
 struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
   static constexpr bool kPreload = true;
   typedef int Row;
+  typedef float2 Col;
   __device__ __forceinline__ Row row(int) const { return 0; }
   const T* bias;
   float* x;
@@ -350,7 +352,7 @@ struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
     if (has_b && (ldx & 1) == 0) return *reinterpret_cast<const float2*>(p);
     return make_float2(p[0], has_b ? p[1] : 0.f);
   }
-  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, float2 bs, float2 xo) const {
+  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, const Col& bs, float2 xo) const {
     a = xo.x + (a + bs.x);
     if (has_b) b = xo.y + (b + bs.y);
     store_pair(x + (size_t)m * ldx + n, a, b, has_b, (ldx & 1) == 0);
@@ -376,24 +378,25 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   T* v; long long v_bh;             // v[(b*H+h)*v_bh + tc*D + d]
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
   struct Row { int b, t, tc; };
+  struct Col { float2 bias; T* base; long long bh_stride; bool is_q; };
   __device__ __forceinline__ Row row(int m) const {
     const int bb = div_small(m, T_seq, inv_T), t = m - bb * T_seq;
     return Row{bb, t, t + (pos ? *pos : 0)};
   }
-  __device__ __forceinline__ float2 col(int n, bool) const { return make_float2(to_f32(bias[n]), to_f32(bias[n + 1])); }
-  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
-  __device__ __forceinline__ void pair(const Row& r, int, int n, float a, float b, bool, float2 bs, float2) const {
-    // D is even, so n and n + 1 fall in the same head of the same projection
-    a += bs.x;
-    b += bs.y;
+  // Column n (even) -> projection, head and head column; D is even, so n and
+  // n + 1 fall in the same head of the same projection.
+  __device__ __forceinline__ Col col(int n, bool) const {
     const int which = n / C;
     const int c = n - which * C;
     const int h = c / D, d = c - h * D;
-    const long long bh = (long long)r.b * H + h;
-    T* dst;
-    if (which == 0) dst = q + bh * q_bh + (long long)r.t * D + d;
-    else dst = (which == 1 ? k + bh * k_bh : v + bh * v_bh) + (long long)r.tc * D + d;
-    store_pair(dst, a, b, true, true);
+    const long long st = which == 0 ? q_bh : (which == 1 ? k_bh : v_bh);
+    T* arr = which == 0 ? q : (which == 1 ? k : v);
+    return Col{make_float2(to_f32(bias[n]), to_f32(bias[n + 1])), arr + h * st + d, st * H, which == 0};
+  }
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ void pair(const Row& r, int, int, float a, float b, bool, const Col& cl, float2) const {
+    T* dst = cl.base + r.b * cl.bh_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
+    store_pair(dst, a + cl.bias.x, b + cl.bias.y, true, true);
   }
 };
 
@@ -410,13 +413,13 @@ __device__ __forceinline__ void pair_coords(int i, int j, int rp, int mbase, int
 }
 
 template <int TM, int TN, typename Epi>
-__device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], float2 (&colv)[TN], int mbase, int nbase,
-                                              int M, int N, const Epi& epi) {
+__device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], typename Epi::Col (&colv)[TN], int mbase,
+                                              int nbase, int M, int N, const Epi& epi) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     int m, n;
     pair_coords<TM, TN>(0, j, 0, mbase, nbase, m, n);
-    colv[j] = n < N ? epi.col(n, n + 1 < N) : make_float2(0.f, 0.f);
+    if (n < N) colv[j] = epi.col(n, n + 1 < N);
   }
   if constexpr (Epi::kPreload) {
 #pragma unroll
@@ -434,7 +437,7 @@ __device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], float2 (
 
 template <int TM, int TN, typename Epi>
 __device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], const float2 (&pre)[TM][TN][8],
-                                               const float2 (&colv)[TN], int mbase, int nbase, int M, int N,
+                                               const typename Epi::Col (&colv)[TN], int mbase, int nbase, int M, int N,
                                                const Epi& epi) {
   const bool odd = threadIdx.x & 1;
 #pragma unroll
@@ -467,7 +470,8 @@ gemm_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, 
   const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
-  float2 pre[G::TM][G::TN][8], colv[G::TN];
+  float2 pre[G::TM][G::TN][8];
+  typename Epi::Col colv[G::TN];
   preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
   gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
@@ -490,7 +494,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64) gemm_dma_kernel(co
   const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / D::NWN) * WM, nb = n0 + (wave % D::NWN) * WN;
-  float2 pre[D::TM][D::TN][8], colv[D::TN];
+  float2 pre[D::TM][D::TN][8];
+  typename Epi::Col colv[D::TN];
   preload_pairs<D::TM, D::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[D::TM][D::TN];
   dma_mainloop<BM, BN, WM, WN, K>(A, W, M, N, m0, n0, s0, s1, s2, s3, acc);
