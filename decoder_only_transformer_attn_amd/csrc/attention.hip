@@ -247,4 +247,68 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   return attn_t<bf16>(a, st);
 }
 
+// Decode step: the one new query of each (b, h) against cache positions
+// 0 .. *pos (its own K/U were appended at *pos by the QKV epilogue), the
+// KV-cache form of the same causal attention ("预训练一个 Mini GPT", KV
+// cache: only the new token's q, k, u are computed; earlier k, u are read
+// back).  One wave per (b, h): lanes own keys for the scores and head columns
+// for the weighted sum.  HBM-bound: every cached K and U row of the sequence
+// is read once.
+constexpr int DEC_MAXT = 4096;
+
+template <typename T>
+__global__ void __launch_bounds__(64) attn_decode_kernel(DecAttnArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float p[DEC_MAXT];
+  __shared__ float qs[128];
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H, D = a.D;
+  const T* q = reinterpret_cast<const T*>(a.q) + (long long)bh * D;
+  for (int d = lane; d < D; d += 64) qs[d] = to_f32(q[d]) * a.scale_log2;
+  __syncthreads();
+  int n = *a.pos + 1;
+  n = n < 1 ? 1 : (n < a.Tmax ? n : a.Tmax);   // a position outside [0, Tmax) violates the contract
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * a.kv_bh;
+  const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.kv_bh;
+  float mx = -INFINITY;
+  for (int k = lane; k < n; k += 64) {
+    const T* kr = K + (long long)k * D;
+    float s = 0.f;
+    for (int d = 0; d < D; d += VEC) {
+      T kv[VEC];
+      *reinterpret_cast<uint4*>(kv) = *reinterpret_cast<const uint4*>(kr + d);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s = fmaf(qs[d + e], to_f32(kv[e]), s);
+    }
+    p[k] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int k = lane; k < n; k += 64) {
+    const float e = fast_exp2(p[k] - mx);
+    p[k] = e;
+    sum += e;
+  }
+  sum = wave_sum(sum);
+  __syncthreads();
+  const float inv = 1.0f / sum;
+  T* orow = reinterpret_cast<T*>(a.o) + (long long)b * a.o_ld + h * D;
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.f;
+    for (int k = 0; k < n; ++k) acc = fmaf(p[k], to_f32(U[(long long)k * D + d]), acc);
+    orow[d] = from_f32<T>(acc * inv);
+  }
+}
+
+hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t st) {
+  if (a.Tmax > DEC_MAXT || a.D > 128) return hipErrorInvalidValue;
+  if (dtype == 0)
+    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(a.B * a.H), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(a.B * a.H), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace gptmi

@@ -71,6 +71,40 @@ __global__ void __launch_bounds__(256) ce_mean_kernel(int nblocks, const double*
 
 int ce_reduce_blocks(int M) { return (M + CE_ROWS - 1) / CE_ROWS; }
 
+// Greedy next token per row: the largest logit over all vocab tiles, the
+// lowest index among equal values ("GPT-1学习笔记" §6.1: greedy generation
+// takes the argmax of the last position's logits).  One wave per row.
+__global__ void __launch_bounds__(256) argmax_rows_kernel(int M, int ntiles, const float* __restrict__ part_max,
+                                                          const int32_t* __restrict__ part_idx,
+                                                          int32_t* __restrict__ next_tok, int32_t* pos, int set_pos) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m < M) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int t = lane; t < ntiles; t += 64) {
+      const float v = part_max[(long long)m * ntiles + t];
+      const int i = part_idx[(long long)m * ntiles + t];
+      if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
+      const int i2 = __shfl_xor(bi, o, 64);
+      if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+    }
+    if (lane == 0) next_tok[m] = bi;
+  }
+  if (pos && blockIdx.x == 0 && threadIdx.x == 0) *pos = set_pos >= 0 ? set_pos : *pos + 1;
+}
+
+hipError_t launch_argmax_reduce(int M, int ntiles, const float* part_max, const int32_t* part_idx, int32_t* next_tok,
+                                int32_t* pos, int set_pos, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3((M + 3) / 4), dim3(256), 0, st, M, ntiles, part_max, part_idx, next_tok,
+                     pos, set_pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,
                             const int32_t* targets, const int32_t* idx, int T_seq, int V, float* token_loss,
                             double* block_sums, float* mean_loss, hipStream_t st) {

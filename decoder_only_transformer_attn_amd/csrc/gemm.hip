@@ -377,6 +377,7 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   T* k; long long k_bh;             // k[(b*H+h)*k_bh + tc*D + d]
   T* v; long long v_bh;             // v[(b*H+h)*v_bh + tc*D + d]
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
+  int Tk;                           // K/U rows; cache positions >= Tk are not written
   struct Row { int b, t, tc; };
   struct Col { float2 bias; T* base; long long bh_stride; bool is_q; };
   __device__ __forceinline__ Row row(int m) const {
@@ -395,6 +396,7 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
   __device__ __forceinline__ void pair(const Row& r, int, int, float a, float b, bool, const Col& cl, float2) const {
+    if (!cl.is_q && (r.tc < 0 || r.tc >= Tk)) return;   // outside the cache: contract violation, nothing written
     T* dst = cl.base + r.b * cl.bh_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
     store_pair(dst, a + cl.bias.x, b + cl.bias.y, true, true);
   }
@@ -517,13 +519,18 @@ struct HeadArgs {
   float* part_max;
   float* part_sum;
   float* tgt;
+  int32_t* part_idx;      // argmax mode when non-null
   int ntiles;
   const int32_t* targets;
   const int32_t* idx;
   int T_seq;
 };
 
+// (value, index) order of the greedy choice: larger value, then lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
 __device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
+  if (ha.part_idx) return -1;
   if (ha.targets) return ha.targets[m];
   return ((m % ha.T_seq) < ha.T_seq - 1) ? ha.idx[m + 1] : -1;
 }
@@ -572,6 +579,7 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
   __shared__ __align__(1024) char s2[D::STAGE];
   __shared__ __align__(1024) char s3[D::STAGE];
   __shared__ float red[D::NWM][BN][2];
+  __shared__ int redi[D::NWM][BN];
   const int num_v = (V + BM - 1) / BM, num_t = (Mtok + BN - 1) / BN;
   int tt, vt;
   tile_of(blockIdx.x, gridDim.x, num_t, num_v, tt, vt);   // groups of token tiles sweep the vocab
@@ -592,9 +600,32 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
   f32x16 acc[D::TM][D::TN];
   dma_mainloop<BM, BN, WM, WN, K>(wte, act, V, Mtok, v0, t0, s0, s1, s2, s3, acc);
 
+  const bool amax = ha.part_idx != nullptr;
+  if (amax) {
+    // greedy choice: per token, the largest logit and its lowest vocab index.
+    // Register order i, r visits this lane's vocab rows in increasing order.
+#pragma unroll
+    for (int j = 0; j < D::TN; ++j) {
+      const int tl = wn * WN + j * 32 + (lane & 31);
+      float mx = -INFINITY;
+      int mi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vw0 + i * 32 + acc_row(r, lane);
+          if (v < V && acc[i][j][r] > mx) { mx = acc[i][j][r]; mi = v; }
+        }
+      const float v2 = __shfl_xor(mx, 32, 64);
+      const int i2 = __shfl_xor(mi, 32, 64);
+      if (better(v2, i2, mx, mi)) { mx = v2; mi = i2; }
+      if (g == 0) { red[wm][tl][0] = mx; redi[wm][tl] = mi; }
+    }
+  }
   // softmax partials and target logit, per token
 #pragma unroll
   for (int j = 0; j < D::TN; ++j) {
+    if (amax) break;
     const int tl = wn * WN + j * 32 + (lane & 31);
     const int m = t0 + tl;
     float mx = -INFINITY, sum = 0.f;
@@ -661,6 +692,16 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
   for (int tl = tid; tl < BN; tl += D::NT) {
     const int m = t0 + tl;
     if (m >= Mtok) continue;
+    if (amax) {
+      float mx = red[0][tl][0];
+      int mi = redi[0][tl];
+#pragma unroll
+      for (int w = 1; w < D::NWM; ++w)
+        if (better(red[w][tl][0], redi[w][tl], mx, mi)) { mx = red[w][tl][0]; mi = redi[w][tl]; }
+      ha.part_max[(long long)m * ha.ntiles + vt] = mx;
+      ha.part_idx[(long long)m * ha.ntiles + vt] = mi;
+      continue;
+    }
     float M_ = red[0][tl][0];
 #pragma unroll
     for (int w = 1; w < D::NWM; ++w) M_ = fmaxf(M_, red[w][tl][0]);
@@ -710,6 +751,7 @@ head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ld
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   __shared__ __align__(16) T smem[G::SMEM_ELEMS];
   __shared__ float red[G::NWN][BM];
+  __shared__ int redi[G::NWN][BM];
   __shared__ float rowmax[BM];
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
   int mt, nt;
@@ -717,6 +759,7 @@ head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ld
   const int m0 = mt * BM, n0 = nt * BN;
   f32x16 acc[G::TM][G::TN];
   gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
+  const bool amax = ha.part_idx != nullptr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / G::NWN, wn = wave % G::NWN;
   const int ncol0 = n0 + wn * WN + (lane & 31);
@@ -728,9 +771,7 @@ head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ld
     for (int r = 0; r < 16; ++r) {
       const int m = m0 + wm * WM + i * 32 + acc_row(r, lane);
       if (m >= M) continue;
-      int y;
-      if (ha.targets) y = ha.targets[m];
-      else y = ((m % ha.T_seq) < ha.T_seq - 1) ? ha.idx[m + 1] : -1;
+      const int y = head_target(ha, m);
 #pragma unroll
       for (int j = 0; j < G::TN; ++j) {
         const int n = ncol0 + j * 32;
@@ -741,25 +782,46 @@ head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ld
       }
     }
 
-  // row max over this block's columns
+  // row max (and, in argmax mode, its lowest column) over this block's columns
 #pragma unroll
   for (int i = 0; i < G::TM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float mx = -INFINITY;
+      int mi = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < G::TN; ++j)
-        if (ncol0 + j * 32 < N) mx = fmaxf(mx, acc[i][j][r]);
-      mx = half_max(mx);
-      if ((lane & 31) == 0) red[wn][wm * WM + i * 32 + acc_row(r, lane)] = mx;
+        if (ncol0 + j * 32 < N && acc[i][j][r] > mx) { mx = acc[i][j][r]; mi = ncol0 + j * 32; }
+      if (amax) {
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) {
+          const float v2 = __shfl_xor(mx, o, 64);
+          const int i2 = __shfl_xor(mi, o, 64);
+          if (better(v2, i2, mx, mi)) { mx = v2; mi = i2; }
+        }
+      } else {
+        mx = half_max(mx);
+      }
+      if ((lane & 31) == 0) {
+        red[wn][wm * WM + i * 32 + acc_row(r, lane)] = mx;
+        redi[wn][wm * WM + i * 32 + acc_row(r, lane)] = mi;
+      }
     }
   __syncthreads();
   for (int rr = threadIdx.x; rr < BM; rr += G::NT) {
     float mx = red[0][rr];
+    int mi = redi[0][rr];
 #pragma unroll
-    for (int w = 1; w < G::NWN; ++w) mx = fmaxf(mx, red[w][rr]);
+    for (int w = 1; w < G::NWN; ++w)
+      if (better(red[w][rr], redi[w][rr], mx, mi)) { mx = red[w][rr]; mi = redi[w][rr]; }
     rowmax[rr] = mx;
+    const int m = m0 + rr;
+    if (amax && m < M) {
+      ha.part_max[(long long)m * ha.ntiles + nt] = mx;
+      ha.part_idx[(long long)m * ha.ntiles + nt] = mi;
+    }
   }
+  if (amax) return;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < G::TM; ++i)
@@ -770,7 +832,7 @@ head_ce_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ld
       float s = 0.f;
 #pragma unroll
       for (int j = 0; j < G::TN; ++j)
-        if (ncol0 + j * 32 < N) s += __expf(acc[i][j][r] - mx);
+        if (ncol0 + j * 32 < N) s += fast_exp2((acc[i][j][r] - mx) * 1.4426950408889634f);
       s = half_sum(s);
       if ((lane & 31) == 0) red[wn][rl] = s;
     }
@@ -871,7 +933,7 @@ hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W,
 template <typename T>
 static hipError_t qkv_t(const QKVArgs& a, hipStream_t st) {
   EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, 1.0f / (float)a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh,
-              (T*)a.v, a.v_bh, a.pos};
+              (T*)a.v, a.v_bh, a.pos, a.Tk};
   return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, 3 * a.C, a.C, e, st);
 }
 
@@ -883,9 +945,9 @@ hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st) {
 int head_tile_n(int dtype) { return dtype == 0 ? 64 : 256; }
 
 hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int V, int C, void* logits,
-                          long long ld_logits, float* part_max, float* part_sum, float* tgt, const int32_t* targets,
-                          const int32_t* idx, int T_seq, hipStream_t st) {
-  HeadArgs ha{logits, ld_logits, part_max, part_sum, tgt, 0, targets, idx, T_seq};
+                          long long ld_logits, float* part_max, float* part_sum, float* tgt, int32_t* part_idx,
+                          const int32_t* targets, const int32_t* idx, int T_seq, hipStream_t st) {
+  HeadArgs ha{logits, ld_logits, part_max, part_sum, tgt, part_idx, 0, targets, idx, T_seq};
   if (dtype == 0) {
     constexpr int BM = 64, BN = 64;
     ha.ntiles = (V + BN - 1) / BN;

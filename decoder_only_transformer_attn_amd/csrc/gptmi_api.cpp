@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/gptmi.h: validation, parameter
-// blob offsets, workspace plan and the launch sequence of the forward pass.
-// Stateless: every call validates on the host, then enqueues kernels on the
-// caller's stream and returns without synchronising.
+// blob offsets, workspace plan and the launch sequences of the forward pass,
+// the prefill and the decode step.  Stateless: every call validates on the
+// host, then enqueues kernels on the caller's stream and returns without
+// synchronising.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -44,9 +45,6 @@ int check_config(const gpt_config* c) {
   return GPT_OK;
 }
 
-// Parameter blob views (element offsets), packing order as documented.
-struct LayerP { int64_t ln1_g, ln1_b, attn_w, attn_b, proj_w, proj_b, ln2_g, ln2_b, fc_w, fc_b, fcproj_w, fcproj_b; };
-
 int64_t offsets(const gpt_config* c, int64_t* out, int n) {
   const int64_t V = c->vocab, C = c->n_embd, F = c->n_ff, ctx = c->ctx;
   int64_t off = 0;
@@ -68,14 +66,52 @@ int64_t offsets(const gpt_config* c, int64_t* out, int n) {
   return off;
 }
 
+// Element offsets of the tensors of one layer, packing order as documented.
+struct LayerP { int64_t ln1_g, ln1_b, attn_w, attn_b, proj_w, proj_b, ln2_g, ln2_b, fc_w, fc_b, fcproj_w, fcproj_b; };
+
+struct Params {
+  const char* base;
+  size_t es;
+  int64_t C, F, V, ctx, L;
+  const void* at(int64_t e) const { return base + e * (int64_t)es; }
+  int64_t layer_base(int l) const {
+    return V * C + ctx * C + (int64_t)l * (4 * C * C + 4 * C + 2 * C * F + F + C + 4 * C);
+  }
+  LayerP layer(int l) const {
+    LayerP r;
+    r.ln1_g = layer_base(l);
+    r.ln1_b = r.ln1_g + C;
+    r.attn_w = r.ln1_b + C;
+    r.attn_b = r.attn_w + 3 * C * C;
+    r.proj_w = r.attn_b + 3 * C;
+    r.proj_b = r.proj_w + C * C;
+    r.ln2_g = r.proj_b + C;
+    r.ln2_b = r.ln2_g + C;
+    r.fc_w = r.ln2_b + C;
+    r.fc_b = r.fc_w + F * C;
+    r.fcproj_w = r.fc_b + F;
+    r.fcproj_b = r.fcproj_w + C * F;
+    return r;
+  }
+  int64_t lnf_g() const { return layer_base((int)L); }
+  int64_t lnf_b() const { return layer_base((int)L) + C; }
+};
+
+Params params_of(const gpt_config* c, const void* p) {
+  return Params{static_cast<const char*>(p), esize(c), c->n_embd, c->n_ff, c->vocab, c->ctx, c->n_layer};
+}
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Workspace of a [B, T] pass.  Decode calls keep K/U in the caller's caches
+// and run the head on B rows only; they add a_last [B, C] and the argmax
+// partial indices.
 struct Plan {
-  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, total;
+  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, alast, pidx, total;
   int ntiles, nblocks;
 };
 
-Plan plan(const gpt_config* c, int B, int T) {
+Plan plan(const gpt_config* c, int B, int T, bool decode) {
   Plan p{};
   const size_t M = (size_t)B * T, C = c->n_embd, F = c->n_ff, es = esize(c);
   p.ntiles = (c->vocab + head_tile_n(c->dtype) - 1) / head_tile_n(c->dtype);
@@ -85,20 +121,150 @@ Plan plan(const gpt_config* c, int B, int T) {
   p.x = take(M * C * 4);
   p.a = take(M * C * es);
   p.q = take(M * C * es);
-  p.k = take(M * C * es);
-  p.v = take(M * C * es);
+  p.k = decode ? 0 : take(M * C * es);
+  p.v = decode ? 0 : take(M * C * es);
   p.o = take(M * C * es);
   p.h = take(M * F * es);
-  p.pmax = take(M * p.ntiles * 4);
-  p.psum = take(M * p.ntiles * 4);
-  p.tgt = take(M * 4);
-  p.tok = take(M * 4);
-  p.bsum = take((size_t)p.nblocks * 2 * 8);
+  const size_t head_rows = decode ? (size_t)B : M;
+  p.pmax = take(head_rows * p.ntiles * 4);
+  p.psum = decode ? 0 : take(head_rows * p.ntiles * 4);
+  p.tgt = decode ? 0 : take(M * 4);
+  p.tok = decode ? 0 : take(M * 4);
+  p.bsum = decode ? 0 : take((size_t)p.nblocks * 2 * 8);
+  p.alast = decode ? take((size_t)B * C * es) : 0;
+  p.pidx = decode ? take((size_t)B * p.ntiles * 4) : 0;
   p.total = off;
   return p;
 }
 
 template <typename P> P* at(void* base, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(base) + off); }
+
+// How a pass stores K/U and attends:
+//   FORWARD: K/U of the batch in the workspace, causal flash attention;
+//   PREFILL: K/U written to the cache at positions 0..T-1, flash attention on the cache;
+//   STEP:    T = 1, K/U appended to the cache at *pos, one-query attention over the cache.
+enum Mode { FORWARD, PREFILL, STEP };
+
+struct Pass {
+  const gpt_config* cfg;
+  Params P;
+  const int32_t* idx;
+  int B, T;
+  Mode mode;
+  const int32_t* pos;        // STEP: device position of the new token
+  void* kc; void* vc;        // PREFILL / STEP caches [L][B][H][Tmax][D]
+  int Tmax;
+  void* ws;
+  Plan pl;
+  hipStream_t st;
+  void* ev_begin; void* ev_end; int which;   // timing hook
+};
+
+hipError_t mark(const Pass& s, int kind, bool last_layer, bool begin) {
+  if (kind != s.which || !last_layer) return hipSuccess;
+  void* ev = begin ? s.ev_begin : s.ev_end;
+  return ev ? hipEventRecord(static_cast<hipEvent_t>(ev), s.st) : hipSuccess;
+}
+
+// Embedding and the L blocks; leaves the fp32 residual stream in ws.x (with
+// no blocks, ws.a already holds ln_f of the embedding).
+int run_blocks(const Pass& s) {
+  const gpt_config* cfg = s.cfg;
+  const Params& P = s.P;
+  const int dt = cfg->dtype, B = s.B, T = s.T, M = B * T, C = cfg->n_embd, F = cfg->n_ff;
+  const int H = cfg->n_head, D = C / H, L = cfg->n_layer;
+  float* x = at<float>(s.ws, s.pl.x);
+  void* a = at<char>(s.ws, s.pl.a);
+  void* q = at<char>(s.ws, s.pl.q);
+  void* o = at<char>(s.ws, s.pl.o);
+  void* h = at<char>(s.ws, s.pl.h);
+  const size_t es = esize(cfg);
+  const long long cache_layer = (long long)B * H * s.Tmax * D;   // elements per layer of each cache
+
+  LnArgs la{};
+  la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps;
+  la.idx = s.idx; la.wte = P.at(0); la.wpe = P.at(P.V * P.C); la.vocab = cfg->vocab; la.ctx = cfg->ctx;
+  la.pos = s.mode == STEP ? s.pos : nullptr;
+  la.x = x; la.in_mul = 1; la.in_add = 0;
+  la.g = P.at(L > 0 ? P.layer(0).ln1_g : P.lnf_g());
+  la.b = P.at(L > 0 ? P.layer(0).ln1_b : P.lnf_b());
+  la.out = a;
+  GPT_TRY(launch_embed_ln(dt, la, s.st));
+  la.idx = nullptr; la.pos = nullptr;
+
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  for (int l = 0; l < L; ++l) {
+    const LayerP w = P.layer(l);
+    const bool last = l == L - 1;
+    void* kbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.k) : static_cast<char*>(s.kc) + l * cache_layer * es;
+    void* vbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.v) : static_cast<char*>(s.vc) + l * cache_layer * es;
+    const long long kv_bh = s.mode == FORWARD ? (long long)T * D : (long long)s.Tmax * D;
+    QKVArgs qa{};
+    qa.A = a; qa.W = P.at(w.attn_w); qa.bias = P.at(w.attn_b);
+    qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
+    qa.q = q; qa.q_bh = (long long)T * D;
+    qa.k = kbuf; qa.k_bh = kv_bh;
+    qa.v = vbuf; qa.v_bh = kv_bh;
+    qa.pos = s.mode == STEP ? s.pos : nullptr;
+    qa.Tk = s.mode == FORWARD ? T : s.Tmax;
+    GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
+    GPT_TRY(launch_qkv(dt, qa, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, true));
+    if (s.mode == STEP) {
+      DecAttnArgs da{};
+      da.q = q; da.k = kbuf; da.v = vbuf; da.kv_bh = kv_bh; da.Tmax = s.Tmax; da.pos = s.pos;
+      da.o = o; da.o_ld = C; da.B = B; da.H = H; da.D = D; da.scale_log2 = scale_log2;
+      GPT_TRY(launch_attention_decode(dt, da, s.st));
+    } else {
+      AttnArgs aa{};
+      aa.q = q; aa.q_bh = (long long)T * D;
+      aa.k = kbuf; aa.k_bh = kv_bh;
+      aa.v = vbuf; aa.v_bh = kv_bh;
+      aa.o = o; aa.o_ld = C;
+      aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D;
+      aa.scale_log2 = scale_log2;
+      GPT_TRY(launch_attention(dt, aa, s.st));
+    }
+    GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, true));
+    GPT_TRY(launch_linear_resid(dt, o, C, P.at(w.proj_w), C, P.at(w.proj_b), M, C, C, x, C, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, false));
+    la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
+    GPT_TRY(launch_layernorm(dt, la, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
+    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, 1, 0, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, true));
+    GPT_TRY(launch_linear_resid(dt, h, F, P.at(w.fcproj_w), F, P.at(w.fcproj_b), M, C, F, x, C, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, false));
+    if (l + 1 < L) {   // ln_1 of the next block (ln_f is applied by the caller)
+      la.g = P.at(P.layer(l + 1).ln1_g); la.b = P.at(P.layer(l + 1).ln1_b);
+      GPT_TRY(launch_layernorm(dt, la, s.st));
+    }
+  }
+  return GPT_OK;
+}
+
+// ln_f of M rows: residual row (r * mul + add) -> dense row r of out.  With no
+// blocks, the embedding kernel applied ln_f already (to every row, into ws.a).
+int final_norm(const Pass& s, int M, int mul, int add, void* out) {
+  const gpt_config* cfg = s.cfg;
+  LnArgs la{};
+  la.M = M; la.C = cfg->n_embd; la.T_seq = s.T; la.eps = cfg->ln_eps;
+  la.x = at<float>(s.ws, s.pl.x); la.in_mul = mul; la.in_add = add;
+  la.g = s.P.at(s.P.lnf_g()); la.b = s.P.at(s.P.lnf_b());
+  la.out = out;
+  return hip_status(launch_layernorm(cfg->dtype, la, s.st));
+}
+
+int check_cache_args(const gpt_config* cfg, void* kc, void* vc, int Tmax, int B) {
+  if (!kc || !vc) return GPT_ERR_NULL;
+  if (Tmax <= 0 || Tmax > cfg->ctx || Tmax > 4096 || B <= 0) return GPT_ERR_SHAPE;
+  return GPT_OK;
+}
 
 }  // namespace
 
@@ -125,7 +291,17 @@ int gpt_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes) {
   if (!bytes) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
   if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
-  *bytes = plan(cfg, B, T).total;
+  *bytes = plan(cfg, B, T, false).total;
+  return GPT_OK;
+}
+
+int gpt_decode_workspace_bytes(const gpt_config* cfg, int B, int Tp, size_t* bytes) {
+  const int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!bytes) return GPT_ERR_NULL;
+  if (B <= 0 || Tp <= 0) return GPT_ERR_SHAPE;
+  if (Tp > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  *bytes = plan(cfg, B, Tp, true).total;   // covers the step's [B, 1] plan as well
   return GPT_OK;
 }
 
@@ -158,104 +334,89 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
   if (!params || !idx || !ws) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
   if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
-  if ((long long)B * T > (1LL << 30)) return GPT_ERR_SHAPE;
-  const Plan p = plan(cfg, B, T);
-  if (ws_bytes < p.total) return GPT_ERR_WORKSPACE;
+  if ((long long)B * T > (1LL << 24)) return GPT_ERR_SHAPE;
+  const Plan pl = plan(cfg, B, T, false);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // Records the caller's events around one launch (timing hook; no-op by default).
-  auto mark = [&](int kind, bool last_layer, bool begin) -> hipError_t {
-    if (kind != which || !last_layer) return hipSuccess;
-    void* ev = begin ? ev_begin : ev_end;
-    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev), st) : hipSuccess;
-  };
-  const int dt = cfg->dtype, M = B * T, C = cfg->n_embd, F = cfg->n_ff, H = cfg->n_head, D = C / H;
-  const int L = cfg->n_layer, V = cfg->vocab;
-  const float eps = cfg->ln_eps;
-  const size_t es = esize(cfg);
-  const char* P = static_cast<const char*>(params);
-  auto poff = [&](int64_t e) { return static_cast<const void*>(P + e * (int64_t)es); };
-  const int64_t V_C = (int64_t)V * C, ctxC = (int64_t)cfg->ctx * C;
-  const int64_t per_layer = 4 * (int64_t)C * C + 4 * C + 2 * (int64_t)C * F + F + C + 4 * C;
-  auto layer_base = [&](int l) { return V_C + ctxC + (int64_t)l * per_layer; };
-  auto lp = [&](int l) {
-    const int64_t b = layer_base(l);
-    LayerP r;
-    r.ln1_g = b;
-    r.ln1_b = r.ln1_g + C;
-    r.attn_w = r.ln1_b + C;
-    r.attn_b = r.attn_w + 3LL * C * C;
-    r.proj_w = r.attn_b + 3LL * C;
-    r.proj_b = r.proj_w + (int64_t)C * C;
-    r.ln2_g = r.proj_b + C;
-    r.ln2_b = r.ln2_g + C;
-    r.fc_w = r.ln2_b + C;
-    r.fc_b = r.fc_w + (int64_t)F * C;
-    r.fcproj_w = r.fc_b + F;
-    r.fcproj_b = r.fcproj_w + (int64_t)C * F;
-    return r;
-  };
-  const int64_t lnf_g = layer_base(L), lnf_b = lnf_g + C;
-
-  float* x = at<float>(ws, p.x);
-  void* a = at<char>(ws, p.a);
-  void* q = at<char>(ws, p.q);
-  void* k = at<char>(ws, p.k);
-  void* v = at<char>(ws, p.v);
-  void* o = at<char>(ws, p.o);
-  void* h = at<char>(ws, p.h);
-  float* pmax = at<float>(ws, p.pmax);
-  float* psum = at<float>(ws, p.psum);
-  float* tgt = at<float>(ws, p.tgt);
-  float* tok = token_loss ? token_loss : at<float>(ws, p.tok);
-  double* bsum = at<double>(ws, p.bsum);
-
-  {
-    const int64_t g0 = L > 0 ? lp(0).ln1_g : lnf_g, b0 = L > 0 ? lp(0).ln1_b : lnf_b;
-    GPT_TRY(launch_embed_ln(dt, M, C, T, eps, idx, poff(0), poff(V_C), V, x, poff(g0), poff(b0), a, st));
+  Pass ps{cfg, params_of(cfg, params), idx, B, T, FORWARD, nullptr, nullptr, nullptr, T, ws, pl,
+          static_cast<hipStream_t>(stream), ev_begin, ev_end, which};
+  s = run_blocks(ps);
+  if (s != GPT_OK) return s;
+  const int M = B * T, V = cfg->vocab, C = cfg->n_embd;
+  void* a = at<char>(ws, pl.a);
+  if (cfg->n_layer > 0) {
+    s = final_norm(ps, M, 1, 0, a);
+    if (s != GPT_OK) return s;
   }
-  AttnArgs aa{};
-  aa.q = q; aa.q_bh = (long long)T * D;
-  aa.k = k; aa.k_bh = (long long)T * D;
-  aa.v = v; aa.v_bh = (long long)T * D;
-  aa.o = o; aa.o_ld = C;
-  aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D;
-  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-  for (int l = 0; l < L; ++l) {
-    const LayerP w = lp(l);
-    QKVArgs qa{};
-    qa.A = a; qa.W = poff(w.attn_w); qa.bias = poff(w.attn_b);
-    qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
-    qa.q = q; qa.q_bh = (long long)T * D;
-    qa.k = k; qa.k_bh = (long long)T * D;
-    qa.v = v; qa.v_bh = (long long)T * D;
-    qa.pos = nullptr;
-    const bool last = l == L - 1;
-    GPT_TRY(mark(GPT_KERNEL_QKV, last, true));
-    GPT_TRY(launch_qkv(dt, qa, st));
-    GPT_TRY(mark(GPT_KERNEL_QKV, last, false));
-    GPT_TRY(mark(GPT_KERNEL_ATTN, last, true));
-    GPT_TRY(launch_attention(dt, aa, st));
-    GPT_TRY(mark(GPT_KERNEL_ATTN, last, false));
-    GPT_TRY(mark(GPT_KERNEL_PROJ, last, true));
-    GPT_TRY(launch_linear_resid(dt, o, C, poff(w.proj_w), C, poff(w.proj_b), M, C, C, x, C, st));
-    GPT_TRY(mark(GPT_KERNEL_PROJ, last, false));
-    GPT_TRY(mark(GPT_KERNEL_LN, last, true));
-    GPT_TRY(launch_layernorm(dt, M, C, eps, x, poff(w.ln2_g), poff(w.ln2_b), a, st));
-    GPT_TRY(mark(GPT_KERNEL_LN, last, false));
-    GPT_TRY(mark(GPT_KERNEL_FC, last, true));
-    GPT_TRY(launch_linear(dt, a, C, poff(w.fc_w), C, poff(w.fc_b), M, F, C, h, F, 1, 0, st));
-    GPT_TRY(mark(GPT_KERNEL_FC, last, false));
-    GPT_TRY(mark(GPT_KERNEL_FCPROJ, last, true));
-    GPT_TRY(launch_linear_resid(dt, h, F, poff(w.fcproj_w), F, poff(w.fcproj_b), M, C, F, x, C, st));
-    GPT_TRY(mark(GPT_KERNEL_FCPROJ, last, false));
-    const int64_t ng = l + 1 < L ? lp(l + 1).ln1_g : lnf_g, nb = l + 1 < L ? lp(l + 1).ln1_b : lnf_b;
-    GPT_TRY(launch_layernorm(dt, M, C, eps, x, poff(ng), poff(nb), a, st));
+  float* tok = token_loss ? token_loss : at<float>(ws, pl.tok);
+  GPT_TRY(mark(ps, GPT_KERNEL_HEAD, true, true));
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(0), M, V, C, logits, V, at<float>(ws, pl.pmax),
+                         at<float>(ws, pl.psum), at<float>(ws, pl.tgt), nullptr, targets, idx, T, ps.st));
+  GPT_TRY(mark(ps, GPT_KERNEL_HEAD, true, false));
+  GPT_TRY(launch_ce_reduce(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), at<float>(ws, pl.tgt),
+                           targets, idx, T, V, tok, at<double>(ws, pl.bsum), mean_loss, ps.st));
+  return GPT_OK;
+}
+
+int gpt_prefill(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int Tp, void* k_cache,
+                void* v_cache, int Tmax, int32_t* pos, int32_t* next_tok, void* last_logits, void* ws,
+                size_t ws_bytes, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!params || !idx || !ws || !pos || !next_tok) return GPT_ERR_NULL;
+  s = check_cache_args(cfg, k_cache, v_cache, Tmax, B);
+  if (s != GPT_OK) return s;
+  if (Tp <= 0) return GPT_ERR_SHAPE;
+  if (Tp > Tmax) return GPT_ERR_SEQ_TOO_LONG;
+  if ((long long)B * Tp > (1LL << 24)) return GPT_ERR_SHAPE;
+  const Plan pl = plan(cfg, B, Tp, true);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
+
+  Pass ps{cfg, params_of(cfg, params), idx, B, Tp, PREFILL, nullptr, k_cache, v_cache, Tmax, ws, pl,
+          static_cast<hipStream_t>(stream), nullptr, nullptr, -1};
+  s = run_blocks(ps);
+  if (s != GPT_OK) return s;
+  // the greedy choice uses the last position of every sequence only
+  void* alast = at<char>(ws, pl.alast);
+  s = cfg->n_layer > 0 ? final_norm(ps, B, Tp, Tp - 1, alast) : GPT_OK;
+  if (s != GPT_OK) return s;
+  if (cfg->n_layer == 0)   // rows of ws.a already hold ln_f: gather the last ones
+    GPT_TRY(hipMemcpy2DAsync(alast, esize(cfg) * cfg->n_embd, at<char>(ws, pl.a) + (size_t)(Tp - 1) * esize(cfg) * cfg->n_embd,
+                             (size_t)Tp * esize(cfg) * cfg->n_embd, esize(cfg) * cfg->n_embd, B, hipMemcpyDeviceToDevice,
+                             ps.st));
+  const int V = cfg->vocab;
+  GPT_TRY(launch_head_ce(cfg->dtype, alast, ps.P.at(0), B, V, cfg->n_embd, last_logits, V, at<float>(ws, pl.pmax),
+                         nullptr, nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1, ps.st));
+  GPT_TRY(launch_argmax_reduce(B, pl.ntiles, at<float>(ws, pl.pmax), at<int32_t>(ws, pl.pidx), next_tok, pos, Tp,
+                               ps.st));
+  return GPT_OK;
+}
+
+int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* tok, int B, int32_t* pos,
+                    void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!params || !tok || !ws || !pos || !next_tok) return GPT_ERR_NULL;
+  s = check_cache_args(cfg, k_cache, v_cache, Tmax, B);
+  if (s != GPT_OK) return s;
+  const Plan pl = plan(cfg, B, 1, true);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
+
+  Pass ps{cfg, params_of(cfg, params), tok, B, 1, STEP, pos, k_cache, v_cache, Tmax, ws, pl,
+          static_cast<hipStream_t>(stream), nullptr, nullptr, -1};
+  s = run_blocks(ps);
+  if (s != GPT_OK) return s;
+  void* a = at<char>(ws, pl.a);
+  if (cfg->n_layer > 0) {
+    s = final_norm(ps, B, 1, 0, a);
+    if (s != GPT_OK) return s;
   }
-  GPT_TRY(mark(GPT_KERNEL_HEAD, true, true));
-  GPT_TRY(launch_head_ce(dt, a, poff(0), M, V, C, logits, V, pmax, psum, tgt, targets, idx, T, st));
-  GPT_TRY(mark(GPT_KERNEL_HEAD, true, false));
-  GPT_TRY(launch_ce_reduce(M, p.ntiles, pmax, psum, tgt, targets, idx, T, V, tok, bsum, mean_loss, st));
+  const int V = cfg->vocab;
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(0), B, V, cfg->n_embd, logits, V, at<float>(ws, pl.pmax), nullptr,
+                         nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1, ps.st));
+  GPT_TRY(launch_argmax_reduce(B, pl.ntiles, at<float>(ws, pl.pmax), at<int32_t>(ws, pl.pidx), next_tok, pos, -1,
+                               ps.st));
   return GPT_OK;
 }
 
@@ -265,8 +426,11 @@ int gpt_debug_layernorm(const gpt_config* cfg, const float* x, const void* g, co
   if (s != GPT_OK) return s;
   if (!x || !g || !b || !out) return GPT_ERR_NULL;
   if (M <= 0) return GPT_ERR_SHAPE;
-  return hip_status(launch_layernorm(cfg->dtype, M, cfg->n_embd, cfg->ln_eps, x, g, b, out,
-                                     static_cast<hipStream_t>(stream)));
+  LnArgs la{};
+  la.M = M; la.C = cfg->n_embd; la.T_seq = 1; la.eps = cfg->ln_eps;
+  la.x = const_cast<float*>(x); la.in_mul = 1; la.in_add = 0;
+  la.g = g; la.b = b; la.out = out;
+  return hip_status(launch_layernorm(cfg->dtype, la, static_cast<hipStream_t>(stream)));
 }
 
 int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const void* bias, int M, int N, int K,
@@ -279,8 +443,8 @@ int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const 
                                   static_cast<hipStream_t>(stream)));
 }
 
-int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* u, int B, int T, void* out,
-                        void* stream) {
+int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* u, int B, int T,
+                        void* out, void* stream) {
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
   if (!q || !k || !u || !out) return GPT_ERR_NULL;

@@ -16,6 +16,33 @@ struct QKVArgs {
   void* k; long long k_bh;             // K [B,H,Tk,D]
   void* v; long long v_bh;             // U [B,H,Tk,D]
   const int32_t* pos;                  // nullable: cache position of t = 0
+  int Tk;                              // K/U rows available; writes at positions >= Tk are dropped
+};
+
+// Embedding (+ first LayerNorm) or LayerNorm of M rows.
+struct LnArgs {
+  int M, C, T_seq;
+  float eps;
+  const int32_t* idx;                  // embedding: token ids [M]
+  const void* wte; const void* wpe;    // embedding tables
+  int vocab, ctx;
+  const int32_t* pos;                  // embedding: nullable device position added to t
+  float* x;                            // residual [rows, C]: written by the embedding, read by LayerNorm
+  int in_mul, in_add;                  // LayerNorm input row = row * in_mul + in_add
+  const void* g; const void* b;        // LayerNorm gain / bias
+  void* out;                           // [M, C] normalised rows
+};
+
+// Attention of one new query per (b, h) over positions 0 .. *pos of the cache.
+struct DecAttnArgs {
+  const void* q;                       // [B, H, D]
+  const void* k; const void* v;        // this layer's caches [B, H, Tmax, D]
+  long long kv_bh;                     // Tmax * D
+  int Tmax;
+  const int32_t* pos;                  // device
+  void* o; int o_ld;                   // [B, o_ld], head h at columns [hD, hD+D)
+  int B, H, D;
+  float scale_log2;
 };
 
 struct AttnArgs {
@@ -27,11 +54,8 @@ struct AttnArgs {
   float scale_log2;                    // log2(e) / sqrt(D)
 };
 
-hipError_t launch_embed_ln(int dtype, int M, int C, int T_seq, float eps, const int32_t* idx, const void* wte,
-                           const void* wpe, int vocab, float* x, const void* g, const void* b, void* out,
-                           hipStream_t st);
-hipError_t launch_layernorm(int dtype, int M, int C, float eps, const float* x, const void* g, const void* b,
-                            void* out, hipStream_t st);
+hipError_t launch_embed_ln(int dtype, const LnArgs& a, hipStream_t st);
+hipError_t launch_layernorm(int dtype, const LnArgs& a, hipStream_t st);
 hipError_t launch_linear(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N,
                          int K, void* out, int ldo, int act, int out_f32, hipStream_t st);
 hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M,
@@ -39,9 +63,17 @@ hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W,
 hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 int head_tile_n(int dtype);
+// Tied head over M token rows.  CE mode (part_idx == NULL): softmax partials
+// and target logits for the next-token loss.  Argmax mode (part_idx != NULL):
+// per-(row, N-tile) maximum and its lowest index; part_sum/tgt unused.
 hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int V, int C, void* logits,
-                          long long ld_logits, float* part_max, float* part_sum, float* tgt, const int32_t* targets,
-                          const int32_t* idx, int T_seq, hipStream_t st);
+                          long long ld_logits, float* part_max, float* part_sum, float* tgt, int32_t* part_idx,
+                          const int32_t* targets, const int32_t* idx, int T_seq, hipStream_t st);
+// Greedy choice per row from the head's argmax partials (lowest index wins
+// ties); then *pos = set_pos if set_pos >= 0, else *pos += 1 (if pos).
+hipError_t launch_argmax_reduce(int M, int ntiles, const float* part_max, const int32_t* part_idx, int32_t* next_tok,
+                                int32_t* pos, int set_pos, hipStream_t st);
+hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t st);
 // Per-token loss from the head partials, then a deterministic mean.
 int ce_reduce_blocks(int M);
 hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,

@@ -16,24 +16,22 @@ namespace gptmi {
 
 // NCH = number of 4-float chunks per lane; C <= 256 * NCH.
 template <typename T, int NCH, bool EMBED>
-__global__ void __launch_bounds__(256) ln_rows_kernel(
-    int M, int C, int T_seq, float eps,
-    const int32_t* __restrict__ idx, const T* __restrict__ wte, const T* __restrict__ wpe, int vocab,
-    float* __restrict__ x,                 // [M, C] fp32 residual (written when EMBED, else read)
-    const T* __restrict__ g, const T* __restrict__ b,
-    T* __restrict__ out)                   // [M, C] normalised, compute dtype
-{
+__global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+  if (row >= a.M) return;
+  const int C = a.C;
+  const T* g = reinterpret_cast<const T*>(a.g);
+  const T* bta = reinterpret_cast<const T*>(a.b);
   float v[NCH][4];
-  float* xr = x + (size_t)row * C;
   if (EMBED) {
-    int tok = idx[row];
-    tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);  // ids outside [0,V) violate the contract; never read out of bounds
-    const int t = row % T_seq;
-    const T* er = wte + (size_t)tok * C;
-    const T* pr = wpe + (size_t)t * C;
+    float* xr = a.x + (size_t)row * C;
+    int tok = a.idx[row];
+    tok = tok < 0 ? 0 : (tok >= a.vocab ? a.vocab - 1 : tok);  // ids outside [0,V) violate the contract; never read out of bounds
+    int t = row % a.T_seq + (a.pos ? *a.pos : 0);
+    t = t < 0 ? 0 : (t < a.ctx ? t : a.ctx - 1);                // positions outside the table violate the contract
+    const T* er = reinterpret_cast<const T*>(a.wte) + (size_t)tok * C;
+    const T* pr = reinterpret_cast<const T*>(a.wpe) + (size_t)t * C;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = (j * 64 + lane) * 4;
@@ -44,6 +42,7 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(
       }
     }
   } else {
+    const float* xr = a.x + (size_t)(row * a.in_mul + a.in_add) * C;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = (j * 64 + lane) * 4;
@@ -65,53 +64,43 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) { float d = v[j][e] - mean; s2 += d * d; }
   const float var = wave_sum(s2) / (float)C;
-  const float rstd = 1.0f / sqrtf(var + eps);
-  T* orow = out + (size_t)row * C;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  T* orow = reinterpret_cast<T*>(a.out) + (size_t)row * C;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = (j * 64 + lane) * 4;
     if (c < C) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        orow[c + e] = from_f32<T>((v[j][e] - mean) * rstd * to_f32(g[c + e]) + to_f32(b[c + e]));
+        orow[c + e] = from_f32<T>((v[j][e] - mean) * rstd * to_f32(g[c + e]) + to_f32(bta[c + e]));
     }
   }
 }
 
 template <typename T, bool EMBED>
-static hipError_t launch_ln_t(int M, int C, int T_seq, float eps, const int32_t* idx, const T* wte, const T* wpe,
-                              int vocab, float* x, const T* g, const T* b, T* out, hipStream_t st) {
-  dim3 grid((M + 3) / 4), block(256);
-  if (C <= 256)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 1, EMBED>), grid, block, 0, st, M, C, T_seq, eps, idx, wte, wpe, vocab, x, g, b, out);
-  else if (C <= 512)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 2, EMBED>), grid, block, 0, st, M, C, T_seq, eps, idx, wte, wpe, vocab, x, g, b, out);
-  else if (C <= 1024)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 4, EMBED>), grid, block, 0, st, M, C, T_seq, eps, idx, wte, wpe, vocab, x, g, b, out);
-  else if (C <= 2048)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 8, EMBED>), grid, block, 0, st, M, C, T_seq, eps, idx, wte, wpe, vocab, x, g, b, out);
+static hipError_t launch_ln_t(const LnArgs& a, hipStream_t st) {
+  dim3 grid((a.M + 3) / 4), block(256);
+  if (a.C <= 256)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 1, EMBED>), grid, block, 0, st, a);
+  else if (a.C <= 512)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 2, EMBED>), grid, block, 0, st, a);
+  else if (a.C <= 1024)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 4, EMBED>), grid, block, 0, st, a);
+  else if (a.C <= 2048)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 8, EMBED>), grid, block, 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_embed_ln(int dtype, int M, int C, int T_seq, float eps, const int32_t* idx, const void* wte,
-                           const void* wpe, int vocab, float* x, const void* g, const void* b, void* out,
-                           hipStream_t st) {
-  if (dtype == 0)
-    return launch_ln_t<float, true>(M, C, T_seq, eps, idx, (const float*)wte, (const float*)wpe, vocab, x,
-                                    (const float*)g, (const float*)b, (float*)out, st);
-  return launch_ln_t<bf16, true>(M, C, T_seq, eps, idx, (const bf16*)wte, (const bf16*)wpe, vocab, x,
-                                 (const bf16*)g, (const bf16*)b, (bf16*)out, st);
+hipError_t launch_embed_ln(int dtype, const LnArgs& a, hipStream_t st) {
+  if (dtype == 0) return launch_ln_t<float, true>(a, st);
+  return launch_ln_t<bf16, true>(a, st);
 }
 
-hipError_t launch_layernorm(int dtype, int M, int C, float eps, const float* x, const void* g, const void* b,
-                            void* out, hipStream_t st) {
-  if (dtype == 0)
-    return launch_ln_t<float, false>(M, C, 1, eps, nullptr, nullptr, nullptr, 0, const_cast<float*>(x),
-                                     (const float*)g, (const float*)b, (float*)out, st);
-  return launch_ln_t<bf16, false>(M, C, 1, eps, nullptr, nullptr, nullptr, 0, const_cast<float*>(x),
-                                  (const bf16*)g, (const bf16*)b, (bf16*)out, st);
+hipError_t launch_layernorm(int dtype, const LnArgs& a, hipStream_t st) {
+  if (dtype == 0) return launch_ln_t<float, false>(a, st);
+  return launch_ln_t<bf16, false>(a, st);
 }
 
 }  // namespace gptmi

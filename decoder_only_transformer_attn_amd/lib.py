@@ -40,6 +40,9 @@ SIGNATURES = {
     "gpt_debug_layernorm": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _vp, _vp]),
     "gpt_debug_linear": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "gpt_debug_attention": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "gpt_decode_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt_prefill": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_decode_step": (_c_int, [_CFG, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -184,6 +187,56 @@ class Forward:
     def __call__(self, params, idx, targets=None, stream=None):
         forward(self.cfg, params, idx, targets, self.logits, self.token_loss, self.mean_loss, self.ws, stream)
         return self.logits, self.token_loss, self.mean_loss
+
+
+def decode_workspace_bytes(cfg, B: int, Tp: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().gpt_decode_workspace_bytes(ctypes.byref(cfg_c(cfg)), B, Tp, ctypes.byref(out)))
+    return int(out.value)
+
+
+def prefill(cfg, params, idx, k_cache, v_cache, pos, next_tok, last_logits=None, ws=None, stream=None) -> None:
+    """Enqueue gpt_prefill.  idx int32 [B, Tp]; caches [L, B, H, Tmax, D]; pos int32 [1]; next_tok int32 [B]."""
+    B, Tp = idx.shape
+    Tmax = k_cache.shape[3] if k_cache.dim() == 5 else 0
+    check(load().gpt_prefill(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, Tp, _ptr(k_cache), _ptr(v_cache),
+                             Tmax, _ptr(pos), _ptr(next_tok), _ptr(last_logits), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def decode_step(cfg, params, tok, k_cache, v_cache, pos, next_tok, logits=None, ws=None, stream=None) -> None:
+    """Enqueue gpt_decode_step.  tok, next_tok int32 [B] (may be the same tensor)."""
+    B = tok.shape[0]
+    Tmax = k_cache.shape[3] if k_cache.dim() == 5 else 0
+    check(load().gpt_decode_step(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(tok), B, _ptr(pos), _ptr(k_cache),
+                                 _ptr(v_cache), Tmax, _ptr(next_tok), _ptr(logits), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+class Decoder:
+    """Caches, position counter and workspace for greedy decoding of B
+    sequences with prompts of Tp tokens and at most Tmax cached positions."""
+
+    def __init__(self, cfg, B: int, Tp: int, Tmax: int, device="cuda"):
+        import torch
+        H = cfg.n_head
+        D = cfg.n_embd // H
+        self.cfg, self.B, self.Tp, self.Tmax = cfg, B, Tp, Tmax
+        shape = (max(cfg.n_layer, 1), B, H, Tmax, D)
+        self.k_cache = torch.zeros(shape, dtype=torch_dtype(cfg), device=device)
+        self.v_cache = torch.zeros(shape, dtype=torch_dtype(cfg), device=device)
+        self.pos = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.tok = torch.zeros((B,), dtype=torch.int32, device=device)
+        self.ws = torch.empty(decode_workspace_bytes(cfg, B, Tp), dtype=torch.uint8, device=device)
+
+    def prefill(self, params, idx, last_logits=None, stream=None):
+        prefill(self.cfg, params, idx, self.k_cache, self.v_cache, self.pos, self.tok, last_logits, self.ws, stream)
+        return self.tok
+
+    def step(self, params, logits=None, stream=None):
+        """Feed the last chosen tokens; self.tok is overwritten with the next ones."""
+        decode_step(self.cfg, params, self.tok, self.k_cache, self.v_cache, self.pos, self.tok, logits, self.ws, stream)
+        return self.tok
 
 
 def debug_layernorm(cfg, x, g, b, out, stream=None) -> None:

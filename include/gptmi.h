@@ -117,6 +117,44 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
                       const int32_t* targets, void* logits, float* token_loss, float* mean_loss,
                       void* ws, size_t ws_bytes, void* stream, void* ev_begin, void* ev_end, int which);
 
+/* ---- greedy decoding with a key/value cache ----
+ * "预训练一个 Mini GPT" (KV cache section, 第7步): a new token computes only
+ * its own q, k and u; the keys and values of earlier positions are read back
+ * from a per-layer cache.  "GPT-1学习笔记" §6.1: the next token is the argmax of
+ * the last position's logits (lowest index on ties).
+ *
+ * Cache layout (device, caller-owned, cfg->dtype): k_cache and v_cache each
+ * [L][B][H][Tmax][D]; row t of (l, b, h) holds position t.  Requires
+ * 1 <= Tmax <= min(ctx, 4096).  pos (device, int32[1]) is the number of cache
+ * positions already filled, the same for every sequence; the library updates
+ * it on the device, so a decode loop needs no host round trip.
+ * A position outside [0, Tmax) at a step violates the contract: nothing is
+ * written outside the caches and the results are unspecified. */
+
+/* Workspace bytes for gpt_prefill on a [B, Tp] prompt batch; it also covers
+ * gpt_decode_step at the same B (host only). */
+int gpt_decode_workspace_bytes(const gpt_config* cfg, int B, int Tp, size_t* bytes);
+
+/* Prefill: the forward pass over prompts idx (device, int32 [B, Tp]) at
+ * positions 0..Tp-1, storing every layer's K and U in the caches, then ln_f
+ * and the tied head on the last position of each sequence only.
+ *   next_tok    (device) int32 [B]: argmax of the last position's logits.
+ *   last_logits (device, nullable) [B, V] in cfg->dtype.
+ *   pos         (device) int32[1]: set to Tp.
+ * Requires 1 <= Tp <= Tmax; else GPT_ERR_SEQ_TOO_LONG. */
+int gpt_prefill(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int Tp,
+                void* k_cache, void* v_cache, int Tmax, int32_t* pos, int32_t* next_tok,
+                void* last_logits, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step: tok (device, int32 [B]) enters at position p = *pos; its
+ * K and U are appended at row p of every layer's cache and its query attends
+ * over rows 0..p.  Writes next_tok (device, int32 [B]; may alias tok) and,
+ * if logits (device, [B, V], cfg->dtype) is not NULL, the step's logits; then
+ * *pos = p + 1.  ws as for gpt_prefill at this B (or larger). */
+int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* tok, int B, int32_t* pos,
+                    void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits,
+                    void* ws, size_t ws_bytes, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* gpt_status_string(int status);
 

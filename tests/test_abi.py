@@ -100,3 +100,34 @@ def test_workspace_grows_with_batch():
     assert 3.5 * a < b < 4.5 * a
     with pytest.raises(lib.GPTError):
         lib.workspace_bytes(synth.GPT2, 1, 1025)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="dummy-pointer validation tests run only without a GPU")
+def test_decode_validation_before_any_hip_call():
+    L = lib.load()
+    m = synth.MICRO                                   # ctx 12
+    c = ctypes.byref(lib.cfg_c(m))
+    big = 1 << 30
+
+    def pre(B=2, Tp=4, kc=1, vc=1, Tmax=12, pos=1, nt=1, ws=1, ws_bytes=big, idx=1):
+        return L.gpt_prefill(c, 1, idx, B, Tp, kc, vc, Tmax, pos, nt, None, ws, ws_bytes, None)
+
+    def step(B=2, kc=1, vc=1, Tmax=12, pos=1, nt=1, tok=1, ws=1, ws_bytes=big):
+        return L.gpt_decode_step(c, 1, tok, B, pos, kc, vc, Tmax, nt, None, ws, ws_bytes, None)
+
+    assert pre(kc=None) == -1 and pre(pos=None) == -1 and pre(nt=None) == -1 and pre(idx=None) == -1
+    assert pre(Tmax=13) == -4                         # cache longer than the position table
+    assert pre(Tmax=0) == -4 and pre(B=0) == -4 and pre(Tp=0) == -4
+    assert pre(Tp=5, Tmax=4) == -3                    # prompt longer than the cache
+    assert pre(ws_bytes=16) == -5
+    assert step(vc=None) == -1 and step(tok=None) == -1 and step(pos=None) == -1
+    assert step(Tmax=13) == -4 and step(B=0) == -4
+    assert step(ws_bytes=16) == -5
+
+
+def test_decode_workspace_covers_step_and_is_smaller_than_forward():
+    pre = lib.decode_workspace_bytes(synth.GPT2, 64, 128)
+    assert pre < lib.workspace_bytes(synth.GPT2, 64, 128)   # no K/U copies, head on B rows only
+    assert lib.decode_workspace_bytes(synth.GPT2, 64, 1) <= pre
+    with pytest.raises(lib.GPTError):
+        lib.decode_workspace_bytes(synth.GPT2, 1, 1025)
