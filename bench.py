@@ -1,23 +1,31 @@
 #!/usr/bin/env python3
-"""Benchmark: GPT-2 124M bf16 forward + next-token cross-entropy on one MI355X.
+"""Benchmark of the GPT-2-style forward pass (and greedy decode) on one MI355X.
 
-One step = one gpt_forward call over one [B, T] batch of synthetic token ids
-(uniform in [0, V)) with seeded N(0, 0.02) weights, inputs resident in HBM:
-embedding, 12 pre-norm blocks, ln_f, tied head (bf16 logits written) and the
-fused cross-entropy.  Prints one JSON line.
+Default (workload 3): GPT-2 124M bf16, B=8, T=1024.  One step = one
+gpt_forward call over one batch of synthetic token ids (uniform in [0, V))
+with seeded N(0, 0.02) weights, inputs resident in HBM: embedding, 12
+pre-norm blocks, ln_f, tied head (bf16 logits written) and the fused
+cross-entropy.  Workload 4: B=32 without logits.  Workload 5: greedy decode,
+B=64 prompts of 128 tokens then 128 steps (each step replayed from a HIP
+graph); one step = one decode step.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4|5] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # plain device copy of known size, for HBM counter scaling
 
-The roofline object reports the tied head + cross-entropy kernel (the
-largest single launch, 29% of the step's FLOPs) from hipEvents recorded
-around its launch inside every timed step.  cpu_baseline times the fp64
-oracle on one sequence of the same workload on the host cores.
+Step times come from hipEvents recorded on the library's stream at every
+step boundary.  The roofline object reports the dominant kernel (the tied
+head) from hipEvents recorded immediately around its launch inside every
+timed step.  cpu_baseline times the fp64 oracle on a bounded sample of the
+same workload on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -27,10 +35,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+# HBM bytes per launch of the head kernel at B=8, T=1024, from two rocprofv3
+# --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
+# factor the same counters read for a plain device copy of known size.  Valid
+# only for the kernel source it was taken on: null once gemm.hip changes.
+HEAD_TRAFFIC = {"gemm_src_sha256": "28169d60a13f67b9079fac789de21263dbd7163ce47c1c37a709c6f6c96b83ba",
+                "bytes": 1839769064}
 
 
-def flops_per_step(cfg, B, T):
+def src_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def forward_flops(cfg, B, T):
     """Algorithmic FLOPs: 2MNK for c_attn, c_proj, c_fc, mlp.c_proj and the tied
     head, plus causal attention 4*D*B*H*T(T+1)/2 (the masked half excluded)."""
     M, C, F, V, L, H = B * T, cfg.n_embd, cfg.n_ff, cfg.vocab, cfg.n_layer, cfg.n_head
@@ -41,46 +61,107 @@ def flops_per_step(cfg, B, T):
     return gemm + head + attn, head
 
 
-def cpu_baseline(cfg, params, ids, n_seq):
-    """Time the fp64 oracle on the first n_seq sequences (bounded sample)."""
+def decode_step_bytes(cfg, B, p):
+    """Algorithmic HBM bytes of one decode step at position p (bf16): every
+    parameter except the position table read once (the token table once,
+    shared by the embedding rows and the head), the cache rows 0..p of K and U
+    read, row p written, and the small activations ignored."""
+    C, F, V, L, H = cfg.n_embd, cfg.n_ff, cfg.vocab, cfg.n_layer, cfg.n_head
+    per_layer = 4 * C * C + 4 * C + 2 * C * F + F + C + 4 * C
+    weights = 2 * (V * C + L * per_layer + 2 * C)
+    kv_row = 2 * 2 * L * B * C            # K and U, all layers, one position, bf16
+    return weights + kv_row * (p + 1) + kv_row
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        blas = ",".join(sorted({f"{d.get('internal_api')}" for d in info if d.get("user_api") == "blas"})) or blas
+    except Exception:
+        pass
+    return model, blas
+
+
+def cpu_baseline_forward(cfg, params, ids, n_seq):
+    """Time the fp64 oracle forward (logits + loss) on the first n_seq sequences."""
+    from decoder_only_transformer_attn_amd import synth
+    from oracle import gpt_oracle as O
     threads = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_limits
-        ctx = threadpool_limits(limits=threads)
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover
-        ctx = None
-    from decoder_only_transformer_attn_amd import synth
-    from oracle import gpt_oracle as O
+        limiter = None
     P = synth.unpack_f64(cfg, params)
     t0 = time.perf_counter()
     O.forward(P, ids[:n_seq], cfg.n_head, cfg.ln_eps, want_logits=True)
     dt = time.perf_counter() - t0
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
+    if limiter is not None and hasattr(limiter, "restore_original_limits"):
+        limiter.restore_original_limits()
+    model, blas = cpu_info()
     toks = n_seq * ids.shape[1]
     return {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_seq} of {ids.shape[0]} sequences x {ids.shape[1]} tokens, fp64 numpy forward + logits "
-                      f"+ loss, {dt:.1f} s"}
+            "sample": f"{n_seq} of {ids.shape[0]} sequences x {ids.shape[1]} tokens, fp64 numpy forward with "
+                      f"logits and loss, {dt:.1f} s",
+            "cpu": model, "blas": blas}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=[3, 4])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(sequences shard data-parallel across GPUs by design, not implemented here)"}))
-        sys.exit(2)
+def cpu_baseline_decode(cfg, params, prompt, steps, n_seq):
+    """Time the oracle's cached greedy decode on n_seq of the sequences."""
+    from decoder_only_transformer_attn_amd import synth
+    from oracle import gpt_oracle as O
+    threads = len(os.sched_getaffinity(0))
+    P = synth.unpack_f64(cfg, params)
+    O.greedy_cached(P, prompt[:n_seq], 1, cfg.n_head, cfg.ln_eps)        # warm
+    t0 = time.perf_counter()
+    O.greedy_cached(P, prompt[:n_seq], steps, cfg.n_head, cfg.ln_eps)
+    dt = time.perf_counter() - t0
+    model, blas = cpu_info()
+    return {"value": round(n_seq * steps / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {prompt.shape[0]} sequences, prompt {prompt.shape[1]} + {steps} cached greedy "
+                      f"steps, fp64 numpy, {dt:.1f} s (prefill included)",
+            "cpu": model, "blas": blas}
 
+
+class Events:
+    """hipEvent_t handles from libamdhip64 (torch's Event does not expose its handle)."""
+
+    def __init__(self, n):
+        from decoder_only_transformer_attn_amd import lib
+        self.h = lib.HipEvents(n)
+        self.hip = self.h.hip
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.ev = self.h.ev
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        return self.h.elapsed_ms(a, b)
+
+    def close(self):
+        self.h.close()
+
+
+def bench_forward(args, w):
     import torch
     from decoder_only_transformer_attn_amd import lib, synth
-
-    lib.load()
-    w = synth.WORKLOADS[args.workload]
     cfg, B, T = w["cfg"], w["B"], w["T"]
     want_logits = args.workload == 3
     params = synth.make_params(cfg, seed=42, cfg_id=args.workload)
@@ -89,36 +170,39 @@ def main():
     idx = torch.from_numpy(ids).cuda()
     fwd = lib.Forward(cfg, B, T, want_logits=want_logits)
     stream = torch.cuda.current_stream()
-
-    ev = lib.HipEvents(2 * args.steps + 2)
+    K = args.steps
+    ev = Events(3 * K + 1)          # step boundaries 0..K, then head begin/end per step
     for _ in range(args.warmup):
         fwd(dev_params, idx)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    hip = ev.hip
-    hip.hipEventRecord.argtypes = [lib.ctypes.c_void_p, lib.ctypes.c_void_p]
-    hip.hipEventRecord(ev.ev[-2], stream.cuda_stream)
-    for s in range(args.steps):
+    ev.record(0, stream.cuda_stream)
+    for s in range(K):
         lib.forward_timed(cfg, dev_params, idx, None, fwd.logits, fwd.token_loss, fwd.mean_loss, fwd.ws,
-                          ev.ev[2 * s], ev.ev[2 * s + 1], "head")
-    hip.hipEventRecord(ev.ev[-1], stream.cuda_stream)
+                          ev.ev[K + 1 + 2 * s], ev.ev[K + 2 + 2 * s], "head")
+        ev.record(s + 1, stream.cuda_stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = ev.elapsed_ms(len(ev.ev) - 2, len(ev.ev) - 1)
-    head_ms = float(np.mean([ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.steps)]))
+    total_ms = ev.ms(0, K)
+    step_ms = [ev.ms(s, s + 1) for s in range(K)]
+    head_ms = float(np.mean([ev.ms(K + 1 + 2 * s, K + 2 + 2 * s) for s in range(K)]))
     ev.close()
     loss = float(fwd.mean_loss.item())
 
-    ms = total_ms / args.steps
+    ms = total_ms / K
     tokens = B * T
-    flops, head_flops = flops_per_step(cfg, B, T)
+    flops, head_flops = forward_flops(cfg, B, T)
     achieved = head_flops / (head_ms * 1e-3) / 1e12
+    traffic = None
+    if args.workload == 3 and HEAD_TRAFFIC["bytes"] and HEAD_TRAFFIC["gemm_src_sha256"] == src_sha(
+            "decoder_only_transformer_attn_amd/csrc/gemm.hip"):
+        traffic = HEAD_TRAFFIC["bytes"]
     out = {
         "metric": "tokens/s fwd+loss, GPT-2 124M bf16 B=8 T=1024; % of MFMA peak",
         "value": round(tokens / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
@@ -128,17 +212,143 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "global_batch": B, "seq_len": T, "parallelism": "single-gpu",
                    "logits_written": want_logits},
+        "step_ms": {"median": round(pct(step_ms, 50), 4), "min": round(min(step_ms), 4),
+                    "p90": round(pct(step_ms, 90), 4)},
         "mfma_frac_end_to_end": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "tflops_end_to_end": round(flops / (ms * 1e-3) / 1e12, 1),
+        "flops_per_step": flops,
         "loss": round(loss, 5),
         "wall_s_timed": round(t_wall, 3),
-        "roofline": {"bound": "mfma", "kernel": "head_ce_kernel (tied head GEMM + CE partials)",
+        "roofline": {"bound": "mfma", "kernel": "head_ce_dma_kernel (tied head GEMM + CE partials + bf16 logits)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(head_ms, 4), "flops_per_launch": head_flops},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, params, ids, 1)
+        out["cpu_baseline"] = cpu_baseline_forward(cfg, params, ids, args.cpu_seqs)
+    return out
+
+
+def bench_decode(args, w):
+    import torch
+    from decoder_only_transformer_attn_amd import lib, synth
+    cfg, B, Tp = w["cfg"], w["B"], w["T"]
+    n_steps, Tmax = 128, 256
+    params = synth.make_params(cfg, seed=42, cfg_id=5)
+    prompt = synth.make_ids(cfg, B, Tp, seed=42, cfg_id=5)
+    dev_params = lib.params_to_device(cfg, synth.pack(cfg, params))
+    idx = torch.from_numpy(prompt).cuda()
+    dec = lib.Decoder(cfg, B, Tp, Tmax)
+    stream = torch.cuda.current_stream()
+
+    # one step captured in a HIP graph (the position lives on the device, so
+    # the same graph serves every step)
+    dec.prefill(dev_params, idx)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dec.step(dev_params)
+    # the capture did not run the step; rewind and warm up
+    for _ in range(max(args.warmup, 1)):
+        dec.prefill(dev_params, idx)
+        for _ in range(n_steps):
+            graph.replay()
+    torch.cuda.synchronize()
+
+    R = max(args.steps // 10, 1)     # repetitions of (prefill + 128 steps)
+    ev = Events(R * (n_steps + 2))
+    t_wall = time.perf_counter()
+    k = 0
+    marks = []
+    for r in range(R):
+        ev.record(k, stream.cuda_stream)
+        dec.prefill(dev_params, idx)
+        ev.record(k + 1, stream.cuda_stream)
+        for s in range(n_steps):
+            graph.replay()
+            ev.record(k + 2 + s, stream.cuda_stream)
+        marks.append(k)
+        k += n_steps + 2
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    prefill_ms = [ev.ms(m, m + 1) for m in marks]
+    steps_ms = [ev.ms(m + 1, m + 1 + n_steps) for m in marks]
+    step_ms = [ev.ms(m + 1 + s, m + 2 + s) for m in marks for s in range(n_steps)]
+    ev.close()
+    pos = int(dec.pos.item())
+    assert pos == Tp + n_steps, pos
+
+    t_steps = float(np.mean(steps_ms))
+    ms = t_steps / n_steps
+    bytes_total = sum(decode_step_bytes(cfg, B, Tp + s) for s in range(n_steps))
+    achieved = bytes_total / (t_steps * 1e-3) / 1e9
+    pf_flops = forward_flops(cfg, B, Tp)[0] - 2 * B * Tp * cfg.vocab * cfg.n_embd + 2 * B * cfg.vocab * cfg.n_embd
+    pf_ms = float(np.mean(prefill_ms))
+    out = {
+        "metric": "decode tokens/s, GPT-2 124M bf16 B=64 prompt 128 + 128 greedy steps; % of HBM roofline",
+        "value": round(B * n_steps / (t_steps * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n_steps * R,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "global_batch": B, "seq_len": Tp, "decode_steps": n_steps,
+                   "cache_len": Tmax, "parallelism": "single-gpu", "step": "hip graph replay"},
+        "step_ms": {"median": round(pct(step_ms, 50), 4), "min": round(min(step_ms), 4),
+                    "p90": round(pct(step_ms, 90), 4)},
+        "prefill": {"ms": round(pf_ms, 4), "tokens_per_s": round(B * Tp / (pf_ms * 1e-3), 1),
+                    "flops": pf_flops, "mfma_frac": round(pf_flops / (pf_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {"bound": "hbm", "kernel": "whole decode step (weights once + K/U cache rows 0..p)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_step_avg": round(bytes_total / n_steps)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(cfg, params, prompt, 32, 8)
+    return out
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, ten times: the HBM byte counters
+    of this launch scale the head kernel's counters to bytes."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=[3, 4, 5])
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(sequences shard data-parallel across GPUs by design, not implemented here)"}))
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from decoder_only_transformer_attn_amd import lib, synth
+    lib.load()
+    w = synth.WORKLOADS[args.workload]
+    out = bench_decode(args, w) if args.workload == 5 else bench_forward(args, w)
     print(json.dumps(out), flush=True)
 
 

@@ -14,6 +14,23 @@
 
 namespace gptmi {
 
+// Four consecutive elements as one 16-byte (fp32) or 8-byte (bf16) access.
+__device__ __forceinline__ void load4(const float* p, float (&o)[4]) {
+  const float4 q = *reinterpret_cast<const float4*>(p);
+  o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float (&o)[4]) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(q.x << 16); o[1] = __uint_as_float(q.x & 0xffff0000u);
+  o[2] = __uint_as_float(q.y << 16); o[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+__device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16* p, const float (&v)[4]) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
 // NCH = number of 4-float chunks per lane; C <= 256 * NCH.
 template <typename T, int NCH, bool EMBED>
 __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
@@ -21,35 +38,35 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.M) return;
   const int C = a.C;
-  const T* g = reinterpret_cast<const T*>(a.g);
-  const T* bta = reinterpret_cast<const T*>(a.b);
+  const T* __restrict__ g = reinterpret_cast<const T*>(a.g);
+  const T* __restrict__ bta = reinterpret_cast<const T*>(a.b);
   float v[NCH][4];
   if (EMBED) {
-    float* xr = a.x + (size_t)row * C;
+    float* __restrict__ xr = a.x + (size_t)row * C;
     int tok = a.idx[row];
     tok = tok < 0 ? 0 : (tok >= a.vocab ? a.vocab - 1 : tok);  // ids outside [0,V) violate the contract; never read out of bounds
     int t = row % a.T_seq + (a.pos ? *a.pos : 0);
     t = t < 0 ? 0 : (t < a.ctx ? t : a.ctx - 1);                // positions outside the table violate the contract
-    const T* er = reinterpret_cast<const T*>(a.wte) + (size_t)tok * C;
-    const T* pr = reinterpret_cast<const T*>(a.wpe) + (size_t)t * C;
+    const T* __restrict__ er = reinterpret_cast<const T*>(a.wte) + (size_t)tok * C;
+    const T* __restrict__ pr = reinterpret_cast<const T*>(a.wpe) + (size_t)t * C;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = (j * 64 + lane) * 4;
       if (c < C) {
+        float e4[4], p4[4];
+        load4(er + c, e4);
+        load4(pr + c, p4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[j][e] = to_f32(er[c + e]) + to_f32(pr[c + e]);
-        *reinterpret_cast<float4*>(xr + c) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+        for (int e = 0; e < 4; ++e) v[j][e] = e4[e] + p4[e];
+        store4(xr + c, v[j]);
       }
     }
   } else {
-    const float* xr = a.x + (size_t)(row * a.in_mul + a.in_add) * C;
+    const float* __restrict__ xr = a.x + (size_t)(row * a.in_mul + a.in_add) * C;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = (j * 64 + lane) * 4;
-      if (c < C) {
-        float4 q = *reinterpret_cast<const float4*>(xr + c);
-        v[j][0] = q.x; v[j][1] = q.y; v[j][2] = q.z; v[j][3] = q.w;
-      }
+      if (c < C) load4(xr + c, v[j]);
     }
   }
   float s = 0.f;
@@ -65,14 +82,17 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
       for (int e = 0; e < 4; ++e) { float d = v[j][e] - mean; s2 += d * d; }
   const float var = wave_sum(s2) / (float)C;
   const float rstd = 1.0f / sqrtf(var + a.eps);
-  T* orow = reinterpret_cast<T*>(a.out) + (size_t)row * C;
+  T* __restrict__ orow = reinterpret_cast<T*>(a.out) + (size_t)row * C;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = (j * 64 + lane) * 4;
     if (c < C) {
+      float g4[4], b4[4], o4[4];
+      load4(g + c, g4);
+      load4(bta + c, b4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        orow[c + e] = from_f32<T>((v[j][e] - mean) * rstd * to_f32(g[c + e]) + to_f32(bta[c + e]));
+      for (int e = 0; e < 4; ++e) o4[e] = (v[j][e] - mean) * rstd * g4[e] + b4[e];
+      store4(orow + c, o4);
     }
   }
 }

@@ -54,6 +54,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
+    # torch ships its own HIP runtime; importing it first makes the library
+    # bind to that same runtime (one HIP runtime per process, shared streams)
+    import torch  # noqa: F401
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m decoder_only_transformer_attn_amd.build`")
     lib = ctypes.CDLL(p)

@@ -20,6 +20,9 @@
  *  - Every host-checkable condition is checked before the first HIP call; on
  *    an error nothing is enqueued and the outputs are untouched.  A HIP
  *    launch failure returns GPT_ERR_HIP; outputs are then undefined.
+ *  - Device buffers must be 16-byte aligned (every HIP or torch allocation
+ *    is); the parameter blob's tensors then are too, since every tensor
+ *    size is a multiple of C or n_ff.
  *  - Matrices are row-major [out, in]; a linear layer is y = x W^T + b.
  *  - dtype GPT_F32: parameters, activations and outputs fp32, MFMA in fp32.
  *    dtype GPT_BF16: parameters, activations and logits bf16 (round to

@@ -176,3 +176,40 @@ def test_gpt2_bf16_decode_agrees_with_forward(gpt2_decode_run):
     err = (zstep.float() - ref).abs().max().item()
     print(f"decode vs forward max|dlogit| {err:.4f}")
     assert err <= 1e-1
+
+
+def test_decode_step_graph_replay_matches_eager():
+    # one decode step captured in a HIP graph and replayed (the position is
+    # read on the device), with eager work and synchronisations between
+    # replays; every replay's tokens and logits equal the eager path's
+    lib = _lib()
+    cfg = synth.GPTConfig(vocab=257, ctx=64, n_embd=64, n_head=2, n_layer=2, n_ff=256, dtype=synth.BF16)
+    params = synth.make_params(cfg, seed=6, cfg_id=9, init="stress")
+    prompt = torch.from_numpy(synth.make_ids(cfg, 4, 10, seed=6, cfg_id=9)).cuda()
+    P = lib.params_to_device(cfg, synth.pack(cfg, params))
+    steps = 6
+
+    eager = lib.Decoder(cfg, 4, 10, 32)
+    eager.prefill(P, prompt)
+    ref_tok, ref_z = [], []
+    for _ in range(steps):
+        z = torch.empty((4, cfg.vocab), dtype=torch.bfloat16, device="cuda")
+        eager.step(P, logits=z)
+        ref_tok.append(eager.tok.clone())
+        ref_z.append(z)
+    torch.cuda.synchronize()
+
+    g = lib.Decoder(cfg, 4, 10, 32)
+    zg = torch.empty((4, cfg.vocab), dtype=torch.bfloat16, device="cuda")
+    g.prefill(P, prompt)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.step(P, logits=zg)
+    for s in range(steps):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g.tok, ref_tok[s]), f"replay {s}: tokens differ"
+        assert torch.equal(zg, ref_z[s]), f"replay {s}: logits differ"
+        _ = (zg.float() * 2).sum().item()          # unrelated eager work between replays
+    assert int(g.pos.item()) == 10 + steps
