@@ -251,63 +251,148 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
 // 0 .. *pos (its own K/U were appended at *pos by the QKV epilogue), the
 // KV-cache form of the same causal attention ("预训练一个 Mini GPT", KV
 // cache: only the new token's q, k, u are computed; earlier k, u are read
-// back).  One wave per (b, h): lanes own keys for the scores and head columns
-// for the weighted sum.  HBM-bound: every cached K and U row of the sequence
-// is read once.
+// back).  One block of 256 threads per (b, h).  A key row of D values is cut
+// into 16-byte chunks held by LPK adjacent lanes (8 lanes for D = 64 in bf16),
+// so a group of lanes reads a whole row and a wave reads consecutive rows:
+//   1. scores: group g takes keys g, g + G, ... (G = 256 / LPK groups), dots
+//      its chunks with the matching slice of q, reduces over the group, and
+//      the group's first lane writes the score to LDS;
+//   2. block max and the sum of exp2(score - max) (q carries log2(e)/sqrt(D));
+//   3. weighted sum: the groups walk the keys again, each lane accumulating
+//      its chunk of U weighted by p; the G partial rows meet in LDS.
+// HBM-bound: every cached K and U row of positions 0 .. *pos is read once.
 constexpr int DEC_MAXT = 4096;
+constexpr int DEC_THREADS = 256;
 
 template <typename T>
-__global__ void __launch_bounds__(64) attn_decode_kernel(DecAttnArgs a) {
+__device__ __forceinline__ void chunk_f32(const uint4& v, float (&o)[16 / sizeof(T)]);
+template <>
+__device__ __forceinline__ void chunk_f32<bf16>(const uint4& v, float (&o)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void chunk_f32<float>(const uint4& v, float (&o)[4]) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a) {
   constexpr int VEC = 16 / sizeof(T);
+  constexpr int UNR = 4;
   __shared__ float p[DEC_MAXT];
   __shared__ float qs[128];
-  const int lane = threadIdx.x;
+  __shared__ float part[DEC_THREADS * VEC];
+  __shared__ float wred[DEC_THREADS / 64];
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H, D = a.D;
+  const int nch = D / VEC;                  // 16-byte chunks per row (D % VEC == 0)
+  int lpk = 1;
+  while (lpk < nch) lpk <<= 1;              // lanes per key, a power of two dividing 64
+  const int G = DEC_THREADS / lpk;
+  const int g = tid / lpk, c = tid - g * lpk;
+  const bool act = c < nch;
   const T* q = reinterpret_cast<const T*>(a.q) + (long long)bh * D;
-  for (int d = lane; d < D; d += 64) qs[d] = to_f32(q[d]) * a.scale_log2;
+  for (int d = tid; d < D; d += DEC_THREADS) qs[d] = to_f32(q[d]) * a.scale_log2;
   __syncthreads();
+  float qv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) qv[e] = act ? qs[c * VEC + e] : 0.f;
   int n = *a.pos + 1;
   n = n < 1 ? 1 : (n < a.Tmax ? n : a.Tmax);   // a position outside [0, Tmax) violates the contract
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * a.kv_bh;
-  const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.kv_bh;
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * a.kv_bh + c * VEC;
+  const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.kv_bh + c * VEC;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+
   float mx = -INFINITY;
-  for (int k = lane; k < n; k += 64) {
-    const T* kr = K + (long long)k * D;
-    float s = 0.f;
-    for (int d = 0; d < D; d += VEC) {
-      T kv[VEC];
-      *reinterpret_cast<uint4*>(kv) = *reinterpret_cast<const uint4*>(kr + d);
+  for (int k0 = 0; k0 < n; k0 += UNR * G) {
+    uint4 kv[UNR];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) s = fmaf(qs[d + e], to_f32(kv[e]), s);
+    for (int u = 0; u < UNR; ++u) {
+      const int k = k0 + u * G + g;
+      kv[u] = (act && k < n) ? *reinterpret_cast<const uint4*>(K + (long long)k * D) : z;
     }
-    p[k] = s;
-    mx = fmaxf(mx, s);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float kf[VEC];
+      chunk_f32<T>(kv[u], kf);
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sc = fmaf(qv[e], kf[e], sc);
+      for (int o = lpk >> 1; o > 0; o >>= 1) sc += __shfl_xor(sc, o, 64);
+      const int k = k0 + u * G + g;
+      if (k < n) {
+        if (c == 0) p[k] = sc;
+        mx = fmaxf(mx, sc);
+      }
+    }
   }
   mx = wave_max(mx);
+  if ((tid & 63) == 0) wred[wave] = mx;
+  __syncthreads();
+  mx = wred[0];
+#pragma unroll
+  for (int w = 1; w < DEC_THREADS / 64; ++w) mx = fmaxf(mx, wred[w]);
   float sum = 0.f;
-  for (int k = lane; k < n; k += 64) {
+  for (int k = tid; k < n; k += DEC_THREADS) {
     const float e = fast_exp2(p[k] - mx);
     p[k] = e;
     sum += e;
   }
   sum = wave_sum(sum);
+  __syncthreads();                          // every read of wred and every p update done
+  if ((tid & 63) == 0) wred[wave] = sum;
   __syncthreads();
+  sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < DEC_THREADS / 64; ++w) sum += wred[w];
   const float inv = 1.0f / sum;
+
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < n; k0 += UNR * G) {
+    uint4 uv[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int k = k0 + u * G + g;
+      uv[u] = (act && k < n) ? *reinterpret_cast<const uint4*>(U + (long long)k * D) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int k = k0 + u * G + g;
+      const float w = k < n ? p[k] : 0.f;
+      float uf[VEC];
+      chunk_f32<T>(uv[u], uf);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, uf[e], acc[e]);
+    }
+  }
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) part[g * D + c * VEC + e] = acc[e];
+  }
+  __syncthreads();
   T* orow = reinterpret_cast<T*>(a.o) + (long long)b * a.o_ld + h * D;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int k = 0; k < n; ++k) acc = fmaf(p[k], to_f32(U[(long long)k * D + d]), acc);
-    orow[d] = from_f32<T>(acc * inv);
+  for (int d = tid; d < D; d += DEC_THREADS) {
+    float t = 0.f;
+    for (int gg = 0; gg < G; ++gg) t += part[gg * D + d];
+    orow[d] = from_f32<T>(t * inv);
   }
 }
 
 hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t st) {
-  if (a.Tmax > DEC_MAXT || a.D > 128) return hipErrorInvalidValue;
+  const int vec = dtype == 0 ? 4 : 8;
+  if (a.Tmax > DEC_MAXT || a.D > 128 || a.D % vec) return hipErrorInvalidValue;
   if (dtype == 0)
-    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(a.B * a.H), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(a.B * a.H), dim3(DEC_THREADS), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(a.B * a.H), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(a.B * a.H), dim3(DEC_THREADS), 0, st, a);
   return hipGetLastError();
 }
 

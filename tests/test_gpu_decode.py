@@ -78,7 +78,7 @@ def test_micro_fp32_decode(seed, init):
     check_against_oracle(cfg, params, prompt, toks, z, range(3), fp32_tol, fp32_tol)
 
 
-@pytest.mark.parametrize("B,Tp,Tmax,steps", [(5, 17, 40, 20), (1, 1, 8, 7), (2, 64, 128, 9)])
+@pytest.mark.parametrize("B,Tp,Tmax,steps", [(5, 17, 40, 20), (1, 1, 8, 7), (2, 64, 128, 9), (1, 100, 128, 28)])
 def test_minigpt_fp32_decode(B, Tp, Tmax, steps):
     cfg = synth.MINI
     params = synth.make_params(cfg, seed=Tp, cfg_id=2, init="stress")
@@ -129,13 +129,15 @@ def bf16_band(_):
     return 1e-1
 
 
-def test_small_bf16_decode_generic_head():
+@pytest.mark.parametrize("B", [3, 70])
+def test_small_bf16_decode(B):
+    # B <= 64: skinny products and the skinny greedy head; B = 70: tiled paths
     cfg = synth.GPTConfig(vocab=257, ctx=64, n_embd=64, n_head=2, n_layer=2, n_ff=256, dtype=synth.BF16)
     params = synth.make_params(cfg, seed=4, cfg_id=9, init="stress")
-    prompt = synth.make_ids(cfg, 3, 20, seed=4, cfg_id=9)
-    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=12, Tmax=40)
+    prompt = synth.make_ids(cfg, B, 20, seed=4, cfg_id=9)
+    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=12, Tmax=40, rows=[0, 1, B - 1])
     assert pos == 32
-    check_against_oracle(cfg, params, prompt, toks, z, range(3), bf16_tol, bf16_band)
+    check_against_oracle(cfg, params, prompt, toks, z, [0, 1, B - 1], bf16_tol, bf16_band)
 
 
 @pytest.fixture(scope="module")

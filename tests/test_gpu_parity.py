@@ -80,7 +80,10 @@ def test_layernorm_kernel(dtype, C, M):
 @pytest.mark.parametrize("M,N,K,act", [(48, 48, 16, 0), (256, 384, 128, 1), (100, 77, 40, 0),
                                       (333, 1000, 768, 1), (1024, 2304, 768, 0), (130, 17, 3072, 0),
                                       # pipelined bf16 path (K = 768 / 3072), odd and ragged M
-                                      (8191, 2304, 768, 0), (4097, 768, 3072, 1), (2049, 3072, 768, 1)])
+                                      (8191, 2304, 768, 0), (4097, 768, 3072, 1), (2049, 3072, 768, 1),
+                                      # skinny path (at most 64 rows): K and N tails, one row
+                                      (1, 2304, 768, 0), (64, 3072, 768, 1), (37, 768, 3072, 0),
+                                      (64, 50, 24, 1), (5, 96, 8, 0)])
 def test_linear_kernel(dtype, M, N, K, act):
     lib = _lib()
     cfg = synth.GPTConfig(vocab=17, ctx=16, n_embd=16, n_head=2, n_layer=1, n_ff=64, dtype=dtype)
