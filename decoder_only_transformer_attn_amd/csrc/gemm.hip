@@ -160,18 +160,28 @@ __device__ __forceinline__ void tile_of(int pid, int nblocks, int num_m, int num
 // ---------------------------------------------------------------------------
 // Pipelined bf16 main loop with direct-to-LDS loads.
 //
-// Tiles of 256 x 256 with K steps of 32 flow through a ring of four LDS
-// stages: gfx950's buffer_load ... lds writes each 16-byte chunk straight
-// into LDS (no VGPR staging, no ds_write), three K steps are in flight while
-// the fourth is multiplied, and one barrier per K step hands a stage from the
-// loads to the MFMAs.  Each wave waits for its own loads of step t
-// (s_waitcnt vmcnt) before the barrier, so after it every wave's loads of
-// step t are in LDS.  The four stages are distinct LDS objects so the
-// compiler can tell a read of one stage from the loads into another.  Rows
-// are 64 bytes (4 chunks); chunk c of row r is stored at slot c ^ ((r>>1)&3),
-// which makes the MFMA fragment reads (ds_read_b128, 32 rows x one chunk per
-// half-wave) bank-conflict free.  K is a template parameter and the K loop is
-// unrolled completely.
+// Tiles flow through a ring of NST LDS stages, each holding BK (32 or 64)
+// K-columns of the BM rows of A and the BN rows of W: gfx950's buffer_load
+// ... lds writes each 16-byte chunk straight into LDS (no VGPR staging, no
+// ds_write), NST - 1 stages are in flight while one is multiplied, and one
+// barrier per stage hands a stage from the loads to the MFMAs.  Each wave
+// waits for its own loads of stage t (s_waitcnt vmcnt) before the barrier, so
+// after it every wave's loads of stage t are in LDS.  The stages are distinct
+// LDS objects so the compiler can tell a read of one stage from the loads
+// into another.
+//
+// A row of a stage is ROWB = 2 BK bytes, CPR = BK / 8 chunks of 16 bytes.
+// With BK = 64 a row is one whole 128-byte cache line, so every load
+// instruction (8 rows of 128 bytes) reads whole lines; that is what lets the
+// per-CU load path run near its streaming rate (half-line rows, BK = 32,
+// reach about half of it).  Chunk c of row r is stored at slot
+// c ^ ((r / (16 / CPR)) % CPR): a fragment read (ds_read_b128) has 16
+// consecutive lanes read one chunk of 16 consecutive rows, LDS serves 64
+// banks (256 bytes) per cycle, and row r, slot s lies in 16-byte bank group
+// (r CPR + s) % 16, so rows that share r % (16 / CPR) must use different
+// slots, which the XOR term gives.  Fragment reads run one k-substep (16) ahead
+// of the MFMAs.  K is a template parameter and the K loop is unrolled
+// completely.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -184,32 +194,53 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 // it but, unlike __syncthreads, does not wait for outstanding loads.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 1) & 3); }
+template <int CPR> __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r / (16 / CPR)) % CPR); }
 
 // One 1 KB direct-to-LDS load: lane l's 16 bytes land at lds + 16 l.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST_ = 4, int BK_ = 32>
 struct DmaCfg {
-  static constexpr int BK = 32, NST = 4, ROWB = 64;
+  static constexpr int BK = BK_, NST = NST_, ROWB = 2 * BK, CPR = BK / 8, RPI = 1024 / ROWB;
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * WAVE;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int STAGE = (BM + BN) * ROWB;        // bytes per stage
-  static constexpr int NI = (BM + BN) / 16;             // 1 KB load instructions per stage
+  static constexpr int NI = (BM + BN) / RPI;            // 1 KB load instructions per stage
   static constexpr int DPW = NI / NW;                   // per wave
-  static_assert(NI % NW == 0 && BM % 16 == 0 && BN % 16 == 0, "loads must split evenly over the waves");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(NI % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "loads must split evenly over the waves");
 };
 
-template <int BM, int BN, int WM, int WN, int K>
+// The ring's stages: up to eight distinct LDS arrays (see above).
+struct Stages {
+  char* p[8];
+};
+
+// Wait until at most g of this wave's load groups (DPW loads each) are still
+// in flight; g is a constant once the K loop is unrolled.
+template <int DPW> __device__ __forceinline__ void wait_groups(int g) {
+  switch (g) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<DPW>(); break;
+    case 2: wait_vmcnt<2 * DPW>(); break;
+    case 3: wait_vmcnt<3 * DPW>(); break;
+    case 4: wait_vmcnt<4 * DPW>(); break;
+    case 5: wait_vmcnt<5 * DPW>(); break;
+    default: wait_vmcnt<6 * DPW>(); break;
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int K, int NST, int BK>
 __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N,
-                                             int m0, int n0, char* s0, char* s1, char* s2, char* s3,
-                                             f32x16 (&acc)[WM / 32][WN / 32]) {
-  typedef DmaCfg<BM, BN, WM, WN> D;
-  constexpr int NK = K / D::BK;
-  static_assert(K % D::BK == 0, "K must be a multiple of 32");
-  char* const st[4] = {s0, s1, s2, s3};
+                                             int m0, int n0, const Stages& st, f32x16 (&acc)[WM / 32][WN / 32]) {
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
+  constexpr int NK = K / BK;          // stages along K
+  constexpr int KS = BK / 16;         // MFMA k-substeps per stage
+  constexpr int CPR = D::CPR;
+  static_assert(K % BK == 0, "K must be a multiple of the stage depth");
+  static_assert(NST >= 2 && NST <= 8 && (NST - 2) * D::DPW < 64, "stage count");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / D::NWN, wn = wave % D::NWN;
@@ -220,8 +251,8 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Stage layout: A rows [0, BM) then W rows, 64 bytes each.  Load
-  // instruction i (16 rows) goes to LDS offset 1024 i and is issued by wave
+  // Stage layout: A rows [0, BM) then W rows, ROWB bytes each.  Load
+  // instruction i (RPI rows) goes to LDS offset 1024 i and is issued by wave
   // i % NW; the wave index is uniform, so the A/W choice stays scalar.
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)min(BM, M - m0) * K * sizeof(bf16)));
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)min(BN, N - n0) * K * sizeof(bf16)));
@@ -229,15 +260,16 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 #pragma unroll
   for (int d = 0; d < D::DPW; ++d) {
     const int ins = wave + d * D::NW;
-    const int row = (ins < BM / 16 ? ins : ins - BM / 16) * 16 + (lane >> 2), slot = lane & 3;
-    voff[d] = (uint32_t)((row * K + swz4(row, slot) * 8) * sizeof(bf16));
+    constexpr int IA = BM / D::RPI;   // instructions covering A
+    const int row = (ins < IA ? ins : ins - IA) * D::RPI + lane / CPR, slot = lane % CPR;
+    voff[d] = (uint32_t)((row * K + swz<CPR>(row, slot) * 8) * sizeof(bf16));
   }
   auto issue = [&](int t) {
-    char* s = st[t % D::NST];
+    char* s = st.p[t % NST];
 #pragma unroll
     for (int d = 0; d < D::DPW; ++d) {
       const int ins = wave + d * D::NW;
-      dma16(ins < BM / 16 ? rsA : rsB, s + ins * 1024, voff[d], t * D::BK * 2);
+      dma16(ins < BM / D::RPI ? rsA : rsB, s + ins * 1024, voff[d], t * BK * 2);
     }
   };
   const int lrow = lane & 31, g = lane >> 5;
@@ -246,13 +278,13 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 #pragma unroll
     for (int i = 0; i < D::TM; ++i) {
       const int r = wm * WM + i * 32 + lrow;
-      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(s + r * D::ROWB + swz4(r, c) * 16));
+      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(s + r * D::ROWB + swz<CPR>(r, c) * 16));
     }
 #pragma unroll
     for (int j = 0; j < D::TN; ++j) {
       const int r = wn * WN + j * 32 + lrow;
-      bfr[j] = __builtin_bit_cast(bf16x8,
-                                  *reinterpret_cast<const uint4*>(s + BM * D::ROWB + r * D::ROWB + swz4(r, c) * 16));
+      bfr[j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(s + BM * D::ROWB + r * D::ROWB + swz<CPR>(r, c) * 16));
     }
   };
   auto mm = [&](const bf16x8 (&af)[D::TM], const bf16x8 (&bfr)[D::TN]) {
@@ -261,25 +293,24 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 #pragma unroll
       for (int j = 0; j < D::TN; ++j) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
   };
-  issue(0);
-  if (NK > 1) issue(1);
-  if (NK > 2) issue(2);
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < NK) issue(t);
 #pragma unroll
   for (int t = 0; t < NK; ++t) {
-    if (t + 2 < NK) wait_vmcnt<2 * D::DPW>();
-    else if (t + 1 < NK) wait_vmcnt<D::DPW>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (t + 3 < NK) issue(t + 3);
-    const char* s = st[t % D::NST];
-    bf16x8 a0[D::TM], b0[D::TN], a1[D::TM], b1[D::TN];
-    ldfrag(s, 0, a0, b0);
-    ldfrag(s, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mm(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mm(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
+    wait_groups<D::DPW>(min(NST - 2, NK - 1 - t));   // this wave's loads of stage t have landed
+    lds_barrier();                                   // ... and every other wave's
+    if (t + NST - 1 < NK) issue(t + NST - 1);        // into the stage consumed at step t - 1
+    const char* s = st.p[t % NST];
+    bf16x8 af[2][D::TM], bfr[2][D::TN];
+    ldfrag(s, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) ldfrag(s, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(af[ks & 1], bfr[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __syncthreads();  // every wave is done with the stages: the epilogue may reuse LDS
 }
@@ -310,24 +341,44 @@ __device__ __forceinline__ void store_pair(T* p, float a, float b, bool has_b, b
   }
 }
 
+// Bias values of a column pair, kept in storage form until the epilogue so
+// that no instruction before the main loop waits for their loads.
+template <typename T>
+struct RawPair {
+  uint32_t a, b;   // bit patterns: bf16 zero-extended, fp32 as is
+  static __device__ __forceinline__ uint32_t bits(T v) {
+    if constexpr (sizeof(T) == 2) return (uint32_t)v;
+    else return __float_as_uint(v);
+  }
+  static __device__ __forceinline__ float f32(uint32_t u) {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(u << 16);
+    else return __uint_as_float(u);
+  }
+};
+
 template <typename T>
 struct EpiAct {  // out[m, n] = act(v + bias[n])
   static constexpr bool kPreload = false;
+  static constexpr bool kCompact = true;
   typedef int Row;
-  typedef float2 Col;
+  typedef RawPair<T> Col;
   __device__ __forceinline__ Row row(int) const { return 0; }
   const T* bias;
   void* out;
   int ldo;
   int act;       // 0 none, 1 tanh-GELU
   int out_f32;   // store fp32 instead of T
-  __device__ __forceinline__ float2 col(int n, bool has_b) const {
-    return bias ? make_float2(to_f32(bias[n]), has_b ? to_f32(bias[n + 1]) : 0.f) : make_float2(0.f, 0.f);
+  __device__ __forceinline__ Col col(int n, bool has_b) const {
+    // branch-free: without a bias the (valid) output row is read instead and ignored
+    const T* bp = bias ? bias : reinterpret_cast<const T*>(out);
+    return Col{Col::bits(bp[n]), Col::bits(bp[has_b ? n + 1 : n])};
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
   __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, const Col& bs, float2) const {
-    a += bs.x;
-    b += bs.y;
+    if (bias) {
+      a += Col::f32(bs.a);
+      b += Col::f32(bs.b);
+    }
     if (act == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
     const size_t o = (size_t)m * ldo + n;
     if (out_f32) store_pair(reinterpret_cast<float*>(out) + o, a, b, has_b, (ldo & 1) == 0);
@@ -338,14 +389,15 @@ struct EpiAct {  // out[m, n] = act(v + bias[n])
 template <typename T>
 struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
   static constexpr bool kPreload = true;
+  static constexpr bool kCompact = false;
   typedef int Row;
-  typedef float2 Col;
+  typedef RawPair<T> Col;
   __device__ __forceinline__ Row row(int) const { return 0; }
   const T* bias;
   float* x;
   int ldx;
-  __device__ __forceinline__ float2 col(int n, bool has_b) const {
-    return make_float2(to_f32(bias[n]), has_b ? to_f32(bias[n + 1]) : 0.f);
+  __device__ __forceinline__ Col col(int n, bool has_b) const {
+    return Col{Col::bits(bias[n]), Col::bits(bias[has_b ? n + 1 : n])};
   }
   __device__ __forceinline__ float2 preload(int m, int n, bool has_b) const {
     const float* p = x + (size_t)m * ldx + n;
@@ -353,8 +405,8 @@ struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
     return make_float2(p[0], has_b ? p[1] : 0.f);
   }
   __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, const Col& bs, float2 xo) const {
-    a = xo.x + (a + bs.x);
-    if (has_b) b = xo.y + (b + bs.y);
+    a = xo.x + (a + Col::f32(bs.a));
+    if (has_b) b = xo.y + (b + Col::f32(bs.b));
     store_pair(x + (size_t)m * ldx + n, a, b, has_b, (ldx & 1) == 0);
   }
 };
@@ -370,6 +422,7 @@ __device__ __forceinline__ int div_small(int m, int d, float inv_d) {
 template <typename T>
 struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all three [B,H,T,D]
   static constexpr bool kPreload = false;
+  static constexpr bool kCompact = false;
   const T* bias;
   int C, H, D, T_seq;
   float inv_T;
@@ -379,7 +432,7 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
   int Tk;                           // K/U rows; cache positions >= Tk are not written
   struct Row { int b, t, tc; };
-  struct Col { float2 bias; T* base; long long bh_stride; bool is_q; };
+  struct Col { RawPair<T> bias; T* base; long long bh_stride; bool is_q; };
   __device__ __forceinline__ Row row(int m) const {
     const int bb = div_small(m, T_seq, inv_T), t = m - bb * T_seq;
     return Row{bb, t, t + (pos ? *pos : 0)};
@@ -392,13 +445,14 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
     const int h = c / D, d = c - h * D;
     const long long st = which == 0 ? q_bh : (which == 1 ? k_bh : v_bh);
     T* arr = which == 0 ? q : (which == 1 ? k : v);
-    return Col{make_float2(to_f32(bias[n]), to_f32(bias[n + 1])), arr + h * st + d, st * H, which == 0};
+    return Col{RawPair<T>{RawPair<T>::bits(bias[n]), RawPair<T>::bits(bias[n + 1])}, arr + h * st + d, st * H,
+               which == 0};
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
   __device__ __forceinline__ void pair(const Row& r, int, int, float a, float b, bool, const Col& cl, float2) const {
     if (!cl.is_q && (r.tc < 0 || r.tc >= Tk)) return;   // outside the cache: contract violation, nothing written
     T* dst = cl.base + r.b * cl.bh_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
-    store_pair(dst, a + cl.bias.x, b + cl.bias.y, true, true);
+    store_pair(dst, a + RawPair<T>::f32(cl.bias.a), b + RawPair<T>::f32(cl.bias.b), true, true);
   }
 };
 
@@ -421,7 +475,10 @@ __device__ __forceinline__ void preload_pairs(float2 (&pre)[TM][TN][8], typename
   for (int j = 0; j < TN; ++j) {
     int m, n;
     pair_coords<TM, TN>(0, j, 0, mbase, nbase, m, n);
-    if (n < N) colv[j] = epi.col(n, n + 1 < N);
+    // no branch around these loads (columns past N read column N-1, unused),
+    // so nothing waits for them before the main loop
+    const int nc = min(n, N - 1);
+    colv[j] = epi.col(nc, nc + 1 < N);
   }
   if constexpr (Epi::kPreload) {
 #pragma unroll
@@ -481,15 +538,30 @@ gemm_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, 
 }
 
 // bf16 GEMM through the pipelined main loop, element-wise epilogue.
-template <int BM, int BN, int WM, int WN, int K, typename Epi>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64) gemm_dma_kernel(const bf16* __restrict__ A,
-                                                                             const bf16* __restrict__ W, int M, int N,
-                                                                             Epi epi) {
-  typedef DmaCfg<BM, BN, WM, WN> D;
+// Waves per SIMD the register budget must allow so that every block the LDS
+// budget admits (160 KB per CU) can be resident at once.
+template <int BM, int BN, int WM, int WN, int NST, int BK>
+constexpr int dma_waves_per_eu() {
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
+  const int blocks = (160 * 1024) / (D::STAGE * NST);
+  const int w = blocks * D::NW / 4;
+  return w < 1 ? 1 : (w > 8 ? 8 : w);
+}
+
+template <int BM, int BN, int WM, int WN, int K, int NST, int BK, typename Epi>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN, NST, BK>())))
+gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, Epi epi) {
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
   __shared__ __align__(1024) char s2[D::STAGE];
-  __shared__ __align__(1024) char s3[D::STAGE];
+  __shared__ __align__(1024) char s3[NST > 3 ? D::STAGE : 16];
+  __shared__ __align__(1024) char s4[NST > 4 ? D::STAGE : 16];
+  __shared__ __align__(1024) char s5[NST > 5 ? D::STAGE : 16];
+  __shared__ __align__(1024) char s6[NST > 6 ? D::STAGE : 16];
+  __shared__ __align__(1024) char s7[NST > 7 ? D::STAGE : 16];
+  const Stages stages{{s0, s1, s2, s3, s4, s5, s6, s7}};
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
   int mt, nt;
   tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
@@ -500,7 +572,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64) gemm_dma_kernel(co
   typename Epi::Col colv[D::TN];
   preload_pairs<D::TM, D::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[D::TM][D::TN];
-  dma_mainloop<BM, BN, WM, WN, K>(A, W, M, N, m0, n0, s0, s1, s2, s3, acc);
+  dma_mainloop<BM, BN, WM, WN, K, NST, BK>(A, W, M, N, m0, n0, stages, acc);
   epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, epi);
 }
 
@@ -800,7 +872,8 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
   }
 
   f32x16 acc[D::TM][D::TN];
-  dma_mainloop<BM, BN, WM, WN, K>(wte, act, V, Mtok, v0, t0, s0, s1, s2, s3, acc);
+  const Stages stages{{s0, s1, s2, s3, s3, s3, s3, s3}};
+  dma_mainloop<BM, BN, WM, WN, K, 4, 32>(wte, act, V, Mtok, v0, t0, stages, acc);
 
   const bool amax = ha.part_idx != nullptr;
   if (amax) {
@@ -1069,21 +1142,28 @@ static hipError_t run_gemm(const T* A, int lda, const T* W, int ldw, int M, int 
 
 // Tile choice.  Large bf16 products use 256x256 tiles (128x128 per wave); the
 // fp32 path serves the small correctness configurations.
-template <int BM, int BN, int WM, int WN, int K, typename Epi>
+template <int BM, int BN, int WM, int WN, int K, int NST, int BK, typename Epi>
 static hipError_t run_gemm_dma(const bf16* A, const bf16* W, int M, int N, const Epi& epi, hipStream_t st) {
   const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, K, Epi>), dim3(blocks), dim3(DmaCfg<BM, BN, WM, WN>::NT), 0, st,
-                     A, W, M, N, epi);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, K, NST, BK, Epi>), dim3(blocks),
+                     dim3(DmaCfg<BM, BN, WM, WN, NST, BK>::NT), 0, st, A, W, M, N, epi);
   return hipGetLastError();
 }
 
-// 128 x 192 tiles (4 waves of 64 x 96) make every block GEMM of the 124M
+// 128 x 192 tiles make every block GEMM of the 124M
 // model a whole number of rounds over 256 CUs at M = 8192 (N = 2304: 768
 // tiles, 3072: 1024, 768: 256); 256 x 256 (8 waves of 64 x 128) otherwise.
 template <int K, typename Epi>
 static hipError_t run_gemm_dma_k(const bf16* A, const bf16* W, int M, int N, const Epi& epi, hipStream_t st) {
-  if (N % 192 == 0) return run_gemm_dma<128, 192, 64, 96, K>(A, W, M, N, epi, st);
-  return run_gemm_dma<256, 256, 64, 128, K>(A, W, M, N, epi, st);
+  if (N % 192 == 0) {
+    // 8 waves of 32 x 96; 64-deep stages.  Short K with an epilogue that keeps
+    // little in registers across the main loop (kCompact): two stages (80 KB)
+    // and two blocks per CU (128 registers per lane); otherwise three stages
+    // and one block per CU.
+    if (K <= 768 && Epi::kCompact) return run_gemm_dma<128, 192, 32, 96, K, 2, 64>(A, W, M, N, epi, st);
+    return run_gemm_dma<128, 192, 32, 96, K, 3, 64>(A, W, M, N, epi, st);
+  }
+  return run_gemm_dma<256, 256, 64, 128, K, 4, 32>(A, W, M, N, epi, st);
 }
 
 template <typename Epi>
