@@ -16,9 +16,13 @@ OUT = os.path.join(HERE, "libgptmi.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-# Packed fp32 VALU forms are disabled for all device code.
+# Packed fp32 VALU forms are disabled for all device code.  MFMA results are
+# kept in ordinary VGPRs (the unified register file allows it), so kernels
+# that post-process accumulators with VALU code (the attention softmax) do not
+# copy them between AGPRs and VGPRs.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wno-unused-result", "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "ce.hip", "gptmi_api.cpp"]

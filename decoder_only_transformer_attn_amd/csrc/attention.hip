@@ -26,11 +26,22 @@ template <typename T> struct VtFrag;
 // bf16: instruction hh of a 32-key sub-tile consumes accumulator registers
 // r = 8hh .. 8hh+7 of the S^T tile, i.e. keys 16hh + 4g + {0..3} and
 // 16hh + 8 + 4g + {0..3} for lane group g = lane / 32.
+// U^T rows hold 64 keys as 32 key pairs; pair p of row d is stored at pair
+// slot p ^ vt_swz(d).  With a row stride of 68 elements (34 banks) the 32
+// rows one ds_read_b64 phase touches start on 32 distinct even banks, and the
+// transposed stores (8 rows d, d+8, ... by 8 key pairs per instruction) land
+// on 64 distinct banks because rows 32 apart are shifted by 8 pairs.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 5) & 1) << 3; }
+
 template <> struct VtFrag<bf16> {
   static constexpr int NI = 2;  // instructions per 32 keys
-  static __device__ __forceinline__ bf16x8 load(const bf16* row, int hh, int g) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * hh + 4 * g);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * hh + 8 + 4 * g);
+  // keys k0 .. k0+3 (k0 % 4 == 0) of row d: pairs k0/2, k0/2+1 stay adjacent
+  static __device__ __forceinline__ uint2 keys4(const bf16* row, int d, int k0) {
+    return *reinterpret_cast<const uint2*>(row + 2 * ((k0 >> 1) ^ vt_swz(d)));
+  }
+  static __device__ __forceinline__ bf16x8 load(const bf16* row, int d, int kbase, int hh, int g) {
+    const uint2 lo = keys4(row, d, kbase + 16 * hh + 4 * g);
+    const uint2 hi = keys4(row, d, kbase + 16 * hh + 8 + 4 * g);
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
   static __device__ __forceinline__ bf16x8 pack(const f32x16& p, int hh) {
@@ -44,8 +55,9 @@ template <> struct VtFrag<bf16> {
 // fp32: instruction hh (0..15) consumes register r = hh: key (hh/4)*8 + 4g + hh%4.
 template <> struct VtFrag<float> {
   static constexpr int NI = 16;
-  static __device__ __forceinline__ float load(const float* row, int hh, int g) {
-    return row[(hh >> 2) * 8 + 4 * g + (hh & 3)];
+  static __device__ __forceinline__ float load(const float* row, int d, int kbase, int hh, int g) {
+    const int k = kbase + (hh >> 2) * 8 + 4 * g + (hh & 3);
+    return row[2 * ((k >> 1) ^ vt_swz(d)) + (k & 1)];
   }
   static __device__ __forceinline__ float pack(const f32x16& p, int hh) { return p[hh]; }
 };
@@ -60,7 +72,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   constexpr int BQ = 128;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int LDKS = DP + VEC;    // padded LDS row of K (elements)
-  constexpr int LDVS = BKV + VEC;   // padded LDS row of U^T
+  constexpr int LDVS = BKV + 4;     // LDS row of U^T (see vt_swz)
+  static_assert(BKV == 64, "the U^T swizzle assumes 64-key tiles");
   constexpr int NDI = DP / MF::KPI; // MFMA k steps over the head dim
   constexpr int NDT = DP / 32;      // 32-row d tiles of O^T
   constexpr int NST = BKV / 32;     // 32-key sub-tiles per KV tile
@@ -132,7 +145,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
       *reinterpret_cast<uint4*>(u1) = ur1[c];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        T* dst = &sV[buf][(dc + e) * LDVS + kp];   // kp and LDVS even: pair-aligned
+        T* dst = &sV[buf][(dc + e) * LDVS + 2 * ((kp >> 1) ^ vt_swz(dc + e))];   // pair-aligned
         if constexpr (sizeof(T) == 2)
           *reinterpret_cast<uint32_t*>(dst) = uint32_t(u0[e]) | (uint32_t(u1[e]) << 16);
         else
@@ -205,8 +218,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
           const auto pb = VtFrag<T>::pack(s[st], hh);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const T* vrow = &sV[cur][(dt * 32 + (lane & 31)) * LDVS + st * 32];
-            acc[dt] = MF::mma(VtFrag<T>::load(vrow, hh, g), pb, acc[dt]);
+            const int d = dt * 32 + (lane & 31);
+            const T* vrow = &sV[cur][d * LDVS];
+            acc[dt] = MF::mma(VtFrag<T>::load(vrow, d, st * 32, hh, g), pb, acc[dt]);
           }
         }
     }
