@@ -362,7 +362,9 @@ struct EpiAct {  // out[m, n] = act(v + bias[n])
   static constexpr bool kCompact = true;
   typedef int Row;
   typedef RawPair<T> Col;
+  typedef RawPair<T> ColX;
   __device__ __forceinline__ Row row(int) const { return 0; }
+  __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
   const T* bias;
   void* out;
   int ldo;
@@ -392,7 +394,9 @@ struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
   static constexpr bool kCompact = false;
   typedef int Row;
   typedef RawPair<T> Col;
+  typedef RawPair<T> ColX;
   __device__ __forceinline__ Row row(int) const { return 0; }
+  __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
   const T* bias;
   float* x;
   int ldx;
@@ -422,7 +426,7 @@ __device__ __forceinline__ int div_small(int m, int d, float inv_d) {
 template <typename T>
 struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all three [B,H,T,D]
   static constexpr bool kPreload = false;
-  static constexpr bool kCompact = false;
+  static constexpr bool kCompact = true;
   const T* bias;
   int C, H, D, T_seq;
   float inv_T;
@@ -432,26 +436,30 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
   int Tk;                           // K/U rows; cache positions >= Tk are not written
   struct Row { int b, t, tc; };
-  struct Col { RawPair<T> bias; T* base; long long bh_stride; bool is_q; };
+  typedef RawPair<T> Col;   // held across the main loop: the bias pair only
+  struct ColX { RawPair<T> bias; T* base; int b_stride; bool is_q; };   // b_stride = H * rows * D < 2^31
   __device__ __forceinline__ Row row(int m) const {
     const int bb = div_small(m, T_seq, inv_T), t = m - bb * T_seq;
     return Row{bb, t, t + (pos ? *pos : 0)};
   }
-  // Column n (even) -> projection, head and head column; D is even, so n and
-  // n + 1 fall in the same head of the same projection.
   __device__ __forceinline__ Col col(int n, bool) const {
+    return Col{RawPair<T>::bits(bias[n]), RawPair<T>::bits(bias[n + 1])};
+  }
+  // Column n (even) -> projection, head and head column, worked out once per
+  // column tile when the epilogue starts; D is even, so n and n + 1 fall in
+  // the same head of the same projection.
+  __device__ __forceinline__ ColX colx(int n, const Col& bs) const {
     const int which = n / C;
     const int c = n - which * C;
     const int h = c / D, d = c - h * D;
     const long long st = which == 0 ? q_bh : (which == 1 ? k_bh : v_bh);
     T* arr = which == 0 ? q : (which == 1 ? k : v);
-    return Col{RawPair<T>{RawPair<T>::bits(bias[n]), RawPair<T>::bits(bias[n + 1])}, arr + h * st + d, st * H,
-               which == 0};
+    return ColX{bs, arr + h * st + d, (int)(st * H), which == 0};
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
-  __device__ __forceinline__ void pair(const Row& r, int, int, float a, float b, bool, const Col& cl, float2) const {
+  __device__ __forceinline__ void pair(const Row& r, int, int, float a, float b, bool, const ColX& cl, float2) const {
     if (!cl.is_q && (r.tc < 0 || r.tc >= Tk)) return;   // outside the cache: contract violation, nothing written
-    T* dst = cl.base + r.b * cl.bh_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
+    T* dst = cl.base + (long long)r.b * cl.b_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
     store_pair(dst, a + RawPair<T>::f32(cl.bias.a), b + RawPair<T>::f32(cl.bias.b), true, true);
   }
 };
@@ -499,6 +507,13 @@ __device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], cons
                                                const typename Epi::Col (&colv)[TN], int mbase, int nbase, int M, int N,
                                                const Epi& epi) {
   const bool odd = threadIdx.x & 1;
+  typename Epi::ColX cx[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    int m, n;
+    pair_coords<TM, TN>(0, j, 0, mbase, nbase, m, n);
+    cx[j] = epi.colx(min(n, N - 1), colv[j]);
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -513,7 +528,7 @@ __device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], cons
         const float recv = __shfl_xor(odd ? v0 : v1, 1, 64);
         const int n = n0 + j * 32;
         const float a = odd ? recv : v0, b = odd ? v1 : recv;
-        if (m < M && n < N) epi.pair(rc, m, n, a, b, n + 1 < N, colv[j], pre[i][j][rp]);
+        if (m < M && n < N) epi.pair(rc, m, n, a, b, n + 1 < N, cx[j], pre[i][j][rp]);
       }
     }
 }
