@@ -830,8 +830,8 @@ __device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
 // reduction over the lane's own registers, one exchange with the lane holding
 // the other half of the rows (l ^ 32), and a 4-way combine over the waves
 // along the vocab axis.  The target ids are read before the main loop.
-// Logits: the whole 256 x 256 bf16 tile is staged in the four (then free)
-// pipeline stages, 64 token rows of 512 bytes each with 16-byte chunks
+// Logits: the whole 256 x 256 bf16 tile is staged in the two (then free)
+// pipeline stages, four quarters of 64 token rows of 512 bytes each with 16-byte chunks
 // XOR-swizzled by row, behind a single barrier; each 16-byte window of a
 // global logits row (V is odd, so rows are only 2-byte aligned) is then
 // assembled from two LDS chunks and written with one aligned 16-byte store;
@@ -861,12 +861,11 @@ template <int K>
 __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act,
                                                           int V, int Mtok, HeadArgs ha) {
   constexpr int BM = 256, BN = 256, WM = 64, WN = 128;   // BM: vocab, BN: tokens
-  typedef DmaCfg<BM, BN, WM, WN> D;
-  static_assert(64 * BM * 2 == D::STAGE, "a stage holds 64 staged token rows");
+  typedef DmaCfg<BM, BN, WM, WN, 2, 64> D;                 // two 64-deep stages
+  constexpr int SUB = 64 * BM * 2;                         // 64 staged token rows of logits
+  static_assert(2 * SUB == D::STAGE, "a stage holds 128 staged token rows");
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
-  __shared__ __align__(1024) char s2[D::STAGE];
-  __shared__ __align__(1024) char s3[D::STAGE];
   __shared__ float red[D::NWM][BN][2];
   __shared__ int redi[D::NWM][BN];
   const int num_v = (V + BM - 1) / BM, num_t = (Mtok + BN - 1) / BN;
@@ -887,8 +886,8 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
   }
 
   f32x16 acc[D::TM][D::TN];
-  const Stages stages{{s0, s1, s2, s3, s3, s3, s3, s3}};
-  dma_mainloop<BM, BN, WM, WN, K, 4, 32>(wte, act, V, Mtok, v0, t0, stages, acc);
+  const Stages stages{{s0, s1, s1, s1, s1, s1, s1, s1}};
+  dma_mainloop<BM, BN, WM, WN, K, 2, 64>(wte, act, V, Mtok, v0, t0, stages, acc);
 
   const bool amax = ha.part_idx != nullptr;
   if (amax) {
@@ -959,8 +958,8 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
     }
   }
 
-  // stage the bf16 logits tile: token row tl -> stage tl / 64, row tl % 64
-  auto stg = [&](int i) -> char* { return i == 0 ? s0 : (i == 1 ? s1 : (i == 2 ? s2 : s3)); };
+  // stage the bf16 logits tile: token row tl -> quarter tl / 64, row tl % 64
+  auto stg = [&](int i) -> char* { return (i < 2 ? s0 : s1) + (i & 1) * SUB; };
   if (ha.logits) {
 #pragma unroll
     for (int j = 0; j < D::TN; ++j) {
