@@ -958,23 +958,36 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
     }
   }
 
-  // stage the bf16 logits tile: token row tl -> quarter tl / 64, row tl % 64
-  auto stg = [&](int i) -> char* { return (i < 2 ? s0 : s1) + (i & 1) * SUB; };
+  // bf16 logits straight from the accumulators: registers 4q .. 4q+3 hold
+  // 4 consecutive vocab entries of one token, i.e. 8 contiguous bytes of its
+  // logits row (only 2-byte aligned: V is odd), written with one store; the
+  // lanes of one store instruction cover 16 contiguous bytes of 32 rows, and
+  // a wave's 8 stores per token fill whole 128-byte spans of the row.
   if (ha.logits) {
+    bf16* const L = reinterpret_cast<bf16*>(ha.logits);
 #pragma unroll
     for (int j = 0; j < D::TN; ++j) {
-      const int tl = wn * WN + j * 32 + (lane & 31);
-      char* row = stg((wn * WN + j * 32) >> 6) + (tl & 63) * (BM * 2);
-      const int sw = tl & 31;
+      const int m = t0 + wn * WN + j * 32 + (lane & 31);
+      if (m < Mtok) {
+        bf16* const rowp = L + (long long)m * ha.ld_logits;
 #pragma unroll
-      for (int i = 0; i < D::TM; ++i)
+        for (int i = 0; i < D::TM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {   // registers 4q .. 4q+3: 4 consecutive vocab rows
-          const int u = (wm * WM + i * 32 + q * 8 + g * 4) >> 2;   // 8-byte unit within the row
-          const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<uint2*>(row + (((u >> 1) ^ sw) << 4) + ((u & 1) << 3)) = make_uint2(lo, hi);
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int v = vw0 + i * 32 + q * 8 + g * 4;
+            const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            if (v + 3 < V) {
+              __builtin_memcpy(rowp + v, &lo, 4);
+              __builtin_memcpy(rowp + v + 2, &hi, 4);
+            } else {
+              const uint32_t ww[2] = {lo, hi};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (v + e < V) rowp[v + e] = bf16(ww[e >> 1] >> (16 * (e & 1)));
+            }
+          }
+      }
     }
   }
   __syncthreads();
@@ -1002,35 +1015,6 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
     }
     ha.part_max[(long long)m * ha.ntiles + vt] = M_;
     ha.part_sum[(long long)m * ha.ntiles + vt] = S;
-  }
-  if (!ha.logits) return;
-
-  bf16* const L = reinterpret_cast<bf16*>(ha.logits);
-  const int elem_mis = (int)((reinterpret_cast<uintptr_t>(ha.logits) >> 1) & 7);
-  const int nv = min(BM, V - v0);
-  constexpr int NWIN = (BM + 7 + 7) / 8;   // windows per row, enough for any shift
-  for (int it = tid; it < BN * NWIN; it += D::NT) {
-    const int tl = it / NWIN, k = it - tl * NWIN;
-    const int m = t0 + tl;
-    if (m >= Mtok) continue;
-    const long long e0 = (long long)m * ha.ld_logits + v0;   // element index of (m, v0)
-    const int sh = (int)((e0 + elem_mis) & 7);                // its offset in a 16-byte window
-    const int p0 = 8 * k;                                       // window start, in shifted positions
-    if (p0 >= sh + nv) continue;
-    const char* row = stg(tl >> 6) + (tl & 63) * (BM * 2);
-    const int q0 = p0 - sh;                                     // first tile column of the window
-    const int clo = q0 >= 0 ? (q0 >> 3) : -1;
-    const int o = q0 - 8 * clo;
-    const uint4 w = window8(lds_chunk(row, clo, tl & 31), lds_chunk(row, clo + 1, tl & 31), o);
-    bf16* gp = L + e0 - sh + p0;                                // 16-byte aligned
-    if (p0 >= sh && p0 + 8 <= sh + nv) {
-      *reinterpret_cast<uint4*>(gp) = w;
-    } else {
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (p0 + e >= sh && p0 + e < sh + nv) gp[e] = bf16(ww[e >> 1] >> (16 * (e & 1)));
-    }
   }
 }
 
