@@ -109,8 +109,11 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   }
 
   // prefetch registers: K chunks and U key pairs; rows/cols outside the sequence are zero
-  uint4 kr[KCH], ur0[UCH], ur1[UCH];
-  auto gload = [&](int kb) {
+  struct RegSet { uint4 kr[KCH], ur0[UCH], ur1[UCH]; };
+  auto gload = [&](RegSet& R, int kb) {
+    uint4 (&kr)[KCH] = R.kr;
+    uint4 (&ur0)[UCH] = R.ur0;
+    uint4 (&ur1)[UCH] = R.ur1;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
@@ -130,7 +133,10 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     }
   };
   // K as is; U transposed to U^T [d][key], written as (key, key+1) pairs
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const RegSet& R, int buf) {
+    const uint4 (&kr)[KCH] = R.kr;
+    const uint4 (&ur0)[UCH] = R.ur0;
+    const uint4 (&ur1)[UCH] = R.ur1;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
@@ -159,18 +165,12 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   for (int i = 0; i < NDT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 domain) and lane-partial sum
+  float m_run = -INFINITY, l_run = 0.f;   // exponent reference (log2 domain) and lane-partial sum
   const float sc = a.scale_log2;
 
   const int kv_end = min(T_seq, q0 + BQ);  // keys [0, kv_end) can be visible to this block
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kb = 0, it = 0; kb < kv_end; kb += BKV, ++it) {
-    const int cur = it & 1;
-    const bool more = kb + BKV < kv_end;
-    if (more) gload(kb + BKV);
-
+  // one key tile: scores, online softmax, O^T update, from LDS buffer `cur`
+  auto tile = [&](int kb, int cur) {
     if (kb <= qw0 + 31) {  // otherwise every key of this tile is in this wave's future
       f32x16 s[NST];
 #pragma unroll
@@ -194,7 +194,11 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
-      const float m_new = fmaxf(m_run, mx);
+      // The exponent reference moves only when the tile's maximum exceeds it
+      // by more than 8 (log2 units): probabilities stay below 2^8, which fp32
+      // sums and bf16 P tolerate, and the O rescale below is skipped whenever
+      // no lane of the wave moved its reference (alpha == 1 exactly).
+      const float m_new = mx > m_run + 8.f ? mx : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
@@ -207,10 +211,12 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
         }
       l_run = l_run * alpha + psum;
       m_run = m_new;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
 #pragma unroll
       for (int st = 0; st < NST; ++st)
 #pragma unroll
@@ -224,8 +230,31 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
           }
         }
     }
-    if (more) sstore(cur ^ 1);
+  };
+  // Global loads run two tiles ahead (register sets RA and RB in turn): tile
+  // t + 2 is requested while tile t is computed, and tile t + 1, requested
+  // one tile earlier, is written to the other LDS buffer after it.  A block
+  // walks up to T / 64 tiles one after another, so the load latency has to
+  // hide under more than one tile's work.
+  RegSet RA, RB;
+  gload(RA, 0);
+  sstore(RA, 0);
+  __syncthreads();
+  if (BKV < kv_end) gload(RA, BKV);
+  for (int kb = 0, it = 0; kb < kv_end;) {
+    if (kb + 2 * BKV < kv_end) gload(RB, kb + 2 * BKV);
+    tile(kb, it & 1);
+    if (kb + BKV < kv_end) sstore(RA, (it + 1) & 1);
     __syncthreads();
+    kb += BKV;
+    ++it;
+    if (kb >= kv_end) break;
+    if (kb + 2 * BKV < kv_end) gload(RA, kb + 2 * BKV);
+    tile(kb, it & 1);
+    if (kb + BKV < kv_end) sstore(RB, (it + 1) & 1);
+    __syncthreads();
+    kb += BKV;
+    ++it;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
