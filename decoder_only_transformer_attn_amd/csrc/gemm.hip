@@ -232,6 +232,43 @@ template <int DPW> __device__ __forceinline__ void wait_groups(int g) {
   }
 }
 
+// Tile (m0, n0)'s load plan: buffer resources over the tile's A and W rows
+// and each lane's offsets; issue(t) sends this wave's share of stage t.
+template <int BM, int BN, int WM, int WN, int K, int NST, int BK>
+struct DmaLoads {
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  uint32_t voff[D::DPW];
+  int wave;
+  __device__ __forceinline__ DmaLoads(const bf16* A, const bf16* W, int M, int N, int m0, int n0) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rsA = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)min(BM, M - m0) * K * sizeof(bf16)));
+    rsB = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)min(BN, N - n0) * K * sizeof(bf16)));
+#pragma unroll
+    for (int d = 0; d < D::DPW; ++d) {
+      const int ins = wave + d * D::NW;
+      constexpr int IA = BM / D::RPI;   // instructions covering A
+      const int row = (ins < IA ? ins : ins - IA) * D::RPI + lane / D::CPR, slot = lane % D::CPR;
+      voff[d] = (uint32_t)((row * K + swz<D::CPR>(row, slot) * 8) * sizeof(bf16));
+    }
+  }
+  __device__ __forceinline__ void issue(int t, const Stages& st) const {
+    char* s = st.p[t % NST];
+#pragma unroll
+    for (int d = 0; d < D::DPW; ++d) {
+      const int ins = wave + d * D::NW;
+      dma16(ins < BM / D::RPI ? rsA : rsB, s + ins * 1024, voff[d], t * BK * 2);
+    }
+  }
+  // the first NST - 1 stages of the tile
+  __device__ __forceinline__ void prologue(const Stages& st) const {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+      if (t < K / BK) issue(t, st);
+  }
+};
+
 template <int BM, int BN, int WM, int WN, int K, int NST, int BK>
 __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N,
                                              int m0, int n0, const Stages& st, f32x16 (&acc)[WM / 32][WN / 32]) {
@@ -254,24 +291,7 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
   // Stage layout: A rows [0, BM) then W rows, ROWB bytes each.  Load
   // instruction i (RPI rows) goes to LDS offset 1024 i and is issued by wave
   // i % NW; the wave index is uniform, so the A/W choice stays scalar.
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)min(BM, M - m0) * K * sizeof(bf16)));
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)min(BN, N - n0) * K * sizeof(bf16)));
-  uint32_t voff[D::DPW];
-#pragma unroll
-  for (int d = 0; d < D::DPW; ++d) {
-    const int ins = wave + d * D::NW;
-    constexpr int IA = BM / D::RPI;   // instructions covering A
-    const int row = (ins < IA ? ins : ins - IA) * D::RPI + lane / CPR, slot = lane % CPR;
-    voff[d] = (uint32_t)((row * K + swz<CPR>(row, slot) * 8) * sizeof(bf16));
-  }
-  auto issue = [&](int t) {
-    char* s = st.p[t % NST];
-#pragma unroll
-    for (int d = 0; d < D::DPW; ++d) {
-      const int ins = wave + d * D::NW;
-      dma16(ins < BM / D::RPI ? rsA : rsB, s + ins * 1024, voff[d], t * BK * 2);
-    }
-  };
+  const DmaLoads<BM, BN, WM, WN, K, NST, BK> ld(A, W, M, N, m0, n0);
   const int lrow = lane & 31, g = lane >> 5;
   auto ldfrag = [&](const char* s, int ks, bf16x8 (&af)[D::TM], bf16x8 (&bfr)[D::TN]) {
     const int c = ks * 2 + g;
@@ -293,14 +313,12 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 #pragma unroll
       for (int j = 0; j < D::TN; ++j) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
   };
-#pragma unroll
-  for (int t = 0; t < NST - 1; ++t)
-    if (t < NK) issue(t);
+  ld.prologue(st);
 #pragma unroll
   for (int t = 0; t < NK; ++t) {
     wait_groups<D::DPW>(min(NST - 2, NK - 1 - t));   // this wave's loads of stage t have landed
     lds_barrier();                                   // ... and every other wave's
-    if (t + NST - 1 < NK) issue(t + NST - 1);        // into the stage consumed at step t - 1
+    if (t + NST - 1 < NK) ld.issue(t + NST - 1, st); // into the stage consumed at step t - 1
     const char* s = st.p[t % NST];
     bf16x8 af[2][D::TM], bfr[2][D::TN];
     ldfrag(s, 0, af[0], bfr[0]);
@@ -862,8 +880,6 @@ __global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict
                                                           int V, int Mtok, HeadArgs ha) {
   constexpr int BM = 256, BN = 256, WM = 64, WN = 128;   // BM: vocab, BN: tokens
   typedef DmaCfg<BM, BN, WM, WN, 2, 64> D;                 // two 64-deep stages
-  constexpr int SUB = 64 * BM * 2;                         // 64 staged token rows of logits
-  static_assert(2 * SUB == D::STAGE, "a stage holds 128 staged token rows");
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
   __shared__ float red[D::NWM][BN][2];
