@@ -875,15 +875,17 @@ __device__ __forceinline__ uint4 window8(uint4 lo, uint4 hi, int o) {
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-template <int K>
-__global__ void __launch_bounds__(512) head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act,
-                                                          int V, int Mtok, HeadArgs ha) {
-  constexpr int BM = 256, BN = 256, WM = 64, WN = 128;   // BM: vocab, BN: tokens
+template <int K, int BM, int BN, int WM, int WN>   // BM: vocab, BN: tokens
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN, 2, 64>())))
+head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, int V, int Mtok, HeadArgs ha) {
   typedef DmaCfg<BM, BN, WM, WN, 2, 64> D;                 // two 64-deep stages
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
-  __shared__ float red[D::NWM][BN][2];
-  __shared__ int redi[D::NWM][BN];
+  // per-wave token partials, in the first stage once the main loop is done
+  static_assert(D::NWM * BN * 3 * 4 <= D::STAGE, "partials must fit in a stage");
+  float (*red)[BN][2] = reinterpret_cast<float (*)[BN][2]>(s0);
+  int (*redi)[BN] = reinterpret_cast<int (*)[BN]>(s0 + D::NWM * BN * 2 * 4);
   const int num_v = (V + BM - 1) / BM, num_t = (Mtok + BN - 1) / BN;
   int tt, vt;
   tile_of(blockIdx.x, gridDim.x, num_t, num_v, tt, vt);   // groups of token tiles sweep the vocab
@@ -1257,10 +1259,13 @@ hipError_t launch_linear_ln(const LnFuse& f, const void* W, const void* bias, in
   return run_skinny(nullptr, 0, &ln, (const bf16*)W, K, M, N, K, e, st);
 }
 
-int head_ntiles(int dtype, int M, int V, bool argmax) {
+// bf16 head tile for C = 768 (vocab x tokens, per-wave vocab x tokens)
+constexpr int HEAD_BM = 192, HEAD_BN = 128, HEAD_WM = 96, HEAD_WN = 64;
+
+int head_ntiles(int dtype, int M, int V, int C, bool argmax) {
   (void)M;
   (void)argmax;
-  const int bn = dtype == 0 ? 64 : 256;
+  const int bn = dtype == 0 ? 64 : (C == 768 ? HEAD_BM : 256);
   return (V + bn - 1) / bn;
 }
 
@@ -1285,8 +1290,11 @@ hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int 
     ha.ntiles = (V + BN - 1) / BN;
     const int blocks = ((M + BM - 1) / BM) * ha.ntiles;
     if (C == 768) {
-      hipLaunchKernelGGL((head_ce_dma_kernel<768>), dim3(blocks), dim3(512), 0, st, (const bf16*)wte, (const bf16*)A, V,
-                         M, ha);
+      typedef DmaCfg<HEAD_BM, HEAD_BN, HEAD_WM, HEAD_WN, 2, 64> HD;
+      ha.ntiles = (V + HEAD_BM - 1) / HEAD_BM;
+      const int hblocks = ((M + HEAD_BN - 1) / HEAD_BN) * ha.ntiles;
+      hipLaunchKernelGGL((head_ce_dma_kernel<768, HEAD_BM, HEAD_BN, HEAD_WM, HEAD_WN>), dim3(hblocks), dim3(HD::NT), 0,
+                         st, (const bf16*)wte, (const bf16*)A, V, M, ha);
       return hipGetLastError();
     }
     if (C % 64 == 0)

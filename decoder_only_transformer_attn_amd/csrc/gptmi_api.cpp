@@ -115,7 +115,7 @@ Plan plan(const gpt_config* c, int B, int T, bool decode) {
   Plan p{};
   const size_t M = (size_t)B * T, C = c->n_embd, F = c->n_ff, es = esize(c);
   const size_t head_rows = decode ? (size_t)B : M;
-  p.ntiles = head_ntiles(c->dtype, (int)head_rows, c->vocab, decode);
+  p.ntiles = head_ntiles(c->dtype, (int)head_rows, c->vocab, c->n_embd, decode);
   p.nblocks = ce_reduce_blocks((int)M);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };

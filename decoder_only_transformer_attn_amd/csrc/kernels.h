@@ -75,7 +75,7 @@ hipError_t launch_qkv_ln(const QKVArgs& a, const LnFuse& f, hipStream_t st);
 hipError_t launch_linear_ln(const LnFuse& f, const void* W, const void* bias, int M, int N, int K, void* out, int ldo,
                             int act, hipStream_t st);
 // Vocabulary tiles of the head's partials for M rows (CE or argmax mode).
-int head_ntiles(int dtype, int M, int V, bool argmax);
+int head_ntiles(int dtype, int M, int V, int C, bool argmax);
 // Tied head over M token rows.  CE mode (part_idx == NULL): softmax partials
 // and target logits for the next-token loss.  Argmax mode (part_idx != NULL):
 // per-(row, N-tile) maximum and its lowest index; part_sum/tgt unused.

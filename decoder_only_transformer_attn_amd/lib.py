@@ -12,7 +12,8 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgptmi.so")
+# the in-tree build, unless GPTMI_LIB names another copy of the library
+LIB_PATH = os.environ.get("GPTMI_LIB") or os.path.join(HERE, "libgptmi.so")
 
 GPT_OK = 0
 STATUS = {0: "GPT_OK", -1: "GPT_ERR_NULL", -2: "GPT_ERR_CONFIG", -3: "GPT_ERR_SEQ_TOO_LONG",
