@@ -621,106 +621,27 @@ gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, i
 // (rows 0-31 in acc[0], 32-63 in acc[1]).  Returns true in wave 0 only.
 constexpr int SK_WAVES = 8;
 constexpr int SK_RED = 2 * 16 * 64;   // floats of one wave's partial tile
-constexpr int SK_LN_MAXK = 768;       // widest LayerNorm input built in LDS
-constexpr int SK_LN_LD = SK_LN_MAXK + 8;
-constexpr int SK_SMEM_LN = 64 * SK_LN_LD * 2;   // bytes; also holds the reduction afterwards
 constexpr int SK_SMEM = SK_WAVES * SK_RED * 4;
-static_assert(SK_SMEM_LN >= SK_SMEM, "reduction must fit in the LayerNorm tile");
 
-// Fused LayerNorm input of a skinny product: A = LN(x; g, b) of fp32 rows.
-struct LnIn {
-  const float* x;
-  const bf16* g;
-  const bf16* b;
-  float eps;
-};
-
-// Builds A = LN(x) for rows 0..63 (zero past M) in LDS, [64][K + 8] bf16: one
-// wave per row (8 rows per wave), two-pass mean/variance over registers.  The
-// gain/bias and all of the wave's rows are loaded before any arithmetic, so
-// the global-load latency is paid once.  K <= 768.
-__device__ __forceinline__ void skinny_ln_tile(const LnIn& ln, int M, int K, bf16* sA) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ld = K + 8;
-  constexpr int NCH = SK_LN_MAXK / 256;   // float4 chunks per lane and row
-  constexpr int RPW = 64 / SK_WAVES;      // rows per wave
-  uint2 gq[NCH], bq[NCH];
-  float4 v[RPW][NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = (j * 64 + lane) * 4;
-    gq[j] = c < K ? *reinterpret_cast<const uint2*>(ln.g + c) : make_uint2(0, 0);
-    bq[j] = c < K ? *reinterpret_cast<const uint2*>(ln.b + c) : make_uint2(0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int row = wave + i * SK_WAVES;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = (j * 64 + lane) * 4;
-      v[i][j] = (row < M && c < K) ? *reinterpret_cast<const float4*>(ln.x + (size_t)row * K + c)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int row = wave + i * SK_WAVES;
-    float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) sum += (v[i][j].x + v[i][j].y) + (v[i][j].z + v[i][j].w);
-    const float mean = wave_sum(sum) / (float)K;
-    float s2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j)
-      if ((j * 64 + lane) * 4 < K) {
-        const float d0 = v[i][j].x - mean, d1 = v[i][j].y - mean, d2 = v[i][j].z - mean, d3 = v[i][j].w - mean;
-        s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
-      }
-    const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)K + ln.eps);
-    const bool live = row < M;
-    bf16* dst = sA + row * ld;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = (j * 64 + lane) * 4;
-      if (c < K) {
-        const float x4[4] = {v[i][j].x, v[i][j].y, v[i][j].z, v[i][j].w};
-        const float g4[4] = {__uint_as_float(gq[j].x << 16), __uint_as_float(gq[j].x & 0xffff0000u),
-                             __uint_as_float(gq[j].y << 16), __uint_as_float(gq[j].y & 0xffff0000u)};
-        const float b4[4] = {__uint_as_float(bq[j].x << 16), __uint_as_float(bq[j].x & 0xffff0000u),
-                             __uint_as_float(bq[j].y << 16), __uint_as_float(bq[j].y & 0xffff0000u)};
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = live ? (x4[e] - mean) * rstd * g4[e] + b4[e] : 0.f;
-        *reinterpret_cast<uint2*>(dst + c) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      }
-    }
-  }
-}
-
-// LN_A = false: A [M, K] bf16 in global memory (lda).  LN_A = true: A is
-// LN(x) built by the block in LDS first (K <= 768), then read from there.
-// `smem` holds the LayerNorm tile (LN_A) and then the partial-sum reduction.
-template <bool LN_A>
-__device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int lda, const LnIn& ln,
-                                                const bf16* __restrict__ W, int ldw, int M, int N, int K, int n0,
-                                                char* smem, f32x16 (&acc)[2][1]) {
+// A [M, K] bf16 in global memory (lda); `smem` holds the partial-sum reduction.
+// U k-steps of loads are in flight per wave (more for long K: fewer round trips).
+template <int U>
+__device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W,
+                                                int ldw, int M, int N, int K, int n0, char* smem,
+                                                f32x16 (&acc)[2][1]) {
   typedef Mfma<bf16> MF;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  bf16* sA = reinterpret_cast<bf16*>(smem);
   const int steps = (K + 15) >> 4;
   const int per = (steps + SK_WAVES - 1) / SK_WAVES;
   const int s_begin = wave * per, s_end = min(steps, s_begin + per);
   const int nrows = min(32, N - n0);
   // rows past M (A) and past N (W) lie outside the resources and read as zero
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, LN_A ? 0u : (uint32_t)((size_t)M * lda * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((size_t)M * lda * sizeof(bf16)));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * ldw, (uint32_t)((size_t)nrows * ldw * sizeof(bf16)));
   const int r = lane & 31, kh = (lane >> 5) * MF::KPL;
   const uint32_t oa0 = (uint32_t)(r * lda + kh) * 2, oa1 = (uint32_t)((r + 32) * lda + kh) * 2;
   const uint32_t ow = (uint32_t)(r * ldw + kh) * 2;
-  const bf16* la0 = sA + r * (K + 8) + kh;
-  const bf16* la1 = la0 + 32 * (K + 8);
   const uint4 z = make_uint4(0, 0, 0, 0);
-  constexpr int U = 8;
   uint4 w[U];
   auto load_w = [&](int s) {
 #pragma unroll
@@ -730,12 +651,7 @@ __device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int 
       w[u] = ok ? buf_load16(rw, ow, k * 2) : z;
     }
   };
-  // the first weight batch is in flight while the LayerNorm tile is built
   load_w(s_begin);
-  if constexpr (LN_A) {
-    skinny_ln_tile(ln, M, K, sA);
-    __syncthreads();
-  }
   f32x16 c0, c1;
 #pragma unroll
   for (int e = 0; e < 16; ++e) { c0[e] = 0.f; c1[e] = 0.f; }
@@ -746,13 +662,8 @@ __device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int 
     for (int u = 0; u < U; ++u) {
       const int k = (s + u) * 16;
       const bool ok = s + u < s_end && k + kh < K;
-      if constexpr (LN_A) {
-        a0[u] = ok ? *reinterpret_cast<const uint4*>(la0 + k) : z;
-        a1[u] = ok ? *reinterpret_cast<const uint4*>(la1 + k) : z;
-      } else {
-        a0[u] = ok ? buf_load16(ra, oa0, k * 2) : z;
-        a1[u] = ok ? buf_load16(ra, oa1, k * 2) : z;
-      }
+      a0[u] = ok ? buf_load16(ra, oa0, k * 2) : z;
+      a1[u] = ok ? buf_load16(ra, oa1, k * 2) : z;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -762,7 +673,6 @@ __device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int 
     }
   }
   float* red = reinterpret_cast<float*>(smem);
-  if constexpr (LN_A) __syncthreads();   // every wave is done with the LayerNorm tile
   float* mine = red + wave * SK_RED;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -786,28 +696,29 @@ __device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int 
   return true;
 }
 
-template <typename Epi, bool LN_A>
-__global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_kernel(const bf16* __restrict__ A, int lda, LnIn ln,
+template <typename Epi, int U>
+__global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_kernel(const bf16* __restrict__ A, int lda,
                                                                    const bf16* __restrict__ W, int ldw, int M, int N,
                                                                    int K, Epi epi) {
-  __shared__ __align__(16) char smem[LN_A ? SK_SMEM_LN : SK_SMEM];
+  __shared__ __align__(16) char smem[SK_SMEM];
   const int n0 = blockIdx.x * 32;
   float2 pre[2][1][8];
   typename Epi::Col colv[1];
   if ((threadIdx.x >> 6) == 0) preload_pairs<2, 1>(pre, colv, 0, n0, M, N, epi);
   f32x16 acc[2][1];
-  if (!skinny_mainloop<LN_A>(A, lda, ln, W, ldw, M, N, K, n0, smem, acc)) return;
+  if (!skinny_mainloop<U>(A, lda, W, ldw, M, N, K, n0, smem, acc)) return;
   epilogue_pairs<2, 1>(acc, pre, colv, 0, n0, M, N, epi);
 }
 
 template <typename Epi>
-static hipError_t run_skinny(const bf16* A, int lda, const LnIn* ln, const bf16* W, int ldw, int M, int N, int K,
-                             const Epi& epi, hipStream_t st) {
-  const dim3 grid((N + 31) / 32), block(SK_WAVES * 64);
-  if (ln)
-    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, true>), grid, block, 0, st, A, lda, *ln, W, ldw, M, N, K, epi);
+static hipError_t run_skinny(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
+                             hipStream_t st) {
+  if (K <= 1024)
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 8>), dim3((N + 31) / 32), dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw, M,
+                       N, K, epi);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, false>), grid, block, 0, st, A, lda, LnIn{}, W, ldw, M, N, K, epi);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 12>), dim3((N + 31) / 32), dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw,
+                       M, N, K, epi);
   return hipGetLastError();
 }
 
@@ -1185,7 +1096,7 @@ static hipError_t run_gemm_dma_k(const bf16* A, const bf16* W, int M, int N, con
 template <typename Epi>
 static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
                                 hipStream_t st) {
-  if (M <= 64 && lda % 8 == 0 && ldw % 8 == 0) return run_skinny(A, lda, nullptr, W, ldw, M, N, K, epi, st);
+  if (M <= 64 && lda % 8 == 0 && ldw % 8 == 0) return run_skinny(A, lda, W, ldw, M, N, K, epi, st);
   const long long tiles256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= 64 && lda == K && ldw == K) {
     if (K == 768) return run_gemm_dma_k<768>(A, W, M, N, epi, st);
@@ -1239,24 +1150,6 @@ static hipError_t qkv_t(const QKVArgs& a, hipStream_t st) {
 hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st) {
   if (dtype == 0) return qkv_t<float>(a, st);
   return qkv_t<bf16>(a, st);
-}
-
-bool skinny_ln_ok(int dtype, int M, int K) { return dtype == 1 && M <= 64 && K <= SK_LN_MAXK && K % 8 == 0; }
-
-hipError_t launch_qkv_ln(const QKVArgs& a, const LnFuse& f, hipStream_t st) {
-  if (!skinny_ln_ok(1, a.M, a.C)) return hipErrorInvalidValue;
-  const LnIn ln{f.x, (const bf16*)f.g, (const bf16*)f.b, f.eps};
-  EpiQKV<bf16> e{(const bf16*)a.bias, a.C, a.H, a.D, a.T_seq, 1.0f / (float)a.T_seq, (bf16*)a.q, a.q_bh,
-                 (bf16*)a.k, a.k_bh, (bf16*)a.v, a.v_bh, a.pos, a.Tk};
-  return run_skinny(nullptr, 0, &ln, (const bf16*)a.W, a.C, a.M, 3 * a.C, a.C, e, st);
-}
-
-hipError_t launch_linear_ln(const LnFuse& f, const void* W, const void* bias, int M, int N, int K, void* out, int ldo,
-                            int act, hipStream_t st) {
-  if (!skinny_ln_ok(1, M, K)) return hipErrorInvalidValue;
-  const LnIn ln{f.x, (const bf16*)f.g, (const bf16*)f.b, f.eps};
-  EpiAct<bf16> e{(const bf16*)bias, out, ldo, act, 0};
-  return run_skinny(nullptr, 0, &ln, (const bf16*)W, K, M, N, K, e, st);
 }
 
 // bf16 head tile for C = 768 (vocab x tokens, per-wave vocab x tokens)

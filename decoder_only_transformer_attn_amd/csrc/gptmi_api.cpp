@@ -193,9 +193,6 @@ int run_blocks(const Pass& s) {
   la.idx = nullptr; la.pos = nullptr;
 
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-  // A decode step's products see at most 64 rows: LN1 and LN2 are then built
-  // inside the c_attn and c_fc kernels instead of being launched on their own.
-  const bool fuse_ln = s.mode == STEP && skinny_ln_ok(dt, M, C);
   for (int l = 0; l < L; ++l) {
     const LayerP w = P.layer(l);
     const bool last = l == L - 1;
@@ -211,10 +208,7 @@ int run_blocks(const Pass& s) {
     qa.pos = s.mode == STEP ? s.pos : nullptr;
     qa.Tk = s.mode == FORWARD ? T : s.Tmax;
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
-    if (fuse_ln)
-      GPT_TRY(launch_qkv_ln(qa, LnFuse{x, P.at(w.ln1_g), P.at(w.ln1_b), cfg->ln_eps}, s.st));
-    else
-      GPT_TRY(launch_qkv(dt, qa, s.st));
+    GPT_TRY(launch_qkv(dt, qa, s.st));
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, true));
     if (s.mode == STEP) {
@@ -236,24 +230,17 @@ int run_blocks(const Pass& s) {
     GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, true));
     GPT_TRY(launch_linear_resid(dt, o, C, P.at(w.proj_w), C, P.at(w.proj_b), M, C, C, x, C, s.st));
     GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, false));
-    if (fuse_ln) {
-      GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
-      GPT_TRY(launch_linear_ln(LnFuse{x, P.at(w.ln2_g), P.at(w.ln2_b), cfg->ln_eps}, P.at(w.fc_w), P.at(w.fc_b), M, F,
-                               C, h, F, 1, s.st));
-      GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
-    } else {
-      la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
-      GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
-      GPT_TRY(launch_layernorm(dt, la, s.st));
-      GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
-      GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
-      GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, 1, 0, s.st));
-      GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
-    }
+    la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
+    GPT_TRY(launch_layernorm(dt, la, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
+    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, 1, 0, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, true));
     GPT_TRY(launch_linear_resid(dt, h, F, P.at(w.fcproj_w), F, P.at(w.fcproj_b), M, C, F, x, C, s.st));
     GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, false));
-    if (l + 1 < L && !fuse_ln) {   // ln_1 of the next block (ln_f is applied by the caller)
+    if (l + 1 < L) {   // ln_1 of the next block (ln_f is applied by the caller)
       la.g = P.at(P.layer(l + 1).ln1_g); la.b = P.at(P.layer(l + 1).ln1_b);
       GPT_TRY(launch_layernorm(dt, la, s.st));
     }

@@ -62,18 +62,6 @@ hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W,
                                int N, int K, float* x, int ldx, hipStream_t st);
 hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
-// LayerNorm fused into a skinny product's input: A = LN(x; g, b), x fp32 [M, K].
-struct LnFuse {
-  const float* x;
-  const void* g;
-  const void* b;
-  float eps;
-};
-// bf16, M <= 64, K <= 768: the product builds LN(x) itself (no separate LayerNorm launch).
-bool skinny_ln_ok(int dtype, int M, int K);
-hipError_t launch_qkv_ln(const QKVArgs& a, const LnFuse& f, hipStream_t st);
-hipError_t launch_linear_ln(const LnFuse& f, const void* W, const void* bias, int M, int N, int K, void* out, int ldo,
-                            int act, hipStream_t st);
 // Vocabulary tiles of the head's partials for M rows (CE or argmax mode).
 int head_ntiles(int dtype, int M, int V, int C, bool argmax);
 // Tied head over M token rows.  CE mode (part_idx == NULL): softmax partials
