@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "28169d60a13f67b9079fac789de21263dbd7163ce47c1c37a709c6f6c96b83ba",
-                "bytes": 1839769064}
+HEAD_TRAFFIC = {"gemm_src_sha256": "19026da8f79a829a05619eaf1b2897d1616b3129f372e9f576229284800aa211",
+                "bytes": 2004122079}
 
 
 def src_sha(rel):
@@ -219,7 +219,7 @@ def bench_forward(args, w):
         "flops_per_step": flops,
         "loss": round(loss, 5),
         "wall_s_timed": round(t_wall, 3),
-        "roofline": {"bound": "mfma", "kernel": "head_ce_dma_kernel (tied head GEMM + CE partials + bf16 logits)",
+        "roofline": {"bound": "mfma", "kernel": "head_ce_dma_kernel<768,192,128,96,64> (tied head GEMM + CE partials + bf16 logits)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(head_ms, 4), "flops_per_launch": head_flops},
