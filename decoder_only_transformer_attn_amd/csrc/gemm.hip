@@ -14,6 +14,8 @@
 //   EpiAct   : + bias, optional tanh-GELU, store in the output dtype
 //   head     : optional logits store + per-(row, N-tile) softmax partials
 //              (max, sum exp) and the target logit, all from fp32 accumulators.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -374,35 +376,43 @@ struct RawPair {
   }
 };
 
-template <typename T>
-struct EpiAct {  // out[m, n] = act(v + bias[n])
+template <typename T, int ACT = 0, bool F32OUT = false>
+struct EpiAct {  // out[m, n] = act(v + bias[n]); ACT 1 = tanh GELU; F32OUT: store fp32 instead of T
   static constexpr bool kPreload = false;
   static constexpr bool kCompact = true;
   typedef int Row;
   typedef RawPair<T> Col;
   typedef RawPair<T> ColX;
+  typedef typename std::conditional<F32OUT, float, T>::type O;
   __device__ __forceinline__ Row row(int) const { return 0; }
   __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
   const T* bias;
   void* out;
   int ldo;
-  int act;       // 0 none, 1 tanh-GELU
-  int out_f32;   // store fp32 instead of T
   __device__ __forceinline__ Col col(int n, bool has_b) const {
     // branch-free: without a bias the (valid) output row is read instead and ignored
     const T* bp = bias ? bias : reinterpret_cast<const T*>(out);
     return Col{Col::bits(bp[n]), Col::bits(bp[has_b ? n + 1 : n])};
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ float2 value(float a, float b, const Col& bs) const {
+    const float w = bias ? 1.f : 0.f;   // uniform
+    a = fmaf(w, Col::f32(bs.a), a);
+    b = fmaf(w, Col::f32(bs.b), b);
+    if constexpr (ACT == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
+    return make_float2(a, b);
+  }
   __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, const Col& bs, float2) const {
-    if (bias) {
-      a += Col::f32(bs.a);
-      b += Col::f32(bs.b);
-    }
-    if (act == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
-    const size_t o = (size_t)m * ldo + n;
-    if (out_f32) store_pair(reinterpret_cast<float*>(out) + o, a, b, has_b, (ldo & 1) == 0);
-    else store_pair(reinterpret_cast<T*>(out) + o, a, b, has_b, (ldo & 1) == 0);
+    const float2 v = value(a, b, bs);
+    store_pair(reinterpret_cast<O*>(out) + (size_t)m * ldo + n, v.x, v.y, has_b, (ldo & 1) == 0);
+  }
+  // interior tiles: both columns exist and pairs are aligned
+  __device__ __forceinline__ bool vec_ok() const { return (ldo & 1) == 0; }
+  __device__ __forceinline__ void pair_in(Row, int m, int n, float a, float b, const Col& bs, float2) const {
+    const float2 v = value(a, b, bs);
+    O* p = reinterpret_cast<O*>(out) + (size_t)m * ldo + n;
+    if constexpr (sizeof(O) == 4) *reinterpret_cast<float2*>(p) = v;
+    else *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v.x, v.y);
   }
 };
 
@@ -430,6 +440,11 @@ struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
     a = xo.x + (a + Col::f32(bs.a));
     if (has_b) b = xo.y + (b + Col::f32(bs.b));
     store_pair(x + (size_t)m * ldx + n, a, b, has_b, (ldx & 1) == 0);
+  }
+  __device__ __forceinline__ bool vec_ok() const { return (ldx & 1) == 0; }
+  __device__ __forceinline__ void pair_in(Row, int m, int n, float a, float b, const Col& bs, float2 xo) const {
+    *reinterpret_cast<float2*>(x + (size_t)m * ldx + n) =
+        make_float2(xo.x + (a + Col::f32(bs.a)), xo.y + (b + Col::f32(bs.b)));
   }
 };
 
@@ -479,6 +494,11 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
     if (!cl.is_q && (r.tc < 0 || r.tc >= Tk)) return;   // outside the cache: contract violation, nothing written
     T* dst = cl.base + (long long)r.b * cl.b_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
     store_pair(dst, a + RawPair<T>::f32(cl.bias.a), b + RawPair<T>::f32(cl.bias.b), true, true);
+  }
+  __device__ __forceinline__ bool vec_ok() const { return true; }
+  __device__ __forceinline__ void pair_in(const Row& r, int m, int n, float a, float b, const ColX& cl,
+                                          float2 pre) const {
+    pair(r, m, n, a, b, true, cl, pre);
   }
 };
 
@@ -531,6 +551,25 @@ __device__ __forceinline__ void epilogue_pairs(const f32x16 (&acc)[TM][TN], cons
     int m, n;
     pair_coords<TM, TN>(0, j, 0, mbase, nbase, m, n);
     cx[j] = epi.colx(min(n, N - 1), colv[j]);
+  }
+  // a wave tile that lies wholly inside [0, M) x [0, N) (uniform test) takes
+  // the unguarded path: no per-pair bounds checks, always a paired store
+  if (mbase + TM * 32 <= M && nbase + TN * 32 <= N && epi.vec_ok()) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int rp = 0; rp < 8; ++rp) {
+        int m, n0;
+        pair_coords<TM, TN>(i, 0, rp, mbase, nbase, m, n0);
+        const typename Epi::Row rc = epi.row(m);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float v0 = acc[i][j][2 * rp], v1 = acc[i][j][2 * rp + 1];
+          const float recv = __shfl_xor(odd ? v0 : v1, 1, 64);
+          epi.pair_in(rc, m, n0 + j * 32, odd ? recv : v0, odd ? v1 : recv, cx[j], pre[i][j][rp]);
+        }
+      }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -1117,8 +1156,13 @@ static hipError_t dispatch_gemm(const float* A, int lda, const float* W, int ldw
 template <typename T>
 static hipError_t linear_t(const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N, int K,
                            void* out, int ldo, int act, int out_f32, hipStream_t st) {
-  EpiAct<T> e{(const T*)bias, out, ldo, act, out_f32};
-  return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, e, st);
+  if (act == 1 && !out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
+                                                 EpiAct<T, 1, false>{(const T*)bias, out, ldo}, st);
+  if (act == 1) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
+                                     EpiAct<T, 1, true>{(const T*)bias, out, ldo}, st);
+  if (!out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
+                                     EpiAct<T, 0, false>{(const T*)bias, out, ldo}, st);
+  return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, EpiAct<T, 0, true>{(const T*)bias, out, ldo}, st);
 }
 
 hipError_t launch_linear(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N,
