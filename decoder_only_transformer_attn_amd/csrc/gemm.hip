@@ -222,15 +222,18 @@ struct Stages {
 
 // Wait until at most g of this wave's load groups (DPW loads each) are still
 // in flight; g is a constant once the K loop is unrolled.
+// (Counts past the counter's range only appear in cases a given stage count
+// never reaches, see the static_assert in dma_mainloop; they are clamped.)
 template <int DPW> __device__ __forceinline__ void wait_groups(int g) {
+  constexpr int C = 63;
   switch (g) {
     case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<DPW>(); break;
-    case 2: wait_vmcnt<2 * DPW>(); break;
-    case 3: wait_vmcnt<3 * DPW>(); break;
-    case 4: wait_vmcnt<4 * DPW>(); break;
-    case 5: wait_vmcnt<5 * DPW>(); break;
-    default: wait_vmcnt<6 * DPW>(); break;
+    case 1: wait_vmcnt<(DPW < C ? DPW : C)>(); break;
+    case 2: wait_vmcnt<(2 * DPW < C ? 2 * DPW : C)>(); break;
+    case 3: wait_vmcnt<(3 * DPW < C ? 3 * DPW : C)>(); break;
+    case 4: wait_vmcnt<(4 * DPW < C ? 4 * DPW : C)>(); break;
+    case 5: wait_vmcnt<(5 * DPW < C ? 5 * DPW : C)>(); break;
+    default: wait_vmcnt<(6 * DPW < C ? 6 * DPW : C)>(); break;
   }
 }
 
@@ -651,19 +654,87 @@ gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, i
 // ---------------------------------------------------------------------------
 // Skinny products: at most 64 rows (one token per sequence in a decode step,
 // or the last position of each prompt).  Every weight is used by at most 64
-// rows, so the weight stream from HBM sets the time and the kernel is built
-// to read W once at full bandwidth: a block owns 32 output columns and all
-// rows; its 8 waves split K into contiguous ranges and load their MFMA
-// fragments straight from global memory (no LDS staging; eight k-steps of
-// loads in flight per wave).  The eight partial 64 x 32 tiles are summed
-// through LDS and wave 0 holds the total in the usual accumulator layout
-// (rows 0-31 in acc[0], 32-63 in acc[1]).  Returns true in wave 0 only.
+// rows, so the weight stream from HBM sets the time.  Two kernels:
+//  * the LDS-staged one (rows contiguous, K a multiple of 128; further below)
+//    for every product of the model;
+//  * a register path for the rest: a block owns 32 output columns and all
+//    rows; its 8 waves split K into contiguous ranges and load their MFMA
+//    fragments straight from global memory (no LDS staging; U k-steps of
+//    loads in flight per wave).
+// Both sum the eight waves' partial 64 x 32 tiles through LDS; wave 0 then
+// holds the block's sum in the usual accumulator layout (rows 0-31 in
+// acc[0], 32-63 in acc[1]) and runs the epilogue.
 constexpr int SK_WAVES = 8;
 constexpr int SK_RED = 2 * 16 * 64;   // floats of one wave's partial tile
 constexpr int SK_SMEM = SK_WAVES * SK_RED * 4;
 
-// A [M, K] bf16 in global memory (lda); `smem` holds the partial-sum reduction.
-// U k-steps of loads are in flight per wave (more for long K: fewer round trips).
+// Split K over blocks (S = gridDim.y > 1), called by wave 0 with the block's
+// partial tile: publish it and count it on the column tile's counter.  Returns
+// true in the block that arrives last, which then holds the sum of the S
+// partials in split order and has reset the counter to zero.
+__device__ __forceinline__ bool skinny_split_finish(f32x16 (&acc)[2][1], float* __restrict__ part,
+                                                    int* __restrict__ cnt) {
+  const int lane = threadIdx.x & 63, S = gridDim.y;
+  float* const tile = part + (size_t)blockIdx.x * S * SK_RED;
+  float* const mine = tile + (size_t)blockIdx.y * SK_RED;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    mine[e * 64 + lane] = acc[0][0][e];
+    mine[1024 + e * 64 + lane] = acc[1][0][e];
+  }
+  // device scope: the blocks of one column tile may run on different XCDs
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(cnt + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, 64);
+  if (old != S - 1) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    acc[0][0][e] = tile[e * 64 + lane];
+    acc[1][0][e] = tile[1024 + e * 64 + lane];
+  }
+  for (int y = 1; y < S; ++y) {
+    const float* py = tile + (size_t)y * SK_RED;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc[0][0][e] += py[e * 64 + lane];
+      acc[1][0][e] += py[1024 + e * 64 + lane];
+    }
+  }
+  if (lane == 0) cnt[blockIdx.x] = 0;
+  return true;
+}
+
+// Sum of the eight waves' partial tiles through LDS (`red`, SK_SMEM bytes, free
+// on entry); wave 0 receives the total.  Returns true in wave 0 only.
+__device__ __forceinline__ bool skinny_block_sum(const f32x16& c0, const f32x16& c1, float* red, f32x16 (&acc)[2][1]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* mine = red + wave * SK_RED;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    mine[e * 64 + lane] = c0[e];
+    mine[1024 + e * 64 + lane] = c1[e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < SK_RED; e += SK_WAVES * 64) {
+    float t = red[e];
+#pragma unroll
+    for (int w2 = 1; w2 < SK_WAVES; ++w2) t += red[w2 * SK_RED + e];
+    red[e] = t;
+  }
+  __syncthreads();
+  if (wave != 0) return false;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    acc[0][0][e] = red[e * 64 + lane];
+    acc[1][0][e] = red[1024 + e * 64 + lane];
+  }
+  return true;
+}
+
+// A [M, K] bf16 in global memory (lda); `smem` holds the partial-sum
+// reduction.  U k-steps of loads are in flight per wave.
 template <int U>
 __device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W,
                                                 int ldw, int M, int N, int K, int n0, char* smem,
@@ -711,28 +782,7 @@ __device__ __forceinline__ bool skinny_mainloop(const bf16* __restrict__ A, int 
       c1 = MF::mma(__builtin_bit_cast(MF::frag, a1[u]), wf, c1);
     }
   }
-  float* red = reinterpret_cast<float*>(smem);
-  float* mine = red + wave * SK_RED;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    mine[e * 64 + lane] = c0[e];
-    mine[1024 + e * 64 + lane] = c1[e];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < SK_RED; e += SK_WAVES * 64) {
-    float t = red[e];
-#pragma unroll
-    for (int w2 = 1; w2 < SK_WAVES; ++w2) t += red[w2 * SK_RED + e];
-    red[e] = t;
-  }
-  __syncthreads();
-  if (wave != 0) return false;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    acc[0][0][e] = red[e * 64 + lane];
-    acc[1][0][e] = red[1024 + e * 64 + lane];
-  }
-  return true;
+  return skinny_block_sum(c0, c1, reinterpret_cast<float*>(smem), acc);
 }
 
 template <typename Epi, int U>
@@ -749,15 +799,114 @@ __global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_kernel(const bf16* 
   epilogue_pairs<2, 1>(acc, pre, colv, 0, n0, M, N, epi);
 }
 
+// Skinny products whose K range is staged in LDS with full-line DMA loads
+// (rows contiguous: lda = ldw = K, K a multiple of 64 NSTG).  The register
+// path above reads 32 bytes of 32 different rows per load instruction; here
+// every instruction reads eight whole 128-byte lines.  Block: 32 output
+// columns, all rows (<= 64), K range [k0, k0 + 64 NSTG) of split
+// blockIdx.y.  LDS: NSTG stages of 96 rows x 128 bytes (A rows 0-63, W rows
+// 64-95), chunk c of row r at slot swz<8>(r, c).  Every load is issued at
+// once; then each wave multiplies its share of the 4 NSTG k-substeps and the
+// eight partial tiles are summed in the (then free) stages.
+template <int NSTG>
+struct SkLds {
+  static constexpr int ROWS = 96, STAGE = ROWS * 128, NI = NSTG * ROWS / 8, DPW = NI / SK_WAVES;
+  static constexpr int BYTES = NSTG * STAGE > SK_SMEM ? NSTG * STAGE : SK_SMEM;
+  static_assert(NI % SK_WAVES == 0 && DPW < 64, "loads must split evenly over the waves");
+};
+
+template <typename Epi, int NSTG>
+__global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_lds_kernel(const bf16* __restrict__ A,
+                                                                       const bf16* __restrict__ W, int M, int N, int K,
+                                                                       Epi epi, float* __restrict__ part,
+                                                                       int* __restrict__ cnt) {
+  typedef SkLds<NSTG> L;
+  __shared__ __align__(1024) char lds[L::BYTES];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 32, k0 = blockIdx.y * NSTG * 64;
+  const int nrows = min(32, N - n0);
+  // rows past M (A) and past N (W) lie outside the resources and read as zero
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((size_t)M * K * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)nrows * K * sizeof(bf16)));
+#pragma unroll
+  for (int d = 0; d < L::DPW; ++d) {
+    const int ins = wave + d * SK_WAVES;           // uniform: stage ins / 12, rows 8 (ins % 12) ..
+    const int st = ins / 12, ri = ins % 12;
+    const int row = ri * 8 + lane / 8, slot = lane % 8;
+    const int grow = ri < 8 ? row : row - 64;
+    dma16(ri < 8 ? ra : rw, lds + st * L::STAGE + ri * 1024, (uint32_t)((grow * K + swz<8>(row, slot) * 8) * 2),
+          (uint32_t)((k0 + st * 64) * 2));
+  }
+  float2 pre[2][1][8];
+  typename Epi::Col colv[1];
+  if (wave == 0) preload_pairs<2, 1>(pre, colv, 0, n0, M, N, epi);
+  wait_vmcnt<0>();
+  lds_barrier();
+  typedef Mfma<bf16> MF;
+  f32x16 c0, c1;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) { c0[e] = 0.f; c1[e] = 0.f; }
+  const int lrow = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int it = 0; it < NSTG * 4 / SK_WAVES; ++it) {
+    const int j = it * SK_WAVES + wave, c = (j & 3) * 2 + g;
+    const char* s = lds + (j >> 2) * L::STAGE;
+    const MF::frag a0 = __builtin_bit_cast(MF::frag, *reinterpret_cast<const uint4*>(s + lrow * 128 + swz<8>(lrow, c) * 16));
+    const MF::frag a1 = __builtin_bit_cast(
+        MF::frag, *reinterpret_cast<const uint4*>(s + (lrow + 32) * 128 + swz<8>(lrow + 32, c) * 16));
+    const MF::frag wf = __builtin_bit_cast(
+        MF::frag, *reinterpret_cast<const uint4*>(s + (lrow + 64) * 128 + swz<8>(lrow + 64, c) * 16));
+    c0 = MF::mma(a0, wf, c0);
+    c1 = MF::mma(a1, wf, c1);
+  }
+  __syncthreads();   // the stages become the reduction buffer
+  f32x16 acc[2][1];
+  if (!skinny_block_sum(c0, c1, reinterpret_cast<float*>(lds), acc)) return;
+  if (gridDim.y > 1 && !skinny_split_finish(acc, part, cnt)) return;
+  epilogue_pairs<2, 1>(acc, pre, colv, 0, n0, M, N, epi);
+}
+
+template <int NSTG, typename Epi>
+static hipError_t run_skinny_lds(const bf16* A, const bf16* W, int M, int N, int K, const Epi& epi,
+                                 const SkinnyWs* sk, hipStream_t st) {
+  const int tiles = (N + 31) / 32, S = K / (64 * NSTG);
+  if (K % (64 * NSTG) != 0) return hipErrorInvalidValue;
+  if (S > 1 && (!sk || !sk->part || !sk->cnt || tiles > sk->cnt_len || tiles * S > sk->part_tiles))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_skinny_lds_kernel<Epi, NSTG>), dim3(tiles, S), dim3(SK_WAVES * 64), 0, st, A, W, M, N, K,
+                     epi, S > 1 ? sk->part : nullptr, S > 1 ? sk->cnt : nullptr);
+  return hipGetLastError();
+}
+
+// The LDS-staged kernel takes every product with contiguous rows and K a
+// multiple of 128: up to 768 columns of K in one block, longer K split over
+// blocks in ranges of 768 (or 512) when the caller gave split-K scratch.
 template <typename Epi>
 static hipError_t run_skinny(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
-                             hipStream_t st) {
-  if (K <= 1024)
-    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 8>), dim3((N + 31) / 32), dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw, M,
-                       N, K, epi);
+                             const SkinnyWs* sk, hipStream_t st) {
+  if (lda == K && ldw == K && K % 128 == 0) {
+    const int n = K / 64, tiles = (N + 31) / 32;
+    switch (n) {
+      case 2: return run_skinny_lds<2>(A, W, M, N, K, epi, sk, st);
+      case 4: return run_skinny_lds<4>(A, W, M, N, K, epi, sk, st);
+      case 6: return run_skinny_lds<6>(A, W, M, N, K, epi, sk, st);
+      case 8: return run_skinny_lds<8>(A, W, M, N, K, epi, sk, st);
+      case 10: return run_skinny_lds<10>(A, W, M, N, K, epi, sk, st);
+      case 12: return run_skinny_lds<12>(A, W, M, N, K, epi, sk, st);
+      default: break;
+    }
+    const bool room = sk && sk->part && sk->cnt && tiles <= sk->cnt_len;
+    if (room && n % 12 == 0 && tiles * (n / 12) <= sk->part_tiles) return run_skinny_lds<12>(A, W, M, N, K, epi, sk, st);
+    if (room && n % 8 == 0 && tiles * (n / 8) <= sk->part_tiles) return run_skinny_lds<8>(A, W, M, N, K, epi, sk, st);
+  }
+  const int steps = (K + 15) / 16, per_wave = (steps + SK_WAVES - 1) / SK_WAVES;
+  const dim3 grid((N + 31) / 32);
+  if (per_wave <= 4)
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 4>), grid, dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw, M, N, K, epi);
+  else if (per_wave <= 8)
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 8>), grid, dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw, M, N, K, epi);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 12>), dim3((N + 31) / 32), dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw,
-                       M, N, K, epi);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 12>), grid, dim3(SK_WAVES * 64), 0, st, A, lda, W, ldw, M, N, K, epi);
   return hipGetLastError();
 }
 
@@ -1134,8 +1283,8 @@ static hipError_t run_gemm_dma_k(const bf16* A, const bf16* W, int M, int N, con
 
 template <typename Epi>
 static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
-                                hipStream_t st) {
-  if (M <= 64 && lda % 8 == 0 && ldw % 8 == 0) return run_skinny(A, lda, W, ldw, M, N, K, epi, st);
+                                const SkinnyWs* sk, hipStream_t st) {
+  if (M <= 64 && lda % 8 == 0 && ldw % 8 == 0) return run_skinny(A, lda, W, ldw, M, N, K, epi, sk, st);
   const long long tiles256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= 64 && lda == K && ldw == K) {
     if (K == 768) return run_gemm_dma_k<768>(A, W, M, N, epi, st);
@@ -1149,51 +1298,52 @@ static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, 
 
 template <typename Epi>
 static hipError_t dispatch_gemm(const float* A, int lda, const float* W, int ldw, int M, int N, int K, const Epi& epi,
-                                hipStream_t st) {
+                                const SkinnyWs*, hipStream_t st) {
   return run_gemm<float, 64, 64, 32, 32, 32>(A, lda, W, ldw, M, N, K, epi, st);
 }
 
 template <typename T>
 static hipError_t linear_t(const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N, int K,
-                           void* out, int ldo, int act, int out_f32, hipStream_t st) {
+                           void* out, int ldo, int act, int out_f32, const SkinnyWs* sk, hipStream_t st) {
   if (act == 1 && !out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
-                                                 EpiAct<T, 1, false>{(const T*)bias, out, ldo}, st);
+                                                 EpiAct<T, 1, false>{(const T*)bias, out, ldo}, sk, st);
   if (act == 1) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
-                                     EpiAct<T, 1, true>{(const T*)bias, out, ldo}, st);
+                                     EpiAct<T, 1, true>{(const T*)bias, out, ldo}, sk, st);
   if (!out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
-                                     EpiAct<T, 0, false>{(const T*)bias, out, ldo}, st);
-  return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, EpiAct<T, 0, true>{(const T*)bias, out, ldo}, st);
+                                     EpiAct<T, 0, false>{(const T*)bias, out, ldo}, sk, st);
+  return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, EpiAct<T, 0, true>{(const T*)bias, out, ldo}, sk,
+                       st);
 }
 
 hipError_t launch_linear(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N,
-                         int K, void* out, int ldo, int act, int out_f32, hipStream_t st) {
-  if (dtype == 0) return linear_t<float>(A, lda, W, ldw, bias, M, N, K, out, ldo, act, out_f32, st);
-  return linear_t<bf16>(A, lda, W, ldw, bias, M, N, K, out, ldo, act, out_f32, st);
+                         int K, void* out, int ldo, int act, int out_f32, hipStream_t st, const SkinnyWs* sk) {
+  if (dtype == 0) return linear_t<float>(A, lda, W, ldw, bias, M, N, K, out, ldo, act, out_f32, sk, st);
+  return linear_t<bf16>(A, lda, W, ldw, bias, M, N, K, out, ldo, act, out_f32, sk, st);
 }
 
 template <typename T>
 static hipError_t resid_t(const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N, int K,
-                          float* x, int ldx, hipStream_t st) {
+                          float* x, int ldx, const SkinnyWs* sk, hipStream_t st) {
   EpiResid<T> e{(const T*)bias, x, ldx};
-  return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, e, st);
+  return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, e, sk, st);
 }
 
 hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M,
-                               int N, int K, float* x, int ldx, hipStream_t st) {
-  if (dtype == 0) return resid_t<float>(A, lda, W, ldw, bias, M, N, K, x, ldx, st);
-  return resid_t<bf16>(A, lda, W, ldw, bias, M, N, K, x, ldx, st);
+                               int N, int K, float* x, int ldx, hipStream_t st, const SkinnyWs* sk) {
+  if (dtype == 0) return resid_t<float>(A, lda, W, ldw, bias, M, N, K, x, ldx, sk, st);
+  return resid_t<bf16>(A, lda, W, ldw, bias, M, N, K, x, ldx, sk, st);
 }
 
 template <typename T>
-static hipError_t qkv_t(const QKVArgs& a, hipStream_t st) {
+static hipError_t qkv_t(const QKVArgs& a, const SkinnyWs* sk, hipStream_t st) {
   EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, 1.0f / (float)a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh,
               (T*)a.v, a.v_bh, a.pos, a.Tk};
-  return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, 3 * a.C, a.C, e, st);
+  return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, 3 * a.C, a.C, e, sk, st);
 }
 
-hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st) {
-  if (dtype == 0) return qkv_t<float>(a, st);
-  return qkv_t<bf16>(a, st);
+hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyWs* sk) {
+  if (dtype == 0) return qkv_t<float>(a, sk, st);
+  return qkv_t<bf16>(a, sk, st);
 }
 
 // bf16 head tile for C = 768 (vocab x tokens, per-wave vocab x tokens)

@@ -105,11 +105,15 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace of a [B, T] pass.  Decode calls keep K/U in the caller's caches
 // and run the head on B rows only; they add a_last [B, C] and the argmax
-// partial indices.
+// partial indices.  Passes of at most 64 bf16 rows (decode steps) add the
+// split-K scratch of the skinny products.
 struct Plan {
-  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, alast, pidx, total;
+  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, alast, pidx, skpart, skcnt, total;
   int ntiles, nblocks;
 };
+
+constexpr int SK_PART_TILES = 512;   // 64 x 32 fp32 partial tiles (4 MB)
+constexpr int SK_COUNTERS = 256;     // column tiles of 32 (N <= 8192)
 
 Plan plan(const gpt_config* c, int B, int T, bool decode) {
   Plan p{};
@@ -133,6 +137,9 @@ Plan plan(const gpt_config* c, int B, int T, bool decode) {
   p.bsum = decode ? 0 : take((size_t)p.nblocks * 2 * 8);
   p.alast = decode ? take((size_t)B * C * es) : 0;
   p.pidx = decode ? take((size_t)B * p.ntiles * 4) : 0;
+  const bool split = M <= 64 && c->dtype == GPT_BF16;
+  p.skpart = split ? take((size_t)SK_PART_TILES * 64 * 32 * 4) : 0;
+  p.skcnt = split ? take((size_t)SK_COUNTERS * 4) : 0;
   p.total = off;
   return p;
 }
@@ -180,6 +187,9 @@ int run_blocks(const Pass& s) {
   void* h = at<char>(s.ws, s.pl.h);
   const size_t es = esize(cfg);
   const long long cache_layer = (long long)B * H * s.Tmax * D;   // elements per layer of each cache
+  SkinnyWs skw{};
+  if (s.pl.skpart) skw = SkinnyWs{at<float>(s.ws, s.pl.skpart), SK_PART_TILES, at<int>(s.ws, s.pl.skcnt), SK_COUNTERS};
+  const SkinnyWs* sk = s.pl.skpart ? &skw : nullptr;
 
   LnArgs la{};
   la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps;
@@ -189,8 +199,9 @@ int run_blocks(const Pass& s) {
   la.g = P.at(L > 0 ? P.layer(0).ln1_g : P.lnf_g());
   la.b = P.at(L > 0 ? P.layer(0).ln1_b : P.lnf_b());
   la.out = a;
+  la.zero = sk ? skw.cnt : nullptr; la.zero_n = sk ? skw.cnt_len : 0;
   GPT_TRY(launch_embed_ln(dt, la, s.st));
-  la.idx = nullptr; la.pos = nullptr;
+  la.idx = nullptr; la.pos = nullptr; la.zero = nullptr; la.zero_n = 0;
 
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   for (int l = 0; l < L; ++l) {
@@ -208,7 +219,7 @@ int run_blocks(const Pass& s) {
     qa.pos = s.mode == STEP ? s.pos : nullptr;
     qa.Tk = s.mode == FORWARD ? T : s.Tmax;
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
-    GPT_TRY(launch_qkv(dt, qa, s.st));
+    GPT_TRY(launch_qkv(dt, qa, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, true));
     if (s.mode == STEP) {
@@ -228,17 +239,17 @@ int run_blocks(const Pass& s) {
     }
     GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, true));
-    GPT_TRY(launch_linear_resid(dt, o, C, P.at(w.proj_w), C, P.at(w.proj_b), M, C, C, x, C, s.st));
+    GPT_TRY(launch_linear_resid(dt, o, C, P.at(w.proj_w), C, P.at(w.proj_b), M, C, C, x, C, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, false));
     la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
     GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
     GPT_TRY(launch_layernorm(dt, la, s.st));
     GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
-    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, 1, 0, s.st));
+    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, 1, 0, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, true));
-    GPT_TRY(launch_linear_resid(dt, h, F, P.at(w.fcproj_w), F, P.at(w.fcproj_b), M, C, F, x, C, s.st));
+    GPT_TRY(launch_linear_resid(dt, h, F, P.at(w.fcproj_w), F, P.at(w.fcproj_b), M, C, F, x, C, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, false));
     if (l + 1 < L) {   // ln_1 of the next block (ln_f is applied by the caller)
       la.g = P.at(P.layer(l + 1).ln1_g); la.b = P.at(P.layer(l + 1).ln1_b);
@@ -301,7 +312,8 @@ int gpt_decode_workspace_bytes(const gpt_config* cfg, int B, int Tp, size_t* byt
   if (!bytes) return GPT_ERR_NULL;
   if (B <= 0 || Tp <= 0) return GPT_ERR_SHAPE;
   if (Tp > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
-  *bytes = plan(cfg, B, Tp, true).total;   // covers the step's [B, 1] plan as well
+  const size_t pre = plan(cfg, B, Tp, true).total, step = plan(cfg, B, 1, true).total;
+  *bytes = pre > step ? pre : step;   // one workspace serves the prefill and every step
   return GPT_OK;
 }
 

@@ -31,6 +31,7 @@ struct LnArgs {
   int in_mul, in_add;                  // LayerNorm input row = row * in_mul + in_add
   const void* g; const void* b;        // LayerNorm gain / bias
   void* out;                           // [M, C] normalised rows
+  int* zero; int zero_n;               // embedding: nullable ints set to zero (split-K counters)
 };
 
 // Attention of one new query per (b, h) over positions 0 .. *pos of the cache.
@@ -54,13 +55,23 @@ struct AttnArgs {
   float scale_log2;                    // log2(e) / sqrt(D)
 };
 
+// Split-K scratch of the skinny (M <= 64) bf16 products: per-column-tile
+// arrival counters, which must be zero when a product starts and are zero
+// again when it ends, and fp32 partial tiles of 64 x 32 (8 KB each).  With
+// a null pointer (or too little room) the products run without split-K.
+struct SkinnyWs {
+  float* part; int part_tiles;
+  int* cnt; int cnt_len;
+};
+
 hipError_t launch_embed_ln(int dtype, const LnArgs& a, hipStream_t st);
 hipError_t launch_layernorm(int dtype, const LnArgs& a, hipStream_t st);
 hipError_t launch_linear(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N,
-                         int K, void* out, int ldo, int act, int out_f32, hipStream_t st);
+                         int K, void* out, int ldo, int act, int out_f32, hipStream_t st,
+                         const SkinnyWs* sk = nullptr);
 hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M,
-                               int N, int K, float* x, int ldx, hipStream_t st);
-hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st);
+                               int N, int K, float* x, int ldx, hipStream_t st, const SkinnyWs* sk = nullptr);
+hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyWs* sk = nullptr);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 // Vocabulary tiles of the head's partials for M rows (CE or argmax mode).
 int head_ntiles(int dtype, int M, int V, int C, bool argmax);

@@ -36,6 +36,8 @@ template <typename T, int NCH, bool EMBED>
 __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (EMBED && a.zero)   // the pass's first kernel clears the split-K counters of the products after it
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < a.zero_n; i += gridDim.x * 256) a.zero[i] = 0;
   if (row >= a.M) return;
   const int C = a.C;
   const T* __restrict__ g = reinterpret_cast<const T*>(a.g);

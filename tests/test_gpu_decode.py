@@ -140,6 +140,18 @@ def test_small_bf16_decode(B):
     check_against_oracle(cfg, params, prompt, toks, z, [0, 1, B - 1], bf16_tol, bf16_band)
 
 
+@pytest.mark.parametrize("B", [5, 64])
+def test_bf16_decode_split_k(B):
+    # n_ff = 1536: the skinny fc-projection of a step (K = 1536) is split over
+    # two blocks per column tile, whose partial sums meet in the workspace
+    cfg = synth.GPTConfig(vocab=300, ctx=64, n_embd=128, n_head=2, n_layer=2, n_ff=1536, dtype=synth.BF16)
+    params = synth.make_params(cfg, seed=8, cfg_id=10, init="stress")
+    prompt = synth.make_ids(cfg, B, 9, seed=8, cfg_id=10)
+    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=10, Tmax=32, rows=[0, B - 1])
+    assert pos == 19
+    check_against_oracle(cfg, params, prompt, toks, z, [0, B - 1], bf16_tol, bf16_band)
+
+
 @pytest.fixture(scope="module")
 def gpt2_decode_run():
     cfg = synth.GPT2
@@ -180,12 +192,14 @@ def test_gpt2_bf16_decode_agrees_with_forward(gpt2_decode_run):
     assert err <= 1e-1
 
 
-def test_decode_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("n_ff", [256, 1536])
+def test_decode_step_graph_replay_matches_eager(n_ff):
     # one decode step captured in a HIP graph and replayed (the position is
     # read on the device), with eager work and synchronisations between
     # replays; every replay's tokens and logits equal the eager path's
+    # (n_ff = 1536: split-K products, whose counters the step clears itself)
     lib = _lib()
-    cfg = synth.GPTConfig(vocab=257, ctx=64, n_embd=64, n_head=2, n_layer=2, n_ff=256, dtype=synth.BF16)
+    cfg = synth.GPTConfig(vocab=257, ctx=64, n_embd=64, n_head=2, n_layer=2, n_ff=n_ff, dtype=synth.BF16)
     params = synth.make_params(cfg, seed=6, cfg_id=9, init="stress")
     prompt = torch.from_numpy(synth.make_ids(cfg, 4, 10, seed=6, cfg_id=9)).cuda()
     P = lib.params_to_device(cfg, synth.pack(cfg, params))

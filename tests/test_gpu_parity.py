@@ -83,7 +83,8 @@ def test_layernorm_kernel(dtype, C, M):
                                       (8191, 2304, 768, 0), (4097, 768, 3072, 1), (2049, 3072, 768, 1),
                                       # skinny path (at most 64 rows): K and N tails, one row
                                       (1, 2304, 768, 0), (64, 3072, 768, 1), (37, 768, 3072, 0),
-                                      (64, 50, 24, 1), (5, 96, 8, 0)])
+                                      (64, 50, 24, 1), (5, 96, 8, 0), (64, 96, 128, 0), (17, 200, 640, 1),
+                                      (33, 768, 768, 0), (3, 64, 1536, 1)])
 def test_linear_kernel(dtype, M, N, K, act):
     lib = _lib()
     cfg = synth.GPTConfig(vocab=17, ctx=16, n_embd=16, n_head=2, n_layer=1, n_ff=64, dtype=dtype)
@@ -262,6 +263,22 @@ def test_gpt2_bf16_odd_length_explicit_targets():
     _bf16_check(lg, tok, ref_l, ref_t, [0])
     assert abs(mean - ref_m) <= 1e-2
     np.testing.assert_array_equal(tok[0, ::7], 0.0)
+
+
+@pytest.mark.parametrize("B,T", [(2, 16), (4, 16), (1, 7)])
+def test_small_bf16_forward_skinny_products(B, T):
+    # at most 64 token rows: every block product takes the skinny path, the
+    # fc-projection (K = 1536) split over blocks through the workspace
+    cfg = synth.GPTConfig(vocab=300, ctx=64, n_embd=128, n_head=2, n_layer=2, n_ff=1536, dtype=synth.BF16)
+    params = synth.make_params(cfg, seed=12, cfg_id=10, init="stress")
+    ids = synth.make_ids(cfg, B, T, seed=12 + T, cfg_id=10)
+    lg, tok, mean = run_gpu(cfg, params, ids)
+    ref_l, ref_t, ref_m = O.forward(synth.unpack_f64(cfg, params), ids, cfg.n_head, cfg.ln_eps)
+    _bf16_check(lg, tok, ref_l, ref_t, list(range(B)))
+    assert abs(mean - ref_m) <= 1e-2
+    lg2, tok2, _ = run_gpu(cfg, params, ids)     # deterministic: split partials summed in a fixed order
+    np.testing.assert_array_equal(lg, lg2)
+    np.testing.assert_array_equal(tok, tok2)
 
 
 def test_gpt2_bf16_no_logits_b32_matches_logits_path(gpt2_inputs):
