@@ -943,37 +943,13 @@ __device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
 
 // bf16 tied head computed transposed, Z^T = E . A^T: the MFMA rows are vocab
 // entries and the columns are tokens, so every lane owns whole tokens.  The
-// softmax partials of a token over this block's 256 vocab entries are then a
+// softmax partials of a token over this block's vocab entries are then a
 // reduction over the lane's own registers, one exchange with the lane holding
-// the other half of the rows (l ^ 32), and a 4-way combine over the waves
-// along the vocab axis.  The target ids are read before the main loop.
-// Logits: the whole 256 x 256 bf16 tile is staged in the two (then free)
-// pipeline stages, four quarters of 64 token rows of 512 bytes each with 16-byte chunks
-// XOR-swizzled by row, behind a single barrier; each 16-byte window of a
-// global logits row (V is odd, so rows are only 2-byte aligned) is then
-// assembled from two LDS chunks and written with one aligned 16-byte store;
-// the partial windows at the two ends of a row are written per element.
-__device__ __forceinline__ uint4 lds_chunk(const char* row, int c, int sw) {
-  if (c < 0 || c >= 32) return make_uint4(0, 0, 0, 0);
-  return *reinterpret_cast<const uint4*>(row + ((c ^ sw) << 4));
-}
-
-// Elements o .. o+7 of the 16-element concatenation lo ++ hi (o in 0..7).
-__device__ __forceinline__ uint4 window8(uint4 lo, uint4 hi, int o) {
-  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  const int o2 = o >> 1;
-  uint32_t y[5];
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const uint32_t a0 = w[j], a1 = w[j + 1], a2 = w[j + 2], a3 = (j + 3 < 8) ? w[j + 3] : 0u;
-    y[j] = o2 == 0 ? a0 : (o2 == 1 ? a1 : (o2 == 2 ? a2 : a3));
-  }
-  uint32_t r[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = (o & 1) ? __builtin_amdgcn_alignbyte(y[j + 1], y[j], 2) : y[j];
-  return make_uint4(r[0], r[1], r[2], r[3]);
-}
-
+// the other half of the rows (l ^ 32), and a combine over the waves along the
+// vocab axis (through the first stage, free after the main loop).  The target
+// ids are read before the main loop.  Logits are stored straight from the
+// accumulators (staging the tile in LDS for row-contiguous stores measured
+// slower).
 template <int K, int BM, int BN, int WM, int WN>   // BM: vocab, BN: tokens
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN, 2, 64>())))
