@@ -294,16 +294,15 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
 // 0 .. *pos (its own K/U were appended at *pos by the QKV epilogue), the
 // KV-cache form of the same causal attention ("预训练一个 Mini GPT", KV
 // cache: only the new token's q, k, u are computed; earlier k, u are read
-// back).  One block of 256 threads per (b, h).  A key row of D values is cut
-// into 16-byte chunks held by LPK adjacent lanes (8 lanes for D = 64 in bf16),
-// so a group of lanes reads a whole row and a wave reads consecutive rows:
-//   1. scores: group g takes keys g, g + G, ... (G = 256 / LPK groups), dots
-//      its chunks with the matching slice of q, reduces over the group, and
-//      the group's first lane writes the score to LDS;
-//   2. block max and the sum of exp2(score - max) (q carries log2(e)/sqrt(D));
-//   3. weighted sum: the groups walk the keys again, each lane accumulating
-//      its chunk of U weighted by p; the G partial rows meet in LDS.
-// HBM-bound: every cached K and U row of positions 0 .. *pos is read once.
+// back).  One block of 256 threads per (b, h), a single pass over the cache:
+// a key row of D values is cut into 16-byte chunks held by LPK adjacent lanes
+// (8 lanes for D = 64 in bf16), and group g of LPK lanes takes keys g, g + G,
+// ... (G = 256 / LPK groups), loading the key's K and U chunks together, UNR
+// keys at a time.  Each group keeps an online softmax of its own keys (running
+// maximum, sum and U-weighted sum, rescaled once per batch of UNR keys); the
+// G partial states meet in LDS at the end.  HBM-bound: every cached K and U row
+// of positions 0 .. *pos is read once, with one round trip of latency per UNR
+// keys of a group (one in all for up to 256 positions).
 constexpr int DEC_MAXT = 4096;
 constexpr int DEC_THREADS = 256;
 
@@ -323,23 +322,19 @@ __device__ __forceinline__ void chunk_f32<float>(const uint4& v, float (&o)[4]) 
   o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
 }
 
-template <typename T>
+template <typename T, int LPK>
 __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a) {
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int UNR = 4;
-  __shared__ float p[DEC_MAXT];
+  constexpr int UNR = 8;
+  constexpr int G = DEC_THREADS / LPK;
   __shared__ float qs[128];
-  __shared__ float part[DEC_THREADS * VEC];
-  __shared__ float wred[DEC_THREADS / 64];
-  const int tid = threadIdx.x, wave = tid >> 6;
+  __shared__ float gacc[G * LPK * VEC];   // per group: U-weighted sums, columns [0, LPK VEC)
+  __shared__ float gm[G], gl[G];
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H, D = a.D;
-  const int nch = D / VEC;                  // 16-byte chunks per row (D % VEC == 0)
-  int lpk = 1;
-  while (lpk < nch) lpk <<= 1;              // lanes per key, a power of two dividing 64
-  const int G = DEC_THREADS / lpk;
-  const int g = tid / lpk, c = tid - g * lpk;
-  const bool act = c < nch;
+  const int g = tid / LPK, c = tid - g * LPK;
+  const bool act = c * VEC < D;             // lanes past the row's chunks hold zeros
   const T* q = reinterpret_cast<const T*>(a.q) + (long long)bh * D;
   for (int d = tid; d < D; d += DEC_THREADS) qs[d] = to_f32(q[d]) * a.scale_log2;
   __syncthreads();
@@ -352,90 +347,93 @@ __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a)
   const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.kv_bh + c * VEC;
   const uint4 z = make_uint4(0, 0, 0, 0);
 
-  float mx = -INFINITY;
+  float m = -INFINITY, l = 0.f, acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   for (int k0 = 0; k0 < n; k0 += UNR * G) {
-    uint4 kv[UNR];
+    uint4 kv[UNR], uv[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int k = k0 + u * G + g;
-      kv[u] = (act && k < n) ? *reinterpret_cast<const uint4*>(K + (long long)k * D) : z;
+      const bool in = act && k < n;
+      kv[u] = in ? *reinterpret_cast<const uint4*>(K + (long long)k * D) : z;
+      uv[u] = in ? *reinterpret_cast<const uint4*>(U + (long long)k * D) : z;
     }
+    float s[UNR];
+    float mb = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       float kf[VEC];
       chunk_f32<T>(kv[u], kf);
-      float sc = 0.f;
+      float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) sc = fmaf(qv[e], kf[e], sc);
-      for (int o = lpk >> 1; o > 0; o >>= 1) sc += __shfl_xor(sc, o, 64);
-      const int k = k0 + u * G + g;
-      if (k < n) {
-        if (c == 0) p[k] = sc;
-        mx = fmaxf(mx, sc);
-      }
+      for (int e = 0; e < VEC; ++e) t = fmaf(qv[e], kf[e], t);
+#pragma unroll
+      for (int o = LPK >> 1; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      s[u] = k0 + u * G + g < n ? t : -INFINITY;
+      mb = fmaxf(mb, s[u]);
     }
-  }
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) wred[wave] = mx;
-  __syncthreads();
-  mx = wred[0];
+    const float m_new = fmaxf(m, mb);
+    if (m_new == -INFINITY) continue;       // no key of this group in the batch
+    const float alpha = fast_exp2(m - m_new);
+    l *= alpha;
 #pragma unroll
-  for (int w = 1; w < DEC_THREADS / 64; ++w) mx = fmaxf(mx, wred[w]);
-  float sum = 0.f;
-  for (int k = tid; k < n; k += DEC_THREADS) {
-    const float e = fast_exp2(p[k] - mx);
-    p[k] = e;
-    sum += e;
-  }
-  sum = wave_sum(sum);
-  __syncthreads();                          // every read of wred and every p update done
-  if ((tid & 63) == 0) wred[wave] = sum;
-  __syncthreads();
-  sum = 0.f;
-#pragma unroll
-  for (int w = 0; w < DEC_THREADS / 64; ++w) sum += wred[w];
-  const float inv = 1.0f / sum;
-
-  float acc[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  for (int k0 = 0; k0 < n; k0 += UNR * G) {
-    uint4 uv[UNR];
+    for (int e = 0; e < VEC; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int k = k0 + u * G + g;
-      uv[u] = (act && k < n) ? *reinterpret_cast<const uint4*>(U + (long long)k * D) : z;
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int k = k0 + u * G + g;
-      const float w = k < n ? p[k] : 0.f;
+      const float pw = fast_exp2(s[u] - m_new);   // 0 for keys past n
+      l += pw;
       float uf[VEC];
       chunk_f32<T>(uv[u], uf);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, uf[e], acc[e]);
+      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(pw, uf[e], acc[e]);
     }
+    m = m_new;
   }
-  if (act) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) part[g * D + c * VEC + e] = acc[e];
-  }
+  for (int e = 0; e < VEC; ++e) gacc[g * LPK * VEC + c * VEC + e] = acc[e];
+  if (c == 0) { gm[g] = m; gl[g] = l; }
   __syncthreads();
+  // combine the groups: every group with keys has a finite maximum (group 0 holds key 0)
+  float M = gm[0];
+#pragma unroll
+  for (int gg = 1; gg < G; ++gg) M = fmaxf(M, gm[gg]);
   T* orow = reinterpret_cast<T*>(a.o) + (long long)b * a.o_ld + h * D;
   for (int d = tid; d < D; d += DEC_THREADS) {
-    float t = 0.f;
-    for (int gg = 0; gg < G; ++gg) t += part[gg * D + d];
-    orow[d] = from_f32<T>(t * inv);
+    float num = 0.f, den = 0.f;
+#pragma unroll 8
+    for (int gg = 0; gg < G; ++gg) {
+      const float w = fast_exp2(gm[gg] - M);   // 0 for a group without keys
+      num = fmaf(w, gacc[gg * LPK * VEC + d], num);
+      den = fmaf(w, gl[gg], den);
+    }
+    orow[d] = from_f32<T>(num / den);
   }
 }
 
 hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t st) {
   const int vec = dtype == 0 ? 4 : 8;
   if (a.Tmax > DEC_MAXT || a.D > 128 || a.D % vec) return hipErrorInvalidValue;
-  if (dtype == 0)
-    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(a.B * a.H), dim3(DEC_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(a.B * a.H), dim3(DEC_THREADS), 0, st, a);
+  // lanes per key: the row's 16-byte chunks rounded up to a power of two
+  const int nch = a.D / vec;
+  const int lpk = nch <= 2 ? 2 : (nch <= 4 ? 4 : (nch <= 8 ? 8 : (nch <= 16 ? 16 : 32)));
+  const dim3 grid(a.B * a.H), block(DEC_THREADS);
+  if (dtype == 0) {
+    switch (lpk) {
+      case 2: hipLaunchKernelGGL((attn_decode_kernel<float, 2>), grid, block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((attn_decode_kernel<float, 4>), grid, block, 0, st, a); break;
+      case 8: hipLaunchKernelGGL((attn_decode_kernel<float, 8>), grid, block, 0, st, a); break;
+      case 16: hipLaunchKernelGGL((attn_decode_kernel<float, 16>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((attn_decode_kernel<float, 32>), grid, block, 0, st, a); break;
+    }
+  } else {
+    switch (lpk) {
+      case 2: hipLaunchKernelGGL((attn_decode_kernel<bf16, 2>), grid, block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((attn_decode_kernel<bf16, 4>), grid, block, 0, st, a); break;
+      case 8: hipLaunchKernelGGL((attn_decode_kernel<bf16, 8>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((attn_decode_kernel<bf16, 16>), grid, block, 0, st, a); break;
+    }
+  }
   return hipGetLastError();
 }
 
