@@ -108,28 +108,33 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     else qf[i] = typename MF::frag{};
   }
 
-  // prefetch registers: K chunks and U key pairs; rows/cols outside the sequence are zero
+  // prefetch registers: K chunks and U key pairs.  Buffer loads: keys past the
+  // sequence lie outside the resources and chunks past D (or past the tile)
+  // take an offset outside them, so every such read is zero without a branch;
+  // the per-thread offsets are fixed and the tile start goes in the scalar
+  // offset.
   struct RegSet { uint4 kr[KCH], ur0[UCH], ur1[UCH]; };
-  auto gload = [&](RegSet& R, int kb) {
-    uint4 (&kr)[KCH] = R.kr;
-    uint4 (&ur0)[UCH] = R.ur0;
-    uint4 (&ur1)[UCH] = R.ur1;
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(K, (uint32_t)((size_t)T_seq * D * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rsu = make_rsrc(U, (uint32_t)((size_t)T_seq * D * sizeof(T)));
+  uint32_t koff[KCH], uoff[UCH];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
-      const int key = kb + row;
-      kr[c] = (ch < KTOT && key < T_seq && dc < D) ? *reinterpret_cast<const uint4*>(K + (long long)key * D + dc)
-                                                   : make_uint4(0, 0, 0, 0);
-    }
+  for (int c = 0; c < KCH; ++c) {
+    const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
+    koff[c] = (ch < KTOT && dc < D) ? (uint32_t)((row * D + dc) * sizeof(T)) : OOB_OFFSET;
+  }
+#pragma unroll
+  for (int c = 0; c < UCH; ++c) {
+    const int ch = tid + c * 256, kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
+    uoff[c] = (ch < UTOT && dc < D) ? (uint32_t)((kp * D + dc) * sizeof(T)) : OOB_OFFSET;
+  }
+  auto gload = [&](RegSet& R, int kb) {
+    const uint32_t so = (uint32_t)(kb * D * sizeof(T));
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) R.kr[c] = buf_load16(rsk, koff[c], so);
 #pragma unroll
     for (int c = 0; c < UCH; ++c) {
-      const int ch = tid + c * 256, kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
-      const int key = kb + kp;
-      const bool in = ch < UTOT && dc < D;
-      ur0[c] = (in && key < T_seq) ? *reinterpret_cast<const uint4*>(U + (long long)key * D + dc)
-                                   : make_uint4(0, 0, 0, 0);
-      ur1[c] = (in && key + 1 < T_seq) ? *reinterpret_cast<const uint4*>(U + (long long)(key + 1) * D + dc)
-                                       : make_uint4(0, 0, 0, 0);
+      R.ur0[c] = buf_load16(rsu, uoff[c], so);
+      R.ur1[c] = buf_load16(rsu, uoff[c] == OOB_OFFSET ? OOB_OFFSET : uoff[c] + (uint32_t)(D * sizeof(T)), so);
     }
   };
   // K as is; U transposed to U^T [d][key], written as (key, key+1) pairs

@@ -65,6 +65,19 @@ template <> struct Mfma<float> {
 };
 
 // Row index (within a 32x32 tile) of accumulator register r for lane l.
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return zero,
+// which handles the tails of a tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// An offset past every resource this code builds (at most 2^31 bytes): reads zero.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
 __device__ __forceinline__ float wave_sum(float v) {

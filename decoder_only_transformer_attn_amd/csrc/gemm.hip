@@ -36,16 +36,6 @@ struct GemmCfg {
   static_assert(BK % Mfma<T>::KPI == 0, "BK must hold whole MFMA k steps");
 };
 
-// Buffer resource over [base, base + bytes): loads beyond `bytes` return zero,
-// which handles the M and N tails of a tile without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
 // Main loop: acc[i][j] += A[m0 + wm*WM + 32i .., :] . W[n0 + wn*WN + 32j .., :]^T
 // Rows past M (N) read as zero; KTAIL zeroes the chunks past K when K % BK != 0.
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL>
