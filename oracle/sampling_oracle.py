@@ -1,0 +1,103 @@
+"""Next-token sampling from one row of logits: repetition penalty, temperature,
+top-k and top-p (nucleus), then one draw.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this module: only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
+leg may use it.  It shares no code with the HIP library.
+
+Sources (web pages, cited by title and section):
+  [P1] "预训练一个 Mini GPT（1.24 亿参数）", 构建它 第7步 (文本生成): logits of
+       the last position divided by the temperature, softmax with the maximum
+       subtracted, one draw with np.random.choice (inverse CDF in float64);
+       temperature 0 is the greedy choice.
+  [P2] "第 25 章 从小 GPT 到 GPT-2", §25.7: top-k = 50 as the course setting,
+       draws from the relative probabilities of the kept candidates.
+  [P4] "02 GPT 架构——Decoder-Only 的自回归语言模型", 第 8 章 §8.1 temperature,
+       §8.2 top-k, §8.3 top-p (sort by probability, accumulate until the sum
+       reaches p), §8.4 repetition penalty (a logit of a token that already
+       appeared is divided by alpha when positive, multiplied when negative),
+       and the remark that the strategies are used together.
+  [P5] "GPT-1学习笔记", §6.2: temperature, top-k (renormalise the k largest),
+       top-p (the smallest set whose cumulative probability reaches p).
+
+Readings (the pages leave these open):
+  * order of the steps: penalty, temperature, top-k, top-p, draw;
+  * the key z'/T and the penalty are formed in float32 (the precision the GPU
+    holds the logits in), so both sides rank identical keys; probabilities,
+    masses and the draw are float64 (the precision of [P1]'s sampler);
+  * the nucleus is taken of the distribution left by top-k (renormalised),
+    as the smallest prefix in descending probability whose mass is >= p * Z;
+  * candidates are ordered by descending key, equal keys by ascending index;
+    this order decides which of several equal logits top-k / top-p keep, and
+    it is the order the inverse CDF walks: the draw u in [0, 1) returns the
+    first candidate whose cumulative mass exceeds u * (mass of the nucleus);
+  * temperature <= 0 is the greedy choice (lowest index among equal maxima);
+  * the uniform u is an input (the caller's random stream), one per row.
+
+Every function is pinned by CPU tests (tests/test_oracle_sampling.py) against
+closed forms (softmax frequencies of a stratified set of draws), brute force
+over small vocabularies and the worked penalty rule of [P4] §8.4.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+
+def penalize(z: np.ndarray, seen: Optional[np.ndarray], alpha: float) -> np.ndarray:
+    """[P4] §8.4: z/alpha where the token appeared and z > 0, z*alpha where it
+    appeared and z < 0, unchanged otherwise (float32)."""
+    z = np.asarray(z, dtype=np.float32)
+    if seen is None or alpha == 1.0:
+        return z.copy()
+    a = np.float32(alpha)
+    seen = np.asarray(seen, dtype=bool)
+    out = z.copy()
+    pos = seen & (z > 0)
+    neg = seen & (z < 0)
+    out[pos] = z[pos] / a
+    out[neg] = z[neg] * a
+    return out
+
+
+def candidate_order(key: np.ndarray) -> np.ndarray:
+    """Indices by descending key, ascending index among equal keys."""
+    V = key.size
+    return np.lexsort((np.arange(V), -key.astype(np.float64)))
+
+
+def filtered(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, top_k: int, top_p: float,
+             alpha: float = 1.0):
+    """The candidates left after penalty, temperature, top-k and top-p, in
+    candidate order, with their unnormalised float64 weights exp(key - max)."""
+    zp = penalize(z, seen, alpha)
+    key = (zp / np.float32(temperature)).astype(np.float32)          # [P1] 第7步, [P4] §8.1
+    order = candidate_order(key)
+    V = key.size
+    cand = order[:top_k] if 0 < top_k < V else order                # [P4] §8.2, [P5] §6.2
+    m = float(key[order[0]])
+    w = np.exp(key[cand].astype(np.float64) - m)
+    if top_p < 1.0:                                                 # [P4] §8.3, [P5] §6.2
+        cum = np.cumsum(w)
+        n = int(np.searchsorted(cum, top_p * cum[-1], side="left")) + 1   # first prefix with mass >= p Z
+        cand, w = cand[:n], w[:n]
+    return cand, w
+
+
+def sample_row(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, top_k: int, top_p: float,
+               alpha: float, u: float) -> int:
+    """One next token for one row of logits, from the uniform draw u in [0, 1)."""
+    if temperature <= 0:
+        return int(np.argmax(penalize(z, seen, alpha)))             # first maximum: lowest index
+    cand, w = filtered(z, seen, temperature, top_k, top_p, alpha)
+    r = float(np.float32(u)) * float(w.sum())
+    pos = int(np.searchsorted(np.cumsum(w), r, side="right"))       # first cumulative mass > r
+    return int(cand[min(pos, len(cand) - 1)])
+
+
+def sample_rows(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, top_k: int, top_p: float,
+                alpha: float, u: np.ndarray) -> np.ndarray:
+    """sample_row over the rows of z [B, V] (seen [B, V] bool or None, u [B])."""
+    return np.array([sample_row(z[b], None if seen is None else seen[b], temperature, top_k, top_p, alpha,
+                                float(u[b])) for b in range(z.shape[0])], dtype=np.int64)
