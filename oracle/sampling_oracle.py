@@ -23,14 +23,17 @@ Sources (web pages, cited by title and section):
 Readings (the pages leave these open):
   * order of the steps: penalty, temperature, top-k, top-p, draw;
   * the key z'/T and the penalty are formed in float32 (the precision the GPU
-    holds the logits in), so both sides rank identical keys; probabilities,
-    masses and the draw are float64 (the precision of [P1]'s sampler);
+    holds the logits in); each candidate's unnormalised probability weight is
+    exp(key - max key) evaluated in float64 and rounded once to float32, so
+    both sides rank and weigh identical values; masses, thresholds and the
+    draw are float64 sums of those weights (the precision of [P1]'s sampler);
   * the nucleus is taken of the distribution left by top-k (renormalised),
     as the smallest prefix in descending probability whose mass is >= p * Z;
-  * candidates are ordered by descending key, equal keys by ascending index;
-    this order decides which of several equal logits top-k / top-p keep, and
-    it is the order the inverse CDF walks: the draw u in [0, 1) returns the
-    first candidate whose cumulative mass exceeds u * (mass of the nucleus);
+  * candidates are ordered by descending weight, equal weights by ascending
+    index; this order decides which of several equally probable tokens top-k
+    and top-p keep, and it is the order the inverse CDF walks: the draw u in
+    [0, 1) returns the first candidate whose cumulative mass exceeds
+    u * (mass of the nucleus);
   * temperature <= 0 is the greedy choice (lowest index among equal maxima);
   * the uniform u is an input (the caller's random stream), one per row.
 
@@ -61,23 +64,28 @@ def penalize(z: np.ndarray, seen: Optional[np.ndarray], alpha: float) -> np.ndar
     return out
 
 
-def candidate_order(key: np.ndarray) -> np.ndarray:
-    """Indices by descending key, ascending index among equal keys."""
-    V = key.size
-    return np.lexsort((np.arange(V), -key.astype(np.float64)))
+def candidate_order(w: np.ndarray) -> np.ndarray:
+    """Indices by descending weight, ascending index among equal weights."""
+    V = w.size
+    return np.lexsort((np.arange(V), -w.astype(np.float64)))
+
+
+def weights(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, alpha: float = 1.0) -> np.ndarray:
+    """Unnormalised probability weights exp(key - max key), key = z'/T in
+    float32 ([P1] 第7步, [P4] §8.1), the exponential in float64 rounded to float32."""
+    key = (penalize(z, seen, alpha) / np.float32(temperature)).astype(np.float32)
+    return np.exp(key.astype(np.float64) - np.float64(key.max())).astype(np.float32)
 
 
 def filtered(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, top_k: int, top_p: float,
              alpha: float = 1.0):
     """The candidates left after penalty, temperature, top-k and top-p, in
-    candidate order, with their unnormalised float64 weights exp(key - max)."""
-    zp = penalize(z, seen, alpha)
-    key = (zp / np.float32(temperature)).astype(np.float32)          # [P1] 第7步, [P4] §8.1
-    order = candidate_order(key)
-    V = key.size
+    candidate order, with their float64 weights."""
+    w32 = weights(z, seen, temperature, alpha)
+    order = candidate_order(w32)
+    V = w32.size
     cand = order[:top_k] if 0 < top_k < V else order                # [P4] §8.2, [P5] §6.2
-    m = float(key[order[0]])
-    w = np.exp(key[cand].astype(np.float64) - m)
+    w = w32[cand].astype(np.float64)
     if top_p < 1.0:                                                 # [P4] §8.3, [P5] §6.2
         cum = np.cumsum(w)
         n = int(np.searchsorted(cum, top_p * cum[-1], side="left")) + 1   # first prefix with mass >= p Z
