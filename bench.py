@@ -309,9 +309,39 @@ def bench_decode(args, w):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "bytes_per_step_avg": round(bytes_total / n_steps)},
     }
+    out["sampler"] = bench_sampler(cfg, dec, dev_params, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(cfg, params, prompt, 32, 8)
     return out
+
+
+def bench_sampler(cfg, dec, dev_params, stream, reps=20):
+    """gpt_sample on one decode step's logits [B, V]: microseconds per call
+    for three settings (penalty + temperature + top-k + top-p; top-p over the
+    whole vocabulary; temperature alone)."""
+    import torch
+    from decoder_only_transformer_attn_amd import lib
+    z = torch.empty((dec.B, cfg.vocab), dtype=lib.torch_dtype(cfg), device="cuda")
+    dec.step(dev_params, logits=z)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    u = torch.rand(dec.B, generator=g, device="cuda")
+    seen = torch.zeros_like(dec.seen)
+    tok = torch.empty((dec.B,), dtype=torch.int32, device="cuda")
+    res = {}
+    for name, s in (("T0.8_k50_p0.95_rp1.1", lib.sampling(0.8, 50, 0.95, 1.1)),
+                    ("T1.0_p0.9", lib.sampling(1.0, 0, 0.9, 1.0)),
+                    ("T0.8", lib.sampling(0.8, 0, 1.0, 1.0))):
+        for _ in range(3):
+            lib.sample(cfg, z, s, u, seen, tok, stream)
+        ev = Events(2)
+        ev.record(0, stream.cuda_stream)
+        for _ in range(reps):
+            lib.sample(cfg, z, s, u, seen, tok, stream)
+        ev.record(1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        res[name] = round(ev.ms(0, 1) / reps * 1e3, 1)
+        ev.close()
+    return {"rows": dec.B, "vocab": cfg.vocab, "us_per_call": res}
 
 
 def copy_calibration():

@@ -432,6 +432,32 @@ int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* to
   return GPT_OK;
 }
 
+int gpt_sample(const gpt_config* cfg, const void* logits, int B, const gpt_sampling* sp, const float* u,
+               uint32_t* seen, int32_t* next_tok, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!logits || !sp || !next_tok) return GPT_ERR_NULL;
+  if (B <= 0) return GPT_ERR_SHAPE;
+  if (cfg->vocab > 53248) return GPT_ERR_CONFIG;
+  if (!std::isfinite(sp->temperature) || !(sp->top_p > 0.f) || !std::isfinite(sp->top_p) ||
+      !(sp->repetition_penalty > 0.f) || !std::isfinite(sp->repetition_penalty))
+    return GPT_ERR_SHAPE;
+  if (sp->temperature > 0.f && !u) return GPT_ERR_NULL;
+  SampleArgs a{};
+  a.logits = logits; a.ld = cfg->vocab; a.V = cfg->vocab; a.B = B;
+  a.temperature = sp->temperature; a.top_k = sp->top_k; a.top_p = sp->top_p; a.penalty = sp->repetition_penalty;
+  a.u = u; a.seen = seen; a.seen_words = (cfg->vocab + 31) / 32; a.out = next_tok;
+  return hip_status(launch_sample(cfg->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int gpt_mark_seen(const gpt_config* cfg, const int32_t* tokens, int B, int T, uint32_t* seen, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!tokens || !seen) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
+  return hip_status(launch_mark_seen(tokens, B, T, cfg->vocab, seen, static_cast<hipStream_t>(stream)));
+}
+
 int gpt_debug_layernorm(const gpt_config* cfg, const float* x, const void* g, const void* b, int M, void* out,
                         void* stream) {
   int s = check_config(cfg);

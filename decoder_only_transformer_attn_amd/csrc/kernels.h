@@ -86,6 +86,21 @@ hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int 
 hipError_t launch_argmax_reduce(int M, int ntiles, const float* part_max, const int32_t* part_idx, int32_t* next_tok,
                                 int32_t* pos, int set_pos, hipStream_t st);
 hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t st);
+// Next-token sampling of B rows of logits (one block per row).
+struct SampleArgs {
+  const void* logits; long long ld;    // [B, ld] in the compute dtype, V valid columns
+  int V, B;
+  float temperature;                   // <= 0: greedy
+  int top_k;                           // <= 0 or >= V: off
+  float top_p;                         // >= 1: off (> 0)
+  float penalty;                       // repetition penalty (1: off)
+  const float* u;                      // [B] uniforms in [0, 1)
+  uint32_t* seen;                      // nullable [B, seen_words] bit sets; the chosen token's bit is set
+  int seen_words;
+  int32_t* out;                        // [B]
+};
+hipError_t launch_sample(int dtype, const SampleArgs& a, hipStream_t st);
+hipError_t launch_mark_seen(const int32_t* tokens, int B, int T, int V, uint32_t* seen, hipStream_t st);
 // Per-token loss from the head partials, then a deterministic mean.
 int ce_reduce_blocks(int M);
 hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,

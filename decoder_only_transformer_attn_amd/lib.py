@@ -29,6 +29,11 @@ class gpt_config(ctypes.Structure):
                 ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
 
 
+class gpt_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float),
+                ("repetition_penalty", ctypes.c_float)]
+
+
 _CFG = ctypes.POINTER(gpt_config)
 SIGNATURES = {
     "gpt_param_count": (_c_i64, [_CFG]),
@@ -44,6 +49,8 @@ SIGNATURES = {
     "gpt_decode_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "gpt_prefill": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gpt_decode_step": (_c_int, [_CFG, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_sample": (_c_int, [_CFG, _vp, _c_int, ctypes.POINTER(gpt_sampling), _vp, _vp, _vp, _vp]),
+    "gpt_mark_seen": (_c_int, [_CFG, _vp, _c_int, _c_int, _vp, _vp]),
 }
 
 _lib = None
@@ -217,9 +224,38 @@ def decode_step(cfg, params, tok, k_cache, v_cache, pos, next_tok, logits=None, 
                                  0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def sampling(temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, repetition_penalty: float = 1.0):
+    return gpt_sampling(float(temperature), int(top_k), float(top_p), float(repetition_penalty))
+
+
+def seen_words(cfg) -> int:
+    return (cfg.vocab + 31) // 32
+
+
+def sample(cfg, logits, s, u=None, seen=None, next_tok=None, stream=None):
+    """Enqueue gpt_sample.  logits [B, V] (compute dtype); s = sampling(...);
+    u float32 [B] uniforms in [0, 1); seen int32 [B, seen_words(cfg)] bit sets
+    (or None); next_tok int32 [B] (allocated if None).  Returns next_tok."""
+    import torch
+    B = logits.shape[0]
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    check(load().gpt_sample(ctypes.byref(cfg_c(cfg)), _ptr(logits), B, ctypes.byref(s), _ptr(u), _ptr(seen),
+                            _ptr(next_tok), _stream(stream)))
+    return next_tok
+
+
+def mark_seen(cfg, tokens, seen, stream=None) -> None:
+    """Enqueue gpt_mark_seen: the bits of tokens int32 [B, T] set in seen."""
+    B, T = tokens.shape
+    check(load().gpt_mark_seen(ctypes.byref(cfg_c(cfg)), _ptr(tokens), B, T, _ptr(seen), _stream(stream)))
+
+
 class Decoder:
-    """Caches, position counter and workspace for greedy decoding of B
-    sequences with prompts of Tp tokens and at most Tmax cached positions."""
+    """Caches, position counter and workspace for decoding B sequences with
+    prompts of Tp tokens and at most Tmax cached positions: greedy by
+    default, or sampled (prefill / step with `sampling=` and one uniform per
+    sequence in `u`; a repetition penalty reads and updates self.seen)."""
 
     def __init__(self, cfg, B: int, Tp: int, Tmax: int, device="cuda"):
         import torch
@@ -232,15 +268,36 @@ class Decoder:
         self.pos = torch.zeros((1,), dtype=torch.int32, device=device)
         self.tok = torch.zeros((B,), dtype=torch.int32, device=device)
         self.ws = torch.empty(decode_workspace_bytes(cfg, B, Tp), dtype=torch.uint8, device=device)
+        self.seen = torch.zeros((B, seen_words(cfg)), dtype=torch.int32, device=device)
+        self._logits = None
 
-    def prefill(self, params, idx, last_logits=None, stream=None):
-        prefill(self.cfg, params, idx, self.k_cache, self.v_cache, self.pos, self.tok, last_logits, self.ws, stream)
-        return self.tok
+    def _row_logits(self, logits):
+        import torch
+        if logits is not None:
+            return logits
+        if self._logits is None:
+            self._logits = torch.empty((self.B, self.cfg.vocab), dtype=torch_dtype(self.cfg), device=self.tok.device)
+        return self._logits
 
-    def step(self, params, logits=None, stream=None):
+    def prefill(self, params, idx, last_logits=None, stream=None, sampling=None, u=None):
+        if sampling is None:
+            prefill(self.cfg, params, idx, self.k_cache, self.v_cache, self.pos, self.tok, last_logits, self.ws,
+                    stream)
+            return self.tok
+        z = self._row_logits(last_logits)
+        prefill(self.cfg, params, idx, self.k_cache, self.v_cache, self.pos, self.tok, z, self.ws, stream)
+        mark_seen(self.cfg, idx, self.seen, stream)
+        return sample(self.cfg, z, sampling, u, self.seen, self.tok, stream)
+
+    def step(self, params, logits=None, stream=None, sampling=None, u=None):
         """Feed the last chosen tokens; self.tok is overwritten with the next ones."""
-        decode_step(self.cfg, params, self.tok, self.k_cache, self.v_cache, self.pos, self.tok, logits, self.ws, stream)
-        return self.tok
+        if sampling is None:
+            decode_step(self.cfg, params, self.tok, self.k_cache, self.v_cache, self.pos, self.tok, logits, self.ws,
+                        stream)
+            return self.tok
+        z = self._row_logits(logits)
+        decode_step(self.cfg, params, self.tok, self.k_cache, self.v_cache, self.pos, self.tok, z, self.ws, stream)
+        return sample(self.cfg, z, sampling, u, self.seen, self.tok, stream)
 
 
 def debug_layernorm(cfg, x, g, b, out, stream=None) -> None:

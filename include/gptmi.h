@@ -158,6 +158,46 @@ int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* to
                     void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---- sampling the next token from rows of logits ----
+ * Steps, in this order (the pages name them; the order is a reading):
+ *   repetition penalty ("02 GPT 架构" §8.4): the logit of a token whose bit is
+ *     set in `seen` is divided by the penalty when positive, multiplied by it
+ *     when negative;
+ *   temperature ("预训练一个 Mini GPT" 第7步; "02 GPT 架构" §8.1): key = z'/T;
+ *     T <= 0 selects the greedy choice (largest penalised logit, lowest index);
+ *   top-k ("02 GPT 架构" §8.2; "GPT-1学习笔记" §6.2): the k most probable;
+ *   top-p ("02 GPT 架构" §8.3; "GPT-1学习笔记" §6.2): of those, the smallest
+ *     most-probable prefix whose renormalised mass reaches p;
+ *   draw ("预训练一个 Mini GPT" 第7步): the first candidate, in the order of
+ *     descending weight (equal weights: ascending index), whose cumulative
+ *     mass exceeds u times the mass of the candidates.
+ * Weights are exp(key - max key) evaluated in double and rounded once to
+ * float; masses are double sums of them.  Deterministic: the same inputs give
+ * the same tokens (no atomics decide a value). */
+typedef struct gpt_sampling {
+  float temperature;          /* <= 0: greedy */
+  int32_t top_k;              /* <= 0 or >= V: no top-k */
+  float top_p;                /* in (0, 1]; 1: no top-p */
+  float repetition_penalty;   /* > 0; 1: no penalty */
+} gpt_sampling;
+
+/* Samples one token per row.
+ *   logits   (device) [B, V] in cfg->dtype, row stride V.
+ *   s        (host) sampling settings, checked before any launch.
+ *   u        (device) float [B], uniforms in [0, 1), one per row (the caller's
+ *            random stream); may be NULL when s->temperature <= 0.
+ *   seen     (device, nullable) uint32 [B][(V + 31) / 32] bit sets: bit i of
+ *            row b marks token i as already present in sequence b.  Read for
+ *            the penalty; the chosen token's bit is set.
+ *   next_tok (device) int32 [B].
+ * Requires V <= 53248 (GPT_ERR_CONFIG otherwise) and B >= 1.  No workspace. */
+int gpt_sample(const gpt_config* cfg, const void* logits, int B, const gpt_sampling* s, const float* u,
+               uint32_t* seen, int32_t* next_tok, void* stream);
+
+/* Sets the bits of tokens (device, int32 [B, T]; ids outside [0, V) are
+ * ignored) in seen (device, uint32 [B][(V + 31) / 32]); bits already set stay. */
+int gpt_mark_seen(const gpt_config* cfg, const int32_t* tokens, int B, int T, uint32_t* seen, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* gpt_status_string(int status);
 

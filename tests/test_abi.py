@@ -131,3 +131,23 @@ def test_decode_workspace_covers_step_and_is_smaller_than_forward():
     assert lib.decode_workspace_bytes(synth.GPT2, 64, 1) <= pre
     with pytest.raises(lib.GPTError):
         lib.decode_workspace_bytes(synth.GPT2, 1, 1025)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="dummy-pointer validation tests run only without a GPU")
+def test_sample_validation_before_any_hip_call():
+    L = lib.load()
+    c = ctypes.byref(lib.cfg_c(synth.GPT2))
+
+    def smp(logits=1, B=4, s=None, u=1, seen=None, nt=1, cfg=c):
+        s = s if s is not None else lib.sampling(0.8, 50, 0.9, 1.1)
+        return L.gpt_sample(cfg, logits, B, ctypes.byref(s), u, seen, nt, None)
+
+    assert smp(logits=None) == -1 and smp(nt=None) == -1
+    assert smp(u=None) == -1                                   # a draw needs its uniform
+    assert smp(B=0) == -4
+    assert smp(s=lib.sampling(float("nan"))) == -4
+    assert smp(s=lib.sampling(1.0, 0, 0.0)) == -4              # top-p must be positive
+    assert smp(s=lib.sampling(1.0, 0, 1.0, 0.0)) == -4         # penalty must be positive
+    big = ctypes.byref(lib.cfg_c(synth.GPTConfig(vocab=60000, ctx=8, n_embd=16, n_head=2, n_layer=1, n_ff=64)))
+    assert smp(cfg=big) == -2                                  # vocabulary beyond one block's slices
+    assert L.gpt_mark_seen(c, None, 2, 3, 1, None) == -1 and L.gpt_mark_seen(c, 1, 0, 3, 1, None) == -4
