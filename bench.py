@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "19026da8f79a829a05619eaf1b2897d1616b3129f372e9f576229284800aa211",
-                "bytes": 2004122079}
+HEAD_TRAFFIC = {"gemm_src_sha256": "49d702f434eddca34e9e91697ad2ba3126cdaac93698ab30096ae7702552470b",
+                "bytes": 2000845672}
 
 
 def src_sha(rel):
