@@ -44,6 +44,9 @@ class GPTConfig:
     n_ff: int
     ln_eps: float = 1e-5
     dtype: int = F32  # 0 = fp32, 1 = bf16 (storage and MFMA operand type)
+    act: int = 0      # 0 = tanh GELU (GPT-2), 1 = exact erf GELU
+    post_ln: int = 0  # 0 = pre-LN blocks + ln_f (GPT-2), 1 = post-LN blocks, no ln_f (GPT-1)
+    untied: int = 0   # 0 = head tied to the token table, 1 = separate head matrix [V, C]
 
     @property
     def head_dim(self) -> int:
@@ -91,8 +94,11 @@ def blob_layout(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...], int]]:
     for l in range(cfg.n_layer):
         for name, shape in layer_shapes(cfg):
             add(f"h{l}.{name}", shape)
-    add("lnf_g", (cfg.n_embd,))
-    add("lnf_b", (cfg.n_embd,))
+    if not cfg.post_ln:
+        add("lnf_g", (cfg.n_embd,))
+        add("lnf_b", (cfg.n_embd,))
+    if cfg.untied:
+        add("head_w", (cfg.vocab, cfg.n_embd))
     out.append(("__end__", (), off))
     return out
 
@@ -163,10 +169,16 @@ def pack(cfg: GPTConfig, params: Dict[str, np.ndarray]) -> np.ndarray:
 
 
 def unpack_f64(cfg: GPTConfig, params: Dict[str, np.ndarray]) -> dict:
-    """Nested float64 view for the oracle: {'wte','wpe','layers':[{...}], 'lnf_g','lnf_b'}."""
+    """Nested float64 view for the oracle: {'wte','wpe','layers':[{...}], 'lnf_g','lnf_b'}
+    (no ln_f for post-LN configurations, 'head_w' for an untied head), plus the
+    variant names 'act' ('tanh' or 'erf') and 'norm' ('pre' or 'post')."""
     out = {"wte": params["wte"].astype(np.float64), "wpe": params["wpe"].astype(np.float64),
-           "lnf_g": params["lnf_g"].astype(np.float64), "lnf_b": params["lnf_b"].astype(np.float64),
-           "layers": []}
+           "layers": [], "act": "erf" if cfg.act else "tanh", "norm": "post" if cfg.post_ln else "pre"}
+    if not cfg.post_ln:
+        out["lnf_g"] = params["lnf_g"].astype(np.float64)
+        out["lnf_b"] = params["lnf_b"].astype(np.float64)
+    if cfg.untied:
+        out["head_w"] = params["head_w"].astype(np.float64)
     for l in range(cfg.n_layer):
         out["layers"].append({f: params[f"h{l}.{f}"].astype(np.float64) for f in LAYER_FIELDS})
     return out

@@ -41,11 +41,15 @@ import numpy as np
 # the final LayerNorm's 2C.  The tied head adds nothing.  With an explicit
 # MLP width F the per-block term is 4C^2+4C + 2CF+F+C + 4C.
 # ----------------------------------------------------------------------------
-def param_count(vocab: int, n_embd: int, n_layer: int, ctx: int, n_ff: Optional[int] = None) -> int:
+def param_count(vocab: int, n_embd: int, n_layer: int, ctx: int, n_ff: Optional[int] = None,
+                post_ln: bool = False, untied: bool = False) -> int:
+    """post_ln: GPT-1 blocks with no final LayerNorm ([P5] §4.1 feeds the last
+    block's output to the head); untied: a separate V x C head matrix without
+    bias ([P3] 二十三 LM Head)."""
     C = n_embd
     F = 4 * C if n_ff is None else n_ff
     per_block = (4 * C * C + 4 * C) + (2 * C * F + F + C) + 4 * C
-    return n_layer * per_block + vocab * C + ctx * C + 2 * C
+    return n_layer * per_block + vocab * C + ctx * C + (0 if post_ln else 2 * C) + (vocab * C if untied else 0)
 
 
 # ----------------------------------------------------------------------------
@@ -64,6 +68,17 @@ def gelu_tanh(z: np.ndarray) -> np.ndarray:
     """GELU, tanh approximation: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
     ([P5] §3.6 激活函数; [P2] §25.3 keeps the approximation)."""
     return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def gelu_erf(z: np.ndarray) -> np.ndarray:
+    """GELU, exact form: z Phi(z) = 0.5 z (1 + erf(z / sqrt(2))) ([P5] §3.6 标准公式;
+    [P3] builds the MLP with nn.GELU(), whose default is this form)."""
+    from scipy.special import erf
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def activation(z: np.ndarray, act: str = "tanh") -> np.ndarray:
+    return gelu_erf(z) if act == "erf" else gelu_tanh(z)
 
 
 def linear(x: np.ndarray, W: np.ndarray, b: Optional[np.ndarray] = None) -> np.ndarray:
@@ -154,32 +169,47 @@ def attention_sublayer(a: np.ndarray, lp: dict, n_head: int, trace: Optional[dic
     return linear(o, lp["proj_w"], lp["proj_b"])
 
 
-def mlp_sublayer(a: np.ndarray, lp: dict) -> np.ndarray:
-    """C -> F -> C with tanh GELU in between ([P2] §25.3)."""
-    return linear(gelu_tanh(linear(a, lp["fc_w"], lp["fc_b"])), lp["fcproj_w"], lp["fcproj_b"])
+def mlp_sublayer(a: np.ndarray, lp: dict, act: str = "tanh") -> np.ndarray:
+    """C -> F -> C with GELU in between ([P2] §25.3; tanh form unless act="erf")."""
+    return linear(activation(linear(a, lp["fc_w"], lp["fc_b"]), act), lp["fcproj_w"], lp["fcproj_b"])
 
 
-def block(x: np.ndarray, lp: dict, n_head: int, eps: float, trace: Optional[dict] = None) -> np.ndarray:
+def block(x: np.ndarray, lp: dict, n_head: int, eps: float, trace: Optional[dict] = None,
+          act: str = "tanh") -> np.ndarray:
     """Pre-norm block: x += attn(LN1(x)); x += mlp(LN2(x)) ([P1] Transformer 块 and
     第4步; [P2] §25.1; [P5] §3.2 notes GPT-2's move to pre-LN)."""
     x = x + attention_sublayer(layer_norm(x, lp["ln1_g"], lp["ln1_b"], eps), lp, n_head, trace)
-    x = x + mlp_sublayer(layer_norm(x, lp["ln2_g"], lp["ln2_b"], eps), lp)
+    x = x + mlp_sublayer(layer_norm(x, lp["ln2_g"], lp["ln2_b"], eps), lp, act)
     return x
+
+
+def block_post(x: np.ndarray, lp: dict, n_head: int, eps: float, act: str = "tanh") -> np.ndarray:
+    """Post-norm (GPT-1) block: n = LN1(x + attn(x)); h = LN2(n + mlp(n))
+    ([P5] §3.1 Block.forward, §3.2 Post-LN)."""
+    n = layer_norm(x + attention_sublayer(x, lp, n_head), lp["ln1_g"], lp["ln1_b"], eps)
+    return layer_norm(n + mlp_sublayer(n, lp, act), lp["ln2_g"], lp["ln2_b"], eps)
 
 
 def final_hidden(params: dict, idx: np.ndarray, n_head: int, eps: float = 1e-5,
                  trace: Optional[dict] = None) -> np.ndarray:
-    """ln_f(blocks(embed(idx))) -> [B,T,C]."""
+    """ln_f(blocks(embed(idx))) -> [B,T,C]; for post-LN models the last block's
+    output itself ([P5] §4.1: the head reads h_n)."""
+    act = params.get("act", "tanh")
     x = embed(params, idx)
+    if params.get("norm", "pre") == "post":
+        for lp in params["layers"]:
+            x = block_post(x, lp, n_head, eps, act)
+        return x
     for lp in params["layers"]:
-        x = block(x, lp, n_head, eps, trace)
+        x = block(x, lp, n_head, eps, trace, act)
     return layer_norm(x, params["lnf_g"], params["lnf_b"], eps)
 
 
 def head(params: dict, a: np.ndarray) -> np.ndarray:
     """Tied head: logits = a E^T with the same E as the token lookup ([P2] §25.4;
-    [P1] 第5步 logits = x @ token_embed.T; [P5] §4.1 softmax(h_n W_e^T))."""
-    return a @ params["wte"].T
+    [P1] 第5步 logits = x @ token_embed.T; [P5] §4.1 softmax(h_n W_e^T)); with an
+    untied head, a W_head^T ([P3] 二十三: nn.Linear(C, V, bias=False))."""
+    return a @ params.get("head_w", params["wte"]).T
 
 
 def derived_targets(idx: np.ndarray) -> np.ndarray:
@@ -220,7 +250,7 @@ def forward(params: dict, idx: np.ndarray, n_head: int, eps: float = 1e-5,
     B, T = idx.shape
     a = final_hidden(params, idx, n_head, eps, trace)
     y = derived_targets(idx) if targets is None else np.asarray(targets, dtype=np.int64)
-    V = params["wte"].shape[0]
+    V = params.get("head_w", params["wte"]).shape[0]
     if y.max() >= V:
         raise ValueError("target outside [0, V)")
     a2 = a.reshape(B * T, -1)
@@ -280,11 +310,14 @@ def greedy_cached(params: dict, prompt: np.ndarray, steps: int, n_head: int, eps
     kc = [None] * L  # each [B,H,t,D]
     uc = [None] * L
 
+    post = params.get("norm", "pre") == "post"
+    act = params.get("act", "tanh")
+
     def run(tokens: np.ndarray, pos0: int) -> np.ndarray:
         n = tokens.shape[1]
         x = params["wte"][tokens] + params["wpe"][pos0:pos0 + n]
         for l, lp in enumerate(params["layers"]):
-            a = layer_norm(x, lp["ln1_g"], lp["ln1_b"], eps)
+            a = x if post else layer_norm(x, lp["ln1_g"], lp["ln1_b"], eps)
             qkv = linear(a, lp["attn_w"], lp["attn_b"])
             q = qkv[..., :C].reshape(B, n, n_head, D).transpose(0, 2, 1, 3)
             k = qkv[..., C:2 * C].reshape(B, n, n_head, D).transpose(0, 2, 1, 3)
@@ -300,9 +333,13 @@ def greedy_cached(params: dict, prompt: np.ndarray, steps: int, n_head: int, eps
                     s = np.where(np.arange(tot)[None, :] > qpos, -np.inf, s)
                     y[b, h] = softmax_rows(s) @ uc[l][b, h]
             o = y.transpose(0, 2, 1, 3).reshape(B, n, C)
-            x = x + linear(o, lp["proj_w"], lp["proj_b"])
-            x = x + mlp_sublayer(layer_norm(x, lp["ln2_g"], lp["ln2_b"], eps), lp)
-        a = layer_norm(x[:, -1], params["lnf_g"], params["lnf_b"], eps)
+            if post:
+                x = layer_norm(x + linear(o, lp["proj_w"], lp["proj_b"]), lp["ln1_g"], lp["ln1_b"], eps)
+                x = layer_norm(x + mlp_sublayer(x, lp, act), lp["ln2_g"], lp["ln2_b"], eps)
+            else:
+                x = x + linear(o, lp["proj_w"], lp["proj_b"])
+                x = x + mlp_sublayer(layer_norm(x, lp["ln2_g"], lp["ln2_b"], eps), lp, act)
+        a = x[:, -1] if post else layer_norm(x[:, -1], params["lnf_g"], params["lnf_b"], eps)
         return head(params, a)
 
     toks, zs = [], []
