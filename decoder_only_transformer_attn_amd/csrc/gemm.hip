@@ -369,8 +369,11 @@ struct RawPair {
   }
 };
 
+// GELU, exact form: 0.5 z (1 + erf(z / sqrt 2)) (HIP's erff)
+__device__ __forceinline__ float gelu_erf(float v) { return 0.5f * v * (1.0f + erff(v * 0.7071067811865476f)); }
+
 template <typename T, int ACT = 0, bool F32OUT = false>
-struct EpiAct {  // out[m, n] = act(v + bias[n]); ACT 1 = tanh GELU; F32OUT: store fp32 instead of T
+struct EpiAct {  // out[m, n] = act(v + bias[n]); ACT 1 = tanh GELU, 2 = exact GELU; F32OUT: store fp32 instead of T
   static constexpr bool kPreload = false;
   static constexpr bool kCompact = true;
   typedef int Row;
@@ -393,6 +396,7 @@ struct EpiAct {  // out[m, n] = act(v + bias[n]); ACT 1 = tanh GELU; F32OUT: sto
     a = fmaf(w, Col::f32(bs.a), a);
     b = fmaf(w, Col::f32(bs.b), b);
     if constexpr (ACT == 1) { a = gelu_tanh(a); b = gelu_tanh(b); }
+    if constexpr (ACT == 2) { a = gelu_erf(a); b = gelu_erf(b); }
     return make_float2(a, b);
   }
   __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, const Col& bs, float2) const {
@@ -1271,6 +1275,10 @@ static hipError_t dispatch_gemm(const float* A, int lda, const float* W, int ldw
 template <typename T>
 static hipError_t linear_t(const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N, int K,
                            void* out, int ldo, int act, int out_f32, const SkinnyWs* sk, hipStream_t st) {
+  if (act == 2 && !out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
+                                                 EpiAct<T, 2, false>{(const T*)bias, out, ldo}, sk, st);
+  if (act == 2) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
+                                     EpiAct<T, 2, true>{(const T*)bias, out, ldo}, sk, st);
   if (act == 1 && !out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
                                                  EpiAct<T, 1, false>{(const T*)bias, out, ldo}, sk, st);
   if (act == 1) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,

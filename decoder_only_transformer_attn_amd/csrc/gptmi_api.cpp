@@ -39,6 +39,9 @@ int check_config(const gpt_config* c) {
   if (c->vocab <= 0 || c->ctx <= 0 || c->n_embd <= 0 || c->n_head <= 0 || c->n_layer < 0 || c->n_ff <= 0)
     return GPT_ERR_CONFIG;
   if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return GPT_ERR_CONFIG;
+  if ((c->activation != 0 && c->activation != 1) || (c->post_ln != 0 && c->post_ln != 1) ||
+      (c->untied_head != 0 && c->untied_head != 1))
+    return GPT_ERR_CONFIG;
   if (c->n_embd % c->n_head != 0) return GPT_ERR_CONFIG;
   const int D = c->n_embd / c->n_head, v = vec_of(c);
   if (c->n_embd % v || c->n_ff % v || D % v || D > 128 || c->n_embd > 2048) return GPT_ERR_CONFIG;
@@ -60,11 +63,16 @@ int64_t offsets(const gpt_config* c, int64_t* out, int n) {
     put(C); put(C); put(3 * C * C); put(3 * C); put(C * C); put(C);
     put(C); put(C); put(F * C); put(F); put(C * F); put(C);
   }
-  put(C);
-  put(C);
+  if (!c->post_ln) {   // final LayerNorm
+    put(C);
+    put(C);
+  }
+  if (c->untied_head) put(V * C);
   if (out && k < n) out[k] = off;
   return off;
 }
+
+int offset_count(const gpt_config* c) { return 2 + 12 * c->n_layer + (c->post_ln ? 0 : 2) + (c->untied_head ? 1 : 0) + 1; }
 
 // Element offsets of the tensors of one layer, packing order as documented.
 struct LayerP { int64_t ln1_g, ln1_b, attn_w, attn_b, proj_w, proj_b, ln2_g, ln2_b, fc_w, fc_b, fcproj_w, fcproj_b; };
@@ -73,6 +81,7 @@ struct Params {
   const char* base;
   size_t es;
   int64_t C, F, V, ctx, L;
+  bool post_ln, untied;
   const void* at(int64_t e) const { return base + e * (int64_t)es; }
   int64_t layer_base(int l) const {
     return V * C + ctx * C + (int64_t)l * (4 * C * C + 4 * C + 2 * C * F + F + C + 4 * C);
@@ -93,12 +102,15 @@ struct Params {
     r.fcproj_b = r.fcproj_w + C * F;
     return r;
   }
-  int64_t lnf_g() const { return layer_base((int)L); }
+  int64_t lnf_g() const { return layer_base((int)L); }   // pre-LN models only
   int64_t lnf_b() const { return layer_base((int)L) + C; }
+  // the head matrix: the token table, or the tensor after the last layer (and ln_f)
+  int64_t head_w() const { return untied ? layer_base((int)L) + (post_ln ? 0 : 2 * C) : 0; }
 };
 
 Params params_of(const gpt_config* c, const void* p) {
-  return Params{static_cast<const char*>(p), esize(c), c->n_embd, c->n_ff, c->vocab, c->ctx, c->n_layer};
+  return Params{static_cast<const char*>(p), esize(c), c->n_embd, c->n_ff, c->vocab, c->ctx, c->n_layer,
+                c->post_ln != 0, c->untied_head != 0};
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -196,12 +208,17 @@ int run_blocks(const Pass& s) {
   la.idx = s.idx; la.wte = P.at(0); la.wpe = P.at(P.V * P.C); la.vocab = cfg->vocab; la.ctx = cfg->ctx;
   la.pos = s.mode == STEP ? s.pos : nullptr;
   la.x = x; la.in_mul = 1; la.in_add = 0;
-  la.g = P.at(L > 0 ? P.layer(0).ln1_g : P.lnf_g());
-  la.b = P.at(L > 0 ? P.layer(0).ln1_b : P.lnf_b());
+  // pre-LN: the embedding kernel applies LN1 of block 0 (ln_f with no blocks);
+  // post-LN: block 0 reads the embedding itself
+  const bool post = cfg->post_ln != 0;
+  la.ident = post ? 1 : 0;
+  la.g = P.at(post ? 0 : (L > 0 ? P.layer(0).ln1_g : P.lnf_g()));
+  la.b = P.at(post ? 0 : (L > 0 ? P.layer(0).ln1_b : P.lnf_b()));
   la.out = a;
   la.zero = sk ? skw.cnt : nullptr; la.zero_n = sk ? skw.cnt_len : 0;
   GPT_TRY(launch_embed_ln(dt, la, s.st));
-  la.idx = nullptr; la.pos = nullptr; la.zero = nullptr; la.zero_n = 0;
+  la.idx = nullptr; la.pos = nullptr; la.zero = nullptr; la.zero_n = 0; la.ident = 0;
+  la.write_x = post ? 1 : 0;   // post-LN: each LayerNorm also replaces the residual row
 
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   for (int l = 0; l < L; ++l) {
@@ -241,17 +258,22 @@ int run_blocks(const Pass& s) {
     GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, true));
     GPT_TRY(launch_linear_resid(dt, o, C, P.at(w.proj_w), C, P.at(w.proj_b), M, C, C, x, C, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, false));
-    la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
+    // pre-LN: a = LN2(x) feeds the MLP; post-LN: x = a = LN1(x + attn)
+    la.g = P.at(post ? w.ln1_g : w.ln2_g); la.b = P.at(post ? w.ln1_b : w.ln2_b);
     GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
     GPT_TRY(launch_layernorm(dt, la, s.st));
     GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
-    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, 1, 0, s.st, sk));
+    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, cfg->activation ? 2 : 1, 0, s.st,
+                          sk));
     GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, true));
     GPT_TRY(launch_linear_resid(dt, h, F, P.at(w.fcproj_w), F, P.at(w.fcproj_b), M, C, F, x, C, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, false));
-    if (l + 1 < L) {   // ln_1 of the next block (ln_f is applied by the caller)
+    if (post) {        // x = a = LN2(n + mlp(n)): the next block's input (or the final hidden)
+      la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
+      GPT_TRY(launch_layernorm(dt, la, s.st));
+    } else if (l + 1 < L) {   // ln_1 of the next block (ln_f is applied by the caller)
       la.g = P.at(P.layer(l + 1).ln1_g); la.b = P.at(P.layer(l + 1).ln1_b);
       GPT_TRY(launch_layernorm(dt, la, s.st));
     }
@@ -260,7 +282,10 @@ int run_blocks(const Pass& s) {
 }
 
 // ln_f of M rows: residual row (r * mul + add) -> dense row r of out.  With no
-// blocks, the embedding kernel applied ln_f already (to every row, into ws.a).
+// blocks, the embedding kernel applied ln_f already (to every row, into ws.a);
+// post-LN models have no ln_f and ws.a holds the final hidden rows.
+bool rows_final(const gpt_config* c) { return c->n_layer == 0 || c->post_ln != 0; }
+
 int final_norm(const Pass& s, int M, int mul, int add, void* out) {
   const gpt_config* cfg = s.cfg;
   LnArgs la{};
@@ -291,7 +316,7 @@ int gpt_param_offsets(const gpt_config* cfg, int64_t* off, int n) {
   const int s = check_config(cfg);
   if (s != GPT_OK) return s;
   if (!off) return GPT_ERR_NULL;
-  if (n < 2 + 12 * cfg->n_layer + 3) return GPT_ERR_SHAPE;
+  if (n < offset_count(cfg)) return GPT_ERR_SHAPE;
   offsets(cfg, off, n);
   return GPT_OK;
 }
@@ -356,13 +381,13 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
   if (s != GPT_OK) return s;
   const int M = B * T, V = cfg->vocab, C = cfg->n_embd;
   void* a = at<char>(ws, pl.a);
-  if (cfg->n_layer > 0) {
+  if (!rows_final(cfg)) {
     s = final_norm(ps, M, 1, 0, a);
     if (s != GPT_OK) return s;
   }
   float* tok = token_loss ? token_loss : at<float>(ws, pl.tok);
   GPT_TRY(mark(ps, GPT_KERNEL_HEAD, true, true));
-  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(0), M, V, C, logits, V, at<float>(ws, pl.pmax),
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), M, V, C, logits, V, at<float>(ws, pl.pmax),
                          at<float>(ws, pl.psum), at<float>(ws, pl.tgt), nullptr, targets, idx, T, ps.st));
   GPT_TRY(mark(ps, GPT_KERNEL_HEAD, true, false));
   GPT_TRY(launch_ce_reduce(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), at<float>(ws, pl.tgt),
@@ -390,15 +415,16 @@ int gpt_prefill(const gpt_config* cfg, const void* params, const int32_t* idx, i
   if (s != GPT_OK) return s;
   // the greedy choice uses the last position of every sequence only
   void* alast = at<char>(ws, pl.alast);
-  s = cfg->n_layer > 0 ? final_norm(ps, B, Tp, Tp - 1, alast) : GPT_OK;
+  s = !rows_final(cfg) ? final_norm(ps, B, Tp, Tp - 1, alast) : GPT_OK;
   if (s != GPT_OK) return s;
-  if (cfg->n_layer == 0)   // rows of ws.a already hold ln_f: gather the last ones
+  if (rows_final(cfg))   // rows of ws.a already hold the final hidden: gather the last ones
     GPT_TRY(hipMemcpy2DAsync(alast, esize(cfg) * cfg->n_embd, at<char>(ws, pl.a) + (size_t)(Tp - 1) * esize(cfg) * cfg->n_embd,
                              (size_t)Tp * esize(cfg) * cfg->n_embd, esize(cfg) * cfg->n_embd, B, hipMemcpyDeviceToDevice,
                              ps.st));
   const int V = cfg->vocab;
-  GPT_TRY(launch_head_ce(cfg->dtype, alast, ps.P.at(0), B, V, cfg->n_embd, last_logits, V, at<float>(ws, pl.pmax),
-                         nullptr, nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1, ps.st));
+  GPT_TRY(launch_head_ce(cfg->dtype, alast, ps.P.at(ps.P.head_w()), B, V, cfg->n_embd, last_logits, V,
+                         at<float>(ws, pl.pmax), nullptr, nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1,
+                         ps.st));
   GPT_TRY(launch_argmax_reduce(B, pl.ntiles, at<float>(ws, pl.pmax), at<int32_t>(ws, pl.pidx), next_tok, pos, Tp,
                                ps.st));
   return GPT_OK;
@@ -420,13 +446,14 @@ int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* to
   s = run_blocks(ps);
   if (s != GPT_OK) return s;
   void* a = at<char>(ws, pl.a);
-  if (cfg->n_layer > 0) {
+  if (!rows_final(cfg)) {
     s = final_norm(ps, B, 1, 0, a);
     if (s != GPT_OK) return s;
   }
   const int V = cfg->vocab;
-  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(0), B, V, cfg->n_embd, logits, V, at<float>(ws, pl.pmax), nullptr,
-                         nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1, ps.st));
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), B, V, cfg->n_embd, logits, V,
+                         at<float>(ws, pl.pmax), nullptr, nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1,
+                         ps.st));
   GPT_TRY(launch_argmax_reduce(B, pl.ntiles, at<float>(ws, pl.pmax), at<int32_t>(ws, pl.pidx), next_tok, pos, -1,
                                ps.st));
   return GPT_OK;
@@ -476,7 +503,7 @@ int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const 
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
   if (!A || !W || !out) return GPT_ERR_NULL;
-  if (M <= 0 || N <= 0 || K <= 0 || K % vec_of(cfg) != 0 || (act != 0 && act != 1)) return GPT_ERR_SHAPE;
+  if (M <= 0 || N <= 0 || K <= 0 || K % vec_of(cfg) != 0 || act < 0 || act > 2) return GPT_ERR_SHAPE;
   return hip_status(launch_linear(cfg->dtype, A, K, W, K, bias, M, N, K, out, N, act, out_f32 ? 1 : 0,
                                   static_cast<hipStream_t>(stream)));
 }

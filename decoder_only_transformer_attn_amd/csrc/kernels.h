@@ -32,6 +32,8 @@ struct LnArgs {
   const void* g; const void* b;        // LayerNorm gain / bias
   void* out;                           // [M, C] normalised rows
   int* zero; int zero_n;               // embedding: nullable ints set to zero (split-K counters)
+  int ident;                           // embedding: out = x itself (no LayerNorm; post-LN models)
+  int write_x;                         // LayerNorm: the normalised row also replaces its x row (post-LN)
 };
 
 // Attention of one new query per (b, h) over positions 0 .. *pos of the cache.

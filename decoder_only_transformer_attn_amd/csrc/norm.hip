@@ -71,6 +71,15 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
       if (c < C) load4(xr + c, v[j]);
     }
   }
+  T* __restrict__ orow = reinterpret_cast<T*>(a.out) + (size_t)row * C;
+  if (EMBED && a.ident) {   // post-LN model: the first block reads the embedding itself
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = (j * 64 + lane) * 4;
+      if (c < C) store4(orow + c, v[j]);
+    }
+    return;
+  }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j)
@@ -84,7 +93,7 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
       for (int e = 0; e < 4; ++e) { float d = v[j][e] - mean; s2 += d * d; }
   const float var = wave_sum(s2) / (float)C;
   const float rstd = 1.0f / sqrtf(var + a.eps);
-  T* __restrict__ orow = reinterpret_cast<T*>(a.out) + (size_t)row * C;
+  float* __restrict__ xw = (!EMBED && a.write_x) ? a.x + (size_t)(row * a.in_mul + a.in_add) * C : nullptr;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = (j * 64 + lane) * 4;
@@ -95,6 +104,7 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = (v[j][e] - mean) * rstd * g4[e] + b4[e];
       store4(orow + c, o4);
+      if (xw) store4(xw + c, o4);   // post-LN: the normalised row is the new residual stream
     }
   }
 }

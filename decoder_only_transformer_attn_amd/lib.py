@@ -26,7 +26,8 @@ _c_int, _c_i64, _vp, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes
 class gpt_config(ctypes.Structure):
     _fields_ = [("vocab", ctypes.c_int32), ("ctx", ctypes.c_int32), ("n_embd", ctypes.c_int32),
                 ("n_head", ctypes.c_int32), ("n_layer", ctypes.c_int32), ("n_ff", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("post_ln", ctypes.c_int32), ("untied_head", ctypes.c_int32)]
 
 
 class gpt_sampling(ctypes.Structure):
@@ -88,7 +89,8 @@ def check(status: int) -> None:
 
 
 def cfg_c(cfg) -> gpt_config:
-    return gpt_config(cfg.vocab, cfg.ctx, cfg.n_embd, cfg.n_head, cfg.n_layer, cfg.n_ff, cfg.ln_eps, cfg.dtype)
+    return gpt_config(cfg.vocab, cfg.ctx, cfg.n_embd, cfg.n_head, cfg.n_layer, cfg.n_ff, cfg.ln_eps, cfg.dtype,
+                      getattr(cfg, "act", 0), getattr(cfg, "post_ln", 0), getattr(cfg, "untied", 0))
 
 
 def param_count(cfg) -> int:
@@ -96,7 +98,7 @@ def param_count(cfg) -> int:
 
 
 def param_offsets(cfg):
-    n = 2 + 12 * cfg.n_layer + 3
+    n = 2 + 12 * cfg.n_layer + (0 if getattr(cfg, "post_ln", 0) else 2) + (1 if getattr(cfg, "untied", 0) else 0) + 1
     arr = (ctypes.c_int64 * n)()
     check(load().gpt_param_offsets(ctypes.byref(cfg_c(cfg)), arr, n))
     return list(arr)

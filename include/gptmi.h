@@ -54,7 +54,17 @@ enum gpt_status {
 };
 
 /* Model configuration (host).  n_ff is the MLP width (4 * n_embd for GPT-2,
- * "第 25 章 从小 GPT 到 GPT-2" §25.3).  ln_eps is 1e-5 for every model here. */
+ * "第 25 章 从小 GPT 到 GPT-2" §25.3).  ln_eps is 1e-5 for every model here.
+ * The last three fields select the variants the pages describe besides GPT-2
+ * (all 0 for GPT-2):
+ *   activation   0: tanh GELU ("GPT-1学习笔记" §3.6 approximation; §25.3);
+ *                1: exact GELU 0.5 z (1 + erf(z / sqrt 2)) ("GPT-1学习笔记"
+ *                §3.6 standard formula; "Day 16" nn.GELU()).
+ *   post_ln      0: pre-LN blocks and a final LayerNorm (GPT-2);
+ *                1: post-LN blocks, n = LN1(x + attn(x)), h = LN2(n + mlp(n)),
+ *                and no final LayerNorm ("GPT-1学习笔记" §3.1-§3.2, §4.1).
+ *   untied_head  0: the head reuses the token table (tying);
+ *                1: a separate head matrix [V, C] without bias ("Day 16" 二十三). */
 typedef struct gpt_config {
   int32_t vocab;    /* V */
   int32_t ctx;      /* maximum sequence length (rows of the position table) */
@@ -64,11 +74,15 @@ typedef struct gpt_config {
   int32_t n_ff;     /* MLP hidden width */
   float ln_eps;
   int32_t dtype;    /* enum gpt_dtype */
+  int32_t activation;
+  int32_t post_ln;
+  int32_t untied_head;
 } gpt_config;
 
 /* Number of unique parameters, closed form ("第 25 章 从小 GPT 到 GPT-2" §25.4):
  * L(4C^2+4C + 2C*F+F+C + 4C) + VC + ctx*C + 2C, which is L(12C^2+13C)+VC+ctx*C+2C
- * at F = 4C.  Also the element count of the parameter blob.  Returns a
+ * at F = 4C; a post-LN model has no final LayerNorm (no 2C), an untied head
+ * adds VC.  Also the element count of the parameter blob.  Returns a
  * negative gpt_status on an invalid config (host only, no HIP call). */
 int64_t gpt_param_count(const gpt_config* cfg);
 
@@ -76,10 +90,13 @@ int64_t gpt_param_count(const gpt_config* cfg);
  *   wte[V,C], wpe[ctx,C],
  *   per layer l: ln1_g[C], ln1_b[C], attn_w[3C,C], attn_b[3C], proj_w[C,C], proj_b[C],
  *                ln2_g[C], ln2_b[C], fc_w[F,C], fc_b[F], fcproj_w[C,F], fcproj_b[C],
- *   lnf_g[C], lnf_b[C], end.
- * There is no head tensor: the head reads wte (tying as one shared tensor, §25.4).
- * off (host) receives n = 2 + 12 L + 3 values.  Returns GPT_OK, or
- * GPT_ERR_SHAPE if n is too small (host only). */
+ *   lnf_g[C], lnf_b[C]   (pre-LN models only),
+ *   head_w[V,C]          (untied head only),
+ *   end.
+ * With a tied head there is no head tensor: the head reads wte (tying as one
+ * shared tensor, §25.4).  off (host) receives 2 + 12 L + (post_ln ? 0 : 2) +
+ * (untied_head ? 1 : 0) + 1 values.  Returns GPT_OK, or GPT_ERR_SHAPE if n is
+ * too small (host only). */
 int gpt_param_offsets(const gpt_config* cfg, int64_t* off, int n);
 
 /* Device workspace bytes needed by gpt_forward for a [B, T] batch (host only). */
@@ -209,7 +226,7 @@ int gpt_debug_layernorm(const gpt_config* cfg, const float* x, const void* g, co
                         void* out, void* stream);
 
 /* out[M,N] = act(A[M,K] W[N,K]^T + bias[N]); A, W, bias in cfg->dtype (bias
- * nullable); act 0 = none, 1 = tanh GELU; out fp32 if out_f32 else cfg->dtype.
+ * nullable); act 0 = none, 1 = tanh GELU, 2 = exact GELU; out fp32 if out_f32 else cfg->dtype.
  * Requires K % 8 == 0 (bf16) or K % 4 == 0 (fp32). */
 int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const void* bias, int M, int N,
                      int K, int act, int out_f32, void* out, void* stream);

@@ -151,3 +151,18 @@ def test_sample_validation_before_any_hip_call():
     big = ctypes.byref(lib.cfg_c(synth.GPTConfig(vocab=60000, ctx=8, n_embd=16, n_head=2, n_layer=1, n_ff=64)))
     assert smp(cfg=big) == -2                                  # vocabulary beyond one block's slices
     assert L.gpt_mark_seen(c, None, 2, 3, 1, None) == -1 and L.gpt_mark_seen(c, 1, 0, 3, 1, None) == -4
+
+
+@pytest.mark.parametrize("post_ln,untied", [(1, 0), (0, 1), (1, 1)])
+def test_param_count_and_offsets_of_variants(post_ln, untied):
+    import dataclasses as dc
+    cfg = dc.replace(synth.MINI, post_ln=post_ln, untied=untied, act=1)
+    assert lib.param_count(cfg) == O.param_count(cfg.vocab, cfg.n_embd, cfg.n_layer, cfg.ctx, cfg.n_ff,
+                                                 post_ln=bool(post_ln), untied=bool(untied))
+    assert lib.param_offsets(cfg) == [off for _, _, off in synth.blob_layout(cfg)]
+
+
+def test_variant_flags_are_validated():
+    import dataclasses as dc
+    for bad in (dict(act=2), dict(post_ln=-1), dict(untied=3)):
+        assert lib.load().gpt_param_count(ctypes.byref(lib.cfg_c(dc.replace(synth.MICRO, **bad)))) == -2

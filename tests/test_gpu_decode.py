@@ -88,6 +88,30 @@ def test_minigpt_fp32_decode(B, Tp, Tmax, steps):
     check_against_oracle(cfg, params, prompt, toks, z, range(B), fp32_tol, fp32_tol)
 
 
+@pytest.mark.parametrize("var", [dict(act=1, post_ln=1, untied=1), dict(post_ln=1), dict(untied=1)],
+                         ids=lambda v: "-".join(v))
+def test_variant_decode_fp32(var):
+    # GPT-1 style blocks (post-LN, no ln_f), exact GELU and an untied head,
+    # through prefill and cached steps
+    cfg = dc.replace(synth.MINI, **var)
+    params = synth.make_params(cfg, seed=9, cfg_id=2, init="stress")
+    prompt = synth.make_ids(cfg, 3, 21, seed=9, cfg_id=2)
+    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=10, Tmax=40)
+    assert pos == 31
+    check_against_oracle(cfg, params, prompt, toks, z, range(3), fp32_tol, fp32_tol)
+
+
+def test_variant_decode_bf16_skinny():
+    # the same variants in bf16 at B = 5: skinny products, split-K fc-projection
+    cfg = synth.GPTConfig(vocab=300, ctx=64, n_embd=128, n_head=2, n_layer=2, n_ff=1536, dtype=synth.BF16,
+                          act=1, post_ln=1, untied=1)
+    params = synth.make_params(cfg, seed=10, cfg_id=10, init="stress")
+    prompt = synth.make_ids(cfg, 5, 9, seed=10, cfg_id=10)
+    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=10, Tmax=32, rows=[0, 4])
+    assert pos == 19
+    check_against_oracle(cfg, params, prompt, toks, z, [0, 4], bf16_tol, bf16_band)
+
+
 def test_zero_layer_decode_fp32():
     cfg = dc.replace(synth.MICRO, n_layer=0)
     params = synth.make_params(cfg, seed=3, cfg_id=1, init="stress")

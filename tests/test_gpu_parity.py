@@ -198,6 +198,63 @@ def test_causal_batch_invariance_and_determinism_fp32():
 
 
 # ---------------------------------------------------------------------------
+# Model variants: exact GELU, post-LN GPT-1 blocks without ln_f, untied head
+# ---------------------------------------------------------------------------
+VARIANTS = [dict(act=1), dict(post_ln=1), dict(untied=1), dict(act=1, post_ln=1, untied=1)]
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(v))
+@pytest.mark.parametrize("base,B,T", [("micro", 4, 12), ("mini", 3, 37)])
+def test_variants_fp32_parity(var, base, B, T):
+    import dataclasses as dc
+    cfg = dc.replace(synth.MICRO if base == "micro" else synth.MINI, **var)
+    params = synth.make_params(cfg, seed=21, cfg_id=8, init="stress")
+    ids = synth.make_ids(cfg, B, T, seed=21, cfg_id=8)
+    check_fp32(cfg, params, ids)
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(v))
+def test_variants_zero_layers_fp32(var):
+    import dataclasses as dc
+    cfg = dc.replace(synth.MICRO, n_layer=0, **var)
+    params = synth.make_params(cfg, seed=22, cfg_id=8, init="stress")
+    check_fp32(cfg, params, synth.make_ids(cfg, 2, 12, seed=22))
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(v))
+def test_variants_bf16_parity(var):
+    import dataclasses as dc
+    cfg = dc.replace(synth.GPTConfig(vocab=1000, ctx=256, n_embd=256, n_head=4, n_layer=2, n_ff=1024,
+                                     dtype=synth.BF16), **var)
+    params = synth.make_params(cfg, seed=23, cfg_id=8, init="stress")
+    ids = synth.make_ids(cfg, 2, 200, seed=23, cfg_id=8)
+    lg, tok, mean = run_gpu(cfg, params, ids)
+    ref_l, ref_t, ref_m = O.forward(synth.unpack_f64(cfg, params), ids, cfg.n_head)
+    _bf16_check(lg, tok, ref_l, ref_t, [0, 1])
+    assert abs(mean - ref_m) <= 1e-2
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("M,N,K", [(100, 77, 40), (1024, 2304, 768), (37, 768, 3072)])
+def test_linear_exact_gelu(dtype, M, N, K):
+    lib = _lib()
+    cfg = synth.GPTConfig(vocab=17, ctx=16, n_embd=16, n_head=2, n_layer=1, n_ff=64, dtype=dtype)
+    rng = np.random.default_rng(M + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = (0.05 * rng.standard_normal((N, K))).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    if dtype == synth.BF16:
+        A, W, bias = synth.round_bf16(A), synth.round_bf16(W), synth.round_bf16(bias)
+    td = lib.torch_dtype(cfg)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    lib.debug_linear(cfg, torch.from_numpy(A).to(td).cuda(), torch.from_numpy(W).to(td).cuda(),
+                     torch.from_numpy(bias).to(td).cuda(), out, act=2, out_f32=True)
+    torch.cuda.synchronize()
+    ref = O.gelu_erf(O.linear(A.astype(np.float64), W.astype(np.float64), bias.astype(np.float64)))
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
 # GPT-2 124M bf16 at full size
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
