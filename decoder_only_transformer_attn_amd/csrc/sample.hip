@@ -126,15 +126,19 @@ struct Blk {
 // A thread's slice of the row: the first NREG values in registers, the rest
 // in LDS at stride SMP_THREADS (bank-conflict free).  Values are visited in
 // index order; f(v, i) may change v, which is written back.
-constexpr int SMP_LDS_SLOTS = 36;   // 144 KB of LDS
+constexpr int SMP_LDS_SLOTS = 36;   // 144 KB of LDS (+ 8 KB for the compacted top-k list)
 constexpr int SMP_NREG = 16;
 constexpr int SMP_MAXPT = SMP_NREG + SMP_LDS_SLOTS;   // V <= 53248
 
+// After a top-k of at most SMP_THREADS candidates the slice is compacted: each
+// thread then holds one candidate (r[0], vocabulary index i0; zero if none).
 struct Slice {
   float r[SMP_NREG];
   float* lds;
   int nl, i0, tid;
+  bool compact;
   template <typename F> __device__ __forceinline__ void for_each(F f) {
+    if (compact) { f(r[0], i0); return; }
 #pragma unroll
     for (int j = 0; j < SMP_NREG; ++j) f(r[j], i0 + j);
     for (int l = 0; l < nl; ++l) {
@@ -144,6 +148,7 @@ struct Slice {
     }
   }
   template <typename F> __device__ __forceinline__ void visit(F f) const {   // read only
+    if (compact) { f(r[0], i0); return; }
 #pragma unroll
     for (int j = 0; j < SMP_NREG; ++j) f(r[j], i0 + j);
     for (int l = 0; l < nl; ++l) f(lds[l * SMP_THREADS + tid], i0 + SMP_NREG + l);
@@ -152,6 +157,7 @@ struct Slice {
   // sums so that the additions do not form one long dependent chain; the
   // order is fixed, so the result is the same on every run
   template <typename X, typename G> __device__ __forceinline__ X sum(G g) const {
+    if (compact) return g(r[0]);
     X p0 = X(0), p1 = X(0), p2 = X(0), p3 = X(0);
 #pragma unroll
     for (int j = 0; j < SMP_NREG; j += 4) {
@@ -173,6 +179,8 @@ template <typename T>
 __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
   __shared__ SmpShared sh;
   __shared__ float slots[SMP_LDS_SLOTS * SMP_THREADS];
+  __shared__ float cw[SMP_THREADS];   // compacted top-k candidates: weight, vocabulary index
+  __shared__ int ci[SMP_THREADS];
   const int tid = threadIdx.x;
   Blk blk{&sh, 0, tid & 63, tid >> 6};
   const int row = blockIdx.x, V = a.V;
@@ -187,6 +195,7 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
   sl.nl = max(0, npt - SMP_NREG);
   sl.i0 = i0;
   sl.tid = tid;
+  sl.compact = false;
 
   // penalised logits; indices past the slice hold -inf (weight 0 later)
   sl.for_each([&](float& v, int i) {
@@ -249,6 +258,22 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
           if (b < t) v = 0.f;
           else if (b == t) { if (r >= need) v = 0.f; ++r; }
         });
+      }
+      if (a.top_k <= SMP_THREADS) {
+        // at most 1024 candidates (weight > 0) remain: gather them, in index
+        // order, one per thread, so that the later searches visit one value each
+        int cnt = 0;
+        sl.visit([&](float v, int) { cnt += v > 0.f; });
+        int at = blk.exscan(cnt);
+        const int total = blk.sum(cnt);
+        sl.visit([&](float v, int i) {
+          if (v > 0.f) { cw[at] = v; ci[at] = i; ++at; }
+        });
+        __syncthreads();
+        const bool have = tid < total;
+        sl.compact = true;
+        sl.r[0] = have ? cw[tid] : 0.f;
+        sl.i0 = have ? ci[tid] : 0;
       }
     }
     // Largest pattern t whose mass(w >= t) is above the target (>= when ge,
