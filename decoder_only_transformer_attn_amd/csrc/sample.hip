@@ -179,7 +179,7 @@ template <typename T>
 __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
   __shared__ SmpShared sh;
   __shared__ float slots[SMP_LDS_SLOTS * SMP_THREADS];
-  __shared__ float cw[SMP_THREADS];   // compacted top-k candidates: weight, vocabulary index
+  __shared__ float cw[SMP_THREADS];   // compacted top-k candidates (weight, vocabulary index), or the weights a search narrowed to
   __shared__ int ci[SMP_THREADS];
   const int tid = threadIdx.x;
   Blk blk{&sh, 0, tid & 63, tid >> 6};
@@ -280,12 +280,43 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
     // > otherwise); returns in `cum` the mass of the weights above t plus that
     // of the weights equal to t in the threads before this one, for the caller
     // to resolve the equal ones in index order.
+    //
+    // Once the bits above `bit` are fixed, only the weights whose patterns
+    // share them, [t, t + 2^(bit+1)), are still undecided: those above count
+    // in every later step, those below in none.  At a few checkpoints the
+    // undecided weights are counted; when at most SMP_THREADS remain they are
+    // gathered one per thread (cw) and the remaining steps sum that one value
+    // plus the fixed mass above the range.
     auto threshold = [&](double target, bool ge, uint32_t& t, double& cum) {
       t = 0;
+      bool nar = false;
+      float nv = 0.f;
+      double base = 0.0;
       for (int bit = 29; bit >= 0; --bit) {
+        if (!nar && !sl.compact && (bit == 22 || bit == 19 || bit == 16 || bit == 13)) {
+          const uint32_t lo = t, hi = t + (2u << bit);
+          const int n = sl.sum<int>([&](float v) {
+            const uint32_t b = __float_as_uint(v);
+            return b >= lo && b < hi ? 1 : 0;
+          });
+          int at = blk.exscan(n);
+          const int total = blk.sum(n);
+          if (total <= SMP_THREADS) {
+            double ab = 0.0;
+            sl.visit([&](float v, int) {
+              const uint32_t b = __float_as_uint(v);
+              ab += b >= hi ? wd(v) : 0.0;
+              if (b >= lo && b < hi) cw[at++] = v;
+            });
+            base = blk.sum(ab);   // (its barrier also publishes cw)
+            nv = tid < total ? cw[tid] : 0.f;
+            nar = true;
+          }
+        }
         const uint32_t c = t | (1u << bit);
-        double sm = sl.sum<double>([&](float v) { return __float_as_uint(v) >= c ? wd(v) : 0.0; });
-        sm = blk.sum(sm);
+        double sm;
+        if (nar) sm = base + blk.sum(__float_as_uint(nv) >= c ? wd(nv) : 0.0);
+        else sm = blk.sum(sl.sum<double>([&](float v) { return __float_as_uint(v) >= c ? wd(v) : 0.0; }));
         if (ge ? sm >= target : sm > target) t = c;
       }
       double above = 0.0, eq = 0.0;
