@@ -25,7 +25,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wno-unused-result", "-I", os.path.join(os.path.dirname(HERE), "include")]
 
-SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "ce.hip", "sample.hip", "gptmi_api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "ce.hip", "sample.hip", "backward.hip", "gptmi_api.cpp"]
 
 
 def hipcc() -> str:

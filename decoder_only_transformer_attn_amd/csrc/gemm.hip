@@ -499,6 +499,83 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   }
 };
 
+// Loss gradient of the head's logits: dz[m, n] = (exp(v - lse[m]) - [n == y[m]])
+// * s[m], s = 1 / (number of rows with a target) for a row with one, else 0.
+template <typename T>
+struct EpiDz {
+  static constexpr bool kPreload = false;
+  static constexpr bool kCompact = true;
+  struct Row { float lse, s; int y; };
+  typedef int Col;
+  typedef int ColX;
+  const float* lse;      // [M]
+  const int32_t* y;      // [M] target of each row, -1 for none
+  const float* inv;      // [1] 1 / n_valid (0 when no row has a target)
+  T* dz;
+  long long ld;
+  int M;
+  __device__ __forceinline__ Row row(int m) const {
+    if (m >= M) return Row{0.f, 0.f, -1};   // (rows past M are never stored)
+    const int yy = y[m];
+    return Row{lse[m], yy >= 0 ? *inv : 0.f, yy};
+  }
+  __device__ __forceinline__ Col col(int, bool) const { return 0; }
+  __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ float2 value(const Row& r, int n, float a, float b) const {
+    constexpr float LOG2E = 1.4426950408889634f;
+    a = (fast_exp2((a - r.lse) * LOG2E) - (n == r.y ? 1.f : 0.f)) * r.s;
+    b = (fast_exp2((b - r.lse) * LOG2E) - (n + 1 == r.y ? 1.f : 0.f)) * r.s;
+    return make_float2(a, b);
+  }
+  __device__ __forceinline__ void pair(const Row& r, int m, int n, float a, float b, bool has_b, ColX, float2) const {
+    const float2 v = value(r, n, a, b);
+    store_pair(dz + (long long)m * ld + n, v.x, v.y, has_b, (ld & 1) == 0);
+  }
+  __device__ __forceinline__ bool vec_ok() const { return (ld & 1) == 0; }
+  __device__ __forceinline__ void pair_in(const Row& r, int m, int n, float a, float b, ColX, float2) const {
+    const float2 v = value(r, n, a, b);
+    T* p = dz + (long long)m * ld + n;
+    if constexpr (sizeof(T) == 4) *reinterpret_cast<float2*>(p) = v;
+    else *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v.x, v.y);
+  }
+};
+
+// fp32 output, out[m, n] = v (ACC false) or out[m, n] += v (ACC true; the
+// old value is read at the store, so nothing is held across the main loop)
+template <bool ACC>
+struct EpiF32 {
+  static constexpr bool kPreload = false;
+  static constexpr bool kCompact = true;
+  typedef int Row;
+  typedef int Col;
+  typedef int ColX;
+  float* out;
+  int ldo;
+  __device__ __forceinline__ Row row(int) const { return 0; }
+  __device__ __forceinline__ Col col(int, bool) const { return 0; }
+  __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ void pair(Row, int m, int n, float a, float b, bool has_b, ColX, float2) const {
+    float* p = out + (size_t)m * ldo + n;
+    if constexpr (ACC) {
+      a += p[0];
+      if (has_b) b += p[1];
+    }
+    store_pair(p, a, b, has_b, (ldo & 1) == 0);
+  }
+  __device__ __forceinline__ bool vec_ok() const { return (ldo & 1) == 0; }
+  __device__ __forceinline__ void pair_in(Row, int m, int n, float a, float b, ColX, float2) const {
+    float2* p = reinterpret_cast<float2*>(out + (size_t)m * ldo + n);
+    if constexpr (ACC) {
+      const float2 o = *p;
+      a += o.x;
+      b += o.y;
+    }
+    *p = make_float2(a, b);
+  }
+};
+
 // Output driver.  Lanes 2k and 2k+1 hold columns n and n+1 of a 32x32 tile,
 // and registers r, r+1 (r even) are rows m, m+1.  One exchange gives the even
 // lane (row m; n, n+1) and the odd lane (row m+1; n, n+1), so every lane
@@ -1251,10 +1328,11 @@ static hipError_t run_gemm_dma_k(const bf16* A, const bf16* W, int M, int N, con
   return run_gemm_dma<256, 256, 64, 128, K, 4, 32>(A, W, M, N, epi, st);
 }
 
+// Block-tiled products (any M; K a multiple of 64 for the pipelined path,
+// otherwise chunks past K read as zero)
 template <typename Epi>
-static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
-                                const SkinnyWs* sk, hipStream_t st) {
-  if (M <= 64 && lda % 8 == 0 && ldw % 8 == 0) return run_skinny(A, lda, W, ldw, M, N, K, epi, sk, st);
+static hipError_t dispatch_gemm_tiled(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+                                      const Epi& epi, hipStream_t st) {
   const long long tiles256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= 64 && lda == K && ldw == K) {
     if (K == 768) return run_gemm_dma_k<768>(A, W, M, N, epi, st);
@@ -1264,6 +1342,19 @@ static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, 
   if ((long long)M * N >= (long long)256 * 1024 * 16)
     return run_gemm<bf16, 128, 128, 64, 64, 64>(A, lda, W, ldw, M, N, K, epi, st);
   return run_gemm<bf16, 64, 64, 64, 32, 32>(A, lda, W, ldw, M, N, K, epi, st);
+}
+
+template <typename Epi>
+static hipError_t dispatch_gemm(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const Epi& epi,
+                                const SkinnyWs* sk, hipStream_t st) {
+  if (M <= 64 && lda % 8 == 0 && ldw % 8 == 0) return run_skinny(A, lda, W, ldw, M, N, K, epi, sk, st);
+  return dispatch_gemm_tiled(A, lda, W, ldw, M, N, K, epi, st);
+}
+
+template <typename Epi>
+static hipError_t dispatch_gemm_tiled(const float* A, int lda, const float* W, int ldw, int M, int N, int K,
+                                      const Epi& epi, hipStream_t st) {
+  return run_gemm<float, 64, 64, 32, 32, 32>(A, lda, W, ldw, M, N, K, epi, st);
 }
 
 template <typename Epi>
@@ -1318,6 +1409,29 @@ static hipError_t qkv_t(const QKVArgs& a, const SkinnyWs* sk, hipStream_t st) {
 hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyWs* sk) {
   if (dtype == 0) return qkv_t<float>(a, sk, st);
   return qkv_t<bf16>(a, sk, st);
+}
+
+// Loss gradient of the logits A W^T ([M, C] x [V, C]^T) into dz [M, V] (ld).
+hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V, int C, const float* lse,
+                          const int32_t* y, const float* inv, void* dz, long long ld, hipStream_t st) {
+  if (dtype == 0)
+    return dispatch_gemm_tiled((const float*)A, C, (const float*)W, C, M, V, C,
+                               EpiDz<float>{lse, y, inv, (float*)dz, ld, M}, st);
+  return dispatch_gemm_tiled((const bf16*)A, C, (const bf16*)W, C, M, V, C, EpiDz<bf16>{lse, y, inv, (bf16*)dz, ld, M},
+                             st);
+}
+
+// out [M, N] fp32 (=, or += with accumulate) A [M, K] . W [N, K]^T
+hipError_t launch_gemm_f32out(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+                              float* out, int ldo, int accumulate, hipStream_t st) {
+  if (dtype == 0) {
+    if (accumulate)
+      return dispatch_gemm_tiled((const float*)A, lda, (const float*)W, ldw, M, N, K, EpiF32<true>{out, ldo}, st);
+    return dispatch_gemm_tiled((const float*)A, lda, (const float*)W, ldw, M, N, K, EpiF32<false>{out, ldo}, st);
+  }
+  if (accumulate)
+    return dispatch_gemm_tiled((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, EpiF32<true>{out, ldo}, st);
+  return dispatch_gemm_tiled((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, EpiF32<false>{out, ldo}, st);
 }
 
 // bf16 head tile for C = 768 (vocab x tokens, per-wave vocab x tokens)

@@ -302,6 +302,48 @@ int check_cache_args(const gpt_config* cfg, void* kc, void* vc, int Tmax, int B)
   return GPT_OK;
 }
 
+// Workspace of the head backward.  dz [M, Vp] and its transpose [V, Np], the
+// head matrix's transpose [C, Vp] and a's [C, Np] are zero-padded to multiples
+// of 64 along the contracted axis, so both gradient products run without a
+// K tail.
+struct BwdPlan {
+  size_t a, aT, ET, dz, dzT, pmax, psum, tgt, tok, bsum, lse, yv, inv, da, mu, rs, lnpart, total;
+  int ntiles, nblocks, Vp, Np, nchunks;
+};
+
+constexpr long long BWD_MAX_ROWS = 1LL << 20;
+
+BwdPlan bwd_plan(const gpt_config* c, int B, int T) {
+  BwdPlan p{};
+  const size_t M = (size_t)B * T, C = c->n_embd, V = c->vocab, es = esize(c);
+  p.ntiles = head_ntiles(c->dtype, (int)M, c->vocab, c->n_embd, false);
+  p.nblocks = ce_reduce_blocks((int)M);
+  p.Vp = (int)align_up(V, 64);
+  p.Np = (int)align_up(M, 64);
+  p.nchunks = ln_bwd_chunks((int)M);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  p.a = take(M * C * es);
+  p.aT = take(C * p.Np * es);
+  p.ET = take(C * p.Vp * es);
+  p.dz = take(M * p.Vp * es);
+  p.dzT = take(V * p.Np * es);
+  p.pmax = take(M * p.ntiles * 4);
+  p.psum = take(M * p.ntiles * 4);
+  p.tgt = take(M * 4);
+  p.tok = take(M * 4);
+  p.bsum = take((size_t)p.nblocks * 2 * 8);
+  p.lse = take(M * 4);
+  p.yv = take(M * 4);
+  p.inv = take(4);
+  p.da = take(M * C * 4);
+  p.mu = take(M * 4);
+  p.rs = take(M * 4);
+  p.lnpart = take((size_t)p.nchunks * 2 * C * 4);
+  p.total = off;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -483,6 +525,87 @@ int gpt_mark_seen(const gpt_config* cfg, const int32_t* tokens, int B, int T, ui
   if (!tokens || !seen) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
   return hip_status(launch_mark_seen(tokens, B, T, cfg->vocab, seen, static_cast<hipStream_t>(stream)));
+}
+
+int gpt_head_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!bytes) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0 || (long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
+  if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  *bytes = bwd_plan(cfg, B, T).total;
+  return GPT_OK;
+}
+
+int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                      const int32_t* targets, const float* x, float* dx, float* grads, float* mean_loss, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!params || !idx || !x || !dx || !grads || !ws) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0 || (long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
+  if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  const BwdPlan pl = bwd_plan(cfg, B, T);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
+  const Params P = params_of(cfg, params);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = cfg->dtype, M = B * T, V = cfg->vocab, C = cfg->n_embd;
+  const bool post = cfg->post_ln != 0;
+  const void* Wh = P.at(P.head_w());
+  void* a = at<char>(ws, pl.a);
+
+  // final hidden rows in the compute dtype: ln_f(x), or x itself (post-LN)
+  if (!post) {
+    LnArgs la{};
+    la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps;
+    la.x = const_cast<float*>(x); la.in_mul = 1; la.in_add = 0;   // read only (write_x is 0)
+    la.g = P.at(P.lnf_g()); la.b = P.at(P.lnf_b());
+    la.out = a;
+    GPT_TRY(launch_layernorm(dt, la, st));
+  } else {
+    GPT_TRY(launch_cast_rows(dt, x, (long long)M * C, a, st));
+  }
+  // log-sum-exp of every row, targets, 1 / n_valid and the mean loss
+  GPT_TRY(launch_head_ce(dt, a, Wh, M, V, C, nullptr, 0, at<float>(ws, pl.pmax), at<float>(ws, pl.psum),
+                         at<float>(ws, pl.tgt), nullptr, targets, idx, T, st));
+  GPT_TRY(launch_ce_reduce(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), at<float>(ws, pl.tgt),
+                           targets, idx, T, V, at<float>(ws, pl.tok), at<double>(ws, pl.bsum), mean_loss, st));
+  GPT_TRY(launch_bwd_rows(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), targets, idx, T, V,
+                          at<float>(ws, pl.lse), at<int32_t>(ws, pl.yv), at<float>(ws, pl.inv), st));
+  // dz = (softmax - onehot) / n_valid, recomputed from the fp32 accumulators of a second head product
+  void* dz = at<char>(ws, pl.dz);
+  GPT_TRY(launch_head_dz(dt, a, Wh, M, V, C, at<float>(ws, pl.lse), at<int32_t>(ws, pl.yv), at<float>(ws, pl.inv),
+                         dz, pl.Vp, st));
+  GPT_TRY(launch_zero_cols(dt, dz, pl.Vp, M, V, pl.Vp, st));
+  void* ET = at<char>(ws, pl.ET);
+  void* aT = at<char>(ws, pl.aT);
+  void* dzT = at<char>(ws, pl.dzT);
+  GPT_TRY(launch_transpose(dt, Wh, C, V, C, ET, pl.Vp, st));
+  GPT_TRY(launch_transpose(dt, a, C, M, C, aT, pl.Np, st));
+  GPT_TRY(launch_transpose(dt, dz, pl.Vp, M, V, dzT, pl.Np, st));
+  // da = dz W_head (contraction over the padded vocabulary); post-LN: that is dx
+  float* da = post ? dx : at<float>(ws, pl.da);
+  GPT_TRY(launch_gemm_f32out(dt, dz, pl.Vp, ET, pl.Vp, M, C, pl.Vp, da, C, 0, st));
+  // dW_head += dz^T a (contraction over the padded rows)
+  GPT_TRY(launch_gemm_f32out(dt, dzT, pl.Np, aT, pl.Np, V, C, pl.Np, grads + P.head_w(), C, 1, st));
+  if (!post)
+    GPT_TRY(launch_ln_backward(dt, M, C, x, P.at(P.lnf_g()), da, cfg->ln_eps, dx, at<float>(ws, pl.mu),
+                               at<float>(ws, pl.rs), at<float>(ws, pl.lnpart), grads + P.lnf_g(), grads + P.lnf_b(),
+                               st));
+  return GPT_OK;
+}
+
+int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int T, const float* dx0, float* grads,
+                           void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!idx || !dx0 || !grads) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0 || (long long)B * T > (1LL << 24)) return GPT_ERR_SHAPE;
+  if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  const int64_t wpe = (int64_t)cfg->vocab * cfg->n_embd;
+  GPT_TRY(launch_embed_backward(idx, B, T, cfg->n_embd, cfg->vocab, dx0, grads, grads + wpe,
+                                static_cast<hipStream_t>(stream)));
+  return GPT_OK;
 }
 
 int gpt_debug_layernorm(const gpt_config* cfg, const float* x, const void* g, const void* b, int M, void* out,

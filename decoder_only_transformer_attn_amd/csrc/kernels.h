@@ -105,6 +105,22 @@ hipError_t launch_sample(int dtype, const SampleArgs& a, hipStream_t st);
 hipError_t launch_mark_seen(const int32_t* tokens, int B, int T, int V, uint32_t* seen, hipStream_t st);
 // Per-token loss from the head partials, then a deterministic mean.
 int ce_reduce_blocks(int M);
+// Backward of the loss through the head, the final LayerNorm and the embeddings.
+hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V, int C, const float* lse,
+                          const int32_t* y, const float* inv, void* dz, long long ld, hipStream_t st);
+hipError_t launch_gemm_f32out(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+                              float* out, int ldo, int accumulate, hipStream_t st);
+hipError_t launch_bwd_rows(int M, int ntiles, const float* part_max, const float* part_sum, const int32_t* targets,
+                           const int32_t* idx, int T_seq, int V, float* lse, int32_t* yv, float* inv, hipStream_t st);
+hipError_t launch_transpose(int dtype, const void* in, long long ld_in, int R, int Cc, void* out, int Rp,
+                            hipStream_t st);
+hipError_t launch_zero_cols(int dtype, void* p, long long ld, int R, int c0, int c1, hipStream_t st);
+hipError_t launch_cast_rows(int dtype, const float* x, long long n, void* out, hipStream_t st);
+int ln_bwd_chunks(int M);
+hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const void* g, const float* dy, float eps,
+                              float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st);
+hipError_t launch_embed_backward(const int32_t* idx, int B, int T, int C, int V, const float* dx0, float* dwte,
+                                 float* dwpe, hipStream_t st);
 hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,
                             const int32_t* targets, const int32_t* idx, int T_seq, int V, float* token_loss,
                             double* block_sums, float* mean_loss, hipStream_t st);

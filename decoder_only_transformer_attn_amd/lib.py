@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("GPTMI_LIB") or os.path.join(HERE, "libgptmi.so")
 GPT_OK = 0
 STATUS = {0: "GPT_OK", -1: "GPT_ERR_NULL", -2: "GPT_ERR_CONFIG", -3: "GPT_ERR_SEQ_TOO_LONG",
           -4: "GPT_ERR_SHAPE", -5: "GPT_ERR_WORKSPACE", -6: "GPT_ERR_DTYPE", -7: "GPT_ERR_HIP"}
+GPT_ERR_NULL, GPT_ERR_CONFIG, GPT_ERR_SEQ_TOO_LONG, GPT_ERR_SHAPE, GPT_ERR_WORKSPACE = -1, -2, -3, -4, -5
 
 # Every exported function and its ctypes signature.
 _c_int, _c_i64, _vp, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -52,6 +53,9 @@ SIGNATURES = {
     "gpt_decode_step": (_c_int, [_CFG, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _sz, _vp]),
     "gpt_sample": (_c_int, [_CFG, _vp, _c_int, ctypes.POINTER(gpt_sampling), _vp, _vp, _vp, _vp]),
     "gpt_mark_seen": (_c_int, [_CFG, _vp, _c_int, _c_int, _vp, _vp]),
+    "gpt_head_backward_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt_head_backward": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_embedding_backward": (_c_int, [_CFG, _vp, _c_int, _c_int, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -129,6 +133,31 @@ def forward(cfg, params, idx, targets=None, logits=None, token_loss=None, mean_l
     check(load().gpt_forward(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets), _ptr(logits),
                              _ptr(token_loss), _ptr(mean_loss), _ptr(ws), 0 if ws is None else ws.numel(),
                              _stream(stream)))
+
+
+def head_backward_workspace_bytes(cfg, B: int, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().gpt_head_backward_workspace_bytes(ctypes.byref(cfg_c(cfg)), B, T, ctypes.byref(out)))
+    return int(out.value)
+
+
+def head_backward(cfg, params, idx, x, dx, grads, targets=None, mean_loss=None, ws=None, stream=None) -> None:
+    """Enqueue gpt_head_backward: x f32 [B*T, C] (rows the final LayerNorm
+    reads, or the final hidden rows of a post-LN model), dx f32 [B*T, C]
+    (written), grads f32 [param_count] (accumulated), idx / targets int32
+    [B, T], mean_loss f32 [1], ws uint8."""
+    B, T = idx.shape
+    check(load().gpt_head_backward(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets), _ptr(x),
+                                   _ptr(dx), _ptr(grads), _ptr(mean_loss), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(stream)))
+
+
+def embedding_backward(cfg, idx, dx0, grads, stream=None) -> None:
+    """Enqueue gpt_embedding_backward: idx int32 [B, T], dx0 f32 [B*T, C],
+    grads f32 [param_count] (token and position rows accumulated)."""
+    B, T = idx.shape
+    check(load().gpt_embedding_backward(ctypes.byref(cfg_c(cfg)), _ptr(idx), B, T, _ptr(dx0), _ptr(grads),
+                                        _stream(stream)))
 
 
 KERNEL = {"head": 0, "qkv": 1, "attn": 2, "proj": 3, "fc": 4, "fcproj": 5, "ln": 6}

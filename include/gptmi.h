@@ -215,6 +215,57 @@ int gpt_sample(const gpt_config* cfg, const void* logits, int B, const gpt_sampl
  * ignored) in seen (device, uint32 [B][(V + 31) / 32]); bits already set stay. */
 int gpt_mark_seen(const gpt_config* cfg, const int32_t* tokens, int B, int T, uint32_t* seen, void* stream);
 
+/* ---- backward of the loss through the head ----
+ * A training step back-propagates the mean next-token cross-entropy to every
+ * parameter ("预训练一个 Mini GPT（1.24 亿参数）", 训练循环).  The loss
+ * gradient of the logits is (softmax(z) - onehot(y)) / n_valid on rows with a
+ * target and 0 elsewhere (n_valid = number of rows with a target); with a tied
+ * head the token table's gradient is the sum of the head's share and the
+ * lookup's share ("第 25 章 从小 GPT 到 GPT-2" §25.4): gpt_head_backward adds
+ * the first, gpt_embedding_backward the second.
+ *
+ * Gradients are fp32 in a blob laid out like the parameter blob
+ * (gpt_param_offsets, gpt_param_count elements) and are ACCUMULATED (+=):
+ * the caller zeroes the blob at the start of a step.  Products use the
+ * compute dtype (cfg->dtype) with fp32 accumulation; dz is rounded to it
+ * before the two gradient products. */
+
+/* Device workspace bytes of gpt_head_backward for a [B, T] batch (host only).
+ * Requires B * T <= 2^20. */
+int gpt_head_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes);
+
+/* From the rows the final LayerNorm reads (pre-LN models) or the final hidden
+ * rows themselves (post-LN models) to the loss:
+ *   params     (device) parameter blob in cfg->dtype.
+ *   idx        (device) int32 [B, T]: only used to derive targets when
+ *              targets is NULL (same rule as gpt_forward).
+ *   targets    (device, nullable) int32 [B, T]; -1 (or an id outside [0, V))
+ *              = no target.
+ *   x          (device) fp32 [B*T, C] (the residual stream after the last
+ *              block; read only).
+ *   dx         (device) fp32 [B*T, C]: d loss / d x, overwritten.
+ *   grads      (device) fp32 gradient blob: += the head matrix's gradient
+ *              (the token table's head share when tied, head_w when untied)
+ *              and, for pre-LN models, lnf_g / lnf_b.
+ *   mean_loss  (device, nullable) fp32 [1]: the loss itself (as gpt_forward).
+ *   ws         (device) at least gpt_head_backward_workspace_bytes.
+ * The logits are recomputed twice (row log-sum-exp, then dz from fp32
+ * accumulators) and never stored.  Requires 1 <= T <= ctx, B * T <= 2^20.
+ * No position with a target: every gradient added is 0 (mean_loss NaN). */
+int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                      const int32_t* targets, const float* x, float* dx, float* grads, float* mean_loss, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Embedding backward, x0[b, t] = wte[idx[b, t]] + wpe[t]:
+ *   grads[wte row v] += sum of dx0 over the positions holding v (position
+ *   order), grads[wpe row t] += sum over the batch of dx0[:, t].
+ *   idx  (device) int32 [B, T]; a position holding an id outside [0, V)
+ *        adds nothing to the token table (its position row still gets dx0).
+ *   dx0  (device) fp32 [B*T, C]: d loss / d x0.
+ * Requires 1 <= T <= ctx, B * T <= 2^24.  No workspace. */
+int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int T, const float* dx0, float* grads,
+                           void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* gpt_status_string(int status);
 

@@ -166,3 +166,27 @@ def test_variant_flags_are_validated():
     import dataclasses as dc
     for bad in (dict(act=2), dict(post_ln=-1), dict(untied=3)):
         assert lib.load().gpt_param_count(ctypes.byref(lib.cfg_c(dc.replace(synth.MICRO, **bad)))) == -2
+
+
+def test_backward_validation_and_workspace():
+    L = lib.load()
+    cfg = synth.MICRO
+    c = ctypes.byref(lib.cfg_c(cfg))
+    w1 = lib.head_backward_workspace_bytes(cfg, 2, 5)
+    w2 = lib.head_backward_workspace_bytes(cfg, 4, 10)
+    assert 0 < w1 < w2
+
+    def hb(params=1, idx=1, B=2, T=5, x=1, dx=1, grads=1, ws=1, ws_bytes=1 << 40):
+        return L.gpt_head_backward(c, params, idx, B, T, None, x, dx, grads, None, ws, ws_bytes, None)
+
+    for kw in (dict(params=None), dict(idx=None), dict(x=None), dict(dx=None), dict(grads=None), dict(ws=None)):
+        assert hb(**kw) == lib.GPT_ERR_NULL, kw
+    assert hb(B=0) == lib.GPT_ERR_SHAPE and hb(T=0) == lib.GPT_ERR_SHAPE
+    assert hb(B=(1 << 20) // cfg.ctx + 1, T=cfg.ctx) == lib.GPT_ERR_SHAPE    # more than 2^20 rows
+    assert hb(T=cfg.ctx + 1) == lib.GPT_ERR_SEQ_TOO_LONG
+    assert hb(ws_bytes=w1 - 1) == lib.GPT_ERR_WORKSPACE
+    eb = L.gpt_embedding_backward
+    assert eb(c, None, 2, 5, 1, 1, None) == lib.GPT_ERR_NULL and eb(c, 1, 2, 5, None, 1, None) == lib.GPT_ERR_NULL
+    assert eb(c, 1, 2, 5, 1, None, None) == lib.GPT_ERR_NULL
+    assert eb(c, 1, 0, 5, 1, 1, None) == lib.GPT_ERR_SHAPE
+    assert eb(c, 1, 2, cfg.ctx + 1, 1, 1, None) == lib.GPT_ERR_SEQ_TOO_LONG
