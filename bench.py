@@ -224,9 +224,41 @@ def bench_forward(args, w):
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(head_ms, 4), "flops_per_launch": head_flops},
     }
+    if args.workload == 3:
+        out["head_backward"] = bench_head_backward(cfg, B, T, dev_params, idx, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_forward(cfg, params, ids, args.cpu_seqs)
     return out
+
+
+def bench_head_backward(cfg, B, T, dev_params, idx, stream, reps=10):
+    """gpt_head_backward (loss + gradients of the final hidden rows, the tied
+    head and ln_f) on synthetic residual rows of the forward's shape.
+    Algorithmic work 6 M V C flops: the logits, dz W and dz^T a (the kernels
+    run the logits product twice: 8 M V C)."""
+    import torch
+    from decoder_only_transformer_attn_amd import lib
+    M, V, C = B * T, cfg.vocab, cfg.n_embd
+    g = torch.Generator(device="cuda").manual_seed(1)
+    x = torch.randn((M, C), generator=g, device="cuda", dtype=torch.float32)
+    dx = torch.empty_like(x)
+    grads = torch.zeros(lib.param_count(cfg), dtype=torch.float32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lib.head_backward_workspace_bytes(cfg, B, T), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        lib.head_backward(cfg, dev_params, idx, x, dx, grads, None, loss, ws, stream)
+    torch.cuda.synchronize()
+    ev = Events(2)
+    ev.record(0, stream.cuda_stream)
+    for _ in range(reps):
+        lib.head_backward(cfg, dev_params, idx, x, dx, grads, None, loss, ws, stream)
+    ev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / reps
+    ev.close()
+    alg = 6 * M * V * C
+    return {"ms": round(ms, 4), "algorithmic_flops": alg, "tflops": round(alg / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "loss": round(float(loss.item()), 5)}
 
 
 def bench_decode(args, w):

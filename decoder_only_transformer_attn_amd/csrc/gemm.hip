@@ -499,45 +499,96 @@ struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all 
   }
 };
 
+// An epilogue with kRaw takes the wave's whole accumulator tile (raw<TM, TN>)
+// instead of the paired-column driver below.
+template <typename E, typename = void>
+struct IsRaw { static constexpr bool value = false; };
+template <typename E>
+struct IsRaw<E, std::void_t<decltype(E::kRaw)>> { static constexpr bool value = E::kRaw; };
+
 // Loss gradient of the head's logits: dz[m, n] = (exp(v - lse[m]) - [n == y[m]])
 // * s[m], s = 1 / (number of rows with a target) for a row with one, else 0.
+// Written twice: row-major dz [M, ld] and transposed dzT [N, ldT] (tokens
+// contiguous), the operands of the two gradient products.  In the MFMA
+// accumulator a lane holds four consecutive rows (tokens) of one column, so
+// the transposed copy is one 4-element store per register quad; the row-major
+// copy pairs adjacent columns with the neighbouring lane.
 template <typename T>
 struct EpiDz {
   static constexpr bool kPreload = false;
   static constexpr bool kCompact = true;
-  struct Row { float lse, s; int y; };
+  static constexpr bool kRaw = true;
+  typedef int Row;
   typedef int Col;
   typedef int ColX;
   const float* lse;      // [M]
   const int32_t* y;      // [M] target of each row, -1 for none
   const float* inv;      // [1] 1 / n_valid (0 when no row has a target)
   T* dz;
-  long long ld;
-  int M;
-  __device__ __forceinline__ Row row(int m) const {
-    if (m >= M) return Row{0.f, 0.f, -1};   // (rows past M are never stored)
-    const int yy = y[m];
-    return Row{lse[m], yy >= 0 ? *inv : 0.f, yy};
-  }
+  long long ld;          // even
+  T* dzT;
+  long long ldT;         // multiple of 4
+  __device__ __forceinline__ Row row(int) const { return 0; }
   __device__ __forceinline__ Col col(int, bool) const { return 0; }
   __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
-  __device__ __forceinline__ float2 value(const Row& r, int n, float a, float b) const {
+
+  template <int TM, int TN>
+  __device__ __forceinline__ void raw(const f32x16 (&acc)[TM][TN], int mbase, int nbase, int M, int N) const {
     constexpr float LOG2E = 1.4426950408889634f;
-    a = (fast_exp2((a - r.lse) * LOG2E) - (n == r.y ? 1.f : 0.f)) * r.s;
-    b = (fast_exp2((b - r.lse) * LOG2E) - (n + 1 == r.y ? 1.f : 0.f)) * r.s;
-    return make_float2(a, b);
-  }
-  __device__ __forceinline__ void pair(const Row& r, int m, int n, float a, float b, bool has_b, ColX, float2) const {
-    const float2 v = value(r, n, a, b);
-    store_pair(dz + (long long)m * ld + n, v.x, v.y, has_b, (ld & 1) == 0);
-  }
-  __device__ __forceinline__ bool vec_ok() const { return (ld & 1) == 0; }
-  __device__ __forceinline__ void pair_in(const Row& r, int m, int n, float a, float b, ColX, float2) const {
-    const float2 v = value(r, n, a, b);
-    T* p = dz + (long long)m * ld + n;
-    if constexpr (sizeof(T) == 4) *reinterpret_cast<float2*>(p) = v;
-    else *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v.x, v.y);
+    const int lane = threadIdx.x & 63;
+    const bool odd = lane & 1;
+    const float iv = *inv;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = mbase + i * 32 + q * 8 + (lane >> 5) * 4;   // rows m0 .. m0 + 3 (acc_row of 4q + e)
+        float l4[4], s4[4];
+        int y4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + e;
+          const int yy = m < M ? y[m] : -1;
+          l4[e] = m < M ? lse[m] : 0.f;
+          s4[e] = yy >= 0 ? iv : 0.f;
+          y4[e] = yy;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = nbase + j * 32 + (lane & 31);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (fast_exp2((acc[i][j][4 * q + e] - l4[e]) * LOG2E) - (n == y4[e] ? 1.f : 0.f)) * s4[e];
+          // row-major: lanes 2k, 2k+1 hold columns n, n+1; after one exchange
+          // per row pair the even lane stores row m0+e and the odd lane row
+          // m0+e+1, both at columns (n_even, n_even + 1)
+          const int ne = n & ~1;
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float recv = __shfl_xor(odd ? v[e] : v[e + 1], 1, 64);
+            const int m = m0 + e + (odd ? 1 : 0);
+            const float a = odd ? recv : v[e], b = odd ? v[e + 1] : recv;
+            if (m < M && ne < N) store_pair(dz + (long long)m * ld + ne, a, b, ne + 1 < N, true);
+          }
+          if (n < N) {
+            T* p = dzT + (long long)n * ldT + m0;
+            if (m0 + 3 < M) {
+              if constexpr (sizeof(T) == 4) {
+                *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+              } else {
+                const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                *reinterpret_cast<uint2*>(p) = w;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (m0 + e < M) p[e] = from_f32<T>(v[e]);
+            }
+          }
+        }
+      }
   }
 };
 
@@ -680,7 +731,8 @@ gemm_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, 
   preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
   gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
-  epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  if constexpr (IsRaw<Epi>::value) epi.template raw<G::TM, G::TN>(acc, mb, nb, M, N);
+  else epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
 }
 
 // bf16 GEMM through the pipelined main loop, element-wise epilogue.
@@ -719,7 +771,8 @@ gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, i
   preload_pairs<D::TM, D::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[D::TM][D::TN];
   dma_mainloop<BM, BN, WM, WN, K, NST, BK>(A, W, M, N, m0, n0, stages, acc);
-  epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  if constexpr (IsRaw<Epi>::value) epi.template raw<D::TM, D::TN>(acc, mb, nb, M, N);
+  else epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1413,12 +1466,13 @@ hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyW
 
 // Loss gradient of the logits A W^T ([M, C] x [V, C]^T) into dz [M, V] (ld).
 hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V, int C, const float* lse,
-                          const int32_t* y, const float* inv, void* dz, long long ld, hipStream_t st) {
+                          const int32_t* y, const float* inv, void* dz, long long ld, void* dzT, long long ldT,
+                          hipStream_t st) {
   if (dtype == 0)
     return dispatch_gemm_tiled((const float*)A, C, (const float*)W, C, M, V, C,
-                               EpiDz<float>{lse, y, inv, (float*)dz, ld, M}, st);
-  return dispatch_gemm_tiled((const bf16*)A, C, (const bf16*)W, C, M, V, C, EpiDz<bf16>{lse, y, inv, (bf16*)dz, ld, M},
-                             st);
+                               EpiDz<float>{lse, y, inv, (float*)dz, ld, (float*)dzT, ldT}, st);
+  return dispatch_gemm_tiled((const bf16*)A, C, (const bf16*)W, C, M, V, C,
+                             EpiDz<bf16>{lse, y, inv, (bf16*)dz, ld, (bf16*)dzT, ldT}, st);
 }
 
 // out [M, N] fp32 (=, or += with accumulate) A [M, K] . W [N, K]^T

@@ -573,16 +573,17 @@ int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* 
   GPT_TRY(launch_bwd_rows(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), targets, idx, T, V,
                           at<float>(ws, pl.lse), at<int32_t>(ws, pl.yv), at<float>(ws, pl.inv), st));
   // dz = (softmax - onehot) / n_valid, recomputed from the fp32 accumulators of a second head product
+  // (written in both layouts: dz [M, Vp] and dzT [V, Np]; the pads are zeroed)
   void* dz = at<char>(ws, pl.dz);
+  void* dzT = at<char>(ws, pl.dzT);
   GPT_TRY(launch_head_dz(dt, a, Wh, M, V, C, at<float>(ws, pl.lse), at<int32_t>(ws, pl.yv), at<float>(ws, pl.inv),
-                         dz, pl.Vp, st));
+                         dz, pl.Vp, dzT, pl.Np, st));
   GPT_TRY(launch_zero_cols(dt, dz, pl.Vp, M, V, pl.Vp, st));
+  GPT_TRY(launch_zero_cols(dt, dzT, pl.Np, V, M, pl.Np, st));
   void* ET = at<char>(ws, pl.ET);
   void* aT = at<char>(ws, pl.aT);
-  void* dzT = at<char>(ws, pl.dzT);
   GPT_TRY(launch_transpose(dt, Wh, C, V, C, ET, pl.Vp, st));
   GPT_TRY(launch_transpose(dt, a, C, M, C, aT, pl.Np, st));
-  GPT_TRY(launch_transpose(dt, dz, pl.Vp, M, V, dzT, pl.Np, st));
   // da = dz W_head (contraction over the padded vocabulary); post-LN: that is dx
   float* da = post ? dx : at<float>(ws, pl.da);
   GPT_TRY(launch_gemm_f32out(dt, dz, pl.Vp, ET, pl.Vp, M, C, pl.Vp, da, C, 0, st));

@@ -107,7 +107,8 @@ hipError_t launch_mark_seen(const int32_t* tokens, int B, int T, int V, uint32_t
 int ce_reduce_blocks(int M);
 // Backward of the loss through the head, the final LayerNorm and the embeddings.
 hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V, int C, const float* lse,
-                          const int32_t* y, const float* inv, void* dz, long long ld, hipStream_t st);
+                          const int32_t* y, const float* inv, void* dz, long long ld, void* dzT, long long ldT,
+                          hipStream_t st);
 hipError_t launch_gemm_f32out(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                               float* out, int ldo, int accumulate, hipStream_t st);
 hipError_t launch_bwd_rows(int M, int ntiles, const float* part_max, const float* part_sum, const int32_t* targets,
