@@ -47,10 +47,17 @@ class GPTConfig:
     act: int = 0      # 0 = tanh GELU (GPT-2), 1 = exact erf GELU
     post_ln: int = 0  # 0 = pre-LN blocks + ln_f (GPT-2), 1 = post-LN blocks, no ln_f (GPT-1)
     untied: int = 0   # 0 = head tied to the token table, 1 = separate head matrix [V, C]
+    arch: int = 0     # 0 = GPT-2 blocks, 1 = LLaMA-style blocks (RMSNorm, RoPE, SwiGLU, GQA, no biases)
+    n_kv_head: int = 0  # LLaMA: K/V heads shared by groups of query heads (0 = n_head)
+    rope_theta: float = 10000.0
 
     @property
     def head_dim(self) -> int:
         return self.n_embd // self.n_head
+
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_head or self.n_head
 
 
 # Named workloads.  Ids: 1 micro fp32, 2 MiniGPT fp32, 3 GPT-2 124M bf16
@@ -72,8 +79,17 @@ LAYER_FIELDS = ("ln1_g", "ln1_b", "attn_w", "attn_b", "proj_w", "proj_b",
                 "ln2_g", "ln2_b", "fc_w", "fc_b", "fcproj_w", "fcproj_b")
 
 
+LLAMA_FIELDS = ("rms1_g", "wqkv_w", "wo_w", "rms2_g", "w13_w", "w2_w")
+
+
 def layer_shapes(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...]]]:
     C, F = cfg.n_embd, cfg.n_ff
+    if cfg.arch == 1:
+        # wqkv: rows of W_q (H*D), then W_k and W_v (Hkv*D each); w13: rows
+        # interleaved, 2j = gate (W1) row j, 2j+1 = up (W3) row j
+        D = cfg.head_dim
+        return [("rms1_g", (C,)), ("wqkv_w", ((cfg.n_head + 2 * cfg.kv_heads) * D, C)), ("wo_w", (C, C)),
+                ("rms2_g", (C,)), ("w13_w", (2 * F, C)), ("w2_w", (C, F))]
     return [("ln1_g", (C,)), ("ln1_b", (C,)), ("attn_w", (3 * C, C)), ("attn_b", (3 * C,)),
             ("proj_w", (C, C)), ("proj_b", (C,)), ("ln2_g", (C,)), ("ln2_b", (C,)),
             ("fc_w", (F, C)), ("fc_b", (F,)), ("fcproj_w", (C, F)), ("fcproj_b", (C,))]
@@ -90,11 +106,14 @@ def blob_layout(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...], int]]:
         off += int(np.prod(shape))
 
     add("wte", (cfg.vocab, cfg.n_embd))
-    add("wpe", (cfg.ctx, cfg.n_embd))
+    if cfg.arch == 0:
+        add("wpe", (cfg.ctx, cfg.n_embd))
     for l in range(cfg.n_layer):
         for name, shape in layer_shapes(cfg):
             add(f"h{l}.{name}", shape)
-    if not cfg.post_ln:
+    if cfg.arch == 1:
+        add("rmsf_g", (cfg.n_embd,))
+    elif not cfg.post_ln:
         add("lnf_g", (cfg.n_embd,))
         add("lnf_b", (cfg.n_embd,))
     if cfg.untied:
@@ -172,6 +191,14 @@ def unpack_f64(cfg: GPTConfig, params: Dict[str, np.ndarray]) -> dict:
     """Nested float64 view for the oracle: {'wte','wpe','layers':[{...}], 'lnf_g','lnf_b'}
     (no ln_f for post-LN configurations, 'head_w' for an untied head), plus the
     variant names 'act' ('tanh' or 'erf') and 'norm' ('pre' or 'post')."""
+    if cfg.arch == 1:
+        out = {"arch": "llama", "wte": params["wte"].astype(np.float64), "rmsf_g": params["rmsf_g"].astype(np.float64),
+               "n_kv_head": cfg.kv_heads, "rope_theta": float(cfg.rope_theta), "layers": []}
+        if cfg.untied:
+            out["head_w"] = params["head_w"].astype(np.float64)
+        for l in range(cfg.n_layer):
+            out["layers"].append({f: params[f"h{l}.{f}"].astype(np.float64) for f in LLAMA_FIELDS})
+        return out
     out = {"wte": params["wte"].astype(np.float64), "wpe": params["wpe"].astype(np.float64),
            "layers": [], "act": "erf" if cfg.act else "tanh", "norm": "post" if cfg.post_ln else "pre"}
     if not cfg.post_ln:

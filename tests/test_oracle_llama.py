@@ -1,0 +1,223 @@
+"""Pins of the LLaMA-style oracle (oracle/llama_oracle.py).
+
+* RoPE: closed-form values (one pair rotates to (cos m, sin m); the second
+  pair of D = 4 turns by m / 100), the identity at position 0, norm
+  preservation, and the page's property that the rotated dot product depends
+  only on m - n; a torch composition in complex numbers (q * e^{i m theta});
+* RMSNorm against torch's rms_norm (fp64) and its unit-rms closed form;
+  SiLU against torch's silu and sigma(0) = 1/2;
+* GQA against torch's scaled_dot_product_attention with enable_gqa (fp64),
+  Hkv = H reducing to the GPT-2 oracle's per-head attention;
+* the whole block against a torch fp64 composition of its steps;
+* parameter counts: LLaMA-7B 6.7B and LLaMA-13B 13B of the page's table
+  (vocabulary 32000, untied head: the pages give neither, a reading);
+* greedy decoding with caches equals recomputation;
+* planted mistakes.
+"""
+import dataclasses as dc
+import math
+
+import numpy as np
+import pytest
+
+from decoder_only_transformer_attn_amd import synth
+from oracle import gpt_oracle as O
+from oracle import llama_oracle as L
+
+CFG = synth.GPTConfig(vocab=41, ctx=16, n_embd=32, n_head=4, n_layer=2, n_ff=48, arch=1, n_kv_head=2)
+
+
+def _P(cfg=CFG, seed=0):
+    return synth.unpack_f64(cfg, synth.make_params(cfg, seed=seed, cfg_id=51, init="stress"))
+
+
+def test_rope_closed_forms():
+    for m in (0, 1, 3, 7):
+        out = L.rope(np.array([[1.0, 0.0]]), np.array([m]), 10000.0)
+        np.testing.assert_allclose(out[0], [math.cos(m), math.sin(m)], atol=1e-15)
+    # D = 4: the second pair turns by m * 10000^(-2/4) = m / 100
+    x = np.array([[0.0, 0.0, 0.0, 1.0]])
+    out = L.rope(x, np.array([5]), 10000.0)[0]
+    np.testing.assert_allclose(out, [0.0, 0.0, -math.sin(0.05), math.cos(0.05)], atol=1e-15)
+    rng = np.random.default_rng(0)
+    q = rng.normal(size=(6, 16))
+    np.testing.assert_array_equal(L.rope(q, np.zeros(6), 10000.0), q)
+    r = L.rope(q, np.arange(6) * 3, 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(r.reshape(6, 8, 2), axis=-1), np.linalg.norm(q.reshape(6, 8, 2), axis=-1))
+
+
+def test_rope_dot_product_depends_on_relative_position_only():
+    rng = np.random.default_rng(1)
+    q, k = rng.normal(size=(1, 64)), rng.normal(size=(1, 64))
+    ref = (L.rope(q, [7], 1e4) @ L.rope(k, [3], 1e4).T).item()
+    for s in (1, 10, 250):
+        got = (L.rope(q, [7 + s], 1e4) @ L.rope(k, [3 + s], 1e4).T).item()
+        assert abs(got - ref) < 1e-12
+    assert abs((L.rope(q, [8], 1e4) @ L.rope(k, [3], 1e4).T).item() - ref) > 1e-3
+
+
+def test_rope_matches_complex_rotation_in_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(2)
+    x = rng.normal(size=(3, 9, 32))
+    pos = np.arange(9) + 4
+    xc = torch.view_as_complex(torch.from_numpy(x).reshape(3, 9, 16, 2).contiguous())
+    freq = 10000.0 ** (-torch.arange(0, 32, 2, dtype=torch.float64) / 32)
+    rot = torch.polar(torch.ones(9, 16, dtype=torch.float64), torch.from_numpy(pos).double()[:, None] * freq)
+    ref = torch.view_as_real(xc * rot).reshape(3, 9, 32).numpy()
+    np.testing.assert_allclose(L.rope(x, pos, 10000.0), ref, atol=1e-13)
+
+
+def test_rms_norm_and_silu():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 3, (5, 24))
+    g = rng.normal(1, 0.2, 24)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (24,), torch.from_numpy(g), 1e-5).numpy()
+    np.testing.assert_allclose(L.rms_norm(x, g), ref, rtol=1e-13)
+    y = L.rms_norm(x, np.ones(24), 0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(-1)), 1.0, rtol=1e-14)
+    # no mean centring: a constant row stays constant (LayerNorm would zero it)
+    np.testing.assert_allclose(L.rms_norm(np.full((1, 8), 2.0), np.ones(8), 0.0), 1.0)
+    z = rng.normal(0, 4, 100)
+    np.testing.assert_allclose(L.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(), rtol=1e-14)
+    assert L.silu(np.array([0.0]))[0] == 0.0 and abs(L.silu(np.array([1.0]))[0] - 1 / (1 + math.exp(-1))) < 1e-16
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 2), (4, 1), (6, 3)])
+def test_gqa_matches_torch_sdpa(H, Hkv):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(H * 10 + Hkv)
+    q = rng.normal(size=(2, H, 7, 8))
+    k, v = rng.normal(size=(2, Hkv, 7, 8)), rng.normal(size=(2, Hkv, 7, 8))
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                                           torch.from_numpy(v), is_causal=True,
+                                                           enable_gqa=True).numpy()
+    np.testing.assert_allclose(L.gqa_attention(q, k, v), ref, atol=1e-13)
+    if H == Hkv:
+        for h in range(H):
+            np.testing.assert_allclose(L.gqa_attention(q, k, v)[0, h], O.causal_attention(q[0, h], k[0, h], v[0, h]),
+                                       atol=1e-14)
+
+
+def test_block_matches_torch_composition():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    P = _P()
+    lp = {k: torch.from_numpy(v) for k, v in P["layers"][0].items()}
+    rng = np.random.default_rng(4)
+    B, T, C, H, Hkv = 2, 9, 32, 4, 2
+    D = C // H
+    x = rng.normal(0, 1, (B, T, C))
+    xt = torch.from_numpy(x)
+
+    def rot(t, pos):   # complex-number rotation of adjacent pairs
+        tc = torch.view_as_complex(t.reshape(*t.shape[:-1], D // 2, 2).contiguous())
+        freq = 10000.0 ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+        return torch.view_as_real(tc * torch.polar(torch.ones(T, D // 2, dtype=torch.float64),
+                                                    pos[:, None] * freq)).reshape(t.shape)
+
+    a = F.rms_norm(xt, (C,), lp["rms1_g"], 1e-5)
+    Wq, Wk, Wv = lp["wqkv_w"][:H * D], lp["wqkv_w"][H * D:(H + Hkv) * D], lp["wqkv_w"][(H + Hkv) * D:]
+    q = F.linear(a, Wq).view(B, T, H, D).transpose(1, 2)
+    k = F.linear(a, Wk).view(B, T, Hkv, D).transpose(1, 2)
+    v = F.linear(a, Wv).view(B, T, Hkv, D).transpose(1, 2)
+    pos = torch.arange(T, dtype=torch.float64)
+    y = F.scaled_dot_product_attention(rot(q, pos), rot(k, pos), v, is_causal=True, enable_gqa=True)
+    x1 = xt + F.linear(y.transpose(1, 2).reshape(B, T, C), lp["wo_w"])
+    b2 = F.rms_norm(x1, (C,), lp["rms2_g"], 1e-5)
+    ref = x1 + F.linear(F.silu(F.linear(b2, lp["w13_w"][0::2])) * F.linear(b2, lp["w13_w"][1::2]), lp["w2_w"])
+    np.testing.assert_allclose(L.block(x, P["layers"][0], H, Hkv, 10000.0, 1e-5), ref.numpy(), atol=1e-12)
+
+
+def test_param_counts():
+    cfg = dc.replace(CFG, untied=1)
+    assert L.param_count(cfg.vocab, cfg.n_embd, cfg.n_layer, cfg.n_head, cfg.kv_heads, cfg.n_ff, True) == \
+        synth.blob_numel(cfg)
+    assert L.param_count(CFG.vocab, CFG.n_embd, CFG.n_layer, CFG.n_head, CFG.kv_heads, CFG.n_ff) == \
+        synth.blob_numel(CFG)
+    # the page's table (6.3): LLaMA-7B 6.7B, LLaMA-13B 13B
+    assert round(L.param_count(32000, 4096, 32, 32, 32, 11008, True) / 1e9, 1) == 6.7
+    assert round(L.param_count(32000, 5120, 40, 40, 40, 13824, True) / 1e9) == 13
+    # GQA shrinks only W_k and W_v: 8 K/V heads of 64 save 2 C (H - 8) D per block
+    full = L.param_count(32000, 4096, 32, 32, 32, 11008, True)
+    gqa = L.param_count(32000, 4096, 32, 32, 8, 11008, True)
+    assert full - gqa == 32 * 2 * 4096 * 24 * 128
+
+
+@pytest.mark.parametrize("Hkv,untied", [(2, 0), (1, 1), (4, 0)])
+def test_cached_decode_equals_recompute(Hkv, untied):
+    cfg = dc.replace(CFG, n_kv_head=Hkv, untied=untied)
+    P = _P(cfg, seed=Hkv)
+    prompt = synth.make_ids(cfg, 2, 5, seed=9)
+    t1, z1 = L.greedy_recompute(P, prompt, 6, cfg.n_head)
+    t2, z2 = L.greedy_cached(P, prompt, 6, cfg.n_head)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_allclose(z1, z2, rtol=1e-11, atol=1e-11)
+
+
+def test_forward_loss_is_the_gpt2_loss_rule():
+    P = _P()
+    idx = synth.make_ids(CFG, 2, 8, seed=3)
+    lg, tok, mean = L.forward(P, idx, CFG.n_head)
+    y = O.derived_targets(idx)
+    np.testing.assert_allclose(tok.reshape(-1), O.cross_entropy_rows(lg.reshape(16, -1), y.reshape(-1)))
+    assert abs(mean - tok[:, :-1].mean()) < 1e-14
+    # causal: the first positions ignore later tokens
+    idx2 = idx.copy()
+    idx2[:, 5:] = (idx2[:, 5:] + 1) % CFG.vocab
+    lg2, _, _ = L.forward(P, idx2, CFG.n_head)
+    np.testing.assert_allclose(lg2[:, :5], lg[:, :5], atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# planted mistakes
+# --------------------------------------------------------------------------
+def _pins_pass():
+    try:
+        test_rope_closed_forms()
+        test_rope_dot_product_depends_on_relative_position_only()
+        test_rms_norm_and_silu()
+        for h, g in ((4, 2), (4, 1)):
+            test_gqa_matches_torch_sdpa(h, g)
+        test_block_matches_torch_composition()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    pytest.importorskip("torch")
+    assert _pins_pass()
+    orig_rope, orig_attn = L.rope, L.gqa_attention
+
+    def rope_wrong_direction(x, pos, theta=10000.0):
+        return orig_rope(x, -np.asarray(pos, dtype=np.float64), theta)
+
+    def rope_wrong_exponent(x, pos, theta=10000.0):
+        D = x.shape[-1]
+        return orig_rope(x, pos, theta ** 0.5) if D > 2 else orig_rope(x, pos, theta)
+
+    def rms_centred(x, g, eps=1e-5):
+        xc = x - x.mean(axis=-1, keepdims=True)
+        return g * xc / np.sqrt((xc * xc).mean(axis=-1, keepdims=True) + eps)
+
+    def silu_sigmoid_only(z):
+        return 1.0 / (1.0 + np.exp(-z))
+
+    def swiglu_gate_on_up(a, w13, w2):
+        return (L.silu(a @ w13[1::2].T) * (a @ w13[0::2].T)) @ w2.T
+
+    def gqa_modulo(q, k, v):
+        B, H, T, D = q.shape
+        Hkv = k.shape[1]
+        kk = np.stack([k[:, h % Hkv] for h in range(H)], 1)
+        vv = np.stack([v[:, h % Hkv] for h in range(H)], 1)
+        return orig_attn(q, kk, vv)
+
+    mutants = [("rope", rope_wrong_direction), ("rope", rope_wrong_exponent), ("rms_norm", rms_centred),
+               ("silu", silu_sigmoid_only), ("swiglu_mlp", swiglu_gate_on_up), ("gqa_attention", gqa_modulo)]
+    for name, fn in mutants:
+        with monkeypatch.context() as m:
+            m.setattr(L, name, fn)
+            assert not _pins_pass(), f"planted mistake {fn.__name__} went unnoticed"
