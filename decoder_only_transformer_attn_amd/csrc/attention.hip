@@ -95,9 +95,11 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   const int qcol = qw0 + (lane & 31);
   const int T_seq = a.T_seq, D = a.D;
 
+  // grouped-query attention: query head h reads K/U head h / (H / Hkv)
+  const int kvbh = b * a.Hkv + h / (a.H / a.Hkv);
   const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * a.q_bh;
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * a.k_bh;
-  const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.v_bh;
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)kvbh * a.k_bh;
+  const T* U = reinterpret_cast<const T*>(a.v) + (long long)kvbh * a.v_bh;
 
   // Q^T fragments (B operand) for this lane's query column.
   typename MF::frag qf[NDI];
@@ -348,8 +350,9 @@ __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a)
   for (int e = 0; e < VEC; ++e) qv[e] = act ? qs[c * VEC + e] : 0.f;
   int n = *a.pos + 1;
   n = n < 1 ? 1 : (n < a.Tmax ? n : a.Tmax);   // a position outside [0, Tmax) violates the contract
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * a.kv_bh + c * VEC;
-  const T* U = reinterpret_cast<const T*>(a.v) + (long long)bh * a.kv_bh + c * VEC;
+  const int kvbh = b * a.Hkv + h / (a.H / a.Hkv);   // grouped-query attention
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)kvbh * a.kv_bh + c * VEC;
+  const T* U = reinterpret_cast<const T*>(a.v) + (long long)kvbh * a.kv_bh + c * VEC;
   const uint4 z = make_uint4(0, 0, 0, 0);
 
   float m = -INFINITY, l = 0.f, acc[VEC];
@@ -439,6 +442,23 @@ hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t 
       default: hipLaunchKernelGGL((attn_decode_kernel<bf16, 16>), grid, block, 0, st, a); break;
     }
   }
+  return hipGetLastError();
+}
+
+// Rotary angles ("02 GPT 架构" §5.2): tab[p * D/2 + i] = (cos, sin) of
+// p * theta^(-2i/D), computed in double and rounded once to float.
+__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tab, int rows, int half, int D,
+                                                         double theta) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= rows * half) return;
+  const int p = e / half, i = e - p * half;
+  const double ang = (double)p * pow(theta, -2.0 * i / (double)D);
+  tab[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+hipError_t launch_rope_table(float2* tab, int rows, int D, double theta, hipStream_t st) {
+  const int n = rows * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, tab, rows, D / 2, D, theta);
   return hipGetLastError();
 }
 

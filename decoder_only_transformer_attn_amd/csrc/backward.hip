@@ -315,7 +315,7 @@ hipError_t launch_embed_backward(const int32_t* idx, int B, int T, int C, int V,
                                  float* dwpe, hipStream_t st) {
   const int N = B * T;
   hipLaunchKernelGGL(embed_bwd_tok_kernel, dim3(N), dim3(256), 0, st, idx, N, C, V, dx0, dwte);
-  hipLaunchKernelGGL(embed_bwd_pos_kernel, dim3(T, (C + 255) / 256), dim3(256), 0, st, B, T, C, dx0, dwpe);
+  if (dwpe) hipLaunchKernelGGL(embed_bwd_pos_kernel, dim3(T, (C + 255) / 256), dim3(256), 0, st, B, T, C, dx0, dwpe);
   return hipGetLastError();
 }
 

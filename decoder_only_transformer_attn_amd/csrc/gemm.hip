@@ -426,6 +426,7 @@ struct EpiResid {  // x[m, n] += v + bias[n]   (fp32 residual stream)
   float* x;
   int ldx;
   __device__ __forceinline__ Col col(int n, bool has_b) const {
+    if (!bias) return Col{0u, 0u};   // no bias
     return Col{Col::bits(bias[n]), Col::bits(bias[has_b ? n + 1 : n])};
   }
   __device__ __forceinline__ float2 preload(int m, int n, bool has_b) const {
@@ -454,48 +455,88 @@ __device__ __forceinline__ int div_small(int m, int d, float inv_d) {
 }
 
 template <typename T>
-struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; all three [B,H,T,D]
+struct EpiQKV {  // + bias, split Q|K|U, heads as column blocks of width D; Q [B,H,T,D], K/U [B,Hkv,Tk,D]
   static constexpr bool kPreload = false;
   static constexpr bool kCompact = true;
-  const T* bias;
+  const T* bias;                    // nullable
   int C, H, D, T_seq;
   float inv_T;
   T* q; long long q_bh;             // q[(b*H+h)*q_bh + t*D + d]
-  T* k; long long k_bh;             // k[(b*H+h)*k_bh + tc*D + d]
-  T* v; long long v_bh;             // v[(b*H+h)*v_bh + tc*D + d]
+  T* k; long long k_bh;             // k[(b*Hkv+h)*k_bh + tc*D + d]
+  T* v; long long v_bh;             // v[(b*Hkv+h)*v_bh + tc*D + d]
   const int32_t* pos;               // nullable: tc = t + *pos (cache append)
   int Tk;                           // K/U rows; cache positions >= Tk are not written
+  int Hkv;
+  const float2* rope;               // nullable: rotate the (2i, 2i+1) pairs of Q and K by position tc
   struct Row { int b, t, tc; };
   typedef RawPair<T> Col;   // held across the main loop: the bias pair only
-  struct ColX { RawPair<T> bias; T* base; int b_stride; bool is_q; };   // b_stride = H * rows * D < 2^31
+  struct ColX { RawPair<T> bias; T* base; int b_stride; bool is_q; bool rot; int pair; };   // b_stride < 2^31
   __device__ __forceinline__ Row row(int m) const {
     const int bb = div_small(m, T_seq, inv_T), t = m - bb * T_seq;
     return Row{bb, t, t + (pos ? *pos : 0)};
   }
   __device__ __forceinline__ Col col(int n, bool) const {
+    if (!bias) return Col{0u, 0u};
     return Col{RawPair<T>::bits(bias[n]), RawPair<T>::bits(bias[n + 1])};
   }
   // Column n (even) -> projection, head and head column, worked out once per
   // column tile when the epilogue starts; D is even, so n and n + 1 fall in
-  // the same head of the same projection.
+  // the same head of the same projection (and form one rotary pair).
   __device__ __forceinline__ ColX colx(int n, const Col& bs) const {
-    const int which = n / C;
-    const int c = n - which * C;
+    const int kvd = Hkv * D;
+    const int which = n < C ? 0 : (n < C + kvd ? 1 : 2);
+    const int c = n - (which == 0 ? 0 : (which == 1 ? C : C + kvd));
     const int h = c / D, d = c - h * D;
     const long long st = which == 0 ? q_bh : (which == 1 ? k_bh : v_bh);
     T* arr = which == 0 ? q : (which == 1 ? k : v);
-    return ColX{bs, arr + h * st + d, (int)(st * H), which == 0};
+    return ColX{bs, arr + h * st + d, (int)(st * (which == 0 ? H : Hkv)), which == 0, rope && which < 2, d >> 1};
   }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
   __device__ __forceinline__ void pair(const Row& r, int, int, float a, float b, bool, const ColX& cl, float2) const {
     if (!cl.is_q && (r.tc < 0 || r.tc >= Tk)) return;   // outside the cache: contract violation, nothing written
     T* dst = cl.base + (long long)r.b * cl.b_stride + (long long)(cl.is_q ? r.t : r.tc) * D;
-    store_pair(dst, a + RawPair<T>::f32(cl.bias.a), b + RawPair<T>::f32(cl.bias.b), true, true);
+    a += RawPair<T>::f32(cl.bias.a);
+    b += RawPair<T>::f32(cl.bias.b);
+    if (cl.rot) {
+      // (a query past the cache also violates the contract: its row is clamped
+      // into the table, which has at least Tk rows)
+      const int p = r.tc < 0 ? 0 : (r.tc < Tk ? r.tc : Tk - 1);
+      const float2 cs = rope[(long long)p * (D >> 1) + cl.pair];
+      const float ra = cs.x * a - cs.y * b, rb = cs.y * a + cs.x * b;
+      a = ra;
+      b = rb;
+    }
+    store_pair(dst, a, b, true, true);
   }
   __device__ __forceinline__ bool vec_ok() const { return true; }
   __device__ __forceinline__ void pair_in(const Row& r, int m, int n, float a, float b, const ColX& cl,
                                           float2 pre) const {
     pair(r, m, n, a, b, true, cl, pre);
+  }
+};
+
+// SwiGLU: columns (2j, 2j+1) of the product are (gate, up) of hidden unit j;
+// out[m, j] = SiLU(gate) * up, SiLU(z) = z / (1 + e^-z)  ("02 GPT 架构" §6.1;
+// "GPT-1学习笔记" §10.2).  N (= 2F) is even, so every pair exists.
+template <typename T>
+struct EpiSwiGLU {
+  static constexpr bool kPreload = false;
+  static constexpr bool kCompact = true;
+  typedef int Row;
+  typedef int Col;
+  typedef int ColX;
+  T* out;
+  int ldo;
+  __device__ __forceinline__ Row row(int) const { return 0; }
+  __device__ __forceinline__ Col col(int, bool) const { return 0; }
+  __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ void pair(Row, int m, int n, float g, float u, bool, ColX, float2) const {
+    out[(size_t)m * ldo + (n >> 1)] = from_f32<T>(g / (1.0f + __expf(-g)) * u);
+  }
+  __device__ __forceinline__ bool vec_ok() const { return true; }
+  __device__ __forceinline__ void pair_in(Row r, int m, int n, float g, float u, ColX c, float2 p) const {
+    pair(r, m, n, g, u, true, c, p);
   }
 };
 
@@ -1419,6 +1460,7 @@ static hipError_t dispatch_gemm(const float* A, int lda, const float* W, int ldw
 template <typename T>
 static hipError_t linear_t(const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N, int K,
                            void* out, int ldo, int act, int out_f32, const SkinnyWs* sk, hipStream_t st) {
+  if (act == 3) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K, EpiSwiGLU<T>{(T*)out, ldo}, sk, st);
   if (act == 2 && !out_f32) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
                                                  EpiAct<T, 2, false>{(const T*)bias, out, ldo}, sk, st);
   if (act == 2) return dispatch_gemm((const T*)A, lda, (const T*)W, ldw, M, N, K,
@@ -1455,8 +1497,8 @@ hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W,
 template <typename T>
 static hipError_t qkv_t(const QKVArgs& a, const SkinnyWs* sk, hipStream_t st) {
   EpiQKV<T> e{(const T*)a.bias, a.C, a.H, a.D, a.T_seq, 1.0f / (float)a.T_seq, (T*)a.q, a.q_bh, (T*)a.k, a.k_bh,
-              (T*)a.v, a.v_bh, a.pos, a.Tk};
-  return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, 3 * a.C, a.C, e, sk, st);
+              (T*)a.v, a.v_bh, a.pos, a.Tk, a.Hkv, a.rope};
+  return dispatch_gemm((const T*)a.A, a.C, (const T*)a.W, a.C, a.M, a.C + 2 * a.Hkv * a.D, a.C, e, sk, st);
 }
 
 hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyWs* sk) {

@@ -45,8 +45,20 @@ int check_config(const gpt_config* c) {
   if (c->n_embd % c->n_head != 0) return GPT_ERR_CONFIG;
   const int D = c->n_embd / c->n_head, v = vec_of(c);
   if (c->n_embd % v || c->n_ff % v || D % v || D > 128 || c->n_embd > 2048) return GPT_ERR_CONFIG;
+  if (c->arch != 0 && c->arch != 1) return GPT_ERR_CONFIG;
+  if (c->arch == 1) {
+    // the GPT-2 variant flags do not apply to LLaMA-style blocks
+    if (c->activation != 0 || c->post_ln != 0) return GPT_ERR_CONFIG;
+    if (c->n_kv_head < 0 || c->n_kv_head > c->n_head || (c->n_kv_head > 0 && c->n_head % c->n_kv_head != 0))
+      return GPT_ERR_CONFIG;
+    if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return GPT_ERR_CONFIG;
+  } else if (c->n_kv_head != 0 && c->n_kv_head != c->n_head) {
+    return GPT_ERR_CONFIG;
+  }
   return GPT_OK;
 }
+
+int kv_heads(const gpt_config* c) { return c->n_kv_head > 0 ? c->n_kv_head : c->n_head; }
 
 int64_t offsets(const gpt_config* c, int64_t* out, int n) {
   const int64_t V = c->vocab, C = c->n_embd, F = c->n_ff, ctx = c->ctx;
@@ -58,6 +70,16 @@ int64_t offsets(const gpt_config* c, int64_t* out, int n) {
     off += size;
   };
   put(V * C);
+  if (c->arch == 1) {   // LLaMA-style: no position table, no biases, one final RMSNorm gain
+    const int64_t KV = (int64_t)kv_heads(c) * (C / c->n_head);
+    for (int l = 0; l < c->n_layer; ++l) {
+      put(C); put((C + 2 * KV) * C); put(C * C); put(C); put(2 * F * C); put(C * F);
+    }
+    put(C);
+    if (c->untied_head) put(V * C);
+    if (out && k < n) out[k] = off;
+    return off;
+  }
   put(ctx * C);
   for (int l = 0; l < c->n_layer; ++l) {
     put(C); put(C); put(3 * C * C); put(3 * C); put(C * C); put(C);
@@ -72,22 +94,42 @@ int64_t offsets(const gpt_config* c, int64_t* out, int n) {
   return off;
 }
 
-int offset_count(const gpt_config* c) { return 2 + 12 * c->n_layer + (c->post_ln ? 0 : 2) + (c->untied_head ? 1 : 0) + 1; }
+int offset_count(const gpt_config* c) {
+  if (c->arch == 1) return 1 + 6 * c->n_layer + 1 + (c->untied_head ? 1 : 0) + 1;
+  return 2 + 12 * c->n_layer + (c->post_ln ? 0 : 2) + (c->untied_head ? 1 : 0) + 1;
+}
 
 // Element offsets of the tensors of one layer, packing order as documented.
 struct LayerP { int64_t ln1_g, ln1_b, attn_w, attn_b, proj_w, proj_b, ln2_g, ln2_b, fc_w, fc_b, fcproj_w, fcproj_b; };
 
+// LLaMA-style models use the same fields: ln1_g / ln2_g are the RMSNorm gains,
+// attn_w the stacked W_q|W_k|W_v, proj_w W_o, fc_w the interleaved gate/up
+// rows, fcproj_w the down projection; the biases are absent (-1).
 struct Params {
   const char* base;
   size_t es;
   int64_t C, F, V, ctx, L;
   bool post_ln, untied;
+  int arch;
+  int64_t KV;   // K/V width Hkv * D
   const void* at(int64_t e) const { return base + e * (int64_t)es; }
+  const void* opt(int64_t e) const { return e < 0 ? nullptr : at(e); }
   int64_t layer_base(int l) const {
+    if (arch == 1) return V * C + (int64_t)l * (2 * C + (C + 2 * KV) * C + C * C + 3 * F * C);
     return V * C + ctx * C + (int64_t)l * (4 * C * C + 4 * C + 2 * C * F + F + C + 4 * C);
   }
   LayerP layer(int l) const {
     LayerP r;
+    if (arch == 1) {
+      r.ln1_g = layer_base(l);
+      r.attn_w = r.ln1_g + C;
+      r.proj_w = r.attn_w + (C + 2 * KV) * C;
+      r.ln2_g = r.proj_w + C * C;
+      r.fc_w = r.ln2_g + C;
+      r.fcproj_w = r.fc_w + 2 * F * C;
+      r.ln1_b = r.attn_b = r.proj_b = r.ln2_b = r.fc_b = r.fcproj_b = -1;
+      return r;
+    }
     r.ln1_g = layer_base(l);
     r.ln1_b = r.ln1_g + C;
     r.attn_w = r.ln1_b + C;
@@ -102,15 +144,21 @@ struct Params {
     r.fcproj_b = r.fcproj_w + C * F;
     return r;
   }
-  int64_t lnf_g() const { return layer_base((int)L); }   // pre-LN models only
-  int64_t lnf_b() const { return layer_base((int)L) + C; }
-  // the head matrix: the token table, or the tensor after the last layer (and ln_f)
-  int64_t head_w() const { return untied ? layer_base((int)L) + (post_ln ? 0 : 2 * C) : 0; }
+  int64_t lnf_g() const { return layer_base((int)L); }   // pre-LN (or the final RMSNorm gain)
+  int64_t lnf_b() const { return arch == 1 ? -1 : layer_base((int)L) + C; }
+  int64_t wpe() const { return arch == 1 ? -1 : V * C; }
+  // the head matrix: the token table, or the tensor after the last layer (and the final norm)
+  int64_t head_w() const {
+    if (!untied) return 0;
+    if (arch == 1) return layer_base((int)L) + C;
+    return layer_base((int)L) + (post_ln ? 0 : 2 * C);
+  }
 };
 
 Params params_of(const gpt_config* c, const void* p) {
   return Params{static_cast<const char*>(p), esize(c), c->n_embd, c->n_ff, c->vocab, c->ctx, c->n_layer,
-                c->post_ln != 0, c->untied_head != 0};
+                c->post_ln != 0, c->untied_head != 0, c->arch,
+                (int64_t)kv_heads(c) * (c->n_embd / c->n_head)};
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -120,7 +168,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // partial indices.  Passes of at most 64 bf16 rows (decode steps) add the
 // split-K scratch of the skinny products.
 struct Plan {
-  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, alast, pidx, skpart, skcnt, total;
+  size_t x, a, q, k, v, o, h, pmax, psum, tgt, tok, bsum, alast, pidx, skpart, skcnt, rope, total;
   int ntiles, nblocks;
 };
 
@@ -138,8 +186,9 @@ Plan plan(const gpt_config* c, int B, int T, bool decode) {
   p.x = take(M * C * 4);
   p.a = take(M * C * es);
   p.q = take(M * C * es);
-  p.k = decode ? 0 : take(M * C * es);
-  p.v = decode ? 0 : take(M * C * es);
+  const size_t KV = (size_t)kv_heads(c) * (C / c->n_head);
+  p.k = decode ? 0 : take(M * KV * es);
+  p.v = decode ? 0 : take(M * KV * es);
   p.o = take(M * C * es);
   p.h = take(M * F * es);
   p.pmax = take(head_rows * p.ntiles * 4);
@@ -152,6 +201,7 @@ Plan plan(const gpt_config* c, int B, int T, bool decode) {
   const bool split = M <= 64 && c->dtype == GPT_BF16;
   p.skpart = split ? take((size_t)SK_PART_TILES * 64 * 32 * 4) : 0;
   p.skcnt = split ? take((size_t)SK_COUNTERS * 4) : 0;
+  p.rope = c->arch == 1 ? take((size_t)c->ctx * (C / c->n_head / 2) * 8) : 0;
   p.total = off;
   return p;
 }
@@ -185,9 +235,102 @@ hipError_t mark(const Pass& s, int kind, bool last_layer, bool begin) {
   return ev ? hipEventRecord(static_cast<hipEvent_t>(ev), s.st) : hipSuccess;
 }
 
+// LLaMA-style embedding and blocks ("02 GPT 架构" §6.1-6.3): token rows only,
+// then per block RMSNorm -> W_q|W_k|W_v with RoPE on Q and K (angle table in
+// the workspace) -> grouped-query attention -> W_o + residual -> RMSNorm ->
+// gate/up product with the SwiGLU epilogue -> down projection + residual.
+// Leaves the residual stream in ws.x (with no blocks ws.a holds the final
+// RMSNorm of the embedding).
+int run_blocks_llama(const Pass& s) {
+  const gpt_config* cfg = s.cfg;
+  const Params& P = s.P;
+  const int dt = cfg->dtype, B = s.B, T = s.T, M = B * T, C = cfg->n_embd, F = cfg->n_ff;
+  const int H = cfg->n_head, D = C / H, L = cfg->n_layer, Hkv = kv_heads(cfg);
+  float* x = at<float>(s.ws, s.pl.x);
+  void* a = at<char>(s.ws, s.pl.a);
+  void* q = at<char>(s.ws, s.pl.q);
+  void* o = at<char>(s.ws, s.pl.o);
+  void* h = at<char>(s.ws, s.pl.h);
+  const size_t es = esize(cfg);
+  const long long cache_layer = (long long)B * Hkv * s.Tmax * D;
+  SkinnyWs skw{};
+  if (s.pl.skpart) skw = SkinnyWs{at<float>(s.ws, s.pl.skpart), SK_PART_TILES, at<int>(s.ws, s.pl.skcnt), SK_COUNTERS};
+  const SkinnyWs* sk = s.pl.skpart ? &skw : nullptr;
+  float2* rope = at<float2>(s.ws, s.pl.rope);
+  GPT_TRY(launch_rope_table(rope, cfg->ctx, D, (double)cfg->rope_theta, s.st));
+
+  LnArgs la{};
+  la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps; la.rms = 1;
+  la.idx = s.idx; la.wte = P.at(0); la.wpe = nullptr; la.vocab = cfg->vocab; la.ctx = cfg->ctx;
+  la.pos = s.mode == STEP ? s.pos : nullptr;
+  la.x = x; la.in_mul = 1; la.in_add = 0;
+  la.g = P.at(L > 0 ? P.layer(0).ln1_g : P.lnf_g()); la.b = nullptr;
+  la.out = a;
+  la.zero = sk ? skw.cnt : nullptr; la.zero_n = sk ? skw.cnt_len : 0;
+  GPT_TRY(launch_embed_ln(dt, la, s.st));
+  la.idx = nullptr; la.pos = nullptr; la.zero = nullptr; la.zero_n = 0;
+
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  for (int l = 0; l < L; ++l) {
+    const LayerP w = P.layer(l);
+    const bool last = l == L - 1;
+    void* kbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.k) : static_cast<char*>(s.kc) + l * cache_layer * es;
+    void* vbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.v) : static_cast<char*>(s.vc) + l * cache_layer * es;
+    const long long kv_bh = s.mode == FORWARD ? (long long)T * D : (long long)s.Tmax * D;
+    QKVArgs qa{};
+    qa.A = a; qa.W = P.at(w.attn_w); qa.bias = nullptr;
+    qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
+    qa.q = q; qa.q_bh = (long long)T * D;
+    qa.k = kbuf; qa.k_bh = kv_bh;
+    qa.v = vbuf; qa.v_bh = kv_bh;
+    qa.pos = s.mode == STEP ? s.pos : nullptr;
+    qa.Tk = s.mode == FORWARD ? T : s.Tmax;
+    qa.Hkv = Hkv; qa.rope = rope;
+    GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
+    GPT_TRY(launch_qkv(dt, qa, s.st, sk));
+    GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, true));
+    if (s.mode == STEP) {
+      DecAttnArgs da{};
+      da.q = q; da.k = kbuf; da.v = vbuf; da.kv_bh = kv_bh; da.Tmax = s.Tmax; da.pos = s.pos;
+      da.o = o; da.o_ld = C; da.B = B; da.H = H; da.D = D; da.scale_log2 = scale_log2; da.Hkv = Hkv;
+      GPT_TRY(launch_attention_decode(dt, da, s.st));
+    } else {
+      AttnArgs aa{};
+      aa.q = q; aa.q_bh = (long long)T * D;
+      aa.k = kbuf; aa.k_bh = kv_bh;
+      aa.v = vbuf; aa.v_bh = kv_bh;
+      aa.o = o; aa.o_ld = C;
+      aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = Hkv;
+      aa.scale_log2 = scale_log2;
+      GPT_TRY(launch_attention(dt, aa, s.st));
+    }
+    GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, true));
+    GPT_TRY(launch_linear_resid(dt, o, C, P.at(w.proj_w), C, nullptr, M, C, C, x, C, s.st, sk));
+    GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, false));
+    la.g = P.at(w.ln2_g);
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
+    GPT_TRY(launch_layernorm(dt, la, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
+    GPT_TRY(launch_linear(dt, a, C, P.at(w.fc_w), C, nullptr, M, 2 * F, C, h, F, 3, 0, s.st, sk));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, true));
+    GPT_TRY(launch_linear_resid(dt, h, F, P.at(w.fcproj_w), F, nullptr, M, C, F, x, C, s.st, sk));
+    GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, false));
+    if (l + 1 < L) {   // RMSNorm of the next block (the final one is applied by the caller)
+      la.g = P.at(P.layer(l + 1).ln1_g);
+      GPT_TRY(launch_layernorm(dt, la, s.st));
+    }
+  }
+  return GPT_OK;
+}
+
 // Embedding and the L blocks; leaves the fp32 residual stream in ws.x (with
 // no blocks, ws.a already holds ln_f of the embedding).
 int run_blocks(const Pass& s) {
+  if (s.cfg->arch == 1) return run_blocks_llama(s);
   const gpt_config* cfg = s.cfg;
   const Params& P = s.P;
   const int dt = cfg->dtype, B = s.B, T = s.T, M = B * T, C = cfg->n_embd, F = cfg->n_ff;
@@ -205,7 +348,7 @@ int run_blocks(const Pass& s) {
 
   LnArgs la{};
   la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps;
-  la.idx = s.idx; la.wte = P.at(0); la.wpe = P.at(P.V * P.C); la.vocab = cfg->vocab; la.ctx = cfg->ctx;
+  la.idx = s.idx; la.wte = P.at(0); la.wpe = P.at(P.wpe()); la.vocab = cfg->vocab; la.ctx = cfg->ctx;
   la.pos = s.mode == STEP ? s.pos : nullptr;
   la.x = x; la.in_mul = 1; la.in_add = 0;
   // pre-LN: the embedding kernel applies LN1 of block 0 (ln_f with no blocks);
@@ -235,6 +378,7 @@ int run_blocks(const Pass& s) {
     qa.v = vbuf; qa.v_bh = kv_bh;
     qa.pos = s.mode == STEP ? s.pos : nullptr;
     qa.Tk = s.mode == FORWARD ? T : s.Tmax;
+    qa.Hkv = H; qa.rope = nullptr;
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
     GPT_TRY(launch_qkv(dt, qa, s.st, sk));
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
@@ -242,7 +386,7 @@ int run_blocks(const Pass& s) {
     if (s.mode == STEP) {
       DecAttnArgs da{};
       da.q = q; da.k = kbuf; da.v = vbuf; da.kv_bh = kv_bh; da.Tmax = s.Tmax; da.pos = s.pos;
-      da.o = o; da.o_ld = C; da.B = B; da.H = H; da.D = D; da.scale_log2 = scale_log2;
+      da.o = o; da.o_ld = C; da.B = B; da.H = H; da.D = D; da.scale_log2 = scale_log2; da.Hkv = H;
       GPT_TRY(launch_attention_decode(dt, da, s.st));
     } else {
       AttnArgs aa{};
@@ -250,7 +394,7 @@ int run_blocks(const Pass& s) {
       aa.k = kbuf; aa.k_bh = kv_bh;
       aa.v = vbuf; aa.v_bh = kv_bh;
       aa.o = o; aa.o_ld = C;
-      aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D;
+      aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
       aa.scale_log2 = scale_log2;
       GPT_TRY(launch_attention(dt, aa, s.st));
     }
@@ -291,7 +435,8 @@ int final_norm(const Pass& s, int M, int mul, int add, void* out) {
   LnArgs la{};
   la.M = M; la.C = cfg->n_embd; la.T_seq = s.T; la.eps = cfg->ln_eps;
   la.x = at<float>(s.ws, s.pl.x); la.in_mul = mul; la.in_add = add;
-  la.g = s.P.at(s.P.lnf_g()); la.b = s.P.at(s.P.lnf_b());
+  la.g = s.P.at(s.P.lnf_g()); la.b = s.P.opt(s.P.lnf_b());
+  la.rms = cfg->arch == 1 ? 1 : 0;   // LLaMA-style: the final RMSNorm
   la.out = out;
   return hip_status(launch_layernorm(cfg->dtype, la, s.st));
 }
@@ -530,6 +675,7 @@ int gpt_mark_seen(const gpt_config* cfg, const int32_t* tokens, int B, int T, ui
 int gpt_head_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes) {
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
+  if (cfg->arch != 0) return GPT_ERR_CONFIG;
   if (!bytes) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0 || (long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
   if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
@@ -542,6 +688,7 @@ int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* 
                       size_t ws_bytes, void* stream) {
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
+  if (cfg->arch != 0) return GPT_ERR_CONFIG;   // the final RMSNorm's backward is not provided
   if (!params || !idx || !x || !dx || !grads || !ws) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0 || (long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
   if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
@@ -603,8 +750,8 @@ int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int
   if (!idx || !dx0 || !grads) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0 || (long long)B * T > (1LL << 24)) return GPT_ERR_SHAPE;
   if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
-  const int64_t wpe = (int64_t)cfg->vocab * cfg->n_embd;
-  GPT_TRY(launch_embed_backward(idx, B, T, cfg->n_embd, cfg->vocab, dx0, grads, grads + wpe,
+  const int64_t wpe = params_of(cfg, nullptr).wpe();   // LLaMA-style models have no position table
+  GPT_TRY(launch_embed_backward(idx, B, T, cfg->n_embd, cfg->vocab, dx0, grads, wpe < 0 ? nullptr : grads + wpe,
                                 static_cast<hipStream_t>(stream)));
   return GPT_OK;
 }
@@ -644,7 +791,7 @@ int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, con
   aa.k = k; aa.k_bh = (long long)T * D;
   aa.v = u; aa.v_bh = (long long)T * D;
   aa.o = out; aa.o_ld = C;
-  aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D;
+  aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   return hip_status(launch_attention(cfg->dtype, aa, static_cast<hipStream_t>(stream)));
 }

@@ -8,16 +8,20 @@
 namespace gptmi {
 
 struct QKVArgs {
-  const void* A;      // LN output [M, C]
-  const void* W;      // c_attn weight [3C, C]
-  const void* bias;   // [3C]
+  const void* A;      // normalised rows [M, C]
+  const void* W;      // weight [(H + 2 Hkv) D, C]: rows of W_q, W_k, W_v
+  const void* bias;   // [(H + 2 Hkv) D], nullable (no bias)
   int M, C, H, D, T_seq;
   void* q; long long q_bh;             // Q [B,H,T,D]
-  void* k; long long k_bh;             // K [B,H,Tk,D]
-  void* v; long long v_bh;             // U [B,H,Tk,D]
+  void* k; long long k_bh;             // K [B,Hkv,Tk,D]
+  void* v; long long v_bh;             // U [B,Hkv,Tk,D]
   const int32_t* pos;                  // nullable: cache position of t = 0
   int Tk;                              // K/U rows available; writes at positions >= Tk are dropped
+  int Hkv;                             // K/U heads (= H without grouping)
+  const float2* rope;                  // nullable: (cos, sin) [positions][D/2]; rotates Q and K pairs
 };
+// (cos, sin) of p * theta^(-2i/D) for p < rows, i < D/2, in double, rounded to float.
+hipError_t launch_rope_table(float2* tab, int rows, int D, double theta, hipStream_t st);
 
 // Embedding (+ first LayerNorm) or LayerNorm of M rows.
 struct LnArgs {
@@ -34,26 +38,29 @@ struct LnArgs {
   int* zero; int zero_n;               // embedding: nullable ints set to zero (split-K counters)
   int ident;                           // embedding: out = x itself (no LayerNorm; post-LN models)
   int write_x;                         // LayerNorm: the normalised row also replaces its x row (post-LN)
+  int rms;                             // RMSNorm: no mean centring (b is then NULL: no bias)
 };
 
 // Attention of one new query per (b, h) over positions 0 .. *pos of the cache.
 struct DecAttnArgs {
   const void* q;                       // [B, H, D]
-  const void* k; const void* v;        // this layer's caches [B, H, Tmax, D]
+  const void* k; const void* v;        // this layer's caches [B, Hkv, Tmax, D]
   long long kv_bh;                     // Tmax * D
   int Tmax;
   const int32_t* pos;                  // device
   void* o; int o_ld;                   // [B, o_ld], head h at columns [hD, hD+D)
   int B, H, D;
   float scale_log2;
+  int Hkv;                             // cache heads; query head h reads head h / (H / Hkv)
 };
 
 struct AttnArgs {
   const void* q; long long q_bh;       // Q [B,H,T,D]
-  const void* k; long long k_bh;       // K [B,H,*,D]
-  const void* v; long long v_bh;       // U [B,H,*,D]
+  const void* k; long long k_bh;       // K [B,Hkv,*,D]
+  const void* v; long long v_bh;       // U [B,Hkv,*,D]
   void* o; int o_ld;                   // O [B*T, o_ld], head h at columns [hD, hD+D)
   int B, H, T_seq, D;
+  int Hkv;                             // K/U heads; query head h reads K/U head h / (H / Hkv)
   float scale_log2;                    // log2(e) / sqrt(D)
 };
 

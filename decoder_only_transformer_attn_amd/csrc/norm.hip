@@ -3,7 +3,9 @@
 // Token + position embedding: x[b,t,:] = E[idx[b,t],:] + P[t,:]  ("第 25 章 从小
 // GPT 到 GPT-2" §25.1; "预训练一个 Mini GPT" 第1步).  LayerNorm over the C
 // channels with biased variance and eps inside the square root ("预训练一个
-// Mini GPT" 第4步; "GPT-1学习笔记" §3.2).
+// Mini GPT" 第4步; "GPT-1学习笔记" §3.2).  RMSNorm (LLaMA-style models,
+// "02 GPT 架构" §6.1; "GPT-1学习笔记" §10.2): no mean centring and no bias,
+// g * x / sqrt(mean(x^2) + eps); those models also have no position table.
 //
 // One wavefront per row: the row lives in registers (C / 64 values per lane),
 // mean and variance are two passes over registers with wavefront reductions,
@@ -50,14 +52,14 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
     int t = row % a.T_seq + (a.pos ? *a.pos : 0);
     t = t < 0 ? 0 : (t < a.ctx ? t : a.ctx - 1);                // positions outside the table violate the contract
     const T* __restrict__ er = reinterpret_cast<const T*>(a.wte) + (size_t)tok * C;
-    const T* __restrict__ pr = reinterpret_cast<const T*>(a.wpe) + (size_t)t * C;
+    const T* __restrict__ pr = a.wpe ? reinterpret_cast<const T*>(a.wpe) + (size_t)t * C : nullptr;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = (j * 64 + lane) * 4;
       if (c < C) {
-        float e4[4], p4[4];
+        float e4[4], p4[4] = {0.f, 0.f, 0.f, 0.f};
         load4(er + c, e4);
-        load4(pr + c, p4);
+        if (pr) load4(pr + c, p4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[j][e] = e4[e] + p4[e];
         store4(xr + c, v[j]);
@@ -84,7 +86,7 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
 #pragma unroll
   for (int j = 0; j < NCH; ++j)
     if ((j * 64 + lane) * 4 < C) s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
-  const float mean = wave_sum(s) / (float)C;
+  const float mean = a.rms ? 0.f : wave_sum(s) / (float)C;   // (uniform branch)
   float s2 = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j)
@@ -98,9 +100,9 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   for (int j = 0; j < NCH; ++j) {
     const int c = (j * 64 + lane) * 4;
     if (c < C) {
-      float g4[4], b4[4], o4[4];
+      float g4[4], b4[4] = {0.f, 0.f, 0.f, 0.f}, o4[4];
       load4(g + c, g4);
-      load4(bta + c, b4);
+      if (bta) load4(bta + c, b4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = (v[j][e] - mean) * rstd * g4[e] + b4[e];
       store4(orow + c, o4);

@@ -28,7 +28,8 @@ class gpt_config(ctypes.Structure):
     _fields_ = [("vocab", ctypes.c_int32), ("ctx", ctypes.c_int32), ("n_embd", ctypes.c_int32),
                 ("n_head", ctypes.c_int32), ("n_layer", ctypes.c_int32), ("n_ff", ctypes.c_int32),
                 ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
-                ("post_ln", ctypes.c_int32), ("untied_head", ctypes.c_int32)]
+                ("post_ln", ctypes.c_int32), ("untied_head", ctypes.c_int32), ("arch", ctypes.c_int32),
+                ("n_kv_head", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
 
 
 class gpt_sampling(ctypes.Structure):
@@ -94,7 +95,8 @@ def check(status: int) -> None:
 
 def cfg_c(cfg) -> gpt_config:
     return gpt_config(cfg.vocab, cfg.ctx, cfg.n_embd, cfg.n_head, cfg.n_layer, cfg.n_ff, cfg.ln_eps, cfg.dtype,
-                      getattr(cfg, "act", 0), getattr(cfg, "post_ln", 0), getattr(cfg, "untied", 0))
+                      getattr(cfg, "act", 0), getattr(cfg, "post_ln", 0), getattr(cfg, "untied", 0),
+                      getattr(cfg, "arch", 0), getattr(cfg, "n_kv_head", 0), getattr(cfg, "rope_theta", 10000.0))
 
 
 def param_count(cfg) -> int:
@@ -102,7 +104,10 @@ def param_count(cfg) -> int:
 
 
 def param_offsets(cfg):
-    n = 2 + 12 * cfg.n_layer + (0 if getattr(cfg, "post_ln", 0) else 2) + (1 if getattr(cfg, "untied", 0) else 0) + 1
+    if getattr(cfg, "arch", 0) == 1:
+        n = 1 + 6 * cfg.n_layer + 1 + (1 if getattr(cfg, "untied", 0) else 0) + 1
+    else:
+        n = 2 + 12 * cfg.n_layer + (0 if getattr(cfg, "post_ln", 0) else 2) + (1 if getattr(cfg, "untied", 0) else 0) + 1
     arr = (ctypes.c_int64 * n)()
     check(load().gpt_param_offsets(ctypes.byref(cfg_c(cfg)), arr, n))
     return list(arr)
@@ -292,8 +297,9 @@ class Decoder:
         import torch
         H = cfg.n_head
         D = cfg.n_embd // H
+        Hkv = getattr(cfg, "n_kv_head", 0) or H     # caches hold the K/V heads only
         self.cfg, self.B, self.Tp, self.Tmax = cfg, B, Tp, Tmax
-        shape = (max(cfg.n_layer, 1), B, H, Tmax, D)
+        shape = (max(cfg.n_layer, 1), B, Hkv, Tmax, D)
         self.k_cache = torch.zeros(shape, dtype=torch_dtype(cfg), device=device)
         self.v_cache = torch.zeros(shape, dtype=torch_dtype(cfg), device=device)
         self.pos = torch.zeros((1,), dtype=torch.int32, device=device)

@@ -77,6 +77,14 @@ typedef struct gpt_config {
   int32_t activation;
   int32_t post_ln;
   int32_t untied_head;
+  int32_t arch;       /* 0: GPT-2 blocks; 1: LLaMA-style blocks ("02 GPT 架构" §6.1-6.3):
+                       * RMSNorm g*x/sqrt(mean(x^2)+ln_eps) in place of LayerNorm, no position
+                       * table, RoPE on Q and K (adjacent pairs (2i, 2i+1) turned by
+                       * p * rope_theta^(-2i/D), §5.2), grouped-query attention (§6.2),
+                       * SwiGLU MLP W2(SiLU(x W1) * (x W3)), no biases, a final RMSNorm.
+                       * activation and post_ln must be 0. */
+  int32_t n_kv_head;  /* arch 1: K/V heads (divides n_head; 1 = MQA; 0 = n_head).  arch 0: 0 or n_head. */
+  float rope_theta;   /* arch 1: RoPE base (the pages use 10000); > 0 */
 } gpt_config;
 
 /* Number of unique parameters, closed form ("第 25 章 从小 GPT 到 GPT-2" §25.4):
@@ -85,6 +93,8 @@ typedef struct gpt_config {
  * adds VC.  Also the element count of the parameter blob.  Returns a
  * negative gpt_status on an invalid config (host only, no HIP call). */
 int64_t gpt_param_count(const gpt_config* cfg);
+/*   (arch 1: per block 2C + (C + 2 Hkv D) C + C^2 + 3 C F, plus VC, the final
+ *   RMSNorm's C and, untied, VC.) */
 
 /* Element offsets of every tensor in the parameter blob, in packing order:
  *   wte[V,C], wpe[ctx,C],
@@ -93,6 +103,12 @@ int64_t gpt_param_count(const gpt_config* cfg);
  *   lnf_g[C], lnf_b[C]   (pre-LN models only),
  *   head_w[V,C]          (untied head only),
  *   end.
+ * arch 1 (LLaMA-style):
+ *   wte[V,C],
+ *   per layer l: rms1_g[C], wqkv[(H + 2 Hkv) D, C] (rows of W_q, then W_k, W_v),
+ *                wo[C,C], rms2_g[C], w13[2F, C] (rows interleaved: 2j = gate W1
+ *                row j, 2j+1 = up W3 row j), w2[C,F],
+ *   rmsf_g[C], head_w[V,C] (untied head only), end: 1 + 6 L + 1 (+1) + 1 offsets.
  * With a tied head there is no head tensor: the head reads wte (tying as one
  * shared tensor, §25.4).  off (host) receives 2 + 12 L + (post_ln ? 0 : 2) +
  * (untied_head ? 1 : 0) + 1 values.  Returns GPT_OK, or GPT_ERR_SHAPE if n is
@@ -144,7 +160,8 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
  * the last position's logits (lowest index on ties).
  *
  * Cache layout (device, caller-owned, cfg->dtype): k_cache and v_cache each
- * [L][B][H][Tmax][D]; row t of (l, b, h) holds position t.  Requires
+ * [L][B][Hkv][Tmax][D] (Hkv = K/V heads: n_head for GPT-2 blocks); row t of
+ * (l, b, h) holds position t (arch 1: the key after its rotation).  Requires
  * 1 <= Tmax <= min(ctx, 4096).  pos (device, int32[1]) is the number of cache
  * positions already filled, the same for every sequence; the library updates
  * it on the device, so a decode loop needs no host round trip.
@@ -251,7 +268,8 @@ int gpt_head_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size_
  *   ws         (device) at least gpt_head_backward_workspace_bytes.
  * The logits are recomputed twice (row log-sum-exp, then dz from fp32
  * accumulators) and never stored.  Requires 1 <= T <= ctx, B * T <= 2^20.
- * No position with a target: every gradient added is 0 (mean_loss NaN). */
+ * No position with a target: every gradient added is 0 (mean_loss NaN).
+ * GPT-2 blocks only (arch 1: GPT_ERR_CONFIG). */
 int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
                       const int32_t* targets, const float* x, float* dx, float* grads, float* mean_loss, void* ws,
                       size_t ws_bytes, void* stream);
@@ -260,7 +278,8 @@ int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* 
  *   grads[wte row v] += sum of dx0 over the positions holding v (position
  *   order), grads[wpe row t] += sum over the batch of dx0[:, t].
  *   idx  (device) int32 [B, T]; a position holding an id outside [0, V)
- *        adds nothing to the token table (its position row still gets dx0).
+ *        adds nothing to the token table (its position row still gets dx0;
+ *        arch 1 models have no position table). 
  *   dx0  (device) fp32 [B*T, C]: d loss / d x0.
  * Requires 1 <= T <= ctx, B * T <= 2^24.  No workspace. */
 int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int T, const float* dx0, float* grads,

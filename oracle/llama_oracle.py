@@ -167,11 +167,13 @@ def greedy_recompute(params: dict, prompt: np.ndarray, steps: int, H: int, eps: 
     return np.stack(toks, 1), np.stack(lasts, 1)
 
 
-def greedy_cached(params: dict, prompt: np.ndarray, steps: int, H: int, eps: float = 1e-5):
-    """Greedy decoding with per-layer K/V caches (rotated keys, Hkv heads)."""
+def greedy_cached(params: dict, prompt: np.ndarray, steps: int, H: int, eps: float = 1e-5,
+                  forced: Optional[np.ndarray] = None):
+    """Greedy decoding with per-layer K/V caches (rotated keys, Hkv heads).
+    forced [B, steps]: feed these tokens instead of the argmax (teacher
+    forcing, to compare logits along another decoder's history)."""
     prompt = np.asarray(prompt)
     caches = [dict() for _ in params["layers"]]
-    x = params["wte"][prompt]
     pos0, toks, lasts = 0, [], []
     cur = prompt
     for it in range(steps + 1):
@@ -183,5 +185,5 @@ def greedy_cached(params: dict, prompt: np.ndarray, steps: int, H: int, eps: flo
         t = O.argmax_lowest(z)
         toks.append(t)
         lasts.append(z)
-        cur = t[:, None]
+        cur = (t if forced is None or it >= steps else np.asarray(forced)[:, it])[:, None]
     return np.stack(toks, 1), np.stack(lasts, 1)

@@ -190,3 +190,32 @@ def test_backward_validation_and_workspace():
     assert eb(c, 1, 2, 5, 1, None, None) == lib.GPT_ERR_NULL
     assert eb(c, 1, 0, 5, 1, 1, None) == lib.GPT_ERR_SHAPE
     assert eb(c, 1, 2, cfg.ctx + 1, 1, 1, None) == lib.GPT_ERR_SEQ_TOO_LONG
+
+
+@pytest.mark.parametrize("Hkv,untied,L", [(0, 0, 2), (2, 1, 3), (1, 0, 1), (4, 1, 0)])
+def test_llama_param_count_and_offsets(Hkv, untied, L):
+    import dataclasses as dc
+    from oracle import llama_oracle as LO
+    cfg = synth.GPTConfig(vocab=101, ctx=32, n_embd=64, n_head=4, n_layer=L, n_ff=96, arch=1, n_kv_head=Hkv,
+                          untied=untied)
+    assert lib.param_count(cfg) == LO.param_count(cfg.vocab, cfg.n_embd, L, 4, cfg.kv_heads, cfg.n_ff, bool(untied))
+    assert lib.param_count(cfg) == synth.blob_numel(cfg)
+    assert lib.param_offsets(cfg) == [off for _, _, off in synth.blob_layout(cfg)]
+    bf = dc.replace(cfg, dtype=synth.BF16)
+    assert lib.param_count(bf) == synth.blob_numel(bf)
+
+
+def test_llama_config_is_validated():
+    import dataclasses as dc
+    good = synth.GPTConfig(vocab=101, ctx=32, n_embd=64, n_head=4, n_layer=1, n_ff=96, arch=1, n_kv_head=2)
+    count = lambda c: lib.load().gpt_param_count(ctypes.byref(lib.cfg_c(c)))
+    assert count(good) > 0
+    for bad in (dict(n_kv_head=3), dict(n_kv_head=8), dict(n_kv_head=-1), dict(act=1), dict(post_ln=1),
+                dict(rope_theta=0.0), dict(rope_theta=float("inf")), dict(arch=2)):
+        assert count(dc.replace(good, **bad)) == lib.GPT_ERR_CONFIG, bad
+    assert count(dc.replace(good, arch=0, n_kv_head=1)) == lib.GPT_ERR_CONFIG   # no grouping in GPT-2 blocks
+    assert count(dc.replace(good, arch=0, n_kv_head=4)) > 0
+    # the head backward covers GPT-2 blocks only
+    out = ctypes.c_size_t(0)
+    assert lib.load().gpt_head_backward_workspace_bytes(ctypes.byref(lib.cfg_c(good)), 2, 4,
+                                                        ctypes.byref(out)) == lib.GPT_ERR_CONFIG

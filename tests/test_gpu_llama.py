@@ -1,0 +1,136 @@
+"""GPU parity of the LLaMA-style model (RMSNorm, RoPE, grouped-query
+attention, SwiGLU, no biases or position table) through the C ABI against the
+fp64 LLaMA oracle: forward logits and loss, and greedy decoding with the
+key/value cache (caches of Hkv heads, rotated keys).
+
+Bounds as for the GPT-2 model: fp32 max|dlogit| <= 1e-4 max|z_ref|, loss
+1e-4 relative; bf16 max|dlogit| <= 5e-2, loss 1e-2 relative (bf16 operands,
+fp32 accumulation; the rotary angles come from a double-precision table, so
+they add no error beyond the rounding of Q and K).  Decoding replays the GPU's
+tokens in the oracle (teacher forcing) and accepts a token whose oracle logit
+is within the tie band of the maximum (fp32 1e-4 max|z|, bf16 0.1).
+"""
+import dataclasses as dc
+
+import numpy as np
+import pytest
+
+from decoder_only_transformer_attn_amd import synth
+from oracle import llama_oracle as LO
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _lib():
+    from decoder_only_transformer_attn_amd import lib
+    lib.load()
+    return lib
+
+
+def _cfg(**kw):
+    base = dict(vocab=1000, ctx=64, n_embd=128, n_head=4, n_layer=2, n_ff=352, arch=1, n_kv_head=2)
+    base.update(kw)
+    return synth.GPTConfig(**base)
+
+
+def run_forward(cfg, params, ids, targets=None):
+    lib = _lib()
+    P = lib.params_to_device(cfg, synth.pack(cfg, params))
+    idx = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    tg = None if targets is None else torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int32)).cuda()
+    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], True)
+    logits, tok, mean = f(P, idx, tg)
+    torch.cuda.synchronize()
+    return logits.float().cpu().numpy(), tok.cpu().numpy(), float(mean.item())
+
+
+def check(cfg, params, ids, targets=None):
+    lg, tok, mean = run_forward(cfg, params, ids, targets)
+    ref_l, ref_t, ref_m = LO.forward(synth.unpack_f64(cfg, params), ids, cfg.n_head, cfg.ln_eps, targets=targets)
+    err = np.abs(lg - ref_l).max()
+    scale = np.abs(ref_l).max()
+    print(f"max|dlogit| {err:.3e} (scale {scale:.3e}), loss gpu {mean:.6f} ref {ref_m:.6f}")
+    if cfg.dtype == synth.F32:
+        assert err <= 1e-4 * scale
+        assert abs(mean - ref_m) <= 1e-4 * abs(ref_m)
+    else:
+        assert err <= 5e-2
+        assert abs(mean - ref_m) <= 1e-2 * abs(ref_m)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("kw", [dict(n_kv_head=2), dict(n_kv_head=4), dict(n_kv_head=1, untied=1),
+                                dict(n_kv_head=2, n_layer=0), dict(n_kv_head=2, rope_theta=500.0)])
+@pytest.mark.parametrize("B,T", [(2, 37), (3, 64)])
+def test_llama_forward_matches_oracle(dtype, kw, B, T):
+    cfg = _cfg(dtype=dtype, **kw)
+    params = synth.make_params(cfg, seed=B * T, cfg_id=61, init="stress")
+    ids = synth.make_ids(cfg, B, T, seed=B + T)
+    tg = None
+    if T == 37:
+        tg = np.random.default_rng(T).integers(0, cfg.vocab, (B, T)).astype(np.int32)
+        tg[0, 5] = -1
+    check(cfg, params, ids, tg)
+
+
+def test_llama_gpt2_width_bf16():
+    # C = 768, 12 heads of 64 sharing 4 K/V heads, F = 2048: the block products
+    # take the large-tile paths (N = 1280 and 4096, K = 768 and 2048)
+    cfg = _cfg(vocab=5003, ctx=256, n_embd=768, n_head=12, n_kv_head=4, n_ff=2048, dtype=synth.BF16)
+    params = synth.make_params(cfg, seed=7, cfg_id=62, init="bench")
+    ids = synth.make_ids(cfg, 2, 256, seed=7)
+    check(cfg, params, ids)
+
+
+def test_llama_causality_and_position_dependence():
+    # later tokens leave earlier logits unchanged; RoPE makes a shifted copy of
+    # a sequence produce different logits only through relative positions
+    cfg = _cfg(dtype=synth.F32)
+    params = synth.make_params(cfg, seed=3, cfg_id=63, init="stress")
+    ids = synth.make_ids(cfg, 2, 40, seed=3)
+    lg, _, _ = run_forward(cfg, params, ids)
+    ids2 = ids.copy()
+    ids2[:, 25:] = (ids2[:, 25:] + 7) % cfg.vocab
+    lg2, _, _ = run_forward(cfg, params, ids2)
+    assert np.abs(lg2[:, :25] - lg[:, :25]).max() <= 1e-5 * np.abs(lg).max()
+    assert np.abs(lg2[:, 25:] - lg[:, 25:]).max() > 1e-3
+
+
+def run_decode(cfg, params, prompt, steps, Tmax):
+    lib = _lib()
+    B, Tp = prompt.shape
+    P = lib.params_to_device(cfg, synth.pack(cfg, params))
+    idx = torch.from_numpy(np.ascontiguousarray(prompt, dtype=np.int32)).cuda()
+    dec = lib.Decoder(cfg, B, Tp, Tmax)
+    z = torch.empty((steps + 1, B, cfg.vocab), dtype=lib.torch_dtype(cfg), device="cuda")
+    toks = torch.empty((steps + 1, B), dtype=torch.int32, device="cuda")
+    dec.prefill(P, idx, last_logits=z[0])
+    toks[0] = dec.tok
+    for s in range(steps):
+        dec.step(P, logits=z[s + 1])
+        toks[s + 1] = dec.tok
+    torch.cuda.synchronize()
+    return toks.t().cpu().numpy(), z.float().permute(1, 0, 2).cpu().numpy(), int(dec.pos.item())
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("kw", [dict(n_kv_head=2), dict(n_kv_head=1, untied=1), dict(n_kv_head=4)])
+def test_llama_decode_matches_oracle(dtype, kw):
+    cfg = _cfg(dtype=dtype, **kw)
+    params = synth.make_params(cfg, seed=11, cfg_id=64, init="stress")
+    B, Tp, steps, Tmax = 3, 9, 12, 32
+    prompt = synth.make_ids(cfg, B, Tp, seed=11)
+    toks, z, pos = run_decode(cfg, params, prompt, steps, Tmax)
+    assert pos == Tp + steps
+    P = synth.unpack_f64(cfg, params)
+    ref_tok, ref_z = LO.greedy_cached(P, prompt, steps, cfg.n_head, cfg.ln_eps, forced=toks[:, :steps])
+    for b in range(B):
+        err = np.abs(z[b] - ref_z[b]).max()
+        tol = 1e-4 * np.abs(ref_z[b]).max() if dtype == synth.F32 else 5e-2
+        band = 1e-4 * np.abs(ref_z[b]).max() if dtype == synth.F32 else 0.1
+        print(f"seq {b}: max|dlogit| {err:.3e}")
+        assert err <= tol
+        picked = ref_z[b][np.arange(steps + 1), toks[b]]
+        assert np.all(picked >= ref_z[b].max(-1) - band)
