@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "49d702f434eddca34e9e91697ad2ba3126cdaac93698ab30096ae7702552470b",
-                "bytes": 2000845672}
+HEAD_TRAFFIC = {"gemm_src_sha256": "3ca3681855eee3813872603b943aa16c3ae2cda71282ed0115ae457fa115fb07",
+                "bytes": 2004988441}
 
 
 def src_sha(rel):
@@ -52,10 +52,15 @@ def src_sha(rel):
 
 def forward_flops(cfg, B, T):
     """Algorithmic FLOPs: 2MNK for c_attn, c_proj, c_fc, mlp.c_proj and the tied
-    head, plus causal attention 4*D*B*H*T(T+1)/2 (the masked half excluded)."""
+    head, plus causal attention 4*D*B*H*T(T+1)/2 (the masked half excluded).
+    LLaMA-style blocks: W_q|W_k|W_v (N = C + 2 Hkv D), W_o, the gate/up
+    product (N = 2F) and the down projection."""
     M, C, F, V, L, H = B * T, cfg.n_embd, cfg.n_ff, cfg.vocab, cfg.n_layer, cfg.n_head
     D = C // H
-    gemm = 2 * M * C * (3 * C + C + F + F) * L
+    if getattr(cfg, "arch", 0) == 1:
+        gemm = 2 * M * C * ((C + 2 * cfg.kv_heads * D) + C + 2 * F + F) * L
+    else:
+        gemm = 2 * M * C * (3 * C + C + F + F) * L
     head = 2 * M * V * C
     attn = 4 * D * B * H * T * (T + 1) // 2 * L
     return gemm + head + attn, head
@@ -226,9 +231,41 @@ def bench_forward(args, w):
     }
     if args.workload == 3:
         out["head_backward"] = bench_head_backward(cfg, B, T, dev_params, idx, stream)
+        out["llama"] = bench_llama_forward(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_forward(cfg, params, ids, args.cpu_seqs)
     return out
+
+
+def bench_llama_forward(args):
+    """Forward + loss of the LLaMA-style model at the GPT-2 width (no logits
+    written): time per step, tokens/s and the fraction of the bf16 MFMA peak."""
+    import torch
+    from decoder_only_transformer_attn_amd import lib, synth
+    w = synth.WORKLOADS[6]
+    cfg, B, T = w["cfg"], w["B"], w["T"]
+    params = synth.make_params(cfg, seed=42, cfg_id=6)
+    dev_params = lib.params_to_device(cfg, synth.pack(cfg, params))
+    idx = torch.from_numpy(synth.make_ids(cfg, B, T, seed=42, cfg_id=6)).cuda()
+    fwd = lib.Forward(cfg, B, T, want_logits=False)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        fwd(dev_params, idx)
+    torch.cuda.synchronize()
+    K = max(1, args.steps // 2)
+    ev = Events(2)
+    ev.record(0, stream.cuda_stream)
+    for _ in range(K):
+        fwd(dev_params, idx)
+    ev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / K
+    ev.close()
+    flops, _ = forward_flops(cfg, B, T)
+    return {"workload": w["name"], "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "loss": round(float(fwd.mean_loss.item()), 5)}
 
 
 def bench_head_backward(cfg, B, T, dev_params, idx, stream, reps=10):

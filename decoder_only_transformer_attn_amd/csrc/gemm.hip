@@ -1411,7 +1411,10 @@ static hipError_t run_gemm_dma(const bf16* A, const bf16* W, int M, int N, const
 // tiles, 3072: 1024, 768: 256); 256 x 256 (8 waves of 64 x 128) otherwise.
 template <int K, typename Epi>
 static hipError_t run_gemm_dma_k(const bf16* A, const bf16* W, int M, int N, const Epi& epi, hipStream_t st) {
-  if (N % 192 == 0) {
+  // 128 x 192 also when 256 x 256 tiles could not fill the 256 CUs (a ragged
+  // last column tile is cheaper than idle CUs, e.g. N = 1280)
+  const long long blocks256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  if (N % 192 == 0 || blocks256 < 256) {
     // 8 waves of 32 x 96; 64-deep stages.  Short K with an epilogue that keeps
     // little in registers across the main loop (kCompact): two stages (80 KB)
     // and two blocks per CU (128 registers per lane); otherwise three stages
@@ -1430,6 +1433,7 @@ static hipError_t dispatch_gemm_tiled(const bf16* A, int lda, const bf16* W, int
   const long long tiles256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= 64 && lda == K && ldw == K) {
     if (K == 768) return run_gemm_dma_k<768>(A, W, M, N, epi, st);
+    if (K == 2048) return run_gemm_dma_k<2048>(A, W, M, N, epi, st);   // SwiGLU down projection at F = 8/3 C
     if (K == 3072) return run_gemm_dma_k<3072>(A, W, M, N, epi, st);
   }
   if (tiles256 >= 192) return run_gemm<bf16, 256, 256, 64, 128, 64>(A, lda, W, ldw, M, N, K, epi, st);

@@ -66,6 +66,10 @@ MICRO = GPTConfig(vocab=17, ctx=12, n_embd=16, n_head=2, n_layer=2, n_ff=64, dty
 MINI = GPTConfig(vocab=5000, ctx=128, n_embd=128, n_head=4, n_layer=4, n_ff=512, dtype=F32)
 GPT2 = GPTConfig(vocab=50257, ctx=1024, n_embd=768, n_head=12, n_layer=12, n_ff=3072, dtype=BF16)
 GPT2_F32 = dataclasses.replace(GPT2, dtype=F32)
+# LLaMA-style blocks at the GPT-2 width: 12 query heads sharing 4 K/V heads,
+# SwiGLU width 8/3 C = 2048, tied head over the GPT-2 vocabulary
+LLAMA_124 = GPTConfig(vocab=50257, ctx=1024, n_embd=768, n_head=12, n_layer=12, n_ff=2048, dtype=BF16, arch=1,
+                      n_kv_head=4)
 
 WORKLOADS = {
     1: dict(cfg=MICRO, B=4, T=12, name="micro-fp32 V17 C16 H2 L2 B4 T12"),
@@ -73,6 +77,7 @@ WORKLOADS = {
     3: dict(cfg=GPT2, B=8, T=1024, name="gpt2-124M-bf16 B8 T1024 fwd+loss"),
     4: dict(cfg=GPT2, B=32, T=1024, name="gpt2-124M-bf16 B32 T1024 fused CE, no logits"),
     5: dict(cfg=GPT2, B=64, T=128, name="gpt2-124M-bf16 decode B64 prompt128 +128 greedy"),
+    6: dict(cfg=LLAMA_124, B=8, T=1024, name="llama-style-bf16 C768 H12 KV4 L12 F2048 B8 T1024 fwd+loss"),
 }
 
 LAYER_FIELDS = ("ln1_g", "ln1_b", "attn_w", "attn_b", "proj_w", "proj_b",
