@@ -28,11 +28,17 @@ Derivatives used (standard calculus, no page prints them):
   * x0[b, t] = E[idx[b, t]] + P[t]  =>  dE[v] += sum of dx0 over the positions
     holding token v, dP[t] = sum over the batch of dx0[:, t].
 
+  * a block (pre-LN GPT-2): the same rules through both residual paths,
+    the two LayerNorms, the GELU (tanh form: derivative of 0.5 z (1 + tanh u)),
+    the projections and each causal head: dU = P^T dY, dP = dY U^T,
+    dS = P * (dP - rowsum(dP * P)), dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D).
+
 Pinned by tests/test_oracle_grad.py against central finite differences of the
 forward oracle's loss, torch float64 autograd, invariants and planted mistakes.
 """
 from __future__ import annotations
 
+import math
 from typing import Optional
 
 import numpy as np
@@ -134,4 +140,112 @@ def grads_no_blocks(params: dict, idx: np.ndarray, targets: Optional[np.ndarray]
         g["wte"] = dE + hb["head"]
     if "lnf_g" in hb:
         g["lnf_g"], g["lnf_b"] = hb["lnf_g"], hb["lnf_b"]
+    return g
+
+
+# ----------------------------------------------------------------------------
+# Block backward (pre-LN GPT-2 blocks)
+# ----------------------------------------------------------------------------
+def gelu_tanh_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of 0.5 z (1 + tanh u), u = sqrt(2/pi) (z + 0.044715 z^3)."""
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (z + 0.044715 * z ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * c * (1.0 + 3 * 0.044715 * z * z)
+
+
+def gelu_erf_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of z Phi(z) = Phi(z) + z phi(z)."""
+    from scipy.special import erf
+    return 0.5 * (1.0 + erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, u: np.ndarray, dy: np.ndarray):
+    """One causal head y = softmax(q k^T / sqrt(D) + M) u: returns (dq, dk, du).
+    With P the softmax: du = P^T dy; dP = dy u^T; dS = P * (dP - rowsum(dP * P));
+    dq = dS k / sqrt(D); dk = dS^T q / sqrt(D)."""
+    T, D = q.shape
+    s = (q @ k.T) / math.sqrt(D)
+    s = np.where(np.triu(np.ones((T, T), dtype=bool), k=1), -np.inf, s)
+    p = O.softmax_rows(s)
+    du = p.T @ dy
+    dp = dy @ u.T
+    ds = p * (dp - (dp * p).sum(axis=-1, keepdims=True))
+    return ds @ k / math.sqrt(D), ds.T @ q / math.sqrt(D), du
+
+
+def block_backward(x: np.ndarray, lp: dict, dy: np.ndarray, n_head: int, eps: float = 1e-5,
+                   act: str = "tanh"):
+    """Gradient of a pre-norm block out = x1 + mlp(LN2(x1)), x1 = x + attn(LN1(x))
+    for the upstream dy = d loss / d out.  x, dy [B, T, C].  Recomputes the
+    block's forward, then applies the chain rule in reverse.  Returns (dx,
+    grads keyed like lp)."""
+    B, T, C = x.shape
+    D = C // n_head
+    g = {}
+    a1 = O.layer_norm(x, lp["ln1_g"], lp["ln1_b"], eps)
+    qkv = O.linear(a1, lp["attn_w"], lp["attn_b"])
+    heads = lambda z: z.reshape(B, T, n_head, D).transpose(0, 2, 1, 3)
+    qh, kh, uh = heads(qkv[..., :C]), heads(qkv[..., C:2 * C]), heads(qkv[..., 2 * C:])
+    yh = np.empty_like(qh)
+    for b in range(B):
+        for h in range(n_head):
+            yh[b, h] = O.causal_attention(qh[b, h], kh[b, h], uh[b, h])
+    o = yh.transpose(0, 2, 1, 3).reshape(B, T, C)
+    x1 = x + O.linear(o, lp["proj_w"], lp["proj_b"])
+    a2 = O.layer_norm(x1, lp["ln2_g"], lp["ln2_b"], eps)
+    z = O.linear(a2, lp["fc_w"], lp["fc_b"])
+    hmid = O.activation(z, act)
+    flat = lambda t: t.reshape(-1, t.shape[-1])
+    # MLP
+    g["fcproj_w"] = flat(dy).T @ flat(hmid)
+    g["fcproj_b"] = flat(dy).sum(axis=0)
+    dz = (dy @ lp["fcproj_w"]) * (gelu_erf_grad(z) if act == "erf" else gelu_tanh_grad(z))
+    g["fc_w"] = flat(dz).T @ flat(a2)
+    g["fc_b"] = flat(dz).sum(axis=0)
+    dx1_ln, g["ln2_g"], g["ln2_b"] = layer_norm_backward(x1, lp["ln2_g"], dz @ lp["fc_w"], eps)
+    dx1 = dy + dx1_ln
+    # attention
+    g["proj_w"] = flat(dx1).T @ flat(o)
+    g["proj_b"] = flat(dx1).sum(axis=0)
+    doh = heads(dx1 @ lp["proj_w"])
+    dq, dk, du = np.empty_like(qh), np.empty_like(kh), np.empty_like(uh)
+    for b in range(B):
+        for h in range(n_head):
+            dq[b, h], dk[b, h], du[b, h] = attention_backward(qh[b, h], kh[b, h], uh[b, h], doh[b, h])
+    merge = lambda t: t.transpose(0, 2, 1, 3).reshape(B, T, C)
+    dqkv = np.concatenate([merge(dq), merge(dk), merge(du)], axis=-1)
+    g["attn_w"] = flat(dqkv).T @ flat(a1)
+    g["attn_b"] = flat(dqkv).sum(axis=0)
+    dx_ln, g["ln1_g"], g["ln1_b"] = layer_norm_backward(x, lp["ln1_g"], dqkv @ lp["attn_w"], eps)
+    return dx1 + dx_ln, g
+
+
+def grads_full(params: dict, idx: np.ndarray, n_head: int, targets: Optional[np.ndarray] = None,
+               eps: float = 1e-5) -> dict:
+    """Every parameter gradient of the mean next-token loss of a pre-LN GPT-2
+    model: forward keeping each block's input, head backward, the blocks in
+    reverse, then the embeddings (the tied table's two shares summed, [P2]
+    §25.4).  Returns {"wte", "wpe", "layers": [grads per block], "lnf_g",
+    "lnf_b", "head_w" (untied), "loss"}."""
+    if params.get("norm", "pre") != "pre":
+        raise ValueError("pre-LN blocks only")
+    idx = np.asarray(idx)
+    B, T = idx.shape
+    act = params.get("act", "tanh")
+    y = O.derived_targets(idx) if targets is None else np.asarray(targets, dtype=np.int64)
+    xs = [O.embed(params, idx)]
+    for lp in params["layers"]:
+        xs.append(O.block(xs[-1], lp, n_head, eps, act=act))
+    C = xs[0].shape[-1]
+    hb = head_backward(params, xs[-1].reshape(B * T, C), y.reshape(B * T), eps)
+    dx = hb["dx"].reshape(B, T, C)
+    layers = [None] * len(params["layers"])
+    for l in range(len(params["layers"]) - 1, -1, -1):
+        dx, layers[l] = block_backward(xs[l], params["layers"][l], dx, n_head, eps, act)
+    dE, dP = embedding_backward(idx, dx, params["wte"].shape[0], params["wpe"].shape[0])
+    g = {"wpe": dP, "layers": layers, "lnf_g": hb["lnf_g"], "lnf_b": hb["lnf_b"], "loss": hb["loss"]}
+    if "head_w" in params:
+        g["wte"], g["head_w"] = dE, hb["head"]
+    else:
+        g["wte"] = dE + hb["head"]
     return g

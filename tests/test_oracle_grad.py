@@ -211,3 +211,158 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         with monkeypatch.context() as m:
             m.setattr(G, name, fn)
             assert not _pins_pass(), f"planted mistake {fn.__name__} went unnoticed"
+
+
+# --------------------------------------------------------------------------
+# block backward and the full model
+# --------------------------------------------------------------------------
+BLK = synth.GPTConfig(vocab=23, ctx=12, n_embd=16, n_head=2, n_layer=2, n_ff=48)
+
+
+def _block_f(x, lp, dy, act="tanh"):
+    return float((dy * O.block(x, lp, BLK.n_head, 1e-5, act=act)).sum())
+
+
+@pytest.mark.parametrize("act", ["tanh", "erf"])
+def test_block_backward_matches_finite_differences(act):
+    P = _P(dc.replace(BLK, act=1 if act == "erf" else 0), seed=12)
+    lp = P["layers"][0]
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 1.5, (2, 7, BLK.n_embd))
+    dy = rng.normal(0, 1, x.shape)
+    dx, g = G.block_backward(x, lp, dy, BLK.n_head, 1e-5, act)
+    h = 1e-5
+    for idx in [(0, 0, 0), (1, 6, 15), (0, 3, 7), (1, 2, 9)]:
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd = (_block_f(xp, lp, dy, act) - _block_f(xm, lp, dy, act)) / (2 * h)
+        assert abs(dx[idx] - fd) < 1e-7 * max(1.0, abs(fd)), ("x", idx)
+    for key, arr in lp.items():
+        for e in _entries(arr.shape, rng, n=3):
+            old = arr[e]
+            arr[e] = old + h
+            fp = _block_f(x, lp, dy, act)
+            arr[e] = old - h
+            fm = _block_f(x, lp, dy, act)
+            arr[e] = old
+            fd = (fp - fm) / (2 * h)
+            assert abs(g[key][e] - fd) < 1e-7 * max(1.0, abs(fd)), (key, e, g[key][e], fd)
+
+
+def test_attention_backward_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(13)
+    q, k, u, dy = (rng.normal(size=(9, 8)) for _ in range(4))
+    tq, tk, tu = (torch.tensor(a, requires_grad=True) for a in (q, k, u))
+    y = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tu[None], is_causal=True)[0]
+    y.backward(torch.from_numpy(dy))
+    for got, t in zip(G.attention_backward(q, k, u, dy), (tq, tk, tu)):
+        np.testing.assert_allclose(got, t.grad.numpy(), atol=1e-13)
+
+
+def test_gelu_grads_match_torch():
+    torch = pytest.importorskip("torch")
+    z = torch.linspace(-6, 6, 241, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.gelu(z, approximate="tanh").sum().backward()
+    np.testing.assert_allclose(G.gelu_tanh_grad(z.detach().numpy()), z.grad.numpy(), atol=1e-14)
+    z.grad = None
+    torch.nn.functional.gelu(z).sum().backward()
+    np.testing.assert_allclose(G.gelu_erf_grad(z.detach().numpy()), z.grad.numpy(), atol=1e-14)
+
+
+def test_full_gradients_match_finite_differences():
+    P = _P(BLK, seed=14)
+    idx = synth.make_ids(BLK, 2, 8, seed=14)
+    g = G.grads_full(P, idx, BLK.n_head)
+    assert abs(g["loss"] - _loss(P, idx)) < 1e-12
+    rng = np.random.default_rng(14)
+    h = 1e-5
+    for key in ("wte", "wpe", "lnf_g", "lnf_b"):
+        ent = _entries(P[key].shape, rng, n=4)
+        np.testing.assert_allclose([g[key][e] for e in ent], _fd(P, idx, key, ent), rtol=1e-6, atol=1e-9,
+                                   err_msg=key)
+    for l in range(BLK.n_layer):
+        lp = P["layers"][l]
+        for key, arr in lp.items():
+            for e in _entries(arr.shape, rng, n=2):
+                old = arr[e]
+                arr[e] = old + h
+                lp_ = _loss(P, idx)
+                arr[e] = old - h
+                lm = _loss(P, idx)
+                arr[e] = old
+                fd = (lp_ - lm) / (2 * h)
+                assert abs(g["layers"][l][key][e] - fd) < 1e-6 * max(1e-3, abs(fd)) + 1e-9, (l, key, e)
+
+
+def test_full_gradients_match_torch_autograd():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    P = _P(BLK, seed=15)
+    idx = synth.make_ids(BLK, 2, 9, seed=15)
+    g = G.grads_full(P, idx, BLK.n_head)
+    T = {k: torch.tensor(v, requires_grad=True) for k, v in P.items() if isinstance(v, np.ndarray)}
+    L = [{k: torch.tensor(v, requires_grad=True) for k, v in lp.items()} for lp in P["layers"]]
+    B, Tn, C, H = 2, 9, BLK.n_embd, BLK.n_head
+    x = F.embedding(torch.from_numpy(idx), T["wte"]) + T["wpe"][:Tn]
+    for lp in L:
+        a = F.layer_norm(x, (C,), lp["ln1_g"], lp["ln1_b"], 1e-5)
+        q, k, v = F.linear(a, lp["attn_w"], lp["attn_b"]).split(C, dim=-1)
+        sh = lambda z: z.view(B, Tn, H, C // H).transpose(1, 2)
+        y = F.scaled_dot_product_attention(sh(q), sh(k), sh(v), is_causal=True).transpose(1, 2).reshape(B, Tn, C)
+        x = x + F.linear(y, lp["proj_w"], lp["proj_b"])
+        a = F.layer_norm(x, (C,), lp["ln2_g"], lp["ln2_b"], 1e-5)
+        x = x + F.linear(F.gelu(F.linear(a, lp["fc_w"], lp["fc_b"]), approximate="tanh"), lp["fcproj_w"],
+                         lp["fcproj_b"])
+    z = F.linear(F.layer_norm(x, (C,), T["lnf_g"], T["lnf_b"], 1e-5), T["wte"])
+    F.cross_entropy(z.reshape(-1, BLK.vocab), torch.from_numpy(O.derived_targets(idx)).reshape(-1),
+                    ignore_index=-1).backward()
+    for key in ("wte", "wpe", "lnf_g", "lnf_b"):
+        np.testing.assert_allclose(g[key], T[key].grad.numpy(), rtol=1e-9, atol=1e-12, err_msg=key)
+    for l in range(BLK.n_layer):
+        for key, t in L[l].items():
+            np.testing.assert_allclose(g["layers"][l][key], t.grad.numpy(), rtol=1e-9, atol=1e-12,
+                                       err_msg=f"{l}.{key}")
+
+
+def _block_pins_pass():
+    try:
+        test_block_backward_matches_finite_differences("tanh")
+        test_attention_backward_matches_torch()
+        test_gelu_grads_match_torch()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_block_pins_catch_planted_mistakes(monkeypatch):
+    pytest.importorskip("torch")
+    assert _block_pins_pass()
+    orig_attn, orig_blk = G.attention_backward, G.block_backward
+
+    def attn_without_rowsum(q, k, u, dy):
+        T, D = q.shape
+        s = np.where(np.triu(np.ones((T, T), dtype=bool), k=1), -np.inf, (q @ k.T) / np.sqrt(D))
+        p = O.softmax_rows(s)
+        ds = p * (dy @ u.T)
+        return ds @ k / np.sqrt(D), ds.T @ q / np.sqrt(D), p.T @ dy
+
+    def gelu_grad_one(z):
+        return np.ones_like(z)
+
+    def blk_dropping_residual(x, lp, dy, n_head, eps=1e-5, act="tanh"):
+        dx, g = orig_blk(x, lp, dy, n_head, eps, act)
+        return dx - dy, g
+
+    def blk_bias_sign_flipped(x, lp, dy, n_head, eps=1e-5, act="tanh"):
+        dx, g = orig_blk(x, lp, dy, n_head, eps, act)
+        g = dict(g)
+        g["fcproj_b"] = -g["fcproj_b"]
+        return dx, g
+
+    for name, fn in [("attention_backward", attn_without_rowsum), ("gelu_tanh_grad", gelu_grad_one),
+                     ("block_backward", blk_dropping_residual), ("block_backward", blk_bias_sign_flipped)]:
+        with monkeypatch.context() as m:
+            m.setattr(G, name, fn)
+            assert not _block_pins_pass(), f"planted mistake {fn.__name__} went unnoticed"
