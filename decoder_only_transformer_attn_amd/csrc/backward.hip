@@ -13,6 +13,7 @@
 // with gd = dy * g;  dg = sum_rows dy * xh;  db = sum_rows dy.
 // Every sum runs in a fixed order, so results are bit-reproducible.
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 #include "kernels.h"
@@ -114,7 +115,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) ln_bwd_rows_kernel(int M, int C, const float* __restrict__ x,
                                                           const T* __restrict__ g, const float* __restrict__ dy,
                                                           float eps, float* __restrict__ dx, float* __restrict__ mu,
-                                                          float* __restrict__ rs) {
+                                                          float* __restrict__ rs, int accumulate) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;   // (no block-wide barrier below)
@@ -141,7 +142,7 @@ __global__ void __launch_bounds__(256) ln_bwd_rows_kernel(int M, int C, const fl
   for (int c = lane; c < C; c += 64) {
     const float xh = (xr[c] - mean) * rstd;
     const float gd = dr[c] * to_f32(g[c]);
-    o[c] = rstd * (gd - m1 - xh * m2);
+    o[c] = (accumulate ? o[c] : 0.f) + rstd * (gd - m1 - xh * m2);
   }
   if (lane == 0) {
     mu[m] = mean;
@@ -297,13 +298,14 @@ hipError_t launch_cast_rows(int dtype, const float* x, long long n, void* out, h
 int ln_bwd_chunks(int M) { return (M + LNB_CHUNK - 1) / LNB_CHUNK; }
 
 hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const void* g, const float* dy, float eps,
-                              float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st) {
+                              float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st,
+                              int accumulate) {
   if (dtype == 0)
     hipLaunchKernelGGL(ln_bwd_rows_kernel<float>, dim3((M + 3) / 4), dim3(256), 0, st, M, C, x, (const float*)g, dy,
-                       eps, dx, mu, rs);
+                       eps, dx, mu, rs, accumulate);
   else
     hipLaunchKernelGGL(ln_bwd_rows_kernel<bf16>, dim3((M + 3) / 4), dim3(256), 0, st, M, C, x, (const bf16*)g, dy,
-                       eps, dx, mu, rs);
+                       eps, dx, mu, rs, accumulate);
   const int nch = ln_bwd_chunks(M);
   hipLaunchKernelGGL(ln_bwd_cols_kernel, dim3((C + 63) / 64, nch), dim3(256), 0, st, M, C, x, dy, (const float*)mu,
                      (const float*)rs, part);
@@ -316,6 +318,317 @@ hipError_t launch_embed_backward(const int32_t* idx, int B, int T, int C, int V,
   const int N = B * T;
   hipLaunchKernelGGL(embed_bwd_tok_kernel, dim3(N), dim3(256), 0, st, idx, N, C, V, dx0, dwte);
   if (dwpe) hipLaunchKernelGGL(embed_bwd_pos_kernel, dim3(T, (C + 255) / 256), dim3(256), 0, st, B, T, C, dx0, dwpe);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block backward: element-wise parts and the attention backward
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float gelu_tanh_f(float z) {
+  const float u = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+  return 0.5f * z * (1.0f + tanhf(u));
+}
+__device__ __forceinline__ float gelu_tanh_d(float z) {   // d/dz 0.5 z (1 + tanh u)
+  const float u = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+  const float t = tanhf(u);
+  return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * 0.7978845608028654f * (1.0f + 0.134145f * z * z);
+}
+__device__ __forceinline__ float gelu_erf_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.7071067811865476f)); }
+__device__ __forceinline__ float gelu_erf_d(float z) {    // Phi(z) + z phi(z)
+  return 0.5f * (1.0f + erff(z * 0.7071067811865476f)) + z * 0.3989422804014327f * __expf(-0.5f * z * z);
+}
+
+// h = GELU(u) (act 0: tanh form, 1: exact)
+template <typename T>
+__global__ void __launch_bounds__(256) act_fwd_kernel(const T* __restrict__ u, long long n, int act, T* __restrict__ h) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+    const float z = to_f32(u[e]);
+    h[e] = from_f32<T>(act ? gelu_erf_f(z) : gelu_tanh_f(z));
+  }
+}
+
+// d (fp32, in place) *= GELU'(u); dc = d in the compute dtype
+template <typename T>
+__global__ void __launch_bounds__(256) act_bwd_kernel(float* __restrict__ d, const T* __restrict__ u, long long n,
+                                                      int act, T* __restrict__ dc) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+    const float z = to_f32(u[e]);
+    const float v = d[e] * (act ? gelu_erf_d(z) : gelu_tanh_d(z));
+    d[e] = v;
+    dc[e] = from_f32<T>(v);
+  }
+}
+
+// Column sums of an fp32 [M, N] matrix into per-chunk partials (fixed order),
+// then out[n] += sum of the partials in chunk order.
+__global__ void __launch_bounds__(256) colsum_part_kernel(int M, int N, const float* __restrict__ a,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + tx;
+  const int r0 = blockIdx.y * LNB_CHUNK, r1 = min(M, r0 + LNB_CHUNK);
+  float s = 0.f;
+  if (c < N)
+    for (int r = r0 + ty; r < r1; r += 4) s += a[(long long)r * N + c];
+  red[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && c < N) part[(long long)blockIdx.y * N + c] = (red[0][tx] + red[1][tx]) + (red[2][tx] + red[3][tx]);
+}
+
+__global__ void __launch_bounds__(256) colsum_final_kernel(int N, int nchunks, const float* __restrict__ part,
+                                                           float* __restrict__ out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= N) return;
+  float s = 0.f;
+  for (int k = 0; k < nchunks; ++k) s += part[(long long)k * N + c];
+  out[c] += s;
+}
+
+// Attention backward for causal heads, scores s = q.k / sqrt(D), P = softmax
+// over keys <= t.  With lse_t = log sum_j e^{s_tj} and Dt = sum_d dO[t,d] O[t,d]
+// (= sum_j P_tj dP_tj): dV_j = sum_t P_tj dO_t, dS_tj = P_tj (dO_t.V_j - Dt),
+// dQ_t = sum_j dS_tj K_j / sqrt(D), dK_j = sum_t dS_tj Q_t / sqrt(D).
+// One thread per row (query or key) holds its vectors in registers (DM >= D,
+// fully unrolled loops); the other side's rows stream through LDS tiles in
+// fp32.  Q, K, U are head-major [B, H, T, D]; O (compute dtype) and dO (fp32)
+// are [B*T, C] with head h at columns [hD, hD+D); dQKV is fp32 [B*T, 3C]
+// (q, k, u column blocks).  All sums run in a fixed order.
+constexpr int AB_ROWS = 256;   // rows (threads) per block
+constexpr int AB_TILE = 32;    // rows of the other side per LDS tile
+
+struct AttnBwdArgs {
+  const void* q; const void* k; const void* u;   // [B, H, T, D]
+  const void* o;                                  // [B*T, C]
+  const float* dout;                              // [B*T, C]
+  float* lse; float* dd;                          // [B*H*T]
+  float* dqkv;                                    // [B*T, 3C]
+  int B, H, T, D;
+  float scale;                                    // 1 / sqrt(D)
+};
+
+template <typename T, int DM>
+__device__ __forceinline__ void load_row(const T* __restrict__ p, int D, float (&r)[DM]) {
+#pragma unroll
+  for (int d = 0; d < DM; ++d) r[d] = d < D ? to_f32(p[d]) : 0.f;
+}
+
+// lse and Dt per query row
+template <typename T, int DM>
+__global__ void __launch_bounds__(AB_ROWS) attn_bwd_prep_kernel(AttnBwdArgs a) {
+  __shared__ float sk[AB_TILE][DM];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  const int t = blockIdx.y * AB_ROWS + threadIdx.x;
+  const int D = a.D, C = a.H * D, T_ = a.T;
+  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * T_ * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * T_ * D;
+  float q[DM];
+  if (t < T_) load_row<T, DM>(Q + (long long)t * D, D, q);
+  else
+#pragma unroll
+    for (int d = 0; d < DM; ++d) q[d] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int tmax = min(T_ - 1, blockIdx.y * AB_ROWS + AB_ROWS - 1);
+  for (int j0 = 0; j0 <= tmax; j0 += AB_TILE) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < AB_TILE * DM; e += AB_ROWS) {
+      const int r = e / DM, d = e - r * DM;
+      sk[r][d] = (j0 + r < T_ && d < D) ? to_f32(K[(long long)(j0 + r) * D + d]) : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < AB_TILE; ++r) {
+      const int j = j0 + r;
+      if (t < T_ && j <= t) {
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < DM; ++d) s = fmaf(q[d], sk[r][d], s);
+        s *= a.scale;
+        if (s > m) { l = l * __expf(m - s) + 1.f; m = s; }
+        else l += __expf(s - m);
+      }
+    }
+  }
+  if (t < T_) {
+    a.lse[(long long)bh * T_ + t] = m + __logf(l);
+    const T* orow = reinterpret_cast<const T*>(a.o) + ((long long)b * T_ + t) * C + h * D;
+    const float* drow = a.dout + ((long long)b * T_ + t) * C + h * D;
+    float dd = 0.f;
+    for (int d = 0; d < D; ++d) dd = fmaf(drow[d], to_f32(orow[d]), dd);
+    a.dd[(long long)bh * T_ + t] = dd;
+  }
+}
+
+// dQ: thread = query row t, keys j <= t in tiles
+template <typename T, int DM>
+__global__ void __launch_bounds__(AB_ROWS) attn_bwd_dq_kernel(AttnBwdArgs a) {
+  __shared__ float sk[AB_TILE][DM];
+  __shared__ float su[AB_TILE][DM];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  const int t = blockIdx.y * AB_ROWS + threadIdx.x;
+  const int D = a.D, C = a.H * D, T_ = a.T;
+  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * T_ * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * T_ * D;
+  const T* U = reinterpret_cast<const T*>(a.u) + (long long)bh * T_ * D;
+  const bool live = t < T_;
+  float q[DM], go[DM], dq[DM];
+#pragma unroll
+  for (int d = 0; d < DM; ++d) { q[d] = 0.f; go[d] = 0.f; dq[d] = 0.f; }
+  float lse = 0.f, dd = 0.f;
+  if (live) {
+    load_row<T, DM>(Q + (long long)t * D, D, q);
+    const float* drow = a.dout + ((long long)b * T_ + t) * C + h * D;
+#pragma unroll
+    for (int d = 0; d < DM; ++d) go[d] = d < D ? drow[d] : 0.f;
+    lse = a.lse[(long long)bh * T_ + t];
+    dd = a.dd[(long long)bh * T_ + t];
+  }
+  const int tmax = min(T_ - 1, blockIdx.y * AB_ROWS + AB_ROWS - 1);
+  for (int j0 = 0; j0 <= tmax; j0 += AB_TILE) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < AB_TILE * DM; e += AB_ROWS) {
+      const int r = e / DM, d = e - r * DM;
+      const bool in = j0 + r < T_ && d < D;
+      sk[r][d] = in ? to_f32(K[(long long)(j0 + r) * D + d]) : 0.f;
+      su[r][d] = in ? to_f32(U[(long long)(j0 + r) * D + d]) : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < AB_TILE; ++r) {
+      const int j = j0 + r;
+      if (live && j <= t) {
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < DM; ++d) {
+          s = fmaf(q[d], sk[r][d], s);
+          dp = fmaf(go[d], su[r][d], dp);
+        }
+        const float p = __expf(s * a.scale - lse);
+        const float ds = p * (dp - dd);
+#pragma unroll
+        for (int d = 0; d < DM; ++d) dq[d] = fmaf(ds, sk[r][d], dq[d]);
+      }
+    }
+  }
+  if (live) {
+    float* out = a.dqkv + ((long long)b * T_ + t) * (3 * C) + h * D;
+#pragma unroll
+    for (int d = 0; d < DM; ++d)
+      if (d < D) out[d] = dq[d] * a.scale;
+  }
+}
+
+// dK (WHICH 0) or dU (WHICH 1): thread = key row j, queries t >= j in tiles
+template <typename T, int DM, int WHICH>
+__global__ void __launch_bounds__(AB_ROWS) attn_bwd_dkv_kernel(AttnBwdArgs a) {
+  __shared__ float sq[AB_TILE][DM];
+  __shared__ float sg[AB_TILE][DM];
+  __shared__ float sl[AB_TILE], sd[AB_TILE];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  const int j = blockIdx.y * AB_ROWS + threadIdx.x;
+  const int D = a.D, C = a.H * D, T_ = a.T;
+  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * T_ * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * T_ * D;
+  const T* U = reinterpret_cast<const T*>(a.u) + (long long)bh * T_ * D;
+  const bool live = j < T_;
+  float k[DM], u[DM], acc[DM];
+#pragma unroll
+  for (int d = 0; d < DM; ++d) { k[d] = 0.f; u[d] = 0.f; acc[d] = 0.f; }
+  if (live) {
+    load_row<T, DM>(K + (long long)j * D, D, k);
+    if (WHICH == 0) load_row<T, DM>(U + (long long)j * D, D, u);
+  }
+  const int jmin = blockIdx.y * AB_ROWS;   // the block's first key: queries before it see none of its keys
+  for (int t0 = (jmin / AB_TILE) * AB_TILE; t0 < T_; t0 += AB_TILE) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < AB_TILE * DM; e += AB_ROWS) {
+      const int r = e / DM, d = e - r * DM;
+      const int t = t0 + r;
+      const bool in = t < T_ && d < D;
+      sq[r][d] = in ? to_f32(Q[(long long)t * D + d]) : 0.f;
+      sg[r][d] = in ? a.dout[((long long)b * T_ + t) * C + h * D + d] : 0.f;
+    }
+    if (threadIdx.x < AB_TILE) {
+      const int t = t0 + threadIdx.x;
+      sl[threadIdx.x] = t < T_ ? a.lse[(long long)bh * T_ + t] : 0.f;
+      sd[threadIdx.x] = t < T_ ? a.dd[(long long)bh * T_ + t] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < AB_TILE; ++r) {
+      const int t = t0 + r;
+      if (live && t < T_ && t >= j) {
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < DM; ++d) s = fmaf(sq[r][d], k[d], s);
+        const float p = __expf(s * a.scale - sl[r]);
+        if (WHICH == 1) {
+#pragma unroll
+          for (int d = 0; d < DM; ++d) acc[d] = fmaf(p, sg[r][d], acc[d]);
+        } else {
+          float dp = 0.f;
+#pragma unroll
+          for (int d = 0; d < DM; ++d) dp = fmaf(sg[r][d], u[d], dp);
+          const float ds = p * (dp - sd[r]);
+#pragma unroll
+          for (int d = 0; d < DM; ++d) acc[d] = fmaf(ds, sq[r][d], acc[d]);
+        }
+      }
+    }
+  }
+  if (live) {
+    float* out = a.dqkv + ((long long)b * T_ + j) * (3 * C) + (WHICH == 0 ? C : 2 * C) + h * D;
+    const float f = WHICH == 0 ? a.scale : 1.f;
+#pragma unroll
+    for (int d = 0; d < DM; ++d)
+      if (d < D) out[d] = acc[d] * f;
+  }
+}
+
+template <typename T, int DM>
+static void attn_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
+  const dim3 grid(a.B * a.H, (a.T + AB_ROWS - 1) / AB_ROWS);
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<T, DM>), grid, dim3(AB_ROWS), 0, st, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DM>), grid, dim3(AB_ROWS), 0, st, a);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DM, 0>), grid, dim3(AB_ROWS), 0, st, a);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DM, 1>), grid, dim3(AB_ROWS), 0, st, a);
+}
+
+template <typename T>
+static hipError_t attn_bwd_d(const AttnBwdArgs& a, hipStream_t st) {
+  if (a.D <= 32) attn_bwd_t<T, 32>(a, st);
+  else if (a.D <= 64) attn_bwd_t<T, 64>(a, st);
+  else if (a.D <= 128) attn_bwd_t<T, 128>(a, st);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const void* o,
+                                     const float* dout, float* lse, float* dd, float* dqkv, int B, int H, int T,
+                                     int D, hipStream_t st) {
+  const AttnBwdArgs a{q, k, u, o, dout, lse, dd, dqkv, B, H, T, D, (float)(1.0 / std::sqrt((double)D))};
+  if (dtype == 0) return attn_bwd_d<float>(a, st);
+  return attn_bwd_d<bf16>(a, st);
+}
+
+hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(act_fwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, (const float*)u, n, act, (float*)h);
+  else
+    hipLaunchKernelGGL(act_fwd_kernel<bf16>, dim3(grid_for(n)), dim3(256), 0, st, (const bf16*)u, n, act, (bf16*)h);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int act, void* dc, hipStream_t st) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(act_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, d, (const float*)u, n, act,
+                       (float*)dc);
+  else
+    hipLaunchKernelGGL(act_bwd_kernel<bf16>, dim3(grid_for(n)), dim3(256), 0, st, d, (const bf16*)u, n, act,
+                       (bf16*)dc);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(int M, int N, const float* a, float* part, float* out, hipStream_t st) {
+  const int nch = ln_bwd_chunks(M);
+  hipLaunchKernelGGL(colsum_part_kernel, dim3((N + 63) / 64, nch), dim3(256), 0, st, M, N, a, part);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, st, N, nch, (const float*)part, out);
   return hipGetLastError();
 }
 

@@ -227,6 +227,7 @@ struct Pass {
   Plan pl;
   hipStream_t st;
   void* ev_begin; void* ev_end; int which;   // timing hook
+  float* xs;                 // nullable: each block's input residual [L+1][M][C] (the last: ln_f's input)
 };
 
 hipError_t mark(const Pass& s, int kind, bool last_layer, bool begin) {
@@ -364,9 +365,11 @@ int run_blocks(const Pass& s) {
   la.write_x = post ? 1 : 0;   // post-LN: each LayerNorm also replaces the residual row
 
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  const size_t row_bytes = (size_t)M * C * sizeof(float);
   for (int l = 0; l < L; ++l) {
     const LayerP w = P.layer(l);
     const bool last = l == L - 1;
+    if (s.xs) GPT_TRY(hipMemcpyAsync(s.xs + (size_t)l * M * C, x, row_bytes, hipMemcpyDeviceToDevice, s.st));
     void* kbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.k) : static_cast<char*>(s.kc) + l * cache_layer * es;
     void* vbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.v) : static_cast<char*>(s.vc) + l * cache_layer * es;
     const long long kv_bh = s.mode == FORWARD ? (long long)T * D : (long long)s.Tmax * D;
@@ -422,6 +425,7 @@ int run_blocks(const Pass& s) {
       GPT_TRY(launch_layernorm(dt, la, s.st));
     }
   }
+  if (s.xs) GPT_TRY(hipMemcpyAsync(s.xs + (size_t)L * M * C, x, row_bytes, hipMemcpyDeviceToDevice, s.st));
   return GPT_OK;
 }
 
@@ -485,6 +489,44 @@ BwdPlan bwd_plan(const gpt_config* c, int B, int T) {
   p.mu = take(M * 4);
   p.rs = take(M * 4);
   p.lnpart = take((size_t)p.nchunks * 2 * C * 4);
+  p.total = off;
+  return p;
+}
+
+// Workspace of one block's backward (pre-LN GPT-2 blocks): the recomputed
+// forward (a1, q, k, u, o, x1, a2, u_fc, h), the compute-dtype copies and
+// zero-padded transposes the gradient products read ([rows, Mp] with Mp = M
+// rounded up to 64, and the four weight transposes), and the fp32 gradients
+// of the intermediate tensors.
+struct BlkPlan {
+  size_t a1, q, k, v, o, x1, a2, uf, hm, dyc, dyT, hT, dh, duc, duT, a2T, da, dx1, dx1c, dx1T, oT, dout, dqkv,
+      dqkvc, dqkvT, a1T, lse, dd, wfpT, wfcT, wpT, waT, mu, rs, part, total;
+  int Mp, Fp, C3p, nchunks;
+};
+
+BlkPlan blk_plan(const gpt_config* c, int B, int T) {
+  BlkPlan p{};
+  const size_t M = (size_t)B * T, C = c->n_embd, F = c->n_ff, es = esize(c), H = c->n_head;
+  p.Mp = (int)align_up(M, 64);
+  p.Fp = (int)align_up(F, 64);
+  p.C3p = (int)align_up(3 * C, 64);
+  p.nchunks = ln_bwd_chunks((int)M);
+  const size_t Mp = p.Mp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  p.a1 = take(M * C * es); p.q = take(M * C * es); p.k = take(M * C * es); p.v = take(M * C * es);
+  p.o = take(M * C * es); p.x1 = take(M * C * 4); p.a2 = take(M * C * es); p.uf = take(M * F * es);
+  p.hm = take(M * F * es); p.dyc = take(M * C * es); p.dyT = take(C * Mp * es); p.hT = take(F * Mp * es);
+  p.dh = take(M * F * 4); p.duc = take(M * F * es); p.duT = take(F * Mp * es); p.a2T = take(C * Mp * es);
+  p.da = take(M * C * 4); p.dx1 = take(M * C * 4); p.dx1c = take(M * C * es); p.dx1T = take(C * Mp * es);
+  p.oT = take(C * Mp * es); p.dout = take(M * C * 4); p.dqkv = take(M * 3 * C * 4); p.dqkvc = take(M * 3 * C * es);
+  p.dqkvT = take(3 * C * Mp * es); p.a1T = take(C * Mp * es);
+  p.lse = take(B * H * T * 4); p.dd = take(B * H * T * 4);
+  p.wfpT = take(F * C * es); p.wfcT = take(C * (size_t)p.Fp * es); p.wpT = take(C * C * es);
+  p.waT = take(C * (size_t)p.C3p * es);
+  p.mu = take(M * 4); p.rs = take(M * 4);
+  // column partials: the widest of the sums (3C for the c_attn bias, F for c_fc's, 2C for a LayerNorm)
+  p.part = take((size_t)p.nchunks * (3 * C > F ? 3 * C : F) * 4);
   p.total = off;
   return p;
 }
@@ -739,7 +781,7 @@ int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* 
   if (!post)
     GPT_TRY(launch_ln_backward(dt, M, C, x, P.at(P.lnf_g()), da, cfg->ln_eps, dx, at<float>(ws, pl.mu),
                                at<float>(ws, pl.rs), at<float>(ws, pl.lnpart), grads + P.lnf_g(), grads + P.lnf_b(),
-                               st));
+                               st, 0));
   return GPT_OK;
 }
 
@@ -753,6 +795,139 @@ int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int
   const int64_t wpe = params_of(cfg, nullptr).wpe();   // LLaMA-style models have no position table
   GPT_TRY(launch_embed_backward(idx, B, T, cfg->n_embd, cfg->vocab, dx0, grads, wpe < 0 ? nullptr : grads + wpe,
                                 static_cast<hipStream_t>(stream)));
+  return GPT_OK;
+}
+
+int gpt_forward_train(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                      const int32_t* targets, float* xs, float* mean_loss, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (cfg->arch != 0 || cfg->post_ln != 0) return GPT_ERR_CONFIG;   // pre-LN GPT-2 blocks only
+  if (!params || !idx || !xs || !ws) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
+  if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  if ((long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
+  const Plan pl = plan(cfg, B, T, false);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
+  Pass ps{cfg, params_of(cfg, params), idx, B, T, FORWARD, nullptr, nullptr, nullptr, T, ws, pl,
+          static_cast<hipStream_t>(stream), nullptr, nullptr, -1, xs};
+  s = run_blocks(ps);
+  if (s != GPT_OK) return s;
+  const int M = B * T, V = cfg->vocab, C = cfg->n_embd;
+  void* a = at<char>(ws, pl.a);
+  if (!rows_final(cfg)) {
+    s = final_norm(ps, M, 1, 0, a);
+    if (s != GPT_OK) return s;
+  }
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), M, V, C, nullptr, V, at<float>(ws, pl.pmax),
+                         at<float>(ws, pl.psum), at<float>(ws, pl.tgt), nullptr, targets, idx, T, ps.st));
+  GPT_TRY(launch_ce_reduce(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), at<float>(ws, pl.tgt),
+                           targets, idx, T, V, at<float>(ws, pl.tok), at<double>(ws, pl.bsum), mean_loss, ps.st));
+  return GPT_OK;
+}
+
+int gpt_block_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (cfg->arch != 0 || cfg->post_ln != 0) return GPT_ERR_CONFIG;
+  if (!bytes) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0 || (long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
+  if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  *bytes = blk_plan(cfg, B, T).total;
+  return GPT_OK;
+}
+
+int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int B, int T, const float* x,
+                       const float* dy, float* dx, float* grads, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (cfg->arch != 0 || cfg->post_ln != 0) return GPT_ERR_CONFIG;
+  if (!params || !x || !dy || !dx || !grads || !ws) return GPT_ERR_NULL;
+  if (layer < 0 || layer >= cfg->n_layer) return GPT_ERR_SHAPE;
+  if (B <= 0 || T <= 0 || (long long)B * T > BWD_MAX_ROWS) return GPT_ERR_SHAPE;
+  if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
+  const BlkPlan pl = blk_plan(cfg, B, T);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
+  const Params P = params_of(cfg, params);
+  const LayerP w = P.layer(layer);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = cfg->dtype, M = B * T, C = cfg->n_embd, F = cfg->n_ff, H = cfg->n_head, D = C / H;
+  const int Mp = pl.Mp, act = cfg->activation;
+  const size_t rowf = (size_t)M * C * 4;
+  auto W = [&](size_t off) { return at<char>(ws, off); };
+  auto Wf = [&](size_t off) { return at<float>(ws, off); };
+
+  // ---- recompute the block's forward from its input x
+  LnArgs la{};
+  la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps; la.in_mul = 1; la.in_add = 0;
+  la.x = const_cast<float*>(x); la.g = P.at(w.ln1_g); la.b = P.at(w.ln1_b); la.out = W(pl.a1);   // read only
+  GPT_TRY(launch_layernorm(dt, la, st));
+  QKVArgs qa{};
+  qa.A = W(pl.a1); qa.W = P.at(w.attn_w); qa.bias = P.at(w.attn_b);
+  qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
+  qa.q = W(pl.q); qa.q_bh = (long long)T * D; qa.k = W(pl.k); qa.k_bh = (long long)T * D;
+  qa.v = W(pl.v); qa.v_bh = (long long)T * D; qa.pos = nullptr; qa.Tk = T; qa.Hkv = H; qa.rope = nullptr;
+  GPT_TRY(launch_qkv(dt, qa, st, nullptr));
+  AttnArgs aa{};
+  aa.q = W(pl.q); aa.q_bh = (long long)T * D; aa.k = W(pl.k); aa.k_bh = (long long)T * D;
+  aa.v = W(pl.v); aa.v_bh = (long long)T * D; aa.o = W(pl.o); aa.o_ld = C;
+  aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  GPT_TRY(launch_attention(dt, aa, st));
+  float* x1 = Wf(pl.x1);
+  GPT_TRY(hipMemcpyAsync(x1, x, rowf, hipMemcpyDeviceToDevice, st));
+  GPT_TRY(launch_linear_resid(dt, W(pl.o), C, P.at(w.proj_w), C, P.at(w.proj_b), M, C, C, x1, C, st, nullptr));
+  la.x = x1; la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b); la.out = W(pl.a2);
+  GPT_TRY(launch_layernorm(dt, la, st));
+  GPT_TRY(launch_linear(dt, W(pl.a2), C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, W(pl.uf), F, 0, 0, st, nullptr));
+  GPT_TRY(launch_act_fwd(dt, W(pl.uf), (long long)M * F, act, W(pl.hm), st));
+
+  // ---- weight transposes (operands with the contraction axis contiguous)
+  GPT_TRY(launch_transpose(dt, P.at(w.fcproj_w), F, C, F, W(pl.wfpT), C, st));    // [C,F] -> [F,C]
+  GPT_TRY(launch_transpose(dt, P.at(w.fc_w), C, F, C, W(pl.wfcT), pl.Fp, st));    // [F,C] -> [C,Fp]
+  GPT_TRY(launch_transpose(dt, P.at(w.proj_w), C, C, C, W(pl.wpT), C, st));      // [C,C] -> [C,C]
+  GPT_TRY(launch_transpose(dt, P.at(w.attn_w), C, 3 * C, C, W(pl.waT), pl.C3p, st));   // [3C,C] -> [C,3Cp]
+
+  // ---- MLP: dh = dy Wfp, dWfp += dy^T h, dbfp += sum dy
+  GPT_TRY(launch_cast_rows(dt, dy, (long long)M * C, W(pl.dyc), st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.dyc), C, W(pl.wfpT), C, M, F, C, Wf(pl.dh), F, 0, st));
+  GPT_TRY(launch_transpose(dt, W(pl.dyc), C, M, C, W(pl.dyT), Mp, st));
+  GPT_TRY(launch_transpose(dt, W(pl.hm), F, M, F, W(pl.hT), Mp, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.dyT), Mp, W(pl.hT), Mp, C, F, Mp, grads + w.fcproj_w, F, 1, st));
+  GPT_TRY(launch_colsum(M, C, dy, Wf(pl.part), grads + w.fcproj_b, st));
+  // du = dh * GELU'(u); dWfc += du^T a2; dbfc += sum du; da2 = du Wfc
+  GPT_TRY(launch_act_bwd(dt, Wf(pl.dh), W(pl.uf), (long long)M * F, act, W(pl.duc), st));
+  GPT_TRY(launch_colsum(M, F, Wf(pl.dh), Wf(pl.part), grads + w.fc_b, st));
+  GPT_TRY(launch_transpose(dt, W(pl.duc), F, M, F, W(pl.duT), Mp, st));
+  GPT_TRY(launch_transpose(dt, W(pl.a2), C, M, C, W(pl.a2T), Mp, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.duT), Mp, W(pl.a2T), Mp, F, C, Mp, grads + w.fc_w, C, 1, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.duc), F, W(pl.wfcT), pl.Fp, M, C, F, Wf(pl.da), C, 0, st));
+  // dx1 = dy + LN2 backward
+  float* dx1 = Wf(pl.dx1);
+  GPT_TRY(hipMemcpyAsync(dx1, dy, rowf, hipMemcpyDeviceToDevice, st));
+  GPT_TRY(launch_ln_backward(dt, M, C, x1, P.at(w.ln2_g), Wf(pl.da), cfg->ln_eps, dx1, Wf(pl.mu), Wf(pl.rs),
+                             Wf(pl.part), grads + w.ln2_g, grads + w.ln2_b, st, 1));
+
+  // ---- attention: dWp += dx1^T o, dbp += sum dx1, dO = dx1 Wp
+  GPT_TRY(launch_cast_rows(dt, dx1, (long long)M * C, W(pl.dx1c), st));
+  GPT_TRY(launch_transpose(dt, W(pl.dx1c), C, M, C, W(pl.dx1T), Mp, st));
+  GPT_TRY(launch_transpose(dt, W(pl.o), C, M, C, W(pl.oT), Mp, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1T), Mp, W(pl.oT), Mp, C, C, Mp, grads + w.proj_w, C, 1, st));
+  GPT_TRY(launch_colsum(M, C, dx1, Wf(pl.part), grads + w.proj_b, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1c), C, W(pl.wpT), C, M, C, C, Wf(pl.dout), C, 0, st));
+  GPT_TRY(launch_attention_backward(dt, W(pl.q), W(pl.k), W(pl.v), W(pl.o), Wf(pl.dout), Wf(pl.lse), Wf(pl.dd),
+                                    Wf(pl.dqkv), B, H, T, D, st));
+  // dWattn += dqkv^T a1, dbattn += sum dqkv, da1 = dqkv Wattn
+  GPT_TRY(launch_colsum(M, 3 * C, Wf(pl.dqkv), Wf(pl.part), grads + w.attn_b, st));
+  GPT_TRY(launch_cast_rows(dt, Wf(pl.dqkv), (long long)M * 3 * C, W(pl.dqkvc), st));
+  GPT_TRY(launch_transpose(dt, W(pl.dqkvc), 3 * C, M, 3 * C, W(pl.dqkvT), Mp, st));
+  GPT_TRY(launch_transpose(dt, W(pl.a1), C, M, C, W(pl.a1T), Mp, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.dqkvT), Mp, W(pl.a1T), Mp, 3 * C, C, Mp, grads + w.attn_w, C, 1, st));
+  GPT_TRY(launch_gemm_f32out(dt, W(pl.dqkvc), 3 * C, W(pl.waT), pl.C3p, M, C, 3 * C, Wf(pl.da), C, 0, st));
+  // dx = dx1 + LN1 backward
+  GPT_TRY(hipMemcpyAsync(dx, dx1, rowf, hipMemcpyDeviceToDevice, st));
+  GPT_TRY(launch_ln_backward(dt, M, C, x, P.at(w.ln1_g), Wf(pl.da), cfg->ln_eps, dx, Wf(pl.mu), Wf(pl.rs),
+                             Wf(pl.part), grads + w.ln1_g, grads + w.ln1_b, st, 1));
   return GPT_OK;
 }
 

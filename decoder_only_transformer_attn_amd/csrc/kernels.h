@@ -126,7 +126,14 @@ hipError_t launch_zero_cols(int dtype, void* p, long long ld, int R, int c0, int
 hipError_t launch_cast_rows(int dtype, const float* x, long long n, void* out, hipStream_t st);
 int ln_bwd_chunks(int M);
 hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const void* g, const float* dy, float eps,
-                              float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st);
+                              float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st,
+                              int accumulate);
+hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const void* o,
+                                     const float* dout, float* lse, float* dd, float* dqkv, int B, int H, int T,
+                                     int D, hipStream_t st);
+hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st);
+hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int act, void* dc, hipStream_t st);
+hipError_t launch_colsum(int M, int N, const float* a, float* part, float* out, hipStream_t st);
 hipError_t launch_embed_backward(const int32_t* idx, int B, int T, int C, int V, const float* dx0, float* dwte,
                                  float* dwpe, hipStream_t st);
 hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,

@@ -57,6 +57,9 @@ SIGNATURES = {
     "gpt_head_backward_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "gpt_head_backward": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gpt_embedding_backward": (_c_int, [_CFG, _vp, _c_int, _c_int, _vp, _vp, _vp]),
+    "gpt_forward_train": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_block_backward_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt_block_backward": (_c_int, [_CFG, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -163,6 +166,50 @@ def embedding_backward(cfg, idx, dx0, grads, stream=None) -> None:
     B, T = idx.shape
     check(load().gpt_embedding_backward(ctypes.byref(cfg_c(cfg)), _ptr(idx), B, T, _ptr(dx0), _ptr(grads),
                                         _stream(stream)))
+
+
+def forward_train(cfg, params, idx, xs, ws, targets=None, mean_loss=None, stream=None) -> None:
+    """Enqueue gpt_forward_train: xs f32 [L+1, B*T, C] receives each block's
+    input residual (and ln_f's input); ws as for forward()."""
+    B, T = idx.shape
+    check(load().gpt_forward_train(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets), _ptr(xs),
+                                   _ptr(mean_loss), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def block_backward_workspace_bytes(cfg, B: int, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().gpt_block_backward_workspace_bytes(ctypes.byref(cfg_c(cfg)), B, T, ctypes.byref(out)))
+    return int(out.value)
+
+
+def block_backward(cfg, params, layer: int, B: int, T: int, x, dy, dx, grads, ws, stream=None) -> None:
+    """Enqueue gpt_block_backward for block `layer`: x, dy, dx f32 [B*T, C];
+    grads f32 [param_count] (accumulated)."""
+    check(load().gpt_block_backward(ctypes.byref(cfg_c(cfg)), _ptr(params), layer, B, T, _ptr(x), _ptr(dy), _ptr(dx),
+                                    _ptr(grads), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gradients(cfg, params, idx, grads, targets=None, stream=None):
+    """Every parameter gradient of the mean next-token loss (pre-LN GPT-2
+    blocks), accumulated into grads: training forward, head backward, the
+    blocks in reverse, embedding backward.  Returns the mean loss tensor."""
+    import torch
+    B, T = idx.shape
+    M, C, L = B * T, cfg.n_embd, cfg.n_layer
+    dev = idx.device
+    xs = torch.empty((L + 1, M, C), dtype=torch.float32, device=dev)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(workspace_bytes(cfg, B, T), head_backward_workspace_bytes(cfg, B, T),
+                         block_backward_workspace_bytes(cfg, B, T) if L else 0), dtype=torch.uint8, device=dev)
+    forward_train(cfg, params, idx, xs, ws, targets, loss, stream)
+    d = torch.empty((M, C), dtype=torch.float32, device=dev)
+    d2 = torch.empty_like(d)
+    head_backward(cfg, params, idx, xs[L], d, grads, targets, None, ws, stream)
+    for l in range(L - 1, -1, -1):
+        block_backward(cfg, params, l, B, T, xs[l], d, d2, grads, ws, stream)
+        d, d2 = d2, d
+    embedding_backward(cfg, idx, d, grads, stream)
+    return loss
 
 
 KERNEL = {"head": 0, "qkv": 1, "attn": 2, "proj": 3, "fc": 4, "fcproj": 5, "ln": 6}

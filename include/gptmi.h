@@ -285,6 +285,36 @@ int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* 
 int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int T, const float* dx0, float* grads,
                            void* stream);
 
+/* ---- backward of the blocks (pre-LN GPT-2 blocks: arch 0, post_ln 0) ----
+ * A whole gradient of the mean loss: gpt_forward_train (the loss, and each
+ * block's input residual), gpt_head_backward on xs[L], gpt_block_backward for
+ * l = L-1 .. 0 (each turns d loss / d(block l's output) into d loss / d(its
+ * input)), then gpt_embedding_backward on the last dx.  Blocks are recomputed
+ * from their inputs (only the L+1 residual rows are kept between the passes). */
+
+/* The forward pass and mean loss (no logits), writing xs (device, fp32
+ * [L+1][B*T][C]): xs[l] = the residual entering block l, xs[L] = the rows
+ * the final LayerNorm reads.  Same workspace as gpt_forward.  B*T <= 2^20. */
+int gpt_forward_train(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                      const int32_t* targets, float* xs, float* mean_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Device workspace bytes of gpt_block_backward for a [B, T] batch (host only). */
+int gpt_block_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size_t* bytes);
+
+/* Backward of block `layer` (0 <= layer < L): out = x1 + mlp(LN2(x1)),
+ * x1 = x + attn(LN1(x)).
+ *   x      (device) fp32 [B*T, C]: the block's input (read only).
+ *   dy     (device) fp32 [B*T, C]: d loss / d out (read only).
+ *   dx     (device) fp32 [B*T, C]: d loss / d x, overwritten (must not alias
+ *          x or dy).
+ *   grads  (device) fp32 gradient blob: += this block's twelve tensors.
+ * The block's forward is recomputed with the forward kernels; the products
+ * run on bf16 (or fp32) operands with fp32 accumulation; attention's
+ * gradient is computed in fp32 from the recomputed probabilities
+ * (exp(s - lse), rows re-normalised by a prep pass).  B*T <= 2^20. */
+int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int B, int T, const float* x,
+                       const float* dy, float* dx, float* grads, void* ws, size_t ws_bytes, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* gpt_status_string(int status);
 

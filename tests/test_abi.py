@@ -219,3 +219,26 @@ def test_llama_config_is_validated():
     out = ctypes.c_size_t(0)
     assert lib.load().gpt_head_backward_workspace_bytes(ctypes.byref(lib.cfg_c(good)), 2, 4,
                                                         ctypes.byref(out)) == lib.GPT_ERR_CONFIG
+
+
+def test_block_backward_validation():
+    L = lib.load()
+    cfg = synth.MICRO
+    c = ctypes.byref(lib.cfg_c(cfg))
+    w = lib.block_backward_workspace_bytes(cfg, 2, 5)
+    assert w > 0
+
+    def bb(layer=0, B=2, T=5, x=1, dy=1, dx=1, grads=1, ws=1, ws_bytes=1 << 40, params=1, cc=c):
+        return L.gpt_block_backward(cc, params, layer, B, T, x, dy, dx, grads, ws, ws_bytes, None)
+
+    for kw in (dict(params=None), dict(x=None), dict(dy=None), dict(dx=None), dict(grads=None), dict(ws=None)):
+        assert bb(**kw) == lib.GPT_ERR_NULL, kw
+    assert bb(layer=-1) == lib.GPT_ERR_SHAPE and bb(layer=cfg.n_layer) == lib.GPT_ERR_SHAPE
+    assert bb(B=0) == lib.GPT_ERR_SHAPE and bb(T=cfg.ctx + 1) == lib.GPT_ERR_SEQ_TOO_LONG
+    assert bb(ws_bytes=w - 1) == lib.GPT_ERR_WORKSPACE
+    import dataclasses as dc
+    for var in (dict(post_ln=1), dict(arch=1, n_kv_head=1)):
+        bad = ctypes.byref(lib.cfg_c(dc.replace(cfg, **var)))
+        assert bb(cc=bad) == lib.GPT_ERR_CONFIG
+        assert L.gpt_forward_train(bad, 1, 1, 2, 5, None, 1, None, 1, 1 << 40, None) == lib.GPT_ERR_CONFIG
+    assert L.gpt_forward_train(c, 1, 1, 2, 5, None, None, None, 1, 1 << 40, None) == lib.GPT_ERR_NULL
