@@ -20,6 +20,12 @@
 
 namespace gptmi {
 
+#define GPT_BWD_TRY(expr)                   \
+  do {                                      \
+    const hipError_t _e = (expr);           \
+    if (_e != hipSuccess) return _e;        \
+  } while (0)
+
 constexpr int BR_ROWS = 16;   // rows per block of the row kernel (4 per wave)
 
 __device__ __forceinline__ int bwd_target(const int32_t* targets, const int32_t* idx, int m, int T_seq, int V) {
@@ -384,227 +390,132 @@ __global__ void __launch_bounds__(256) colsum_final_kernel(int N, int nchunks, c
   out[c] += s;
 }
 
-// Attention backward for causal heads, scores s = q.k / sqrt(D), P = softmax
-// over keys <= t.  With lse_t = log sum_j e^{s_tj} and Dt = sum_d dO[t,d] O[t,d]
-// (= sum_j P_tj dP_tj): dV_j = sum_t P_tj dO_t, dS_tj = P_tj (dO_t.V_j - Dt),
-// dQ_t = sum_j dS_tj K_j / sqrt(D), dK_j = sum_t dS_tj Q_t / sqrt(D).
-// One thread per row (query or key) holds its vectors in registers (DM >= D,
-// fully unrolled loops); the other side's rows stream through LDS tiles in
-// fp32.  Q, K, U are head-major [B, H, T, D]; O (compute dtype) and dO (fp32)
-// are [B*T, C] with head h at columns [hD, hD+D); dQKV is fp32 [B*T, 3C]
-// (q, k, u column blocks).  All sums run in a fixed order.
-constexpr int AB_ROWS = 256;   // rows (threads) per block
-constexpr int AB_TILE = 32;    // rows of the other side per LDS tile
+// Attention backward for causal heads on the matrix cores, with the score
+// matrices materialised per head (T x Tp, Tp = T rounded up to 64):
+//   S = Q K^T;  P = softmax(S / sqrt(D)) over keys j <= t (0 elsewhere);
+//   dP = dO U^T;  dS = P (dP - rowsum(P dP)) / sqrt(D);
+//   dU = P^T dO,  dQ = dS K,  dK = dS^T Q.
+// The five products are batched launches of the tiled GEMM (grid.y = B*H) on
+// zero-padded per-head transposes, so every contraction runs over Tp with
+// exact zeros in the pads; the row kernels use one wave per row and
+// fixed-order reductions.
 
-struct AttnBwdArgs {
-  const void* q; const void* k; const void* u;   // [B, H, T, D]
-  const void* o;                                  // [B*T, C]
-  const float* dout;                              // [B*T, C]
-  float* lse; float* dd;                          // [B*H*T]
-  float* dqkv;                                    // [B*T, 3C]
-  int B, H, T, D;
-  float scale;                                    // 1 / sqrt(D)
-};
-
-template <typename T, int DM>
-__device__ __forceinline__ void load_row(const T* __restrict__ p, int D, float (&r)[DM]) {
-#pragma unroll
-  for (int d = 0; d < DM; ++d) r[d] = d < D ? to_f32(p[d]) : 0.f;
-}
-
-// lse and Dt per query row
-template <typename T, int DM>
-__global__ void __launch_bounds__(AB_ROWS) attn_bwd_prep_kernel(AttnBwdArgs a) {
-  __shared__ float sk[AB_TILE][DM];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
-  const int t = blockIdx.y * AB_ROWS + threadIdx.x;
-  const int D = a.D, C = a.H * D, T_ = a.T;
-  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * T_ * D;
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * T_ * D;
-  float q[DM];
-  if (t < T_) load_row<T, DM>(Q + (long long)t * D, D, q);
-  else
-#pragma unroll
-    for (int d = 0; d < DM; ++d) q[d] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  const int tmax = min(T_ - 1, blockIdx.y * AB_ROWS + AB_ROWS - 1);
-  for (int j0 = 0; j0 <= tmax; j0 += AB_TILE) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < AB_TILE * DM; e += AB_ROWS) {
-      const int r = e / DM, d = e - r * DM;
-      sk[r][d] = (j0 + r < T_ && d < D) ? to_f32(K[(long long)(j0 + r) * D + d]) : 0.f;
-    }
-    __syncthreads();
-    for (int r = 0; r < AB_TILE; ++r) {
-      const int j = j0 + r;
-      if (t < T_ && j <= t) {
-        float s = 0.f;
-#pragma unroll
-        for (int d = 0; d < DM; ++d) s = fmaf(q[d], sk[r][d], s);
-        s *= a.scale;
-        if (s > m) { l = l * __expf(m - s) + 1.f; m = s; }
-        else l += __expf(s - m);
-      }
-    }
+// out_z[c, r] = in_z[r, c] (r < R, c < Cc), 0 for R <= r < Rp; in_z starts at
+// b * in_b + h * in_h (z = b * H + h), out_z at z * out_z.
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(256) transpose_batched_kernel(const TI* __restrict__ in, long long ld_in,
+                                                                long long in_b, long long in_h, int H, int R, int Cc,
+                                                                TO* __restrict__ out, long long ld_out,
+                                                                long long out_z, int Rp) {
+  __shared__ float tile[64][65];
+  const int z = blockIdx.z, b = z / H, h = z - b * H;
+  in += b * in_b + h * in_h;
+  out += (long long)z * out_z;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < Cc) ? to_f32(in[(long long)r * ld_in + c]) : 0.f;
   }
-  if (t < T_) {
-    a.lse[(long long)bh * T_ + t] = m + __logf(l);
-    const T* orow = reinterpret_cast<const T*>(a.o) + ((long long)b * T_ + t) * C + h * D;
-    const float* drow = a.dout + ((long long)b * T_ + t) * C + h * D;
-    float dd = 0.f;
-    for (int d = 0; d < D; ++d) dd = fmaf(drow[d], to_f32(orow[d]), dd);
-    a.dd[(long long)bh * T_ + t] = dd;
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < Cc && r < Rp) out[(long long)c * ld_out + r] = from_f32<TO>(tile[tx][i]);
   }
 }
 
-// dQ: thread = query row t, keys j <= t in tiles
-template <typename T, int DM>
-__global__ void __launch_bounds__(AB_ROWS) attn_bwd_dq_kernel(AttnBwdArgs a) {
-  __shared__ float sk[AB_TILE][DM];
-  __shared__ float su[AB_TILE][DM];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
-  const int t = blockIdx.y * AB_ROWS + threadIdx.x;
-  const int D = a.D, C = a.H * D, T_ = a.T;
-  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * T_ * D;
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * T_ * D;
-  const T* U = reinterpret_cast<const T*>(a.u) + (long long)bh * T_ * D;
-  const bool live = t < T_;
-  float q[DM], go[DM], dq[DM];
-#pragma unroll
-  for (int d = 0; d < DM; ++d) { q[d] = 0.f; go[d] = 0.f; dq[d] = 0.f; }
-  float lse = 0.f, dd = 0.f;
-  if (live) {
-    load_row<T, DM>(Q + (long long)t * D, D, q);
-    const float* drow = a.dout + ((long long)b * T_ + t) * C + h * D;
-#pragma unroll
-    for (int d = 0; d < DM; ++d) go[d] = d < D ? drow[d] : 0.f;
-    lse = a.lse[(long long)bh * T_ + t];
-    dd = a.dd[(long long)bh * T_ + t];
-  }
-  const int tmax = min(T_ - 1, blockIdx.y * AB_ROWS + AB_ROWS - 1);
-  for (int j0 = 0; j0 <= tmax; j0 += AB_TILE) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < AB_TILE * DM; e += AB_ROWS) {
-      const int r = e / DM, d = e - r * DM;
-      const bool in = j0 + r < T_ && d < D;
-      sk[r][d] = in ? to_f32(K[(long long)(j0 + r) * D + d]) : 0.f;
-      su[r][d] = in ? to_f32(U[(long long)(j0 + r) * D + d]) : 0.f;
-    }
-    __syncthreads();
-    for (int r = 0; r < AB_TILE; ++r) {
-      const int j = j0 + r;
-      if (live && j <= t) {
-        float s = 0.f, dp = 0.f;
-#pragma unroll
-        for (int d = 0; d < DM; ++d) {
-          s = fmaf(q[d], sk[r][d], s);
-          dp = fmaf(go[d], su[r][d], dp);
-        }
-        const float p = __expf(s * a.scale - lse);
-        const float ds = p * (dp - dd);
-#pragma unroll
-        for (int d = 0; d < DM; ++d) dq[d] = fmaf(ds, sk[r][d], dq[d]);
-      }
-    }
-  }
-  if (live) {
-    float* out = a.dqkv + ((long long)b * T_ + t) * (3 * C) + h * D;
-#pragma unroll
-    for (int d = 0; d < DM; ++d)
-      if (d < D) out[d] = dq[d] * a.scale;
-  }
+template <typename TI, typename TO>
+static void transpose_batched(const TI* in, long long ld_in, long long in_b, long long in_h, int H, int R, int Cc,
+                              TO* out, long long ld_out, long long out_z, int Rp, int Z, hipStream_t st) {
+  const dim3 grid((Rp + 63) / 64, (Cc + 63) / 64, Z);
+  hipLaunchKernelGGL((transpose_batched_kernel<TI, TO>), grid, dim3(256), 0, st, in, ld_in, in_b, in_h, H, R, Cc, out,
+                     ld_out, out_z, Rp);
 }
 
-// dK (WHICH 0) or dU (WHICH 1): thread = key row j, queries t >= j in tiles
-template <typename T, int DM, int WHICH>
-__global__ void __launch_bounds__(AB_ROWS) attn_bwd_dkv_kernel(AttnBwdArgs a) {
-  __shared__ float sq[AB_TILE][DM];
-  __shared__ float sg[AB_TILE][DM];
-  __shared__ float sl[AB_TILE], sd[AB_TILE];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
-  const int j = blockIdx.y * AB_ROWS + threadIdx.x;
-  const int D = a.D, C = a.H * D, T_ = a.T;
-  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * T_ * D;
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)bh * T_ * D;
-  const T* U = reinterpret_cast<const T*>(a.u) + (long long)bh * T_ * D;
-  const bool live = j < T_;
-  float k[DM], u[DM], acc[DM];
-#pragma unroll
-  for (int d = 0; d < DM; ++d) { k[d] = 0.f; u[d] = 0.f; acc[d] = 0.f; }
-  if (live) {
-    load_row<T, DM>(K + (long long)j * D, D, k);
-    if (WHICH == 0) load_row<T, DM>(U + (long long)j * D, D, u);
-  }
-  const int jmin = blockIdx.y * AB_ROWS;   // the block's first key: queries before it see none of its keys
-  for (int t0 = (jmin / AB_TILE) * AB_TILE; t0 < T_; t0 += AB_TILE) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < AB_TILE * DM; e += AB_ROWS) {
-      const int r = e / DM, d = e - r * DM;
-      const int t = t0 + r;
-      const bool in = t < T_ && d < D;
-      sq[r][d] = in ? to_f32(Q[(long long)t * D + d]) : 0.f;
-      sg[r][d] = in ? a.dout[((long long)b * T_ + t) * C + h * D + d] : 0.f;
-    }
-    if (threadIdx.x < AB_TILE) {
-      const int t = t0 + threadIdx.x;
-      sl[threadIdx.x] = t < T_ ? a.lse[(long long)bh * T_ + t] : 0.f;
-      sd[threadIdx.x] = t < T_ ? a.dd[(long long)bh * T_ + t] : 0.f;
-    }
-    __syncthreads();
-    for (int r = 0; r < AB_TILE; ++r) {
-      const int t = t0 + r;
-      if (live && t < T_ && t >= j) {
-        float s = 0.f;
-#pragma unroll
-        for (int d = 0; d < DM; ++d) s = fmaf(sq[r][d], k[d], s);
-        const float p = __expf(s * a.scale - sl[r]);
-        if (WHICH == 1) {
-#pragma unroll
-          for (int d = 0; d < DM; ++d) acc[d] = fmaf(p, sg[r][d], acc[d]);
-        } else {
-          float dp = 0.f;
-#pragma unroll
-          for (int d = 0; d < DM; ++d) dp = fmaf(sg[r][d], u[d], dp);
-          const float ds = p * (dp - sd[r]);
-#pragma unroll
-          for (int d = 0; d < DM; ++d) acc[d] = fmaf(ds, sq[r][d], acc[d]);
-        }
-      }
-    }
-  }
-  if (live) {
-    float* out = a.dqkv + ((long long)b * T_ + j) * (3 * C) + (WHICH == 0 ? C : 2 * C) + h * D;
-    const float f = WHICH == 0 ? a.scale : 1.f;
-#pragma unroll
-    for (int d = 0; d < DM; ++d)
-      if (d < D) out[d] = acc[d] * f;
-  }
+// P row (z, t) from the S row: causal softmax of S / sqrt(D), zeros past t and in the pads
+template <typename T>
+__global__ void __launch_bounds__(256) attn_bwd_softmax_kernel(const float* __restrict__ S, T* __restrict__ P,
+                                                               int Z, int Tn, int Tp, float scale) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long long)Z * Tn) return;   // (no block-wide barrier)
+  const int t = (int)(row % Tn);
+  const float* sr = S + row * Tp;
+  T* pr = P + row * Tp;
+  float m = -INFINITY;
+  for (int j = lane; j <= t; j += 64) m = fmaxf(m, sr[j] * scale);
+  m = wave_max(m);
+  float l = 0.f;
+  for (int j = lane; j <= t; j += 64) l += __expf(sr[j] * scale - m);
+  const float inv = 1.0f / wave_sum(l);
+  for (int j = lane; j < Tp; j += 64) pr[j] = from_f32<T>(j <= t ? __expf(sr[j] * scale - m) * inv : 0.f);
 }
 
-template <typename T, int DM>
-static void attn_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.B * a.H, (a.T + AB_ROWS - 1) / AB_ROWS);
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<T, DM>), grid, dim3(AB_ROWS), 0, st, a);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DM>), grid, dim3(AB_ROWS), 0, st, a);
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DM, 0>), grid, dim3(AB_ROWS), 0, st, a);
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DM, 1>), grid, dim3(AB_ROWS), 0, st, a);
+// dS row (z, t) = P (dP - sum_j P dP) * scale (P is 0 past t and in the pads)
+template <typename T>
+__global__ void __launch_bounds__(256) attn_bwd_ds_kernel(const T* __restrict__ P, const float* __restrict__ dP,
+                                                          T* __restrict__ dS, int Z, int Tn, int Tp, float scale) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long long)Z * Tn) return;
+  const T* pr = P + row * Tp;
+  const float* gr = dP + row * Tp;
+  float s = 0.f;
+  for (int j = lane; j < Tp; j += 64) s = fmaf(to_f32(pr[j]), gr[j], s);
+  const float dd = wave_sum(s);
+  T* out = dS + row * Tp;
+  for (int j = lane; j < Tp; j += 64) out[j] = from_f32<T>(to_f32(pr[j]) * (gr[j] - dd) * scale);
 }
 
 template <typename T>
-static hipError_t attn_bwd_d(const AttnBwdArgs& a, hipStream_t st) {
-  if (a.D <= 32) attn_bwd_t<T, 32>(a, st);
-  else if (a.D <= 64) attn_bwd_t<T, 64>(a, st);
-  else if (a.D <= 128) attn_bwd_t<T, 128>(a, st);
-  else return hipErrorInvalidValue;
+static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* dout, float* dqkv, int B, int H,
+                             int Tn, int D, const AttnBwdWs& w, hipStream_t st) {
+  const int Z = B * H, C = H * D, Tp = w.Tp;
+  const float scale = (float)(1.0 / std::sqrt((double)D));
+  const int dt = sizeof(T) == 2 ? 1 : 0;
+  const long long hT = (long long)Tn * D, hTT = (long long)Tn * Tp, hDT = (long long)D * Tp;
+  T* P = static_cast<T*>(w.P);
+  T* PT = static_cast<T*>(w.PT);
+  T* dS = static_cast<T*>(w.dS);
+  T* dST = static_cast<T*>(w.dST);
+  T* doc = static_cast<T*>(w.doc);
+  T* dOT = static_cast<T*>(w.dOT);
+  T* KT = static_cast<T*>(w.KT);
+  T* QT = static_cast<T*>(w.QT);
+  const int rows_blocks = (int)(((long long)Z * Tn + 3) / 4);
+  hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid_for((long long)B * Tn * C)), dim3(256), 0, st, dout,
+                     (long long)B * Tn * C, doc);
+  // S = Q K^T
+  GPT_BWD_TRY(launch_gemm_batched(dt, q, D, k, D, Tn, Tn, D, w.S, Tp,
+                                  BatchStrides{H * hT, hT, H * hT, hT, H * hTT, hTT, H}, Z, st));
+  hipLaunchKernelGGL(attn_bwd_softmax_kernel<T>, dim3(rows_blocks), dim3(256), 0, st, (const float*)w.S, P, Z, Tn, Tp,
+                     scale);
+  // dU = P^T dO
+  transpose_batched<T, T>(P, Tp, H * hTT, hTT, H, Tn, Tn, PT, Tp, hTT, Tp, Z, st);
+  transpose_batched<T, T>(doc, C, (long long)Tn * C, D, H, Tn, D, dOT, Tp, hDT, Tp, Z, st);
+  GPT_BWD_TRY(launch_gemm_batched(dt, PT, Tp, dOT, Tp, Tn, D, Tp, dqkv + 2 * C, 3 * C,
+                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+  // dP = dO U^T (into the S buffer), dS
+  GPT_BWD_TRY(launch_gemm_batched(dt, doc, C, u, D, Tn, Tn, D, w.S, Tp,
+                                  BatchStrides{(long long)Tn * C, D, H * hT, hT, H * hTT, hTT, H}, Z, st));
+  hipLaunchKernelGGL(attn_bwd_ds_kernel<T>, dim3(rows_blocks), dim3(256), 0, st, (const T*)P, (const float*)w.S, dS, Z,
+                     Tn, Tp, scale);
+  // dQ = dS K, dK = dS^T Q
+  transpose_batched<T, T>(k, D, H * hT, hT, H, Tn, D, KT, Tp, hDT, Tp, Z, st);
+  GPT_BWD_TRY(launch_gemm_batched(dt, dS, Tp, KT, Tp, Tn, D, Tp, dqkv, 3 * C,
+                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+  transpose_batched<T, T>(dS, Tp, H * hTT, hTT, H, Tn, Tn, dST, Tp, hTT, Tp, Z, st);
+  transpose_batched<T, T>(q, D, H * hT, hT, H, Tn, D, QT, Tp, hDT, Tp, Z, st);
+  GPT_BWD_TRY(launch_gemm_batched(dt, dST, Tp, QT, Tp, Tn, D, Tp, dqkv + C, 3 * C,
+                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
   return hipGetLastError();
 }
 
-hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const void* o,
-                                     const float* dout, float* lse, float* dd, float* dqkv, int B, int H, int T,
-                                     int D, hipStream_t st) {
-  const AttnBwdArgs a{q, k, u, o, dout, lse, dd, dqkv, B, H, T, D, (float)(1.0 / std::sqrt((double)D))};
-  if (dtype == 0) return attn_bwd_d<float>(a, st);
-  return attn_bwd_d<bf16>(a, st);
+hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const float* dout,
+                                     float* dqkv, int B, int H, int T, int D, const AttnBwdWs& w, hipStream_t st) {
+  if (dtype == 0)
+    return attn_bwd_t<float>((const float*)q, (const float*)k, (const float*)u, dout, dqkv, B, H, T, D, w, st);
+  return attn_bwd_t<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)u, dout, dqkv, B, H, T, D, w, st);
 }
 
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st) {

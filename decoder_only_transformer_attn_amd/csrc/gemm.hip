@@ -1510,6 +1510,60 @@ hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyW
   return qkv_t<bf16>(a, sk, st);
 }
 
+// Batched products for the attention backward: grid.y runs over z = b * H + h,
+// and every operand and the fp32 output start at b * (stride_b) + h * (stride_h)
+// (BatchStrides).
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, int M, int N, int K,
+                    float* __restrict__ out, int ldo, BatchStrides bs) {
+  typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
+  __shared__ __align__(16) T smem[G::SMEM_ELEMS];
+  const int z = blockIdx.y, b = z / bs.H, h = z - b * bs.H;
+  A += b * bs.ab + h * bs.ah;
+  W += b * bs.wb + h * bs.wh;
+  const EpiF32<false> epi{out + b * bs.ob + h * bs.oh, ldo};
+  const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
+  int mt, nt;
+  tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
+  float2 pre[G::TM][G::TN][8];
+  typename EpiF32<false>::Col colv[G::TN];
+  preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
+  f32x16 acc[G::TM][G::TN];
+  gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
+  epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN>
+static hipError_t run_batched(const T* A, int lda, const T* W, int ldw, int M, int N, int K, float* out, int ldo,
+                              const BatchStrides& bs, int Z, hipStream_t st) {
+  typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
+  const dim3 grid(((M + BM - 1) / BM) * ((N + BN - 1) / BN), Z);
+  if (K % BK == 0)
+    hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, false>), grid, dim3(G::NT), 0, st, A, lda, W, ldw,
+                       M, N, K, out, ldo, bs);
+  else
+    hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, true>), grid, dim3(G::NT), 0, st, A, lda, W, ldw,
+                       M, N, K, out, ldo, bs);
+  return hipGetLastError();
+}
+
+// out_z [M, N] fp32 = A_z [M, K] . W_z [N, K]^T for z < Z (K a multiple of 8, or of 4 in fp32)
+hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+                               float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st) {
+  if (dtype == 0)
+    return run_batched<float, 64, 64, 32, 32, 32>((const float*)A, lda, (const float*)W, ldw, M, N, K, out, ldo, bs,
+                                                  Z, st);
+  if (N >= 128)
+    return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs,
+                                                   Z, st);
+  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs, Z, st);
+}
+
 // Loss gradient of the logits A W^T ([M, C] x [V, C]^T) into dz [M, V] (ld).
 hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V, int C, const float* lse,
                           const int32_t* y, const float* inv, void* dz, long long ld, void* dzT, long long ldT,

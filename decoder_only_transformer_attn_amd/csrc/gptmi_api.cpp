@@ -500,8 +500,8 @@ BwdPlan bwd_plan(const gpt_config* c, int B, int T) {
 // of the intermediate tensors.
 struct BlkPlan {
   size_t a1, q, k, v, o, x1, a2, uf, hm, dyc, dyT, hT, dh, duc, duT, a2T, da, dx1, dx1c, dx1T, oT, dout, dqkv,
-      dqkvc, dqkvT, a1T, lse, dd, wfpT, wfcT, wpT, waT, mu, rs, part, total;
-  int Mp, Fp, C3p, nchunks;
+      dqkvc, dqkvT, a1T, aS, aP, aPT, adS, adST, adoc, adOT, aKT, aQT, wfpT, wfcT, wpT, waT, mu, rs, part, total;
+  int Mp, Fp, C3p, Tp, nchunks;
 };
 
 BlkPlan blk_plan(const gpt_config* c, int B, int T) {
@@ -521,7 +521,12 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   p.da = take(M * C * 4); p.dx1 = take(M * C * 4); p.dx1c = take(M * C * es); p.dx1T = take(C * Mp * es);
   p.oT = take(C * Mp * es); p.dout = take(M * C * 4); p.dqkv = take(M * 3 * C * 4); p.dqkvc = take(M * 3 * C * es);
   p.dqkvT = take(3 * C * Mp * es); p.a1T = take(C * Mp * es);
-  p.lse = take(B * H * T * 4); p.dd = take(B * H * T * 4);
+  // attention backward: per-head score matrices [B*H][T][Tp] and transposes [B*H][D][Tp]
+  p.Tp = (int)align_up((size_t)T, 64);
+  const size_t Z = (size_t)B * H, TT = (size_t)T * p.Tp, DT = (C / H) * (size_t)p.Tp;
+  p.aS = take(Z * TT * 4); p.aP = take(Z * TT * es); p.aPT = take(Z * TT * es); p.adS = take(Z * TT * es);
+  p.adST = take(Z * TT * es); p.adoc = take(M * C * es); p.adOT = take(Z * DT * es); p.aKT = take(Z * DT * es);
+  p.aQT = take(Z * DT * es);
   p.wfpT = take(F * C * es); p.wfcT = take(C * (size_t)p.Fp * es); p.wpT = take(C * C * es);
   p.waT = take(C * (size_t)p.C3p * es);
   p.mu = take(M * 4); p.rs = take(M * 4);
@@ -915,8 +920,9 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1T), Mp, W(pl.oT), Mp, C, C, Mp, grads + w.proj_w, C, 1, st));
   GPT_TRY(launch_colsum(M, C, dx1, Wf(pl.part), grads + w.proj_b, st));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1c), C, W(pl.wpT), C, M, C, C, Wf(pl.dout), C, 0, st));
-  GPT_TRY(launch_attention_backward(dt, W(pl.q), W(pl.k), W(pl.v), W(pl.o), Wf(pl.dout), Wf(pl.lse), Wf(pl.dd),
-                                    Wf(pl.dqkv), B, H, T, D, st));
+  const AttnBwdWs aw{Wf(pl.aS), W(pl.aP), W(pl.aPT), W(pl.adS), W(pl.adST), W(pl.adoc), W(pl.adOT), W(pl.aKT),
+                     W(pl.aQT), pl.Tp};
+  GPT_TRY(launch_attention_backward(dt, W(pl.q), W(pl.k), W(pl.v), Wf(pl.dout), Wf(pl.dqkv), B, H, T, D, aw, st));
   // dWattn += dqkv^T a1, dbattn += sum dqkv, da1 = dqkv Wattn
   GPT_TRY(launch_colsum(M, 3 * C, Wf(pl.dqkv), Wf(pl.part), grads + w.attn_b, st));
   GPT_TRY(launch_cast_rows(dt, Wf(pl.dqkv), (long long)M * 3 * C, W(pl.dqkvc), st));

@@ -128,9 +128,15 @@ int ln_bwd_chunks(int M);
 hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const void* g, const float* dy, float eps,
                               float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st,
                               int accumulate);
-hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const void* o,
-                                     const float* dout, float* lse, float* dd, float* dqkv, int B, int H, int T,
-                                     int D, hipStream_t st);
+// Per-(b, h) operand offsets of a batched product: b * (.b) + h * (.h), z = b * H + h.
+struct BatchStrides { long long ab, ah, wb, wh, ob, oh; int H; };
+hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+                               float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st);
+// Attention backward scratch: S / dP fp32 [B*H][T][Tp]; P, P^T, dS, dS^T [B*H][T][Tp];
+// dO in the compute dtype [B*T][C]; per-head transposes of dO, K, Q [B*H][D][Tp].
+struct AttnBwdWs { float* S; void* P; void* PT; void* dS; void* dST; void* doc; void* dOT; void* KT; void* QT; int Tp; };
+hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const float* dout,
+                                     float* dqkv, int B, int H, int T, int D, const AttnBwdWs& w, hipStream_t st);
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st);
 hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int act, void* dc, hipStream_t st);
 hipError_t launch_colsum(int M, int N, const float* a, float* part, float* out, hipStream_t st);

@@ -310,8 +310,9 @@ int gpt_block_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size
  *   grads  (device) fp32 gradient blob: += this block's twelve tensors.
  * The block's forward is recomputed with the forward kernels; the products
  * run on bf16 (or fp32) operands with fp32 accumulation; attention's
- * gradient is computed in fp32 from the recomputed probabilities
- * (exp(s - lse), rows re-normalised by a prep pass).  B*T <= 2^20. */
+ * gradient materialises each head's probabilities P and dS = P (dP -
+ * rowsum(P dP)) / sqrt(D) ([B*H][T][T] in the workspace) and runs the five
+ * products as batched matrix-core products.  B*T <= 2^20. */
 int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int B, int T, const float* x,
                        const float* dy, float* dx, float* grads, void* ws, size_t ws_bytes, void* stream);
 
