@@ -231,10 +231,36 @@ def bench_forward(args, w):
     }
     if args.workload == 3:
         out["head_backward"] = bench_head_backward(cfg, B, T, dev_params, idx, stream)
+        out["train_grad"] = bench_train_grad(cfg, B, T, dev_params, idx, stream)
         out["llama"] = bench_llama_forward(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_forward(cfg, params, ids, args.cpu_seqs)
     return out
+
+
+def bench_train_grad(cfg, B, T, dev_params, idx, stream, reps=3):
+    """Every parameter gradient of the mean loss (lib.gradients: training
+    forward keeping the block inputs, head backward, the 12 block backwards
+    with recomputation, embedding backward).  Algorithmic work: three times
+    the forward's FLOPs (forward + a backward of twice its products); the
+    blocks' recomputed forward is not counted."""
+    import torch
+    from decoder_only_transformer_attn_amd import lib
+    grads = torch.zeros(lib.param_count(cfg), dtype=torch.float32, device="cuda")
+    lib.gradients(cfg, dev_params, idx, grads, stream=stream)
+    torch.cuda.synchronize()
+    ev = Events(2)
+    ev.record(0, stream.cuda_stream)
+    for _ in range(reps):
+        loss = lib.gradients(cfg, dev_params, idx, grads, stream=stream)
+    ev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / reps
+    ev.close()
+    flops = 3 * forward_flops(cfg, B, T)[0]
+    return {"ms": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1), "algorithmic_flops": flops,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "loss": round(float(loss.item()), 5)}
 
 
 def bench_llama_forward(args):

@@ -432,8 +432,11 @@ static void transpose_batched(const TI* in, long long ld_in, long long in_b, lon
                      ld_out, out_z, Rp);
 }
 
-// P row (z, t) from the S row: causal softmax of S / sqrt(D), zeros past t and in the pads
-template <typename T>
+// P row (z, t) from the S row: causal softmax of S / sqrt(D), zeros past t and
+// in the pads.  Only S[t, j <= t] is read (the tiles above the diagonal are not
+// computed).  NV > 0: the row (Tp <= 256 NV) is held in registers, four
+// consecutive columns per lane and step (16-byte loads); NV = 0: strided.
+template <typename T, int NV>
 __global__ void __launch_bounds__(256) attn_bwd_softmax_kernel(const float* __restrict__ S, T* __restrict__ P,
                                                                int Z, int Tn, int Tp, float scale) {
   const int lane = threadIdx.x & 63;
@@ -442,29 +445,115 @@ __global__ void __launch_bounds__(256) attn_bwd_softmax_kernel(const float* __re
   const int t = (int)(row % Tn);
   const float* sr = S + row * Tp;
   T* pr = P + row * Tp;
-  float m = -INFINITY;
-  for (int j = lane; j <= t; j += 64) m = fmaxf(m, sr[j] * scale);
-  m = wave_max(m);
-  float l = 0.f;
-  for (int j = lane; j <= t; j += 64) l += __expf(sr[j] * scale - m);
-  const float inv = 1.0f / wave_sum(l);
-  for (int j = lane; j < Tp; j += 64) pr[j] = from_f32<T>(j <= t ? __expf(sr[j] * scale - m) * inv : 0.f);
+  if constexpr (NV > 0) {
+    float v[NV][4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = i * 256 + lane * 4;
+      if (j <= t) {   // (j < Tp: t < Tn <= Tp)
+        const float4 x = *reinterpret_cast<const float4*>(sr + j);
+        v[i][0] = x.x * scale; v[i][1] = x.y * scale; v[i][2] = x.z * scale; v[i][3] = x.w * scale;
+      } else {
+        v[i][0] = v[i][1] = v[i][2] = v[i][3] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e > t) v[i][e] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, v[i][e]);
+    }
+    m = wave_max(m);
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[i][e] = __expf(v[i][e] - m);   // exp(-inf) = 0 past t
+        l += v[i][e];
+      }
+    const float inv = 1.0f / wave_sum(l);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = i * 256 + lane * 4;
+      if (j < Tp) {
+        if constexpr (sizeof(T) == 4) {
+          *reinterpret_cast<float4*>(pr + j) = make_float4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+        } else {
+          *reinterpret_cast<uint2*>(pr + j) =
+              make_uint2(pack_bf16x2(v[i][0] * inv, v[i][1] * inv), pack_bf16x2(v[i][2] * inv, v[i][3] * inv));
+        }
+      }
+    }
+  } else {
+    float m = -INFINITY;
+    for (int j = lane; j <= t; j += 64) m = fmaxf(m, sr[j] * scale);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int j = lane; j <= t; j += 64) l += __expf(sr[j] * scale - m);
+    const float inv = 1.0f / wave_sum(l);
+    for (int j = lane; j < Tp; j += 64) pr[j] = from_f32<T>(j <= t ? __expf(sr[j] * scale - m) * inv : 0.f);
+  }
 }
 
-// dS row (z, t) = P (dP - sum_j P dP) * scale (P is 0 past t and in the pads)
-template <typename T>
+// dS row (z, t) = P (dP - sum_{j <= t} P dP) * scale for j <= t, 0 elsewhere
+// (dP is read only at j <= t: the tiles above the diagonal are not computed)
+template <typename T, int NV>
 __global__ void __launch_bounds__(256) attn_bwd_ds_kernel(const T* __restrict__ P, const float* __restrict__ dP,
                                                           T* __restrict__ dS, int Z, int Tn, int Tp, float scale) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (long long)Z * Tn) return;
+  const int t = (int)(row % Tn);
   const T* pr = P + row * Tp;
   const float* gr = dP + row * Tp;
-  float s = 0.f;
-  for (int j = lane; j < Tp; j += 64) s = fmaf(to_f32(pr[j]), gr[j], s);
-  const float dd = wave_sum(s);
   T* out = dS + row * Tp;
-  for (int j = lane; j < Tp; j += 64) out[j] = from_f32<T>(to_f32(pr[j]) * (gr[j] - dd) * scale);
+  if constexpr (NV > 0) {
+    float p[NV][4], g[NV][4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = i * 256 + lane * 4;
+      if (j <= t) {
+        const float4 x = *reinterpret_cast<const float4*>(gr + j);
+        g[i][0] = x.x; g[i][1] = x.y; g[i][2] = x.z; g[i][3] = x.w;
+        if constexpr (sizeof(T) == 4) {
+          const float4 y = *reinterpret_cast<const float4*>(pr + j);
+          p[i][0] = y.x; p[i][1] = y.y; p[i][2] = y.z; p[i][3] = y.w;
+        } else {
+          const uint2 y = *reinterpret_cast<const uint2*>(pr + j);
+          p[i][0] = __uint_as_float(y.x << 16); p[i][1] = __uint_as_float(y.x & 0xffff0000u);
+          p[i][2] = __uint_as_float(y.y << 16); p[i][3] = __uint_as_float(y.y & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { p[i][e] = 0.f; g[i][e] = 0.f; }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (j + e > t) { p[i][e] = 0.f; g[i][e] = 0.f; }
+        s = fmaf(p[i][e], g[i][e], s);
+      }
+    }
+    const float dd = wave_sum(s);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = i * 256 + lane * 4;
+      if (j < Tp) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = p[i][e] * (g[i][e] - dd) * scale;   // 0 past t (p = 0)
+        if constexpr (sizeof(T) == 4) *reinterpret_cast<float4*>(out + j) = make_float4(o[0], o[1], o[2], o[3]);
+        else *reinterpret_cast<uint2*>(out + j) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      }
+    }
+  } else {
+    float s = 0.f;
+    for (int j = lane; j <= t; j += 64) s = fmaf(to_f32(pr[j]), gr[j], s);
+    const float dd = wave_sum(s);
+    for (int j = lane; j < Tp; j += 64)
+      out[j] = from_f32<T>(j <= t ? to_f32(pr[j]) * (gr[j] - dd) * scale : 0.f);
+  }
 }
 
 template <typename T>
@@ -487,9 +576,13 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
                      (long long)B * Tn * C, doc);
   // S = Q K^T
   GPT_BWD_TRY(launch_gemm_batched(dt, q, D, k, D, Tn, Tn, D, w.S, Tp,
-                                  BatchStrides{H * hT, hT, H * hT, hT, H * hTT, hTT, H}, Z, st));
-  hipLaunchKernelGGL(attn_bwd_softmax_kernel<T>, dim3(rows_blocks), dim3(256), 0, st, (const float*)w.S, P, Z, Tn, Tp,
-                     scale);
+                                  BatchStrides{H * hT, hT, H * hT, hT, H * hTT, hTT, H}, Z, st, 1));
+  if (Tp <= 1024)
+    hipLaunchKernelGGL((attn_bwd_softmax_kernel<T, 4>), dim3(rows_blocks), dim3(256), 0, st, (const float*)w.S, P, Z,
+                       Tn, Tp, scale);
+  else
+    hipLaunchKernelGGL((attn_bwd_softmax_kernel<T, 0>), dim3(rows_blocks), dim3(256), 0, st, (const float*)w.S, P, Z,
+                       Tn, Tp, scale);
   // dU = P^T dO
   transpose_batched<T, T>(P, Tp, H * hTT, hTT, H, Tn, Tn, PT, Tp, hTT, Tp, Z, st);
   transpose_batched<T, T>(doc, C, (long long)Tn * C, D, H, Tn, D, dOT, Tp, hDT, Tp, Z, st);
@@ -497,9 +590,13 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
                                   BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
   // dP = dO U^T (into the S buffer), dS
   GPT_BWD_TRY(launch_gemm_batched(dt, doc, C, u, D, Tn, Tn, D, w.S, Tp,
-                                  BatchStrides{(long long)Tn * C, D, H * hT, hT, H * hTT, hTT, H}, Z, st));
-  hipLaunchKernelGGL(attn_bwd_ds_kernel<T>, dim3(rows_blocks), dim3(256), 0, st, (const T*)P, (const float*)w.S, dS, Z,
-                     Tn, Tp, scale);
+                                  BatchStrides{(long long)Tn * C, D, H * hT, hT, H * hTT, hTT, H}, Z, st, 1));
+  if (Tp <= 1024)
+    hipLaunchKernelGGL((attn_bwd_ds_kernel<T, 4>), dim3(rows_blocks), dim3(256), 0, st, (const T*)P,
+                       (const float*)w.S, dS, Z, Tn, Tp, scale);
+  else
+    hipLaunchKernelGGL((attn_bwd_ds_kernel<T, 0>), dim3(rows_blocks), dim3(256), 0, st, (const T*)P,
+                       (const float*)w.S, dS, Z, Tn, Tp, scale);
   // dQ = dS K, dK = dS^T Q
   transpose_batched<T, T>(k, D, H * hT, hT, H, Tn, D, KT, Tp, hDT, Tp, Z, st);
   GPT_BWD_TRY(launch_gemm_batched(dt, dS, Tp, KT, Tp, Tn, D, Tp, dqkv, 3 * C,
@@ -516,6 +613,21 @@ hipError_t launch_attention_backward(int dtype, const void* q, const void* k, co
   if (dtype == 0)
     return attn_bwd_t<float>((const float*)q, (const float*)k, (const float*)u, dout, dqkv, B, H, T, D, w, st);
   return attn_bwd_t<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)u, dout, dqkv, B, H, T, D, w, st);
+}
+
+// out[i] += sum over z < S (in order) of part[z * n + i]
+__global__ void __launch_bounds__(256) add_partials_kernel(float* __restrict__ out, const float* __restrict__ part,
+                                                           long long n, int S) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    float s = 0.f;
+    for (int z = 0; z < S; ++z) s += part[z * n + i];
+    out[i] += s;
+  }
+}
+
+hipError_t launch_add_partials(float* out, const float* part, long long n, int S, hipStream_t st) {
+  hipLaunchKernelGGL(add_partials_kernel, dim3(grid_for(n)), dim3(256), 0, st, out, part, n, S);
+  return hipGetLastError();
 }
 
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st) {

@@ -1517,7 +1517,7 @@ hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyW
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, int M, int N, int K,
-                    float* __restrict__ out, int ldo, BatchStrides bs) {
+                    float* __restrict__ out, int ldo, BatchStrides bs, int causal) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   __shared__ __align__(16) T smem[G::SMEM_ELEMS];
   const int z = blockIdx.y, b = z / bs.H, h = z - b * bs.H;
@@ -1528,6 +1528,9 @@ gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, i
   int mt, nt;
   tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
+  // causal score products: a tile wholly above the diagonal (every column n >
+  // every row m) is never read, so it is not computed (uniform exit)
+  if (causal && n0 > m0 + BM - 1) return;
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
   float2 pre[G::TM][G::TN][8];
@@ -1540,28 +1543,30 @@ gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, i
 
 template <typename T, int BM, int BN, int BK, int WM, int WN>
 static hipError_t run_batched(const T* A, int lda, const T* W, int ldw, int M, int N, int K, float* out, int ldo,
-                              const BatchStrides& bs, int Z, hipStream_t st) {
+                              const BatchStrides& bs, int Z, int causal, hipStream_t st) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   const dim3 grid(((M + BM - 1) / BM) * ((N + BN - 1) / BN), Z);
   if (K % BK == 0)
     hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, false>), grid, dim3(G::NT), 0, st, A, lda, W, ldw,
-                       M, N, K, out, ldo, bs);
+                       M, N, K, out, ldo, bs, causal);
   else
     hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, true>), grid, dim3(G::NT), 0, st, A, lda, W, ldw,
-                       M, N, K, out, ldo, bs);
+                       M, N, K, out, ldo, bs, causal);
   return hipGetLastError();
 }
 
-// out_z [M, N] fp32 = A_z [M, K] . W_z [N, K]^T for z < Z (K a multiple of 8, or of 4 in fp32)
+// out_z [M, N] fp32 = A_z [M, K] . W_z [N, K]^T for z < Z (K a multiple of 8, or of 4 in fp32).
+// causal: tiles wholly above the diagonal are left unwritten.
 hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
-                               float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st) {
+                               float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st, int causal) {
   if (dtype == 0)
     return run_batched<float, 64, 64, 32, 32, 32>((const float*)A, lda, (const float*)W, ldw, M, N, K, out, ldo, bs,
-                                                  Z, st);
+                                                  Z, causal, st);
   if (N >= 128)
     return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs,
-                                                   Z, st);
-  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs, Z, st);
+                                                   Z, causal, st);
+  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs, Z,
+                                               causal, st);
 }
 
 // Loss gradient of the logits A W^T ([M, C] x [V, C]^T) into dz [M, V] (ld).

@@ -498,9 +498,12 @@ BwdPlan bwd_plan(const gpt_config* c, int B, int T) {
 // zero-padded transposes the gradient products read ([rows, Mp] with Mp = M
 // rounded up to 64, and the four weight transposes), and the fp32 gradients
 // of the intermediate tensors.
+constexpr int DW_SPLIT = 4;
+
 struct BlkPlan {
   size_t a1, q, k, v, o, x1, a2, uf, hm, dyc, dyT, hT, dh, duc, duT, a2T, da, dx1, dx1c, dx1T, oT, dout, dqkv,
-      dqkvc, dqkvT, a1T, aS, aP, aPT, adS, adST, adoc, adOT, aKT, aQT, wfpT, wfcT, wpT, waT, mu, rs, part, total;
+      dqkvc, dqkvT, a1T, aS, aP, aPT, adS, adST, adoc, adOT, aKT, aQT, wfpT, wfcT, wpT, waT, mu, rs, part, wpart,
+      total;
   int Mp, Fp, C3p, Tp, nchunks;
 };
 
@@ -532,6 +535,8 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   p.mu = take(M * 4); p.rs = take(M * 4);
   // column partials: the widest of the sums (3C for the c_attn bias, F for c_fc's, 2C for a LayerNorm)
   p.part = take((size_t)p.nchunks * (3 * C > F ? 3 * C : F) * 4);
+  // split-K partials of the weight gradients: up to DW_SPLIT slices of the largest [3C, C] or [F, C]
+  p.wpart = take((size_t)DW_SPLIT * C * (3 * C > F ? 3 * C : F) * 4);
   p.total = off;
   return p;
 }
@@ -861,6 +866,18 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   const size_t rowf = (size_t)M * C * 4;
   auto W = [&](size_t off) { return at<char>(ws, off); };
   auto Wf = [&](size_t off) { return at<float>(ws, off); };
+  // weight gradient out [R, N] += A [R, Mp] . B [N, Mp]^T (contraction over the
+  // padded tokens): split into S slices of Mp run as one batched launch into
+  // fp32 partials, then added in slice order (deterministic)
+  auto dW = [&](const void* A, const void* Bm, int R, int N, float* out) -> hipError_t {
+    int S = DW_SPLIT;
+    while (S > 1 && Mp % (64 * S) != 0) S /= 2;
+    const int Ks = Mp / S;
+    const hipError_t e = launch_gemm_batched(dt, A, Mp, Bm, Mp, R, N, Ks, Wf(pl.wpart), N,
+                                             BatchStrides{Ks, 0, Ks, 0, (long long)R * N, 0, 1}, S, st);
+    if (e != hipSuccess) return e;
+    return launch_add_partials(out, Wf(pl.wpart), (long long)R * N, S, st);
+  };
 
   // ---- recompute the block's forward from its input x
   LnArgs la{};
@@ -898,14 +915,14 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dyc), C, W(pl.wfpT), C, M, F, C, Wf(pl.dh), F, 0, st));
   GPT_TRY(launch_transpose(dt, W(pl.dyc), C, M, C, W(pl.dyT), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.hm), F, M, F, W(pl.hT), Mp, st));
-  GPT_TRY(launch_gemm_f32out(dt, W(pl.dyT), Mp, W(pl.hT), Mp, C, F, Mp, grads + w.fcproj_w, F, 1, st));
+  GPT_TRY(dW(W(pl.dyT), W(pl.hT), C, F, grads + w.fcproj_w));
   GPT_TRY(launch_colsum(M, C, dy, Wf(pl.part), grads + w.fcproj_b, st));
   // du = dh * GELU'(u); dWfc += du^T a2; dbfc += sum du; da2 = du Wfc
   GPT_TRY(launch_act_bwd(dt, Wf(pl.dh), W(pl.uf), (long long)M * F, act, W(pl.duc), st));
   GPT_TRY(launch_colsum(M, F, Wf(pl.dh), Wf(pl.part), grads + w.fc_b, st));
   GPT_TRY(launch_transpose(dt, W(pl.duc), F, M, F, W(pl.duT), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.a2), C, M, C, W(pl.a2T), Mp, st));
-  GPT_TRY(launch_gemm_f32out(dt, W(pl.duT), Mp, W(pl.a2T), Mp, F, C, Mp, grads + w.fc_w, C, 1, st));
+  GPT_TRY(dW(W(pl.duT), W(pl.a2T), F, C, grads + w.fc_w));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.duc), F, W(pl.wfcT), pl.Fp, M, C, F, Wf(pl.da), C, 0, st));
   // dx1 = dy + LN2 backward
   float* dx1 = Wf(pl.dx1);
@@ -917,7 +934,7 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_cast_rows(dt, dx1, (long long)M * C, W(pl.dx1c), st));
   GPT_TRY(launch_transpose(dt, W(pl.dx1c), C, M, C, W(pl.dx1T), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.o), C, M, C, W(pl.oT), Mp, st));
-  GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1T), Mp, W(pl.oT), Mp, C, C, Mp, grads + w.proj_w, C, 1, st));
+  GPT_TRY(dW(W(pl.dx1T), W(pl.oT), C, C, grads + w.proj_w));
   GPT_TRY(launch_colsum(M, C, dx1, Wf(pl.part), grads + w.proj_b, st));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1c), C, W(pl.wpT), C, M, C, C, Wf(pl.dout), C, 0, st));
   const AttnBwdWs aw{Wf(pl.aS), W(pl.aP), W(pl.aPT), W(pl.adS), W(pl.adST), W(pl.adoc), W(pl.adOT), W(pl.aKT),
@@ -928,7 +945,7 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_cast_rows(dt, Wf(pl.dqkv), (long long)M * 3 * C, W(pl.dqkvc), st));
   GPT_TRY(launch_transpose(dt, W(pl.dqkvc), 3 * C, M, 3 * C, W(pl.dqkvT), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.a1), C, M, C, W(pl.a1T), Mp, st));
-  GPT_TRY(launch_gemm_f32out(dt, W(pl.dqkvT), Mp, W(pl.a1T), Mp, 3 * C, C, Mp, grads + w.attn_w, C, 1, st));
+  GPT_TRY(dW(W(pl.dqkvT), W(pl.a1T), 3 * C, C, grads + w.attn_w));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dqkvc), 3 * C, W(pl.waT), pl.C3p, M, C, 3 * C, Wf(pl.da), C, 0, st));
   // dx = dx1 + LN1 backward
   GPT_TRY(hipMemcpyAsync(dx, dx1, rowf, hipMemcpyDeviceToDevice, st));
