@@ -50,6 +50,7 @@ class GPTConfig:
     arch: int = 0     # 0 = GPT-2 blocks, 1 = LLaMA-style blocks (RMSNorm, RoPE, SwiGLU, GQA, no biases)
     n_kv_head: int = 0  # LLaMA: K/V heads shared by groups of query heads (0 = n_head)
     rope_theta: float = 10000.0
+    alibi: int = 0      # LLaMA-style only: ALiBi distance bias in place of RoPE
 
     @property
     def head_dim(self) -> int:
@@ -198,7 +199,8 @@ def unpack_f64(cfg: GPTConfig, params: Dict[str, np.ndarray]) -> dict:
     variant names 'act' ('tanh' or 'erf') and 'norm' ('pre' or 'post')."""
     if cfg.arch == 1:
         out = {"arch": "llama", "wte": params["wte"].astype(np.float64), "rmsf_g": params["rmsf_g"].astype(np.float64),
-               "n_kv_head": cfg.kv_heads, "rope_theta": float(cfg.rope_theta), "layers": []}
+               "n_kv_head": cfg.kv_heads, "rope_theta": float(cfg.rope_theta), "alibi": bool(cfg.alibi),
+               "layers": []}
         if cfg.untied:
             out["head_w"] = params["head_w"].astype(np.float64)
         for l in range(cfg.n_layer):

@@ -22,7 +22,9 @@ Readings where the pages leave a step open (each listed with its pin in the
 project's design notes): d in theta_i is the head width D; RMSNorm is
 g * x / sqrt(mean(x^2) + eps) with the same eps as the LayerNorm models;
 the projections carry no bias; attention scales by 1/sqrt(D) and masks the
-future as the GPT-2 model does; query head h reads K/V head h // (H / Hkv).
+future as the GPT-2 model does; query head h reads K/V head h // (H / Hkv);
+ALiBi (the page's alternative, [P4] §5.3) replaces the rotation with the
+distance bias -m_h |i - j|, slopes m_h = 2^(-8 (h+1) / H).
 Weight storage (a layout choice, not arithmetic): wqkv_w stacks the rows of
 W_q [H*D, C], W_k [Hkv*D, C], W_v [Hkv*D, C]; w13_w interleaves the rows of
 W1 (gate, even rows) and W3 (up, odd rows).
@@ -81,18 +83,28 @@ def swiglu_mlp(a: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
     return (silu(gate) * up) @ w2.T
 
 
-def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+def alibi_slopes(H: int) -> np.ndarray:
+    """Per-head ALiBi slopes, a geometric series ([P4] §5.3 gives no
+    formula; the reading taken is the ALiBi paper's m_h = 2^(-8 (h+1) / H))."""
+    return 2.0 ** (-8.0 * (np.arange(H) + 1) / H)
+
+
+def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, slopes: Optional[np.ndarray] = None) -> np.ndarray:
     """Causal attention where query head h reads K/V head h // (H / Hkv)
     ([P4] §6.2).  q [B, H, T, D], k, v [B, Hkv, Tk, D] with the queries at the
-    last T of the Tk key positions.  Returns [B, H, T, D]."""
+    last T of the Tk key positions.  With ALiBi slopes the scores are
+    q.k / sqrt(D) - m_h |i - j| ([P4] §5.3).  Returns [B, H, T, D]."""
     B, H, T, D = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     grp = H // Hkv
     y = np.empty_like(q)
     off = Tk - T
+    dist = (off + np.arange(T))[:, None] - np.arange(Tk)[None, :]     # i - j
     for b in range(B):
         for h in range(H):
             s = q[b, h] @ k[b, h // grp].T / math.sqrt(D)            # [T, Tk]
+            if slopes is not None:
+                s = s - slopes[h] * np.abs(dist)
             mask = np.arange(Tk)[None, :] > (off + np.arange(T))[:, None]
             s = np.where(mask, -np.inf, s)
             y[b, h] = O.softmax_rows(s) @ v[b, h // grp]
@@ -109,22 +121,24 @@ def _split_qkv(x_a: np.ndarray, lp: dict, H: int, Hkv: int, D: int):
 
 
 def block(x: np.ndarray, lp: dict, H: int, Hkv: int, theta: float, eps: float,
-          cache: Optional[dict] = None, pos0: int = 0) -> np.ndarray:
+          cache: Optional[dict] = None, pos0: int = 0, alibi: bool = False) -> np.ndarray:
     """One LLaMA block ([P4] §6.1) on x [B, T, C] at positions pos0 .. pos0+T-1.
     With a cache dict (keys 'k', 'v' of [B, Hkv, t, D]) the rotated keys and
-    the values are appended and attention reads every cached position."""
+    the values are appended and attention reads every cached position.  alibi:
+    no rotation; the scores carry the ALiBi distance bias instead ([P4] §5.3)."""
     B, T, C = x.shape
     D = C // H
     a = rms_norm(x, lp["rms1_g"], eps)
     q, k, v = _split_qkv(a, lp, H, Hkv, D)
     pos = pos0 + np.arange(T)
-    q, k = rope(q, pos, theta), rope(k, pos, theta)
+    if not alibi:
+        q, k = rope(q, pos, theta), rope(k, pos, theta)
     if cache is not None:
         if "k" in cache:
             k = np.concatenate([cache["k"], k], axis=2)
             v = np.concatenate([cache["v"], v], axis=2)
         cache["k"], cache["v"] = k, v
-    y = gqa_attention(q, k, v).transpose(0, 2, 1, 3).reshape(B, T, C)
+    y = gqa_attention(q, k, v, alibi_slopes(H) if alibi else None).transpose(0, 2, 1, 3).reshape(B, T, C)
     x = x + y @ lp["wo_w"].T
     return x + swiglu_mlp(rms_norm(x, lp["rms2_g"], eps), lp["w13_w"], lp["w2_w"])
 
@@ -133,7 +147,7 @@ def final_hidden(params: dict, idx: np.ndarray, H: int, eps: float = 1e-5) -> np
     """Token embedding (no position table), the blocks, final RMSNorm ([P4] §6.3)."""
     x = params["wte"][np.asarray(idx)]
     for lp in params["layers"]:
-        x = block(x, lp, H, params["n_kv_head"], params["rope_theta"], eps)
+        x = block(x, lp, H, params["n_kv_head"], params["rope_theta"], eps, alibi=params.get("alibi", False))
     return rms_norm(x, params["rmsf_g"], eps)
 
 
@@ -179,7 +193,8 @@ def greedy_cached(params: dict, prompt: np.ndarray, steps: int, H: int, eps: flo
     for it in range(steps + 1):
         x = params["wte"][cur]
         for lp, c in zip(params["layers"], caches):
-            x = block(x, lp, H, params["n_kv_head"], params["rope_theta"], eps, cache=c, pos0=pos0)
+            x = block(x, lp, H, params["n_kv_head"], params["rope_theta"], eps, cache=c, pos0=pos0,
+                      alibi=params.get("alibi", False))
         pos0 += cur.shape[1]
         z = O.head(params, rms_norm(x[:, -1], params["rmsf_g"], eps))
         t = O.argmax_lowest(z)

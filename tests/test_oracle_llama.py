@@ -12,6 +12,9 @@
 * parameter counts: LLaMA-7B 6.7B and LLaMA-13B 13B of the page's table
   (vocabulary 32000, untied head: the pages give neither, a reading);
 * greedy decoding with caches equals recomputation;
+* ALiBi: slopes 1/2 .. 1/256 at H = 8 (geometric), a brute-force biased
+  attention, torch SDPA with an additive bias mask, zero slopes reducing to
+  plain attention, cache = recompute;
 * planted mistakes.
 """
 import dataclasses as dc
@@ -221,3 +224,73 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         with monkeypatch.context() as m:
             m.setattr(L, name, fn)
             assert not _pins_pass(), f"planted mistake {fn.__name__} went unnoticed"
+
+
+# --------------------------------------------------------------------------
+# ALiBi
+# --------------------------------------------------------------------------
+def test_alibi_slopes_and_bias_brute_force():
+    s = L.alibi_slopes(8)
+    np.testing.assert_allclose(s, [2.0 ** -(k + 1) for k in range(8)])        # H = 8: 1/2, 1/4, ..., 1/256
+    np.testing.assert_allclose(s[1:] / s[:-1], 2.0 ** (-8 / 8))                 # geometric
+    np.testing.assert_allclose(L.alibi_slopes(4), [2 ** -2, 2 ** -4, 2 ** -6, 2 ** -8])
+    rng = np.random.default_rng(20)
+    q, k, v = rng.normal(size=(1, 2, 5, 4)), rng.normal(size=(1, 2, 5, 4)), rng.normal(size=(1, 2, 5, 4))
+    got = L.gqa_attention(q, k, v, np.array([0.5, 0.25]))
+    for h, m in enumerate((0.5, 0.25)):
+        for i in range(5):
+            sc = [float(q[0, h, i] @ k[0, h, j]) / 2.0 - m * (i - j) for j in range(i + 1)]
+            w = np.exp(np.array(sc) - max(sc))
+            np.testing.assert_allclose(got[0, h, i], (w / w.sum()) @ v[0, h, :i + 1], atol=1e-14)
+    # zero slopes: plain causal attention
+    np.testing.assert_allclose(L.gqa_attention(q, k, v, np.zeros(2)), L.gqa_attention(q, k, v), atol=1e-15)
+
+
+def test_alibi_matches_torch_sdpa_with_a_bias_mask():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    H, Hkv, T, D = 4, 2, 9, 8
+    q, k, v = rng.normal(size=(2, H, T, D)), rng.normal(size=(2, Hkv, T, D)), rng.normal(size=(2, Hkv, T, D))
+    sl = L.alibi_slopes(H)
+    i = np.arange(T)
+    bias = -sl[:, None, None] * np.abs(i[:, None] - i[None, :])
+    bias = np.where(i[None, :] > i[:, None], -np.inf, bias)                 # causal
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=torch.from_numpy(bias)[None],
+        enable_gqa=True).numpy()
+    np.testing.assert_allclose(L.gqa_attention(q, k, v, sl), ref, atol=1e-13)
+
+
+def test_alibi_cached_decode_equals_recompute():
+    cfg = dc.replace(CFG, alibi=1)
+    P = _P(cfg, seed=22)
+    assert P["alibi"]
+    prompt = synth.make_ids(cfg, 2, 5, seed=22)
+    t1, z1 = L.greedy_recompute(P, prompt, 6, cfg.n_head)
+    t2, z2 = L.greedy_cached(P, prompt, 6, cfg.n_head)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_allclose(z1, z2, rtol=1e-11, atol=1e-11)
+    # the model carries no absolute position: a sequence's last logits do not
+    # change when the rotation base changes (it is unused with ALiBi)
+    P2 = dict(P, rope_theta=123.0)
+    np.testing.assert_allclose(L.forward(P2, prompt, cfg.n_head)[0], L.forward(P, prompt, cfg.n_head)[0])
+
+
+def test_alibi_pins_catch_planted_mistakes(monkeypatch):
+    torch = pytest.importorskip("torch")
+
+    def pins():
+        try:
+            test_alibi_slopes_and_bias_brute_force()
+            test_alibi_matches_torch_sdpa_with_a_bias_mask()
+        except AssertionError:
+            return False
+        return True
+
+    assert pins()
+    orig = L.alibi_slopes
+    for fn in (lambda H: 2.0 ** (-8.0 * np.arange(H) / H), lambda H: 2.0 ** (-4.0 * (np.arange(H) + 1) / H),
+               lambda H: -orig(H)):
+        with monkeypatch.context() as m:
+            m.setattr(L, "alibi_slopes", fn)
+            assert not pins()
