@@ -174,6 +174,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;   // exponent reference (log2 domain) and lane-partial sum
   const float sc = a.scale_log2;
+  // ALiBi slope m_h = 2^(-8 (h+1) / H) divided by the 1/sqrt(D) score scale
+  const float alibi_k = a.alibi ? exp2f(-8.0f * (float)(h + 1) / (float)a.H) * sqrtf((float)D) : 0.f;
 
   const int kv_end = min(T_seq, q0 + BQ);  // keys [0, kv_end) can be visible to this block
   // one key tile: scores, online softmax, O^T update, from LDS buffer `cur`
@@ -187,6 +189,13 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
         const T* krow = &sK[cur][(st * 32 + (lane & 31)) * LDKS + g * MF::KPL];
 #pragma unroll
         for (int i = 0; i < NDI; ++i) s[st] = MF::mma(MF::load(krow + i * MF::KPI), qf[i], s[st]);
+      }
+      if (alibi_k != 0.f) {   // ALiBi (uniform): + (m_h sqrt D)(j - t), i.e. -m_h (t - j) after the 1/sqrt D scale
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[st][r] = fmaf(alibi_k, (float)(kb + st * 32 + acc_row(r, lane) - qcol), s[st][r]);
       }
       if (kb + BKV - 1 > qw0) {   // diagonal tile: mask keys after the query
 #pragma unroll
@@ -358,6 +367,7 @@ __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a)
   float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  const float alibi_l2 = a.alibi ? exp2f(-8.0f * (float)(h + 1) / (float)a.H) * 1.4426950408889634f : 0.f;
   for (int k0 = 0; k0 < n; k0 += UNR * G) {
     uint4 kv[UNR], uv[UNR];
 #pragma unroll
@@ -378,6 +388,7 @@ __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a)
       for (int e = 0; e < VEC; ++e) t = fmaf(qv[e], kf[e], t);
 #pragma unroll
       for (int o = LPK >> 1; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      if (alibi_l2 != 0.f) t = fmaf(alibi_l2, (float)(k0 + u * G + g - (n - 1)), t);   // -m_h (pos - j), log2 units
       s[u] = k0 + u * G + g < n ? t : -INFINITY;
       mb = fmaxf(mb, s[u]);
     }

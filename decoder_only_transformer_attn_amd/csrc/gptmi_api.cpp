@@ -46,6 +46,7 @@ int check_config(const gpt_config* c) {
   const int D = c->n_embd / c->n_head, v = vec_of(c);
   if (c->n_embd % v || c->n_ff % v || D % v || D > 128 || c->n_embd > 2048) return GPT_ERR_CONFIG;
   if (c->arch != 0 && c->arch != 1) return GPT_ERR_CONFIG;
+  if (c->alibi != 0 && (c->alibi != 1 || c->arch != 1)) return GPT_ERR_CONFIG;   // LLaMA-style blocks only
   if (c->arch == 1) {
     // the GPT-2 variant flags do not apply to LLaMA-style blocks
     if (c->activation != 0 || c->post_ln != 0) return GPT_ERR_CONFIG;
@@ -257,8 +258,9 @@ int run_blocks_llama(const Pass& s) {
   SkinnyWs skw{};
   if (s.pl.skpart) skw = SkinnyWs{at<float>(s.ws, s.pl.skpart), SK_PART_TILES, at<int>(s.ws, s.pl.skcnt), SK_COUNTERS};
   const SkinnyWs* sk = s.pl.skpart ? &skw : nullptr;
-  float2* rope = at<float2>(s.ws, s.pl.rope);
-  GPT_TRY(launch_rope_table(rope, cfg->ctx, D, (double)cfg->rope_theta, s.st));
+  const int alibi = cfg->alibi;   // ALiBi: no rotation, a distance bias in the attention scores
+  float2* rope = alibi ? nullptr : at<float2>(s.ws, s.pl.rope);
+  if (!alibi) GPT_TRY(launch_rope_table(rope, cfg->ctx, D, (double)cfg->rope_theta, s.st));
 
   LnArgs la{};
   la.M = M; la.C = C; la.T_seq = T; la.eps = cfg->ln_eps; la.rms = 1;
@@ -295,6 +297,7 @@ int run_blocks_llama(const Pass& s) {
       DecAttnArgs da{};
       da.q = q; da.k = kbuf; da.v = vbuf; da.kv_bh = kv_bh; da.Tmax = s.Tmax; da.pos = s.pos;
       da.o = o; da.o_ld = C; da.B = B; da.H = H; da.D = D; da.scale_log2 = scale_log2; da.Hkv = Hkv;
+      da.alibi = alibi;
       GPT_TRY(launch_attention_decode(dt, da, s.st));
     } else {
       AttnArgs aa{};
@@ -302,7 +305,7 @@ int run_blocks_llama(const Pass& s) {
       aa.k = kbuf; aa.k_bh = kv_bh;
       aa.v = vbuf; aa.v_bh = kv_bh;
       aa.o = o; aa.o_ld = C;
-      aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = Hkv;
+      aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = Hkv; aa.alibi = alibi;
       aa.scale_log2 = scale_log2;
       GPT_TRY(launch_attention(dt, aa, s.st));
     }

@@ -52,6 +52,7 @@ struct DecAttnArgs {
   int B, H, D;
   float scale_log2;
   int Hkv;                             // cache heads; query head h reads head h / (H / Hkv)
+  int alibi;                           // 1: scores carry -m_h (pos - j), m_h = 2^(-8 (h+1) / H)
 };
 
 struct AttnArgs {
@@ -62,6 +63,7 @@ struct AttnArgs {
   int B, H, T_seq, D;
   int Hkv;                             // K/U heads; query head h reads K/U head h / (H / Hkv)
   float scale_log2;                    // log2(e) / sqrt(D)
+  int alibi;                           // 1: scores carry -m_h (t - j), m_h = 2^(-8 (h+1) / H)
 };
 
 // Split-K scratch of the skinny (M <= 64) bf16 products: per-column-tile

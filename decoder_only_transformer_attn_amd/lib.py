@@ -29,7 +29,7 @@ class gpt_config(ctypes.Structure):
                 ("n_head", ctypes.c_int32), ("n_layer", ctypes.c_int32), ("n_ff", ctypes.c_int32),
                 ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
                 ("post_ln", ctypes.c_int32), ("untied_head", ctypes.c_int32), ("arch", ctypes.c_int32),
-                ("n_kv_head", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
+                ("n_kv_head", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("alibi", ctypes.c_int32)]
 
 
 class gpt_sampling(ctypes.Structure):
@@ -99,7 +99,8 @@ def check(status: int) -> None:
 def cfg_c(cfg) -> gpt_config:
     return gpt_config(cfg.vocab, cfg.ctx, cfg.n_embd, cfg.n_head, cfg.n_layer, cfg.n_ff, cfg.ln_eps, cfg.dtype,
                       getattr(cfg, "act", 0), getattr(cfg, "post_ln", 0), getattr(cfg, "untied", 0),
-                      getattr(cfg, "arch", 0), getattr(cfg, "n_kv_head", 0), getattr(cfg, "rope_theta", 10000.0))
+                      getattr(cfg, "arch", 0), getattr(cfg, "n_kv_head", 0), getattr(cfg, "rope_theta", 10000.0),
+                      getattr(cfg, "alibi", 0))
 
 
 def param_count(cfg) -> int:

@@ -85,6 +85,8 @@ typedef struct gpt_config {
                        * activation and post_ln must be 0. */
   int32_t n_kv_head;  /* arch 1: K/V heads (divides n_head; 1 = MQA; 0 = n_head).  arch 0: 0 or n_head. */
   float rope_theta;   /* arch 1: RoPE base (the pages use 10000); > 0 */
+  int32_t alibi;      /* arch 1 only: 1 = ALiBi in place of RoPE ("02 GPT 架构" §5.3): the scores
+                       * carry -m_h |i - j|, m_h = 2^(-8 (h+1) / H) (no rotation); 0 otherwise */
 } gpt_config;
 
 /* Number of unique parameters, closed form ("第 25 章 从小 GPT 到 GPT-2" §25.4):

@@ -214,6 +214,9 @@ def test_llama_config_is_validated():
                 dict(rope_theta=0.0), dict(rope_theta=float("inf")), dict(arch=2)):
         assert count(dc.replace(good, **bad)) == lib.GPT_ERR_CONFIG, bad
     assert count(dc.replace(good, arch=0, n_kv_head=1)) == lib.GPT_ERR_CONFIG   # no grouping in GPT-2 blocks
+    assert count(dc.replace(good, alibi=1)) > 0
+    assert count(dc.replace(good, alibi=2)) == lib.GPT_ERR_CONFIG
+    assert count(dc.replace(good, arch=0, n_kv_head=0, alibi=1)) == lib.GPT_ERR_CONFIG   # LLaMA-style blocks only
     assert count(dc.replace(good, arch=0, n_kv_head=4)) > 0
     # the head backward covers GPT-2 blocks only
     out = ctypes.c_size_t(0)

@@ -6,7 +6,8 @@ key/value cache (caches of Hkv heads, rotated keys).
 Bounds as for the GPT-2 model: fp32 max|dlogit| <= 1e-4 max|z_ref|, loss
 1e-4 relative; bf16 max|dlogit| <= 5e-2, loss 1e-2 relative (bf16 operands,
 fp32 accumulation; the rotary angles come from a double-precision table, so
-they add no error beyond the rounding of Q and K).  Decoding replays the GPU's
+they add no error beyond the rounding of Q and K; the ALiBi bias is one fp32
+FMA per score).  Decoding replays the GPU's
 tokens in the oracle (teacher forcing) and accepts a token whose oracle logit
 is within the tie band of the maximum (fp32 1e-4 max|z|, bf16 0.1).
 """
@@ -62,7 +63,8 @@ def check(cfg, params, ids, targets=None):
 
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 @pytest.mark.parametrize("kw", [dict(n_kv_head=2), dict(n_kv_head=4), dict(n_kv_head=1, untied=1),
-                                dict(n_kv_head=2, n_layer=0), dict(n_kv_head=2, rope_theta=500.0)])
+                                dict(n_kv_head=2, n_layer=0), dict(n_kv_head=2, rope_theta=500.0),
+                                dict(n_kv_head=2, alibi=1)])
 @pytest.mark.parametrize("B,T", [(2, 37), (3, 64)])
 def test_llama_forward_matches_oracle(dtype, kw, B, T):
     cfg = _cfg(dtype=dtype, **kw)
@@ -116,7 +118,8 @@ def run_decode(cfg, params, prompt, steps, Tmax):
 
 
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
-@pytest.mark.parametrize("kw", [dict(n_kv_head=2), dict(n_kv_head=1, untied=1), dict(n_kv_head=4)])
+@pytest.mark.parametrize("kw", [dict(n_kv_head=2), dict(n_kv_head=1, untied=1), dict(n_kv_head=4),
+                                dict(n_kv_head=2, alibi=1)])
 def test_llama_decode_matches_oracle(dtype, kw):
     cfg = _cfg(dtype=dtype, **kw)
     params = synth.make_params(cfg, seed=11, cfg_id=64, init="stress")
