@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "337e35e3b4caecd8a898bb5e06f2d3db5d493860765d26e7648fef2dc45a7eed",
-                "bytes": 1998387947}
+HEAD_TRAFFIC = {"gemm_src_sha256": "6723b88d8d805522072c56df7ce79e64d969a8d9e7f5c4117ee305c9bc0e1051",
+                "bytes": 2001088399}
 
 
 def src_sha(rel):
