@@ -181,8 +181,9 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
   __shared__ float slots[SMP_LDS_SLOTS * SMP_THREADS];
   __shared__ float cw[SMP_THREADS];   // compacted top-k candidates (weight, vocabulary index), or the weights a search narrowed to
   __shared__ int ci[SMP_THREADS];
-  const int tid = threadIdx.x;
-  Blk blk{&sh, 0, tid & 63, tid >> 6};
+  __shared__ uint32_t tshare;         // a threshold found by wave 0 alone
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Blk blk{&sh, 0, lane, wave};
   const int row = blockIdx.x, V = a.V;
   const int npt = (V + SMP_THREADS - 1) / SMP_THREADS;   // <= SMP_MAXPT (checked at launch)
   const int i0 = tid * npt;
@@ -239,11 +240,58 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
     // top-k: T = the k-th largest pattern (largest t with count(w >= t) >= k),
     // then the equal ones with the lowest indices
     if (a.top_k > 0 && a.top_k < V) {
+      // (narrowed like the mass searches below: once at most SMP_THREADS
+      // weights share the leading bits fixed so far, wave 0 finishes on them
+      // with the fixed count of the weights above that range)
       uint32_t t = 0;
-      for (int bit = 29; bit >= 0; --bit) {
+      int bit = 29, above_n = 0, total = 0;
+      bool small = false;
+      for (; bit >= 0; --bit) {
+        if (bit == 22 || bit == 19 || bit == 16 || bit == 13) {
+          const uint32_t lo = t, hi = t + (2u << bit);
+          const int n = sl.sum<int>([&](float v) {
+            const uint32_t b = __float_as_uint(v);
+            return b >= lo && b < hi ? 1 : 0;
+          });
+          int at = blk.exscan(n);
+          total = blk.sum(n);
+          if (total <= SMP_THREADS) {
+            int ab = 0;
+            sl.visit([&](float v, int) {
+              const uint32_t b = __float_as_uint(v);
+              ab += b >= hi ? 1 : 0;
+              if (b >= lo && b < hi) cw[at++] = v;
+            });
+            above_n = blk.sum(ab);   // (its barrier also publishes cw)
+            small = true;
+            break;
+          }
+        }
         const uint32_t c = t | (1u << bit);
         const int n = sl.sum<int>([&](float v) { return __float_as_uint(v) >= c ? 1 : 0; });
         if (blk.sum(n) >= a.top_k) t = c;
+      }
+      if (small) {
+        if (wave == 0) {
+          float v[SMP_THREADS / WAVE];
+#pragma unroll
+          for (int i = 0; i < SMP_THREADS / WAVE; ++i) {
+            const int j = lane + i * WAVE;
+            v[i] = j < total ? cw[j] : 0.f;
+          }
+          for (; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < SMP_THREADS / WAVE; ++i) n += __float_as_uint(v[i]) >= c ? 1 : 0;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+            if (above_n + n >= a.top_k) t = c;
+          }
+          if (lane == 0) tshare = t;
+        }
+        __syncthreads();
+        t = tshare;
       }
       if (t > 0) {   // (t == 0: fewer than k positive weights, all of them stay)
         int above = 0, ties = 0;
@@ -289,18 +337,25 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
     // plus the fixed mass above the range.
     auto threshold = [&](double target, bool ge, uint32_t& t, double& cum) {
       t = 0;
-      bool nar = false;
-      float nv = 0.f;
+      int bit = 29;
       double base = 0.0;
-      for (int bit = 29; bit >= 0; --bit) {
-        if (!nar && !sl.compact && (bit == 22 || bit == 19 || bit == 16 || bit == 13)) {
+      int total = 0;
+      bool small = false;   // the undecided weights (<= SMP_THREADS) are gathered in cw[0, total)
+      if (sl.compact) {     // one weight per thread already
+        cw[tid] = sl.r[0];
+        total = SMP_THREADS;
+        small = true;
+        __syncthreads();
+      }
+      for (; bit >= 0 && !small; --bit) {
+        if (bit == 22 || bit == 19 || bit == 16 || bit == 13) {
           const uint32_t lo = t, hi = t + (2u << bit);
           const int n = sl.sum<int>([&](float v) {
             const uint32_t b = __float_as_uint(v);
             return b >= lo && b < hi ? 1 : 0;
           });
           int at = blk.exscan(n);
-          const int total = blk.sum(n);
+          total = blk.sum(n);
           if (total <= SMP_THREADS) {
             double ab = 0.0;
             sl.visit([&](float v, int) {
@@ -309,15 +364,43 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleArgs a) {
               if (b >= lo && b < hi) cw[at++] = v;
             });
             base = blk.sum(ab);   // (its barrier also publishes cw)
-            nv = tid < total ? cw[tid] : 0.f;
-            nar = true;
+            small = true;
+            break;                // bit is still undecided
           }
         }
         const uint32_t c = t | (1u << bit);
-        double sm;
-        if (nar) sm = base + blk.sum(__float_as_uint(nv) >= c ? wd(nv) : 0.0);
-        else sm = blk.sum(sl.sum<double>([&](float v) { return __float_as_uint(v) >= c ? wd(v) : 0.0; }));
+        const double sm = blk.sum(sl.sum<double>([&](float v) { return __float_as_uint(v) >= c ? wd(v) : 0.0; }));
         if (ge ? sm >= target : sm > target) t = c;
+      }
+      if (small) {
+        // wave 0 finishes the search on the gathered weights, 16 per lane,
+        // with butterfly sums (every lane ends with the same double, so t
+        // stays uniform) and no block barrier per step
+        if (wave == 0) {
+          float v[SMP_THREADS / WAVE];
+#pragma unroll
+          for (int i = 0; i < SMP_THREADS / WAVE; ++i) {
+            const int j = lane + i * WAVE;
+            v[i] = j < total ? cw[j] : 0.f;
+          }
+          for (; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            double p0 = 0.0, p1 = 0.0;
+#pragma unroll
+            for (int i = 0; i < SMP_THREADS / WAVE; i += 2) {
+              p0 += __float_as_uint(v[i]) >= c ? wd(v[i]) : 0.0;
+              p1 += __float_as_uint(v[i + 1]) >= c ? wd(v[i + 1]) : 0.0;
+            }
+            double sm = p0 + p1;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
+            sm += base;
+            if (ge ? sm >= target : sm > target) t = c;
+          }
+          if (lane == 0) tshare = t;
+        }
+        __syncthreads();
+        t = tshare;
       }
       double above = 0.0, eq = 0.0;
       sl.visit([&](float v, int) {   // both sums updated every time (no address select)
