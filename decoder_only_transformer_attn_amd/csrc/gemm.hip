@@ -540,8 +540,9 @@ struct EpiSwiGLU {
   }
 };
 
-// An epilogue with kRaw takes the wave's whole accumulator tile (raw<TM, TN>)
-// instead of the paired-column driver below.
+// An epilogue with kRaw takes the wave's whole accumulator tile (raw<TM, TN,
+// WLB>) instead of the paired-column driver below, together with WLB bytes of
+// LDS (16-byte aligned) that are the wave's own once the main loop is done.
 template <typename E, typename = void>
 struct IsRaw { static constexpr bool value = false; };
 template <typename E>
@@ -553,7 +554,12 @@ struct IsRaw<E, std::void_t<decltype(E::kRaw)>> { static constexpr bool value = 
 // contiguous), the operands of the two gradient products.  In the MFMA
 // accumulator a lane holds four consecutive rows (tokens) of one column, so
 // the transposed copy is one 4-element store per register quad; the row-major
-// copy pairs adjacent columns with the neighbouring lane.
+// copy pairs adjacent columns with the neighbouring lane.  In bf16 with a
+// wave LDS share that holds the wave's whole transposed tile (and ldT a
+// multiple of 8), the quads are first gathered in LDS, tile rows of WM tokens
+// with their 8-byte chunks XOR-swizzled by row so that a quad store of 32
+// consecutive columns meets no bank twice, and then leave as 16-byte stores
+// that cover whole rows of dzT.
 template <typename T>
 struct EpiDz {
   static constexpr bool kPreload = false;
@@ -574,9 +580,14 @@ struct EpiDz {
   __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
   __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
 
-  template <int TM, int TN>
-  __device__ __forceinline__ void raw(const f32x16 (&acc)[TM][TN], int mbase, int nbase, int M, int N) const {
+  template <int TM, int TN, int WLB>
+  __device__ __forceinline__ void raw(const f32x16 (&acc)[TM][TN], int mbase, int nbase, int M, int N,
+                                      char* wl) const {
     constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int WM = TM * 32, WN = TN * 32;
+    constexpr int RB = WM * 2, NC = WM / 4, NU = WM / 8;   // staged row bytes, 8-byte chunks, 16-byte units
+    constexpr bool kStage = sizeof(T) == 2 && WLB >= WN * RB;
+    const bool staged = kStage && (ldT & 7) == 0;         // uniform
     const int lane = threadIdx.x & 63;
     const bool odd = lane & 1;
     const float iv = *inv;
@@ -613,7 +624,11 @@ struct EpiDz {
             const float a = odd ? recv : v[e], b = odd ? v[e + 1] : recv;
             if (m < M && ne < N) store_pair(dz + (long long)m * ld + ne, a, b, ne + 1 < N, true);
           }
-          if (n < N) {
+          if (kStage && staged) {
+            const int r = j * 32 + (lane & 31), c = i * 8 + q * 2 + (lane >> 5);
+            *reinterpret_cast<uint2*>(wl + r * RB + ((c ^ ((r >> 1) & (NC - 1))) << 3)) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          } else if (n < N) {
             T* p = dzT + (long long)n * ldT + m0;
             if (m0 + 3 < M) {
               if constexpr (sizeof(T) == 4) {
@@ -630,6 +645,29 @@ struct EpiDz {
           }
         }
       }
+    if constexpr (kStage) {
+      if (!staged) return;
+      __syncthreads();   // every wave has written its tile (each reads back only its own)
+      // NU lanes per tile row, 64 / NU rows per pass; chunks 2k and 2k + 1 of
+      // row r sit, swapped when the row's swizzle is odd, in unit k ^ (f >> 1)
+#pragma unroll
+      for (int it = 0; it < WN * NU / 64; ++it) {
+        const int r = it * (64 / NU) + lane / NU, k = lane % NU, f = (r >> 1) & (NC - 1);
+        uint4 w = *reinterpret_cast<const uint4*>(wl + r * RB + ((k ^ (f >> 1)) << 4));
+        if (f & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+        const int n = nbase + r, m = mbase + k * 8;
+        if (n >= N || m >= M) continue;
+        T* p = dzT + (long long)n * ldT + m;
+        if (m + 8 <= M) {
+          *reinterpret_cast<uint4*>(p) = w;
+        } else {
+          const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (m + e < M) reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)(h[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
   }
 };
 
@@ -772,8 +810,13 @@ gemm_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, 
   preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
   gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
-  if constexpr (IsRaw<Epi>::value) epi.template raw<G::TM, G::TN>(acc, mb, nb, M, N);
-  else epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  if constexpr (IsRaw<Epi>::value) {
+    constexpr int WLB = (int)(G::SMEM_ELEMS * sizeof(T) / (G::NWM * G::NWN)) & ~15;
+    __syncthreads();   // the tiles of the last K step are read: the LDS is free
+    epi.template raw<G::TM, G::TN, WLB>(acc, mb, nb, M, N, reinterpret_cast<char*>(smem) + wave * WLB);
+  } else {
+    epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  }
 }
 
 // bf16 GEMM through the pipelined main loop, element-wise epilogue.
@@ -812,8 +855,23 @@ gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, i
   preload_pairs<D::TM, D::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[D::TM][D::TN];
   dma_mainloop<BM, BN, WM, WN, K, NST, BK>(A, W, M, N, m0, n0, stages, acc);
-  if constexpr (IsRaw<Epi>::value) epi.template raw<D::TM, D::TN>(acc, mb, nb, M, N);
-  else epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  if constexpr (IsRaw<Epi>::value) {
+    // each wave's share of the (now idle) stages, never straddling two of them
+    constexpr int WPS = (D::NW + NST - 1) / NST, WLB = (D::STAGE / WPS) & ~15;
+    const int sw = __builtin_amdgcn_readfirstlane(wave) / WPS;
+    // (only the stages that exist are named, so no unused array is kept)
+    char* base = s0;
+    if constexpr (NST > 1) base = sw == 1 ? s1 : base;
+    if constexpr (NST > 2) base = sw == 2 ? s2 : base;
+    if constexpr (NST > 3) base = sw == 3 ? s3 : base;
+    if constexpr (NST > 4) base = sw == 4 ? s4 : base;
+    if constexpr (NST > 5) base = sw == 5 ? s5 : base;
+    if constexpr (NST > 6) base = sw == 6 ? s6 : base;
+    if constexpr (NST > 7) base = sw == 7 ? s7 : base;
+    epi.template raw<D::TM, D::TN, WLB>(acc, mb, nb, M, N, base + (wave % WPS) * WLB);
+  } else {
+    epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  }
 }
 
 // ---------------------------------------------------------------------------
