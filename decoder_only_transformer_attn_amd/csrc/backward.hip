@@ -616,17 +616,49 @@ hipError_t launch_attention_backward(int dtype, const void* q, const void* k, co
 }
 
 // out[i] += sum over z < S (in order) of part[z * n + i]
+// out (+)= part[0] + part[1] + ... + part[S-1] (slice order), four elements
+// per thread when n is a multiple of 4 (the slices then stay 16-byte aligned)
+template <bool ACC, int W>
 __global__ void __launch_bounds__(256) add_partials_kernel(float* __restrict__ out, const float* __restrict__ part,
                                                            long long n, int S) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-    float s = 0.f;
-    for (int z = 0; z < S; ++z) s += part[z * n + i];
-    out[i] += s;
+  typedef typename std::conditional<W == 4, float4, float>::type V;
+  const long long nv = n / W;
+  V* o = reinterpret_cast<V*>(out);
+  const V* p = reinterpret_cast<const V*>(part);
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < nv; i += (long long)gridDim.x * 256) {
+    V s = p[i];
+    for (int z = 1; z < S; ++z) {
+      const V t = p[z * nv + i];
+      if constexpr (W == 4) {
+        s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+      } else {
+        s += t;
+      }
+    }
+    if constexpr (ACC) {
+      const V a = o[i];
+      if constexpr (W == 4) {
+        s.x = a.x + s.x; s.y = a.y + s.y; s.z = a.z + s.z; s.w = a.w + s.w;
+      } else {
+        s = a + s;
+      }
+    }
+    o[i] = s;
   }
 }
 
-hipError_t launch_add_partials(float* out, const float* part, long long n, int S, hipStream_t st) {
-  hipLaunchKernelGGL(add_partials_kernel, dim3(grid_for(n)), dim3(256), 0, st, out, part, n, S);
+hipError_t launch_add_partials(float* out, const float* part, long long n, int S, hipStream_t st, int accumulate) {
+  if (n <= 0) return hipSuccess;
+  const bool v4 = n % 4 == 0 && ((uintptr_t)out & 15) == 0 && ((uintptr_t)part & 15) == 0;
+  const long long nv = v4 ? n / 4 : n;
+  if (v4 && accumulate)
+    hipLaunchKernelGGL((add_partials_kernel<true, 4>), dim3(grid_for(nv)), dim3(256), 0, st, out, part, n, S);
+  else if (v4)
+    hipLaunchKernelGGL((add_partials_kernel<false, 4>), dim3(grid_for(nv)), dim3(256), 0, st, out, part, n, S);
+  else if (accumulate)
+    hipLaunchKernelGGL((add_partials_kernel<true, 1>), dim3(grid_for(nv)), dim3(256), 0, st, out, part, n, S);
+  else
+    hipLaunchKernelGGL((add_partials_kernel<false, 1>), dim3(grid_for(nv)), dim3(256), 0, st, out, part, n, S);
   return hipGetLastError();
 }
 

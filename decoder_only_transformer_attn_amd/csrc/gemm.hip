@@ -228,28 +228,32 @@ template <int DPW> __device__ __forceinline__ void wait_groups(int g) {
 }
 
 // Tile (m0, n0)'s load plan: buffer resources over the tile's A and W rows
-// and each lane's offsets; issue(t) sends this wave's share of stage t.
-template <int BM, int BN, int WM, int WN, int K, int NST, int BK>
+// (row strides lda, ldw elements; nk stages of BK columns) and each lane's
+// offsets; issue(t, s) sends this wave's share of stage t into LDS stage s.
+// A resource spans whole rows of the tile that exist, so rows past M (N)
+// read as zero; the host keeps rows * ld * 2 bytes below 2^32.
+template <int BM, int BN, int WM, int WN, int NST, int BK>
 struct DmaLoads {
   typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
   __amdgpu_buffer_rsrc_t rsA, rsB;
   uint32_t voff[D::DPW];
-  int wave;
-  __device__ __forceinline__ DmaLoads(const bf16* A, const bf16* W, int M, int N, int m0, int n0) {
+  int wave, nk;
+  __device__ __forceinline__ DmaLoads(const bf16* A, int lda, const bf16* W, int ldw, int K, int M, int N, int m0,
+                                      int n0) {
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    rsA = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)min(BM, M - m0) * K * sizeof(bf16)));
-    rsB = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)min(BN, N - n0) * K * sizeof(bf16)));
+    nk = K / BK;
+    rsA = make_rsrc(A + (size_t)m0 * lda, (uint32_t)((size_t)min(BM, M - m0) * lda * sizeof(bf16)));
+    rsB = make_rsrc(W + (size_t)n0 * ldw, (uint32_t)((size_t)min(BN, N - n0) * ldw * sizeof(bf16)));
 #pragma unroll
     for (int d = 0; d < D::DPW; ++d) {
       const int ins = wave + d * D::NW;
       constexpr int IA = BM / D::RPI;   // instructions covering A
       const int row = (ins < IA ? ins : ins - IA) * D::RPI + lane / D::CPR, slot = lane % D::CPR;
-      voff[d] = (uint32_t)((row * K + swz<D::CPR>(row, slot) * 8) * sizeof(bf16));
+      voff[d] = (uint32_t)((row * (ins < IA ? lda : ldw) + swz<D::CPR>(row, slot) * 8) * sizeof(bf16));
     }
   }
-  __device__ __forceinline__ void issue(int t, const Stages& st) const {
-    char* s = st.p[t % NST];
+  __device__ __forceinline__ void issue(int t, char* s) const {
 #pragma unroll
     for (int d = 0; d < D::DPW; ++d) {
       const int ins = wave + d * D::NW;
@@ -260,15 +264,18 @@ struct DmaLoads {
   __device__ __forceinline__ void prologue(const Stages& st) const {
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
-      if (t < K / BK) issue(t, st);
+      if (t < nk) issue(t, st.p[t]);
   }
 };
 
+// K > 0: a compile-time depth (rows of K elements, the loop fully unrolled);
+// K == 0: depth Kr (a multiple of BK) and row strides lda, ldw at run time,
+// the loop unrolled by the ring's length so every stage index is constant.
 template <int BM, int BN, int WM, int WN, int K, int NST, int BK>
-__device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N,
-                                             int m0, int n0, const Stages& st, f32x16 (&acc)[WM / 32][WN / 32]) {
+__device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
+                                             int Kr, int M, int N, int m0, int n0, const Stages& st,
+                                             f32x16 (&acc)[WM / 32][WN / 32]) {
   typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
-  constexpr int NK = K / BK;          // stages along K
   constexpr int KS = BK / 16;         // MFMA k-substeps per stage
   constexpr int CPR = D::CPR;
   static_assert(K % BK == 0, "K must be a multiple of the stage depth");
@@ -286,7 +293,7 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
   // Stage layout: A rows [0, BM) then W rows, ROWB bytes each.  Load
   // instruction i (RPI rows) goes to LDS offset 1024 i and is issued by wave
   // i % NW; the wave index is uniform, so the A/W choice stays scalar.
-  const DmaLoads<BM, BN, WM, WN, K, NST, BK> ld(A, W, M, N, m0, n0);
+  const DmaLoads<BM, BN, WM, WN, NST, BK> ld(A, K > 0 ? K : lda, W, K > 0 ? K : ldw, K > 0 ? K : Kr, M, N, m0, n0);
   const int lrow = lane & 31, g = lane >> 5;
   auto ldfrag = [&](const char* s, int ks, bf16x8 (&af)[D::TM], bf16x8 (&bfr)[D::TN]) {
     const int c = ks * 2 + g;
@@ -308,13 +315,7 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
 #pragma unroll
       for (int j = 0; j < D::TN; ++j) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
   };
-  ld.prologue(st);
-#pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    wait_groups<D::DPW>(min(NST - 2, NK - 1 - t));   // this wave's loads of stage t have landed
-    lds_barrier();                                   // ... and every other wave's
-    if (t + NST - 1 < NK) ld.issue(t + NST - 1, st); // into the stage consumed at step t - 1
-    const char* s = st.p[t % NST];
+  auto step = [&](const char* s) {
     bf16x8 af[2][D::TM], bfr[2][D::TN];
     ldfrag(s, 0, af[0], bfr[0]);
 #pragma unroll
@@ -323,6 +324,32 @@ __device__ __forceinline__ void dma_mainloop(const bf16* __restrict__ A, const b
       __builtin_amdgcn_sched_barrier(0);
       mm(af[ks & 1], bfr[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  ld.prologue(st);
+  if constexpr (K > 0) {
+    constexpr int NK = K / BK;        // stages along K
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      wait_groups<D::DPW>(min(NST - 2, NK - 1 - t));   // this wave's loads of stage t have landed
+      lds_barrier();                                   // ... and every other wave's
+      if (t + NST - 1 < NK) ld.issue(t + NST - 1, st.p[(t + NST - 1) % NST]);   // the stage consumed at t - 1
+      step(st.p[t % NST]);
+    }
+  } else {
+    const int NK = ld.nk;
+    for (int t0 = 0; t0 < NK; t0 += NST) {
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int t = t0 + u;
+        if (t >= NK) break;
+        // near the end fewer groups follow stage t: wait for all of them
+        if (t + NST - 2 < NK) wait_groups<D::DPW>(NST - 2);
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (t + NST - 1 < NK) ld.issue(t + NST - 1, st.p[(u + NST - 1) % NST]);
+        step(st.p[u]);
+      }
     }
   }
   __syncthreads();  // every wave is done with the stages: the epilogue may reuse LDS
@@ -682,6 +709,7 @@ struct EpiF32 {
   typedef int ColX;
   float* out;
   int ldo;
+  __device__ __forceinline__ void shift(long long off) { out += off; }
   __device__ __forceinline__ Row row(int) const { return 0; }
   __device__ __forceinline__ Col col(int, bool) const { return 0; }
   __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
@@ -833,7 +861,8 @@ constexpr int dma_waves_per_eu() {
 template <int BM, int BN, int WM, int WN, int K, int NST, int BK, typename Epi>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN, NST, BK>())))
-gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, Epi epi) {
+gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw, int M, int N, int Kr,
+                long long zstride, Epi epi) {
   typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
@@ -854,7 +883,19 @@ gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, i
   typename Epi::Col colv[D::TN];
   preload_pairs<D::TM, D::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[D::TM][D::TN];
-  dma_mainloop<BM, BN, WM, WN, K, NST, BK>(A, W, M, N, m0, n0, stages, acc);
+  if constexpr (K == 0) {
+    // split K: slice blockIdx.y covers columns [y Kr, (y + 1) Kr) and writes
+    // its own output, zstride elements after the previous slice's
+    const int z = blockIdx.y;
+    dma_mainloop<BM, BN, WM, WN, 0, NST, BK>(A + (size_t)z * Kr, lda, W + (size_t)z * Kr, ldw, Kr, M, N, m0, n0,
+                                             stages, acc);
+    Epi e = epi;
+    e.shift((long long)z * zstride);
+    epilogue_pairs<D::TM, D::TN>(acc, pre, colv, mb, nb, M, N, e);
+    return;
+  } else {
+    dma_mainloop<BM, BN, WM, WN, K, NST, BK>(A, K, W, K, K, M, N, m0, n0, stages, acc);
+  }
   if constexpr (IsRaw<Epi>::value) {
     // each wave's share of the (now idle) stages, never straddling two of them
     constexpr int WPS = (D::NW + NST - 1) / NST, WLB = (D::STAGE / WPS) & ~15;
@@ -1203,7 +1244,7 @@ head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, i
 
   f32x16 acc[D::TM][D::TN];
   const Stages stages{{s0, s1, s1, s1, s1, s1, s1, s1}};
-  dma_mainloop<BM, BN, WM, WN, K, 2, 64>(wte, act, V, Mtok, v0, t0, stages, acc);
+  dma_mainloop<BM, BN, WM, WN, K, 2, 64>(wte, K, act, K, K, V, Mtok, v0, t0, stages, acc);
 
   const bool amax = ha.part_idx != nullptr;
   if (amax) {
@@ -1460,7 +1501,18 @@ template <int BM, int BN, int WM, int WN, int K, int NST, int BK, typename Epi>
 static hipError_t run_gemm_dma(const bf16* A, const bf16* W, int M, int N, const Epi& epi, hipStream_t st) {
   const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, K, NST, BK, Epi>), dim3(blocks),
-                     dim3(DmaCfg<BM, BN, WM, WN, NST, BK>::NT), 0, st, A, W, M, N, epi);
+                     dim3(DmaCfg<BM, BN, WM, WN, NST, BK>::NT), 0, st, A, K, W, K, M, N, K, 0LL, epi);
+  return hipGetLastError();
+}
+
+// Run-time depth: S slices of Ks columns (grid.y), slice z's output zstride
+// elements after slice z - 1's (fp32 epilogues with shift()).
+template <int BM, int BN, int WM, int WN, int NST, int BK, typename Epi>
+static hipError_t run_gemm_dma_rt(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int Ks, int S,
+                                  long long zstride, const Epi& epi, hipStream_t st) {
+  const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, 0, NST, BK, Epi>), dim3(blocks, S),
+                     dim3(DmaCfg<BM, BN, WM, WN, NST, BK>::NT), 0, st, A, lda, W, ldw, M, N, Ks, zstride, epi);
   return hipGetLastError();
 }
 
@@ -1638,6 +1690,28 @@ hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V,
                              EpiDz<bf16>{lse, y, inv, (bf16*)dz, ld, (bf16*)dzT, ldT}, st);
 }
 
+// The pipelined path at a run-time depth takes bf16 operands whose rows are
+// 16-byte aligned, a depth that is a multiple of 64 (at least 256), and row
+// strides small enough that 256 rows stay below 4 GB of buffer range.
+static bool f32_rt_ok(const void* A, int lda, const void* W, int ldw, int Ks) {
+  return Ks % 32 == 0 && Ks >= 256 && lda % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)A & 15) == 0 &&
+         ((uintptr_t)W & 15) == 0 && (size_t)256 * lda * 2 < (1ull << 32) && (size_t)256 * ldw * 2 < (1ull << 32);
+}
+
+// S slices (S >= 1) of Ks columns; slice z writes out + z zstride, [M, ldo].
+// 256 x 256 tiles (four 32-deep stages; twice the flops per loaded byte of
+// 128 x 192) once they fill three quarters of the CUs, else 128 x 192 (three
+// 64-deep stages, Ks a multiple of 64).
+template <bool ACC>
+static hipError_t f32out_rt(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int Ks, int S, float* out,
+                            int ldo, long long zstride, hipStream_t st) {
+  const EpiF32<ACC> epi{out, ldo};
+  const long long blocks256 = (long long)((M + 255) / 256) * ((N + 255) / 256) * S;
+  if (blocks256 >= 192 || Ks % 64 != 0)
+    return run_gemm_dma_rt<256, 256, 64, 128, 4, 32>(A, lda, W, ldw, M, N, Ks, S, zstride, epi, st);
+  return run_gemm_dma_rt<128, 192, 32, 96, 3, 64>(A, lda, W, ldw, M, N, Ks, S, zstride, epi, st);
+}
+
 // out [M, N] fp32 (=, or += with accumulate) A [M, K] . W [N, K]^T
 hipError_t launch_gemm_f32out(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                               float* out, int ldo, int accumulate, hipStream_t st) {
@@ -1646,9 +1720,27 @@ hipError_t launch_gemm_f32out(int dtype, const void* A, int lda, const void* W, 
       return dispatch_gemm_tiled((const float*)A, lda, (const float*)W, ldw, M, N, K, EpiF32<true>{out, ldo}, st);
     return dispatch_gemm_tiled((const float*)A, lda, (const float*)W, ldw, M, N, K, EpiF32<false>{out, ldo}, st);
   }
+  // depths without a compile-time main loop (the head's vocabulary and token
+  // contractions, 3C) take the run-time one when the product is large
+  const long long tiles256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  const bool templ = (K == 768 || K == 2048 || K == 3072) && lda == K && ldw == K && tiles256 >= 64;
+  if (!templ && (long long)M * N >= (long long)256 * 1024 * 16 && ldo % 2 == 0 && f32_rt_ok(A, lda, W, ldw, K)) {
+    if (accumulate) return f32out_rt<true>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, 1, out, ldo, 0, st);
+    return f32out_rt<false>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, 1, out, ldo, 0, st);
+  }
   if (accumulate)
     return dispatch_gemm_tiled((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, EpiF32<true>{out, ldo}, st);
   return dispatch_gemm_tiled((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, EpiF32<false>{out, ldo}, st);
+}
+
+// Split-K partials: out + z zstride [M, N] = A[:, z Ks, +Ks) . W[:, z Ks, +Ks)^T
+// for z < S (summed afterwards in a fixed order by launch_add_partials).
+hipError_t launch_gemm_f32_splitk(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int Ks,
+                                  int S, float* out, long long zstride, hipStream_t st) {
+  if (dtype != 0 && N % 2 == 0 && f32_rt_ok(A, lda, W, ldw, Ks))
+    return f32out_rt<false>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, Ks, S, out, N, zstride, st);
+  return launch_gemm_batched(dtype, A, lda, W, ldw, M, N, Ks, out, N, BatchStrides{Ks, 0, Ks, 0, zstride, 0, 1}, S,
+                             st);
 }
 
 // bf16 head tile for C = 768 (vocab x tokens, per-wave vocab x tokens)

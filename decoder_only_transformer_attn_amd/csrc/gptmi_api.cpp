@@ -455,13 +455,31 @@ int check_cache_args(const gpt_config* cfg, void* kc, void* vc, int Tmax, int B)
 }
 
 // Workspace of the head backward.  dz [M, Vp] and its transpose [V, Np], the
-// head matrix's transpose [C, Vp] and a's [C, Np] are zero-padded to multiples
-// of 64 along the contracted axis, so both gradient products run without a
-// K tail.
+// head matrix's transpose [C, Vp] and a's [C, Np] are zero-padded along the
+// contracted axis (Vp to a multiple of 256, Np of 64), so both gradient
+// products run without a K tail.  The vocabulary contraction of da = dz W
+// (a small [M, C] output) is split into S slices of Vp / S (fp32 partials,
+// summed in slice order) so that its 256 x 256 tiles fill the CUs.
 struct BwdPlan {
-  size_t a, aT, ET, dz, dzT, pmax, psum, tgt, tok, bsum, lse, yv, inv, da, mu, rs, lnpart, total;
-  int ntiles, nblocks, Vp, Np, nchunks;
+  size_t a, aT, ET, dz, dzT, pmax, psum, tgt, tok, bsum, lse, yv, inv, da, dapart, mu, rs, lnpart, total;
+  int ntiles, nblocks, Vp, Np, nchunks, S;
 };
+
+// Slices of the vocabulary contraction: the S in {1, 2, 4, 8} with the least
+// time per slice-round (rounds of 256 tiles over the CUs, divided by S), the
+// smallest on a tie; Vp / S stays a multiple of 32 and at least 256.
+static int da_split(int dtype, size_t M, size_t C, int Vp) {
+  if (dtype == 0) return 1;
+  const long long tiles = (long long)((M + 255) / 256) * (long long)((C + 255) / 256);
+  int best = 1;
+  double best_t = (double)((tiles + 255) / 256);
+  for (int S = 2; S <= 8; S *= 2) {
+    if ((Vp / S) % 32 != 0 || Vp % S != 0 || Vp / S < 256) break;
+    const double t = (double)((tiles * S + 255) / 256) / S;
+    if (t < best_t) { best_t = t; best = S; }
+  }
+  return best;
+}
 
 constexpr long long BWD_MAX_ROWS = 1LL << 20;
 
@@ -470,8 +488,9 @@ BwdPlan bwd_plan(const gpt_config* c, int B, int T) {
   const size_t M = (size_t)B * T, C = c->n_embd, V = c->vocab, es = esize(c);
   p.ntiles = head_ntiles(c->dtype, (int)M, c->vocab, c->n_embd, false);
   p.nblocks = ce_reduce_blocks((int)M);
-  p.Vp = (int)align_up(V, 64);
+  p.Vp = (int)align_up(V, 256);
   p.Np = (int)align_up(M, 64);
+  p.S = da_split(c->dtype, M, C, p.Vp);
   p.nchunks = ln_bwd_chunks((int)M);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
@@ -489,6 +508,7 @@ BwdPlan bwd_plan(const gpt_config* c, int B, int T) {
   p.yv = take(M * 4);
   p.inv = take(4);
   p.da = take(M * C * 4);
+  p.dapart = take(p.S > 1 ? (size_t)p.S * M * C * 4 : 0);
   p.mu = take(M * 4);
   p.rs = take(M * 4);
   p.lnpart = take((size_t)p.nchunks * 2 * C * 4);
@@ -538,7 +558,7 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   p.mu = take(M * 4); p.rs = take(M * 4);
   // column partials: the widest of the sums (3C for the c_attn bias, F for c_fc's, 2C for a LayerNorm)
   p.part = take((size_t)p.nchunks * (3 * C > F ? 3 * C : F) * 4);
-  // split-K partials of the weight gradients: up to DW_SPLIT slices of the largest [3C, C] or [F, C]
+  // split-K partials of the weight gradients: room for DW_SPLIT copies of the largest [3C, C] or [F, C]
   p.wpart = take((size_t)DW_SPLIT * C * (3 * C > F ? 3 * C : F) * 4);
   p.total = off;
   return p;
@@ -788,7 +808,13 @@ int gpt_head_backward(const gpt_config* cfg, const void* params, const int32_t* 
   GPT_TRY(launch_transpose(dt, a, C, M, C, aT, pl.Np, st));
   // da = dz W_head (contraction over the padded vocabulary); post-LN: that is dx
   float* da = post ? dx : at<float>(ws, pl.da);
-  GPT_TRY(launch_gemm_f32out(dt, dz, pl.Vp, ET, pl.Vp, M, C, pl.Vp, da, C, 0, st));
+  if (pl.S > 1) {
+    GPT_TRY(launch_gemm_f32_splitk(dt, dz, pl.Vp, ET, pl.Vp, M, C, pl.Vp / pl.S, pl.S, at<float>(ws, pl.dapart),
+                                   (long long)M * C, st));
+    GPT_TRY(launch_add_partials(da, at<float>(ws, pl.dapart), (long long)M * C, pl.S, st, 0));
+  } else {
+    GPT_TRY(launch_gemm_f32out(dt, dz, pl.Vp, ET, pl.Vp, M, C, pl.Vp, da, C, 0, st));
+  }
   // dW_head += dz^T a (contraction over the padded rows)
   GPT_TRY(launch_gemm_f32out(dt, dzT, pl.Np, aT, pl.Np, V, C, pl.Np, grads + P.head_w(), C, 1, st));
   if (!post)
@@ -870,14 +896,17 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   auto W = [&](size_t off) { return at<char>(ws, off); };
   auto Wf = [&](size_t off) { return at<float>(ws, off); };
   // weight gradient out [R, N] += A [R, Mp] . B [N, Mp]^T (contraction over the
-  // padded tokens): split into S slices of Mp run as one batched launch into
-  // fp32 partials, then added in slice order (deterministic)
+  // padded tokens): split into S slices of Mp run as one launch into fp32
+  // partials, then added in slice order (deterministic).  S doubles until
+  // about 256 output tiles of 128 x 192 are in flight (at most 16 slices,
+  // within the partials buffer).
   auto dW = [&](const void* A, const void* Bm, int R, int N, float* out) -> hipError_t {
-    int S = DW_SPLIT;
-    while (S > 1 && Mp % (64 * S) != 0) S /= 2;
+    const long long tiles = (long long)((R + 127) / 128) * ((N + 191) / 192);
+    const long long cap = (long long)DW_SPLIT * C * (3 * C > F ? 3 * C : F);
+    int S = 1;
+    while (S < 16 && tiles * S < 256 && Mp % (64 * 2 * S) == 0 && 2LL * S * R * N <= cap) S *= 2;
     const int Ks = Mp / S;
-    const hipError_t e = launch_gemm_batched(dt, A, Mp, Bm, Mp, R, N, Ks, Wf(pl.wpart), N,
-                                             BatchStrides{Ks, 0, Ks, 0, (long long)R * N, 0, 1}, S, st);
+    const hipError_t e = launch_gemm_f32_splitk(dt, A, Mp, Bm, Mp, R, N, Ks, S, Wf(pl.wpart), (long long)R * N, st);
     if (e != hipSuccess) return e;
     return launch_add_partials(out, Wf(pl.wpart), (long long)R * N, S, st);
   };

@@ -134,6 +134,9 @@ hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const voi
 struct BatchStrides { long long ab, ah, wb, wh, ob, oh; int H; };
 hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                                float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st, int causal = 0);
+// Split-K partials: out + z zstride [M, N] = A[:, z Ks, +Ks) . W[:, z Ks, +Ks)^T, z < S.
+hipError_t launch_gemm_f32_splitk(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int Ks,
+                                  int S, float* out, long long zstride, hipStream_t st);
 // Attention backward scratch: S / dP fp32 [B*H][T][Tp]; P, P^T, dS, dS^T [B*H][T][Tp];
 // dO in the compute dtype [B*T][C]; per-head transposes of dO, K, Q [B*H][D][Tp].
 struct AttnBwdWs { float* S; void* P; void* PT; void* dS; void* dST; void* doc; void* dOT; void* KT; void* QT; int Tp; };
@@ -142,7 +145,8 @@ hipError_t launch_attention_backward(int dtype, const void* q, const void* k, co
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st);
 hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int act, void* dc, hipStream_t st);
 hipError_t launch_colsum(int M, int N, const float* a, float* part, float* out, hipStream_t st);
-hipError_t launch_add_partials(float* out, const float* part, long long n, int S, hipStream_t st);
+// out += (accumulate) or = the S slices part[z n, +n) summed in slice order
+hipError_t launch_add_partials(float* out, const float* part, long long n, int S, hipStream_t st, int accumulate = 1);
 hipError_t launch_embed_backward(const int32_t* idx, int B, int T, int C, int V, const float* dx0, float* dwte,
                                  float* dwpe, hipStream_t st);
 hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const float* part_sum, const float* tgt,
