@@ -275,6 +275,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
+  // the row's log-sum-exp of the scaled scores in log2 units (both lane
+  // halves hold the same reference m_run and total)
+  if (a.lse2 != nullptr && qcol < T_seq && g == 0) a.lse2[(long long)bh * T_seq + qcol] = m_run + __log2f(l_tot);
   if (qcol < T_seq) {
     T* orow = reinterpret_cast<T*>(a.o) + ((long long)b * T_seq + qcol) * a.o_ld + h * D;
 #pragma unroll

@@ -556,6 +556,26 @@ __global__ void __launch_bounds__(256) attn_bwd_ds_kernel(const T* __restrict__ 
   }
 }
 
+// Dv[(b H + h) T + t] = sum_d dO[b, t, h D + d] O[b, t, h D + d]: one wave per
+// (b, t, h), whose D-element slices of dO and O are contiguous.  This is
+// sum_j P[t, j] dP[t, j] (O = P U, dP = dO U^T), the term the softmax's
+// backward subtracts.
+template <typename T>
+__global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const float* __restrict__ dout, const T* __restrict__ o,
+                                                              float* __restrict__ Dv, int B, int H, int Tn, int D) {
+  const int lane = threadIdx.x & 63;
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, t, h), h fastest
+  if (r >= (long long)B * Tn * H) return;
+  const long long bt = r / H;
+  const int h = (int)(r - bt * H);
+  const int b = (int)(bt / Tn), t = (int)(bt - (long long)b * Tn);
+  const long long base = bt * H * D + (long long)h * D;
+  float s = 0.f;
+  for (int d = lane; d < D; d += 64) s = fmaf(dout[base + d], to_f32(o[base + d]), s);
+  s = wave_sum(s);
+  if (lane == 0) Dv[((long long)b * H + h) * Tn + t] = s;
+}
+
 template <typename T>
 static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* dout, float* dqkv, int B, int H,
                              int Tn, int D, const AttnBwdWs& w, hipStream_t st) {
@@ -574,6 +594,29 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
   const int rows_blocks = (int)(((long long)Z * Tn + 3) / 4);
   hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid_for((long long)B * Tn * C)), dim3(256), 0, st, dout,
                      (long long)B * Tn * C, doc);
+  if (sizeof(T) == 2 && w.lse2 != nullptr && w.o != nullptr && w.Dv != nullptr) {
+    // fused: P (and P^T) straight from the score product with the forward's
+    // log-sum-exp; dS (and dS^T) straight from the dP product
+    const int rows = B * Tn * H;
+    hipLaunchKernelGGL(attn_bwd_rowdot_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, dout,
+                       static_cast<const T*>(w.o), w.Dv, B, H, Tn, D);
+    GPT_BWD_TRY(launch_attn_scores_bwd(0, q, D, k, D, Tn, D, BatchStrides{H * hT, hT, H * hT, hT, 0, 0, H}, Z,
+                                       w.lse2, nullptr, P, PT, Tp, scale * 1.4426950408889634f, st));
+    // dU = P^T dO
+    transpose_batched<T, T>(doc, C, (long long)Tn * C, D, H, Tn, D, dOT, Tp, hDT, Tp, Z, st);
+    GPT_BWD_TRY(launch_gemm_batched(dt, PT, Tp, dOT, Tp, Tn, D, Tp, dqkv + 2 * C, 3 * C,
+                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+    GPT_BWD_TRY(launch_attn_scores_bwd(1, doc, C, u, D, Tn, D, BatchStrides{(long long)Tn * C, D, H * hT, hT, 0, 0, H},
+                                       Z, w.Dv, PT, dS, dST, Tp, scale, st));
+    // dQ = dS K, dK = dS^T Q
+    transpose_batched<T, T>(k, D, H * hT, hT, H, Tn, D, KT, Tp, hDT, Tp, Z, st);
+    GPT_BWD_TRY(launch_gemm_batched(dt, dS, Tp, KT, Tp, Tn, D, Tp, dqkv, 3 * C,
+                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+    transpose_batched<T, T>(q, D, H * hT, hT, H, Tn, D, QT, Tp, hDT, Tp, Z, st);
+    GPT_BWD_TRY(launch_gemm_batched(dt, dST, Tp, QT, Tp, Tn, D, Tp, dqkv + C, 3 * C,
+                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+    return hipGetLastError();
+  }
   // S = Q K^T
   GPT_BWD_TRY(launch_gemm_batched(dt, q, D, k, D, Tn, Tn, D, w.S, Tp,
                                   BatchStrides{H * hT, hT, H * hT, hT, H * hTT, hTT, H}, Z, st, 1));
@@ -615,7 +658,6 @@ hipError_t launch_attention_backward(int dtype, const void* q, const void* k, co
   return attn_bwd_t<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)u, dout, dqkv, B, H, T, D, w, st);
 }
 
-// out[i] += sum over z < S (in order) of part[z * n + i]
 // out (+)= part[0] + part[1] + ... + part[S-1] (slice order), four elements
 // per thread when n is a multiple of 4 (the slices then stay 16-byte aligned)
 template <bool ACC, int W>

@@ -710,6 +710,9 @@ struct EpiF32 {
   float* out;
   int ldo;
   __device__ __forceinline__ void shift(long long off) { out += off; }
+  __device__ __forceinline__ EpiF32 at(int b, int h, const BatchStrides& bs) const {
+    return EpiF32{out + b * bs.ob + h * bs.oh, ldo};
+  }
   __device__ __forceinline__ Row row(int) const { return 0; }
   __device__ __forceinline__ Col col(int, bool) const { return 0; }
   __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
@@ -1624,16 +1627,16 @@ hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyW
 // and every operand and the fp32 output start at b * (stride_b) + h * (stride_h)
 // (BatchStrides).
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool KTAIL, typename Epi>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, int ldw, int M, int N, int K,
-                    float* __restrict__ out, int ldo, BatchStrides bs, int causal) {
+                    Epi epi_z, BatchStrides bs, int causal) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   __shared__ __align__(16) T smem[G::SMEM_ELEMS];
   const int z = blockIdx.y, b = z / bs.H, h = z - b * bs.H;
   A += b * bs.ab + h * bs.ah;
   W += b * bs.wb + h * bs.wh;
-  const EpiF32<false> epi{out + b * bs.ob + h * bs.oh, ldo};
+  const Epi epi = epi_z.at(b, h, bs);   // this product's outputs
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
   int mt, nt;
   tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
@@ -1644,24 +1647,30 @@ gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, i
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
   float2 pre[G::TM][G::TN][8];
-  typename EpiF32<false>::Col colv[G::TN];
+  typename Epi::Col colv[G::TN];
   preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
   gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
-  epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  if constexpr (IsRaw<Epi>::value) {
+    constexpr int WLB = (int)(G::SMEM_ELEMS * sizeof(T) / (G::NWM * G::NWN)) & ~15;
+    __syncthreads();   // the tiles of the last K step are read: the LDS is free
+    epi.template raw<G::TM, G::TN, WLB>(acc, mb, nb, M, N, reinterpret_cast<char*>(smem) + wave * WLB);
+  } else {
+    epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
+  }
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN>
-static hipError_t run_batched(const T* A, int lda, const T* W, int ldw, int M, int N, int K, float* out, int ldo,
+template <typename T, int BM, int BN, int BK, int WM, int WN, typename Epi>
+static hipError_t run_batched(const T* A, int lda, const T* W, int ldw, int M, int N, int K, const Epi& epi,
                               const BatchStrides& bs, int Z, int causal, hipStream_t st) {
   typedef GemmCfg<T, BM, BN, BK, WM, WN> G;
   const dim3 grid(((M + BM - 1) / BM) * ((N + BN - 1) / BN), Z);
   if (K % BK == 0)
-    hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, false>), grid, dim3(G::NT), 0, st, A, lda, W, ldw,
-                       M, N, K, out, ldo, bs, causal);
+    hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, false, Epi>), grid, dim3(G::NT), 0, st, A, lda, W,
+                       ldw, M, N, K, epi, bs, causal);
   else
-    hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, true>), grid, dim3(G::NT), 0, st, A, lda, W, ldw,
-                       M, N, K, out, ldo, bs, causal);
+    hipLaunchKernelGGL((gemm_batched_kernel<T, BM, BN, BK, WM, WN, true, Epi>), grid, dim3(G::NT), 0, st, A, lda, W,
+                       ldw, M, N, K, epi, bs, causal);
   return hipGetLastError();
 }
 
@@ -1669,14 +1678,133 @@ static hipError_t run_batched(const T* A, int lda, const T* W, int ldw, int M, i
 // causal: tiles wholly above the diagonal are left unwritten.
 hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                                float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st, int causal) {
+  const EpiF32<false> epi{out, ldo};
   if (dtype == 0)
-    return run_batched<float, 64, 64, 32, 32, 32>((const float*)A, lda, (const float*)W, ldw, M, N, K, out, ldo, bs,
-                                                  Z, causal, st);
+    return run_batched<float, 64, 64, 32, 32, 32>((const float*)A, lda, (const float*)W, ldw, M, N, K, epi, bs, Z,
+                                                  causal, st);
   if (N >= 128)
-    return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs,
-                                                   Z, causal, st);
-  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, out, ldo, bs, Z,
-                                               causal, st);
+    return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, epi, bs, Z,
+                                                   causal, st);
+  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, M, N, K, epi, bs, Z, causal,
+                                               st);
+}
+
+// Score-side products of the attention backward (bf16), one per (b, h):
+// MODE 0: P = exp2(sc q.k - lse2[m]) (the causal softmax, the row's log-sum-exp
+//         in log2 units from the forward pass), from acc = q.k;
+// MODE 1: dS = P (acc - Dv[m]) sc, from acc = dO.u, P read from P^T.
+// Entries with n > m, or past the Tn rows, are written as zeros, so both
+// outputs are whole [Tn][ld] matrices (ld = Tn rounded up to 64; the tile
+// grid covers every column below ld): out [m][n] and outT [n][m].  The
+// transposed copy is gathered in LDS per wave (8-byte chunks XOR-swizzled by
+// row, as for the head's loss gradient) and leaves as 16-byte row stores.
+template <typename T, int MODE>
+struct EpiAttnB {
+  static constexpr bool kPreload = false;
+  static constexpr bool kCompact = true;
+  static constexpr bool kRaw = true;
+  typedef int Row;
+  typedef int Col;
+  typedef int ColX;
+  const float* rowv;   // MODE 0: lse2 [Tn]; MODE 1: Dv [Tn] (dO . O of each row)
+  const T* PT;         // MODE 1: P^T [Tn][ld]
+  T* out;
+  T* outT;
+  int ld, Tn;
+  long long zs;        // elements between consecutive products' [Tn][ld] matrices
+  float sc;            // MODE 0: log2(e) / sqrt(D); MODE 1: 1 / sqrt(D)
+  __device__ __forceinline__ Row row(int) const { return 0; }
+  __device__ __forceinline__ Col col(int, bool) const { return 0; }
+  __device__ __forceinline__ ColX colx(int, const Col& c) const { return c; }
+  __device__ __forceinline__ float2 preload(int, int, bool) const { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ EpiAttnB at(int b, int h, const BatchStrides& bs) const {
+    const long long z = (long long)b * bs.H + h;
+    EpiAttnB e = *this;
+    e.rowv += z * Tn;
+    if (MODE == 1) e.PT += z * zs;
+    e.out += z * zs;
+    e.outT += z * zs;
+    return e;
+  }
+
+  template <int TM, int TN, int WLB>
+  __device__ __forceinline__ void raw(const f32x16 (&acc)[TM][TN], int mbase, int nbase, int, int, char* wl) const {
+    static_assert(sizeof(T) == 2, "bf16 only");
+    constexpr int WM = TM * 32, WN = TN * 32;
+    constexpr int RB = WM * 2, NC = WM / 4, NU = WM / 8;   // staged row bytes, 8-byte chunks, 16-byte units
+    static_assert(WLB >= WN * RB, "the wave's LDS share must hold its transposed tile");
+    const int lane = threadIdx.x & 63;
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = mbase + i * 32 + q * 8 + (lane >> 5) * 4;   // rows m0 .. m0 + 3
+        float r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = m0 + e < Tn ? rowv[m0 + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = nbase + j * 32 + (lane & 31);
+          float v[4];
+          if constexpr (MODE == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = (m0 + e < Tn && n <= m0 + e) ? fast_exp2(fmaf(acc[i][j][4 * q + e], sc, -r4[e])) : 0.f;
+          } else {
+            // P^T[n][m0 .. m0 + 3] (zero past the diagonal and in the pads)
+            uint2 pw = make_uint2(0u, 0u);
+            if (n < Tn && m0 < ld) pw = *reinterpret_cast<const uint2*>(PT + (long long)n * ld + m0);
+            const float p4[4] = {__uint_as_float(pw.x << 16), __uint_as_float(pw.x & 0xffff0000u),
+                                 __uint_as_float(pw.y << 16), __uint_as_float(pw.y & 0xffff0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = p4[e] * (acc[i][j][4 * q + e] - r4[e]) * sc;
+          }
+          // row-major pairs (lanes 2k, 2k + 1 hold columns n, n + 1)
+          const int ne = n & ~1;
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float recv = __shfl_xor(odd ? v[e] : v[e + 1], 1, 64);
+            const int m = m0 + e + (odd ? 1 : 0);
+            const float a = odd ? recv : v[e], b = odd ? v[e + 1] : recv;
+            if (m < Tn && ne < ld) *reinterpret_cast<uint32_t*>(out + (long long)m * ld + ne) = pack_bf16x2(a, b);
+          }
+          const int r = j * 32 + (lane & 31), c = i * 8 + q * 2 + (lane >> 5);
+          *reinterpret_cast<uint2*>(wl + r * RB + ((c ^ ((r >> 1) & (NC - 1))) << 3)) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+    __syncthreads();   // every wave has written its tile (each reads back only its own)
+#pragma unroll
+    for (int it = 0; it < WN * NU / 64; ++it) {
+      const int r = it * (64 / NU) + lane / NU, k = lane % NU, f = (r >> 1) & (NC - 1);
+      uint4 w = *reinterpret_cast<const uint4*>(wl + r * RB + ((k ^ (f >> 1)) << 4));
+      if (f & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+      const int n = nbase + r, m = mbase + k * 8;
+      if (n < Tn && m < ld) *reinterpret_cast<uint4*>(outT + (long long)n * ld + m) = w;   // (m + 8 <= ld)
+    }
+  }
+};
+
+// One launch over the Z = B H products of the attention backward's score side
+// (q . k for MODE 0, dO . u for MODE 1; K = D), see EpiAttnB.
+hipError_t launch_attn_scores_bwd(int mode, const void* A, int lda, const void* W, int ldw, int Tn, int D,
+                                  const BatchStrides& bs, int Z, const float* rowv, const void* PT, void* out,
+                                  void* outT, int ld, float sc, hipStream_t st) {
+  if (ld % 64 != 0 || ld < Tn || Tn <= 0) return hipErrorInvalidValue;
+  const long long zs = (long long)Tn * ld;
+  if (mode == 0) {
+    const EpiAttnB<bf16, 0> e{rowv, nullptr, (bf16*)out, (bf16*)outT, ld, Tn, zs, sc};
+    if (Tn >= 128)
+      return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0,
+                                                     st);
+    return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0, st);
+  }
+  const EpiAttnB<bf16, 1> e{rowv, (const bf16*)PT, (bf16*)out, (bf16*)outT, ld, Tn, zs, sc};
+  if (Tn >= 128)
+    return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0,
+                                                   st);
+  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0, st);
 }
 
 // Loss gradient of the logits A W^T ([M, C] x [V, C]^T) into dz [M, V] (ld).

@@ -525,8 +525,8 @@ constexpr int DW_SPLIT = 4;
 
 struct BlkPlan {
   size_t a1, q, k, v, o, x1, a2, uf, hm, dyc, dyT, hT, dh, duc, duT, a2T, da, dx1, dx1c, dx1T, oT, dout, dqkv,
-      dqkvc, dqkvT, a1T, aS, aP, aPT, adS, adST, adoc, adOT, aKT, aQT, wfpT, wfcT, wpT, waT, mu, rs, part, wpart,
-      total;
+      dqkvc, dqkvT, a1T, aS, aP, aPT, adS, adST, adoc, adOT, aKT, aQT, alse, aDv, wfpT, wfcT, wpT, waT, mu, rs, part,
+      wpart, total;
   int Mp, Fp, C3p, Tp, nchunks;
 };
 
@@ -553,6 +553,7 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   p.aS = take(Z * TT * 4); p.aP = take(Z * TT * es); p.aPT = take(Z * TT * es); p.adS = take(Z * TT * es);
   p.adST = take(Z * TT * es); p.adoc = take(M * C * es); p.adOT = take(Z * DT * es); p.aKT = take(Z * DT * es);
   p.aQT = take(Z * DT * es);
+  p.alse = take(Z * T * 4); p.aDv = take(Z * T * 4);   // per-row log-sum-exp (log2) and dO . O
   p.wfpT = take(F * C * es); p.wfcT = take(C * (size_t)p.Fp * es); p.wpT = take(C * C * es);
   p.waT = take(C * (size_t)p.C3p * es);
   p.mu = take(M * 4); p.rs = take(M * 4);
@@ -927,6 +928,7 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   aa.v = W(pl.v); aa.v_bh = (long long)T * D; aa.o = W(pl.o); aa.o_ld = C;
   aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  aa.lse2 = Wf(pl.alse);
   GPT_TRY(launch_attention(dt, aa, st));
   float* x1 = Wf(pl.x1);
   GPT_TRY(hipMemcpyAsync(x1, x, rowf, hipMemcpyDeviceToDevice, st));
@@ -970,7 +972,7 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_colsum(M, C, dx1, Wf(pl.part), grads + w.proj_b, st));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dx1c), C, W(pl.wpT), C, M, C, C, Wf(pl.dout), C, 0, st));
   const AttnBwdWs aw{Wf(pl.aS), W(pl.aP), W(pl.aPT), W(pl.adS), W(pl.adST), W(pl.adoc), W(pl.adOT), W(pl.aKT),
-                     W(pl.aQT), pl.Tp};
+                     W(pl.aQT), pl.Tp, Wf(pl.alse), W(pl.o), Wf(pl.aDv)};
   GPT_TRY(launch_attention_backward(dt, W(pl.q), W(pl.k), W(pl.v), Wf(pl.dout), Wf(pl.dqkv), B, H, T, D, aw, st));
   // dWattn += dqkv^T a1, dbattn += sum dqkv, da1 = dqkv Wattn
   GPT_TRY(launch_colsum(M, 3 * C, Wf(pl.dqkv), Wf(pl.part), grads + w.attn_b, st));

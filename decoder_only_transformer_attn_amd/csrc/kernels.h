@@ -64,6 +64,8 @@ struct AttnArgs {
   int Hkv;                             // K/U heads; query head h reads K/U head h / (H / Hkv)
   float scale_log2;                    // log2(e) / sqrt(D)
   int alibi;                           // 1: scores carry -m_h (t - j), m_h = 2^(-8 (h+1) / H)
+  float* lse2;                         // optional [B*H][T]: log2 of each row's softmax denominator
+                                       // (the log-sum-exp of the scaled scores, in log2 units)
 };
 
 // Split-K scratch of the skinny (M <= 64) bf16 products: per-column-tile
@@ -139,7 +141,16 @@ hipError_t launch_gemm_f32_splitk(int dtype, const void* A, int lda, const void*
                                   int S, float* out, long long zstride, hipStream_t st);
 // Attention backward scratch: S / dP fp32 [B*H][T][Tp]; P, P^T, dS, dS^T [B*H][T][Tp];
 // dO in the compute dtype [B*T][C]; per-head transposes of dO, K, Q [B*H][D][Tp].
-struct AttnBwdWs { float* S; void* P; void* PT; void* dS; void* dST; void* doc; void* dOT; void* KT; void* QT; int Tp; };
+// With lse2 (from the forward pass), O and Dv set, the bf16 path fuses the
+// softmax into the score product and dS into the dP product (S and dP are
+// then never stored): Dv [B*H][T] receives the rows' dO . O.
+struct AttnBwdWs {
+  float* S; void* P; void* PT; void* dS; void* dST; void* doc; void* dOT; void* KT; void* QT; int Tp;
+  const float* lse2; const void* o; float* Dv;
+};
+hipError_t launch_attn_scores_bwd(int mode, const void* A, int lda, const void* W, int ldw, int Tn, int D,
+                                  const BatchStrides& bs, int Z, const float* rowv, const void* PT, void* out,
+                                  void* outT, int ld, float sc, hipStream_t st);
 hipError_t launch_attention_backward(int dtype, const void* q, const void* k, const void* u, const float* dout,
                                      float* dqkv, int B, int H, int T, int D, const AttnBwdWs& w, hipStream_t st);
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st);

@@ -95,6 +95,12 @@ def test_block_backward_gpt2_width_bf16():
     check_block(cfg, 0, 1, 256, seed=5, init="bench")
 
 
+def test_block_backward_gpt2_width_long_ragged_sequence_bf16():
+    # 1000 positions: score tiles of 128 x 128 with a padded last row / column tile
+    cfg = dc.replace(synth.GPT2, n_layer=1)
+    check_block(cfg, 0, 1, 1000, seed=6, init="bench")
+
+
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 def test_full_gradient_chain_matches_oracle(dtype):
     lib = _lib()
