@@ -95,6 +95,40 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in
   }
 }
 
+// bf16 form of the same with 16-byte accesses (Cc, ld_in and Rp multiples of
+// 8, 16-byte aligned rows): each thread loads 8 consecutive columns of one
+// input row and stores 8 consecutive rows of one output row; the tile sits in
+// LDS row-major with a 2-element pad, so the column gathers of the store phase
+// (8 halfwords, 66 elements apart) spread over the banks.
+__global__ void __launch_bounds__(256) transpose16_kernel(const bf16* __restrict__ in, long long ld_in, int R, int Cc,
+                                                          bf16* __restrict__ out, long long ld_out, int Rp) {
+  constexpr int LDT = 66;
+  __shared__ __align__(16) uint16_t tile[64 * LDT];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, sub = tid >> 3, k = tid & 7;   // 32 rows x 8 chunks per pass
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int i = p * 32 + sub, r = r0 + i, c = c0 + k * 8;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R && c < Cc) w = *reinterpret_cast<const uint4*>(in + (long long)r * ld_in + c);
+    const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)   // 4-byte LDS stores (LDT is even)
+      *reinterpret_cast<uint32_t*>(&tile[i * LDT + k * 8 + 2 * e]) = h[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int oi = p * 32 + sub, c = c0 + oi, r = r0 + k * 8;   // output row c, columns r .. r + 7
+    if (c >= Cc || r >= Rp) continue;
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = (uint32_t)tile[(k * 8 + 2 * e) * LDT + oi] | ((uint32_t)tile[(k * 8 + 2 * e + 1) * LDT + oi] << 16);
+    *reinterpret_cast<uint4*>(out + (long long)c * ld_out + r) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
 // p[r, c] = 0 for r < R, c0 <= c < c1
 template <typename T>
 __global__ void __launch_bounds__(256) zero_cols_kernel(T* __restrict__ p, long long ld, int R, int c0, int c1) {
@@ -112,6 +146,15 @@ template <typename T>
 __global__ void __launch_bounds__(256) cast_rows_kernel(const float* __restrict__ x, long long n, T* __restrict__ out) {
   for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256)
     out[e] = from_f32<T>(x[e]);
+}
+
+// bf16 form, four elements per thread (n a multiple of 4, 16-byte aligned x)
+__global__ void __launch_bounds__(256) cast_rows4_kernel(const float4* __restrict__ x, long long n4,
+                                                         uint2* __restrict__ out) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n4; e += (long long)gridDim.x * 256) {
+    const float4 v = x[e];
+    out[e] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
 }
 
 // LayerNorm backward, one wave per row: dx (overwritten) and the row's mean
@@ -277,6 +320,9 @@ hipError_t launch_transpose(int dtype, const void* in, long long ld_in, int R, i
   if (dtype == 0)
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, (const float*)in, ld_in, R, Cc, (float*)out,
                        (long long)Rp, Rp);
+  else if (Cc % 8 == 0 && ld_in % 8 == 0 && Rp % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0)
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, st, (const bf16*)in, ld_in, R, Cc, (bf16*)out,
+                       (long long)Rp, Rp);
   else
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)in, ld_in, R, Cc, (bf16*)out,
                        (long long)Rp, Rp);
@@ -296,6 +342,9 @@ hipError_t launch_zero_cols(int dtype, void* p, long long ld, int R, int c0, int
 hipError_t launch_cast_rows(int dtype, const float* x, long long n, void* out, hipStream_t st) {
   if (dtype == 0)
     hipLaunchKernelGGL(cast_rows_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, x, n, (float*)out);
+  else if (n % 4 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)out & 7) == 0)
+    hipLaunchKernelGGL(cast_rows4_kernel, dim3(grid_for(n / 4)), dim3(256), 0, st, (const float4*)x, n / 4,
+                       (uint2*)out);
   else
     hipLaunchKernelGGL(cast_rows_kernel<bf16>, dim3(grid_for(n)), dim3(256), 0, st, x, n, (bf16*)out);
   return hipGetLastError();
@@ -592,8 +641,7 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
   T* KT = static_cast<T*>(w.KT);
   T* QT = static_cast<T*>(w.QT);
   const int rows_blocks = (int)(((long long)Z * Tn + 3) / 4);
-  hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid_for((long long)B * Tn * C)), dim3(256), 0, st, dout,
-                     (long long)B * Tn * C, doc);
+  GPT_BWD_TRY(launch_cast_rows(dt, dout, (long long)B * Tn * C, doc, st));
   if (sizeof(T) == 2 && w.lse2 != nullptr && w.o != nullptr && w.Dv != nullptr) {
     // fused: P (and P^T) straight from the score product with the forward's
     // log-sum-exp; dS (and dS^T) straight from the dP product
@@ -605,16 +653,16 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
     // dU = P^T dO
     transpose_batched<T, T>(doc, C, (long long)Tn * C, D, H, Tn, D, dOT, Tp, hDT, Tp, Z, st);
     GPT_BWD_TRY(launch_gemm_batched(dt, PT, Tp, dOT, Tp, Tn, D, Tp, dqkv + 2 * C, 3 * C,
-                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st, 2));
     GPT_BWD_TRY(launch_attn_scores_bwd(1, doc, C, u, D, Tn, D, BatchStrides{(long long)Tn * C, D, H * hT, hT, 0, 0, H},
                                        Z, w.Dv, PT, dS, dST, Tp, scale, st));
     // dQ = dS K, dK = dS^T Q
     transpose_batched<T, T>(k, D, H * hT, hT, H, Tn, D, KT, Tp, hDT, Tp, Z, st);
     GPT_BWD_TRY(launch_gemm_batched(dt, dS, Tp, KT, Tp, Tn, D, Tp, dqkv, 3 * C,
-                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st, 3));
     transpose_batched<T, T>(q, D, H * hT, hT, H, Tn, D, QT, Tp, hDT, Tp, Z, st);
     GPT_BWD_TRY(launch_gemm_batched(dt, dST, Tp, QT, Tp, Tn, D, Tp, dqkv + C, 3 * C,
-                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+                                    BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st, 2));
     return hipGetLastError();
   }
   // S = Q K^T
@@ -630,7 +678,7 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
   transpose_batched<T, T>(P, Tp, H * hTT, hTT, H, Tn, Tn, PT, Tp, hTT, Tp, Z, st);
   transpose_batched<T, T>(doc, C, (long long)Tn * C, D, H, Tn, D, dOT, Tp, hDT, Tp, Z, st);
   GPT_BWD_TRY(launch_gemm_batched(dt, PT, Tp, dOT, Tp, Tn, D, Tp, dqkv + 2 * C, 3 * C,
-                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st, 2));
   // dP = dO U^T (into the S buffer), dS
   GPT_BWD_TRY(launch_gemm_batched(dt, doc, C, u, D, Tn, Tn, D, w.S, Tp,
                                   BatchStrides{(long long)Tn * C, D, H * hT, hT, H * hTT, hTT, H}, Z, st, 1));
@@ -643,11 +691,11 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
   // dQ = dS K, dK = dS^T Q
   transpose_batched<T, T>(k, D, H * hT, hT, H, Tn, D, KT, Tp, hDT, Tp, Z, st);
   GPT_BWD_TRY(launch_gemm_batched(dt, dS, Tp, KT, Tp, Tn, D, Tp, dqkv, 3 * C,
-                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st, 3));
   transpose_batched<T, T>(dS, Tp, H * hTT, hTT, H, Tn, Tn, dST, Tp, hTT, Tp, Z, st);
   transpose_batched<T, T>(q, D, H * hT, hT, H, Tn, D, QT, Tp, hDT, Tp, Z, st);
   GPT_BWD_TRY(launch_gemm_batched(dt, dST, Tp, QT, Tp, Tn, D, Tp, dqkv + C, 3 * C,
-                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st));
+                                  BatchStrides{H * hTT, hTT, H * hDT, hDT, (long long)Tn * 3 * C, D, H}, Z, st, 2));
   return hipGetLastError();
 }
 

@@ -1641,16 +1641,20 @@ gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, i
   int mt, nt;
   tile_of(blockIdx.x, gridDim.x, num_m, num_n, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  // causal score products: a tile wholly above the diagonal (every column n >
-  // every row m) is never read, so it is not computed (uniform exit)
-  if (causal && n0 > m0 + BM - 1) return;
+  // causal 1 (score products): a tile wholly above the diagonal (every column
+  // n > every row m) is never read, so it is not computed (uniform exit).
+  // causal 2 / 3 (contractions against a causal [rows][keys] operand, BM a
+  // multiple of BK): row m's terms vanish for k < m (2) or k > m (3), so the
+  // tile contracts only over [m0, K) or [0, min(K, m0 + BM)).
+  if (causal == 1 && n0 > m0 + BM - 1) return;
+  const int k0 = causal == 2 ? m0 : 0, k1 = causal == 3 ? min(K, m0 + BM) : K;
   const int wave = threadIdx.x >> 6;
   const int mb = m0 + (wave / G::NWN) * WM, nb = n0 + (wave % G::NWN) * WN;
   float2 pre[G::TM][G::TN][8];
   typename Epi::Col colv[G::TN];
   preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
-  gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A, lda, W, ldw, M, N, K, m0, n0, smem, acc);
+  gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A + k0, lda, W + k0, ldw, M, N, k1 - k0, m0, n0, smem, acc);
   if constexpr (IsRaw<Epi>::value) {
     constexpr int WLB = (int)(G::SMEM_ELEMS * sizeof(T) / (G::NWM * G::NWN)) & ~15;
     __syncthreads();   // the tiles of the last K step are read: the LDS is free
@@ -1675,7 +1679,9 @@ static hipError_t run_batched(const T* A, int lda, const T* W, int ldw, int M, i
 }
 
 // out_z [M, N] fp32 = A_z [M, K] . W_z [N, K]^T for z < Z (K a multiple of 8, or of 4 in fp32).
-// causal: tiles wholly above the diagonal are left unwritten.
+// causal 1: tiles wholly above the diagonal are left unwritten; 2 / 3: A_z[m, k]
+// is zero for k < m (2) or k > m (3) and K is a multiple of 64, so each row
+// tile contracts over its nonzero range only.
 hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                                float* out, int ldo, const BatchStrides& bs, int Z, hipStream_t st, int causal) {
   const EpiF32<false> epi{out, ldo};

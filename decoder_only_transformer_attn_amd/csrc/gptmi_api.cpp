@@ -550,7 +550,8 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   // attention backward: per-head score matrices [B*H][T][Tp] and transposes [B*H][D][Tp]
   p.Tp = (int)align_up((size_t)T, 64);
   const size_t Z = (size_t)B * H, TT = (size_t)T * p.Tp, DT = (C / H) * (size_t)p.Tp;
-  p.aS = take(Z * TT * 4); p.aP = take(Z * TT * es); p.aPT = take(Z * TT * es); p.adS = take(Z * TT * es);
+  // (S / dP are stored only by the fp32 path: the bf16 one fuses them away)
+  p.aS = take(c->dtype == 0 ? Z * TT * 4 : 0); p.aP = take(Z * TT * es); p.aPT = take(Z * TT * es); p.adS = take(Z * TT * es);
   p.adST = take(Z * TT * es); p.adoc = take(M * C * es); p.adOT = take(Z * DT * es); p.aKT = take(Z * DT * es);
   p.aQT = take(Z * DT * es);
   p.alse = take(Z * T * 4); p.aDv = take(Z * T * 4);   // per-row log-sum-exp (log2) and dO . O
