@@ -430,6 +430,50 @@ __global__ void __launch_bounds__(256) colsum_part_kernel(int M, int N, const fl
   if (ty == 0 && c < N) part[(long long)blockIdx.y * N + c] = (red[0][tx] + red[1][tx]) + (red[2][tx] + red[3][tx]);
 }
 
+// Column sums with 16-byte loads (N a multiple of 4, a 16-byte aligned): a
+// block sums CS_ROWS rows of 256 columns, its 4 waves taking every 4th row
+// (16 independent loads in flight per thread), then adds the waves' sums in
+// wave order; partials [chunk][N].  The final pass: a block per 64 columns,
+// its 4 waves taking every 4th chunk, then the waves' sums in wave order.
+constexpr int CS_ROWS = 64;
+int colsum_chunks(int M) { return (M + CS_ROWS - 1) / CS_ROWS; }
+
+__global__ void __launch_bounds__(256) colsum_part4_kernel(int M, int N, const float* __restrict__ a,
+                                                           float* __restrict__ part) {
+  __shared__ __align__(16) float red[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 256 + lane * 4;
+  const int r0 = blockIdx.y * CS_ROWS;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < N) {
+#pragma unroll
+    for (int i = 0; i < CS_ROWS / 4; ++i) {
+      const int r = r0 + w + 4 * i;
+      if (r < M) {
+        const float4 v = *reinterpret_cast<const float4*>(a + (long long)r * N + c);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(&red[w][lane * 4]) = s;
+  __syncthreads();
+  const int t = threadIdx.x, col = blockIdx.x * 256 + t;
+  if (col < N) part[(long long)blockIdx.y * N + col] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+}
+
+__global__ void __launch_bounds__(256) colsum_final4_kernel(int N, int nchunks, const float* __restrict__ part,
+                                                            float* __restrict__ out) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  float s = 0.f;
+  if (c < N)
+    for (int k = w; k < nchunks; k += 4) s += part[(long long)k * N + c];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < N) out[c] += ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
 __global__ void __launch_bounds__(256) colsum_final_kernel(int N, int nchunks, const float* __restrict__ part,
                                                            float* __restrict__ out) {
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -643,13 +687,14 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
   const int rows_blocks = (int)(((long long)Z * Tn + 3) / 4);
   GPT_BWD_TRY(launch_cast_rows(dt, dout, (long long)B * Tn * C, doc, st));
   if (sizeof(T) == 2 && w.lse2 != nullptr && w.o != nullptr && w.Dv != nullptr) {
-    // fused: P (and P^T) straight from the score product with the forward's
-    // log-sum-exp; dS (and dS^T) straight from the dP product
+    // fused: P^T straight from the score product with the forward's
+    // log-sum-exp (P itself is not needed); dS and dS^T straight from the dP
+    // product
     const int rows = B * Tn * H;
     hipLaunchKernelGGL(attn_bwd_rowdot_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, dout,
                        static_cast<const T*>(w.o), w.Dv, B, H, Tn, D);
     GPT_BWD_TRY(launch_attn_scores_bwd(0, q, D, k, D, Tn, D, BatchStrides{H * hT, hT, H * hT, hT, 0, 0, H}, Z,
-                                       w.lse2, nullptr, P, PT, Tp, scale * 1.4426950408889634f, st));
+                                       w.lse2, nullptr, nullptr, PT, Tp, scale * 1.4426950408889634f, st));
     // dU = P^T dO
     transpose_batched<T, T>(doc, C, (long long)Tn * C, D, H, Tn, D, dOT, Tp, hDT, Tp, Z, st);
     GPT_BWD_TRY(launch_gemm_batched(dt, PT, Tp, dOT, Tp, Tn, D, Tp, dqkv + 2 * C, 3 * C,
@@ -771,6 +816,13 @@ hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int a
 }
 
 hipError_t launch_colsum(int M, int N, const float* a, float* part, float* out, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (N % 4 == 0 && ((uintptr_t)a & 15) == 0) {
+    const int nch = colsum_chunks(M);
+    hipLaunchKernelGGL(colsum_part4_kernel, dim3((N + 255) / 256, nch), dim3(256), 0, st, M, N, a, part);
+    hipLaunchKernelGGL(colsum_final4_kernel, dim3((N + 63) / 64), dim3(256), 0, st, N, nch, (const float*)part, out);
+    return hipGetLastError();
+  }
   const int nch = ln_bwd_chunks(M);
   hipLaunchKernelGGL(colsum_part_kernel, dim3((N + 63) / 64, nch), dim3(256), 0, st, M, N, a, part);
   hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, st, N, nch, (const float*)part, out);

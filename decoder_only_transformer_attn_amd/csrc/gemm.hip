@@ -1701,7 +1701,8 @@ hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W,
 // MODE 1: dS = P (acc - Dv[m]) sc, from acc = dO.u, P read from P^T.
 // Entries with n > m, or past the Tn rows, are written as zeros, so both
 // outputs are whole [Tn][ld] matrices (ld = Tn rounded up to 64; the tile
-// grid covers every column below ld): out [m][n] and outT [n][m].  The
+// grid covers every column below ld): out [m][n] (skipped when null) and
+// outT [n][m].  The
 // transposed copy is gathered in LDS per wave (8-byte chunks XOR-swizzled by
 // row, as for the head's loss gradient) and leaves as 16-byte row stores.
 template <typename T, int MODE>
@@ -1714,7 +1715,7 @@ struct EpiAttnB {
   typedef int ColX;
   const float* rowv;   // MODE 0: lse2 [Tn]; MODE 1: Dv [Tn] (dO . O of each row)
   const T* PT;         // MODE 1: P^T [Tn][ld]
-  T* out;
+  T* out;              // may be null (only outT is written)
   T* outT;
   int ld, Tn;
   long long zs;        // elements between consecutive products' [Tn][ld] matrices
@@ -1728,7 +1729,7 @@ struct EpiAttnB {
     EpiAttnB e = *this;
     e.rowv += z * Tn;
     if (MODE == 1) e.PT += z * zs;
-    e.out += z * zs;
+    if (out != nullptr) e.out += z * zs;
     e.outT += z * zs;
     return e;
   }
@@ -1741,6 +1742,7 @@ struct EpiAttnB {
     static_assert(WLB >= WN * RB, "the wave's LDS share must hold its transposed tile");
     const int lane = threadIdx.x & 63;
     const bool odd = lane & 1;
+    const bool rowmajor = out != nullptr;   // uniform
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1768,12 +1770,14 @@ struct EpiAttnB {
           }
           // row-major pairs (lanes 2k, 2k + 1 hold columns n, n + 1)
           const int ne = n & ~1;
+          if (rowmajor) {
 #pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const float recv = __shfl_xor(odd ? v[e] : v[e + 1], 1, 64);
-            const int m = m0 + e + (odd ? 1 : 0);
-            const float a = odd ? recv : v[e], b = odd ? v[e + 1] : recv;
-            if (m < Tn && ne < ld) *reinterpret_cast<uint32_t*>(out + (long long)m * ld + ne) = pack_bf16x2(a, b);
+            for (int e = 0; e < 4; e += 2) {
+              const float recv = __shfl_xor(odd ? v[e] : v[e + 1], 1, 64);
+              const int m = m0 + e + (odd ? 1 : 0);
+              const float a = odd ? recv : v[e], b = odd ? v[e + 1] : recv;
+              if (m < Tn && ne < ld) *reinterpret_cast<uint32_t*>(out + (long long)m * ld + ne) = pack_bf16x2(a, b);
+            }
           }
           const int r = j * 32 + (lane & 31), c = i * 8 + q * 2 + (lane >> 5);
           *reinterpret_cast<uint2*>(wl + r * RB + ((c ^ ((r >> 1) & (NC - 1))) << 3)) =

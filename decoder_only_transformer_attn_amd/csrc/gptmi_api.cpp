@@ -550,8 +550,9 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   // attention backward: per-head score matrices [B*H][T][Tp] and transposes [B*H][D][Tp]
   p.Tp = (int)align_up((size_t)T, 64);
   const size_t Z = (size_t)B * H, TT = (size_t)T * p.Tp, DT = (C / H) * (size_t)p.Tp;
-  // (S / dP are stored only by the fp32 path: the bf16 one fuses them away)
-  p.aS = take(c->dtype == 0 ? Z * TT * 4 : 0); p.aP = take(Z * TT * es); p.aPT = take(Z * TT * es); p.adS = take(Z * TT * es);
+  // (S / dP and the row-major P are stored only by the fp32 path: the bf16
+  // one fuses them away)
+  p.aS = take(c->dtype == 0 ? Z * TT * 4 : 0); p.aP = take(c->dtype == 0 ? Z * TT * es : 0); p.aPT = take(Z * TT * es); p.adS = take(Z * TT * es);
   p.adST = take(Z * TT * es); p.adoc = take(M * C * es); p.adOT = take(Z * DT * es); p.aKT = take(Z * DT * es);
   p.aQT = take(Z * DT * es);
   p.alse = take(Z * T * 4); p.aDv = take(Z * T * 4);   // per-row log-sum-exp (log2) and dO . O
@@ -559,7 +560,8 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   p.waT = take(C * (size_t)p.C3p * es);
   p.mu = take(M * 4); p.rs = take(M * 4);
   // column partials: the widest of the sums (3C for the c_attn bias, F for c_fc's, 2C for a LayerNorm)
-  p.part = take((size_t)p.nchunks * (3 * C > F ? 3 * C : F) * 4);
+  const size_t nch = std::max<size_t>(p.nchunks, colsum_chunks((int)M));
+  p.part = take(nch * (3 * C > F ? 3 * C : F) * 4);
   // split-K partials of the weight gradients: room for DW_SPLIT copies of the largest [3C, C] or [F, C]
   p.wpart = take((size_t)DW_SPLIT * C * (3 * C > F ? 3 * C : F) * 4);
   p.total = off;

@@ -155,6 +155,8 @@ hipError_t launch_attention_backward(int dtype, const void* q, const void* k, co
                                      float* dqkv, int B, int H, int T, int D, const AttnBwdWs& w, hipStream_t st);
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st);
 hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int act, void* dc, hipStream_t st);
+// out[c] += sum over rows of a[M, N]; part holds max(colsum_chunks(M), ln_bwd_chunks(M)) * N floats
+int colsum_chunks(int M);
 hipError_t launch_colsum(int M, int N, const float* a, float* part, float* out, hipStream_t st);
 // out += (accumulate) or = the S slices part[z n, +n) summed in slice order
 hipError_t launch_add_partials(float* out, const float* part, long long n, int S, hipStream_t st, int accumulate = 1);
