@@ -1702,9 +1702,10 @@ hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W,
 // Entries with n > m, or past the Tn rows, are written as zeros, so both
 // outputs are whole [Tn][ld] matrices (ld = Tn rounded up to 64; the tile
 // grid covers every column below ld): out [m][n] (skipped when null) and
-// outT [n][m].  The
-// transposed copy is gathered in LDS per wave (8-byte chunks XOR-swizzled by
-// row, as for the head's loss gradient) and leaves as 16-byte row stores.
+// outT [n][m].  Both copies are gathered in LDS per wave (the transposed one
+// in 8-byte chunks XOR-swizzled by row, as for the head's loss gradient; the
+// row-major one in column pairs, its 16-byte units XOR-swizzled by row) and
+// leave as 16-byte row stores.
 template <typename T, int MODE>
 struct EpiAttnB {
   static constexpr bool kPreload = false;
@@ -1739,7 +1740,9 @@ struct EpiAttnB {
     static_assert(sizeof(T) == 2, "bf16 only");
     constexpr int WM = TM * 32, WN = TN * 32;
     constexpr int RB = WM * 2, NC = WM / 4, NU = WM / 8;   // staged row bytes, 8-byte chunks, 16-byte units
-    static_assert(WLB >= WN * RB, "the wave's LDS share must hold its transposed tile");
+    static_assert(WLB >= 2 * WN * RB, "the wave's LDS share must hold both copies of its tile");
+    constexpr int RBR = WN * 2, NUR = WN / 8;   // row-major staged row bytes, 16-byte units
+    char* wr = wl + WN * RB;                    // the row-major copy
     const int lane = threadIdx.x & 63;
     const bool odd = lane & 1;
     const bool rowmajor = out != nullptr;   // uniform
@@ -1774,9 +1777,10 @@ struct EpiAttnB {
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
               const float recv = __shfl_xor(odd ? v[e] : v[e + 1], 1, 64);
-              const int m = m0 + e + (odd ? 1 : 0);
+              const int ml = m0 + e + (odd ? 1 : 0) - mbase, nl = ne - nbase;
               const float a = odd ? recv : v[e], b = odd ? v[e + 1] : recv;
-              if (m < Tn && ne < ld) *reinterpret_cast<uint32_t*>(out + (long long)m * ld + ne) = pack_bf16x2(a, b);
+              const int u = (nl >> 3) ^ ((ml >> 2) & (NUR - 1));
+              *reinterpret_cast<uint32_t*>(wr + ml * RBR + u * 16 + (nl & 7) * 2) = pack_bf16x2(a, b);
             }
           }
           const int r = j * 32 + (lane & 31), c = i * 8 + q * 2 + (lane >> 5);
@@ -1792,6 +1796,15 @@ struct EpiAttnB {
       if (f & 1) w = make_uint4(w.z, w.w, w.x, w.y);
       const int n = nbase + r, m = mbase + k * 8;
       if (n < Tn && m < ld) *reinterpret_cast<uint4*>(outT + (long long)n * ld + m) = w;   // (m + 8 <= ld)
+    }
+    if (rowmajor) {
+#pragma unroll
+      for (int it = 0; it < WM * NUR / 64; ++it) {
+        const int r = it * (64 / NUR) + lane / NUR, k = lane % NUR;
+        const uint4 w = *reinterpret_cast<const uint4*>(wr + r * RBR + ((k ^ ((r >> 2) & (NUR - 1))) << 4));
+        const int m = mbase + r, n = nbase + k * 8;
+        if (m < Tn && n < ld) *reinterpret_cast<uint4*>(out + (long long)m * ld + n) = w;   // (n + 8 <= ld)
+      }
     }
   }
 };
