@@ -1318,35 +1318,48 @@ head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, i
     }
   }
 
-  // bf16 logits straight from the accumulators: registers 4q .. 4q+3 hold
-  // 4 consecutive vocab entries of one token, i.e. 8 contiguous bytes of its
-  // logits row (only 2-byte aligned: V is odd), written with one store; the
-  // lanes of one store instruction cover 16 contiguous bytes of 32 rows, and
-  // a wave's 8 stores per token fill whole 128-byte spans of the row.
-  if (ha.logits) {
-    bf16* const L = reinterpret_cast<bf16*>(ha.logits);
+  // bf16 logits, gathered per wave in LDS as [token][vocab] rows (WM entries,
+  // a pitch of WM * 2 + 8 bytes: the quad stores of 32 consecutive tokens
+  // meet no bank twice) and written as 16-byte pieces of whole row spans: in
+  // the accumulators a lane holds 4 consecutive vocab entries of one token,
+  // so direct stores would scatter 8 bytes over 32 token rows per
+  // instruction.  (The rows are only 2-byte aligned, V being odd; the
+  // 16-byte stores are unaligned.)  Waves 0-2 use the second stage, wave 3
+  // the first one past the partials.
+  if (ha.logits) {   // uniform
+    constexpr int PITCH = WM * 2 + 8, NU = WM / 8;
+    static_assert(D::NW == 4 && WM % 8 == 0, "four waves, whole 16-byte units per row");
+    static_assert(3 * WN * PITCH <= D::STAGE && 4096 + WN * PITCH <= D::STAGE, "staging must fit the stages");
+    static_assert(D::NWM * BN * 3 * 4 <= 4096, "the partials end before wave 3's staging");
+    char* const wl = wave < 3 ? s1 + wave * (WN * PITCH) : s0 + 4096;
 #pragma unroll
     for (int j = 0; j < D::TN; ++j) {
-      const int m = t0 + wn * WN + j * 32 + (lane & 31);
-      if (m < Mtok) {
-        bf16* const rowp = L + (long long)m * ha.ld_logits;
+      const int tl = j * 32 + (lane & 31);
 #pragma unroll
-        for (int i = 0; i < D::TM; ++i)
+      for (int i = 0; i < D::TM; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int v = vw0 + i * 32 + q * 8 + g * 4;
-            const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            if (v + 3 < V) {
-              __builtin_memcpy(rowp + v, &lo, 4);
-              __builtin_memcpy(rowp + v + 2, &hi, 4);
-            } else {
-              const uint32_t ww[2] = {lo, hi};
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (v + e < V) rowp[v + e] = bf16(ww[e >> 1] >> (16 * (e & 1)));
-            }
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int vl = i * 32 + q * 8 + g * 4;
+          *reinterpret_cast<uint2*>(wl + tl * PITCH + vl * 2) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+        }
+    }
+    __syncthreads();   // (block-uniform) every wave has staged its tile; each reads back its own
+    bf16* const L = reinterpret_cast<bf16*>(ha.logits);
+    for (int u = lane; u < WN * NU; u += 64) {
+      const int tl = u / NU, k = u - tl * NU;
+      const int m = t0 + wn * WN + tl, v = vw0 + k * 8;
+      if (m >= Mtok || v >= V) continue;
+      const uint2 a = *reinterpret_cast<const uint2*>(wl + tl * PITCH + k * 16);
+      const uint2 b = *reinterpret_cast<const uint2*>(wl + tl * PITCH + k * 16 + 8);
+      bf16* const p = L + (long long)m * ha.ld_logits + v;
+      if (v + 8 <= V) {
+        const uint4 w4 = make_uint4(a.x, a.y, b.x, b.y);
+        __builtin_memcpy(p, &w4, 16);
+      } else {
+        const uint32_t h[4] = {a.x, a.y, b.x, b.y};
+        for (int e = 0; v + e < V; ++e) p[e] = bf16(h[e >> 1] >> (16 * (e & 1)));
       }
     }
   }
