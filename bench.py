@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "6723b88d8d805522072c56df7ce79e64d969a8d9e7f5c4117ee305c9bc0e1051",
-                "bytes": 2001088399}
+HEAD_TRAFFIC = {"gemm_src_sha256": "d3d9838580ad3bfcec3c8b2c0d7614aac4d290162edea09c8845358a63ef3be9",
+                "bytes": 1920324892}
 
 
 def src_sha(rel):
