@@ -83,12 +83,23 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   __shared__ __align__(16) T sV[2][DP * LDVS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-  // 1-D grid, query tile major and longest first: the blocks with the most
-  // key tiles start first, the short ones fill in at the end
+  // 1-D grid over work items sorted longest first (query tile major: the
+  // blocks with the most key tiles first).  Consecutive rounds of 256 blocks
+  // (one per CU) take the order alternately forwards and backwards, so a CU
+  // that drew one of the longest items in one round draws one of the
+  // shortest in the next: at B8 T1024 (three blocks per CU) the busiest CU
+  // walks 28 key tiles instead of 34.
   const int nbh = a.B * a.H;
   const int nqt = (a.T_seq + BQ - 1) / BQ;
-  const int qt = nqt - 1 - (int)(blockIdx.x / nbh);
-  const int bh = blockIdx.x % nbh;
+  const int nitems = nqt * nbh;
+  int item = (int)blockIdx.x;
+  {
+    constexpr int ROUND = 256;
+    const int r = item / ROUND, base = r * ROUND;
+    if (r & 1) item = base + (min(ROUND, nitems - base) - 1 - (item - base));
+  }
+  const int qt = nqt - 1 - item / nbh;
+  const int bh = item % nbh;
   const int b = bh / a.H, h = bh - b * a.H;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
