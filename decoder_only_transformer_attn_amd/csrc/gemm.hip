@@ -1667,12 +1667,16 @@ gemm_batched_kernel(const T* __restrict__ A, int lda, const T* __restrict__ W, i
   typename Epi::Col colv[G::TN];
   preload_pairs<G::TM, G::TN>(pre, colv, mb, nb, M, N, epi);
   f32x16 acc[G::TM][G::TN];
-  gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A + k0, lda, W + k0, ldw, M, N, k1 - k0, m0, n0, smem, acc);
   if constexpr (IsRaw<Epi>::value) {
+    // the epilogue's own inputs are requested before the main loop, so their
+    // latency overlaps the operand loads
+    const auto rp = epi.template raw_preload<G::TM, G::TN>(mb, nb);
+    gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A + k0, lda, W + k0, ldw, M, N, k1 - k0, m0, n0, smem, acc);
     constexpr int WLB = (int)(G::SMEM_ELEMS * sizeof(T) / (G::NWM * G::NWN)) & ~15;
     __syncthreads();   // the tiles of the last K step are read: the LDS is free
-    epi.template raw<G::TM, G::TN, WLB>(acc, mb, nb, M, N, reinterpret_cast<char*>(smem) + wave * WLB);
+    epi.template raw<G::TM, G::TN, WLB>(acc, mb, nb, M, N, reinterpret_cast<char*>(smem) + wave * WLB, rp);
   } else {
+    gemm_mainloop<T, BM, BN, BK, WM, WN, KTAIL>(A + k0, lda, W + k0, ldw, M, N, k1 - k0, m0, n0, smem, acc);
     epilogue_pairs<G::TM, G::TN>(acc, pre, colv, mb, nb, M, N, epi);
   }
 }
@@ -1748,8 +1752,37 @@ struct EpiAttnB {
     return e;
   }
 
+  // per lane: the row values of its 4 TM rows-quads and, for MODE 1, the
+  // P^T quad P^T[n][m0 .. m0 + 3] of each (row quad, column tile)
+  template <int TM, int TN>
+  struct Pre {
+    float r[TM][4][4];
+    uint2 p[TM][4][TN];
+  };
+  template <int TM, int TN>
+  __device__ __forceinline__ Pre<TM, TN> raw_preload(int mbase, int nbase) const {
+    Pre<TM, TN> R;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = mbase + i * 32 + q * 8 + (lane >> 5) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R.r[i][q][e] = m0 + e < Tn ? rowv[m0 + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = nbase + j * 32 + (lane & 31);
+          R.p[i][q][j] = make_uint2(0u, 0u);
+          if (MODE == 1 && n < Tn && m0 < ld) R.p[i][q][j] = *reinterpret_cast<const uint2*>(PT + (long long)n * ld + m0);
+        }
+      }
+    return R;
+  }
+
   template <int TM, int TN, int WLB>
-  __device__ __forceinline__ void raw(const f32x16 (&acc)[TM][TN], int mbase, int nbase, int, int, char* wl) const {
+  __device__ __forceinline__ void raw(const f32x16 (&acc)[TM][TN], int mbase, int nbase, int, int, char* wl,
+                                      const Pre<TM, TN>& R) const {
     static_assert(sizeof(T) == 2, "bf16 only");
     constexpr int WM = TM * 32, WN = TN * 32;
     constexpr int RB = WM * 2, NC = WM / 4, NU = WM / 8;   // staged row bytes, 8-byte chunks, 16-byte units
@@ -1764,9 +1797,7 @@ struct EpiAttnB {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m0 = mbase + i * 32 + q * 8 + (lane >> 5) * 4;   // rows m0 .. m0 + 3
-        float r4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = m0 + e < Tn ? rowv[m0 + e] : 0.f;
+        const float (&r4)[4] = R.r[i][q];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int n = nbase + j * 32 + (lane & 31);
@@ -1777,8 +1808,7 @@ struct EpiAttnB {
               v[e] = (m0 + e < Tn && n <= m0 + e) ? fast_exp2(fmaf(acc[i][j][4 * q + e], sc, -r4[e])) : 0.f;
           } else {
             // P^T[n][m0 .. m0 + 3] (zero past the diagonal and in the pads)
-            uint2 pw = make_uint2(0u, 0u);
-            if (n < Tn && m0 < ld) pw = *reinterpret_cast<const uint2*>(PT + (long long)n * ld + m0);
+            const uint2 pw = R.p[i][q][j];
             const float p4[4] = {__uint_as_float(pw.x << 16), __uint_as_float(pw.x & 0xffff0000u),
                                  __uint_as_float(pw.y << 16), __uint_as_float(pw.y & 0xffff0000u)};
 #pragma unroll
