@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "d3d9838580ad3bfcec3c8b2c0d7614aac4d290162edea09c8845358a63ef3be9",
-                "bytes": 1920324892}
+HEAD_TRAFFIC = {"gemm_src_sha256": "4773c1921cf1faecaad39fafe52d2b104111bc3c529f1238b38ddecab3d14972",
+                "bytes": 1921814677}
 
 
 def src_sha(rel):
