@@ -199,9 +199,79 @@ __global__ void __launch_bounds__(256) ln_bwd_rows_kernel(int M, int C, const fl
   }
 }
 
+// The same with the row in registers (C = 256 NV, 16-byte aligned rows):
+// lane l holds columns 4 (64 i + l) .. + 3 of x, dy and g for i < NV, so x and
+// dy are read once; the sums run over the same terms in another order.
+template <typename T, int NV>
+__global__ void __launch_bounds__(256) ln_bwd_rows4_kernel(int M, int C, const float* __restrict__ x,
+                                                           const T* __restrict__ g, const float* __restrict__ dy,
+                                                           float eps, float* __restrict__ dx, float* __restrict__ mu,
+                                                           float* __restrict__ rs, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;   // (no block-wide barrier below)
+  const float4* xr = reinterpret_cast<const float4*>(x + (long long)m * C);
+  const float4* dr = reinterpret_cast<const float4*>(dy + (long long)m * C);
+  float xv[NV][4], gd[NV][4];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c4 = i * 64 + lane;
+    const float4 a = xr[c4], d = dr[c4];
+    float gg[4];
+    if constexpr (sizeof(T) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(g + 4 * c4);
+      gg[0] = __uint_as_float(w.x << 16); gg[1] = __uint_as_float(w.x & 0xffff0000u);
+      gg[2] = __uint_as_float(w.y << 16); gg[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      const float4 w = *reinterpret_cast<const float4*>(g + 4 * c4);
+      gg[0] = w.x; gg[1] = w.y; gg[2] = w.z; gg[3] = w.w;
+    }
+    xv[i][0] = a.x; xv[i][1] = a.y; xv[i][2] = a.z; xv[i][3] = a.w;
+    gd[i][0] = d.x * gg[0]; gd[i][1] = d.y * gg[1]; gd[i][2] = d.z * gg[2]; gd[i][3] = d.w * gg[3];
+    s += (a.x + a.y) + (a.z + a.w);
+  }
+  const float mean = wave_sum(s) / (float)C;
+  float s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = xv[i][e] - mean;
+      s2 += d * d;
+    }
+  const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)C + eps);
+  float sg = 0.f, sgx = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xv[i][e] = (xv[i][e] - mean) * rstd;   // now x-hat
+      sg += gd[i][e];
+      sgx += gd[i][e] * xv[i][e];
+    }
+  const float m1 = wave_sum(sg) / (float)C, m2 = wave_sum(sgx) / (float)C;
+  float4* o = reinterpret_cast<float4*>(dx + (long long)m * C);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c4 = i * 64 + lane;
+    float4 r = make_float4(rstd * (gd[i][0] - m1 - xv[i][0] * m2), rstd * (gd[i][1] - m1 - xv[i][1] * m2),
+                           rstd * (gd[i][2] - m1 - xv[i][2] * m2), rstd * (gd[i][3] - m1 - xv[i][3] * m2));
+    if (accumulate) {
+      const float4 p = o[c4];
+      r.x = p.x + r.x; r.y = p.y + r.y; r.z = p.z + r.z; r.w = p.w + r.w;
+    }
+    o[c4] = r;
+  }
+  if (lane == 0) {
+    mu[m] = mean;
+    rs[m] = rstd;
+  }
+}
+
 // Column sums of dy * xh and dy over a chunk of LNB_CHUNK rows: block = 64
 // columns x 4 row lanes; part[chunk][0 / 1][C].
-constexpr int LNB_CHUNK = 256;
+constexpr int LNB_CHUNK = 64;
 
 __global__ void __launch_bounds__(256) ln_bwd_cols_kernel(int M, int C, const float* __restrict__ x,
                                                           const float* __restrict__ dy, const float* __restrict__ mu,
@@ -224,6 +294,66 @@ __global__ void __launch_bounds__(256) ln_bwd_cols_kernel(int M, int C, const fl
     float* p = part + (long long)blockIdx.y * 2 * C;
     p[c] = (red[0][0][tx] + red[0][1][tx]) + (red[0][2][tx] + red[0][3][tx]);
     p[C + c] = (red[1][0][tx] + red[1][1][tx]) + (red[1][2][tx] + red[1][3][tx]);
+  }
+}
+
+// 16-byte form (C a multiple of 4, 16-byte aligned rows): block = 256
+// columns x 4 waves taking every 4th row of the chunk; the waves' sums are
+// added in wave order.
+__global__ void __launch_bounds__(256) ln_bwd_cols4_kernel(int M, int C, const float* __restrict__ x,
+                                                           const float* __restrict__ dy, const float* __restrict__ mu,
+                                                           const float* __restrict__ rs, float* __restrict__ part) {
+  __shared__ __align__(16) float red[2][4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 256 + lane * 4;
+  const int r0 = blockIdx.y * LNB_CHUNK;
+  float4 sg = make_float4(0.f, 0.f, 0.f, 0.f), sb = sg;
+  if (c < C) {
+#pragma unroll
+    for (int i = 0; i < LNB_CHUNK / 4; ++i) {
+      const int r = r0 + w + 4 * i;
+      if (r < M) {
+        const float4 d = *reinterpret_cast<const float4*>(dy + (long long)r * C + c);
+        const float4 a = *reinterpret_cast<const float4*>(x + (long long)r * C + c);
+        const float u = mu[r], q = rs[r];
+        sg.x += d.x * ((a.x - u) * q); sg.y += d.y * ((a.y - u) * q);
+        sg.z += d.z * ((a.z - u) * q); sg.w += d.w * ((a.w - u) * q);
+        sb.x += d.x; sb.y += d.y; sb.z += d.z; sb.w += d.w;
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(&red[0][w][lane * 4]) = sg;
+  *reinterpret_cast<float4*>(&red[1][w][lane * 4]) = sb;
+  __syncthreads();
+  const int t = threadIdx.x, col = blockIdx.x * 256 + t;
+  if (col < C) {
+    float* p = part + (long long)blockIdx.y * 2 * C;
+    p[col] = ((red[0][0][t] + red[0][1][t]) + red[0][2][t]) + red[0][3][t];
+    p[C + col] = ((red[1][0][t] + red[1][1][t]) + red[1][2][t]) + red[1][3][t];
+  }
+}
+
+// dg[c] += the chunks' partials, db likewise: a block per 64 columns, its 4
+// waves taking every 4th chunk, then the waves' sums in wave order.
+__global__ void __launch_bounds__(256) ln_bwd_final4_kernel(int C, int nchunks, const float* __restrict__ part,
+                                                            float* __restrict__ dg, float* __restrict__ db) {
+  __shared__ float red[2][4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  float a = 0.f, b = 0.f;
+  if (c < C) {
+#pragma unroll 8
+    for (int k = w; k < nchunks; k += 4) {
+      a += part[(long long)k * 2 * C + c];
+      b += part[(long long)k * 2 * C + C + c];
+    }
+  }
+  red[0][w][lane] = a;
+  red[1][w][lane] = b;
+  __syncthreads();
+  if (w == 0 && c < C) {
+    dg[c] += ((red[0][0][lane] + red[0][1][lane]) + red[0][2][lane]) + red[0][3][lane];
+    db[c] += ((red[1][0][lane] + red[1][1][lane]) + red[1][2][lane]) + red[1][3][lane];
   }
 }
 
@@ -355,16 +485,42 @@ int ln_bwd_chunks(int M) { return (M + LNB_CHUNK - 1) / LNB_CHUNK; }
 hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const void* g, const float* dy, float eps,
                               float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st,
                               int accumulate) {
-  if (dtype == 0)
-    hipLaunchKernelGGL(ln_bwd_rows_kernel<float>, dim3((M + 3) / 4), dim3(256), 0, st, M, C, x, (const float*)g, dy,
-                       eps, dx, mu, rs, accumulate);
-  else
-    hipLaunchKernelGGL(ln_bwd_rows_kernel<bf16>, dim3((M + 3) / 4), dim3(256), 0, st, M, C, x, (const bf16*)g, dy,
-                       eps, dx, mu, rs, accumulate);
+  if (M <= 0) return hipSuccess;
+  const bool v4 = C % 4 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 15) == 0 && ((uintptr_t)dx & 15) == 0 &&
+                  ((uintptr_t)g & (dtype == 0 ? 15 : 7)) == 0;
+  const int nv = C % 256 == 0 ? C / 256 : 0;
+  const dim3 rg((M + 3) / 4);
+#define GPT_LNB_ROWS4(TT, NVV)                                                                                  \
+  hipLaunchKernelGGL((ln_bwd_rows4_kernel<TT, NVV>), rg, dim3(256), 0, st, M, C, x, (const TT*)g, dy, eps, dx, \
+                     mu, rs, accumulate)
+  if (v4 && nv >= 1 && nv <= 4) {
+    if (dtype == 0) {
+      if (nv == 1) GPT_LNB_ROWS4(float, 1); else if (nv == 2) GPT_LNB_ROWS4(float, 2);
+      else if (nv == 3) GPT_LNB_ROWS4(float, 3); else GPT_LNB_ROWS4(float, 4);
+    } else {
+      if (nv == 1) GPT_LNB_ROWS4(bf16, 1); else if (nv == 2) GPT_LNB_ROWS4(bf16, 2);
+      else if (nv == 3) GPT_LNB_ROWS4(bf16, 3); else GPT_LNB_ROWS4(bf16, 4);
+    }
+  } else if (dtype == 0) {
+    hipLaunchKernelGGL(ln_bwd_rows_kernel<float>, rg, dim3(256), 0, st, M, C, x, (const float*)g, dy, eps, dx, mu, rs,
+                       accumulate);
+  } else {
+    hipLaunchKernelGGL(ln_bwd_rows_kernel<bf16>, rg, dim3(256), 0, st, M, C, x, (const bf16*)g, dy, eps, dx, mu, rs,
+                       accumulate);
+  }
+#undef GPT_LNB_ROWS4
   const int nch = ln_bwd_chunks(M);
-  hipLaunchKernelGGL(ln_bwd_cols_kernel, dim3((C + 63) / 64, nch), dim3(256), 0, st, M, C, x, dy, (const float*)mu,
-                     (const float*)rs, part);
-  hipLaunchKernelGGL(ln_bwd_final_kernel, dim3((C + 255) / 256), dim3(256), 0, st, C, nch, (const float*)part, dg, db);
+  if (v4) {
+    hipLaunchKernelGGL(ln_bwd_cols4_kernel, dim3((C + 255) / 256, nch), dim3(256), 0, st, M, C, x, dy,
+                       (const float*)mu, (const float*)rs, part);
+    hipLaunchKernelGGL(ln_bwd_final4_kernel, dim3((C + 63) / 64), dim3(256), 0, st, C, nch, (const float*)part, dg,
+                       db);
+  } else {
+    hipLaunchKernelGGL(ln_bwd_cols_kernel, dim3((C + 63) / 64, nch), dim3(256), 0, st, M, C, x, dy, (const float*)mu,
+                       (const float*)rs, part);
+    hipLaunchKernelGGL(ln_bwd_final_kernel, dim3((C + 255) / 256), dim3(256), 0, st, C, nch, (const float*)part, dg,
+                       db);
+  }
   return hipGetLastError();
 }
 
@@ -467,8 +623,10 @@ __global__ void __launch_bounds__(256) colsum_final4_kernel(int N, int nchunks, 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
   float s = 0.f;
-  if (c < N)
+  if (c < N) {
+#pragma unroll 8
     for (int k = w; k < nchunks; k += 4) s += part[(long long)k * N + c];
+  }
   red[w][lane] = s;
   __syncthreads();
   if (w == 0 && c < N) out[c] += ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];

@@ -90,6 +90,15 @@ def test_block_backward_matches_oracle(dtype, act, B, T):
     check_block(cfg, 1, B, T, seed=B * T + act)
 
 
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("C,H", [(256, 4), (512, 8), (1024, 16)])
+def test_block_backward_register_row_widths(dtype, C, H):
+    # widths of 256, 512 and 1024 columns: the LayerNorm backward holds one,
+    # two or four 16-byte pieces of each row per lane
+    cfg = synth.GPTConfig(vocab=97, ctx=64, n_embd=C, n_head=H, n_layer=1, n_ff=2 * C, dtype=dtype)
+    check_block(cfg, 0, 1, 40, seed=C + H)
+
+
 def test_block_backward_gpt2_width_bf16():
     cfg = dc.replace(synth.GPT2, n_layer=1)
     check_block(cfg, 0, 1, 256, seed=5, init="bench")
