@@ -570,6 +570,39 @@ __global__ void __launch_bounds__(256) act_bwd_kernel(float* __restrict__ d, con
   }
 }
 
+// bf16 forms, four elements per thread (n a multiple of 4, 8-byte aligned
+// bf16 and 16-byte aligned fp32 arrays)
+__device__ __forceinline__ void unpack4(uint2 w, float (&z)[4]) {
+  z[0] = __uint_as_float(w.x << 16); z[1] = __uint_as_float(w.x & 0xffff0000u);
+  z[2] = __uint_as_float(w.y << 16); z[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+__global__ void __launch_bounds__(256) act_fwd4_kernel(const uint2* __restrict__ u, long long n4, int act,
+                                                       uint2* __restrict__ h) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n4; e += (long long)gridDim.x * 256) {
+    float z[4];
+    unpack4(u[e], z);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) z[k] = act ? gelu_erf_f(z[k]) : gelu_tanh_f(z[k]);
+    h[e] = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+  }
+}
+
+__global__ void __launch_bounds__(256) act_bwd4_kernel(float4* __restrict__ d, const uint2* __restrict__ u,
+                                                       long long n4, int act, uint2* __restrict__ dc) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n4; e += (long long)gridDim.x * 256) {
+    float z[4];
+    unpack4(u[e], z);
+    float4 v = d[e];
+    v.x *= act ? gelu_erf_d(z[0]) : gelu_tanh_d(z[0]);
+    v.y *= act ? gelu_erf_d(z[1]) : gelu_tanh_d(z[1]);
+    v.z *= act ? gelu_erf_d(z[2]) : gelu_tanh_d(z[2]);
+    v.w *= act ? gelu_erf_d(z[3]) : gelu_tanh_d(z[3]);
+    d[e] = v;
+    dc[e] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+
 // Column sums of an fp32 [M, N] matrix into per-chunk partials (fixed order),
 // then out[n] += sum of the partials in chunk order.
 __global__ void __launch_bounds__(256) colsum_part_kernel(int M, int N, const float* __restrict__ a,
@@ -958,6 +991,9 @@ hipError_t launch_add_partials(float* out, const float* part, long long n, int S
 hipError_t launch_act_fwd(int dtype, const void* u, long long n, int act, void* h, hipStream_t st) {
   if (dtype == 0)
     hipLaunchKernelGGL(act_fwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, (const float*)u, n, act, (float*)h);
+  else if (n % 4 == 0 && ((uintptr_t)u & 7) == 0 && ((uintptr_t)h & 7) == 0)
+    hipLaunchKernelGGL(act_fwd4_kernel, dim3(grid_for(n / 4)), dim3(256), 0, st, (const uint2*)u, n / 4, act,
+                       (uint2*)h);
   else
     hipLaunchKernelGGL(act_fwd_kernel<bf16>, dim3(grid_for(n)), dim3(256), 0, st, (const bf16*)u, n, act, (bf16*)h);
   return hipGetLastError();
@@ -967,6 +1003,9 @@ hipError_t launch_act_bwd(int dtype, float* d, const void* u, long long n, int a
   if (dtype == 0)
     hipLaunchKernelGGL(act_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, d, (const float*)u, n, act,
                        (float*)dc);
+  else if (n % 4 == 0 && ((uintptr_t)d & 15) == 0 && ((uintptr_t)u & 7) == 0 && ((uintptr_t)dc & 7) == 0)
+    hipLaunchKernelGGL(act_bwd4_kernel, dim3(grid_for(n / 4)), dim3(256), 0, st, (float4*)d, (const uint2*)u, n / 4,
+                       act, (uint2*)dc);
   else
     hipLaunchKernelGGL(act_bwd_kernel<bf16>, dim3(grid_for(n)), dim3(256), 0, st, d, (const bf16*)u, n, act,
                        (bf16*)dc);
