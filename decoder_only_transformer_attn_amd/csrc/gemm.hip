@@ -1716,10 +1716,15 @@ hipError_t launch_gemm_batched(int dtype, const void* A, int lda, const void* W,
 // MODE 0: P = exp2(sc q.k - lse2[m]) (the causal softmax, the row's log-sum-exp
 //         in log2 units from the forward pass), from acc = q.k;
 // MODE 1: dS = P (acc - Dv[m]) sc, from acc = dO.u, P read from P^T.
-// Entries with n > m, or past the Tn rows, are written as zeros, so both
-// outputs are whole [Tn][ld] matrices (ld = Tn rounded up to 64; the tile
-// grid covers every column below ld): out [m][n] (skipped when null) and
-// outT [n][m].  Both copies are gathered in LDS per wave (the transposed one
+// Entries with n > m, or past the Tn rows, are written as zeros, except that
+// tiles wholly above the diagonal (n0 > m0 + BM - 1) are skipped and left
+// unwritten: out [m][n] (skipped when null) and outT [n][m] are [Tn][ld]
+// (ld = Tn rounded up to 64; the tile grid covers every column below ld).
+// Their readers never touch the skipped tiles: the dS product reads P^T only
+// inside the tiles it computes itself (the same grid and skip), and the
+// contractions dU = P^T dO, dK = dS^T Q (over [r0, ld)) and dQ = dS K (over
+// [0, r0 + 64)), with r0 the 64-aligned start of their row tile, stay within
+// the computed 128 x 128 (or 64 x 64) tiles.  Both copies are gathered in LDS per wave (the transposed one
 // in 8-byte chunks XOR-swizzled by row, as for the head's loss gradient; the
 // row-major one in column pairs, its 16-byte units XOR-swizzled by row) and
 // leave as 16-byte row stores.
@@ -1862,15 +1867,15 @@ hipError_t launch_attn_scores_bwd(int mode, const void* A, int lda, const void* 
   if (mode == 0) {
     const EpiAttnB<bf16, 0> e{rowv, nullptr, (bf16*)out, (bf16*)outT, ld, Tn, zs, sc};
     if (Tn >= 128)
-      return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0,
+      return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 1,
                                                      st);
-    return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0, st);
+    return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 1, st);
   }
   const EpiAttnB<bf16, 1> e{rowv, (const bf16*)PT, (bf16*)out, (bf16*)outT, ld, Tn, zs, sc};
   if (Tn >= 128)
-    return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0,
+    return run_batched<bf16, 128, 128, 64, 64, 64>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 1,
                                                    st);
-  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 0, st);
+  return run_batched<bf16, 64, 64, 64, 32, 32>((const bf16*)A, lda, (const bf16*)W, ldw, Tn, Tn, D, e, bs, Z, 1, st);
 }
 
 // Loss gradient of the logits A W^T ([M, C] x [V, C]^T) into dz [M, V] (ld).
