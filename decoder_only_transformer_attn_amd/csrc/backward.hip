@@ -99,11 +99,19 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in
 // 8, 16-byte aligned rows): each thread loads 8 consecutive columns of one
 // input row and stores 8 consecutive rows of one output row; the tile sits in
 // LDS row-major with a 2-element pad, so the column gathers of the store phase
-// (8 halfwords, 66 elements apart) spread over the banks.
-__global__ void __launch_bounds__(256) transpose16_kernel(const bf16* __restrict__ in, long long ld_in, int R, int Cc,
-                                                          bf16* __restrict__ out, long long ld_out, int Rp) {
+// (8 halfwords, 66 elements apart) spread over the banks.  Batched over
+// blockIdx.z = b H + h: input at b in_b + h in_h, output at z out_z.
+__global__ void __launch_bounds__(256) transpose16_kernel(const bf16* __restrict__ in, long long ld_in, long long in_b,
+                                                          long long in_h, int H, int R, int Cc,
+                                                          bf16* __restrict__ out, long long ld_out, long long out_z,
+                                                          int Rp) {
   constexpr int LDT = 66;
   __shared__ __align__(16) uint16_t tile[64 * LDT];
+  {
+    const int z = blockIdx.z, b = z / H, h = z - b * H;
+    in += b * in_b + h * in_h;
+    out += (long long)z * out_z;
+  }
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x, sub = tid >> 3, k = tid & 7;   // 32 rows x 8 chunks per pass
 #pragma unroll
@@ -451,8 +459,8 @@ hipError_t launch_transpose(int dtype, const void* in, long long ld_in, int R, i
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, (const float*)in, ld_in, R, Cc, (float*)out,
                        (long long)Rp, Rp);
   else if (Cc % 8 == 0 && ld_in % 8 == 0 && Rp % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0)
-    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, st, (const bf16*)in, ld_in, R, Cc, (bf16*)out,
-                       (long long)Rp, Rp);
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, st, (const bf16*)in, ld_in, 0LL, 0LL, 1, R, Cc,
+                       (bf16*)out, (long long)Rp, 0LL, Rp);
   else
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)in, ld_in, R, Cc, (bf16*)out,
                        (long long)Rp, Rp);
@@ -712,6 +720,14 @@ template <typename TI, typename TO>
 static void transpose_batched(const TI* in, long long ld_in, long long in_b, long long in_h, int H, int R, int Cc,
                               TO* out, long long ld_out, long long out_z, int Rp, int Z, hipStream_t st) {
   const dim3 grid((Rp + 63) / 64, (Cc + 63) / 64, Z);
+  if constexpr (std::is_same<TI, bf16>::value && std::is_same<TO, bf16>::value) {
+    if (Cc % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 && Rp % 8 == 0 && in_b % 8 == 0 && in_h % 8 == 0 &&
+        out_z % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+      hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, st, in, ld_in, in_b, in_h, H, R, Cc, out, ld_out,
+                         out_z, Rp);
+      return;
+    }
+  }
   hipLaunchKernelGGL((transpose_batched_kernel<TI, TO>), grid, dim3(256), 0, st, in, ld_in, in_b, in_h, H, R, Cc, out,
                      ld_out, out_z, Rp);
 }
