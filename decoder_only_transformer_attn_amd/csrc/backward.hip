@@ -876,6 +876,35 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const float* __res
   if (lane == 0) Dv[((long long)b * H + h) * Tn + t] = s;
 }
 
+// bf16 form for D = 64: 16 lanes per (b, t, h) row, four elements each
+// (16-byte dO and 8-byte O loads), four rows per wave, sums over the 16-lane
+// group by butterfly exchanges.
+__global__ void __launch_bounds__(256) attn_bwd_rowdot64_kernel(const float* __restrict__ dout,
+                                                                const bf16* __restrict__ o, float* __restrict__ Dv,
+                                                                int B, int H, int Tn) {
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const long long r = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);   // (b, t, h)
+  const bool ok = r < (long long)B * Tn * H;
+  float s = 0.f;
+  long long bt = 0;
+  int h = 0;
+  if (ok) {
+    bt = r / H;
+    h = (int)(r - bt * H);
+    const long long base = bt * H * 64 + (long long)h * 64 + sub * 4;
+    const float4 d = *reinterpret_cast<const float4*>(dout + base);
+    const uint2 w = *reinterpret_cast<const uint2*>(o + base);
+    s = d.x * __uint_as_float(w.x << 16) + d.y * __uint_as_float(w.x & 0xffff0000u) +
+        d.z * __uint_as_float(w.y << 16) + d.w * __uint_as_float(w.y & 0xffff0000u);
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (ok && sub == 0) {
+    const int b = (int)(bt / Tn), t = (int)(bt - (long long)b * Tn);
+    Dv[((long long)b * H + h) * Tn + t] = s;
+  }
+}
+
 template <typename T>
 static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* dout, float* dqkv, int B, int H,
                              int Tn, int D, const AttnBwdWs& w, hipStream_t st) {
@@ -898,8 +927,12 @@ static hipError_t attn_bwd_t(const T* q, const T* k, const T* u, const float* do
     // log-sum-exp (P itself is not needed); dS and dS^T straight from the dP
     // product
     const int rows = B * Tn * H;
-    hipLaunchKernelGGL(attn_bwd_rowdot_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, dout,
-                       static_cast<const T*>(w.o), w.Dv, B, H, Tn, D);
+    if (D == 64 && ((uintptr_t)dout & 15) == 0 && ((uintptr_t)w.o & 7) == 0)
+      hipLaunchKernelGGL(attn_bwd_rowdot64_kernel, dim3((rows + 15) / 16), dim3(256), 0, st, dout,
+                         static_cast<const bf16*>(w.o), w.Dv, B, H, Tn);
+    else
+      hipLaunchKernelGGL(attn_bwd_rowdot_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, dout,
+                         static_cast<const T*>(w.o), w.Dv, B, H, Tn, D);
     GPT_BWD_TRY(launch_attn_scores_bwd(0, q, D, k, D, Tn, D, BatchStrides{H * hT, hT, H * hT, hT, 0, 0, H}, Z,
                                        w.lse2, nullptr, nullptr, PT, Tp, scale * 1.4426950408889634f, st));
     // dU = P^T dO
