@@ -856,6 +856,7 @@ int gpt_forward_train(const gpt_config* cfg, const void* params, const int32_t* 
           static_cast<hipStream_t>(stream), nullptr, nullptr, -1, xs};
   s = run_blocks(ps);
   if (s != GPT_OK) return s;
+  if (!mean_loss) return GPT_OK;   // only the residual streams (the head backward computes the loss again)
   const int M = B * T, V = cfg->vocab, C = cfg->n_embd;
   void* a = at<char>(ws, pl.a);
   if (!rows_final(cfg)) {

@@ -202,10 +202,10 @@ def gradients(cfg, params, idx, grads, targets=None, stream=None):
     loss = torch.zeros(1, dtype=torch.float32, device=dev)
     ws = torch.empty(max(workspace_bytes(cfg, B, T), head_backward_workspace_bytes(cfg, B, T),
                          block_backward_workspace_bytes(cfg, B, T) if L else 0), dtype=torch.uint8, device=dev)
-    forward_train(cfg, params, idx, xs, ws, targets, loss, stream)
+    forward_train(cfg, params, idx, xs, ws, targets, None, stream)   # residual streams only
     d = torch.empty((M, C), dtype=torch.float32, device=dev)
     d2 = torch.empty_like(d)
-    head_backward(cfg, params, idx, xs[L], d, grads, targets, None, ws, stream)
+    head_backward(cfg, params, idx, xs[L], d, grads, targets, loss, ws, stream)   # (the loss is computed here)
     for l in range(L - 1, -1, -1):
         block_backward(cfg, params, l, B, T, xs[l], d, d2, grads, ws, stream)
         d, d2 = d2, d

@@ -288,15 +288,19 @@ int gpt_embedding_backward(const gpt_config* cfg, const int32_t* idx, int B, int
                            void* stream);
 
 /* ---- backward of the blocks (pre-LN GPT-2 blocks: arch 0, post_ln 0) ----
- * A whole gradient of the mean loss: gpt_forward_train (the loss, and each
- * block's input residual), gpt_head_backward on xs[L], gpt_block_backward for
+ * A whole gradient of the mean loss: gpt_forward_train (each block's input
+ * residual; with a null mean_loss the head is left to the next step),
+ * gpt_head_backward on xs[L] (which also gives the loss), gpt_block_backward for
  * l = L-1 .. 0 (each turns d loss / d(block l's output) into d loss / d(its
  * input)), then gpt_embedding_backward on the last dx.  Blocks are recomputed
  * from their inputs (only the L+1 residual rows are kept between the passes). */
 
 /* The forward pass and mean loss (no logits), writing xs (device, fp32
  * [L+1][B*T][C]): xs[l] = the residual entering block l, xs[L] = the rows
- * the final LayerNorm reads.  Same workspace as gpt_forward.  B*T <= 2^20. */
+ * the final LayerNorm reads.  mean_loss (device, one float) may be null:
+ * then the final LayerNorm, the head and the loss are skipped (a gradient
+ * computation gets the same loss from gpt_head_backward).  Same workspace as
+ * gpt_forward.  B*T <= 2^20. */
 int gpt_forward_train(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
                       const int32_t* targets, float* xs, float* mean_loss, void* ws, size_t ws_bytes, void* stream);
 
@@ -311,10 +315,13 @@ int gpt_block_backward_workspace_bytes(const gpt_config* cfg, int B, int T, size
  *          x or dy).
  *   grads  (device) fp32 gradient blob: += this block's twelve tensors.
  * The block's forward is recomputed with the forward kernels; the products
- * run on bf16 (or fp32) operands with fp32 accumulation; attention's
- * gradient materialises each head's probabilities P and dS = P (dP -
- * rowsum(P dP)) / sqrt(D) ([B*H][T][T] in the workspace) and runs the five
- * products as batched matrix-core products.  B*T <= 2^20. */
+ * run on bf16 (or fp32) operands with fp32 accumulation.  Attention's
+ * gradient keeps each head's P^T, dS = P (dP - dO.O) / sqrt(D) and dS^T
+ * ([B*H][T][Tp] in the workspace; bf16: P^T comes straight from the q.k
+ * product with the recomputed forward's row log-sum-exp, dS from the dO.u
+ * product, so the scores and dP are never stored; fp32: S and dP are stored
+ * and row kernels form P and dS) and runs the contractions as batched
+ * matrix-core products.  B*T <= 2^20. */
 int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int B, int T, const float* x,
                        const float* dy, float* dx, float* grads, void* ws, size_t ws_bytes, void* stream);
 

@@ -149,3 +149,21 @@ def test_block_backward_is_deterministic():
     b = run_block(cfg, params, 0, x, dy)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_forward_train_without_loss_writes_the_same_residuals():
+    # a null mean_loss skips the head: the residual streams must not change
+    lib = _lib()
+    cfg = synth.GPTConfig(vocab=300, ctx=48, n_embd=64, n_head=2, n_layer=2, n_ff=128, dtype=synth.BF16)
+    params = synth.make_params(cfg, seed=9, cfg_id=74, init="stress")
+    P = lib.params_to_device(cfg, synth.pack(cfg, params))
+    B, T = 2, 33
+    idx = torch.from_numpy(synth.make_ids(cfg, B, T, seed=9)).cuda()
+    ws = torch.empty(lib.workspace_bytes(cfg, B, T), dtype=torch.uint8, device="cuda")
+    xs = [torch.full((cfg.n_layer + 1, B * T, cfg.n_embd), float("nan"), device="cuda") for _ in range(2)]
+    loss = torch.full((1,), float("nan"), device="cuda")
+    lib.forward_train(cfg, P, idx, xs[0], ws, None, loss)
+    lib.forward_train(cfg, P, idx, xs[1], ws, None, None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(loss).all()
+    assert torch.equal(xs[0], xs[1])
