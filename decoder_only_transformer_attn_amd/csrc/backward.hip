@@ -137,6 +137,43 @@ __global__ void __launch_bounds__(256) transpose16_kernel(const bf16* __restrict
   }
 }
 
+// fp32 rows in, both bf16 layouts out: out_rm [R, ld_rm] = in and out_t =
+// its transpose [Cc, Rp] (zeros for R <= r < Rp), one pass over the input
+// (Cc, ld_in, ld_rm and Rp multiples of 8, 16-byte aligned rows).
+__global__ void __launch_bounds__(256) cast_transpose16_kernel(const float* __restrict__ in, long long ld_in, int R,
+                                                               int Cc, bf16* __restrict__ out_rm, long long ld_rm,
+                                                               bf16* __restrict__ out_t, int Rp) {
+  constexpr int LDT = 66;
+  __shared__ __align__(16) uint16_t tile[64 * LDT];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, sub = tid >> 3, k = tid & 7;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int i = p * 32 + sub, r = r0 + i, c = c0 + k * 8;
+    uint32_t h[4] = {0u, 0u, 0u, 0u};
+    if (r < R && c < Cc) {
+      const float4 a = *reinterpret_cast<const float4*>(in + (long long)r * ld_in + c);
+      const float4 b = *reinterpret_cast<const float4*>(in + (long long)r * ld_in + c + 4);
+      h[0] = pack_bf16x2(a.x, a.y); h[1] = pack_bf16x2(a.z, a.w);
+      h[2] = pack_bf16x2(b.x, b.y); h[3] = pack_bf16x2(b.z, b.w);
+      *reinterpret_cast<uint4*>(out_rm + (long long)r * ld_rm + c) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(&tile[i * LDT + k * 8 + 2 * e]) = h[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int oi = p * 32 + sub, c = c0 + oi, r = r0 + k * 8;
+    if (c >= Cc || r >= Rp) continue;
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = (uint32_t)tile[(k * 8 + 2 * e) * LDT + oi] | ((uint32_t)tile[(k * 8 + 2 * e + 1) * LDT + oi] << 16);
+    *reinterpret_cast<uint4*>(out_t + (long long)c * Rp + r) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
 // p[r, c] = 0 for r < R, c0 <= c < c1
 template <typename T>
 __global__ void __launch_bounds__(256) zero_cols_kernel(T* __restrict__ p, long long ld, int R, int c0, int c1) {
@@ -475,6 +512,21 @@ hipError_t launch_zero_cols(int dtype, void* p, long long ld, int R, int c0, int
   else
     hipLaunchKernelGGL(zero_cols_kernel<bf16>, dim3(grid), dim3(256), 0, st, (bf16*)p, ld, R, c0, c1);
   return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose(int dtype, const float* in, int R, int Cc, void* out_rm, void* out_t, int Rp,
+                                 hipStream_t st) {
+  if (R <= 0 || Cc <= 0) return hipSuccess;
+  if (dtype != 0 && Cc % 8 == 0 && Rp % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out_rm & 15) == 0 &&
+      ((uintptr_t)out_t & 15) == 0) {
+    const dim3 grid((Rp + 63) / 64, (Cc + 63) / 64);
+    hipLaunchKernelGGL(cast_transpose16_kernel, grid, dim3(256), 0, st, in, (long long)Cc, R, Cc, (bf16*)out_rm,
+                       (long long)Cc, (bf16*)out_t, Rp);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_cast_rows(dtype, in, (long long)R * Cc, out_rm, st);
+  if (e != hipSuccess) return e;
+  return launch_transpose(dtype, out_rm, Cc, R, Cc, out_t, Rp, st);
 }
 
 hipError_t launch_cast_rows(int dtype, const float* x, long long n, void* out, hipStream_t st) {

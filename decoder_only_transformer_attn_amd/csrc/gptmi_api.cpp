@@ -949,9 +949,8 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_transpose(dt, P.at(w.attn_w), C, 3 * C, C, W(pl.waT), pl.C3p, st));   // [3C,C] -> [C,3Cp]
 
   // ---- MLP: dh = dy Wfp, dWfp += dy^T h, dbfp += sum dy
-  GPT_TRY(launch_cast_rows(dt, dy, (long long)M * C, W(pl.dyc), st));
+  GPT_TRY(launch_cast_transpose(dt, dy, M, C, W(pl.dyc), W(pl.dyT), Mp, st));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dyc), C, W(pl.wfpT), C, M, F, C, Wf(pl.dh), F, 0, st));
-  GPT_TRY(launch_transpose(dt, W(pl.dyc), C, M, C, W(pl.dyT), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.hm), F, M, F, W(pl.hT), Mp, st));
   GPT_TRY(dW(W(pl.dyT), W(pl.hT), C, F, grads + w.fcproj_w));
   GPT_TRY(launch_colsum(M, C, dy, Wf(pl.part), grads + w.fcproj_b, st));
@@ -969,8 +968,7 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
                              Wf(pl.part), grads + w.ln2_g, grads + w.ln2_b, st, 1));
 
   // ---- attention: dWp += dx1^T o, dbp += sum dx1, dO = dx1 Wp
-  GPT_TRY(launch_cast_rows(dt, dx1, (long long)M * C, W(pl.dx1c), st));
-  GPT_TRY(launch_transpose(dt, W(pl.dx1c), C, M, C, W(pl.dx1T), Mp, st));
+  GPT_TRY(launch_cast_transpose(dt, dx1, M, C, W(pl.dx1c), W(pl.dx1T), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.o), C, M, C, W(pl.oT), Mp, st));
   GPT_TRY(dW(W(pl.dx1T), W(pl.oT), C, C, grads + w.proj_w));
   GPT_TRY(launch_colsum(M, C, dx1, Wf(pl.part), grads + w.proj_b, st));
@@ -980,8 +978,7 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   GPT_TRY(launch_attention_backward(dt, W(pl.q), W(pl.k), W(pl.v), Wf(pl.dout), Wf(pl.dqkv), B, H, T, D, aw, st));
   // dWattn += dqkv^T a1, dbattn += sum dqkv, da1 = dqkv Wattn
   GPT_TRY(launch_colsum(M, 3 * C, Wf(pl.dqkv), Wf(pl.part), grads + w.attn_b, st));
-  GPT_TRY(launch_cast_rows(dt, Wf(pl.dqkv), (long long)M * 3 * C, W(pl.dqkvc), st));
-  GPT_TRY(launch_transpose(dt, W(pl.dqkvc), 3 * C, M, 3 * C, W(pl.dqkvT), Mp, st));
+  GPT_TRY(launch_cast_transpose(dt, Wf(pl.dqkv), M, 3 * C, W(pl.dqkvc), W(pl.dqkvT), Mp, st));
   GPT_TRY(launch_transpose(dt, W(pl.a1), C, M, C, W(pl.a1T), Mp, st));
   GPT_TRY(dW(W(pl.dqkvT), W(pl.a1T), 3 * C, C, grads + w.attn_w));
   GPT_TRY(launch_gemm_f32out(dt, W(pl.dqkvc), 3 * C, W(pl.waT), pl.C3p, M, C, 3 * C, Wf(pl.da), C, 0, st));

@@ -128,6 +128,9 @@ hipError_t launch_transpose(int dtype, const void* in, long long ld_in, int R, i
                             hipStream_t st);
 hipError_t launch_zero_cols(int dtype, void* p, long long ld, int R, int c0, int c1, hipStream_t st);
 hipError_t launch_cast_rows(int dtype, const float* x, long long n, void* out, hipStream_t st);
+// in fp32 [R, Cc] (dense) -> out_rm [R, Cc] and its transpose out_t [Cc, Rp] (zero-padded), compute dtype
+hipError_t launch_cast_transpose(int dtype, const float* in, int R, int Cc, void* out_rm, void* out_t, int Rp,
+                                 hipStream_t st);
 int ln_bwd_chunks(int M);
 hipError_t launch_ln_backward(int dtype, int M, int C, const float* x, const void* g, const float* dy, float eps,
                               float* dx, float* mu, float* rs, float* part, float* dg, float* db, hipStream_t st,
