@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "73c658c3cc9de70a7c6b46dcc12d2b9ef99e73ae2f334b4c80f9dff91d1c56af",
-                "bytes": 1921424921}
+HEAD_TRAFFIC = {"gemm_src_sha256": "63972c6c70bf023ac139f3b39303cf9841d887e7fc0236c07a6c1d26eb9d83f7",
+                "bytes": 1920633329}
 
 
 def src_sha(rel):

@@ -1890,8 +1890,10 @@ hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V,
 }
 
 // The pipelined path at a run-time depth takes bf16 operands whose rows are
-// 16-byte aligned, a depth that is a multiple of 64 (at least 256), and row
-// strides small enough that 256 rows stay below 4 GB of buffer range.
+// 16-byte aligned, a depth that is a multiple of 32 and at least 256 (the
+// 128 x 192 tiles need a multiple of 64; f32out_rt takes 256 x 256 tiles
+// otherwise), and row strides small enough that 256 rows stay below 4 GB of
+// buffer range.
 static bool f32_rt_ok(const void* A, int lda, const void* W, int ldw, int Ks) {
   return Ks % 32 == 0 && Ks >= 256 && lda % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)A & 15) == 0 &&
          ((uintptr_t)W & 15) == 0 && (size_t)256 * lda * 2 < (1ull << 32) && (size_t)256 * ldw * 2 < (1ull << 32);
