@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "63972c6c70bf023ac139f3b39303cf9841d887e7fc0236c07a6c1d26eb9d83f7",
-                "bytes": 1920633329}
+HEAD_TRAFFIC = {"gemm_src_sha256": "627ec2ac03f5bb2f094ede1e6a58b810b25786540c4c3d678562b5698a2cb8ef",
+                "bytes": 1918138601}
 
 
 def src_sha(rel):

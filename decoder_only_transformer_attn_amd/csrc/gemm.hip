@@ -1885,8 +1885,12 @@ hipError_t launch_head_dz(int dtype, const void* A, const void* W, int M, int V,
   if (dtype == 0)
     return dispatch_gemm_tiled((const float*)A, C, (const float*)W, C, M, V, C,
                                EpiDz<float>{lse, y, inv, (float*)dz, ld, (float*)dzT, ldT}, st);
-  return dispatch_gemm_tiled((const bf16*)A, C, (const bf16*)W, C, M, V, C,
-                             EpiDz<bf16>{lse, y, inv, (bf16*)dz, ld, (bf16*)dzT, ldT}, st);
+  const EpiDz<bf16> e{lse, y, inv, (bf16*)dz, ld, (bf16*)dzT, ldT};
+  // at C = 768: 128 x 192 tiles in two stages, two blocks per CU, so one
+  // block's store-heavy epilogue overlaps the other's main loop
+  if (C == 768 && M >= 1024 && (long long)((M + 127) / 128) * ((V + 191) / 192) >= 512)
+    return run_gemm_dma<128, 192, 32, 96, 768, 2, 64>((const bf16*)A, (const bf16*)W, M, V, e, st);
+  return dispatch_gemm_tiled((const bf16*)A, C, (const bf16*)W, C, M, V, C, e, st);
 }
 
 // The pipelined path at a run-time depth takes bf16 operands whose rows are
