@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "627ec2ac03f5bb2f094ede1e6a58b810b25786540c4c3d678562b5698a2cb8ef",
-                "bytes": 1918138601}
+HEAD_TRAFFIC = {"gemm_src_sha256": "0426c63183e1f7f33846b85b9bd3426df13962b365214b501bd8d05331dc1ad9",
+                "bytes": 1920548050}
 
 
 def src_sha(rel):

@@ -1904,14 +1904,20 @@ static bool f32_rt_ok(const void* A, int lda, const void* W, int ldw, int Ks) {
 }
 
 // S slices (S >= 1) of Ks columns; slice z writes out + z zstride, [M, ldo].
-// 256 x 256 tiles (four 32-deep stages; twice the flops per loaded byte of
-// 128 x 192) once they fill three quarters of the CUs, else 128 x 192 (three
-// 64-deep stages, Ks a multiple of 64).
+// 128 x 192 tiles in two stages when they give at least 512 blocks (two per
+// CU); else 256 x 256 tiles (four 32-deep stages; twice the flops per loaded
+// byte of 128 x 192) once they fill three quarters of the CUs, else 128 x 192
+// in three 64-deep stages (Ks a multiple of 64).
 template <bool ACC>
 static hipError_t f32out_rt(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int Ks, int S, float* out,
                             int ldo, long long zstride, hipStream_t st) {
   const EpiF32<ACC> epi{out, ldo};
   const long long blocks256 = (long long)((M + 255) / 256) * ((N + 255) / 256) * S;
+  const long long blocks192 = (long long)((M + 127) / 128) * ((N + 191) / 192) * S;
+  // with at least two blocks per CU: 128 x 192 tiles in two stages (80 KB of
+  // LDS), so one block's epilogue and load waits overlap the other's products
+  if (N % 192 == 0 && Ks % 64 == 0 && blocks192 >= 512)
+    return run_gemm_dma_rt<128, 192, 32, 96, 2, 64>(A, lda, W, ldw, M, N, Ks, S, zstride, epi, st);
   if (blocks256 >= 192 || Ks % 64 != 0)
     return run_gemm_dma_rt<256, 256, 64, 128, 4, 32>(A, lda, W, ldw, M, N, Ks, S, zstride, epi, st);
   return run_gemm_dma_rt<128, 192, 32, 96, 3, 64>(A, lda, W, ldw, M, N, Ks, S, zstride, epi, st);

@@ -459,23 +459,29 @@ int check_cache_args(const gpt_config* cfg, void* kc, void* vc, int Tmax, int B)
 // contracted axis (Vp to a multiple of 256, Np of 64), so both gradient
 // products run without a K tail.  The vocabulary contraction of da = dz W
 // (a small [M, C] output) is split into S slices of Vp / S (fp32 partials,
-// summed in slice order) so that its 256 x 256 tiles fill the CUs.
+// summed in slice order) so that its tiles fill the CUs.
 struct BwdPlan {
   size_t a, aT, ET, dz, dzT, pmax, psum, tgt, tok, bsum, lse, yv, inv, da, dapart, mu, rs, lnpart, total;
   int ntiles, nblocks, Vp, Np, nchunks, S;
 };
 
 // Slices of the vocabulary contraction: the S in {1, 2, 4, 8} with the least
-// time per slice-round (rounds of 256 tiles over the CUs, divided by S), the
-// smallest on a tie; Vp / S stays a multiple of 32 and at least 256.
+// time per slice-round (rounds of blocks over the CUs, divided by S), the
+// smallest on a tie; Vp / S stays a whole number of stages and at least 256.
 static int da_split(int dtype, size_t M, size_t C, int Vp) {
   if (dtype == 0) return 1;
-  const long long tiles = (long long)((M + 255) / 256) * (long long)((C + 255) / 256);
+  // C a multiple of 192: 128 x 192 tiles, two blocks per CU (512 per round);
+  // otherwise 256 x 256 tiles, one per CU
+  const bool t192 = C % 192 == 0;
+  const long long tiles = t192 ? (long long)((M + 127) / 128) * (long long)(C / 192)
+                               : (long long)((M + 255) / 256) * (long long)((C + 255) / 256);
+  const long long round = t192 ? 512 : 256;
+  const int quantum = t192 ? 64 : 32;
   int best = 1;
-  double best_t = (double)((tiles + 255) / 256);
+  double best_t = (double)((tiles + round - 1) / round);
   for (int S = 2; S <= 8; S *= 2) {
-    if ((Vp / S) % 32 != 0 || Vp % S != 0 || Vp / S < 256) break;
-    const double t = (double)((tiles * S + 255) / 256) / S;
+    if (Vp % S != 0 || (Vp / S) % quantum != 0 || Vp / S < 256) break;
+    const double t = (double)((tiles * S + round - 1) / round) / S;
     if (t < best_t) { best_t = t; best = S; }
   }
   return best;
