@@ -9,7 +9,7 @@ cross-entropy.  Workload 4: B=32 without logits.  Workload 5: greedy decode,
 B=64 prompts of 128 tokens then 128 steps (each step replayed from a HIP
 graph); one step = one decode step.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4|5] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4|5] [--no-cpu-baseline] [--extra-legs]
   python bench.py --copy-calibration     # plain device copy of known size, for HBM counter scaling
 
 Step times come from hipEvents recorded on the library's stream at every
@@ -229,7 +229,7 @@ def bench_forward(args, w):
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(head_ms, 4), "flops_per_launch": head_flops},
     }
-    if args.workload == 3:
+    if args.workload == 3 and args.extra_legs:
         out["head_backward"] = bench_head_backward(cfg, B, T, dev_params, idx, stream)
         out["train_grad"] = bench_train_grad(cfg, B, T, dev_params, idx, stream)
         out["llama"] = bench_llama_forward(args)
@@ -460,6 +460,10 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[3, 4, 5])
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-legs", action="store_true",
+                    help="workload 3: also time the loss backward, the full gradient and the LLaMA-style forward "
+                         "(after the forward; off by default so a profile of the default run holds only the "
+                         "forward's launches)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -22,11 +22,11 @@ Sources (web pages, cited by title and section):
 
 Readings (the pages leave these open):
   * order of the steps: penalty, temperature, top-k, top-p, draw;
-  * the key z'/T and the penalty are formed in float32 (the precision the GPU
-    holds the logits in); each candidate's unnormalised probability weight is
-    exp(key - max key) evaluated in float64 and rounded once to float32, so
-    both sides rank and weigh identical values; masses, thresholds and the
-    draw are float64 sums of those weights (the precision of [P1]'s sampler);
+  * precision: float64 throughout, the precision of [P1]'s numpy sampler
+    (the logits themselves are the values the model produced, bf16 or fp32,
+    upcast exactly): the penalised logit, the key z'/T, each candidate's
+    unnormalised probability weight exp(key - max key), the masses, the
+    thresholds and the draw;
   * the nucleus is taken of the distribution left by top-k (renormalised),
     as the smallest prefix in descending probability whose mass is >= p * Z;
   * candidates are ordered by descending weight, equal weights by ascending
@@ -50,11 +50,11 @@ import numpy as np
 
 def penalize(z: np.ndarray, seen: Optional[np.ndarray], alpha: float) -> np.ndarray:
     """[P4] §8.4: z/alpha where the token appeared and z > 0, z*alpha where it
-    appeared and z < 0, unchanged otherwise (float32)."""
-    z = np.asarray(z, dtype=np.float32)
+    appeared and z < 0, unchanged otherwise (float64)."""
+    z = np.asarray(z, dtype=np.float64)
     if seen is None or alpha == 1.0:
         return z.copy()
-    a = np.float32(alpha)
+    a = np.float64(alpha)
     seen = np.asarray(seen, dtype=bool)
     out = z.copy()
     pos = seen & (z > 0)
@@ -67,25 +67,30 @@ def penalize(z: np.ndarray, seen: Optional[np.ndarray], alpha: float) -> np.ndar
 def candidate_order(w: np.ndarray) -> np.ndarray:
     """Indices by descending weight, ascending index among equal weights."""
     V = w.size
-    return np.lexsort((np.arange(V), -w.astype(np.float64)))
+    return np.lexsort((np.arange(V), -np.asarray(w, dtype=np.float64)))
+
+
+def keys(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, alpha: float = 1.0) -> np.ndarray:
+    """key = z'/T ([P1] 第7步, [P4] §8.1), z' the penalised logits (float64)."""
+    return penalize(z, seen, alpha) / np.float64(temperature)
 
 
 def weights(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, alpha: float = 1.0) -> np.ndarray:
-    """Unnormalised probability weights exp(key - max key), key = z'/T in
-    float32 ([P1] 第7步, [P4] §8.1), the exponential in float64 rounded to float32."""
-    key = (penalize(z, seen, alpha) / np.float32(temperature)).astype(np.float32)
-    return np.exp(key.astype(np.float64) - np.float64(key.max())).astype(np.float32)
+    """Unnormalised probability weights exp(key - max key) (float64): the
+    softmax numerator with the maximum subtracted ([P1] 第7步)."""
+    key = keys(z, seen, temperature, alpha)
+    return np.exp(key - key.max())
 
 
 def filtered(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, top_k: int, top_p: float,
              alpha: float = 1.0):
     """The candidates left after penalty, temperature, top-k and top-p, in
     candidate order, with their float64 weights."""
-    w32 = weights(z, seen, temperature, alpha)
-    order = candidate_order(w32)
-    V = w32.size
+    w64 = weights(z, seen, temperature, alpha)
+    order = candidate_order(w64)
+    V = w64.size
     cand = order[:top_k] if 0 < top_k < V else order                # [P4] §8.2, [P5] §6.2
-    w = w32[cand].astype(np.float64)
+    w = w64[cand]
     if top_p < 1.0:                                                 # [P4] §8.3, [P5] §6.2
         cum = np.cumsum(w)
         n = int(np.searchsorted(cum, top_p * cum[-1], side="left")) + 1   # first prefix with mass >= p Z
@@ -99,7 +104,7 @@ def sample_row(z: np.ndarray, seen: Optional[np.ndarray], temperature: float, to
     if temperature <= 0:
         return int(np.argmax(penalize(z, seen, alpha)))             # first maximum: lowest index
     cand, w = filtered(z, seen, temperature, top_k, top_p, alpha)
-    r = float(np.float32(u)) * float(w.sum())
+    r = float(u) * float(w.sum())
     pos = int(np.searchsorted(np.cumsum(w), r, side="right"))       # first cumulative mass > r
     return int(cand[min(pos, len(cand) - 1)])
 

@@ -1,13 +1,22 @@
 """GPU parity of the sampler (gpt_sample through the C ABI) against the
-sampling oracle on the same logits, seen sets and uniforms.
+float64 sampling oracle on the same logits, seen sets and uniforms.
 
-Both sides rank identical float32 weights (exp in float64 rounded once) and
-decide on float64 masses, so the chosen tokens must be equal, bit for bit
-(a difference needs a uniform or p * Z within about 1e-15 of a boundary).
-Logit rows cover flat and peaked distributions, many ties (integer logits),
-ragged vocabularies and the full GPT-2 vocabulary; settings cover greedy,
-plain temperature, top-k, top-p, their combination and the repetition
-penalty (the ids of a 64-row batch exercise every path at once).
+The oracle decides in float64 (the precision of the Mini-GPT lesson's numpy
+sampler, 构建它 第7步); the kernel forms the penalised key in float32 and
+rounds each weight exp(key - max) to float32 before summing in double.  A
+GPU token is accepted when it equals the oracle's draw, or when it is a
+correct draw under the float64 distribution up to that rounding
+(``valid_draw``): it survives top-k and top-p under some order of the
+candidates whose keys lie within the rounding bound tau of each other, and
+u * Z lies inside its cumulative-mass interval widened by 2 tau Z.  The
+bound follows from the kernel's arithmetic: two float32 divisions give
+|key_f32 - key| <= 2^-23 |key|, so every weight and mass is within
+tau = 2^-22 (2 max|key| + 1) (relative; a factor 2 of margin) of the float64
+value.  Every test also reports how many tokens differ from the oracle's
+own draw.  Logit rows cover flat and peaked distributions, many ties
+(integer logits), ragged vocabularies and the full GPT-2 vocabulary;
+settings cover greedy, plain temperature, top-k, top-p, their combination
+and the repetition penalty ("02 GPT 架构" 第 8 章 §8.1-§8.4).
 """
 import numpy as np
 import pytest
@@ -48,6 +57,70 @@ SETTINGS = [  # temperature, top_k, top_p, penalty
     (1.3, 200, 0.95, 1.1), (0.5, 1, 1.0, 1.0), (1.0, 0, 0.3, 1.3), (0.0, 0, 1.0, 1.4), (2.0, 7, 0.5, 1.0)]
 
 
+def _tau(key):
+    return 2.0 ** -22 * (2.0 * float(np.abs(key).max()) + 1.0)
+
+
+def valid_draw(z, seen, t, k, p, a, u, tok):
+    """True when tok is a correct draw from the float64 filtered distribution
+    of the row z, up to the kernel's float32 rounding of keys and weights."""
+    V = z.size
+    if not 0 <= tok < V:
+        return False
+    if t <= 0:   # greedy on the penalised logits
+        key = S.penalize(z, seen, a)
+        return key[tok] >= key.max() - _tau(key)
+    key = S.keys(z, seen, t, a)
+    tau = _tau(key)
+    w = np.exp(key - key.max())
+    order = S.candidate_order(w)
+    kk = k if 0 < k < V else V
+    topk = order[:kk]
+    # before tok in every admissible order: keys larger beyond the bound, and
+    # exact ties at lower indices (equal float64 keys are equal in float32,
+    # and both sides break such ties by index)
+    idx = np.arange(V)
+    heavier = (key > key[tok] + tau) | ((key == key[tok]) & (idx < tok))
+    near = (np.abs(key - key[tok]) <= tau) & (key != key[tok])   # may fall either side of tok
+    if heavier.sum() >= kk:                           # tok cannot be among the k largest
+        return False
+    in_k = np.zeros(V, bool)
+    in_k[topk] = True
+    # near ties straddling the k-th place can each be kept
+    if 0 < k < V:
+        in_k |= (np.abs(key - key[topk[-1]]) <= tau) & (key != key[topk[-1]])
+    Zk = float(w[topk].sum())
+    cum = np.cumsum(w[topk])
+    # nucleus sizes consistent with the rounding (the oracle's, or one either
+    # side when p Zk lies within 2 tau Zk of a cumulative boundary)
+    sizes = [len(topk)]
+    if p < 1.0:
+        X = p * Zk
+        n0 = int(np.searchsorted(cum, X, side="left")) + 1
+        sizes = [n for n in (n0 - 1, n0, n0 + 1)
+                 if 1 <= n <= len(topk) and cum[n - 1] >= X - 2 * tau * Zk
+                 and (n == 1 or cum[n - 2] < X + 2 * tau * Zk)]
+    lo = float(w[heavier & in_k].sum())
+    hi = lo + float(w[near & in_k].sum()) + float(w[tok])
+    for n in sizes:
+        if (heavier & in_k).sum() >= n:               # tok cannot be among the first n
+            continue
+        r = float(u) * float(cum[n - 1])
+        if lo - 2 * tau * Zk <= r <= hi + 2 * tau * Zk:
+            return True
+    return False
+
+
+def check_rows(zin, seen, t, k, p, a, u, got, what):
+    """Every GPU token valid; returns the number that differ from the oracle's draw."""
+    ref = S.sample_rows(zin, seen, t, k, p, a, u)
+    bad = [b for b in range(zin.shape[0])
+           if got[b] != ref[b] and not valid_draw(zin[b], None if seen is None else seen[b], t, k, p, a, u[b],
+                                                  int(got[b]))]
+    assert not bad, f"{what}: invalid draws in rows {bad[:8]} (gpu {got[bad[:8]]}, oracle {ref[bad[:8]]})"
+    return int((got != ref).sum())
+
+
 def _rows(V, B, kind, rng):
     if kind == "flat":
         z = rng.normal(0, 0.3, (B, V))
@@ -75,12 +148,14 @@ def test_sampler_matches_oracle(dtype, V, B, kind):
         seen = torch.from_numpy(_bits(seen0)).cuda()
         got = lib.sample(cfg, zt, lib.sampling(t, k, p, a), torch.from_numpy(u).cuda(), seen)
         torch.cuda.synchronize()
-        ref = S.sample_rows(zin, seen0, t, k, p, a, u)
-        np.testing.assert_array_equal(got.cpu().numpy(), ref, err_msg=f"settings {(t, k, p, a)}")
+        g = got.cpu().numpy()
+        diff = check_rows(zin, seen0, t, k, p, a, u, g, f"settings {(t, k, p, a)}")
+        if diff:
+            print(f"V={V} B={B} {kind} {(t, k, p, a)}: {diff} of {B} tokens differ from the oracle's draw (valid)")
         # the chosen tokens' bits are set, the others unchanged
         after = _unbits(seen.cpu().numpy(), V)
         expect = seen0.copy()
-        expect[np.arange(B), ref] = True
+        expect[np.arange(B), g] = True
         np.testing.assert_array_equal(after, expect)
 
 
@@ -94,8 +169,7 @@ def test_sampler_without_seen_and_determinism():
     a = lib.sample(cfg, zt, s, u).cpu().numpy()
     b = lib.sample(cfg, zt, s, u).cpu().numpy()
     np.testing.assert_array_equal(a, b)
-    ref = S.sample_rows(zt.float().cpu().numpy(), None, 0.9, 0, 0.92, 1.2, u.cpu().numpy())
-    np.testing.assert_array_equal(a, ref)
+    check_rows(zt.float().cpu().numpy(), None, 0.9, 0, 0.92, 1.2, u.cpu().numpy(), a, "no seen set")
 
 
 def test_stratified_draws_follow_the_filtered_distribution():
@@ -109,6 +183,10 @@ def test_stratified_draws_follow_the_filtered_distribution():
     u = torch.from_numpy(((np.arange(N) + 0.5) / N).astype(np.float32)).cuda()
     got = lib.sample(cfg, zt, lib.sampling(0.9, 10, 0.8), u).cpu().numpy()
     cand, w = S.filtered(z, None, 0.9, 10, 0.8)
+    # the case is well posed: p Z lies far from every cumulative boundary of
+    # the top-k set, so the float32 rounding cannot change the nucleus
+    ck, wk = S.filtered(z, None, 0.9, 10, 1.0)
+    assert np.min(np.abs(np.cumsum(wk) - 0.8 * wk.sum())) > 1e-4 * wk.sum()
     expect = np.zeros(V)
     expect[cand] = w / w.sum()
     assert np.all(np.abs(np.bincount(got, minlength=V) / N - expect) <= 2.0 / N)
@@ -156,7 +234,7 @@ def test_sampled_decode_follows_the_oracle_sampler():
         else:
             tok = dec.step(P, logits=z, sampling=s, u=torch.from_numpy(u).cuda())
         torch.cuda.synchronize()
-        ref = S.sample_rows(z.float().cpu().numpy(), seen, 0.9, 40, 0.9, 1.2, u)
-        np.testing.assert_array_equal(tok.cpu().numpy(), ref, err_msg=f"emission {it}")
-        seen[np.arange(B), ref] = True
+        g = tok.cpu().numpy()
+        check_rows(z.float().cpu().numpy(), seen, 0.9, 40, 0.9, 1.2, u, g, f"emission {it}")
+        seen[np.arange(B), g] = True
     assert int(dec.pos.item()) == Tp + steps
