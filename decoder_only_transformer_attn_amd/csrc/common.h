@@ -92,6 +92,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// The value of the neighbouring lane l ^ 1, by a DPP quad permutation
+// [1, 0, 3, 2] inside the VALU instruction (no LDS round trip, unlike a
+// general lane shuffle).
+__device__ __forceinline__ float xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
 // Reductions over the 32 lanes of one half-wave (lanes sharing l / 32).
 __device__ __forceinline__ float half_sum(float v) {
 #pragma unroll

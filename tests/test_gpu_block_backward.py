@@ -52,7 +52,9 @@ def run_block(cfg, params, layer, x, dy, seed=0):
     xd = torch.from_numpy(x.reshape(B * T, C).astype(np.float32)).cuda()
     dyd = torch.from_numpy(dy.reshape(B * T, C).astype(np.float32)).cuda()
     dx = torch.full_like(xd, float("nan"))
-    ws = torch.empty(lib.block_backward_workspace_bytes(cfg, B, T), dtype=torch.uint8, device="cuda")
+    # workspace filled with 0xFF bytes (NaN in bf16 and fp32): a read of any
+    # byte no kernel of the call wrote shows up as a non-finite gradient
+    ws = torch.full((lib.block_backward_workspace_bytes(cfg, B, T),), 255, dtype=torch.uint8, device="cuda")
     lib.block_backward(cfg, P, layer, B, T, xd, dyd, dx, grads, ws)
     torch.cuda.synchronize()
     return dx.cpu().numpy().reshape(B, T, C), grads.cpu().numpy().astype(np.float64) - g0
@@ -77,6 +79,7 @@ def check_block(cfg, layer, B, T, seed, init="stress"):
         touched[off:off + n] = True
     print({k: f"{v:.2e}" for k, v in errs.items()})
     assert np.isfinite(dx).all()
+    assert np.isfinite(dg).all()
     for k, v in errs.items():
         assert v <= tol, (k, v)
     assert np.all(dg[~touched] == 0)   # no other tensor's gradient changed
@@ -97,6 +100,16 @@ def test_block_backward_register_row_widths(dtype, C, H):
     # two or four 16-byte pieces of each row per lane
     cfg = synth.GPTConfig(vocab=97, ctx=64, n_embd=C, n_head=H, n_layer=1, n_ff=2 * C, dtype=dtype)
     check_block(cfg, 0, 1, 40, seed=C + H)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("T", [100, 60, 128])
+def test_block_backward_head_width_128(dtype, T):
+    # D = 128 with 64 < T < 128: the contractions of the attention backward
+    # take 128-row tiles, so the score tiles they read must be 128 x 128 too
+    # (64 x 64 score tiles leave the tile above the diagonal unwritten)
+    cfg = synth.GPTConfig(vocab=97, ctx=128, n_embd=256, n_head=2, n_layer=1, n_ff=512, dtype=dtype)
+    check_block(cfg, 0, 2, T, seed=T + 128)
 
 
 def test_block_backward_gpt2_width_bf16():

@@ -35,7 +35,7 @@ def run_decode(cfg, params, prompt, steps, Tmax, rows=None):
     B, Tp = prompt.shape
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
     idx = torch.from_numpy(np.ascontiguousarray(prompt, dtype=np.int32)).cuda()
-    dec = lib.Decoder(cfg, B, Tp, Tmax)
+    dec = lib.Decoder(cfg, B, Tp, Tmax, poison=True)
     z = torch.empty((steps + 1, B, cfg.vocab), dtype=lib.torch_dtype(cfg), device="cuda")
     toks = torch.empty((steps + 1, B), dtype=torch.int32, device="cuda")
     dec.prefill(P, idx, last_logits=z[0])
@@ -142,7 +142,9 @@ def test_decode_cache_matches_forward_kv_fp32():
         scale = max(np.abs(k_ref).max(), np.abs(u_ref).max())
         assert np.abs(kc[l, :, :, :7] - k_ref).max() <= 1e-4 * scale
         assert np.abs(vc[l, :, :, :7] - u_ref).max() <= 1e-4 * scale
-        assert np.all(kc[l, :, :, 7:] == 0)                               # rows past the position untouched
+        # rows past the position untouched: still the 0xFF fill of the poisoned caches
+        raw = dec.k_cache[l, :, :, 7:].contiguous().view(torch.uint8)
+        assert bool((raw == 255).all())
 
 
 def bf16_tol(_):
@@ -201,14 +203,14 @@ def test_gpt2_bf16_decode_agrees_with_forward(gpt2_decode_run):
     cfg, params, prompt, toks, _, _ = gpt2_decode_run
     seq = np.concatenate([prompt, toks[:, :128]], axis=1)             # [64, 256]
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
-    dec = lib.Decoder(cfg, 64, 128, 256)
+    dec = lib.Decoder(cfg, 64, 128, 256, poison=True)
     zstep = torch.empty((129, 64, cfg.vocab), dtype=torch.bfloat16, device="cuda")
     dec.prefill(P, torch.from_numpy(prompt).cuda(), last_logits=zstep[0])
     forced = torch.from_numpy(np.ascontiguousarray(toks[:, :128])).cuda()
     for s in range(128):
         dec.tok.copy_(forced[:, s])
         dec.step(P, logits=zstep[s + 1])
-    f = lib.Forward(cfg, 64, 256, want_logits=True)
+    f = lib.Forward(cfg, 64, 256, want_logits=True, poison=True)
     lg, _, _ = f(P, torch.from_numpy(seq).cuda())
     ref = lg[:, 127:256].float().permute(1, 0, 2)
     err = (zstep.float() - ref).abs().max().item()
@@ -229,7 +231,7 @@ def test_decode_step_graph_replay_matches_eager(n_ff):
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
     steps = 6
 
-    eager = lib.Decoder(cfg, 4, 10, 32)
+    eager = lib.Decoder(cfg, 4, 10, 32, poison=True)
     eager.prefill(P, prompt)
     ref_tok, ref_z = [], []
     for _ in range(steps):
@@ -239,7 +241,7 @@ def test_decode_step_graph_replay_matches_eager(n_ff):
         ref_z.append(z)
     torch.cuda.synchronize()
 
-    g = lib.Decoder(cfg, 4, 10, 32)
+    g = lib.Decoder(cfg, 4, 10, 32, poison=True)
     zg = torch.empty((4, cfg.vocab), dtype=torch.bfloat16, device="cuda")
     g.prefill(P, prompt)
     torch.cuda.synchronize()

@@ -41,7 +41,7 @@ def run_forward(cfg, params, ids, targets=None):
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
     idx = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     tg = None if targets is None else torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int32)).cuda()
-    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], True)
+    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], True, poison=True)
     logits, tok, mean = f(P, idx, tg)
     torch.cuda.synchronize()
     return logits.float().cpu().numpy(), tok.cpu().numpy(), float(mean.item())
@@ -105,7 +105,7 @@ def run_decode(cfg, params, prompt, steps, Tmax):
     B, Tp = prompt.shape
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
     idx = torch.from_numpy(np.ascontiguousarray(prompt, dtype=np.int32)).cuda()
-    dec = lib.Decoder(cfg, B, Tp, Tmax)
+    dec = lib.Decoder(cfg, B, Tp, Tmax, poison=True)
     z = torch.empty((steps + 1, B, cfg.vocab), dtype=lib.torch_dtype(cfg), device="cuda")
     toks = torch.empty((steps + 1, B), dtype=torch.int32, device="cuda")
     dec.prefill(P, idx, last_logits=z[0])

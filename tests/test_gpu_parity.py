@@ -31,7 +31,7 @@ def run_gpu(cfg, params, ids, targets=None, want_logits=True):
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
     idx = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     tg = None if targets is None else torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int32)).cuda()
-    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], want_logits)
+    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], want_logits, poison=True)
     logits, tok, mean = f(P, idx, tg)
     torch.cuda.synchronize()
     lg = None if logits is None else logits.float().cpu().numpy()
@@ -294,6 +294,27 @@ def test_gpt2_bf16_b8_t1024_parity(gpt2_inputs):
     assert abs(mean - math.log(cfg.vocab)) < 0.5
 
 
+def test_gpt2_bf16_b8_t1024_stress_all_sequences():
+    # the full bench shape with the stress init (random biases and LayerNorm
+    # gains/offsets), every sequence compared with the oracle element by
+    # element, and the mean loss against the oracle's mean over all of them
+    cfg = synth.GPT2
+    params = synth.make_params(cfg, seed=13, cfg_id=3, init="stress")
+    P = synth.unpack_f64(cfg, params)
+    ids = synth.make_ids(cfg, 8, 1024, seed=13, cfg_id=3)
+    lg, tok, mean = run_gpu(cfg, params, ids)
+    assert np.isfinite(lg).all()
+    ref_tok = []
+    for b in range(8):
+        l, t, _ = O.forward(P, ids[b:b + 1], cfg.n_head)
+        _bf16_check(lg, tok, [l[0]], [t[0]], [b])
+        ref_tok.append(t[0][:-1])
+        del l
+    ref_mean = float(np.concatenate(ref_tok).mean())
+    print(f"mean loss gpu {mean:.6f} oracle {ref_mean:.6f}")
+    assert abs(mean - ref_mean) <= 1e-2
+
+
 def test_gpt2_bf16_ragged_stress(gpt2_inputs):
     cfg = synth.GPT2
     params = synth.make_params(cfg, seed=9, cfg_id=3, init="stress")
@@ -345,9 +366,13 @@ def test_gpt2_bf16_no_logits_b32_matches_logits_path(gpt2_inputs):
     # same rows through the logits-writing path: identical partials, identical losses
     _, tok8, _ = run_gpu(cfg, params, ids[:8], want_logits=True)
     np.testing.assert_array_equal(tok[:8], tok8)
-    b = 17
-    _, ref_t, _ = O.forward(P, ids[b:b + 1], cfg.n_head, want_logits=False)
-    terr = np.abs(tok[b] - ref_t[0]).max()
-    print(f"C4 seq {b}: max|dtokloss| {terr:.4f}")
-    assert terr <= 5e-2
+    # sequences from both ends and the middle of the batch against the oracle
+    for b in (0, 11, 17, 31):
+        _, ref_t, _ = O.forward(P, ids[b:b + 1], cfg.n_head, want_logits=False)
+        terr = np.abs(tok[b] - ref_t[0]).max()
+        print(f"C4 seq {b}: max|dtokloss| {terr:.4f}, seq mean gpu {tok[b, :-1].mean():.5f} "
+              f"oracle {ref_t[0][:-1].mean():.5f}")
+        assert terr <= 5e-2
+        assert abs(tok[b, :-1].mean() - ref_t[0][:-1].mean()) <= 1e-2
+    assert np.isfinite(tok).all()
     assert abs(mean - tok[:, :-1].astype(np.float64).mean()) <= 1e-5

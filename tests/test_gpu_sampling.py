@@ -219,7 +219,7 @@ def test_sampled_decode_follows_the_oracle_sampler():
     B, Tp, steps = 6, 9, 8
     prompt = synth.make_ids(cfg, B, Tp, seed=7, cfg_id=9)
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
-    dec = lib.Decoder(cfg, B, Tp, 32)
+    dec = lib.Decoder(cfg, B, Tp, 32, poison=True)
     s = lib.sampling(0.9, 40, 0.9, 1.2)
     rng = np.random.default_rng(1)
     z = torch.empty((B, cfg.vocab), dtype=torch.bfloat16, device="cuda")
