@@ -268,16 +268,28 @@ def params_to_device(cfg, blob, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(blob, dtype=np.float32)).to(device)
 
 
+def _poison(t) -> None:
+    """Every byte of t set to 0xFF (a NaN in bf16 and fp32)."""
+    t.view(-1).view(__import__("torch").uint8).fill_(255)
+
+
 class Forward:
     """Holds the output and workspace tensors for repeated gpt_forward calls on one shape."""
 
-    def __init__(self, cfg, B: int, T: int, want_logits: bool = True, device="cuda"):
+    def __init__(self, cfg, B: int, T: int, want_logits: bool = True, device="cuda", poison: bool = False):
+        """poison: fill the workspace and the outputs with 0xFF bytes (NaN in
+        bf16 and fp32), so that a read of anything the call did not write
+        first shows up in the results."""
         import torch
         self.cfg, self.B, self.T = cfg, B, T
         self.ws = torch.empty(workspace_bytes(cfg, B, T), dtype=torch.uint8, device=device)
         self.logits = torch.empty((B, T, cfg.vocab), dtype=torch_dtype(cfg), device=device) if want_logits else None
         self.token_loss = torch.empty((B, T), dtype=torch.float32, device=device)
         self.mean_loss = torch.empty((1,), dtype=torch.float32, device=device)
+        if poison:
+            for t in (self.ws, self.logits, self.token_loss, self.mean_loss):
+                if t is not None:
+                    _poison(t)
 
     def __call__(self, params, idx, targets=None, stream=None):
         forward(self.cfg, params, idx, targets, self.logits, self.token_loss, self.mean_loss, self.ws, stream)
@@ -341,7 +353,10 @@ class Decoder:
     default, or sampled (prefill / step with `sampling=` and one uniform per
     sequence in `u`; a repetition penalty reads and updates self.seen)."""
 
-    def __init__(self, cfg, B: int, Tp: int, Tmax: int, device="cuda"):
+    def __init__(self, cfg, B: int, Tp: int, Tmax: int, device="cuda", poison: bool = False):
+        """poison: fill the workspace and both caches with 0xFF bytes (NaN):
+        cache positions past the current one are never read, and nothing in
+        the workspace is read before the call writes it."""
         import torch
         H = cfg.n_head
         D = cfg.n_embd // H
@@ -355,6 +370,9 @@ class Decoder:
         self.ws = torch.empty(decode_workspace_bytes(cfg, B, Tp), dtype=torch.uint8, device=device)
         self.seen = torch.zeros((B, seen_words(cfg)), dtype=torch.int32, device=device)
         self._logits = None
+        if poison:
+            for t in (self.ws, self.k_cache, self.v_cache):
+                _poison(t)
 
     def _row_logits(self, logits):
         import torch
