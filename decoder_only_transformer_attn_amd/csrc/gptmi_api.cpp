@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gptmi.h"
 #include "kernels.h"
@@ -574,6 +575,63 @@ BlkPlan blk_plan(const gpt_config* c, int B, int T) {
   return p;
 }
 
+int decode_step_impl(const gpt_config* cfg, const void* params, const int32_t* tok, int B, int32_t* pos,
+                     void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!params || !tok || !ws || !pos || !next_tok) return GPT_ERR_NULL;
+  s = check_cache_args(cfg, k_cache, v_cache, Tmax, B);
+  if (s != GPT_OK) return s;
+  const Plan pl = plan(cfg, B, 1, true);
+  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
+
+  Pass ps{cfg, params_of(cfg, params), tok, B, 1, STEP, pos, k_cache, v_cache, Tmax, ws, pl,
+          static_cast<hipStream_t>(stream), nullptr, nullptr, -1};
+  s = run_blocks(ps);
+  if (s != GPT_OK) return s;
+  void* a = at<char>(ws, pl.a);
+  if (!rows_final(cfg)) {
+    s = final_norm(ps, B, 1, 0, a);
+    if (s != GPT_OK) return s;
+  }
+  const int V = cfg->vocab;
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), B, V, cfg->n_embd, logits, V,
+                         at<float>(ws, pl.pmax), nullptr, nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1,
+                         ps.st));
+  GPT_TRY(launch_argmax_reduce(B, pl.ntiles, at<float>(ws, pl.pmax), at<int32_t>(ws, pl.pidx), next_tok, pos, -1,
+                               ps.st));
+  return GPT_OK;
+}
+
+// Scratch of gpt_decode_step_noalloc (for callers that cannot allocate): one
+// copy of this array per GPU, held until the process ends.  Host code never
+// uses the array's name as an address: the device address is fetched once per
+// device with hipGetSymbolAddress (that device current) and kept per device.
+static __device__ __align__(256) char scratch[GPT_DECODE_NOALLOC_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The current device's copy of `scratch`.
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (g_scratch_ptr[dev] == nullptr) return hipErrorInvalidSymbol;
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -705,30 +763,21 @@ int gpt_prefill(const gpt_config* cfg, const void* params, const int32_t* idx, i
 int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* tok, int B, int32_t* pos,
                     void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits, void* ws,
                     size_t ws_bytes, void* stream) {
+  return decode_step_impl(cfg, params, tok, B, pos, k_cache, v_cache, Tmax, next_tok, logits, ws, ws_bytes, stream);
+}
+
+int gpt_decode_step_noalloc(const gpt_config* cfg, const void* params, const int32_t* tok, int B, int32_t* pos,
+                            void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits, void* stream) {
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
-  if (!params || !tok || !ws || !pos || !next_tok) return GPT_ERR_NULL;
+  if (!params || !tok || !pos || !next_tok) return GPT_ERR_NULL;
   s = check_cache_args(cfg, k_cache, v_cache, Tmax, B);
   if (s != GPT_OK) return s;
-  const Plan pl = plan(cfg, B, 1, true);
-  if (ws_bytes < pl.total) return GPT_ERR_WORKSPACE;
-
-  Pass ps{cfg, params_of(cfg, params), tok, B, 1, STEP, pos, k_cache, v_cache, Tmax, ws, pl,
-          static_cast<hipStream_t>(stream), nullptr, nullptr, -1};
-  s = run_blocks(ps);
-  if (s != GPT_OK) return s;
-  void* a = at<char>(ws, pl.a);
-  if (!rows_final(cfg)) {
-    s = final_norm(ps, B, 1, 0, a);
-    if (s != GPT_OK) return s;
-  }
-  const int V = cfg->vocab;
-  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), B, V, cfg->n_embd, logits, V,
-                         at<float>(ws, pl.pmax), nullptr, nullptr, at<int32_t>(ws, pl.pidx), nullptr, nullptr, 1,
-                         ps.st));
-  GPT_TRY(launch_argmax_reduce(B, pl.ntiles, at<float>(ws, pl.pmax), at<int32_t>(ws, pl.pidx), next_tok, pos, -1,
-                               ps.st));
-  return GPT_OK;
+  if (plan(cfg, B, 1, true).total > (size_t)GPT_DECODE_NOALLOC_BYTES) return GPT_ERR_WORKSPACE;
+  void* ws = nullptr;
+  GPT_TRY(noalloc_scratch(&ws));
+  return decode_step_impl(cfg, params, tok, B, pos, k_cache, v_cache, Tmax, next_tok, logits, ws,
+                          (size_t)GPT_DECODE_NOALLOC_BYTES, stream);
 }
 
 int gpt_sample(const gpt_config* cfg, const void* logits, int B, const gpt_sampling* sp, const float* u,

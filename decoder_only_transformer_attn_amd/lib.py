@@ -52,6 +52,7 @@ SIGNATURES = {
     "gpt_decode_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "gpt_prefill": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gpt_decode_step": (_c_int, [_CFG, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_decode_step_noalloc": (_c_int, [_CFG, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "gpt_sample": (_c_int, [_CFG, _vp, _c_int, ctypes.POINTER(gpt_sampling), _vp, _vp, _vp, _vp]),
     "gpt_mark_seen": (_c_int, [_CFG, _vp, _c_int, _c_int, _vp, _vp]),
     "gpt_head_backward_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
@@ -318,6 +319,16 @@ def decode_step(cfg, params, tok, k_cache, v_cache, pos, next_tok, logits=None, 
     check(load().gpt_decode_step(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(tok), B, _ptr(pos), _ptr(k_cache),
                                  _ptr(v_cache), Tmax, _ptr(next_tok), _ptr(logits), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def decode_step_noalloc(cfg, params, tok, k_cache, v_cache, pos, next_tok, logits=None, stream=None) -> None:
+    """Enqueue gpt_decode_step_noalloc (the workspace is the library's static
+    per-GPU array; calls on one GPU must not overlap)."""
+    B = tok.shape[0]
+    Tmax = k_cache.shape[3] if k_cache.dim() == 5 else 0
+    check(load().gpt_decode_step_noalloc(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(tok), B, _ptr(pos),
+                                         _ptr(k_cache), _ptr(v_cache), Tmax, _ptr(next_tok), _ptr(logits),
+                                         _stream(stream)))
 
 
 def sampling(temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, repetition_penalty: float = 1.0):

@@ -194,6 +194,28 @@ int gpt_decode_step(const gpt_config* cfg, const void* params, const int32_t* to
                     void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---- a decode step that allocates nothing ----
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Exactly gpt_decode_step (same arguments, results and errors),
+ * except that the workspace is a library-owned static device array of
+ * GPT_DECODE_NOALLOC_BYTES (8 MiB) per GPU, allocated when the library is
+ * loaded and held until the process ends; its device address is looked up
+ * (hipGetSymbolAddress) on the first call on each device.  The call itself
+ * allocates and frees nothing.
+ *   Limit: the step's workspace at this B must fit, or GPT_ERR_WORKSPACE
+ *   (GPT-2 124M in bf16 fits up to B = 64: 5.3 MB).
+ *   Sharing: every call on one GPU uses that GPU's single array, which keeps
+ *   the previous call's contents (the step clears what must start at zero
+ *   itself); calls that overlap on one GPU (other streams or threads) race
+ *   on it, so the caller serialises them.
+ *   Errors: as gpt_decode_step; GPT_ERR_HIP if the array's address cannot be
+ *   obtained on the current device. */
+#define GPT_DECODE_NOALLOC_BYTES (8u << 20)
+int gpt_decode_step_noalloc(const gpt_config* cfg, const void* params, const int32_t* tok, int B, int32_t* pos,
+                            void* k_cache, void* v_cache, int Tmax, int32_t* next_tok, void* logits,
+                            void* stream);
+
 /* ---- sampling the next token from rows of logits ----
  * Steps, in this order (the pages name them; the order is a reading):
  *   repetition penalty ("02 GPT 架构" §8.4): the logit of a token whose bit is

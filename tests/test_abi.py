@@ -245,3 +245,20 @@ def test_block_backward_validation():
         assert bb(cc=bad) == lib.GPT_ERR_CONFIG
         assert L.gpt_forward_train(bad, 1, 1, 2, 5, None, 1, None, 1, 1 << 40, None) == lib.GPT_ERR_CONFIG
     assert L.gpt_forward_train(c, 1, 1, 2, 5, None, None, None, 1, 1 << 40, None) == lib.GPT_ERR_NULL
+
+
+def test_decode_noalloc_validation_before_any_hip_call():
+    # every host-checkable condition returns before the scratch lookup (a HIP
+    # call, which would fail here without a GPU)
+    L = lib.load()
+    c = ctypes.byref(lib.cfg_c(synth.GPT2))
+    kc = vc = pos = tok = nt = ctypes.c_void_p(16)
+
+    def step(B, Tmax=256, tok_=tok, cfg=c):
+        return L.gpt_decode_step_noalloc(cfg, 1, tok_, B, pos, kc, vc, Tmax, nt, None, None)
+    assert step(4096) == -5                      # the step's workspace exceeds GPT_DECODE_NOALLOC_BYTES
+    assert step(0) == -4 and step(4, Tmax=0) == -4
+    assert step(4, tok_=None) == -1
+    import dataclasses as dc
+    bad = ctypes.byref(lib.cfg_c(dc.replace(synth.GPT2, n_head=5)))
+    assert step(4, cfg=bad) == -2
