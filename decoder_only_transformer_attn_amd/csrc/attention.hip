@@ -107,17 +107,18 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   const int T_seq = a.T_seq, D = a.D;
 
   // grouped-query attention: query head h reads K/U head h / (H / Hkv)
-  const int kvbh = b * a.Hkv + h / (a.H / a.Hkv);
-  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)bh * a.q_bh;
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)kvbh * a.k_bh;
-  const T* U = reinterpret_cast<const T*>(a.v) + (long long)kvbh * a.v_bh;
+  const int hk = h / (a.H / a.Hkv);
+  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)b * a.q_sb + (long long)h * a.q_sh;
+  const T* K = reinterpret_cast<const T*>(a.k) + (long long)b * a.k_sb + (long long)hk * a.k_sh;
+  const T* U = reinterpret_cast<const T*>(a.v) + (long long)b * a.v_sb + (long long)hk * a.v_sh;
+  const int qst = a.q_st, kst = a.k_st, vst = a.v_st;
 
   // Q^T fragments (B operand) for this lane's query column.
   typename MF::frag qf[NDI];
 #pragma unroll
   for (int i = 0; i < NDI; ++i) {
     const int d0 = i * MF::KPI + g * MF::KPL;
-    if (qcol < T_seq && d0 < D) qf[i] = MF::load(Q + (long long)qcol * D + d0);
+    if (qcol < T_seq && d0 < D) qf[i] = MF::load(Q + (long long)qcol * qst + d0);
     else qf[i] = typename MF::frag{};
   }
 
@@ -127,27 +128,28 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   // the per-thread offsets are fixed and the tile start goes in the scalar
   // offset.
   struct RegSet { uint4 kr[KCH], ur0[UCH], ur1[UCH]; };
-  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(K, (uint32_t)((size_t)T_seq * D * sizeof(T)));
-  const __amdgpu_buffer_rsrc_t rsu = make_rsrc(U, (uint32_t)((size_t)T_seq * D * sizeof(T)));
+  // a resource covers rows 0 .. T-1 exactly (the last one only up to D)
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(K, (uint32_t)(((size_t)(T_seq - 1) * kst + D) * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rsu = make_rsrc(U, (uint32_t)(((size_t)(T_seq - 1) * vst + D) * sizeof(T)));
   uint32_t koff[KCH], uoff[UCH];
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
     const int ch = tid + c * 256, row = ch / (DP / VEC), dc = (ch % (DP / VEC)) * VEC;
-    koff[c] = (ch < KTOT && dc < D) ? (uint32_t)((row * D + dc) * sizeof(T)) : OOB_OFFSET;
+    koff[c] = (ch < KTOT && dc < D) ? (uint32_t)((row * kst + dc) * sizeof(T)) : OOB_OFFSET;
   }
 #pragma unroll
   for (int c = 0; c < UCH; ++c) {
     const int ch = tid + c * 256, kp = (ch / (DP / VEC)) * 2, dc = (ch % (DP / VEC)) * VEC;
-    uoff[c] = (ch < UTOT && dc < D) ? (uint32_t)((kp * D + dc) * sizeof(T)) : OOB_OFFSET;
+    uoff[c] = (ch < UTOT && dc < D) ? (uint32_t)((kp * vst + dc) * sizeof(T)) : OOB_OFFSET;
   }
   auto gload = [&](RegSet& R, int kb) {
-    const uint32_t so = (uint32_t)(kb * D * sizeof(T));
+    const uint32_t sk = (uint32_t)(kb * kst * sizeof(T)), sv = (uint32_t)(kb * vst * sizeof(T));
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) R.kr[c] = buf_load16(rsk, koff[c], so);
+    for (int c = 0; c < KCH; ++c) R.kr[c] = buf_load16(rsk, koff[c], sk);
 #pragma unroll
     for (int c = 0; c < UCH; ++c) {
-      R.ur0[c] = buf_load16(rsu, uoff[c], so);
-      R.ur1[c] = buf_load16(rsu, uoff[c] == OOB_OFFSET ? OOB_OFFSET : uoff[c] + (uint32_t)(D * sizeof(T)), so);
+      R.ur0[c] = buf_load16(rsu, uoff[c], sv);
+      R.ur1[c] = buf_load16(rsu, uoff[c] == OOB_OFFSET ? OOB_OFFSET : uoff[c] + (uint32_t)(vst * sizeof(T)), sv);
     }
   };
   // K as is; U transposed to U^T [d][key], written as (key, key+1) pairs
@@ -301,9 +303,240 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, head width 64: key/value tiles of 64 rows reach LDS by direct-to-LDS
+// DMA in their natural [key][d] layout (128-byte rows) through a ring of
+// four stages; the value operand of O^T = U^T P^T (8 consecutive keys of one
+// column d per lane) is read with gfx950's transposing LDS read
+// ds_read_b64_tr_b16, so no register transpose is needed.  Within a group
+// of 16 lanes that instruction returns to lane 4a + b element b of the
+// 4-element rows addressed by lanes a, a + 4, a + 8 and a + 12: when lane j
+// addresses row kb + j / 4 at column d0 + 4 (j % 4), lane i receives rows
+// kb .. kb + 3 of column d0 + i.  The 16-byte chunks of a row are
+// XOR-swizzled by f(r) (bits 1..3 of the row, reordered) so that both the
+// key fragments (16 rows, one chunk) and the transposing reads (4 rows, 4
+// chunks) hit distinct bank groups.  Each wave computes the scores of tile
+// j + 1 while it takes the softmax of tile j.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kv_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+template <int NS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+attn_fwd_d64_kernel(AttnArgs a) {
+  constexpr int D = 64, BQ = 128, BKV = 64, TILE = BKV * 128;   // bytes of K (or U) per tile
+  typedef Mfma<bf16> MF;
+  __shared__ __align__(1024) char ring[NS][2][TILE];
+  typedef __attribute__((address_space(3))) char lch;
+  lch* const lring = (lch*)&ring[0][0][0];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // work items sorted longest first, rounds of 256 alternately reversed (see attn_fwd_kernel)
+  const int nbh = a.B * a.H;
+  const int nqt = (a.T_seq + BQ - 1) / BQ;
+  const int nitems = nqt * nbh;
+  int item = (int)blockIdx.x;
+  {
+    constexpr int ROUND = 256;
+    const int r = item / ROUND, base = r * ROUND;
+    if (r & 1) item = base + (min(ROUND, nitems - base) - 1 - (item - base));
+  }
+  const int qt = nqt - 1 - item / nbh, bh = item % nbh;
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / (a.H / a.Hkv);
+  const int T_seq = a.T_seq;
+  const int q0 = qt * BQ, qw0 = q0 + wave * 32, qcol = qw0 + (lane & 31);
+  const bf16* Q = reinterpret_cast<const bf16*>(a.q) + (long long)b * a.q_sb + (long long)h * a.q_sh;
+  const bf16* K = reinterpret_cast<const bf16*>(a.k) + (long long)b * a.k_sb + (long long)hk * a.k_sh;
+  const bf16* U = reinterpret_cast<const bf16*>(a.v) + (long long)b * a.v_sb + (long long)hk * a.v_sh;
+  const int kst = a.k_st, vst = a.v_st;
+
+  // Q^T fragments of this lane's query column (zero past the sequence)
+  MF::frag qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = qcol < T_seq ? MF::load(Q + (long long)qcol * a.q_st + ks * 16 + g * 8) : MF::frag{};
+
+  // DMA plan: a tile is 16 loads of 1 KB (8 rows each): K rows for loads 0-7,
+  // U rows for 8-15; wave w sends loads w, w + 4, w + 8, w + 12.  Lane l
+  // writes slot l % 8 of row 8 (i % 8) + l / 8, so it fetches chunk
+  // slot ^ f(row) of that row.  Rows past the sequence lie outside the
+  // resources and arrive as zeros.
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(K, (uint32_t)(((size_t)(T_seq - 1) * kst + D) * 2));
+  const __amdgpu_buffer_rsrc_t rsu = make_rsrc(U, (uint32_t)(((size_t)(T_seq - 1) * vst + D) * 2));
+  const int rA = 8 * wave + (lane >> 3), rB = rA + 32, sl = lane & 7;
+  const uint32_t koffA = (uint32_t)((rA * kst + (sl ^ kv_swz(rA)) * 8) * 2);
+  const uint32_t koffB = (uint32_t)((rB * kst + (sl ^ kv_swz(rB)) * 8) * 2);
+  const uint32_t voffA = (uint32_t)((rA * vst + (sl ^ kv_swz(rA)) * 8) * 2);
+  const uint32_t voffB = (uint32_t)((rB * vst + (sl ^ kv_swz(rB)) * 8) * 2);
+  auto dma_tile = [&](int t) {
+    lch* st = lring + (t % NS) * 2 * TILE;
+    const uint32_t sk = (uint32_t)(t * BKV * kst * 2), sv = (uint32_t)(t * BKV * vst * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + wave * 1024), 16, koffA, sk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + (wave + 4) * 1024), 16, koffB, sk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsu, (lds_void*)(st + TILE + wave * 1024), 16, voffA, sv, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsu, (lds_void*)(st + TILE + (wave + 4) * 1024), 16, voffB, sv, 0, 0);
+  };
+
+  const int kv_end = min(T_seq, q0 + BQ);
+  const int nt = (kv_end + BKV - 1) / BKV;                        // key tiles of this block
+  const int lw = qw0 < T_seq ? min(qw0 + 31, T_seq - 1) / BKV : -1;   // this wave's last tile
+
+  // score fragments: row block rb (keys 32 rb ..), k step ks, from the K half of a stage
+  auto kfrag = [&](const lch* st, int rb, int ks) {
+    const int r = rb * 32 + (lane & 31), c = ks * 2 + g;
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st + r * 128 + ((c ^ kv_swz(r)) << 4));
+  };
+  // U^T fragment for O^T rows d = 32 ob + lane % 32, keys 32 rb + 16 hh + 4 g + {0..3, 8..11}
+  auto vfrag = [&](const lch* st, int ob, int rb, int hh) {
+    const int G = lane >> 4, i = lane & 15, half = G & 1;
+    const int c = 4 * ob + 2 * half + ((i & 3) >> 1);
+    const int r0 = rb * 32 + hh * 16 + g * 4 + (i >> 2);
+    const lch* U0 = st + TILE;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(U0 + r0 * 128 + ((c ^ kv_swz(r0)) << 4) + ((i & 1) << 3)));
+    const int r1 = r0 + 8;
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(U0 + r1 * 128 + ((c ^ kv_swz(r1)) << 4) + ((i & 1) << 3)));
+    return __builtin_bit_cast(bf16x8, i16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+  };
+
+  f32x16 o[2], sa[2], sb[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+  // scores of the tile in stage st into sx
+  auto scores = [&](f32x16 (&sx)[2], const lch* st) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sx[rb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sx[rb] = MF::mma(kfrag(st, rb, ks), qf[ks], sx[rb]);
+    }
+  };
+  // tile j + 1 must be in LDS: wait for this wave's share (tile j + 2 may
+  // still be in flight), then the barrier publishes everyone's; every wave
+  // is then done with tile j - 1's stage, which takes tile j + NS - 1
+  auto sync = [&](int j) {
+    if (j + 2 < nt) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+    __syncthreads();
+    if (j + NS - 1 < nt) dma_tile(j + NS - 1);
+  };
+  // tile j: s holds its scores; the next tile's go to sn
+  auto step = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+    if (j > lw) return;                   // every key of tile j is in this wave's future
+    const lch* cur = lring + (j % NS) * 2 * TILE;
+    const int kb = j * BKV;
+    if (kb + BKV - 1 > qw0) {             // causal mask on the diagonal tile(s), in place
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[rb][r] = kb + rb * 32 + acc_row(r, lane) > qcol ? -INFINITY : s[rb][r];
+    }
+    // the next tile's scores: independent of the softmax below, so the MFMAs overlap it
+    if (j + 1 <= lw) scores(sn, lring + ((j + 1) % NS) * 2 * TILE);
+    // online softmax of tile j; the exponent reference moves only by > 8 (log2 units)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
+    {
+      // lanes l and l ^ 32 hold the other keys of the same query: both
+      // halves of the swap carry the pair, in every lane
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sc;
+    }
+    const float m_new = mx > m_run + 8.f ? mx : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+    bf16x8 pf[2][2];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[rb][8 * hh + 2 * e], sc, -m_new));
+          const float p1 = fast_exp2(fmaf(s[rb][8 * hh + 2 * e + 1], sc, -m_new));
+          w[e] = pack_bf16x2(p0, p1);
+          // the row sum of the probabilities as they enter the product (bf16)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, psum, false);
+        }
+        pf[rb][hh] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ob][r] *= alpha;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob) o[ob] = MF::mma(vfrag(cur, ob, rb, hh), pf[rb][hh], o[ob]);
+  };
+
+  // prologue: tiles 0 .. NS - 2 in flight; scores of tile 0
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nt) dma_tile(t);
+  if (nt > 2) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 8);        // tile 0 landed (tiles 1, 2 in flight)
+  else if (nt > 1) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 4);
+  else __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  __syncthreads();
+  if (lw >= 0) scores(sa, lring);
+  // two tiles per pass, so the two score sets trade places without copies
+  for (int j = 0; j < nt; j += 2) {
+    sync(j);
+    step(j, sa, sb);
+    if (j + 1 < nt) {
+      sync(j + 1);
+      step(j + 1, sb, sa);
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (a.lse2 != nullptr && qcol < T_seq && g == 0) a.lse2[(long long)bh * T_seq + qcol] = m_run + __log2f(l_tot);
+  if (qcol < T_seq) {
+    bf16* orow = reinterpret_cast<bf16*>(a.o) + ((long long)b * T_seq + qcol) * a.o_ld + h * D;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = ob * 32 + q * 8 + g * 4;
+        *reinterpret_cast<uint2*>(orow + d) =
+            make_uint2(pack_bf16x2(o[ob][4 * q] * inv, o[ob][4 * q + 1] * inv),
+                       pack_bf16x2(o[ob][4 * q + 2] * inv, o[ob][4 * q + 3] * inv));
+      }
+  }
+}
+
 template <typename T>
 static hipError_t attn_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(((a.T_seq + 127) / 128) * a.B * a.H), block(256);
+  if constexpr (sizeof(T) == 2) {
+    // 16-byte aligned rows (DMA of whole 128-byte rows) and no distance bias
+    const bool rows16 = a.k_st % 8 == 0 && a.v_st % 8 == 0 && a.q_st % 8 == 0 && a.o_ld % 4 == 0 &&
+                        ((uintptr_t)a.k & 15) == 0 && ((uintptr_t)a.v & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
+    if (a.D == 64 && !a.alibi && rows16) {
+      hipLaunchKernelGGL((attn_fwd_d64_kernel<4>), grid, block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.D <= 32)
     hipLaunchKernelGGL((attn_fwd_kernel<T, 32, 64>), grid, block, 0, st, a);
   else if (a.D <= 64)

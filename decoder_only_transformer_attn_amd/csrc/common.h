@@ -64,6 +64,34 @@ template <> struct Mfma<float> {
   static __device__ __forceinline__ frag load(const float* p) { return *p; }
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+// LDS byte and 16-byte types: stage pointers carry the LDS address space in
+// their type, so fragment reads are ds_read instructions by construction and
+// never depend on the compiler inferring where a generic pointer points.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// The LDS view of a __shared__ array.
+template <typename T> __device__ __forceinline__ lds_char* as_lds(T* p) { return (lds_char*)p; }
+
+// 16-, 8- and 4-byte LDS accesses through LDS-typed pointers.
+__device__ __forceinline__ uint4 lds_ld16(const lds_char* p) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p));
+}
+__device__ __forceinline__ bf16x8 lds_frag(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+__device__ __forceinline__ uint2 lds_ld8(const lds_char* p) {
+  return __builtin_bit_cast(uint2, *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(p));
+}
+__device__ __forceinline__ void lds_st8(lds_char* p, uint2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(p) = __builtin_bit_cast(u32x2_t, v);
+}
+__device__ __forceinline__ void lds_st4(lds_char* p, uint32_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(p) = v;
+}
+
 // Row index (within a 32x32 tile) of accumulator register r for lane l.
 // Buffer resource over [base, base + bytes): loads beyond `bytes` return zero,
 // which handles the tails of a tile without branches.

@@ -187,10 +187,16 @@ Plan plan(const gpt_config* c, int B, int T, bool decode) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   p.x = take(M * C * 4);
   p.a = take(M * C * es);
-  p.q = take(M * C * es);
   const size_t KV = (size_t)kv_heads(c) * (C / c->n_head);
-  p.k = decode ? 0 : take(M * KV * es);
-  p.v = decode ? 0 : take(M * KV * es);
+  if (decode) {
+    p.q = take(M * C * es);
+  } else {
+    // one region [M, C + 2 KV]: token-major rows of the fused Q|K|U product
+    // (GPT-2 forward), or head-major Q, K and U one after another
+    p.q = take(M * (C + 2 * KV) * es);
+    p.k = p.q + M * C * es;
+    p.v = p.k + M * KV * es;
+  }
   p.o = take(M * C * es);
   p.h = take(M * F * es);
   p.pmax = take(head_rows * p.ntiles * 4);
@@ -302,9 +308,7 @@ int run_blocks_llama(const Pass& s) {
       GPT_TRY(launch_attention_decode(dt, da, s.st));
     } else {
       AttnArgs aa{};
-      aa.q = q; aa.q_bh = (long long)T * D;
-      aa.k = kbuf; aa.k_bh = kv_bh;
-      aa.v = vbuf; aa.v_bh = kv_bh;
+      attn_headmajor(aa, q, (long long)T * D, kbuf, vbuf, kv_bh, H, Hkv, D);
       aa.o = o; aa.o_ld = C;
       aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = Hkv; aa.alibi = alibi;
       aa.scale_log2 = scale_log2;
@@ -377,17 +381,25 @@ int run_blocks(const Pass& s) {
     void* kbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.k) : static_cast<char*>(s.kc) + l * cache_layer * es;
     void* vbuf = s.mode == FORWARD ? at<char>(s.ws, s.pl.v) : static_cast<char*>(s.vc) + l * cache_layer * es;
     const long long kv_bh = s.mode == FORWARD ? (long long)T * D : (long long)s.Tmax * D;
-    QKVArgs qa{};
-    qa.A = a; qa.W = P.at(w.attn_w); qa.bias = P.at(w.attn_b);
-    qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
-    qa.q = q; qa.q_bh = (long long)T * D;
-    qa.k = kbuf; qa.k_bh = kv_bh;
-    qa.v = vbuf; qa.v_bh = kv_bh;
-    qa.pos = s.mode == STEP ? s.pos : nullptr;
-    qa.Tk = s.mode == FORWARD ? T : s.Tmax;
-    qa.Hkv = H; qa.rope = nullptr;
+    // forward: c_attn writes token-major rows [M, 3C] (Q | K | U, head h at
+    // columns h D of each third), which the attention reads in place; the
+    // cache passes scatter K and U into the cache layout instead
+    const bool rows = s.mode == FORWARD;
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
-    GPT_TRY(launch_qkv(dt, qa, s.st, sk));
+    if (rows) {
+      GPT_TRY(launch_linear(dt, a, C, P.at(w.attn_w), C, P.at(w.attn_b), M, 3 * C, C, q, 3 * C, 0, 0, s.st, sk));
+    } else {
+      QKVArgs qa{};
+      qa.A = a; qa.W = P.at(w.attn_w); qa.bias = P.at(w.attn_b);
+      qa.M = M; qa.C = C; qa.H = H; qa.D = D; qa.T_seq = T;
+      qa.q = q; qa.q_bh = (long long)T * D;
+      qa.k = kbuf; qa.k_bh = kv_bh;
+      qa.v = vbuf; qa.v_bh = kv_bh;
+      qa.pos = s.mode == STEP ? s.pos : nullptr;
+      qa.Tk = s.Tmax;
+      qa.Hkv = H; qa.rope = nullptr;
+      GPT_TRY(launch_qkv(dt, qa, s.st, sk));
+    }
     GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
     GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, true));
     if (s.mode == STEP) {
@@ -397,9 +409,15 @@ int run_blocks(const Pass& s) {
       GPT_TRY(launch_attention_decode(dt, da, s.st));
     } else {
       AttnArgs aa{};
-      aa.q = q; aa.q_bh = (long long)T * D;
-      aa.k = kbuf; aa.k_bh = kv_bh;
-      aa.v = vbuf; aa.v_bh = kv_bh;
+      if (rows) {
+        const long long ld = 3LL * C;
+        char* qkv = static_cast<char*>(q);
+        aa.q = qkv;              aa.q_sb = T * ld; aa.q_sh = D; aa.q_st = (int)ld;
+        aa.k = qkv + C * es;     aa.k_sb = T * ld; aa.k_sh = D; aa.k_st = (int)ld;
+        aa.v = qkv + 2 * C * es; aa.v_sb = T * ld; aa.v_sh = D; aa.v_st = (int)ld;
+      } else {
+        attn_headmajor(aa, q, (long long)T * D, kbuf, vbuf, kv_bh, H, H, D);
+      }
       aa.o = o; aa.o_ld = C;
       aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
       aa.scale_log2 = scale_log2;
@@ -983,8 +1001,8 @@ int gpt_block_backward(const gpt_config* cfg, const void* params, int layer, int
   qa.v = W(pl.v); qa.v_bh = (long long)T * D; qa.pos = nullptr; qa.Tk = T; qa.Hkv = H; qa.rope = nullptr;
   GPT_TRY(launch_qkv(dt, qa, st, nullptr));
   AttnArgs aa{};
-  aa.q = W(pl.q); aa.q_bh = (long long)T * D; aa.k = W(pl.k); aa.k_bh = (long long)T * D;
-  aa.v = W(pl.v); aa.v_bh = (long long)T * D; aa.o = W(pl.o); aa.o_ld = C;
+  attn_headmajor(aa, W(pl.q), (long long)T * D, W(pl.k), W(pl.v), (long long)T * D, H, H, D);
+  aa.o = W(pl.o); aa.o_ld = C;
   aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   aa.lse2 = Wf(pl.alse);
@@ -1075,9 +1093,7 @@ int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, con
   if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
   const int C = cfg->n_embd, H = cfg->n_head, D = C / H;
   AttnArgs aa{};
-  aa.q = q; aa.q_bh = (long long)T * D;
-  aa.k = k; aa.k_bh = (long long)T * D;
-  aa.v = u; aa.v_bh = (long long)T * D;
+  attn_headmajor(aa, q, (long long)T * D, k, u, (long long)T * D, cfg->n_head, cfg->n_head, cfg->n_embd / cfg->n_head);
   aa.o = out; aa.o_ld = C;
   aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));

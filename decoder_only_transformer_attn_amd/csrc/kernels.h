@@ -56,9 +56,13 @@ struct DecAttnArgs {
 };
 
 struct AttnArgs {
-  const void* q; long long q_bh;       // Q [B,H,T,D]
-  const void* k; long long k_bh;       // K [B,Hkv,*,D]
-  const void* v; long long v_bh;       // U [B,Hkv,*,D]
+  // element (b, h, t, d) of Q at q[b q_sb + h q_sh + t q_st + d]; K and U
+  // likewise with their head hk = h / (H / Hkv).  Head-major [B,H,T,D]:
+  // (sb, sh, st) = (H T D, T D, D); token-major rows of the fused QKV product
+  // [B*T, C + 2 Hkv D]: (T (C + 2 Hkv D), D, C + 2 Hkv D).
+  const void* q; long long q_sb, q_sh; int q_st;
+  const void* k; long long k_sb, k_sh; int k_st;
+  const void* v; long long v_sb, v_sh; int v_st;
   void* o; int o_ld;                   // O [B*T, o_ld], head h at columns [hD, hD+D)
   int B, H, T_seq, D;
   int Hkv;                             // K/U heads; query head h reads K/U head h / (H / Hkv)
@@ -67,6 +71,14 @@ struct AttnArgs {
   float* lse2;                         // optional [B*H][T]: log2 of each row's softmax denominator
                                        // (the log-sum-exp of the scaled scores, in log2 units)
 };
+
+// Q, K and U stored head-major: element (b, h, t, d) at base + (b Hx + h) bh + t D + d.
+inline void attn_headmajor(AttnArgs& a, const void* q, long long q_bh, const void* k, const void* v, long long kv_bh,
+                           int H, int Hkv, int D) {
+  a.q = q; a.q_sh = q_bh; a.q_sb = q_bh * H; a.q_st = D;
+  a.k = k; a.k_sh = kv_bh; a.k_sb = kv_bh * Hkv; a.k_st = D;
+  a.v = v; a.v_sh = kv_bh; a.v_sb = kv_bh * Hkv; a.v_st = D;
+}
 
 // Split-K scratch of the skinny (M <= 64) bf16 products: per-column-tile
 // arrival counters, which must be zero when a product starts and are zero
