@@ -69,6 +69,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // their type, so fragment reads are ds_read instructions by construction and
 // never depend on the compiler inferring where a generic pointer points.
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) int lds_int;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 

@@ -277,57 +277,45 @@ static hipError_t run_skinny(const bf16* A, int lda, const bf16* W, int ldw, int
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Tied head + cross-entropy partials.
-//   logits (optional)  : z[m, n] in T
-//   part_max/part_sum  : [M, ntiles] per-row max and sum exp(z - max) over
-//                        this block's N range (n < N only)
-//   tgt                : z[m, y[m]] from the block whose range holds y[m]
-// y[m] = targets[m] if targets, else idx[m+1] inside a sequence and -1 at
-// the last position ("第 25 章 从小 GPT 到 GPT-2" §25.7: predict the next token).
-// ---------------------------------------------------------------------------
-struct HeadArgs {
-  void* logits;
-  long long ld_logits;
-  float* part_max;
-  float* part_sum;
-  float* tgt;
-  int32_t* part_idx;      // argmax mode when non-null
-  int ntiles;
-  const int32_t* targets;
-  const int32_t* idx;
-  int T_seq;
-};
-
-// (value, index) order of the greedy choice: larger value, then lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
-
-__device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
-  if (ha.part_idx) return -1;
-  if (ha.targets) return ha.targets[m];
-  return ((m % ha.T_seq) < ha.T_seq - 1) ? ha.idx[m + 1] : -1;
-}
-
 // bf16 tied head computed transposed, Z^T = E . A^T: the MFMA rows are vocab
 // entries and the columns are tokens, so every lane owns whole tokens.  The
 // softmax partials of a token over this block's vocab entries are then a
 // reduction over the lane's own registers, one exchange with the lane holding
 // the other half of the rows (l ^ 32), and a combine over the waves along the
-// vocab axis (through the first stage, free after the main loop).  The target
-// ids are read before the main loop.  Logits are stored straight from the
-// accumulators (staging the tile in LDS for row-contiguous stores measured
-// slower).
-template <int K, int BM, int BN, int WM, int WN>   // BM: vocab, BN: tokens
+// vocab axis.  The target ids are read before the main loop.
+//
+// LDS after the main loop (the stages are free): every wave owns a slot of
+// SW bytes where it gathers one 32-token column of its logits at a time as
+// [token][vocab] rows (WM entries, a pitch of WM * 2 + 8 bytes, so the quad
+// stores of 32 consecutive tokens meet no bank twice) and writes them out as
+// 16-byte pieces of whole row spans: in the accumulators a lane holds 4
+// consecutive vocab entries of one token, so direct stores would scatter
+// 8 bytes over 32 token rows per instruction.  (The rows are only 2-byte
+// aligned, V being odd; the 16-byte stores are unaligned.)  Slots fill the
+// stages in order; the per-wave partials follow the last slot.
+template <int BM, int BN, int WM, int WN, int NST, int BK>
+struct HeadPlan {
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
+  static constexpr int PITCH = WM * 2 + 8, SW = 32 * PITCH, WPS = D::STAGE / SW;
+  static constexpr int PART = D::NWM * BN * 3 * 4;          // float max, sum; int argmax
+  static constexpr int PST = D::NW / WPS, POFF = (D::NW % WPS) * SW;
+  static_assert(WPS >= 1 && PST < NST && POFF + PART <= D::STAGE, "epilogue LDS plan must fit the stages");
+  static_assert(WM % 8 == 0 && (32 * (WM / 8)) % 64 == 0, "whole 16-byte units per row, whole rounds per wave");
+};
+
+template <int K, int BM, int BN, int WM, int WN, int NST, int BK>   // BM: vocab, BN: tokens
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN, 2, 64>())))
+__attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN, NST, BK>())))
 head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, int V, int Mtok, HeadArgs ha) {
-  typedef DmaCfg<BM, BN, WM, WN, 2, 64> D;                 // two 64-deep stages
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> D;
+  typedef HeadPlan<BM, BN, WM, WN, NST, BK> P;
   __shared__ __align__(1024) char s0[D::STAGE];
   __shared__ __align__(1024) char s1[D::STAGE];
-  // per-wave token partials, in the first stage once the main loop is done
-  static_assert(D::NWM * BN * 3 * 4 <= D::STAGE, "partials must fit in a stage");
-  float (*red)[BN][2] = reinterpret_cast<float (*)[BN][2]>(s0);
-  int (*redi)[BN] = reinterpret_cast<int (*)[BN]>(s0 + D::NWM * BN * 2 * 4);
+  __shared__ __align__(1024) char s2[NST > 2 ? D::STAGE : 16];
+  __shared__ __align__(1024) char s3[NST > 3 ? D::STAGE : 16];
+  static_assert(NST <= 4, "stage count");
+  const Stages stages{{as_lds(s0), as_lds(s1), NST > 2 ? as_lds(s2) : as_lds(s0), NST > 3 ? as_lds(s3) : as_lds(s0),
+                       as_lds(s0), as_lds(s0), as_lds(s0), as_lds(s0)}};
   const int num_v = (V + BM - 1) / BM, num_t = (Mtok + BN - 1) / BN;
   int tt, vt;
   tile_of(blockIdx.x, gridDim.x, num_t, num_v, tt, vt);   // groups of token tiles sweep the vocab
@@ -346,17 +334,28 @@ head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, i
   }
 
   f32x16 acc[D::TM][D::TN];
-  const Stages stages{{as_lds(s0), as_lds(s1), as_lds(s1), as_lds(s1), as_lds(s1), as_lds(s1), as_lds(s1),
-                       as_lds(s1)}};
-  dma_mainloop<BM, BN, WM, WN, K, 2, 64>(wte, K, act, K, K, V, Mtok, v0, t0, stages, acc);
+  dma_mainloop<BM, BN, WM, WN, K, NST, BK>(wte, K, act, K, K, V, Mtok, v0, t0, stages, acc);
 
+  // (stage k by selects: indexing the pointer array with a run-time value
+  // would place the array itself in memory)
+  auto stage = [&](int k) {
+    if constexpr (NST == 2) return k == 0 ? as_lds(s0) : as_lds(s1);
+    else if constexpr (NST == 3) return k == 0 ? as_lds(s0) : k == 1 ? as_lds(s1) : as_lds(s2);
+    else return k == 0 ? as_lds(s0) : k == 1 ? as_lds(s1) : k == 2 ? as_lds(s2) : as_lds(s3);
+  };
+  lds_char* const part = stage(P::PST) + P::POFF;
+  lds_float* const red = reinterpret_cast<lds_float*>(part);                        // [NWM][BN][2]
+  lds_int* const redi = reinterpret_cast<lds_int*>(part + D::NWM * BN * 2 * 4);   // [NWM][BN]
+  lds_char* const wl = stage(wave / P::WPS) + (wave % P::WPS) * P::SW;
   const bool amax = ha.part_idx != nullptr;
-  if (amax) {
-    // greedy choice: per token, the largest logit and its lowest vocab index.
-    // Register order i, r visits this lane's vocab rows in increasing order.
+  constexpr float LOG2E = 1.4426950408889634f;
 #pragma unroll
-    for (int j = 0; j < D::TN; ++j) {
-      const int tl = wn * WN + j * 32 + (lane & 31);
+  for (int j = 0; j < D::TN; ++j) {
+    const int tl = wn * WN + j * 32 + (lane & 31);
+    const int m = t0 + tl;
+    if (amax) {
+      // greedy choice: the largest logit and its lowest vocab index.  Register
+      // order i, r visits this lane's vocab rows in increasing order.
       float mx = -INFINITY;
       int mi = 0x7fffffff;
 #pragma unroll
@@ -369,98 +368,87 @@ head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, i
       const float v2 = __shfl_xor(mx, 32, 64);
       const int i2 = __shfl_xor(mi, 32, 64);
       if (better(v2, i2, mx, mi)) { mx = v2; mi = i2; }
-      if (g == 0) { red[wm][tl][0] = mx; redi[wm][tl] = mi; }
-    }
-  }
-  // softmax partials and target logit, per token
-#pragma unroll
-  for (int j = 0; j < D::TN; ++j) {
-    if (amax) break;
-    const int tl = wn * WN + j * 32 + (lane & 31);
-    const int m = t0 + tl;
-    float mx = -INFINITY, sum = 0.f;
-    constexpr float LOG2E = 1.4426950408889634f;
-    if (full) {
-#pragma unroll
-      for (int i = 0; i < D::TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mxl = mx * LOG2E;
-#pragma unroll
-      for (int i = 0; i < D::TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[i][j][r], LOG2E, -mxl));
+      if (g == 0) { red[(wm * BN + tl) * 2] = mx; redi[wm * BN + tl] = mi; }
     } else {
+      // softmax partials and target logit
+      float mx = -INFINITY, sum = 0.f;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < D::TM; ++i)
+        for (int i = 0; i < D::TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vw0 + i * 32 + acc_row(r, lane) < V) mx = fmaxf(mx, acc[i][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (mx > -INFINITY) {
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mxl = mx * LOG2E;
 #pragma unroll
         for (int i = 0; i < D::TM; ++i)
 #pragma unroll
+          for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[i][j][r], LOG2E, -mxl));
+      } else {
+#pragma unroll
+        for (int i = 0; i < D::TM; ++i)
+#pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (vw0 + i * 32 + acc_row(r, lane) < V) sum += fast_exp2(fmaf(acc[i][j][r], LOG2E, -mxl));
+            if (vw0 + i * 32 + acc_row(r, lane) < V) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (mx > -INFINITY) {
+          const float mxl = mx * LOG2E;
+#pragma unroll
+          for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (vw0 + i * 32 + acc_row(r, lane) < V) sum += fast_exp2(fmaf(acc[i][j][r], LOG2E, -mxl));
+        }
+      }
+      sum += __shfl_xor(sum, 32, 64);
+      if (g == 0) { red[(wm * BN + tl) * 2] = mx; red[(wm * BN + tl) * 2 + 1] = sum; }
+      const int y = ytok[j];
+      if (m < Mtok && y >= vw0 && y < vw0 + WM) {
+#pragma unroll
+        for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vw0 + i * 32 + acc_row(r, lane) == y) ha.tgt[m] = acc[i][j][r];
       }
     }
-    sum += __shfl_xor(sum, 32, 64);
-    if (g == 0) { red[wm][tl][0] = mx; red[wm][tl][1] = sum; }
-    const int y = ytok[j];
-    if (m < Mtok && y >= vw0 && y < vw0 + WM) {
-#pragma unroll
-      for (int i = 0; i < D::TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vw0 + i * 32 + acc_row(r, lane) == y) ha.tgt[m] = acc[i][j][r];
-    }
-  }
-
-  // bf16 logits, gathered per wave in LDS as [token][vocab] rows (WM entries,
-  // a pitch of WM * 2 + 8 bytes: the quad stores of 32 consecutive tokens
-  // meet no bank twice) and written as 16-byte pieces of whole row spans: in
-  // the accumulators a lane holds 4 consecutive vocab entries of one token,
-  // so direct stores would scatter 8 bytes over 32 token rows per
-  // instruction.  (The rows are only 2-byte aligned, V being odd; the
-  // 16-byte stores are unaligned.)  Waves 0-2 use the second stage, wave 3
-  // the first one past the partials.
-  if (ha.logits) {   // uniform
-    constexpr int PITCH = WM * 2 + 8, NU = WM / 8;
-    static_assert(D::NW == 4 && WM % 8 == 0, "four waves, whole 16-byte units per row");
-    static_assert(3 * WN * PITCH <= D::STAGE && 4096 + WN * PITCH <= D::STAGE, "staging must fit the stages");
-    static_assert(D::NWM * BN * 3 * 4 <= 4096, "the partials end before wave 3's staging");
-    lds_char* const wl = wave < 3 ? as_lds(s1) + wave * (WN * PITCH) : as_lds(s0) + 4096;
-#pragma unroll
-    for (int j = 0; j < D::TN; ++j) {
-      const int tl = j * 32 + (lane & 31);
+    if (ha.logits) {   // uniform: this column's bf16 logits through the wave's slot
+      constexpr int NU = WM / 8;
 #pragma unroll
       for (int i = 0; i < D::TM; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int vl = i * 32 + q * 8 + g * 4;
-          lds_st8(wl + tl * PITCH + vl * 2, make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                                       pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])));
+          lds_st8(wl + (lane & 31) * P::PITCH + vl * 2,
+                  make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                             pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])));
         }
-    }
-    __syncthreads();   // (block-uniform) every wave has staged its tile; each reads back its own
-    bf16* const L = reinterpret_cast<bf16*>(ha.logits);
-    for (int u = lane; u < WN * NU; u += 64) {
-      const int tl = u / NU, k = u - tl * NU;
-      const int m = t0 + wn * WN + tl, v = vw0 + k * 8;
-      if (m >= Mtok || v >= V) continue;
-      const uint2 a = lds_ld8(wl + tl * PITCH + k * 16);
-      const uint2 b = lds_ld8(wl + tl * PITCH + k * 16 + 8);
-      bf16* const p = L + (long long)m * ha.ld_logits + v;
-      if (v + 8 <= V) {
-        const uint4 w4 = make_uint4(a.x, a.y, b.x, b.y);
-        __builtin_memcpy(p, &w4, 16);
-      } else {
-        const uint32_t h[4] = {a.x, a.y, b.x, b.y};
-        for (int e = 0; v + e < V; ++e) p[e] = bf16(h[e >> 1] >> (16 * (e & 1)));
+      // the slot is this wave's alone: LDS operations of one wave take effect
+      // in issue order, so a wave-level fence orders the reads after the stores
+      // (and the next column's stores after these reads)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      bf16* const L = reinterpret_cast<bf16*>(ha.logits);
+#pragma unroll
+      for (int u0 = 0; u0 < 32 * NU; u0 += 64) {
+        const int u = u0 + lane, r = u / NU, k = u - r * NU;
+        const int mr = t0 + wn * WN + j * 32 + r, v = vw0 + k * 8;
+        const uint2 a = lds_ld8(wl + r * P::PITCH + k * 16);
+        const uint2 b = lds_ld8(wl + r * P::PITCH + k * 16 + 8);
+        if (mr >= Mtok || v >= V) continue;
+        bf16* const p = L + (long long)mr * ha.ld_logits + v;
+        if (v + 8 <= V) {
+          const uint4 w4 = make_uint4(a.x, a.y, b.x, b.y);
+          __builtin_memcpy(p, &w4, 16);
+        } else {
+          for (int e = 0; v + e < V; ++e) {
+            const uint32_t h = e < 2 ? a.x : e < 4 ? a.y : e < 6 ? b.x : b.y;
+            p[e] = bf16(h >> (16 * (e & 1)));
+          }
+        }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
   __syncthreads();
@@ -468,23 +456,26 @@ head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, i
     const int m = t0 + tl;
     if (m >= Mtok) continue;
     if (amax) {
-      float mx = red[0][tl][0];
-      int mi = redi[0][tl];
+      float mx = red[tl * 2];
+      int mi = redi[tl];
 #pragma unroll
       for (int w = 1; w < D::NWM; ++w)
-        if (better(red[w][tl][0], redi[w][tl], mx, mi)) { mx = red[w][tl][0]; mi = redi[w][tl]; }
+        if (better(red[(w * BN + tl) * 2], redi[w * BN + tl], mx, mi)) {
+          mx = red[(w * BN + tl) * 2];
+          mi = redi[w * BN + tl];
+        }
       ha.part_max[(long long)m * ha.ntiles + vt] = mx;
       ha.part_idx[(long long)m * ha.ntiles + vt] = mi;
       continue;
     }
-    float M_ = red[0][tl][0];
+    float M_ = red[tl * 2];
 #pragma unroll
-    for (int w = 1; w < D::NWM; ++w) M_ = fmaxf(M_, red[w][tl][0]);
+    for (int w = 1; w < D::NWM; ++w) M_ = fmaxf(M_, red[(w * BN + tl) * 2]);
     float S = 0.f;
 #pragma unroll
     for (int w = 0; w < D::NWM; ++w) {
-      const float mw = red[w][tl][0];
-      if (mw > -INFINITY) S += red[w][tl][1] * fast_exp2((mw - M_) * 1.4426950408889634f);
+      const float mw = red[(w * BN + tl) * 2];
+      if (mw > -INFINITY) S += red[(w * BN + tl) * 2 + 1] * fast_exp2((mw - M_) * LOG2E);
     }
     ha.part_max[(long long)m * ha.ntiles + vt] = M_;
     ha.part_sum[(long long)m * ha.ntiles + vt] = S;
@@ -1060,14 +1051,27 @@ hipError_t launch_gemm_f32_splitk(int dtype, const void* A, int lda, const void*
                              st);
 }
 
-// bf16 head tile for C = 768 (vocab x tokens, per-wave vocab x tokens)
-constexpr int HEAD_BM = 192, HEAD_BN = 128, HEAD_WM = 96, HEAD_WN = 64;
+// bf16 heads for C = 768: 256 (vocab) x 256 (token) blocks of eight 128 x 64
+// waves for many tokens (128 flops per byte brought into LDS), 192 x 128
+// blocks of four 96 x 64 waves in argmax mode and for few tokens (decode).
+constexpr int HEAD_BIG_MIN_TOKENS = 2048;
+static bool head_big(int dtype, int M, int C, bool argmax) {
+  return dtype != 0 && C == 768 && !argmax && M >= HEAD_BIG_MIN_TOKENS;
+}
 
 int head_ntiles(int dtype, int M, int V, int C, bool argmax) {
-  (void)M;
-  (void)argmax;
-  const int bn = dtype == 0 ? 64 : (C == 768 ? HEAD_BM : 256);
+  const int bn = dtype == 0 ? 64 : (C == 768 ? (head_big(dtype, M, C, argmax) ? 256 : 192) : 256);
   return (V + bn - 1) / bn;
+}
+
+template <int BM, int BN, int WM, int WN, int NST, int BK>
+static hipError_t run_head_dma(const bf16* wte, const bf16* A, int V, int M, HeadArgs ha, hipStream_t st) {
+  typedef DmaCfg<BM, BN, WM, WN, NST, BK> HD;
+  ha.ntiles = (V + BM - 1) / BM;
+  const int blocks = ((M + BN - 1) / BN) * ha.ntiles;
+  hipLaunchKernelGGL((head_ce_dma_kernel<768, BM, BN, WM, WN, NST, BK>), dim3(blocks), dim3(HD::NT), 0, st, wte, A,
+                     V, M, ha);
+  return hipGetLastError();
 }
 
 hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int V, int C, void* logits,
@@ -1091,12 +1095,9 @@ hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int 
     ha.ntiles = (V + BN - 1) / BN;
     const int blocks = ((M + BM - 1) / BM) * ha.ntiles;
     if (C == 768) {
-      typedef DmaCfg<HEAD_BM, HEAD_BN, HEAD_WM, HEAD_WN, 2, 64> HD;
-      ha.ntiles = (V + HEAD_BM - 1) / HEAD_BM;
-      const int hblocks = ((M + HEAD_BN - 1) / HEAD_BN) * ha.ntiles;
-      hipLaunchKernelGGL((head_ce_dma_kernel<768, HEAD_BM, HEAD_BN, HEAD_WM, HEAD_WN>), dim3(hblocks), dim3(HD::NT), 0,
-                         st, (const bf16*)wte, (const bf16*)A, V, M, ha);
-      return hipGetLastError();
+      if (head_big(dtype, M, C, part_idx != nullptr))
+        return run_head_dma<256, 256, 128, 64, 2, 64>((const bf16*)wte, (const bf16*)A, V, M, ha, st);
+      return run_head_dma<192, 128, 96, 64, 2, 64>((const bf16*)wte, (const bf16*)A, V, M, ha, st);
     }
     if (C % 64 == 0)
       hipLaunchKernelGGL((head_ce_kernel<bf16, BM, BN, 64, 128, 64, false>), dim3(blocks),

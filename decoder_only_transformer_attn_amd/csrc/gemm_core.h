@@ -943,4 +943,35 @@ gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tied head + cross-entropy partials (shared by the head kernels).
+//   logits (optional)  : z[m, n] in T
+//   part_max/part_sum  : [M, ntiles] per-row max and sum exp(z - max) over
+//                        one vocabulary range (n < N only)
+//   tgt                : z[m, y[m]] from the range that holds y[m]
+// y[m] = targets[m] if targets, else idx[m+1] inside a sequence and -1 at
+// the last position ("第 25 章 从小 GPT 到 GPT-2" §25.7: predict the next token).
+// ---------------------------------------------------------------------------
+struct HeadArgs {
+  void* logits;
+  long long ld_logits;
+  float* part_max;
+  float* part_sum;
+  float* tgt;
+  int32_t* part_idx;      // argmax mode when non-null
+  int ntiles;
+  const int32_t* targets;
+  const int32_t* idx;
+  int T_seq;
+};
+
+// (value, index) order of the greedy choice: larger value, then lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+__device__ __forceinline__ int head_target(const HeadArgs& ha, int m) {
+  if (ha.part_idx) return -1;
+  if (ha.targets) return ha.targets[m];
+  return ((m % ha.T_seq) < ha.T_seq - 1) ? ha.idx[m + 1] : -1;
+}
+
 }  // namespace gptmi
