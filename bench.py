@@ -230,6 +230,7 @@ def bench_forward(args, w):
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(head_ms, 4), "flops_per_launch": head_flops},
     }
+    out["kernels"] = kernel_rooflines(cfg, B, T, dev_params, idx, fwd, stream)
     if args.workload == 3 and args.extra_legs:
         out["head_backward"] = bench_head_backward(cfg, B, T, dev_params, idx, stream)
         out["train_grad"] = bench_train_grad(cfg, B, T, dev_params, idx, stream)
@@ -237,6 +238,56 @@ def bench_forward(args, w):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_forward(cfg, params, ids, args.cpu_seqs)
     return out
+
+
+def kernel_rooflines(cfg, B, T, dev_params, idx, fwd, stream, reps=5):
+    """Each kernel class of the last block, timed with HIP events around its
+    launch inside a whole forward (lib.forward_timed), against its roofline:
+    the GEMMs against bf16 MFMA peak with 2MNK flops; attention and ln_2
+    against HBM with their algorithmic bytes (attention: Q, K, U read once
+    and O written, bf16; LayerNorm: the fp32 residual rows read and the bf16
+    normalised rows written), and attention's flops beside them."""
+    from decoder_only_transformer_attn_amd import lib
+    if getattr(cfg, "arch", 0) != 0:
+        return None
+    M, C, F, H = B * T, cfg.n_embd, cfg.n_ff, cfg.n_head
+    D = C // H
+    attn_flops = 4 * D * B * H * T * (T + 1) // 2
+    spec = {
+        "qkv": ("mfma", 2 * M * 3 * C * C, None),
+        "attn": ("hbm", attn_flops, 2 * (3 * M * C + M * C)),
+        "proj": ("mfma", 2 * M * C * C, None),
+        "ln": ("hbm", None, M * C * 4 + M * C * 2),
+        "fc": ("mfma", 2 * M * F * C, None),
+        "fcproj": ("mfma", 2 * M * C * F, None),
+    }
+    out = {}
+    ev = Events(2 * reps)
+    for name, (bound, flops, nbytes) in spec.items():
+        for r in range(reps):
+            lib.forward_timed(cfg, dev_params, idx, None, fwd.logits, fwd.token_loss, fwd.mean_loss, fwd.ws,
+                              ev.ev[2 * r], ev.ev[2 * r + 1], name)
+        torch_sync()
+        us = float(np.mean([ev.ms(2 * r, 2 * r + 1) for r in range(reps)])) * 1e3
+        row = {"us": round(us, 2), "bound": bound}
+        if bound == "mfma":
+            tf = flops / (us * 1e-6) / 1e12
+            row.update({"achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        else:
+            gbs = nbytes / (us * 1e-6) / 1e9
+            row.update({"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes})
+            if flops:
+                row["tflops"] = round(flops / (us * 1e-6) / 1e12, 1)
+        out[name] = row
+    ev.close()
+    return out
+
+
+def torch_sync():
+    import torch
+    torch.cuda.synchronize()
 
 
 def bench_train_grad(cfg, B, T, dev_params, idx, stream, reps=3):

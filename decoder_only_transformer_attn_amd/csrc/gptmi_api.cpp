@@ -17,13 +17,9 @@ using namespace gptmi;
 
 namespace {
 
-thread_local char g_hip_msg[256] = "";
-
-int hip_status(hipError_t e) {
-  if (e == hipSuccess) return GPT_OK;
-  snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
-  return GPT_ERR_HIP;
-}
+// (the library keeps no state between calls: a failed HIP call is reported
+// as GPT_ERR_HIP only, without its HIP code)
+int hip_status(hipError_t e) { return e == hipSuccess ? GPT_OK : GPT_ERR_HIP; }
 
 #define GPT_TRY(expr)                       \
   do {                                      \
@@ -699,7 +695,7 @@ const char* gpt_status_string(int status) {
     case GPT_ERR_SHAPE: return "invalid shape argument";
     case GPT_ERR_WORKSPACE: return "workspace too small";
     case GPT_ERR_DTYPE: return "unsupported dtype";
-    case GPT_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+    case GPT_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     default: return "unknown status";
   }
 }

@@ -15,11 +15,13 @@
  * Conventions for every entry point:
  *  - Buffers marked (device) are device pointers owned by the caller; (host)
  *    are host pointers.  The library never allocates, never frees, keeps no
- *    state between calls, never synchronises and enqueues work only on
- *    `stream` (a hipStream_t; NULL = the default stream).
+ *    state between calls (gpt_decode_step_noalloc's static device array
+ *    aside), never synchronises and enqueues work only on `stream` (a
+ *    hipStream_t; NULL = the default stream).
  *  - Every host-checkable condition is checked before the first HIP call; on
  *    an error nothing is enqueued and the outputs are untouched.  A HIP
- *    launch failure returns GPT_ERR_HIP; outputs are then undefined.
+ *    launch failure returns GPT_ERR_HIP (the HIP code is not kept); outputs
+ *    are then undefined.
  *  - Device buffers must be 16-byte aligned (every HIP or torch allocation
  *    is); the parameter blob's tensors then are too, since every tensor
  *    size is a multiple of C or n_ff.
