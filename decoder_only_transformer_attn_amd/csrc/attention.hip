@@ -305,32 +305,68 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16, head width 64: key/value tiles of 64 rows reach LDS by direct-to-LDS
-// DMA in their natural [key][d] layout (128-byte rows) through a ring of
-// four stages; the value operand of O^T = U^T P^T (8 consecutive keys of one
-// column d per lane) is read with gfx950's transposing LDS read
-// ds_read_b64_tr_b16, so no register transpose is needed.  Within a group
-// of 16 lanes that instruction returns to lane 4a + b element b of the
-// 4-element rows addressed by lanes a, a + 4, a + 8 and a + 12: when lane j
-// addresses row kb + j / 4 at column d0 + 4 (j % 4), lane i receives rows
-// kb .. kb + 3 of column d0 + i.  The 16-byte chunks of a row are
-// XOR-swizzled by f(r) (bits 1..3 of the row, reordered) so that both the
-// key fragments (16 rows, one chunk) and the transposing reads (4 rows, 4
-// chunks) hit distinct bank groups.  Each wave computes the scores of tile
-// j + 1 while it takes the softmax of tile j.
+// DMA in their natural [key][d] layout (128-byte rows), K tiles and U tiles
+// in two rings of NS stages each; the value operand of O^T = U^T P^T (8
+// consecutive keys of one column d per lane) is read with gfx950's
+// transposing LDS read ds_read_b64_tr_b16, so no register transpose is
+// needed.  Within a group of 16 lanes that instruction returns to lane
+// 4a + b element b of the 4-element rows addressed by lanes a, a + 4, a + 8
+// and a + 12: when lane j addresses row kb + j / 4 at column d0 + 4 (j % 4),
+// lane i receives rows kb .. kb + 3 of column d0 + i.  The 16-byte chunks of
+// a row are XOR-swizzled by f(r) (bits 1..3 of the row, reordered) so that
+// both the key fragments (16 rows, one chunk) and the transposing reads (4
+// rows, 4 chunks) hit distinct bank groups.
+//
+// Software pipeline, per wave and key tile j: the MFMAs of the scores of
+// tile j + 1 and of the product P_{j-1} U_{j-1} have no dependence on the
+// softmax of tile j, so one basic block issues all three, and scheduling
+// groups interleave about eight VALU operations of the softmax into the
+// shadow of every MFMA.  Tile t's K is used at step t - 1 and its U at step
+// t + 1: step i loads K(i + 3) and U(i + 2), into the stages that K(i - 1)
+// and U(i - 2) left, two steps before each is read.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int kv_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource words over [base, base + bytes) (loads beyond read zero).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+// One direct-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// dst + 16 l.  Issued from inline assembly so that the compiler does not
+// make every later LDS read wait for all loads in flight (it cannot tell
+// the stages apart); the kernel's own vmcnt waits and barriers order each
+// stage's reads after its loads.
+__device__ __forceinline__ void dma16(const __attribute__((address_space(3))) char* dst, i32x4 rsrc,
+                                      uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "{m0}"(m0), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 template <int NS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_d64_kernel(AttnArgs a) {
+  static_assert(NS == 4, "stage offsets are folded into 16-bit LDS immediates for four stages");
   constexpr int D = 64, BQ = 128, BKV = 64, TILE = BKV * 128;   // bytes of K (or U) per tile
   typedef Mfma<bf16> MF;
-  __shared__ __align__(1024) char ring[NS][2][TILE];
+  __shared__ __align__(1024) char ring[2 * NS][TILE];            // K stages, then U stages
   typedef __attribute__((address_space(3))) char lch;
-  lch* const lring = (lch*)&ring[0][0][0];
+  lch* const lring = (lch*)&ring[0][0];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -359,56 +395,94 @@ attn_fwd_d64_kernel(AttnArgs a) {
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = qcol < T_seq ? MF::load(Q + (long long)qcol * a.q_st + ks * 16 + g * 8) : MF::frag{};
 
-  // DMA plan: a tile is 16 loads of 1 KB (8 rows each): K rows for loads 0-7,
-  // U rows for 8-15; wave w sends loads w, w + 4, w + 8, w + 12.  Lane l
-  // writes slot l % 8 of row 8 (i % 8) + l / 8, so it fetches chunk
-  // slot ^ f(row) of that row.  Rows past the sequence lie outside the
-  // resources and arrive as zeros.
-  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(K, (uint32_t)(((size_t)(T_seq - 1) * kst + D) * 2));
-  const __amdgpu_buffer_rsrc_t rsu = make_rsrc(U, (uint32_t)(((size_t)(T_seq - 1) * vst + D) * 2));
+  // DMA plan: a K (or U) tile is 8 loads of 1 KB (8 rows each); wave w sends
+  // loads w and w + 4 of each.  Lane l writes slot l % 8 of row
+  // 8 (i % 8) + l / 8, so it fetches chunk slot ^ f(row) of that row.  Rows
+  // past the sequence lie outside the resources and arrive as zeros.
+  const i32x4 rsk = rsrc_words(K, (uint32_t)(((size_t)(T_seq - 1) * kst + D) * 2));
+  const i32x4 rsu = rsrc_words(U, (uint32_t)(((size_t)(T_seq - 1) * vst + D) * 2));
   const int rA = 8 * wave + (lane >> 3), rB = rA + 32, sl = lane & 7;
   const uint32_t koffA = (uint32_t)((rA * kst + (sl ^ kv_swz(rA)) * 8) * 2);
   const uint32_t koffB = (uint32_t)((rB * kst + (sl ^ kv_swz(rB)) * 8) * 2);
   const uint32_t voffA = (uint32_t)((rA * vst + (sl ^ kv_swz(rA)) * 8) * 2);
   const uint32_t voffB = (uint32_t)((rB * vst + (sl ^ kv_swz(rB)) * 8) * 2);
-  auto dma_tile = [&](int t) {
-    lch* st = lring + (t % NS) * 2 * TILE;
-    const uint32_t sk = (uint32_t)(t * BKV * kst * 2), sv = (uint32_t)(t * BKV * vst * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + wave * 1024), 16, koffA, sk, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + (wave + 4) * 1024), 16, koffB, sk, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsu, (lds_void*)(st + TILE + wave * 1024), 16, voffA, sv, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsu, (lds_void*)(st + TILE + (wave + 4) * 1024), 16, voffB, sv, 0, 0);
-  };
 
   const int kv_end = min(T_seq, q0 + BQ);
   const int nt = (kv_end + BKV - 1) / BKV;                        // key tiles of this block
   const int lw = qw0 < T_seq ? min(qw0 + 31, T_seq - 1) / BKV : -1;   // this wave's last tile
 
-  // score fragments: row block rb (keys 32 rb ..), k step ks, from the K half of a stage
+  // step i (i = -3 .. nt - 1) loads K(i + 3) and U(i + 2), those that exist
+  auto issue = [&](int i) {
+    const int tk = i + 3, tu = i + 2;
+    if (tk < nt) {
+      lch* st = lring + (tk & (NS - 1)) * TILE;
+      const uint32_t sk = (uint32_t)(tk * BKV * kst * 2);
+      dma16(st + wave * 1024, rsk, koffA, sk);
+      dma16(st + (wave + 4) * 1024, rsk, koffB, sk);
+    }
+    if (tu >= 0 && tu < nt) {
+      lch* st = lring + (NS + (tu & (NS - 1))) * TILE;
+      const uint32_t sv = (uint32_t)(tu * BKV * vst * 2);
+      dma16(st + wave * 1024, rsu, voffA, sv);
+      dma16(st + (wave + 4) * 1024, rsu, voffB, sv);
+    }
+  };
+  // loads step i sent (per lane)
+  auto nload = [&](int i) { return (i + 3 >= 0 && i + 3 < nt ? 2 : 0) + (i + 2 >= 0 && i + 2 < nt ? 2 : 0); };
+  // wait until at most n of this lane's loads are in flight (n even, <= 8)
+  auto wait_loads = [&](int n) {
+    if (n >= 8) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 8);
+    else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 6);
+    else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 4);
+    else if (n >= 2) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 2);
+    else __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  };
+
+  // Per-lane LDS offsets within a stage; the stage and the row-block parts
+  // are compile-time and fold into the instructions' immediates (rows
+  // 16 hh + 32 rb leave f(r) unchanged).
+  int kofs[4], uofs[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int r = lane & 31, c = ks * 2 + g;
+    kofs[ks] = r * 128 + ((c ^ kv_swz(r)) << 4);
+  }
+  {
+    const int G = lane >> 4, i = lane & 15, half = G & 1;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+      const int c = 4 * ob + 2 * half + ((i & 3) >> 1);
+      const int r0 = g * 4 + (i >> 2), r1 = r0 + 8;
+      uofs[ob][0] = r0 * 128 + ((c ^ kv_swz(r0)) << 4) + ((i & 1) << 3);
+      uofs[ob][1] = r1 * 128 + ((c ^ kv_swz(r1)) << 4) + ((i & 1) << 3);
+    }
+  }
+  // score fragment: K rows 32 rb + lane % 32, k step ks, of K stage st
   auto kfrag = [&](const lch* st, int rb, int ks) {
-    const int r = rb * 32 + (lane & 31), c = ks * 2 + g;
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st + r * 128 + ((c ^ kv_swz(r)) << 4));
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st + kofs[ks] + rb * 4096);
   };
   // U^T fragment for O^T rows d = 32 ob + lane % 32, keys 32 rb + 16 hh + 4 g + {0..3, 8..11}
   auto vfrag = [&](const lch* st, int ob, int rb, int hh) {
-    const int G = lane >> 4, i = lane & 15, half = G & 1;
-    const int c = 4 * ob + 2 * half + ((i & 3) >> 1);
-    const int r0 = rb * 32 + hh * 16 + g * 4 + (i >> 2);
-    const lch* U0 = st + TILE;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(U0 + r0 * 128 + ((c ^ kv_swz(r0)) << 4) + ((i & 1) << 3)));
-    const int r1 = r0 + 8;
+        (__attribute__((address_space(3))) i16x4*)(st + uofs[ob][0] + rb * 4096 + hh * 2048));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(U0 + r1 * 128 + ((c ^ kv_swz(r1)) << 4) + ((i & 1) << 3)));
+        (__attribute__((address_space(3))) i16x4*)(st + uofs[ob][1] + rb * 4096 + hh * 2048));
     return __builtin_bit_cast(bf16x8, i16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
   };
 
   f32x16 o[2], sa[2], sb[2];
+  bf16x8 pa[2][2], pb[2][2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
-  float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) pb[rb][hh] = bf16x8{};
+  // exponent reference (log2 domain), lane-partial row sum, and the factor
+  // that O still owes for the last move of the reference
+  float m_run = -INFINITY, l_run = 0.f, alpha_o = 1.f;
   const float sc = a.scale_log2;
-  // scores of the tile in stage st into sx
+
   auto scores = [&](f32x16 (&sx)[2], const lch* st) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -418,94 +492,147 @@ attn_fwd_d64_kernel(AttnArgs a) {
       for (int ks = 0; ks < 4; ++ks) sx[rb] = MF::mma(kfrag(st, rb, ks), qf[ks], sx[rb]);
     }
   };
-  // tile j + 1 must be in LDS: wait for this wave's share (tile j + 2 may
-  // still be in flight), then the barrier publishes everyone's; every wave
-  // is then done with tile j - 1's stage, which takes tile j + NS - 1
-  auto sync = [&](int j) {
-    if (j + 2 < nt) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 4);
-    else __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
-    __syncthreads();
-    if (j + NS - 1 < nt) dma_tile(j + NS - 1);
-  };
-  // tile j: s holds its scores; the next tile's go to sn
-  auto step = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
-    if (j > lw) return;                   // every key of tile j is in this wave's future
-    const lch* cur = lring + (j % NS) * 2 * TILE;
-    const int kb = j * BKV;
-    if (kb + BKV - 1 > qw0) {             // causal mask on the diagonal tile(s), in place
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[rb][r] = kb + rb * 32 + acc_row(r, lane) > qcol ? -INFINITY : s[rb][r];
-    }
-    // the next tile's scores: independent of the softmax below, so the MFMAs overlap it
-    if (j + 1 <= lw) scores(sn, lring + ((j + 1) % NS) * 2 * TILE);
-    // online softmax of tile j; the exponent reference moves only by > 8 (log2 units)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
-    {
-      // lanes l and l ^ 32 hold the other keys of the same query: both
-      // halves of the swap carry the pair, in every lane
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sc;
-    }
-    const float m_new = mx > m_run + 8.f ? mx : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    float psum = 0.f;
-    bf16x8 pf[2][2];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[rb][8 * hh + 2 * e], sc, -m_new));
-          const float p1 = fast_exp2(fmaf(s[rb][8 * hh + 2 * e + 1], sc, -m_new));
-          w[e] = pack_bf16x2(p0, p1);
-          // the row sum of the probabilities as they enter the product (bf16)
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, psum, false);
-        }
-        pf[rb][hh] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[ob][r] *= alpha;
-    }
+  auto pv = [&](const bf16x8 (&pp)[2][2], const lch* st) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int ob = 0; ob < 2; ++ob) o[ob] = MF::mma(vfrag(cur, ob, rb, hh), pf[rb][hh], o[ob]);
+        for (int ob = 0; ob < 2; ++ob) o[ob] = MF::mma(vfrag(st, ob, rb, hh), pp[rb][hh], o[ob]);
+  };
+  auto rescale_o = [&]() {
+    if (__builtin_amdgcn_ballot_w64(alpha_o != 1.f)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[0][r] *= alpha_o;
+        o[1][r] *= alpha_o;
+      }
+    }
+    alpha_o = 1.f;
+  };
+  // causal mask of this wave's diagonal tile kb .. kb + 63, in place
+  auto mask = [&](f32x16 (&s)[2], int kb) {
+    const int e = qcol - kb - 4 * g;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (rb * 32 + (r >> 2) * 8 + (r & 3) > e) s[rb][r] = -INFINITY;
+  };
+  // One pipeline step's arithmetic in 16 MFMA slots.  Slot k issues MFMA
+  // k (even: score MFMA k / 2 of tile j + 1, odd: product MFMA k / 2 of
+  // tile j - 1), the fragment read of MFMA k + 4, and a share of the online
+  // softmax of tile j that takes about as long as one MFMA: the row maximum
+  // in slots 0-2, then one pair of probabilities per slot (2 FMA, 2 exp2, a
+  // bf16 pack and its row-sum dot product).  sched_barrier keeps the slots
+  // apart, so every MFMA runs in the shadow of VALU work and each fragment
+  // read has four slots to land.  The exponent reference moves only by > 8
+  // (log2 units); the probabilities (bf16, B-operand layout) go to pc.
+  auto region = [&](auto S_, const f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[2][2],
+                    bf16x8 (&pc)[2][2]) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    const lch* kst = lring + ((S + 1) & (NS - 1)) * TILE;             // K of tile j + 1
+    const lch* ust = lring + (NS + ((S + NS - 1) & (NS - 1))) * TILE;  // U of tile j - 1
+    // score MFMA i: row block i % 2, k step i / 2; product MFMA i: ob = i % 2,
+    // hh = (i / 2) % 2, rb = i / 4 (consecutive MFMAs of a kind alternate accumulators)
+    bf16x8 fr[16];
+    auto load = [&](auto K_) __attribute__((always_inline)) {
+      constexpr int k = decltype(K_)::value, i = k / 2;
+      if constexpr (k % 2 == 0) fr[k] = kfrag(kst, i % 2, i / 2);
+      else fr[k] = vfrag(ust, i % 2, i / 4, (i / 2) % 2);
+    };
+    float mx = -INFINITY, m_new = 0.f, alpha = 1.f, psum = 0.f;
+    uint32_t w[16];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    auto pair = [&](auto P_) __attribute__((always_inline)) {
+      constexpr int p = decltype(P_)::value, rb = p / 8, c = (p % 8) * 2;
+      const float p0 = fast_exp2(fmaf(s[rb][c], sc, -m_new));
+      const float p1 = fast_exp2(fmaf(s[rb][c + 1], sc, -m_new));
+      w[p] = pack_bf16x2(p0, p1);
+      // the row sum of the probabilities as they enter the product (bf16)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[p]), ones, psum, false);
+    };
+    static_for<0, 4>([&](auto K_) __attribute__((always_inline)) { load(K_); });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 16>([&](auto K_) __attribute__((always_inline)) {
+      constexpr int k = decltype(K_)::value, i = k / 2;
+      if constexpr (k % 2 == 0) {
+        if constexpr (i / 2 == 0) sn[i % 2] = MF::mma(fr[k], qf[0], f32x16{});
+        else sn[i % 2] = MF::mma(fr[k], qf[i / 2], sn[i % 2]);
+      } else {
+        o[i % 2] = MF::mma(fr[k], pp[i / 4][(i / 2) % 2], o[i % 2]);
+      }
+      if constexpr (k + 4 < 16) load(std::integral_constant<int, k + 4>{});
+      if constexpr (k < 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[k][r]);
+      } else if constexpr (k == 2) {
+        // lanes l and l ^ 32 hold the other keys of the same query: both
+        // halves of the swap carry the pair, in every lane
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sc;
+        m_new = mx > m_run + 8.f ? mx : m_run;
+        alpha = fast_exp2(m_run - m_new);
+      } else {
+        pair(std::integral_constant<int, k - 3>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<13, 16>([&](auto P_) __attribute__((always_inline)) { pair(P_); });
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      pc[q / 2][q % 2] = __builtin_bit_cast(bf16x8, make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]));
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    alpha_o = alpha;
   };
 
-  // prologue: tiles 0 .. NS - 2 in flight; scores of tile 0
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < nt) dma_tile(t);
-  if (nt > 2) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 8);        // tile 0 landed (tiles 1, 2 in flight)
-  else if (nt > 1) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 4);
-  else __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  // one step of the pipeline, stage S = j % NS: tile j's scores are in s and
+  // tile j - 1's probabilities in pp (zeros, against a zeroed U stage, at j = 0)
+  auto step = [&](auto S_, int j, f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[2][2],
+                  bf16x8 (&pc)[2][2]) __attribute__((always_inline)) {
+    // tile j + 1's K and tile j - 1's U are in LDS: wait for this wave's
+    // loads of them, then the barrier publishes everyone's; every wave is
+    // then done with step j - 1, whose stages take the loads of step j
+    wait_loads(nload(j - 1));
+    __syncthreads();
+    issue(j);
+    if (j > lw) return;                   // every key of tile j is in this wave's future
+    if (j == lw) mask(s, j * BKV);
+    rescale_o();
+    region(S_, s, sn, pp, pc);
+  };
+
+  // prologue: K(0..2) and U(0..1) in flight; a zeroed U stage stands in for
+  // tile -1; scores of tile 0 once K(0) has landed
+  issue(-3);
+  issue(-2);
+  issue(-1);
+  {
+    lch* z = lring + (2 * NS - 1) * TILE + tid * 32;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(z) = u32x4_t{0, 0, 0, 0};
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(z + 16) = u32x4_t{0, 0, 0, 0};
+  }
+  wait_loads(nload(-2) + nload(-1));
   __syncthreads();
-  if (lw >= 0) scores(sa, lring);
-  // two tiles per pass, so the two score sets trade places without copies
-  for (int j = 0; j < nt; j += 2) {
-    sync(j);
-    step(j, sa, sb);
-    if (j + 1 < nt) {
-      sync(j + 1);
-      step(j + 1, sb, sa);
-    }
+  scores(sa, lring);   // (also in waves past the sequence: the Q loads are then waited for on every path)
+  for (int j = 0; j < nt; j += NS) {
+    step(std::integral_constant<int, 0>{}, j, sa, sb, pb, pa);
+    if (j + 1 >= nt) break;
+    step(std::integral_constant<int, 1>{}, j + 1, sb, sa, pa, pb);
+    if (j + 2 >= nt) break;
+    step(std::integral_constant<int, 2>{}, j + 2, sa, sb, pb, pa);
+    if (j + 3 >= nt) break;
+    step(std::integral_constant<int, 3>{}, j + 3, sb, sa, pa, pb);
+  }
+  // the last tile's product: its U stage, once every wave's loads landed
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  __syncthreads();
+  if (lw >= 0) {
+    rescale_o();
+    const lch* st = lring + (NS + (lw & (NS - 1))) * TILE;
+    if (lw & 1) pv(pb, st);
+    else pv(pa, st);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
