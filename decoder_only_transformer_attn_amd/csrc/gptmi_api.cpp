@@ -1096,4 +1096,23 @@ int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, con
   return hip_status(launch_attention(cfg->dtype, aa, static_cast<hipStream_t>(stream)));
 }
 
+int gpt_debug_attention_rows(const gpt_config* cfg, const void* qkv, int B, int T, void* out, void* stream) {
+  int s = check_config(cfg);
+  if (s != GPT_OK) return s;
+  if (!qkv || !out) return GPT_ERR_NULL;
+  if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
+  const int C = cfg->n_embd, H = cfg->n_head, D = C / H;
+  const long long ld = 3LL * C;
+  const size_t es = cfg->dtype == 0 ? 4 : 2;
+  const char* rows = static_cast<const char*>(qkv);
+  AttnArgs aa{};
+  aa.q = rows;              aa.q_sb = T * ld; aa.q_sh = D; aa.q_st = (int)ld;
+  aa.k = rows + C * es;     aa.k_sb = T * ld; aa.k_sh = D; aa.k_st = (int)ld;
+  aa.v = rows + 2 * C * es; aa.v_sb = T * ld; aa.v_sh = D; aa.v_st = (int)ld;
+  aa.o = out; aa.o_ld = C;
+  aa.B = B; aa.H = H; aa.T_seq = T; aa.D = D; aa.Hkv = H;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  return hip_status(launch_attention(cfg->dtype, aa, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

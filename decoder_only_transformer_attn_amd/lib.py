@@ -49,6 +49,7 @@ SIGNATURES = {
     "gpt_debug_layernorm": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _vp, _vp]),
     "gpt_debug_linear": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "gpt_debug_attention": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "gpt_debug_attention_rows": (_c_int, [_CFG, _vp, _c_int, _c_int, _vp, _vp]),
     "gpt_decode_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "gpt_prefill": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gpt_decode_step": (_c_int, [_CFG, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _sz, _vp]),
@@ -431,3 +432,8 @@ def debug_attention(cfg, q, k, u, out, stream=None) -> None:
     B, H, T, D = q.shape
     check(load().gpt_debug_attention(ctypes.byref(cfg_c(cfg)), _ptr(q), _ptr(k), _ptr(u), B, T, _ptr(out),
                                      _stream(stream)))
+
+
+def debug_attention_rows(cfg, qkv, B: int, T: int, out, stream=None) -> None:
+    """qkv: [B*T, 3C] token-major q | k | u rows (the forward's c_attn output); out [B*T, C]."""
+    check(load().gpt_debug_attention_rows(ctypes.byref(cfg_c(cfg)), _ptr(qkv), B, T, _ptr(out), _stream(stream)))

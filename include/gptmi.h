@@ -371,6 +371,12 @@ int gpt_debug_linear(const gpt_config* cfg, const void* A, const void* W, const 
 int gpt_debug_attention(const gpt_config* cfg, const void* q, const void* k, const void* u,
                         int B, int T, void* out, void* stream);
 
+/* The same attention on token-major rows, the layout the forward's c_attn
+ * writes: qkv [B*T, 3C] in cfg->dtype, row t of sequence b holding q | k | u
+ * (head h in columns [hD, hD+D) of each third); out [B*T, C] as above.
+ * Errors: GPT_ERR_NULL for a null pointer, GPT_ERR_SHAPE for B or T <= 0. */
+int gpt_debug_attention_rows(const gpt_config* cfg, const void* qkv, int B, int T, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

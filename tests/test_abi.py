@@ -92,6 +92,8 @@ def test_debug_entry_validation():
     assert L.gpt_debug_linear(ctypes.byref(c), None, 1, None, 4, 4, 8, 0, 0, 1, None) == -1
     assert L.gpt_debug_layernorm(ctypes.byref(c), 1, 1, 1, 0, 1, None) == -4
     assert L.gpt_debug_attention(ctypes.byref(c), 1, 1, 1, 0, 12, 1, None) == -4  # B = 0
+    assert L.gpt_debug_attention_rows(ctypes.byref(c), 1, 2, 0, 1, None) == -4    # T = 0
+    assert L.gpt_debug_attention_rows(ctypes.byref(c), None, 2, 12, 1, None) == -1
 
 
 def test_workspace_grows_with_batch():

@@ -140,6 +140,33 @@ def test_attention_kernel(dtype, B, H, T, D):
     assert err <= tol, err
 
 
+@pytest.mark.parametrize("B,H,T", [(8, 12, 1024), (3, 12, 333)])
+def test_attention_rows_full_size(B, H, T):
+    """bf16, D = 64 on the token-major q|k|u rows the forward hands over, at
+    the GPT-2 124M workload's shape (every query tile, all 16 key-tile
+    depths) and a ragged length: sampled (sequence, head) pairs from both ends
+    and the middle against the oracle, and two launches bit-identical."""
+    lib = _lib()
+    D = 64
+    cfg = synth.GPTConfig(vocab=17, ctx=1024, n_embd=H * D, n_head=H, n_layer=1, n_ff=4 * H * D, dtype=synth.BF16)
+    rng = np.random.default_rng(7000 + T)
+    qkv = synth.round_bf16(rng.standard_normal((B * T, 3 * H * D)).astype(np.float32))
+    dq = torch.from_numpy(qkv).to(torch.bfloat16).cuda()
+    out = torch.empty((B * T, H * D), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out)
+    lib.debug_attention_rows(cfg, dq, B, T, out)
+    lib.debug_attention_rows(cfg, dq, B, T, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    got = out.float().cpu().numpy().reshape(B, T, H, D)
+    x = qkv.reshape(B, T, 3, H, D).astype(np.float64)
+    for b, h in [(0, 0), (B - 1, H - 1), (B // 2, H // 2), (1, 7), (B - 1, 0), (0, H - 1)]:
+        ref = O.causal_attention(x[b, :, 0, h], x[b, :, 1, h], x[b, :, 2, h])
+        err = np.abs(got[b, :, h] - ref).max()
+        print(f"B{B} T{T} (b {b}, h {h}): max err {err:.4g}")
+        assert err <= 3e-2, (b, h, err)
+
+
 # ---------------------------------------------------------------------------
 # Whole forward, fp32 configurations
 # ---------------------------------------------------------------------------
