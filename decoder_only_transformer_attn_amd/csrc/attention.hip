@@ -389,16 +389,14 @@ attn_fwd_d64_kernel(AttnArgs a) {
   const bf16* U = reinterpret_cast<const bf16*>(a.v) + (long long)b * a.v_sb + (long long)hk * a.v_sh;
   const int kst = a.k_st, vst = a.v_st;
 
-  // Q^T fragments of this lane's query column (zero past the sequence)
+  // Q^T fragments of this lane's query column, read from LDS in the prologue
   MF::frag qf[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = qcol < T_seq ? MF::load(Q + (long long)qcol * a.q_st + ks * 16 + g * 8) : MF::frag{};
 
   // DMA plan: a K (or U) tile is 8 loads of 1 KB (8 rows each); wave w sends
   // loads w and w + 4 of each.  Lane l writes slot l % 8 of row
   // 8 (i % 8) + l / 8, so it fetches chunk slot ^ f(row) of that row.  Rows
-  // past the sequence lie outside the resources and arrive as zeros.
+  // past the sequence lie outside the resources and arrive as zeros: the
+  // whole byte offset goes in the VGPR offset, which the range check covers.
   const i32x4 rsk = rsrc_words(K, (uint32_t)(((size_t)(T_seq - 1) * kst + D) * 2));
   const i32x4 rsu = rsrc_words(U, (uint32_t)(((size_t)(T_seq - 1) * vst + D) * 2));
   const int rA = 8 * wave + (lane >> 3), rB = rA + 32, sl = lane & 7;
@@ -406,6 +404,13 @@ attn_fwd_d64_kernel(AttnArgs a) {
   const uint32_t koffB = (uint32_t)((rB * kst + (sl ^ kv_swz(rB)) * 8) * 2);
   const uint32_t voffA = (uint32_t)((rA * vst + (sl ^ kv_swz(rA)) * 8) * 2);
   const uint32_t voffB = (uint32_t)((rB * vst + (sl ^ kv_swz(rB)) * 8) * 2);
+  // Each wave's 32 query rows reach LDS the same way (4 loads of 8 rows),
+  // into a stage that the first loads of step 0 overwrite: K stage 3 for
+  // waves 0 and 1, U stage 2 for waves 2 and 3.  Read through LDS, they
+  // leave no register loads that a wait for them would order after every
+  // tile load in flight.
+  const i32x4 rsq = rsrc_words(Q, (uint32_t)(((size_t)(T_seq - 1) * a.q_st + D) * 2));
+  lch* const qarea = lring + (wave < 2 ? (NS - 1) * TILE : (NS + 2) * TILE) + (wave & 1) * 4096;
 
   const int kv_end = min(T_seq, q0 + BQ);
   const int nt = (kv_end + BKV - 1) / BKV;                        // key tiles of this block
@@ -417,14 +422,14 @@ attn_fwd_d64_kernel(AttnArgs a) {
     if (tk < nt) {
       lch* st = lring + (tk & (NS - 1)) * TILE;
       const uint32_t sk = (uint32_t)(tk * BKV * kst * 2);
-      dma16(st + wave * 1024, rsk, koffA, sk);
-      dma16(st + (wave + 4) * 1024, rsk, koffB, sk);
+      dma16(st + wave * 1024, rsk, koffA + sk, 0);
+      dma16(st + (wave + 4) * 1024, rsk, koffB + sk, 0);
     }
     if (tu >= 0 && tu < nt) {
       lch* st = lring + (NS + (tu & (NS - 1))) * TILE;
       const uint32_t sv = (uint32_t)(tu * BKV * vst * 2);
-      dma16(st + wave * 1024, rsu, voffA, sv);
-      dma16(st + (wave + 4) * 1024, rsu, voffB, sv);
+      dma16(st + wave * 1024, rsu, voffA + sv, 0);
+      dma16(st + (wave + 4) * 1024, rsu, voffB + sv, 0);
     }
   };
   // loads step i sent (per lane)
@@ -603,9 +608,18 @@ attn_fwd_d64_kernel(AttnArgs a) {
     region(S_, s, sn, pp, pc);
   };
 
-  // prologue: K(0..2) and U(0..1) in flight; a zeroed U stage stands in for
-  // tile -1; scores of tile 0 once K(0) has landed
+  // prologue: K(0), this wave's Q rows, then K(1..2) and U(0..1) in flight;
+  // a zeroed U stage stands in for tile -1; scores of tile 0 once K(0) and
+  // Q have landed
   issue(-3);
+  {
+    const int r = lane >> 3, sl8 = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 8 * i + r;
+      dma16(qarea + i * 1024, rsq, (uint32_t)(((qw0 + rl) * a.q_st + (sl8 ^ kv_swz(rl)) * 8) * 2), 0);
+    }
+  }
   issue(-2);
   issue(-1);
   {
@@ -615,7 +629,10 @@ attn_fwd_d64_kernel(AttnArgs a) {
   }
   wait_loads(nload(-2) + nload(-1));
   __syncthreads();
-  scores(sa, lring);   // (also in waves past the sequence: the Q loads are then waited for on every path)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qarea + kofs[ks]);
+  scores(sa, lring);
   for (int j = 0; j < nt; j += NS) {
     step(std::integral_constant<int, 0>{}, j, sa, sb, pb, pa);
     if (j + 1 >= nt) break;
