@@ -125,8 +125,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   // prefetch registers: K chunks and U key pairs.  Buffer loads: keys past the
   // sequence lie outside the resources and chunks past D (or past the tile)
   // take an offset outside them, so every such read is zero without a branch;
-  // the per-thread offsets are fixed and the tile start goes in the scalar
-  // offset.
+  // the per-thread offsets are fixed and the tile start is added to them (the
+  // range check covers the VGPR offset; OOB_OFFSET plus a tile start stays
+  // outside every resource).
   struct RegSet { uint4 kr[KCH], ur0[UCH], ur1[UCH]; };
   // a resource covers rows 0 .. T-1 exactly (the last one only up to D)
   const __amdgpu_buffer_rsrc_t rsk = make_rsrc(K, (uint32_t)(((size_t)(T_seq - 1) * kst + D) * sizeof(T)));
@@ -145,11 +146,11 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   auto gload = [&](RegSet& R, int kb) {
     const uint32_t sk = (uint32_t)(kb * kst * sizeof(T)), sv = (uint32_t)(kb * vst * sizeof(T));
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) R.kr[c] = buf_load16(rsk, koff[c], sk);
+    for (int c = 0; c < KCH; ++c) R.kr[c] = buf_load16(rsk, koff[c] + sk, 0);
 #pragma unroll
     for (int c = 0; c < UCH; ++c) {
-      R.ur0[c] = buf_load16(rsu, uoff[c], sv);
-      R.ur1[c] = buf_load16(rsu, uoff[c] == OOB_OFFSET ? OOB_OFFSET : uoff[c] + (uint32_t)(vst * sizeof(T)), sv);
+      R.ur0[c] = buf_load16(rsu, uoff[c] + sv, 0);
+      R.ur1[c] = buf_load16(rsu, (uoff[c] == OOB_OFFSET ? OOB_OFFSET : uoff[c] + (uint32_t)(vst * sizeof(T))) + sv, 0);
     }
   };
   // K as is; U transposed to U^T [d][key], written as (key, key+1) pairs
