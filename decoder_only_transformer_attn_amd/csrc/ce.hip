@@ -12,39 +12,55 @@
 
 namespace gptmi {
 
-constexpr int CE_ROWS = 16;  // rows per block (4 per wave)
+constexpr int CE_ROWS = 4;   // rows per block, one per wave
 
 __device__ __forceinline__ int target_of(const int32_t* targets, const int32_t* idx, int m, int T_seq) {
   if (targets) return targets[m];
   return ((m % T_seq) < T_seq - 1) ? idx[m + 1] : -1;
 }
 
+// One wave per token row.  With NPL > 0 the row's (max, sum) pairs sit in
+// registers (NPL per lane, ntiles <= 64 NPL), all loaded at once; NPL = 0
+// walks any number of tiles in two passes.
+template <int NPL>
 __global__ void __launch_bounds__(256) ce_rows_kernel(int M, int ntiles, const float* __restrict__ part_max,
                                                       const float* __restrict__ part_sum, const float* __restrict__ tgt,
                                                       const int32_t* targets, const int32_t* idx, int T_seq, int V,
                                                       float* __restrict__ token_loss, double* __restrict__ block_sums) {
-  __shared__ double wsum[4][2];
+  __shared__ double wsum[CE_ROWS][2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = blockIdx.x * CE_ROWS + wave;
   double s_loss = 0.0, s_cnt = 0.0;
-  for (int rr = wave; rr < CE_ROWS; rr += 4) {
-    const int m = blockIdx.x * CE_ROWS + rr;
-    if (m >= M) break;
+  if (m < M) {
     const float* pm = part_max + (long long)m * ntiles;
     const float* ps = part_sum + (long long)m * ntiles;
-    float mx = -INFINITY;
-    for (int t = lane; t < ntiles; t += 64) mx = fmaxf(mx, pm[t]);
-    mx = wave_max(mx);
-    float s = 0.f;
-    for (int t = lane; t < ntiles; t += 64) s += ps[t] * fast_exp2((pm[t] - mx) * 1.4426950408889634f);
-    s = wave_sum(s);
     const int y = target_of(targets, idx, m, T_seq);
-    const bool valid = y >= 0 && y < V;
-    const float loss = valid ? (mx + __logf(s)) - tgt[m] : 0.f;
-    if (lane == 0) {
-      if (token_loss) token_loss[m] = loss;
-      s_loss += (double)loss;
-      s_cnt += valid ? 1.0 : 0.0;
+    const float zt = tgt[m];
+    float mx = -INFINITY, s = 0.f;
+    if constexpr (NPL > 0) {
+      float vm[NPL], vs[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int t = lane + 64 * i;
+        vm[i] = t < ntiles ? pm[t] : -INFINITY;
+        vs[i] = t < ntiles ? ps[t] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) mx = fmaxf(mx, vm[i]);
+      mx = wave_max(mx);
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) s += vs[i] * fast_exp2((vm[i] - mx) * 1.4426950408889634f);
+    } else {
+      for (int t = lane; t < ntiles; t += 64) mx = fmaxf(mx, pm[t]);
+      mx = wave_max(mx);
+      for (int t = lane; t < ntiles; t += 64) s += ps[t] * fast_exp2((pm[t] - mx) * 1.4426950408889634f);
     }
+    s = wave_sum(s);
+    const bool valid = y >= 0 && y < V;
+    const float loss = valid ? (mx + __logf(s)) - zt : 0.f;
+    if (lane == 0 && token_loss) token_loss[m] = loss;
+    s_loss = (double)loss;
+    s_cnt = valid ? 1.0 : 0.0;
   }
   if (lane == 0) { wsum[wave][0] = s_loss; wsum[wave][1] = s_cnt; }
   __syncthreads();
@@ -109,8 +125,15 @@ hipError_t launch_ce_reduce(int M, int ntiles, const float* part_max, const floa
                             const int32_t* targets, const int32_t* idx, int T_seq, int V, float* token_loss,
                             double* block_sums, float* mean_loss, hipStream_t st) {
   const int nb = ce_reduce_blocks(M);
-  hipLaunchKernelGGL(ce_rows_kernel, dim3(nb), dim3(256), 0, st, M, ntiles, part_max, part_sum, tgt, targets, idx,
-                     T_seq, V, token_loss, block_sums);
+  if (ntiles <= 256)
+    hipLaunchKernelGGL(ce_rows_kernel<4>, dim3(nb), dim3(256), 0, st, M, ntiles, part_max, part_sum, tgt, targets, idx,
+                       T_seq, V, token_loss, block_sums);
+  else if (ntiles <= 512)
+    hipLaunchKernelGGL(ce_rows_kernel<8>, dim3(nb), dim3(256), 0, st, M, ntiles, part_max, part_sum, tgt, targets, idx,
+                       T_seq, V, token_loss, block_sums);
+  else
+    hipLaunchKernelGGL(ce_rows_kernel<0>, dim3(nb), dim3(256), 0, st, M, ntiles, part_max, part_sum, tgt, targets, idx,
+                       T_seq, V, token_loss, block_sums);
   if (mean_loss) hipLaunchKernelGGL(ce_mean_kernel, dim3(1), dim3(256), 0, st, nb, block_sums, mean_loss);
   return hipGetLastError();
 }
