@@ -323,8 +323,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 // softmax of tile j, so one basic block issues all three, and scheduling
 // groups interleave about eight VALU operations of the softmax into the
 // shadow of every MFMA.  Tile t's K is used at step t - 1 and its U at step
-// t + 1: step i loads K(i + 3) and U(i + 2), into the stages that K(i - 1)
-// and U(i - 2) left, two steps before each is read.
+// t + 1; one barrier serves two steps: before step j (j even) the block
+// loads K(j + 3), K(j + 4), U(j + 1) and U(j + 2) into the stages that
+// steps j - 2 and j - 1 left, two steps before each is read.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int kv_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
@@ -417,24 +418,23 @@ attn_fwd_d64_kernel(AttnArgs a) {
   const int nt = (kv_end + BKV - 1) / BKV;                        // key tiles of this block
   const int lw = qw0 < T_seq ? min(qw0 + 31, T_seq - 1) / BKV : -1;   // this wave's last tile
 
-  // step i (i = -3 .. nt - 1) loads K(i + 3) and U(i + 2), those that exist
-  auto issue = [&](int i) {
-    const int tk = i + 3, tu = i + 2;
-    if (tk < nt) {
-      lch* st = lring + (tk & (NS - 1)) * TILE;
-      const uint32_t sk = (uint32_t)(tk * BKV * kst * 2);
+  // direct-to-LDS loads of K(t) and U(t) into their stages (t % NS), those that exist
+  auto issue_k = [&](int t) {
+    if (t >= 0 && t < nt) {
+      lch* st = lring + (t & (NS - 1)) * TILE;
+      const uint32_t sk = (uint32_t)(t * BKV * kst * 2);
       dma16(st + wave * 1024, rsk, koffA + sk, 0);
       dma16(st + (wave + 4) * 1024, rsk, koffB + sk, 0);
     }
-    if (tu >= 0 && tu < nt) {
-      lch* st = lring + (NS + (tu & (NS - 1))) * TILE;
-      const uint32_t sv = (uint32_t)(tu * BKV * vst * 2);
+  };
+  auto issue_u = [&](int t) {
+    if (t >= 0 && t < nt) {
+      lch* st = lring + (NS + (t & (NS - 1))) * TILE;
+      const uint32_t sv = (uint32_t)(t * BKV * vst * 2);
       dma16(st + wave * 1024, rsu, voffA + sv, 0);
       dma16(st + (wave + 4) * 1024, rsu, voffB + sv, 0);
     }
   };
-  // loads step i sent (per lane)
-  auto nload = [&](int i) { return (i + 3 >= 0 && i + 3 < nt ? 2 : 0) + (i + 2 >= 0 && i + 2 < nt ? 2 : 0); };
   // wait until at most n of this lane's loads are in flight (n even, <= 8)
   auto wait_loads = [&](int n) {
     if (n >= 8) __builtin_amdgcn_s_waitcnt(0x70 | 0xF00 | 8);
@@ -593,26 +593,34 @@ attn_fwd_d64_kernel(AttnArgs a) {
     alpha_o = alpha;
   };
 
+  // Before every even step j: K(j + 1), K(j + 2), U(j - 1) and U(j), the
+  // tiles of steps j and j + 1, were loaded before step j - 2; wait for this
+  // wave's loads, then the barrier publishes everyone's.  Every wave is then
+  // done with steps j - 2 and j - 1, which read K(j - 1), K(j), U(j - 3) and
+  // U(j - 2): their stages take K(j + 3), K(j + 4), U(j + 1) and U(j + 2),
+  // which steps j + 2 and j + 3 read.  One barrier per two key tiles.
+  auto sync2 = [&](int j) {
+    __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+    __syncthreads();
+    issue_k(j + 3);
+    issue_k(j + 4);
+    issue_u(j + 1);
+    issue_u(j + 2);
+  };
   // one step of the pipeline, stage S = j % NS: tile j's scores are in s and
   // tile j - 1's probabilities in pp (zeros, against a zeroed U stage, at j = 0)
   auto step = [&](auto S_, int j, f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[2][2],
                   bf16x8 (&pc)[2][2]) __attribute__((always_inline)) {
-    // tile j + 1's K and tile j - 1's U are in LDS: wait for this wave's
-    // loads of them, then the barrier publishes everyone's; every wave is
-    // then done with step j - 1, whose stages take the loads of step j
-    wait_loads(nload(j - 1));
-    __syncthreads();
-    issue(j);
     if (j > lw) return;                   // every key of tile j is in this wave's future
     if (j == lw) mask(s, j * BKV);
     rescale_o();
     region(S_, s, sn, pp, pc);
   };
 
-  // prologue: K(0), this wave's Q rows, then K(1..2) and U(0..1) in flight;
+  // prologue: K(0), this wave's Q rows, then K(1), K(2) and U(0) in flight;
   // a zeroed U stage stands in for tile -1; scores of tile 0 once K(0) and
   // Q have landed
-  issue(-3);
+  issue_k(0);
   {
     const int r = lane >> 3, sl8 = lane & 7;
 #pragma unroll
@@ -621,24 +629,27 @@ attn_fwd_d64_kernel(AttnArgs a) {
       dma16(qarea + i * 1024, rsq, (uint32_t)(((qw0 + rl) * a.q_st + (sl8 ^ kv_swz(rl)) * 8) * 2), 0);
     }
   }
-  issue(-2);
-  issue(-1);
+  issue_k(1);
+  issue_k(2);
+  issue_u(0);
   {
     lch* z = lring + (2 * NS - 1) * TILE + tid * 32;
     *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(z) = u32x4_t{0, 0, 0, 0};
     *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(z + 16) = u32x4_t{0, 0, 0, 0};
   }
-  wait_loads(nload(-2) + nload(-1));
+  wait_loads((nt > 1 ? 2 : 0) + (nt > 2 ? 2 : 0) + 2);   // (K(1), K(2), U(0) may still fly)
   __syncthreads();
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qarea + kofs[ks]);
   scores(sa, lring);
   for (int j = 0; j < nt; j += NS) {
+    sync2(j);
     step(std::integral_constant<int, 0>{}, j, sa, sb, pb, pa);
     if (j + 1 >= nt) break;
     step(std::integral_constant<int, 1>{}, j + 1, sb, sa, pa, pb);
     if (j + 2 >= nt) break;
+    sync2(j + 2);
     step(std::integral_constant<int, 2>{}, j + 2, sa, sb, pb, pa);
     if (j + 3 >= nt) break;
     step(std::integral_constant<int, 3>{}, j + 3, sb, sa, pa, pb);
