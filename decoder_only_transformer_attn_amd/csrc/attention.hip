@@ -741,44 +741,76 @@ __device__ __forceinline__ void chunk_f32<float>(const uint4& v, float (&o)[4]) 
   o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
 }
 
+// One block per (b, h).  The first batch of UNR keys per group (positions
+// up to UNR G - 1: the whole cache for up to 256 positions) is requested
+// before the query is ready, so the cache round trip overlaps the prologue's
+// (the query's, or the slices' of the fused kernel); the prologue then meets
+// the other waves at a bare barrier that leaves those loads in flight.
 template <typename T, int LPK>
-__global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int UNR = 8;
-  constexpr int G = DEC_THREADS / LPK;
-  __shared__ float qs[128];
-  __shared__ float gacc[G * LPK * VEC];   // per group: U-weighted sums, columns [0, LPK VEC)
-  __shared__ float gm[G], gl[G];
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int b = bh / a.H, h = bh - b * a.H, D = a.D;
-  const int g = tid / LPK, c = tid - g * LPK;
-  const bool act = c * VEC < D;             // lanes past the row's chunks hold zeros
-  const T* q = reinterpret_cast<const T*>(a.q) + (long long)bh * D;
-  for (int d = tid; d < D; d += DEC_THREADS) qs[d] = to_f32(q[d]) * a.scale_log2;
-  __syncthreads();
-  float qv[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) qv[e] = act ? qs[c * VEC + e] : 0.f;
-  int n = *a.pos + 1;
-  n = n < 1 ? 1 : (n < a.Tmax ? n : a.Tmax);   // a position outside [0, Tmax) violates the contract
-  const int kvbh = b * a.Hkv + h / (a.H / a.Hkv);   // grouped-query attention
-  const T* K = reinterpret_cast<const T*>(a.k) + (long long)kvbh * a.kv_bh + c * VEC;
-  const T* U = reinterpret_cast<const T*>(a.v) + (long long)kvbh * a.kv_bh + c * VEC;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-
-  float m = -INFINITY, l = 0.f, acc[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  const float alibi_l2 = a.alibi ? exp2f(-8.0f * (float)(h + 1) / (float)a.H) * 1.4426950408889634f : 0.f;
-  for (int k0 = 0; k0 < n; k0 += UNR * G) {
-    uint4 kv[UNR], uv[UNR];
+struct DecPass {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int UNR = 8;
+  static constexpr int G = DEC_THREADS / LPK;
+  const T* K; const T* U;
+  int n, g, c, D;
+  bool act;
+  __device__ __forceinline__ DecPass(const DecAttnArgs& a) {
+    const int tid = threadIdx.x, bh = blockIdx.x;
+    const int b = bh / a.H, h = bh - b * a.H;
+    D = a.D;
+    g = tid / LPK; c = tid - g * LPK;
+    act = c * VEC < D;                        // lanes past the row's chunks hold zeros
+    n = *a.pos + 1;
+    n = n < 1 ? 1 : (n < a.Tmax ? n : a.Tmax);   // a position outside [0, Tmax) violates the contract
+    const int kvbh = b * a.Hkv + h / (a.H / a.Hkv);   // grouped-query attention
+    K = reinterpret_cast<const T*>(a.k) + (long long)kvbh * a.kv_bh + c * VEC;
+    U = reinterpret_cast<const T*>(a.v) + (long long)kvbh * a.kv_bh + c * VEC;
+  }
+  __device__ __forceinline__ void load(int k0, uint4 (&kv)[UNR], uint4 (&uv)[UNR]) const {
+    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int k = k0 + u * G + g;
       const bool in = act && k < n;
       kv[u] = in ? *reinterpret_cast<const uint4*>(K + (long long)k * D) : z;
       uv[u] = in ? *reinterpret_cast<const uint4*>(U + (long long)k * D) : z;
+    }
+  }
+};
+
+// Everything after the prologue: scores, online softmax and U sums of the
+// group's keys (batch 0 already in kv / uv), then the combine of the groups.
+// qs holds the query times scale_log2 (fp32, LDS).  Key position newpos (when
+// knew is given) is taken from knew / unew in LDS instead of the cache.
+template <typename T, int LPK>
+__device__ __forceinline__ void dec_attend(const DecAttnArgs& a, const DecPass<T, LPK>& P, const float* qs,
+                                           uint4 (&kv)[DecPass<T, LPK>::UNR], uint4 (&uv)[DecPass<T, LPK>::UNR],
+                                           const T* knew, const T* unew, int newpos) {
+  typedef DecPass<T, LPK> PS;
+  constexpr int VEC = PS::VEC, UNR = PS::UNR, G = PS::G;
+  __shared__ float gacc[G * LPK * VEC];   // per group: U-weighted sums, columns [0, LPK VEC)
+  __shared__ float gm[G], gl[G];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H, D = a.D;
+  const int g = P.g, c = P.c, n = P.n;
+  float qv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) qv[e] = P.act ? qs[c * VEC + e] : 0.f;
+
+  float m = -INFINITY, l = 0.f, acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  const float alibi_l2 = a.alibi ? exp2f(-8.0f * (float)(h + 1) / (float)a.H) * 1.4426950408889634f : 0.f;
+  for (int k0 = 0; k0 < n; k0 += UNR * G) {
+    if (k0 > 0) P.load(k0, kv, uv);
+    if (knew && P.act && newpos >= k0 && newpos < k0 + UNR * G) {   // uniform range test
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (k0 + u * G + g == newpos) {
+          kv[u] = *reinterpret_cast<const uint4*>(knew + c * VEC);
+          uv[u] = *reinterpret_cast<const uint4*>(unew + c * VEC);
+        }
     }
     float s[UNR];
     float mb = -INFINITY;
@@ -830,6 +862,108 @@ __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a)
       den = fmaf(w, gl[gg], den);
     }
     orow[d] = from_f32<T>(num / den);
+  }
+}
+
+// LDS writes of the prologue done, then a barrier that does not wait for the
+// cache loads still in flight.
+__device__ __forceinline__ void dec_prologue_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, int LPK>
+__global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(DecAttnArgs a) {
+  typedef DecPass<T, LPK> PS;
+  __shared__ float qs[128];
+  const PS P(a);
+  const int bh = blockIdx.x;
+  const T* q = reinterpret_cast<const T*>(a.q) + (long long)bh * a.D;
+  float qd = 0.f;
+  if (threadIdx.x < a.D) qd = to_f32(q[threadIdx.x]) * a.scale_log2;   // D <= 128 < DEC_THREADS
+  uint4 kv[PS::UNR], uv[PS::UNR];
+  P.load(0, kv, uv);
+  if (threadIdx.x < a.D) qs[threadIdx.x] = qd;
+  dec_prologue_barrier();
+  dec_attend<T, LPK>(a, P, qs, kv, uv, nullptr, nullptr, -1);
+}
+
+// The same attention fed by the K-slices of the Q|K|U product instead of a
+// finished q and an appended cache row: part[s][B][3C] (C = H D, head h's q,
+// k, u at columns hD, C + hD, 2C + hD).  The block adds its head's slices in
+// slice order with the bias in fp32 and rounds to bf16, exactly the values
+// the product's own epilogue stores; it appends k and u at *pos of the caches
+// (for the later steps) and attends with the new row taken from LDS in place
+// of the cache row its loads read (before the append, or not yet visible).
+template <int LPK, int NS>
+__global__ void __launch_bounds__(DEC_THREADS) attn_decode_slices_kernel(DecAttnArgs a, const float* __restrict__ part,
+                                                                        const bf16* __restrict__ bias) {
+  typedef DecPass<bf16, LPK> PS;
+  __shared__ float qs[128];
+  __shared__ __align__(16) bf16 kn[128];
+  __shared__ __align__(16) bf16 un[128];
+  const PS P(a);
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H, D = a.D, C3 = 3 * a.H * D;
+  const int pos = *a.pos;
+  const bool keep = pos >= 0 && pos < a.Tmax;   // the cache row the step appends
+  // slices of this thread's q / k / u element (threads past 3D take none)
+  const int i = threadIdx.x, which = i / D, d = i - which * D;
+  const bool mine = i < 3 * D;
+  const int col = which * (C3 / 3) + h * D + d;
+  float ps[NS];   // every slice's load issued before the first add
+  float bv = 0.f;
+  if (mine) {
+    const float* p = part + (long long)b * C3 + col;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ps[s] = p[(long long)s * a.B * C3];
+    if (bias) bv = to_f32(bias[col]);
+  }
+  uint4 kv[PS::UNR], uv[PS::UNR];
+  P.load(0, kv, uv);
+  if (mine) {
+    float t = ps[0];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) t += ps[s];
+    t += bv;
+    const bf16 r = from_f32<bf16>(t);
+    bf16* row = reinterpret_cast<bf16*>(const_cast<void*>(which == 1 ? a.k : a.v)) + (long long)bh * a.kv_bh +
+                (long long)pos * D;
+    if (which == 0) {
+      qs[d] = to_f32(r) * a.scale_log2;
+    } else {
+      (which == 1 ? kn : un)[d] = r;
+      if (keep) row[d] = r;
+    }
+  }
+  dec_prologue_barrier();
+  // the new row from LDS: the cache copy a batch reads may predate the append
+  dec_attend<bf16, LPK>(a, P, qs, kv, uv, kn, un, keep ? pos : -1);
+}
+
+template <int LPK>
+static hipError_t dec_slices_s(const DecAttnArgs& a, const float* part, int S, const bf16* bias, hipStream_t st) {
+  const dim3 grid(a.B * a.H), block(DEC_THREADS);
+  switch (S) {
+    case 1: hipLaunchKernelGGL((attn_decode_slices_kernel<LPK, 1>), grid, block, 0, st, a, part, bias); break;
+    case 2: hipLaunchKernelGGL((attn_decode_slices_kernel<LPK, 2>), grid, block, 0, st, a, part, bias); break;
+    case 3: hipLaunchKernelGGL((attn_decode_slices_kernel<LPK, 3>), grid, block, 0, st, a, part, bias); break;
+    case 4: hipLaunchKernelGGL((attn_decode_slices_kernel<LPK, 4>), grid, block, 0, st, a, part, bias); break;
+    case 6: hipLaunchKernelGGL((attn_decode_slices_kernel<LPK, 6>), grid, block, 0, st, a, part, bias); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_decode_slices(const DecAttnArgs& a, const float* part, int S, const void* bias,
+                                          hipStream_t st) {
+  if (!part || S <= 0 || a.Tmax > DEC_MAXT || a.D > 128 || a.D % 8 || a.Hkv != a.H || a.alibi)
+    return hipErrorInvalidValue;
+  const int nch = a.D / 8;
+  const int lpk = nch <= 2 ? 2 : (nch <= 4 ? 4 : (nch <= 8 ? 8 : 16));
+  const bf16* bb = static_cast<const bf16*>(bias);
+  switch (lpk) {
+    case 2: return dec_slices_s<2>(a, part, S, bb, st);
+    case 4: return dec_slices_s<4>(a, part, S, bb, st);
+    case 8: return dec_slices_s<8>(a, part, S, bb, st);
+    default: return dec_slices_s<16>(a, part, S, bb, st);
   }
 }
 

@@ -334,8 +334,123 @@ int run_blocks_llama(const Pass& s) {
 
 // Embedding and the L blocks; leaves the fp32 residual stream in ws.x (with
 // no blocks, ws.a already holds ln_f of the embedding).
+// Decode steps of bf16 pre-LN GPT-2 blocks split the K range of their three
+// weight-streaming products into slices written as fp32 partial products
+// (no block waits on another): the Q|K|U slices feed the decode attention,
+// which finishes q, k, u and appends the cache row; the slices of c_proj and
+// of mlp.c_proj feed a residual update fused with the LayerNorm that follows
+// it (LN2, then LN1 of the next block or ln_f after the last one).  c_fc
+// keeps its own GELU epilogue.  Slice counts: K / S a whole number of
+// 64-deep stages from {2, 4, 6, 8, 12}, S M N within the partial buffer.
+struct StepSplit { int qkv, proj, fcproj; };
+
+static int pick_split(int K, int M, int N, size_t cap, const int* prefs, int n) {
+  for (int i = 0; i < n; ++i) {
+    const int S = prefs[i];
+    if (K % S != 0) continue;
+    const int d = K / S;
+    if (d != 128 && d != 256 && d != 384 && d != 512 && d != 768) continue;
+    if ((size_t)S * M * N <= cap) return S;
+  }
+  return 0;
+}
+
+bool step_split(const gpt_config* c, int M, const Plan& pl, StepSplit* sp) {
+  if (c->dtype != GPT_BF16 || c->arch != 0 || c->post_ln != 0 || c->n_layer <= 0 || M > 64 || !pl.skpart)
+    return false;
+  const int C = c->n_embd, F = c->n_ff, D = C / c->n_head;
+  if (C % 128 || F % 128 || D % 8 || C > 1024 || kv_heads(c) != c->n_head) return false;
+  const size_t cap = (size_t)SK_PART_TILES * 64 * 32;
+  static const int pq[] = {3, 6, 2, 4, 1}, pp[] = {6, 3, 4, 2, 1}, pf[] = {8, 12, 6, 4, 2, 1};
+  StepSplit r{pick_split(C, M, 3 * C, cap, pq, 5), pick_split(C, M, C, cap, pp, 5), pick_split(F, M, C, cap, pf, 6)};
+  if (!r.qkv || !r.proj || !r.fcproj) return false;
+  if (sp) *sp = r;
+  return true;
+}
+
+// The residual LayerNorms also read the weights of the two products that
+// follow them (LN2: c_fc and mlp.c_proj; LN1: the next block's c_attn and
+// c_proj) with blocks of their own, so those products find them cached.
+static void prefetch(LnArgs& la, const void* w0, size_t b0, const void* w1, size_t b1) {
+  la.pf[0] = w0; la.pf_bytes[0] = b0; la.pf_blocks[0] = w0 ? resid_ln_prefetch_blocks(b0) : 0;
+  la.pf[1] = w1; la.pf_bytes[1] = b1; la.pf_blocks[1] = w1 ? resid_ln_prefetch_blocks(b1) : 0;
+}
+
+int run_blocks_step_split(const Pass& s, const StepSplit& sp) {
+  const gpt_config* cfg = s.cfg;
+  const Params& P = s.P;
+  const int B = s.B, M = B, C = cfg->n_embd, F = cfg->n_ff;
+  const int H = cfg->n_head, D = C / H, L = cfg->n_layer;
+  float* x = at<float>(s.ws, s.pl.x);
+  void* a = at<char>(s.ws, s.pl.a);
+  void* o = at<char>(s.ws, s.pl.o);
+  void* h = at<char>(s.ws, s.pl.h);
+  float* part = at<float>(s.ws, s.pl.skpart);
+  const size_t cap = (size_t)SK_PART_TILES * 64 * 32;
+  const long long cache_layer = (long long)B * H * s.Tmax * D;
+  SkinnyWs skw{part, SK_PART_TILES, at<int>(s.ws, s.pl.skcnt), SK_COUNTERS};
+
+  LnArgs la{};
+  la.M = M; la.C = C; la.T_seq = 1; la.eps = cfg->ln_eps;
+  la.idx = s.idx; la.wte = P.at(0); la.wpe = P.at(P.wpe()); la.vocab = cfg->vocab; la.ctx = cfg->ctx;
+  la.pos = s.pos;
+  la.x = x; la.in_mul = 1; la.in_add = 0;
+  la.g = P.at(P.layer(0).ln1_g); la.b = P.at(P.layer(0).ln1_b);
+  la.out = a;
+  la.zero = skw.cnt; la.zero_n = skw.cnt_len;   // counters of the other skinny products (c_fc uses none)
+  GPT_TRY(launch_embed_ln(GPT_BF16, la, s.st));
+  la.idx = nullptr; la.pos = nullptr; la.zero = nullptr; la.zero_n = 0;
+  la.part = part;
+
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  for (int l = 0; l < L; ++l) {
+    const LayerP w = P.layer(l);
+    const bool last = l == L - 1;
+    GPT_TRY(mark(s, GPT_KERNEL_QKV, last, true));
+    GPT_TRY(launch_skinny_slices(a, P.at(w.attn_w), M, 3 * C, C, sp.qkv, part, cap, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_QKV, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, true));
+    DecAttnArgs da{};
+    da.q = nullptr;
+    da.k = static_cast<char*>(s.kc) + l * cache_layer * 2;
+    da.v = static_cast<char*>(s.vc) + l * cache_layer * 2;
+    da.kv_bh = (long long)s.Tmax * D; da.Tmax = s.Tmax; da.pos = s.pos;
+    da.o = o; da.o_ld = C; da.B = B; da.H = H; da.D = D; da.scale_log2 = scale_log2; da.Hkv = H;
+    GPT_TRY(launch_attention_decode_slices(da, part, sp.qkv, P.at(w.attn_b), s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_ATTN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, true));
+    GPT_TRY(launch_skinny_slices(o, P.at(w.proj_w), M, C, C, sp.proj, part, cap, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_PROJ, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, true));
+    la.nsplit = sp.proj; la.rbias = P.at(w.proj_b);
+    la.g = P.at(w.ln2_g); la.b = P.at(w.ln2_b);
+    prefetch(la, P.at(w.fc_w), (size_t)F * C * 2, P.at(w.fcproj_w), (size_t)C * F * 2);
+    GPT_TRY(launch_resid_layernorm(la, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_LN, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, true));
+    GPT_TRY(launch_linear(GPT_BF16, a, C, P.at(w.fc_w), C, P.at(w.fc_b), M, F, C, h, F, cfg->activation ? 2 : 1, 0,
+                          s.st, &skw));
+    GPT_TRY(mark(s, GPT_KERNEL_FC, last, false));
+    GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, true));
+    GPT_TRY(launch_skinny_slices(h, P.at(w.fcproj_w), M, C, F, sp.fcproj, part, cap, s.st));
+    GPT_TRY(mark(s, GPT_KERNEL_FCPROJ, last, false));
+    // ln_1 of the next block, or ln_f after the last one
+    la.nsplit = sp.fcproj; la.rbias = P.at(w.fcproj_b);
+    la.g = P.at(last ? P.lnf_g() : P.layer(l + 1).ln1_g);
+    la.b = P.at(last ? P.lnf_b() : P.layer(l + 1).ln1_b);
+    if (last) prefetch(la, nullptr, 0, nullptr, 0);
+    else prefetch(la, P.at(P.layer(l + 1).attn_w), (size_t)3 * C * C * 2, P.at(P.layer(l + 1).proj_w), (size_t)C * C * 2);
+    GPT_TRY(launch_resid_layernorm(la, s.st));
+  }
+  return GPT_OK;
+}
+
 int run_blocks(const Pass& s) {
   if (s.cfg->arch == 1) return run_blocks_llama(s);
+  if (s.mode == STEP && !s.xs) {
+    StepSplit sp;
+    if (step_split(s.cfg, s.B, s.pl, &sp)) return run_blocks_step_split(s, sp);
+  }
   const gpt_config* cfg = s.cfg;
   const Params& P = s.P;
   const int dt = cfg->dtype, B = s.B, T = s.T, M = B * T, C = cfg->n_embd, F = cfg->n_ff;
@@ -605,7 +720,7 @@ int decode_step_impl(const gpt_config* cfg, const void* params, const int32_t* t
   s = run_blocks(ps);
   if (s != GPT_OK) return s;
   void* a = at<char>(ws, pl.a);
-  if (!rows_final(cfg)) {
+  if (!rows_final(cfg) && !step_split(cfg, B, pl, nullptr)) {   // the split step applied ln_f already
     s = final_norm(ps, B, 1, 0, a);
     if (s != GPT_OK) return s;
   }

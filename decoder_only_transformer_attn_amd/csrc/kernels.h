@@ -39,6 +39,15 @@ struct LnArgs {
   int ident;                           // embedding: out = x itself (no LayerNorm; post-LN models)
   int write_x;                         // LayerNorm: the normalised row also replaces its x row (post-LN)
   int rms;                             // RMSNorm: no mean centring (b is then NULL: no bias)
+  // residual LayerNorm (launch_resid_layernorm): x += sum of the nsplit fp32
+  // slices part[s][M][C] (slice order) + rbias, then the LayerNorm of the new x
+  const float* part; int nsplit; const void* rbias;
+  // ... and pf_blocks[r] more blocks per byte range pf[r] (r = 0, 1; the
+  // next products' weights, resid_ln_prefetch_blocks(pf_bytes[r]) blocks)
+  // that read it so that those products find it cached; the words read are
+  // folded into one value stored only through pf_sink (null in the library:
+  // it only keeps the loads from being dropped)
+  const void* pf[2]; size_t pf_bytes[2]; int pf_blocks[2]; uint32_t* pf_sink;
 };
 
 // Attention of one new query per (b, h) over positions 0 .. *pos of the cache.
@@ -91,11 +100,20 @@ struct SkinnyWs {
 
 hipError_t launch_embed_ln(int dtype, const LnArgs& a, hipStream_t st);
 hipError_t launch_layernorm(int dtype, const LnArgs& a, hipStream_t st);
+// bf16 only, at most 12 slices: the residual update of a split product
+// followed by the LayerNorm that reads it (one row per block).
+hipError_t launch_resid_layernorm(const LnArgs& a, hipStream_t st);
+int resid_ln_prefetch_blocks(size_t nbytes);
 hipError_t launch_linear(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M, int N,
                          int K, void* out, int ldo, int act, int out_f32, hipStream_t st,
                          const SkinnyWs* sk = nullptr);
 hipError_t launch_linear_resid(int dtype, const void* A, int lda, const void* W, int ldw, const void* bias, int M,
                                int N, int K, float* x, int ldx, hipStream_t st, const SkinnyWs* sk = nullptr);
+// bf16 products of at most 64 rows with K split into S slices (K / S one of
+// 128, 256, 384, 512, 768; rows contiguous): slice s is written as the raw
+// fp32 partial product part[s][M][N] (S M N <= part_floats), no bias.
+hipError_t launch_skinny_slices(const void* A, const void* W, int M, int N, int K, int S, float* part,
+                                size_t part_floats, hipStream_t st);
 hipError_t launch_qkv(int dtype, const QKVArgs& a, hipStream_t st, const SkinnyWs* sk = nullptr);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 // Vocabulary tiles of the head's partials for M rows (CE or argmax mode).
@@ -111,6 +129,10 @@ hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int 
 hipError_t launch_argmax_reduce(int M, int ntiles, const float* part_max, const int32_t* part_idx, int32_t* next_tok,
                                 int32_t* pos, int set_pos, hipStream_t st);
 hipError_t launch_attention_decode(int dtype, const DecAttnArgs& a, hipStream_t st);
+// bf16, Hkv = H, no ALiBi: the decode attention fed by the S K-slices of the
+// Q|K|U product (part[s][B][3C], fp32, no bias); appends k and u at *pos.
+hipError_t launch_attention_decode_slices(const DecAttnArgs& a, const float* part, int S, const void* bias,
+                                          hipStream_t st);
 // Next-token sampling of B rows of logits (one block per row).
 struct SampleArgs {
   const void* logits; long long ld;    // [B, ld] in the compute dtype, V valid columns

@@ -111,6 +111,132 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   }
 }
 
+// Residual update of a K-split product and the LayerNorm after it, one row
+// per 64-thread block: x[row] += (sum over s in order of part[s][row]) +
+// bias, in fp32 (the same x + (v + b) form as the products' own residual
+// epilogue), the new row written back, then normalised exactly as
+// ln_rows_kernel does.  NS = the number of slices (all their loads are issued
+// before the first add).
+// Block j >= M of the residual LayerNorm: share j of the prefetch ranges
+// (range 0's blocks first), 16 bytes per lane and instruction, every load
+// issued before the first use.
+constexpr int PF_LOADS = 48;   // 48 KB per block
+__device__ __forceinline__ void prefetch_share(const LnArgs& a, int j) {
+  const int r = j < a.pf_blocks[0] ? 0 : 1;
+  const int share = r == 0 ? j : j - a.pf_blocks[0];
+  const char* base = static_cast<const char*>(a.pf[r]);
+  const size_t nb = a.pf_bytes[r] & ~(size_t)15;
+  const size_t off = (size_t)share * PF_LOADS * 1024 + (size_t)threadIdx.x * 16;
+  uint4 v[PF_LOADS];
+#pragma unroll
+  for (int i = 0; i < PF_LOADS; ++i) {
+    const size_t o = off + (size_t)i * 1024;
+    v[i] = o < nb ? *reinterpret_cast<const uint4*>(base + o) : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < PF_LOADS; ++i) acc ^= v[i].x ^ v[i].w;
+  if (a.pf_sink) a.pf_sink[threadIdx.x] = acc;
+}
+
+template <int NCH, int NS>
+__global__ void __launch_bounds__(64) resid_ln_kernel(LnArgs a) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  if (row >= a.M) {
+    prefetch_share(a, row - a.M);
+    return;
+  }
+  const int C = a.C;
+  const bf16* __restrict__ g = reinterpret_cast<const bf16*>(a.g);
+  const bf16* __restrict__ bta = reinterpret_cast<const bf16*>(a.b);
+  const bf16* __restrict__ rb = reinterpret_cast<const bf16*>(a.rbias);
+  float* __restrict__ xr = a.x + (size_t)row * C;
+  float v[NCH][4], g4[NCH][4], gb4[NCH][4];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {   // gain and bias with the first loads, not after the reductions
+    const int c = (j * 64 + lane) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { g4[j][e] = 0.f; gb4[j][e] = 0.f; }
+    if (c < C) {
+      load4(g + c, g4[j]);
+      if (bta) load4(bta + c, gb4[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    if (c < C) {
+      float x4[4], b4[4] = {0.f, 0.f, 0.f, 0.f}, p4[NS][4];
+      load4(xr + c, x4);
+      if (rb) load4(rb + c, b4);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) load4(a.part + ((size_t)s * a.M + row) * C + c, p4[s]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = p4[0][e];
+#pragma unroll
+        for (int s = 1; s < NS; ++s) t += p4[s][e];
+        v[j][e] = x4[e] + (t + b4[e]);
+      }
+      store4(xr + c, v[j]);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+    if ((j * 64 + lane) * 4 < C) s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+  const float mean = wave_sum(s) / (float)C;
+  float s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+    if ((j * 64 + lane) * 4 < C)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { float d = v[j][e] - mean; s2 += d * d; }
+  const float var = wave_sum(s2) / (float)C;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  bf16* __restrict__ orow = reinterpret_cast<bf16*>(a.out) + (size_t)row * C;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    if (c < C) {
+      float o4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (v[j][e] - mean) * rstd * g4[j][e] + gb4[j][e];
+      store4(orow + c, o4);
+    }
+  }
+}
+
+template <int NCH>
+static hipError_t launch_resid_ln_c(const LnArgs& a, hipStream_t st) {
+  const dim3 grid(a.M + a.pf_blocks[0] + a.pf_blocks[1]), block(64);
+  switch (a.nsplit) {
+    case 1: hipLaunchKernelGGL((resid_ln_kernel<NCH, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((resid_ln_kernel<NCH, 2>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((resid_ln_kernel<NCH, 3>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((resid_ln_kernel<NCH, 4>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((resid_ln_kernel<NCH, 6>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((resid_ln_kernel<NCH, 8>), grid, block, 0, st, a); break;
+    case 12: hipLaunchKernelGGL((resid_ln_kernel<NCH, 12>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Prefetch blocks for nbytes of weights (48 KB each).
+int resid_ln_prefetch_blocks(size_t nbytes) { return (int)((nbytes + PF_LOADS * 1024 - 1) / (PF_LOADS * 1024)); }
+
+hipError_t launch_resid_layernorm(const LnArgs& a, hipStream_t st) {
+  if (!a.part || !a.x || !a.out || !a.g || a.M <= 0 || a.C <= 0 || a.C % 4) return hipErrorInvalidValue;
+  for (int r = 0; r < 2; ++r)   // each range: no blocks, or just enough to cover it
+    if (a.pf_blocks[r] != (a.pf[r] ? resid_ln_prefetch_blocks(a.pf_bytes[r]) : 0)) return hipErrorInvalidValue;
+  if (a.C <= 256) return launch_resid_ln_c<1>(a, st);
+  if (a.C <= 512) return launch_resid_ln_c<2>(a, st);
+  if (a.C <= 1024) return launch_resid_ln_c<4>(a, st);
+  return hipErrorInvalidValue;
+}
+
 template <typename T, bool EMBED>
 static hipError_t launch_ln_t(const LnArgs& a, hipStream_t st) {
   dim3 grid((a.M + 3) / 4), block(256);

@@ -168,8 +168,9 @@ def test_small_bf16_decode(B):
 
 @pytest.mark.parametrize("B", [5, 64])
 def test_bf16_decode_split_k(B):
-    # n_ff = 1536: the skinny fc-projection of a step (K = 1536) is split over
-    # two blocks per column tile, whose partial sums meet in the workspace
+    # n_embd = 128, n_ff = 1536: the step's products are written as K-slices
+    # (the fc-projection's K = 1536 in 12), which the attention and the
+    # residual LayerNorms add in slice order
     cfg = synth.GPTConfig(vocab=300, ctx=64, n_embd=128, n_head=2, n_layer=2, n_ff=1536, dtype=synth.BF16)
     params = synth.make_params(cfg, seed=8, cfg_id=10, init="stress")
     prompt = synth.make_ids(cfg, B, 9, seed=8, cfg_id=10)
@@ -218,14 +219,16 @@ def test_gpt2_bf16_decode_agrees_with_forward(gpt2_decode_run):
     assert err <= 1e-1
 
 
-@pytest.mark.parametrize("n_ff", [256, 1536])
-def test_decode_step_graph_replay_matches_eager(n_ff):
+@pytest.mark.parametrize("n_embd,n_ff", [(64, 256), (64, 1536), (128, 1536)])
+def test_decode_step_graph_replay_matches_eager(n_embd, n_ff):
     # one decode step captured in a HIP graph and replayed (the position is
     # read on the device), with eager work and synchronisations between
     # replays; every replay's tokens and logits equal the eager path's
-    # (n_ff = 1536: split-K products, whose counters the step clears itself)
+    # (n_ff = 1536: split-K products, whose counters the step clears itself;
+    # n_embd = 128: the step's products written as K-slices, reduced by the
+    # attention and the residual LayerNorms)
     lib = _lib()
-    cfg = synth.GPTConfig(vocab=257, ctx=64, n_embd=64, n_head=2, n_layer=2, n_ff=n_ff, dtype=synth.BF16)
+    cfg = synth.GPTConfig(vocab=257, ctx=64, n_embd=n_embd, n_head=2, n_layer=2, n_ff=n_ff, dtype=synth.BF16)
     params = synth.make_params(cfg, seed=6, cfg_id=9, init="stress")
     prompt = torch.from_numpy(synth.make_ids(cfg, 4, 10, seed=6, cfg_id=9)).cuda()
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
