@@ -33,6 +33,15 @@ __device__ __forceinline__ void store4(bf16* p, const float (&v)[4]) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
+// Four raw elements (8 bytes of bf16 or 16 of fp32), converted at use.
+template <typename T> struct Raw4 { typedef uint2 type; };
+template <> struct Raw4<float> { typedef float4 type; };
+__device__ __forceinline__ void unpack4(const uint2& q, float (&o)[4]) {
+  o[0] = __uint_as_float(q.x << 16); o[1] = __uint_as_float(q.x & 0xffff0000u);
+  o[2] = __uint_as_float(q.y << 16); o[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack4(const float4& q, float (&o)[4]) { o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w; }
+
 // NCH = number of 4-float chunks per lane; C <= 256 * NCH.
 template <typename T, int NCH, bool EMBED>
 __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
@@ -44,6 +53,18 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   const int C = a.C;
   const T* __restrict__ g = reinterpret_cast<const T*>(a.g);
   const T* __restrict__ bta = reinterpret_cast<const T*>(a.b);
+  // gain and bias requested with the row, not after the reductions
+  typedef typename Raw4<T>::type R;
+  R graw[NCH], braw[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    graw[j] = R{}; braw[j] = R{};
+    if (c < C && !(EMBED && a.ident)) {
+      graw[j] = *reinterpret_cast<const R*>(g + c);
+      if (bta) braw[j] = *reinterpret_cast<const R*>(bta + c);
+    }
+  }
   float v[NCH][4];
   if (EMBED) {
     float* __restrict__ xr = a.x + (size_t)row * C;
@@ -100,9 +121,9 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(LnArgs a) {
   for (int j = 0; j < NCH; ++j) {
     const int c = (j * 64 + lane) * 4;
     if (c < C) {
-      float g4[4], b4[4] = {0.f, 0.f, 0.f, 0.f}, o4[4];
-      load4(g + c, g4);
-      if (bta) load4(bta + c, b4);
+      float g4[4], b4[4], o4[4];
+      unpack4(graw[j], g4);
+      unpack4(braw[j], b4);   // zero without a bias
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = (v[j][e] - mean) * rstd * g4[e] + b4[e];
       store4(orow + c, o4);
