@@ -1147,14 +1147,20 @@ hipError_t launch_gemm_f32_splitk(int dtype, const void* A, int lda, const void*
 
 // bf16 heads for C = 768: 256 (vocab) x 256 (token) blocks of eight 128 x 64
 // waves for many tokens (128 flops per byte brought into LDS), 192 x 128
-// blocks of four 96 x 64 waves in argmax mode and for few tokens (decode).
+// blocks of four 96 x 64 waves for the rest, except a decode step's argmax
+// over at most 64 tokens: there the head is a stream of the token table, and
+// 256 x 64 blocks of four 64 x 64 waves in three stages keep 120 KB of it in
+// flight per CU with one block per CU (197 blocks for V = 50257: one round).
 constexpr int HEAD_BIG_MIN_TOKENS = 2048;
 static bool head_big(int dtype, int M, int C, bool argmax) {
   return dtype != 0 && C == 768 && !argmax && M >= HEAD_BIG_MIN_TOKENS;
 }
+static bool head_stream(int dtype, int M, int C, bool argmax) { return dtype != 0 && C == 768 && argmax && M <= 64; }
 
 int head_ntiles(int dtype, int M, int V, int C, bool argmax) {
-  const int bn = dtype == 0 ? 64 : (C == 768 ? (head_big(dtype, M, C, argmax) ? 256 : 192) : 256);
+  const int bn = dtype == 0 ? 64
+                            : (C == 768 ? (head_big(dtype, M, C, argmax) || head_stream(dtype, M, C, argmax) ? 256 : 192)
+                                        : 256);
   return (V + bn - 1) / bn;
 }
 
@@ -1191,6 +1197,8 @@ hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int 
     if (C == 768) {
       if (head_big(dtype, M, C, part_idx != nullptr))
         return run_head_dma<256, 256, 128, 64, 2, 64>((const bf16*)wte, (const bf16*)A, V, M, ha, st);
+      if (head_stream(dtype, M, C, part_idx != nullptr))
+        return run_head_dma<256, 64, 64, 64, 3, 64>((const bf16*)wte, (const bf16*)A, V, M, ha, st);
       return run_head_dma<192, 128, 96, 64, 2, 64>((const bf16*)wte, (const bf16*)A, V, M, ha, st);
     }
     if (C % 64 == 0)

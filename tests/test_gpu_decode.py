@@ -179,6 +179,19 @@ def test_bf16_decode_split_k(B):
     check_against_oracle(cfg, params, prompt, toks, z, [0, B - 1], bf16_tol, bf16_band)
 
 
+@pytest.mark.parametrize("B", [5, 64])
+def test_bf16_decode_c768(B):
+    # GPT-2 widths (C = 768, 12 heads, F = 3072) with one block and a small
+    # vocabulary: the step's K-sliced products at their real depths, and the
+    # argmax head of at most 64 tokens (B = 5: a partial token tile)
+    cfg = dc.replace(synth.GPT2, vocab=1000, n_layer=1)
+    params = synth.make_params(cfg, seed=12, cfg_id=12, init="stress")
+    prompt = synth.make_ids(cfg, B, 11, seed=12, cfg_id=12)
+    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=8, Tmax=24, rows=[0, B - 1])
+    assert pos == 19
+    check_against_oracle(cfg, params, prompt, toks, z, [0, B - 1], bf16_tol, bf16_band)
+
+
 @pytest.fixture(scope="module")
 def gpt2_decode_run():
     cfg = synth.GPT2
