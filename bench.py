@@ -173,7 +173,10 @@ def bench_forward(args, w):
     ids = synth.make_ids(cfg, B, T, seed=42, cfg_id=args.workload)
     dev_params = lib.params_to_device(cfg, synth.pack(cfg, params))
     idx = torch.from_numpy(ids).cuda()
-    fwd = lib.Forward(cfg, B, T, want_logits=want_logits)
+    # logits rows padded to whole 128-byte lines (50304 for V = 50257): every
+    # value is still written, the pad columns are not
+    logits_ld = (args.logits_ld or (cfg.vocab + 63) // 64 * 64) if want_logits else 0
+    fwd = lib.Forward(cfg, B, T, want_logits=want_logits, logits_ld=logits_ld)
     stream = torch.cuda.current_stream()
     K = args.steps
     ev = Events(3 * K + 1)          # step boundaries 0..K, then head begin/end per step
@@ -217,7 +220,7 @@ def bench_forward(args, w):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w["name"], "global_batch": B, "seq_len": T, "parallelism": "single-gpu",
-                   "logits_written": want_logits},
+                   "logits_written": want_logits, **({"logits_row_stride": logits_ld} if want_logits else {})},
         "step_ms": {"median": round(pct(step_ms, 50), 4), "min": round(min(step_ms), 4),
                     "p90": round(pct(step_ms, 90), 4)},
         "mfma_frac_end_to_end": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -517,6 +520,8 @@ def main():
                          "(after the forward; off by default so a profile of the default run holds only the "
                          "forward's launches)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--logits-ld", type=int, default=0,
+                    help="row stride of the written logits (0: V rounded up to 64, whole 128-byte lines per row)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "

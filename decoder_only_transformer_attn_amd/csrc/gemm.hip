@@ -531,8 +531,13 @@ head_ce_dma_kernel(const bf16* __restrict__ wte, const bf16* __restrict__ act, i
         if (mr >= Mtok || v >= V) continue;
         bf16* const p = L + (long long)mr * ha.ld_logits + v;
         if (v + 8 <= V) {
-          const uint4 w4 = make_uint4(a.x, a.y, b.x, b.y);
-          __builtin_memcpy(p, &w4, 16);
+          if (ha.nt) {   // aligned rows: 16-byte pieces of whole lines, kept out of L2
+            const u32x4_t w4 = {a.x, a.y, b.x, b.y};
+            __builtin_nontemporal_store(w4, reinterpret_cast<u32x4_t*>(p));
+          } else {
+            const uint4 w4 = make_uint4(a.x, a.y, b.x, b.y);
+            __builtin_memcpy(p, &w4, 16);
+          }
         } else {
           for (int e = 0; v + e < V; ++e) {
             const uint32_t h = e < 2 ? a.x : e < 4 ? a.y : e < 6 ? b.x : b.y;
@@ -1177,7 +1182,11 @@ static hipError_t run_head_dma(const bf16* wte, const bf16* A, int V, int M, Hea
 hipError_t launch_head_ce(int dtype, const void* A, const void* wte, int M, int V, int C, void* logits,
                           long long ld_logits, float* part_max, float* part_sum, float* tgt, int32_t* part_idx,
                           const int32_t* targets, const int32_t* idx, int T_seq, hipStream_t st) {
-  HeadArgs ha{logits, ld_logits, part_max, part_sum, tgt, part_idx, 0, targets, idx, T_seq};
+  HeadArgs ha{logits, ld_logits, part_max, part_sum, tgt, part_idx, 0, targets, idx, T_seq, 0};
+  // rows on 128-byte lines (bf16: a stride of 64 elements, an aligned base):
+  // the tiles' row pieces are whole lines, written past L2 so that they do
+  // not evict the operand tiles the other CUs' main loops re-read
+  ha.nt = dtype != 0 && logits && ld_logits % 64 == 0 && reinterpret_cast<uintptr_t>(logits) % 128 == 0;
   if (dtype == 0) {
     constexpr int BM = 64, BN = 64;
     ha.ntiles = (V + BN - 1) / BN;

@@ -963,6 +963,7 @@ struct HeadArgs {
   const int32_t* targets;
   const int32_t* idx;
   int T_seq;
+  int nt;   // 1: logits rows start on 128-byte lines; stored non-temporally, whole lines
 };
 
 // (value, index) order of the greedy choice: larger value, then lower index.

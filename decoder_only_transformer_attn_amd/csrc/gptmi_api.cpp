@@ -818,17 +818,27 @@ const char* gpt_status_string(int status) {
 int gpt_forward(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
                 const int32_t* targets, void* logits, float* token_loss, float* mean_loss, void* ws,
                 size_t ws_bytes, void* stream) {
-  return gpt_forward_timed(cfg, params, idx, B, T, targets, logits, token_loss, mean_loss, ws, ws_bytes, stream,
+  return gpt_forward_timed(cfg, params, idx, B, T, targets, logits, 0, token_loss, mean_loss, ws, ws_bytes, stream,
                            nullptr, nullptr, -1);
 }
 
+int gpt_forward_ld(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                   const int32_t* targets, void* logits, long long ld_logits, float* token_loss, float* mean_loss,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return gpt_forward_timed(cfg, params, idx, B, T, targets, logits, ld_logits, token_loss, mean_loss, ws, ws_bytes,
+                           stream, nullptr, nullptr, -1);
+}
+
 int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
-                      const int32_t* targets, void* logits, float* token_loss, float* mean_loss, void* ws,
-                      size_t ws_bytes, void* stream, void* ev_begin, void* ev_end, int which) {
+                      const int32_t* targets, void* logits, long long ld_logits, float* token_loss,
+                      float* mean_loss, void* ws, size_t ws_bytes, void* stream, void* ev_begin, void* ev_end,
+                      int which) {
   int s = check_config(cfg);
   if (s != GPT_OK) return s;
   if (!params || !idx || !ws) return GPT_ERR_NULL;
   if (B <= 0 || T <= 0) return GPT_ERR_SHAPE;
+  if (ld_logits == 0) ld_logits = cfg->vocab;
+  if (ld_logits < cfg->vocab || ld_logits > (1LL << 31)) return GPT_ERR_SHAPE;
   if (T > cfg->ctx) return GPT_ERR_SEQ_TOO_LONG;
   if ((long long)B * T > (1LL << 24)) return GPT_ERR_SHAPE;
   const Plan pl = plan(cfg, B, T, false);
@@ -846,7 +856,7 @@ int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* 
   }
   float* tok = token_loss ? token_loss : at<float>(ws, pl.tok);
   GPT_TRY(mark(ps, GPT_KERNEL_HEAD, true, true));
-  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), M, V, C, logits, V, at<float>(ws, pl.pmax),
+  GPT_TRY(launch_head_ce(cfg->dtype, a, ps.P.at(ps.P.head_w()), M, V, C, logits, ld_logits, at<float>(ws, pl.pmax),
                          at<float>(ws, pl.psum), at<float>(ws, pl.tgt), nullptr, targets, idx, T, ps.st));
   GPT_TRY(mark(ps, GPT_KERNEL_HEAD, true, false));
   GPT_TRY(launch_ce_reduce(M, pl.ntiles, at<float>(ws, pl.pmax), at<float>(ws, pl.psum), at<float>(ws, pl.tgt),

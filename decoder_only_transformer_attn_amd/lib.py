@@ -43,7 +43,8 @@ SIGNATURES = {
     "gpt_param_offsets": (_c_int, [_CFG, ctypes.POINTER(ctypes.c_int64), _c_int]),
     "gpt_workspace_bytes": (_c_int, [_CFG, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "gpt_forward": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "gpt_forward_timed": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+    "gpt_forward_ld": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_i64, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_forward_timed": (_c_int, [_CFG, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_i64, _vp, _vp, _vp, _sz, _vp,
                                    _vp, _vp, _c_int]),
     "gpt_status_string": (ctypes.c_char_p, [_c_int]),
     "gpt_debug_layernorm": (_c_int, [_CFG, _vp, _vp, _vp, _c_int, _vp, _vp]),
@@ -139,11 +140,26 @@ def forward(cfg, params, idx, targets=None, logits=None, token_loss=None, mean_l
             stream=None) -> None:
     """Enqueue gpt_forward on the stream.  All tensors are CUDA (HIP) tensors:
     params [param_count] (float32 or bf16), idx int32 [B,T], optional targets
-    int32 [B,T], logits [B,T,V], token_loss f32 [B,T], mean_loss f32 [1], ws uint8."""
+    int32 [B,T], logits [B,T,V] (rows may be further apart than V: a view of
+    [B,T,ld] storage goes to gpt_forward_ld), token_loss f32 [B,T], mean_loss
+    f32 [1], ws uint8."""
     B, T = idx.shape
-    check(load().gpt_forward(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets), _ptr(logits),
-                             _ptr(token_loss), _ptr(mean_loss), _ptr(ws), 0 if ws is None else ws.numel(),
-                             _stream(stream)))
+    check(load().gpt_forward_ld(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets),
+                                _ptr(logits), _logits_ld(logits, cfg), _ptr(token_loss), _ptr(mean_loss), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def _logits_ld(logits, cfg) -> int:
+    """Row stride of a logits tensor [..., V] whose rows are contiguous and
+    evenly spaced (0 when there is none)."""
+    if logits is None:
+        return 0
+    if logits.stride(-1) != 1 or logits.shape[-1] != cfg.vocab:
+        raise ValueError("logits rows must be [..., V] with unit column stride")
+    ld = logits.stride(-2) if logits.dim() >= 2 else cfg.vocab
+    if logits.dim() == 3 and logits.stride(0) != logits.shape[1] * ld:
+        raise ValueError("logits rows must be evenly spaced")
+    return ld
 
 
 def head_backward_workspace_bytes(cfg, B: int, T: int) -> int:
@@ -223,7 +239,7 @@ def forward_timed(cfg, params, idx, targets, logits, token_loss, mean_loss, ws, 
     """gpt_forward with hipEvent_t handles recorded around one kernel class."""
     B, T = idx.shape
     check(load().gpt_forward_timed(ctypes.byref(cfg_c(cfg)), _ptr(params), _ptr(idx), B, T, _ptr(targets),
-                                   _ptr(logits), _ptr(token_loss), _ptr(mean_loss), _ptr(ws),
+                                   _ptr(logits), _logits_ld(logits, cfg), _ptr(token_loss), _ptr(mean_loss), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream), ev_begin, ev_end,
                                    KERNEL[which]))
 
@@ -278,18 +294,24 @@ def _poison(t) -> None:
 class Forward:
     """Holds the output and workspace tensors for repeated gpt_forward calls on one shape."""
 
-    def __init__(self, cfg, B: int, T: int, want_logits: bool = True, device="cuda", poison: bool = False):
+    def __init__(self, cfg, B: int, T: int, want_logits: bool = True, device="cuda", poison: bool = False,
+                 logits_ld: int = 0):
         """poison: fill the workspace and the outputs with 0xFF bytes (NaN in
         bf16 and fp32), so that a read of anything the call did not write
-        first shows up in the results."""
+        first shows up in the results.  logits_ld: row stride of the logits
+        storage (>= V; 0 = V); self.logits is then the [B, T, V] view of
+        [B, T, logits_ld] storage, kept in self.logits_storage."""
         import torch
         self.cfg, self.B, self.T = cfg, B, T
         self.ws = torch.empty(workspace_bytes(cfg, B, T), dtype=torch.uint8, device=device)
-        self.logits = torch.empty((B, T, cfg.vocab), dtype=torch_dtype(cfg), device=device) if want_logits else None
+        ld = logits_ld or cfg.vocab
+        self.logits_storage = (torch.empty((B, T, ld), dtype=torch_dtype(cfg), device=device) if want_logits
+                               else None)
+        self.logits = self.logits_storage[..., :cfg.vocab] if want_logits else None
         self.token_loss = torch.empty((B, T), dtype=torch.float32, device=device)
         self.mean_loss = torch.empty((1,), dtype=torch.float32, device=device)
         if poison:
-            for t in (self.ws, self.logits, self.token_loss, self.mean_loss):
+            for t in (self.ws, self.logits_storage, self.token_loss, self.mean_loss):
                 if t is not None:
                     _poison(t)
 

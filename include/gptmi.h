@@ -139,6 +139,18 @@ int gpt_forward(const gpt_config* cfg, const void* params, const int32_t* idx, i
                 const int32_t* targets, void* logits, float* token_loss, float* mean_loss,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* gpt_forward with the logits rows ld_logits elements apart: logits is
+ * [B, T, ld_logits] with ld_logits >= V, columns V .. ld_logits - 1 of every
+ * row left untouched (ld_logits = V, or 0, is gpt_forward).  In bf16, a
+ * stride that is a multiple of 64 elements with a 128-byte aligned base puts
+ * every row on 128-byte lines; the head then writes whole lines and keeps
+ * them out of the L2 cache (for GPT-2, ld_logits = 50304: the logits then
+ * cost less time than dense rows of 50257).  Errors as gpt_forward, and
+ * GPT_ERR_SHAPE for ld_logits < V or > 2^31. */
+int gpt_forward_ld(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
+                   const int32_t* targets, void* logits, long long ld_logits, float* token_loss, float* mean_loss,
+                   void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel classes for gpt_forward_timed. */
 enum gpt_kernel {
   GPT_KERNEL_HEAD = 0,   /* tied head GEMM + cross-entropy partials (one launch per forward) */
@@ -150,12 +162,14 @@ enum gpt_kernel {
   GPT_KERNEL_LN = 6      /* ln_2 LayerNorm (last layer's launch) */
 };
 
-/* gpt_forward with a timing hook: ev_begin and ev_end (hipEvent_t, created by
- * the caller, nullable) are recorded on `stream` immediately before and after
- * the launch of kernel class `which`.  Everything else is gpt_forward. */
+/* gpt_forward_ld with a timing hook: ev_begin and ev_end (hipEvent_t,
+ * created by the caller, nullable) are recorded on `stream` immediately
+ * before and after the launch of kernel class `which`.  Everything else is
+ * gpt_forward_ld. */
 int gpt_forward_timed(const gpt_config* cfg, const void* params, const int32_t* idx, int B, int T,
-                      const int32_t* targets, void* logits, float* token_loss, float* mean_loss,
-                      void* ws, size_t ws_bytes, void* stream, void* ev_begin, void* ev_end, int which);
+                      const int32_t* targets, void* logits, long long ld_logits, float* token_loss,
+                      float* mean_loss, void* ws, size_t ws_bytes, void* stream, void* ev_begin, void* ev_end,
+                      int which);
 
 /* ---- greedy decoding with a key/value cache ----
  * "预训练一个 Mini GPT" (KV cache section, 第7步): a new token computes only

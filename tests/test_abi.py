@@ -82,6 +82,13 @@ def test_forward_validation_before_any_hip_call():
     assert _fwd(m, ws_bytes=16) == -5
     msg = lib.load().gpt_status_string(-3).decode()
     assert "context" in msg
+    # gpt_forward_ld: a logits row stride below V (0 means V) or past 2^31
+    L = lib.load()
+    c = lib.cfg_c(m)
+    for ld, want in [(m.vocab - 1, -4), (1 << 32, -4), (-5, -4)]:
+        assert L.gpt_forward_ld(ctypes.byref(c), 1, 1, 2, 4, None, None, ld, None, None, 1, 1 << 30, None) == want
+    assert L.gpt_forward_ld(ctypes.byref(c), None, 1, 2, 4, None, None, m.vocab + 3, None, None, 1, 1 << 30,
+                            None) == -1
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="dummy-pointer validation tests run only without a GPU")

@@ -26,12 +26,12 @@ def _lib():
     return lib
 
 
-def run_gpu(cfg, params, ids, targets=None, want_logits=True):
+def run_gpu(cfg, params, ids, targets=None, want_logits=True, logits_ld=0):
     lib = _lib()
     P = lib.params_to_device(cfg, synth.pack(cfg, params))
     idx = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     tg = None if targets is None else torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int32)).cuda()
-    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], want_logits, poison=True)
+    f = lib.Forward(cfg, ids.shape[0], ids.shape[1], want_logits, poison=True, logits_ld=logits_ld)
     logits, tok, mean = f(P, idx, tg)
     torch.cuda.synchronize()
     lg = None if logits is None else logits.float().cpu().numpy()
@@ -324,12 +324,13 @@ def test_gpt2_bf16_b8_t1024_parity(gpt2_inputs):
 def test_gpt2_bf16_b8_t1024_stress_all_sequences():
     # the full bench shape with the stress init (random biases and LayerNorm
     # gains/offsets), every sequence compared with the oracle element by
-    # element, and the mean loss against the oracle's mean over all of them
+    # element, and the mean loss against the oracle's mean over all of them;
+    # the logits rows 50304 apart, as the bench writes them
     cfg = synth.GPT2
     params = synth.make_params(cfg, seed=13, cfg_id=3, init="stress")
     P = synth.unpack_f64(cfg, params)
     ids = synth.make_ids(cfg, 8, 1024, seed=13, cfg_id=3)
-    lg, tok, mean = run_gpu(cfg, params, ids)
+    lg, tok, mean = run_gpu(cfg, params, ids, logits_ld=50304)
     assert np.isfinite(lg).all()
     ref_tok = []
     for b in range(8):
@@ -340,6 +341,28 @@ def test_gpt2_bf16_b8_t1024_stress_all_sequences():
     ref_mean = float(np.concatenate(ref_tok).mean())
     print(f"mean loss gpu {mean:.6f} oracle {ref_mean:.6f}")
     assert abs(mean - ref_mean) <= 1e-2
+
+
+@pytest.mark.parametrize("ld", [50304, 50257 + 7])
+def test_gpt2_bf16_logits_row_stride(gpt2_inputs, ld):
+    # logits rows ld apart (50304: whole 128-byte lines, stored past L2; an
+    # odd stride: the ordinary stores) hold exactly the dense rows' values,
+    # and the pad columns keep the poison the buffer was filled with
+    cfg, params, _ = gpt2_inputs
+    lib = _lib()
+    P = lib.params_to_device(cfg, synth.pack(cfg, params))
+    ids = synth.make_ids(cfg, 2, 1024, seed=5, cfg_id=3)
+    idx = torch.from_numpy(ids).cuda()
+    dense = lib.Forward(cfg, 2, 1024, poison=True)
+    pad = lib.Forward(cfg, 2, 1024, poison=True, logits_ld=ld)
+    dl, dt, dm = dense(P, idx)
+    pl, pt, pm = pad(P, idx)
+    torch.cuda.synchronize()
+    assert pad.logits.stride(1) == ld
+    assert torch.equal(dl.view(torch.int16), pl.view(torch.int16))
+    assert torch.equal(dt, pt) and torch.equal(dm, pm)
+    tail = pad.logits_storage[..., cfg.vocab:].contiguous().view(torch.int16)
+    assert bool((tail == -1).all()), "a pad column was written"
 
 
 def test_gpt2_bf16_ragged_stress(gpt2_inputs):
