@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "475a2dc412f7ac62ddab409a76994420c453393af5dd9914af7fc5d0907c75b8",
-                "bytes": 1871090091}
+HEAD_TRAFFIC = {"gemm_src_sha256": "a9cd35c06fec920cbe18c351ef6140712bd4bdd62849b30c124d13093827a814",
+                "bytes": 1798911670}
 
 
 def src_sha(rel):
