@@ -7,6 +7,7 @@ configurations max|dlogit| <= 5e-2 absolute, |dloss| <= 1e-2 absolute,
 per-token loss <= 5e-2 absolute.  Full-size GPT-2 runs compare whole sampled
 sequences (sequences are independent, so the oracle runs on those rows alone).
 """
+import dataclasses as dc
 import math
 
 import numpy as np
@@ -363,6 +364,26 @@ def test_gpt2_bf16_logits_row_stride(gpt2_inputs, ld):
     assert torch.equal(dt, pt) and torch.equal(dm, pm)
     tail = pad.logits_storage[..., cfg.vocab:].contiguous().view(torch.int16)
     assert bool((tail == -1).all()), "a pad column was written"
+
+
+@pytest.mark.parametrize("dtype,ld", [(synth.F32, 0), (synth.F32, 3), (synth.BF16, 0), (synth.BF16, 64)])
+def test_small_logits_row_stride(dtype, ld):
+    # strided logits rows for the other head kernels (fp32; bf16 below 2048
+    # tokens): the values equal the dense rows', the pad columns keep their poison
+    cfg = dc.replace(synth.MINI, dtype=dtype)
+    lib = _lib()
+    params = synth.make_params(cfg, seed=3, cfg_id=2)
+    P = lib.params_to_device(cfg, synth.pack(cfg, params))
+    ids = synth.make_ids(cfg, 3, 37, seed=3, cfg_id=2)
+    idx = torch.from_numpy(ids).cuda()
+    stride = (cfg.vocab + 63) // 64 * 64 + ld
+    dense = lib.Forward(cfg, 3, 37, poison=True)
+    pad = lib.Forward(cfg, 3, 37, poison=True, logits_ld=stride)
+    dl, dt, _ = dense(P, idx)
+    pl, pt, _ = pad(P, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(dl, pl) and torch.equal(dt, pt)
+    assert bool(torch.isnan(pad.logits_storage[..., cfg.vocab:].float()).all()), "a pad column was written"
 
 
 def test_gpt2_bf16_ragged_stress(gpt2_inputs):
