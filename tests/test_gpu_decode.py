@@ -192,6 +192,21 @@ def test_bf16_decode_c768(B):
     check_against_oracle(cfg, params, prompt, toks, z, [0, B - 1], bf16_tol, bf16_band)
 
 
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_decode_past_256_positions(dtype):
+    # a cache longer than one batch of the decode attention (8 keys per group
+    # of 32 groups: 256 positions): the steps cross position 256, so the new
+    # key is found in the second batch (bf16 at n_embd 128: the K-sliced step,
+    # whose new row comes from LDS; fp32: the general step)
+    cfg = synth.GPTConfig(vocab=300, ctx=320, n_embd=128, n_head=2, n_layer=2, n_ff=512, dtype=dtype)
+    params = synth.make_params(cfg, seed=21, cfg_id=11, init="stress")
+    prompt = synth.make_ids(cfg, 3, 250, seed=21, cfg_id=11)
+    toks, z, pos, _ = run_decode(cfg, params, prompt, steps=12, Tmax=300, rows=[0, 2])
+    assert pos == 262
+    tol, band = (fp32_tol, fp32_tol) if dtype == synth.F32 else (bf16_tol, bf16_band)
+    check_against_oracle(cfg, params, prompt, toks, z, [0, 2], tol, band)
+
+
 @pytest.fixture(scope="module")
 def gpt2_decode_run():
     cfg = synth.GPT2
