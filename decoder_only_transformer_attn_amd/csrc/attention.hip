@@ -848,20 +848,37 @@ __device__ __forceinline__ void dec_attend(const DecAttnArgs& a, const DecPass<T
   for (int e = 0; e < VEC; ++e) gacc[g * LPK * VEC + c * VEC + e] = acc[e];
   if (c == 0) { gm[g] = m; gl[g] = l; }
   __syncthreads();
-  // combine the groups: every group with keys has a finite maximum (group 0 holds key 0)
+  // combine the groups: every group with keys has a finite maximum (group 0
+  // holds key 0).  All threads take part: thread t sums the VEC groups of
+  // quarter t / DP for column t % DP, then the quarters are added in order.
+  constexpr int DP = LPK * VEC, QN = DEC_THREADS / DP;   // DP >= D columns, QN * VEC = G groups
+  __shared__ float pnum[DEC_THREADS], pden[DEC_THREADS];
   float M = gm[0];
 #pragma unroll
   for (int gg = 1; gg < G; ++gg) M = fmaxf(M, gm[gg]);
-  T* orow = reinterpret_cast<T*>(a.o) + (long long)b * a.o_ld + h * D;
-  for (int d = tid; d < D; d += DEC_THREADS) {
+  {
+    const int d = tid % DP, q = tid / DP;
     float num = 0.f, den = 0.f;
-#pragma unroll 8
-    for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const int gg = q * VEC + i;
       const float w = fast_exp2(gm[gg] - M);   // 0 for a group without keys
-      num = fmaf(w, gacc[gg * LPK * VEC + d], num);
+      num = fmaf(w, gacc[gg * DP + d], num);
       den = fmaf(w, gl[gg], den);
     }
-    orow[d] = from_f32<T>(num / den);
+    pnum[tid] = num;
+    pden[tid] = den;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float num = pnum[tid], den = pden[tid];
+#pragma unroll
+    for (int q = 1; q < QN; ++q) {
+      num += pnum[q * DP + tid];
+      den += pden[q * DP + tid];
+    }
+    T* orow = reinterpret_cast<T*>(a.o) + (long long)b * a.o_ld + h * D;
+    orow[tid] = from_f32<T>(num / den);
   }
 }
 

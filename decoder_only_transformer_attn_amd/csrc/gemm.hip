@@ -327,6 +327,78 @@ hipError_t launch_skinny_slices(const void* A, const void* W, int M, int N, int 
   }
 }
 
+// The same product for 33..64 rows split into two 32-row halves
+// (blockIdx.y): a block stages only its half of A next to its 32 weight rows
+// (64 rows x 128 bytes per stage; 96 KB instead of 144 KB for K = 768), so
+// twice as many blocks each bring in two thirds of the bytes.  Each wave
+// multiplies a share of the k-substeps into one 32 x 32 tile; the eight
+// partial tiles are summed in wave order in the freed stages and wave 0 runs
+// the epilogue on rows 32 h ...
+template <int NSTG>
+struct SkHalf {
+  static constexpr int ROWS = 64, STAGE = ROWS * 128, NI = NSTG * ROWS / 8, DPW = NI / SK_WAVES;
+  static constexpr int RED = SK_WAVES * 16 * 64 * 4;   // eight 32 x 32 fp32 tiles
+  static constexpr int BYTES = NSTG * STAGE > RED ? NSTG * STAGE : RED;
+  static_assert(NI % SK_WAVES == 0 && DPW < 64, "loads must split evenly over the waves");
+};
+
+template <typename Epi, int NSTG>
+__global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_half_kernel(const bf16* __restrict__ A,
+                                                                        const bf16* __restrict__ W, int M, int N, int K,
+                                                                        Epi epi) {
+  typedef SkHalf<NSTG> L;
+  __shared__ __align__(1024) char lds[L::BYTES];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
+  const int nrows = min(32, N - n0), mrows = min(32, M - m0);
+  // rows past M (A) and past N (W) lie outside the resources and read as zero
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)nrows * K * sizeof(bf16)));
+#pragma unroll
+  for (int d = 0; d < L::DPW; ++d) {
+    const int ins = wave + d * SK_WAVES;           // uniform: stage ins / 8, rows 8 (ins % 8) ..
+    const int st = ins / 8, ri = ins % 8;
+    const int row = ri * 8 + lane / 8, slot = lane % 8;
+    const int grow = ri < 4 ? row : row - 32;
+    dma16(ri < 4 ? ra : rw, as_lds(lds) + st * L::STAGE + ri * 1024, (uint32_t)((grow * K + swz<8>(row, slot) * 8) * 2),
+          (uint32_t)(st * 64 * 2));
+  }
+  float2 pre[1][1][8];
+  typename Epi::Col colv[1];
+  if (wave == 0) preload_pairs<1, 1>(pre, colv, m0, n0, M, N, epi);
+  wait_vmcnt<0>();
+  lds_barrier();
+  typedef Mfma<bf16> MF;
+  f32x16 c0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) c0[e] = 0.f;
+  const int lrow = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int it = 0; it < NSTG * 4 / SK_WAVES; ++it) {
+    const int j = it * SK_WAVES + wave, c = (j & 3) * 2 + g;
+    const char* s = lds + (j >> 2) * L::STAGE;
+    const MF::frag a0 = __builtin_bit_cast(MF::frag, *reinterpret_cast<const uint4*>(s + lrow * 128 + swz<8>(lrow, c) * 16));
+    const MF::frag wf = __builtin_bit_cast(
+        MF::frag, *reinterpret_cast<const uint4*>(s + (lrow + 32) * 128 + swz<8>(lrow + 32, c) * 16));
+    c0 = MF::mma(a0, wf, c0);
+  }
+  __syncthreads();   // the stages become the reduction buffer
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[wave * 1024 + e * 64 + lane] = c0[e];
+  __syncthreads();
+  if (wave != 0) return;
+  f32x16 acc[1][1];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float t = red[e * 64 + lane];
+#pragma unroll
+    for (int w2 = 1; w2 < SK_WAVES; ++w2) t += red[w2 * 1024 + e * 64 + lane];
+    acc[0][0][e] = t;
+  }
+  epilogue_pairs<1, 1>(acc, pre, colv, m0, n0, M, N, epi);
+}
+
 template <int NSTG, typename Epi>
 static hipError_t run_skinny_lds(const bf16* A, const bf16* W, int M, int N, int K, const Epi& epi,
                                  const SkinnyWs* sk, hipStream_t st) {
@@ -347,6 +419,11 @@ static hipError_t run_skinny(const bf16* A, int lda, const bf16* W, int ldw, int
                              const SkinnyWs* sk, hipStream_t st) {
   if (lda == K && ldw == K && K % 128 == 0) {
     const int n = K / 64, tiles = (N + 31) / 32;
+    if (n == 12 && M > 32 && tiles <= 128) {   // two row halves: at most 256 blocks of 96 KB
+      hipLaunchKernelGGL((gemm_skinny_half_kernel<Epi, 12>), dim3(tiles, 2), dim3(SK_WAVES * 64), 0, st, A, W, M, N,
+                         K, epi);
+      return hipGetLastError();
+    }
     switch (n) {
       case 2: return run_skinny_lds<2>(A, W, M, N, K, epi, sk, st);
       case 4: return run_skinny_lds<4>(A, W, M, N, K, epi, sk, st);
