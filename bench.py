@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "a9cd35c06fec920cbe18c351ef6140712bd4bdd62849b30c124d13093827a814",
-                "bytes": 1798911670}
+HEAD_TRAFFIC = {"gemm_src_sha256": "66ce3ff03162b655ac35395cae008cf4d13869e43ba796b1001c59d1c8d3c392",
+                "bytes": 1821862889}
 
 
 def src_sha(rel):
