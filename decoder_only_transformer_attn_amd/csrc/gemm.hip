@@ -311,22 +311,6 @@ static hipError_t run_skinny_slices(const bf16* A, const bf16* W, int M, int N, 
   return hipGetLastError();
 }
 
-hipError_t launch_skinny_slices(const void* A, const void* W, int M, int N, int K, int S, float* part,
-                                size_t part_floats, hipStream_t st) {
-  if (!A || !W || !part || M <= 0 || M > 64 || N <= 0 || K <= 0 || S <= 0 || K % S != 0) return hipErrorInvalidValue;
-  if ((size_t)S * M * N > part_floats) return hipErrorInvalidValue;
-  const bf16* a = static_cast<const bf16*>(A);
-  const bf16* w = static_cast<const bf16*>(W);
-  switch (K / S) {   // the slice depth: NSTG stages of 64
-    case 128: return run_skinny_slices<2>(a, w, M, N, K, part, st);
-    case 256: return run_skinny_slices<4>(a, w, M, N, K, part, st);
-    case 384: return run_skinny_slices<6>(a, w, M, N, K, part, st);
-    case 512: return run_skinny_slices<8>(a, w, M, N, K, part, st);
-    case 768: return run_skinny_slices<12>(a, w, M, N, K, part, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 // The same product for 33..64 rows split into two 32-row halves
 // (blockIdx.y): a block stages only its half of A next to its 32 weight rows
 // (64 rows x 128 bytes per stage; 96 KB instead of 144 KB for K = 768), so
@@ -397,6 +381,89 @@ __global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_half_kernel(const b
     acc[0][0][e] = t;
   }
   epilogue_pairs<1, 1>(acc, pre, colv, m0, n0, M, N, epi);
+}
+
+// K-slices of 33..64 rows in two 32-row halves (blockIdx.z): the staging of
+// gemm_skinny_half_kernel, the partial tile stored as gemm_skinny_slices_kernel
+// stores it (rows 32 h ..).
+template <int NSTG>
+__global__ void __launch_bounds__(SK_WAVES * 64) gemm_skinny_slices_half_kernel(const bf16* __restrict__ A,
+                                                                               const bf16* __restrict__ W, int M,
+                                                                               int N, int K, float* __restrict__ part) {
+  typedef SkHalf<NSTG> L;
+  __shared__ __align__(1024) char lds[L::BYTES];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 32, k0 = blockIdx.y * NSTG * 64, m0 = blockIdx.z * 32;
+  const int nrows = min(32, N - n0), mrows = min(32, M - m0);
+  // rows past M (A) and past N (W) lie outside the resources and read as zero
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * K, (uint32_t)((size_t)nrows * K * sizeof(bf16)));
+#pragma unroll
+  for (int d = 0; d < L::DPW; ++d) {
+    const int ins = wave + d * SK_WAVES;           // uniform: stage ins / 8, rows 8 (ins % 8) ..
+    const int st = ins / 8, ri = ins % 8;
+    const int row = ri * 8 + lane / 8, slot = lane % 8;
+    const int grow = ri < 4 ? row : row - 32;
+    dma16(ri < 4 ? ra : rw, as_lds(lds) + st * L::STAGE + ri * 1024, (uint32_t)((grow * K + swz<8>(row, slot) * 8) * 2),
+          (uint32_t)((k0 + st * 64) * 2));
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+  typedef Mfma<bf16> MF;
+  f32x16 c0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) c0[e] = 0.f;
+  const int lrow = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int it = 0; it < NSTG * 4 / SK_WAVES; ++it) {
+    const int j = it * SK_WAVES + wave, c = (j & 3) * 2 + g;
+    const char* s = lds + (j >> 2) * L::STAGE;
+    const MF::frag a0 = __builtin_bit_cast(MF::frag, *reinterpret_cast<const uint4*>(s + lrow * 128 + swz<8>(lrow, c) * 16));
+    const MF::frag wf = __builtin_bit_cast(
+        MF::frag, *reinterpret_cast<const uint4*>(s + (lrow + 32) * 128 + swz<8>(lrow + 32, c) * 16));
+    c0 = MF::mma(a0, wf, c0);
+  }
+  __syncthreads();   // the stages become the reduction buffer
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[wave * 1024 + e * 64 + lane] = c0[e];
+  __syncthreads();
+  float* out = part + (size_t)blockIdx.y * M * N;
+  for (int e = threadIdx.x; e < 1024; e += SK_WAVES * 64) {
+    float t = red[e];
+#pragma unroll
+    for (int w2 = 1; w2 < SK_WAVES; ++w2) t += red[w2 * 1024 + e];
+    // element e: register r, lane l of the MFMA layout
+    const int r = e >> 6, l = e & 63;
+    const int m = m0 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3), n = n0 + (l & 31);
+    if (m < M && n < N) out[(size_t)m * N + n] = t;
+  }
+}
+
+template <int NSTG>
+static hipError_t run_skinny_slices_any(const bf16* A, const bf16* W, int M, int N, int K, float* part,
+                                        hipStream_t st) {
+  if (M <= 32) return run_skinny_slices<NSTG>(A, W, M, N, K, part, st);
+  const int tiles = (N + 31) / 32, S = K / (64 * NSTG);
+  hipLaunchKernelGGL((gemm_skinny_slices_half_kernel<NSTG>), dim3(tiles, S, 2), dim3(SK_WAVES * 64), 0, st, A, W, M,
+                     N, K, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_slices(const void* A, const void* W, int M, int N, int K, int S, float* part,
+                                size_t part_floats, hipStream_t st) {
+  if (!A || !W || !part || M <= 0 || M > 64 || N <= 0 || K <= 0 || S <= 0 || K % S != 0) return hipErrorInvalidValue;
+  if ((size_t)S * M * N > part_floats) return hipErrorInvalidValue;
+  const bf16* a = static_cast<const bf16*>(A);
+  const bf16* w = static_cast<const bf16*>(W);
+  switch (K / S) {   // the slice depth: NSTG stages of 64
+    case 128: return run_skinny_slices_any<2>(a, w, M, N, K, part, st);
+    case 256: return run_skinny_slices_any<4>(a, w, M, N, K, part, st);
+    case 384: return run_skinny_slices_any<6>(a, w, M, N, K, part, st);
+    case 512: return run_skinny_slices_any<8>(a, w, M, N, K, part, st);
+    case 768: return run_skinny_slices_any<12>(a, w, M, N, K, part, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int NSTG, typename Epi>
