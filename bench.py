@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) divided by the
 # factor the same counters read for a plain device copy of known size.  Valid
 # only for the kernel source it was taken on: null once gemm.hip changes.
-HEAD_TRAFFIC = {"gemm_src_sha256": "66ce3ff03162b655ac35395cae008cf4d13869e43ba796b1001c59d1c8d3c392",
-                "bytes": 1821862889}
+HEAD_TRAFFIC = {"gemm_src_sha256": "3444a3031ae4d8a965089be72fdbdc93a861ee48ceb3554456d1dc6523cd93ba",
+                "bytes": 1816586216}
 
 
 def src_sha(rel):
